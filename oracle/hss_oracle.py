@@ -1,0 +1,317 @@
+"""CPU oracle for the sparse + low-rank (HSS) linear layer  Y = X (S + U V^T)^T.
+
+TEST INFRASTRUCTURE ONLY.  This module is the slow, obviously-correct fp64
+statement of what the GPU library computes.  Only the tests, the package's
+smoke check and the benchmark's CPU-baseline leg may import it; the product
+path never does.  It shares no code with the HIP library and imports nothing
+from this repository.
+
+Sources (web pages; section names as printed on each page)
+-----------------------------------------------------------
+[HSS]     "LLMの階層的スパース+低ランク圧縮" (hierarchical sparse + low-rank
+          compression of LLMs), d7fyzohlfz9vz.cloudfront.net/posts/
+          hierarchical-sparse-plus-low-rank-compression-of-llm
+          - section "2段階階層的スパース+低ランク圧縮" (two-stage HSS):
+            the decomposition W ~= S + U V^T with U (m x r), V (n x r);
+            stage 1 keeps the top fraction of weights by absolute magnitude,
+            stage 2 factors the remaining dense residual; the 1024 x 1024
+            worked example (具体例); rank starts at 10 % of the dimension
+            (actionable-implications paragraph).
+          - section "2段階階層的スパース+低ランク圧縮:ハイブリッドの利点" (vision
+            rewrite): top 5-10 % by magnitude, the residual is rebuilt with
+            minimal error; rank = 102 for a 1024-wide layer.
+          - section "実装と運用パターン" (implementation patterns): S stored as
+            indices + values (COO/CSR), U and V dense; the forward pass splits
+            into one sparse product plus two small dense products.
+[HASSLE]  aibr.jp/archives/82335 (explainer of HASSLE-free), section
+          "3.中核となる技術的要素": N:M sparsity as the GPU-friendly structure.
+
+Readings where the pages are silent (each is listed in the design notes):
+* k = floor(m*n*num/den) in exact integer arithmetic (the worked example
+  prints 52,428 for 5 % of 1,048,576, i.e. floor).
+* Ties at the threshold go to the lower row-major linear index; exactly k
+  entries are kept.
+* |+0| = |-0| = 0; NaN/Inf weights are rejected.
+* 2:4 = keep the 2 largest |w| of each group of 4 consecutive columns (along
+  the reduction dimension), ties to the lower column.
+* Stage 2 is one truncated SVD of the whole residual at rank r, with the
+  singular values folded into U (U = U_r diag(s_r), V = V_r).
+* The residual equals W with the kept positions set to +0 (no subtraction).
+
+Storage conventions (the same ones the C library documents):
+  fp32 values are numpy.float32; bf16 values are their bit patterns in
+  numpy.uint16.  Matrices are row-major.  W is m x n (out x in), X is b x n,
+  Y is b x m.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F32 = "f32"
+BF16 = "bf16"
+
+
+# ---------------------------------------------------------------------------
+# Storage-type helpers (exact widening; RNE narrowing)
+# ---------------------------------------------------------------------------
+
+def widen(a, dtype):
+    """Exact fp64 values of stored fp32 / bf16 data."""
+    if dtype == F32:
+        return np.asarray(a, dtype=np.float32).astype(np.float64)
+    if dtype == BF16:
+        bits = np.asarray(a, dtype=np.uint16).astype(np.uint32) << 16
+        return bits.view(np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+def narrow(a64, dtype):
+    """fp64 -> storage type, round to nearest even at each step (fp64->fp32->bf16)."""
+    a32 = np.asarray(a64, dtype=np.float64).astype(np.float32)
+    if dtype == F32:
+        return a32
+    if dtype == BF16:
+        u = a32.view(np.uint32).astype(np.uint64)
+        # bf16 = upper half of fp32; add half an ulp minus one, plus the lsb of
+        # the kept part, then truncate: ties go to the even pattern.
+        return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    raise ValueError(dtype)
+
+
+def bits_equal(a, b):
+    """Bitwise equality of two stored arrays of the same storage type."""
+    a = np.ascontiguousarray(a)
+    b = np.ascontiguousarray(b)
+    if a.shape != b.shape or a.dtype.itemsize != b.dtype.itemsize:
+        return False
+    view = {2: np.uint16, 4: np.uint32, 8: np.uint64}[a.dtype.itemsize]
+    return bool(np.array_equal(a.view(view), b.view(view)))
+
+
+# ---------------------------------------------------------------------------
+# Counts  ([HSS] two-stage section, worked example; vision rewrite, rank rule)
+# ---------------------------------------------------------------------------
+
+def topk_count(m, n, num, den):
+    """Number of weights kept in S for a kept fraction num/den: floor(m*n*num/den)."""
+    m, n, num, den = int(m), int(n), int(num), int(den)
+    if m < 0 or n < 0 or num < 0 or den <= 0:
+        raise ValueError("bad count arguments")
+    return (m * n * num) // den
+
+
+def rank_rule(m, n, num=10, den=100):
+    """Starting rank: num/den of the smaller matrix dimension, floored (1024 -> 102)."""
+    return (min(int(m), int(n)) * int(num)) // int(den)
+
+
+def param_count(k, m, n, r):
+    """Stored parameters of S + U V^T: k sparse values plus (m + n) r factor entries."""
+    return int(k) + (int(m) + int(n)) * int(r)
+
+
+def compression_ratio(m, n, k, r):
+    """Dense parameters over stored parameters (1024^2, 5 %, rank 64 -> 5.714)."""
+    return (int(m) * int(n)) / param_count(k, m, n, r)
+
+
+# ---------------------------------------------------------------------------
+# Stage 1: magnitude top-k and its storage
+# ---------------------------------------------------------------------------
+
+def magnitudes(W, dtype):
+    """|w| in fp64 (exact).  Non-finite weights have no magnitude order: rejected."""
+    a = np.abs(widen(W, dtype))
+    if not np.all(np.isfinite(a)):
+        raise ValueError("non-finite weight")
+    return a
+
+
+def topk_mask(W, dtype, k):
+    """Boolean m x n mask of the k weights of largest |w|.
+
+    Order: |w| descending, then row-major linear index ascending (a stable
+    sort of -|w|), and the first k positions of that order are kept."""
+    m, n = W.shape
+    k = int(k)
+    if not 0 <= k <= m * n:
+        raise ValueError("k out of range")
+    a = magnitudes(W, dtype).reshape(-1)
+    order = np.argsort(-a, kind="stable")
+    mask = np.zeros(m * n, dtype=bool)
+    mask[order[:k]] = True
+    return mask.reshape(m, n)
+
+
+def csr_from_mask(W, mask):
+    """CSR of the masked entries: row_ptr int32[m+1], col_idx int32[nnz]
+    (ascending within each row), values[nnz] = the stored W bits."""
+    m, n = W.shape
+    counts = mask.sum(axis=1)
+    row_ptr = np.zeros(m + 1, dtype=np.int64)
+    row_ptr[1:] = np.cumsum(counts)
+    rows, cols = np.nonzero(mask)          # row-major order: rows asc, cols asc
+    values = np.ascontiguousarray(W[rows, cols])
+    return row_ptr.astype(np.int32), cols.astype(np.int32), values
+
+
+def residual(W, mask):
+    """W with the kept positions replaced by +0 (bit pattern 0); other bits unchanged."""
+    R = np.array(W, copy=True)
+    R[mask] = 0
+    return R
+
+
+def split_csr(W, dtype, k):
+    """Stage 1 in CSR form.  Returns dict(row_ptr, col_idx, values, residual, mask)."""
+    mask = topk_mask(W, dtype, k)
+    row_ptr, col_idx, values = csr_from_mask(W, mask)
+    return dict(row_ptr=row_ptr, col_idx=col_idx, values=values,
+                residual=residual(W, mask), mask=mask)
+
+
+def nm24_mask(W, dtype):
+    """2:4 mask: in each group of 4 consecutive columns keep the 2 largest |w|,
+    ties to the lower column ([HASSLE] N:M structure; groups along the input
+    (reduction) dimension, starting at column 0)."""
+    m, n = W.shape
+    if n % 4 != 0:
+        raise ValueError("2:4 needs n % 4 == 0")
+    a = magnitudes(W, dtype).reshape(m, n // 4, 4)
+    order = np.argsort(-a, axis=-1, kind="stable")      # (|w| desc, column asc)
+    keep = np.zeros_like(a, dtype=bool)
+    np.put_along_axis(keep, order[..., :2], True, axis=-1)
+    return keep.reshape(m, n)
+
+
+def split_24(W, dtype):
+    """Stage 1 in 2:4 form.
+
+    nm_values[i, 2g+s] = W bits of the s-th kept entry (ascending column) of
+    group g of row i; nm_meta[i, g // 8] holds, at bits 4*(g % 8) .. +3, the
+    nibble i0 | (i1 << 2) with i0 < i1 the kept positions inside the group.
+    Returns dict(nm_values, nm_meta, residual, mask)."""
+    m, n = W.shape
+    mask = nm24_mask(W, dtype)
+    groups = n // 4
+    words = (n + 31) // 32
+    kept_pos = np.nonzero(mask.reshape(m, groups, 4))[2].reshape(m, groups, 2)  # ascending
+    nm_values = np.ascontiguousarray(W[mask].reshape(m, groups * 2))
+    nib = (kept_pos[..., 0] | (kept_pos[..., 1] << 2)).astype(np.uint64)
+    nm_meta = np.zeros((m, words), dtype=np.uint64)
+    for g in range(groups):
+        nm_meta[:, g // 8] |= nib[:, g] << np.uint64(4 * (g % 8))
+    return dict(nm_values=nm_values, nm_meta=nm_meta.astype(np.uint32),
+                residual=residual(W, mask), mask=mask)
+
+
+def dense_from_csr(m, n, row_ptr, col_idx, values, dtype):
+    """fp64 dense S rebuilt from CSR (stored values widened exactly)."""
+    S = np.zeros((m, n), dtype=np.float64)
+    v = widen(values, dtype)
+    for i in range(m):
+        lo, hi = int(row_ptr[i]), int(row_ptr[i + 1])
+        S[i, col_idx[lo:hi]] = v[lo:hi]
+    return S
+
+
+def dense_from_24(m, n, nm_values, nm_meta, dtype):
+    """fp64 dense S rebuilt from 2:4 values + nibble metadata."""
+    S = np.zeros((m, n), dtype=np.float64)
+    v = widen(nm_values, dtype).reshape(m, n // 2)
+    meta = np.asarray(nm_meta, dtype=np.uint32).reshape(m, -1)
+    for g in range(n // 4):
+        nib = (meta[:, g // 8] >> np.uint32(4 * (g % 8))) & np.uint32(0xF)
+        i0 = (nib & 3).astype(np.int64)
+        i1 = ((nib >> 2) & 3).astype(np.int64)
+        rows = np.arange(m)
+        S[rows, 4 * g + i0] = v[:, 2 * g]
+        S[rows, 4 * g + i1] = v[:, 2 * g + 1]
+    return S
+
+
+# ---------------------------------------------------------------------------
+# Stage 2: truncated SVD of the residual  ([HSS] two-stage section)
+# ---------------------------------------------------------------------------
+
+def truncated_svd(R64, r):
+    """Rank-r factors of the fp64 residual: U = U_r diag(s_r) (m x r), V = V_r (n x r).
+
+    LAPACK gesdd through numpy.  Each singular pair is sign-normalised so that
+    the largest-|.| entry of the V column is positive (first index on ties).
+    Returns (U, V, s) with s the full vector of singular values."""
+    R64 = np.asarray(R64, dtype=np.float64)
+    m, n = R64.shape
+    r = int(r)
+    if not 0 <= r <= min(m, n):
+        raise ValueError("rank out of range")
+    Uf, s, Vt = np.linalg.svd(R64, full_matrices=False)
+    U = Uf[:, :r] * s[:r][None, :]
+    V = Vt[:r].T.copy()
+    for l in range(r):
+        j = int(np.argmax(np.abs(V[:, l])))
+        if V[j, l] < 0:
+            V[:, l] = -V[:, l]
+            U[:, l] = -U[:, l]
+    return U, V, s
+
+
+# ---------------------------------------------------------------------------
+# Apply: Y = X S^T + (X V) U^T   ([HSS] implementation-patterns section)
+# ---------------------------------------------------------------------------
+
+def apply_factored(S64, U64, V64, X64):
+    """Factored forward in fp64: sparse term plus two small dense products."""
+    Y = X64 @ S64.T
+    if U64.shape[1] > 0:
+        Y = Y + (X64 @ V64) @ U64.T
+    return Y
+
+
+def apply_dense(S64, U64, V64, X64):
+    """Dense forward in fp64 with the rebuilt A = S + U V^T."""
+    return X64 @ (S64 + U64 @ V64.T).T
+
+
+def normaliser(S64, U64, V64, X64):
+    """N[c, i] = sum_j |A_ij X_cj| with A = S + U V^T in fp64: the scale the
+    per-output error bound is stated against."""
+    A = S64 + U64 @ V64.T
+    return np.abs(X64) @ np.abs(A).T
+
+
+def max_normalised_error(Y, Y_ref, N):
+    """max over outputs of |Y - Y_ref| / N; an output with N == 0 must be 0 exactly
+    (else the result is inf)."""
+    Y = np.asarray(Y, dtype=np.float64)
+    err = np.abs(Y - Y_ref)
+    zero = N == 0
+    if np.any(err[zero] != 0):
+        return float("inf")
+    if not np.any(~zero):
+        return 0.0
+    return float(np.max(err[~zero] / N[~zero]))
+
+
+# Error tolerances of the apply step (per output, relative to N).
+TOL = {F32: 1e-5, BF16: 8e-3}
+
+
+# ---------------------------------------------------------------------------
+# Row-sampled apply for full-size checks (same definitions, a subset of rows)
+# ---------------------------------------------------------------------------
+
+def csr_rows_dense(rows, n, row_ptr, col_idx, values, dtype):
+    """fp64 dense rows of S (len(rows) x n) from CSR."""
+    out = np.zeros((len(rows), n), dtype=np.float64)
+    v = widen(values, dtype)
+    for t, i in enumerate(rows):
+        lo, hi = int(row_ptr[i]), int(row_ptr[i + 1])
+        out[t, col_idx[lo:hi]] = v[lo:hi]
+    return out
+
+
+def apply_rows(S_rows64, U_rows64, V64, X64):
+    """Y[:, rows] and N[:, rows] from the dense rows of S and the rows of U."""
+    A_rows = S_rows64 + U_rows64 @ V64.T
+    return X64 @ A_rows.T, np.abs(X64) @ np.abs(A_rows).T

@@ -1,0 +1,150 @@
+"""Planted mistakes in the oracle must fail its pins.
+
+Each case swaps one oracle function for a plausibly wrong variant (a dropped
+term, a reversed tie-break, a transposed operand, a wrong rounding ...) and
+checks that at least one of the pins in test_oracle_pins raises.  This shows
+the pins can see the mistakes they are meant to catch.  Everything runs on the
+CPU; nothing here touches the GPU path.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.hss_oracle as H
+import test_oracle_pins as P
+
+
+def _patch(monkeypatch, name, fn):
+    monkeypatch.setattr(H, name, fn)
+    monkeypatch.setattr(oracle, name, fn)
+
+
+def _fails(*tests):
+    for t in tests:
+        try:
+            t()
+        except (AssertionError, ValueError, IndexError):
+            return True
+    return False
+
+
+def _apply_no_lowrank(S, U, V, X):
+    return X @ S.T
+
+
+def _apply_swapped_factors(S, U, V, X):
+    return X @ S.T + (X @ U) @ V.T          # U and V exchanged
+
+
+def _apply_transposed_sparse(S, U, V, X):
+    return X @ S + (X @ V) @ U.T            # S not transposed
+
+
+def _topk_ties_high(W, dtype, k):
+    m, n = W.shape
+    a = H.magnitudes(W, dtype).reshape(-1)
+    order = np.argsort(-a[::-1], kind="stable")
+    order = (m * n - 1) - order
+    mask = np.zeros(m * n, dtype=bool)
+    mask[order[:k]] = True
+    return mask.reshape(m, n)
+
+
+def _topk_signed(W, dtype, k):
+    m, n = W.shape
+    a = H.widen(W, dtype).reshape(-1)                  # sign kept: not a magnitude
+    order = np.argsort(-a, kind="stable")
+    mask = np.zeros(m * n, dtype=bool)
+    mask[order[:k]] = True
+    return mask.reshape(m, n)
+
+
+def _count_rounded(m, n, num, den):
+    return int(round(m * n * num / den))
+
+
+def _nm24_ties_high(W, dtype):
+    m, n = W.shape
+    a = H.magnitudes(W, dtype).reshape(m, n // 4, 4)[..., ::-1]
+    order = 3 - np.argsort(-a, axis=-1, kind="stable")
+    keep = np.zeros((m, n // 4, 4), dtype=bool)
+    np.put_along_axis(keep, order[..., :2], True, axis=-1)
+    return keep.reshape(m, n)
+
+
+_orig_split_24 = H.split_24
+
+
+def _split24_nibble_swapped(W, dtype):
+    out = _orig_split_24(W, dtype)
+    meta = out["nm_meta"].astype(np.uint64)
+    fixed = np.zeros_like(meta)
+    for s in range(8):
+        nib = (meta >> np.uint64(4 * s)) & np.uint64(0xF)
+        swapped = ((nib & np.uint64(3)) << np.uint64(2)) | (nib >> np.uint64(2))
+        fixed |= swapped << np.uint64(4 * s)
+    out["nm_meta"] = fixed.astype(np.uint32)
+    return out
+
+
+def _svd_sigma_dropped(R64, r):
+    Uf, s, Vt = np.linalg.svd(R64, full_matrices=False)
+    return Uf[:, :r].copy(), Vt[:r].T.copy(), s
+
+
+def _svd_v_not_transposed(R64, r):
+    Uf, s, Vt = np.linalg.svd(R64, full_matrices=False)
+    V = Vt[:r].copy()
+    if V.shape != (R64.shape[1], r):
+        V = np.resize(V, (R64.shape[1], r))
+    return Uf[:, :r] * s[:r], V, s
+
+
+def _normaliser_no_abs_x(S, U, V, X):
+    return X @ np.abs(S + U @ V.T).T
+
+
+_orig_csr_from_mask = H.csr_from_mask
+
+
+def _csr_cols_descending(W, mask):
+    rp, ci, v = _orig_csr_from_mask(W, mask)
+    for i in range(len(rp) - 1):
+        ci[rp[i]:rp[i + 1]] = ci[rp[i]:rp[i + 1]][::-1]
+    return rp, ci, v
+
+
+def _residual_keeps_values(W, mask):
+    return np.array(W, copy=True)
+
+
+CASES = [
+    ("apply_factored", _apply_no_lowrank,
+     [P.test_apply_hand_example, lambda: [P.test_apply_factored_equals_dense(s) for s in range(5)]]),
+    ("apply_factored", _apply_swapped_factors,
+     [P.test_apply_hand_example, lambda: P.test_apply_factored_equals_dense(0)]),
+    ("apply_factored", _apply_transposed_sparse,
+     [P.test_apply_hand_example, lambda: P.test_apply_factored_equals_dense(0)]),
+    ("topk_mask", _topk_ties_high,
+     [lambda: P.test_topk_matches_brute_force("equal", H.BF16, (3, 4)), P.test_topk_tie_split_across_rows]),
+    ("topk_mask", _topk_signed,
+     [lambda: P.test_topk_matches_brute_force("t3", H.F32, (6, 6))]),
+    ("topk_count", _count_rounded, [P.test_worked_example_counts]),
+    ("nm24_mask", _nm24_ties_high,
+     [lambda: P.test_nm24_matches_brute_force("ties", H.BF16), P.test_nm24_hand_row]),
+    ("split_24", _split24_nibble_swapped, [P.test_nm24_hand_row]),
+    ("truncated_svd", _svd_sigma_dropped,
+     [P.test_svd_eckart_young_and_orthonormality, P.test_svd_recovers_known_spectrum]),
+    ("truncated_svd", _svd_v_not_transposed,
+     [P.test_svd_eckart_young_and_orthonormality, P.test_svd_recovers_known_spectrum]),
+    ("normaliser", _normaliser_no_abs_x, [P.test_normaliser_loop_definition]),
+    ("csr_from_mask", _csr_cols_descending,
+     [lambda: P.test_csr_matches_scipy(H.F32), lambda: P.test_csr_roundtrip_and_residual("t3")]),
+    ("residual", _residual_keeps_values, [lambda: P.test_csr_roundtrip_and_residual("t3")]),
+]
+
+
+@pytest.mark.parametrize("name,fn,pins", CASES, ids=[f"{c[0]}:{c[1].__name__}" for c in CASES])
+def test_planted_mistake_is_caught(monkeypatch, name, fn, pins):
+    _patch(monkeypatch, name, fn)
+    assert _fails(*pins), f"no pin caught the planted mistake {fn.__name__} in {name}"

@@ -1,0 +1,360 @@
+"""Pins of the CPU oracle against facts fixed by the pages and by mathematics.
+
+Each test ties an oracle function to something other than itself: numbers the
+pages print (fixtures under tests/golden/, each with its citation), closed
+forms, brute force on tiny inputs, or independent library routines.
+"""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+import scipy.linalg
+import scipy.sparse
+
+import hss_synth as syn
+import oracle as O
+from conftest import GOLDEN
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------
+# Counts: the 1024 x 1024 worked example and the rank rule
+# ---------------------------------------------------------------------------
+
+def test_worked_example_counts():
+    g = _golden("worked_example_1024.json")
+    m, n, r = g["m"], g["n"], g["rank"]
+    k = O.topk_count(m, n, *g["kept_fraction"])
+    assert m * n == g["dense_params"]
+    assert k == g["sparse_kept"]                                   # 52,428: floor, not round
+    assert O.param_count(0, m, n, r) == g["lowrank_params"]         # 2 x 1024 x 64
+    assert O.param_count(k, m, n, r) == g["total_params"]           # 183,500
+    assert round(O.compression_ratio(m, n, k, r), 1) == g["reduction_printed"]
+    # 87 % residual footprint reduction: 131,072 factor entries replace the
+    # m*n - k residual values.
+    assert round(100 * (1 - g["lowrank_params"] / (m * n - k))) == g["residual_footprint_reduction_pct_printed"]
+    # The printed residual count is off by 1,000 (typo on the page).
+    assert m * n - k == 996148
+    assert m * n - k - g["residual_count_printed"] == 1000
+
+
+def test_rank_rule():
+    g = _golden("rank_rule.json")
+    assert O.rank_rule(g["dim"], g["dim"], *g["fraction"]) == g["rank"]
+    # The decoder-layer workload's rank, 10 % of min(m, n) = 4096, floored.
+    assert O.rank_rule(4096, 11008) == 409 == O.rank_rule(11008, 4096)
+
+
+def test_topk_count_is_floor_in_integers():
+    # 0.05 * 1048576 = 52428.8: floor, and exact (no binary 0.05).
+    assert O.topk_count(1024, 1024, 5, 100) == 52428
+    assert O.topk_count(4096, 4096, 5, 100) == 838860
+    assert O.topk_count(4096, 4096, 3, 100) == 503316
+    assert O.topk_count(11008, 4096, 3, 100) == 1352663
+    assert O.topk_count(8192, 8192, 3, 100) == 2013265
+    assert O.topk_count(3, 3, 1, 3) == 3
+    assert O.topk_count(7, 1, 0, 100) == 0
+
+
+def test_config1_oracle_reproduces_worked_example():
+    """The first workload is the worked example's shape: the oracle's split and
+    factor shapes must give the printed parameter total."""
+    cfg = syn.CONFIGS[1]
+    W = syn.weight(cfg)
+    m, n = W.shape
+    k = O.topk_count(m, n, *cfg.frac)
+    s = O.split_csr(W, O.F32, k)
+    assert int(s["row_ptr"][-1]) == len(s["col_idx"]) == 52428
+    nnz_res = int(np.count_nonzero(~s["mask"]))
+    assert nnz_res == 996148
+    assert O.param_count(len(s["values"]), m, n, cfg.rank[0]) == 183500
+
+
+# ---------------------------------------------------------------------------
+# Stage 1: top-k by magnitude
+# ---------------------------------------------------------------------------
+
+def _brute_topk(W, dtype, k):
+    m, n = W.shape
+    vals = O.widen(W, dtype).reshape(-1)
+    keys = [abs(float(v)) for v in vals]
+    order = sorted(range(m * n), key=lambda t: (-keys[t], t))
+    mask = np.zeros(m * n, dtype=bool)
+    for t in order[:k]:
+        mask[t] = True
+    return mask.reshape(m, n)
+
+
+@pytest.mark.parametrize("kind", ["t3", "ties", "equal", "zeros", "ints"])
+@pytest.mark.parametrize("dtype", [O.F32, O.BF16])
+@pytest.mark.parametrize("shape", [(1, 1), (1, 6), (5, 1), (3, 4), (6, 6)])
+def test_topk_matches_brute_force(kind, dtype, shape):
+    m, n = shape
+    W = syn.random_matrix(m, n, dtype, seed=11, kind=kind)
+    for k in range(m * n + 1):
+        assert np.array_equal(O.topk_mask(W, dtype, k), _brute_topk(W, dtype, k)), k
+
+
+def test_topk_invariants_config1():
+    cfg = syn.CONFIGS[1]
+    W = syn.weight(cfg)
+    k = O.topk_count(*W.shape, *cfg.frac)
+    mask = O.topk_mask(W, O.F32, k)
+    a = np.abs(W.astype(np.float64))
+    assert mask.sum() == k
+    assert a[mask].min() >= a[~mask].max()
+    T = a[mask].min()
+    flat_eq = np.flatnonzero((a == T).reshape(-1))
+    kept_eq = np.flatnonzero((mask & (a == T)).reshape(-1))
+    assert np.array_equal(kept_eq, flat_eq[: len(kept_eq)])        # lowest linear indices
+
+
+def test_topk_tie_split_across_rows():
+    # Every magnitude equal: S must be the first k row-major positions.
+    W = syn.random_matrix(7, 5, O.BF16, seed=3, kind="equal")
+    for k in (0, 1, 4, 5, 6, 17, 35):
+        mask = O.topk_mask(W, O.BF16, k)
+        assert np.array_equal(np.flatnonzero(mask.reshape(-1)), np.arange(k))
+
+
+def test_topk_signed_zero_and_nonfinite():
+    W = np.array([[-0.0, 0.0, 1.0]], dtype=np.float32)
+    assert np.array_equal(O.topk_mask(W, O.F32, 2), [[True, False, True]])
+    with pytest.raises(ValueError):
+        O.topk_mask(np.array([[np.nan, 1.0]], dtype=np.float32), O.F32, 1)
+    with pytest.raises(ValueError):
+        O.topk_mask(np.array([[np.inf, 1.0]], dtype=np.float32), O.F32, 1)
+    with pytest.raises(ValueError):
+        O.topk_mask(np.zeros((2, 2), np.float32), O.F32, 5)
+
+
+# ---------------------------------------------------------------------------
+# CSR storage and the residual
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [O.F32, O.BF16])
+def test_csr_matches_scipy(dtype):
+    W = syn.random_matrix(37, 53, dtype, seed=5, kind="t3")
+    k = O.topk_count(37, 53, 5, 100)
+    s = O.split_csr(W, dtype, k)
+    dense = O.widen(W, dtype) * s["mask"]
+    assert np.count_nonzero(dense) == k          # no kept zero, so scipy keeps all
+    ref = scipy.sparse.csr_matrix(dense)
+    ref.sort_indices()
+    assert np.array_equal(s["row_ptr"], ref.indptr)
+    assert np.array_equal(s["col_idx"], ref.indices)
+    assert np.array_equal(O.widen(s["values"], dtype), ref.data)
+
+
+@pytest.mark.parametrize("kind", ["t3", "ties", "zeros"])
+def test_csr_roundtrip_and_residual(kind):
+    dtype = O.BF16
+    W = syn.random_matrix(19, 24, dtype, seed=2, kind=kind)
+    k = 57
+    s = O.split_csr(W, dtype, k)
+    S = O.dense_from_csr(19, 24, s["row_ptr"], s["col_idx"], s["values"], dtype)
+    R = O.widen(s["residual"], dtype)
+    Wd = O.widen(W, dtype)
+    assert np.array_equal(S + R, Wd)                     # R + S == W
+    assert np.all(s["residual"][s["mask"]] == 0)         # +0 bits on supp(S)
+    assert O.bits_equal(s["residual"][~s["mask"]], W[~s["mask"]])
+    assert len(s["values"]) == k
+    assert O.bits_equal(s["values"], W[s["mask"]])       # bits copied (sign of zeros too)
+    for i in range(19):                                  # ascending columns within rows
+        c = s["col_idx"][s["row_ptr"][i]:s["row_ptr"][i + 1]]
+        assert np.all(np.diff(c) > 0)
+
+
+# ---------------------------------------------------------------------------
+# Stage 1, 2:4 form
+# ---------------------------------------------------------------------------
+
+def _brute_pair(mags):
+    """Lexicographically smallest pair (i0 < i1) with every kept |w| >= every dropped |w|."""
+    for i0, i1 in itertools.combinations(range(4), 2):
+        kept = [mags[i0], mags[i1]]
+        dropped = [mags[t] for t in range(4) if t not in (i0, i1)]
+        if min(kept) >= max(dropped):
+            return i0, i1
+    raise AssertionError("no valid pair")
+
+
+@pytest.mark.parametrize("kind", ["t3", "ties", "equal", "zeros", "ints"])
+@pytest.mark.parametrize("dtype", [O.F32, O.BF16])
+def test_nm24_matches_brute_force(kind, dtype):
+    m, n = 9, 40
+    W = syn.random_matrix(m, n, dtype, seed=8, kind=kind)
+    s = O.split_24(W, dtype)
+    a = np.abs(O.widen(W, dtype))
+    for i in range(m):
+        for g in range(n // 4):
+            i0, i1 = _brute_pair(list(a[i, 4 * g:4 * g + 4]))
+            expect = np.zeros(4, bool)
+            expect[[i0, i1]] = True
+            assert np.array_equal(s["mask"][i, 4 * g:4 * g + 4], expect)
+            nib = (int(s["nm_meta"][i, g // 8]) >> (4 * (g % 8))) & 0xF
+            assert nib == i0 | (i1 << 2)
+    S = O.dense_from_24(m, n, s["nm_values"], s["nm_meta"], dtype)
+    assert np.array_equal(S + O.widen(s["residual"], dtype), O.widen(W, dtype))
+    assert np.all((S != 0).reshape(m, n // 4, 4).sum(-1) <= 2)
+
+
+def test_nm24_hand_row():
+    g = _golden("nm24_hand_row.json")
+    W = np.array([g["row"]], dtype=np.float32)
+    s = O.split_24(W, O.F32)
+    assert s["nm_meta"].shape == (1, 1)
+    assert int(s["nm_meta"][0, 0]) == g["meta_word"] == int(g["meta_word_hex"], 16)
+    assert np.array_equal(s["nm_values"][0], np.array(g["values"], dtype=np.float32))
+
+
+def test_nm24_partial_meta_word():
+    # n = 36: 9 groups, two meta words; the unused nibbles of word 1 are zero.
+    W = syn.random_matrix(3, 36, O.BF16, seed=1, kind="t3")
+    s = O.split_24(W, O.BF16)
+    assert s["nm_meta"].shape == (3, 2)
+    assert np.all((s["nm_meta"][:, 1] >> 4) == 0)
+
+
+# ---------------------------------------------------------------------------
+# Stage 2: truncated SVD
+# ---------------------------------------------------------------------------
+
+def _orthonormal(rng, m, k):
+    q, _ = np.linalg.qr(rng.standard_normal((m, k)))
+    return q
+
+
+def test_svd_eckart_young_and_orthonormality():
+    W = syn.random_matrix(80, 60, O.F32, seed=4, kind="t3")
+    k = O.topk_count(80, 60, 5, 100)
+    R = O.widen(O.split_csr(W, O.F32, k)["residual"], O.F32)
+    for r in (0, 1, 7, 60):
+        U, V, s = O.truncated_svd(R, r)
+        assert U.shape == (80, r) and V.shape == (60, r)
+        err = np.linalg.norm(R - U @ V.T)
+        expect = np.sqrt(np.sum(s[r:] ** 2))
+        assert abs(err - expect) <= 1e-10 * max(expect, 1e-300) + 1e-13
+        assert np.max(np.abs(V.T @ V - np.eye(r)), initial=0) <= 1e-12
+        for l in range(r):                        # sign rule
+            j = int(np.argmax(np.abs(V[:, l])))
+            assert V[j, l] > 0
+    s2 = scipy.linalg.svd(R, compute_uv=False, lapack_driver="gesvd")
+    assert np.max(np.abs(s - s2)) <= 1e-12 * s[0]
+
+
+def test_svd_recovers_known_spectrum():
+    rng = np.random.default_rng(0)
+    m, n, true = 50, 30, np.array([9.0, 5.0, 4.0, 1.5, 0.25])
+    A = _orthonormal(rng, m, 5) @ np.diag(true) @ _orthonormal(rng, n, 5).T
+    U, V, s = O.truncated_svd(A, 5)
+    assert np.allclose(s[:5], true, rtol=0, atol=1e-12)
+    assert np.max(np.abs(s[5:])) <= 1e-12
+    assert np.max(np.abs(A - U @ V.T)) <= 1e-12                   # exact for a rank-5 matrix
+    U2, V2, _ = O.truncated_svd(A, 2)                              # best rank 2 drops 4.0, 1.5, 0.25
+    assert abs(np.linalg.norm(A - U2 @ V2.T) - np.sqrt(4.0**2 + 1.5**2 + 0.25**2)) <= 1e-12
+
+
+# ---------------------------------------------------------------------------
+# Apply: factored vs dense, special cases, hand example
+# ---------------------------------------------------------------------------
+
+def _tiny_problem(seed, m=6, n=8, r=3, b=4, k=10):
+    rng = np.random.default_rng(seed)
+    W = syn.random_matrix(m, n, O.F32, seed=seed, kind="t3")
+    s = O.split_csr(W, O.F32, k)
+    S = O.dense_from_csr(m, n, s["row_ptr"], s["col_idx"], s["values"], O.F32)
+    return s, S, rng.standard_normal((m, r)), rng.standard_normal((n, r)), rng.standard_normal((b, n))
+
+
+def test_apply_hand_example():
+    g = _golden("apply_hand_2x3.json")
+    S, U, V, X = (np.array(g[t], dtype=np.float64) for t in ("S", "U", "V", "X"))
+    assert np.array_equal(O.apply_factored(S, U, V, X), np.array(g["Y"]))
+    assert np.array_equal(O.apply_dense(S, U, V, X), np.array(g["Y"]))
+    assert np.array_equal(O.normaliser(S, U, V, X), np.array(g["N"]))
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_apply_factored_equals_dense(seed):
+    _, S, U, V, X = _tiny_problem(seed)
+    N = O.normaliser(S, U, V, X)
+    d = np.abs(O.apply_factored(S, U, V, X) - O.apply_dense(S, U, V, X))
+    assert np.all(d <= 1e-12 * N)
+
+
+def test_apply_rank0_is_scipy_spmv():
+    s, S, U, V, X = _tiny_problem(7)
+    U0, V0 = U[:, :0], V[:, :0]
+    csr = scipy.sparse.csr_matrix((O.widen(s["values"], O.F32), s["col_idx"], s["row_ptr"]), shape=S.shape)
+    ref = np.stack([csr @ x for x in X])
+    assert np.allclose(O.apply_factored(S, U0, V0, X), ref, rtol=1e-14, atol=1e-15)
+
+
+def test_apply_k0_is_pure_low_rank_loops():
+    _, S, U, V, X = _tiny_problem(9)
+    Z = np.zeros_like(S)
+    Y = O.apply_factored(Z, U, V, X)
+    b, n = X.shape
+    m, r = U.shape
+    for c in range(b):
+        for i in range(m):
+            acc = sum(U[i, l] * sum(V[j, l] * X[c, j] for j in range(n)) for l in range(r))
+            assert abs(Y[c, i] - acc) <= 1e-12 * (1 + abs(acc))
+
+
+def test_apply_unit_vector_returns_column():
+    _, S, U, V, _ = _tiny_problem(3)
+    A = S + U @ V.T
+    n = S.shape[1]
+    for j in range(n):
+        e = np.zeros((1, n))
+        e[0, j] = 1.0
+        assert np.allclose(O.apply_factored(S, U, V, e)[0], A[:, j], rtol=1e-14, atol=1e-15)
+
+
+def test_normaliser_loop_definition():
+    _, S, U, V, X = _tiny_problem(2)
+    A = S + U @ V.T
+    N = O.normaliser(S, U, V, X)
+    for c in range(X.shape[0]):
+        for i in range(S.shape[0]):
+            assert abs(N[c, i] - sum(abs(A[i, j] * X[c, j]) for j in range(S.shape[1]))) <= 1e-13
+
+
+def test_apply_rows_matches_full():
+    s, S, U, V, X = _tiny_problem(4, m=9, n=12, r=2, b=3, k=20)
+    rows = np.array([0, 4, 8])
+    Srows = O.csr_rows_dense(rows, 12, s["row_ptr"], s["col_idx"], s["values"], O.F32)
+    Yr, Nr = O.apply_rows(Srows, U[rows], V, X)
+    assert np.allclose(Yr, O.apply_factored(S, U, V, X)[:, rows], rtol=1e-13, atol=1e-15)
+    assert np.allclose(Nr, O.normaliser(S, U, V, X)[:, rows], rtol=1e-13, atol=1e-15)
+
+
+def test_max_normalised_error_rules():
+    N = np.array([[1.0, 0.0]])
+    assert O.max_normalised_error(np.array([[1.5, 0.0]]), np.array([[1.0, 0.0]]), N) == 0.5
+    assert O.max_normalised_error(np.array([[1.0, 1e-30]]), np.array([[1.0, 0.0]]), N) == float("inf")
+
+
+# ---------------------------------------------------------------------------
+# Storage narrowing: RNE against an independent implementation (torch)
+# ---------------------------------------------------------------------------
+
+def test_bf16_narrowing_matches_torch():
+    import torch
+    rng = np.random.default_rng(1)
+    a = np.concatenate([rng.standard_normal(5000) * 10.0 ** rng.integers(-30, 30, 5000),
+                        [0.0, -0.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -9, -1.5,
+                         3.0e38, 1e-40]])
+    mine = O.narrow(a, O.BF16)
+    ref = torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(mine, ref)
+    assert np.array_equal(syn.f32_to_bf16_bits(a.astype(np.float32)), ref)
+    assert np.array_equal(O.widen(mine, O.BF16), torch.from_numpy(ref.view(np.int16)).view(torch.bfloat16).double().numpy())
