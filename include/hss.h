@@ -1,0 +1,181 @@
+/*
+ * hss.h -- C ABI of the sparse + low-rank (HSS) linear layer for AMD MI355X (gfx950).
+ *
+ *   W  ~=  S + U V^T          W: m x n (out features x in features)
+ *   Y   =  X (S + U V^T)^T     X: b x n,  Y: b x m   (row-major)
+ *
+ * Sources (web pages; section names as printed on each page):
+ *   [HSS]    "LLMの階層的スパース+低ランク圧縮" (hierarchical sparse + low-rank
+ *            compression of LLMs), d7fyzohlfz9vz.cloudfront.net/posts/
+ *            hierarchical-sparse-plus-low-rank-compression-of-llm
+ *            section "2段階階層的スパース+低ランク圧縮": the decomposition
+ *            W ~= S + U V^T, U in R^{m x r}, V in R^{n x r}; stage 1 keeps the
+ *            weights of largest absolute magnitude as S (stored as indices +
+ *            values, e.g. CSR), stage 2 factors the dense residual.
+ *            section "実装と運用パターン": the forward product splits into the
+ *            sparse product plus two small dense products.
+ *   [HASSLE] aibr.jp/archives/82335, section "3.中核となる技術的要素": N:M
+ *            (here 2:4) structured sparsity as the GPU-friendly form of S.
+ *
+ * Conventions shared by every call
+ *   - Every pointer is a caller-owned DEVICE pointer unless stated otherwise.
+ *     The library never allocates or frees memory.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = legacy default
+ *     stream) and never synchronise, except hss_get_error.
+ *   - All argument checks run on the host before any device work: a call that
+ *     returns an error has enqueued nothing.
+ *   - Storage types: HSS_F32 = IEEE binary32; HSS_BF16 = bfloat16 (upper 16
+ *     bits of binary32).  Matrices are dense row-major unless stated.
+ *   - Sizes are int32; every array addressed by the library must have fewer
+ *     than 2^31 elements.
+ *   - Calls are thread-safe given distinct workspaces; two calls that share a
+ *     workspace must be ordered (same stream or explicit events).
+ */
+#ifndef HSS_H
+#define HSS_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HSS_VERSION_MAJOR 1
+#define HSS_VERSION_MINOR 0
+
+typedef enum {
+  HSS_OK = 0,
+  HSS_ERR_INVALID_ARG = 1, /* bad size, null pointer, aliasing, unknown enum          */
+  HSS_ERR_UNSUPPORTED = 2, /* valid request this build does not implement            */
+  HSS_ERR_WORKSPACE = 3,   /* workspace pointer null or smaller than *_workspace_size */
+  HSS_ERR_NONFINITE = 4,   /* device-side: a NaN/Inf weight was seen by hss_split     */
+  HSS_ERR_HIP = 5          /* a HIP runtime call or kernel launch failed              */
+} hss_status;
+
+typedef enum { HSS_F32 = 0, HSS_BF16 = 1 } hss_dtype;
+
+typedef enum {
+  HSS_FMT_CSR = 0,  /* unstructured top-k, compressed sparse rows          */
+  HSS_FMT_2OF4 = 1  /* 2 kept of every 4 consecutive columns (N:M = 2:4)   */
+} hss_format;
+
+/* Library version: 100 * major + minor. */
+int hss_version(void);
+
+/* Static text for a status code (never NULL). */
+const char* hss_status_string(hss_status s);
+
+/* Number of weights stage 1 keeps for a kept fraction num/den:
+ *   floor(m * n * num / den), exact integer arithmetic ([HSS] worked example:
+ *   5 % of 1024 x 1024 keeps 52,428).  Returns -1 if m, n, num < 0, den <= 0
+ *   or the product overflows int64. */
+int64_t hss_topk_count(int64_t m, int64_t n, int64_t num, int64_t den);
+
+/* ------------------------------------------------------------------------
+ * Stage 1: hss_split -- magnitude top-k of W into S, plus the residual.
+ * ------------------------------------------------------------------------
+ * [HSS] two-stage section: S holds the k weights of largest |w|; the rest form
+ * the dense residual that stage 2 factors.
+ *
+ * Selection rule (exact, deterministic):
+ *   key(w) = |w| (the bit pattern with the sign cleared; |+0| = |-0|).
+ *   Order entries by key descending, then by row-major linear index i*n+j
+ *   ascending, and keep the first k.  Exactly k entries are kept even when
+ *   many share the threshold magnitude.
+ *
+ * fmt = HSS_FMT_CSR:
+ *   k         in [0, m*n].
+ *   row_ptr   int32[m+1]  out: row_ptr[0] = 0, row_ptr[m] = k.
+ *   col_idx   int32[k]    out: column of each kept entry, ascending within a row.
+ *   values    dt[k]       out: the kept W values, bit-copied.
+ *   nm_values, nm_meta    must be NULL.
+ *   col_idx / values may be NULL only when k == 0.
+ * fmt = HSS_FMT_2OF4  ([HASSLE] N:M structure, groups along the input dim):
+ *   n % 4 == 0 required; k must be m*n/2 or -1.
+ *   In every group of 4 consecutive columns (4g .. 4g+3) of every row, keep the
+ *   2 entries of largest |w|, ties to the lower column.
+ *   nm_values dt[m * n/2]          out: row i, group g: [2g] = kept entry with
+ *                                  the lower column, [2g+1] = the higher one.
+ *   nm_meta   uint32[m * ceil(n/32)] out: row i, word g/8, bits 4*(g%8) .. +3
+ *                                  hold i0 | (i1 << 2), i0 < i1 the kept
+ *                                  positions within the group; unused bits 0.
+ *   row_ptr, col_idx, values must be NULL.
+ * residual  dt[m*n], nullable: out: W with every kept position set to +0 and
+ *           every other position bit-copied (no arithmetic).
+ * W         dt[m*n] in, row-major.  Must not overlap any output.
+ * ws        workspace of at least hss_split_workspace_size() bytes; no
+ *           initial contents required.  After the split, hss_get_error(ws)
+ *           reports HSS_ERR_NONFINITE if W held a NaN or an infinity (the
+ *           outputs are then unspecified).
+ * Returns HSS_ERR_INVALID_ARG for: unknown fmt/dt, m or n <= 0, m*n >= 2^31,
+ *   W null, k out of range, required output null, a forbidden output non-NULL,
+ *   n % 4 != 0 for 2:4, residual aliasing W.  HSS_ERR_WORKSPACE for a null or
+ *   short workspace.  HSS_ERR_HIP if a launch fails.
+ */
+hss_status hss_split_workspace_size(hss_format fmt, hss_dtype dt, int32_t m, int32_t n,
+                                    size_t* bytes);
+hss_status hss_split(hss_format fmt, hss_dtype dt, int32_t m, int32_t n, const void* W, int64_t k,
+                     int32_t* row_ptr, int32_t* col_idx, void* values, void* nm_values,
+                     uint32_t* nm_meta, void* residual, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/* Reads the device error word a split left in `ws`: synchronises `stream`.
+ * Returns HSS_OK, HSS_ERR_NONFINITE, HSS_ERR_INVALID_ARG (ws NULL) or HSS_ERR_HIP. */
+hss_status hss_get_error(const void* ws, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Apply: Y = X S^T + (X V) U^T   ([HSS] implementation-patterns section)
+ * ------------------------------------------------------------------------
+ * The compressed matrix.  All arrays are device memory in `dtype` unless
+ * stated.  r = 0 means no low-rank term (U, Vt ignored).
+ *   fmt == HSS_FMT_CSR:  row_ptr int32[m+1], col_idx int32[nnz] (each row's
+ *     columns in [0, n), any order), values dtype[nnz]; nnz = row_ptr[m].
+ *     The nm_* fields are ignored.
+ *   fmt == HSS_FMT_2OF4: nm_values dtype[m*n/2], nm_meta uint32[m*ceil(n/32)]
+ *     in the layout hss_split writes; CSR fields ignored.
+ *   U  dtype[m*r]  row-major m x r.
+ *   Vt dtype[r*n]  row-major r x n, i.e. the n x r factor V stored
+ *                  column-major, so that V^T x reads contiguous rows.
+ */
+typedef struct hss_matrix {
+  int32_t fmt;   /* hss_format */
+  int32_t dtype; /* hss_dtype  */
+  int32_t m, n, r;
+  int32_t reserved; /* must be 0 */
+  int64_t nnz;      /* CSR: row_ptr[m] (>= 0); 2:4: ignored */
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  const void* values;
+  const void* nm_values;
+  const uint32_t* nm_meta;
+  const void* U;
+  const void* Vt;
+} hss_matrix;
+
+/* Workspace bytes hss_apply needs for this matrix and batch size. */
+hss_status hss_apply_workspace_size(const hss_matrix* A, int32_t b, size_t* bytes);
+
+/* Y (b x m, row-major) = X (b x n, row-major) times (S + U V^T)^T.
+ *   HSS_F32 : X, Y fp32; accumulation fp32.
+ *   HSS_BF16: X bf16; products accumulated in fp32; Y bf16 = round-to-nearest-
+ *             even of the fp32 result.
+ * ws: at least hss_apply_workspace_size() bytes.  Its first 256 bytes are
+ *     control words: they must be zero before the first call that uses the
+ *     workspace, and every call leaves them zero again, so zero-filling a new
+ *     workspace once suffices.  The rest is scratch with no required contents.
+ * Returns HSS_ERR_INVALID_ARG for: A or X or Y null, unknown fmt/dtype,
+ *   reserved != 0, m, n <= 0, r < 0, b < 1, b*m, b*n, m*n, r*(m+n) >= 2^31,
+ *   nnz < 0, required arrays null, n % 4 != 0 for 2:4, X overlapping Y.
+ *   HSS_ERR_WORKSPACE for a null or short workspace.  HSS_ERR_HIP if a launch
+ *   fails.
+ */
+hss_status hss_apply(const hss_matrix* A, int32_t b, const void* X, void* Y, void* ws,
+                     size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HSS_H */

@@ -1,0 +1,202 @@
+"""Sparse + low-rank (HSS) linear layer on AMD MI355X.
+
+Thin Python binding of libhss.so (C ABI in include/hss.h).  The functions keep
+the C names; they only marshal torch tensors (device memory) and the current
+HIP stream into the C calls -- every step runs in the library's HIP kernels.
+
+    W ~= S + U V^T,   Y = X (S + U V^T)^T
+
+    sp = hss_split(W, "csr", frac=(5, 100), residual=True)   # stage 1 on the GPU
+    A  = HSSMatrix.from_split(sp, U, V=V)                     # U: m x r, V: n x r
+    Y  = hss_apply(A, X)                                      # X: b x n -> Y: b x m
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass, field
+from typing import Optional
+
+import torch
+
+from ._lib import (HSS_BF16, HSS_ERR_NONFINITE, HSS_F32, HSS_FMT_2OF4, HSS_FMT_CSR, HSS_OK,
+                   HSSError, HssMatrixStruct, LIB_PATH, check, lib, status_string)
+
+__all__ = [
+    "hss_version", "hss_topk_count", "hss_split_workspace_size", "hss_split", "hss_get_error",
+    "hss_apply_workspace_size", "hss_apply", "HSSMatrix", "SplitResult", "HSSError",
+    "LIB_PATH", "status_string",
+]
+
+_DT = {torch.float32: HSS_F32, torch.bfloat16: HSS_BF16}
+_FMT = {"csr": HSS_FMT_CSR, "2:4": HSS_FMT_2OF4, HSS_FMT_CSR: HSS_FMT_CSR, HSS_FMT_2OF4: HSS_FMT_2OF4}
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}: float32 or bfloat16")
+    return _DT[t.dtype]
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dev(t: torch.Tensor):
+    if not t.is_cuda:
+        raise ValueError("tensor must be on a GPU device")
+    return t.device
+
+
+def hss_version() -> int:
+    return lib.hss_version()
+
+
+def hss_topk_count(m: int, n: int, num: int, den: int) -> int:
+    """floor(m*n*num/den) computed exactly by the library."""
+    k = lib.hss_topk_count(m, n, num, den)
+    if k < 0:
+        raise ValueError("invalid count arguments")
+    return int(k)
+
+
+def hss_split_workspace_size(fmt, dtype: int, m: int, n: int) -> int:
+    out = ctypes.c_size_t(0)
+    check(lib.hss_split_workspace_size(_FMT[fmt], dtype, m, n, ctypes.byref(out)), "hss_split_workspace_size")
+    return int(out.value)
+
+
+@dataclass
+class SplitResult:
+    fmt: int
+    m: int
+    n: int
+    k: int
+    row_ptr: Optional[torch.Tensor] = None    # int32 [m+1]
+    col_idx: Optional[torch.Tensor] = None    # int32 [k]
+    values: Optional[torch.Tensor] = None     # W dtype [k]
+    nm_values: Optional[torch.Tensor] = None  # W dtype [m, n/2]
+    nm_meta: Optional[torch.Tensor] = None    # int32 storage of uint32 [m, ceil(n/32)]
+    residual: Optional[torch.Tensor] = None   # W dtype [m, n]
+    ws: Optional[torch.Tensor] = field(default=None, repr=False)
+
+
+def hss_split(W: torch.Tensor, fmt="csr", k: Optional[int] = None, frac=(5, 100),
+              residual: bool = False, check_finite: bool = True) -> SplitResult:
+    """Stage 1 on the GPU: magnitude top-k of W (m x n) into CSR or 2:4.
+
+    fmt "csr": k defaults to floor(m*n*frac[0]/frac[1]).  fmt "2:4": k is m*n/2.
+    check_finite synchronises and raises HSSError(HSS_ERR_NONFINITE) on NaN/Inf."""
+    dev = _dev(W)
+    if W.dim() != 2 or not W.is_contiguous():
+        raise ValueError("W must be a contiguous 2-D tensor")
+    dt = _dt(W)
+    m, n = W.shape
+    f = _FMT[fmt]
+    ws_bytes = hss_split_workspace_size(f, dt, m, n)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    res = torch.empty_like(W) if residual else None
+    out = SplitResult(fmt=f, m=m, n=n, k=0, residual=res, ws=ws)
+    if f == HSS_FMT_CSR:
+        if k is None:
+            k = hss_topk_count(m, n, *frac)
+        out.k = int(k)
+        out.row_ptr = torch.empty(m + 1, dtype=torch.int32, device=dev)
+        out.col_idx = torch.empty(max(out.k, 0), dtype=torch.int32, device=dev)
+        out.values = torch.empty(max(out.k, 0), dtype=W.dtype, device=dev)
+        code = lib.hss_split(f, dt, m, n, _ptr(W), out.k, _ptr(out.row_ptr),
+                             _ptr(out.col_idx) if out.k > 0 else None,
+                             _ptr(out.values) if out.k > 0 else None, None, None, _ptr(res),
+                             _ptr(ws), ws_bytes, _stream(dev))
+    else:
+        out.k = (m * n) // 2 if k is None else int(k)
+        out.nm_values = torch.empty((m, n // 2), dtype=W.dtype, device=dev)
+        out.nm_meta = torch.empty((m, (n + 31) // 32), dtype=torch.int32, device=dev)
+        code = lib.hss_split(f, dt, m, n, _ptr(W), out.k, None, None, None, _ptr(out.nm_values),
+                             _ptr(out.nm_meta), _ptr(res), _ptr(ws), ws_bytes, _stream(dev))
+    check(code, "hss_split")
+    if check_finite:
+        check(hss_get_error(ws), "hss_split")
+    return out
+
+
+def hss_get_error(ws: torch.Tensor) -> int:
+    """Synchronises the current stream and returns the split's device status code."""
+    return int(lib.hss_get_error(_ptr(ws), _stream(ws.device)))
+
+
+class HSSMatrix:
+    """Compressed matrix S + U V^T in device memory; keeps its tensors alive.
+
+    U: m x r row-major.  The factor V (n x r) is held as Vt (r x n row-major,
+    i.e. V column-major), the layout the library reads."""
+
+    def __init__(self, fmt, m, n, dtype, U=None, Vt=None, row_ptr=None, col_idx=None, values=None,
+                 nnz=None, nm_values=None, nm_meta=None):
+        self.fmt = _FMT[fmt]
+        self.m, self.n = int(m), int(n)
+        self.dtype = dtype
+        self.U, self.Vt = U, Vt
+        self.r = 0 if U is None else int(U.shape[1])
+        if self.r > 0:
+            assert U.shape == (self.m, self.r) and Vt.shape == (self.r, self.n)
+            assert U.dtype == dtype and Vt.dtype == dtype and U.is_contiguous() and Vt.is_contiguous()
+        self.row_ptr, self.col_idx, self.values = row_ptr, col_idx, values
+        self.nm_values, self.nm_meta = nm_values, nm_meta
+        self.nnz = int(nnz if nnz is not None else (values.numel() if values is not None else 0))
+        self._ws = {}
+        s = HssMatrixStruct()
+        s.fmt, s.dtype = self.fmt, _DT[dtype]
+        s.m, s.n, s.r, s.reserved = self.m, self.n, self.r, 0
+        s.nnz = self.nnz
+        s.row_ptr, s.col_idx, s.values = _ptr(row_ptr), _ptr(col_idx), _ptr(values)
+        s.nm_values, s.nm_meta = _ptr(nm_values), _ptr(nm_meta)
+        s.U, s.Vt = (_ptr(U), _ptr(Vt)) if self.r > 0 else (None, None)
+        self.struct = s
+
+    @classmethod
+    def from_split(cls, sp: SplitResult, U=None, V=None, Vt=None, dtype=None):
+        if V is not None:
+            Vt = V.t().contiguous()
+        if dtype is None:
+            dtype = (sp.values if sp.values is not None else sp.nm_values).dtype
+        if sp.fmt == HSS_FMT_CSR:
+            return cls("csr", sp.m, sp.n, dtype, U=U, Vt=Vt, row_ptr=sp.row_ptr,
+                       col_idx=sp.col_idx, values=sp.values, nnz=sp.k)
+        return cls("2:4", sp.m, sp.n, dtype, U=U, Vt=Vt, nm_values=sp.nm_values, nm_meta=sp.nm_meta)
+
+    def workspace(self, b: int, device=None) -> torch.Tensor:
+        """Zero-filled workspace for batch b (cached per device and size)."""
+        size = hss_apply_workspace_size(self, b)
+        dev = device or (self.U.device if self.U is not None else
+                         (self.values.device if self.values is not None else self.nm_values.device))
+        key = (str(dev), size)
+        if key not in self._ws:
+            self._ws[key] = torch.zeros(max(size, 1), dtype=torch.uint8, device=dev)
+        return self._ws[key]
+
+
+def hss_apply_workspace_size(A: HSSMatrix, b: int) -> int:
+    out = ctypes.c_size_t(0)
+    check(lib.hss_apply_workspace_size(ctypes.byref(A.struct), int(b), ctypes.byref(out)),
+          "hss_apply_workspace_size")
+    return int(out.value)
+
+
+def hss_apply(A: HSSMatrix, X: torch.Tensor, Y: Optional[torch.Tensor] = None,
+              ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y (b x m) = X (b x n) (S + U V^T)^T on the current stream."""
+    dev = _dev(X)
+    if X.dim() != 2 or X.shape[1] != A.n or not X.is_contiguous() or X.dtype != A.dtype:
+        raise ValueError("X must be a contiguous b x n tensor of the matrix dtype")
+    b = X.shape[0]
+    if Y is None:
+        Y = torch.empty((b, A.m), dtype=A.dtype, device=dev)
+    if ws is None:
+        ws = A.workspace(b, dev)
+    check(lib.hss_apply(ctypes.byref(A.struct), b, _ptr(X), _ptr(Y), _ptr(ws), ws.numel(),
+                        _stream(dev)), "hss_apply")
+    return Y

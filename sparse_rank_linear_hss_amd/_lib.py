@@ -1,0 +1,80 @@
+"""Loads libhss.so (built in-tree by sparse_rank_linear_hss_amd/build.py) and
+declares its C signatures.  There is no fallback: if the library is missing
+or does not load, importing the package fails with the reason."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhss.so")
+
+HSS_OK = 0
+HSS_ERR_INVALID_ARG = 1
+HSS_ERR_UNSUPPORTED = 2
+HSS_ERR_WORKSPACE = 3
+HSS_ERR_NONFINITE = 4
+HSS_ERR_HIP = 5
+
+HSS_F32 = 0
+HSS_BF16 = 1
+HSS_FMT_CSR = 0
+HSS_FMT_2OF4 = 1
+
+c_int32, c_int64, c_size_t, c_void_p = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+
+
+class HssMatrixStruct(ctypes.Structure):
+    """Mirror of struct hss_matrix in include/hss.h."""
+    _fields_ = [
+        ("fmt", c_int32), ("dtype", c_int32),
+        ("m", c_int32), ("n", c_int32), ("r", c_int32), ("reserved", c_int32),
+        ("nnz", c_int64),
+        ("row_ptr", c_void_p), ("col_idx", c_void_p), ("values", c_void_p),
+        ("nm_values", c_void_p), ("nm_meta", c_void_p),
+        ("U", c_void_p), ("Vt", c_void_p),
+    ]
+
+
+class HSSError(RuntimeError):
+    def __init__(self, code, where=""):
+        self.code = code
+        super().__init__(f"{where}: {status_string(code)} (code {code})")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m sparse_rank_linear_hss_amd.build` "
+            "(hipcc, gfx950). There is no non-HIP fallback.")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    sig = {
+        "hss_version": (ctypes.c_int, []),
+        "hss_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "hss_topk_count": (c_int64, [c_int64, c_int64, c_int64, c_int64]),
+        "hss_split_workspace_size": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, c_int32, c_int32, P(c_size_t)]),
+        "hss_split": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, c_int32, c_int32, c_void_p, c_int64,
+                                     c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                     c_void_p, c_size_t, c_void_p]),
+        "hss_get_error": (ctypes.c_int, [c_void_p, c_void_p]),
+        "hss_apply_workspace_size": (ctypes.c_int, [P(HssMatrixStruct), c_int32, P(c_size_t)]),
+        "hss_apply": (ctypes.c_int, [P(HssMatrixStruct), c_int32, c_void_p, c_void_p, c_void_p,
+                                     c_size_t, c_void_p]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def status_string(code: int) -> str:
+    return lib.hss_status_string(int(code)).decode()
+
+
+def check(code: int, where: str = "hss"):
+    if code != HSS_OK:
+        raise HSSError(code, where)

@@ -1,0 +1,126 @@
+// Host entry points of libhss: argument checks, workspace sizing, dispatch.
+// Every check runs before any HIP call, so an error return has enqueued nothing.
+#include <limits.h>
+
+#include "hss_internal.h"
+
+namespace {
+
+constexpr int64_t kLimit = (int64_t)1 << 31;  // arrays must have fewer elements
+
+bool valid_dtype(int dt) { return dt == HSS_F32 || dt == HSS_BF16; }
+bool valid_fmt(int f) { return f == HSS_FMT_CSR || f == HSS_FMT_2OF4; }
+size_t dsize(int dt) { return dt == HSS_F32 ? 4 : 2; }
+
+bool overlap(const void* a, size_t abytes, const void* b, size_t bbytes) {
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + bbytes && b0 < a0 + abytes;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hss_version(void) { return 100 * HSS_VERSION_MAJOR + HSS_VERSION_MINOR; }
+
+const char* hss_status_string(hss_status s) {
+  switch (s) {
+    case HSS_OK: return "HSS_OK";
+    case HSS_ERR_INVALID_ARG: return "HSS_ERR_INVALID_ARG: invalid argument";
+    case HSS_ERR_UNSUPPORTED: return "HSS_ERR_UNSUPPORTED: not implemented for these arguments";
+    case HSS_ERR_WORKSPACE: return "HSS_ERR_WORKSPACE: workspace missing or too small";
+    case HSS_ERR_NONFINITE: return "HSS_ERR_NONFINITE: non-finite weight seen by hss_split";
+    case HSS_ERR_HIP: return "HSS_ERR_HIP: HIP runtime error";
+  }
+  return "HSS: unknown status";
+}
+
+int64_t hss_topk_count(int64_t m, int64_t n, int64_t num, int64_t den) {
+  if (m < 0 || n < 0 || num < 0 || den <= 0) return -1;
+  __int128 p = (__int128)m * n * num;
+  __int128 q = p / den;
+  if (q > (__int128)INT64_MAX) return -1;
+  return (int64_t)q;
+}
+
+hss_status hss_split_workspace_size(hss_format fmt, hss_dtype dt, int32_t m, int32_t n,
+                                    size_t* bytes) {
+  if (!bytes || !valid_fmt(fmt) || !valid_dtype(dt) || m <= 0 || n <= 0 ||
+      (int64_t)m * n >= kLimit)
+    return HSS_ERR_INVALID_ARG;
+  *bytes = hss::split_ws_bytes(fmt, m);
+  return HSS_OK;
+}
+
+hss_status hss_split(hss_format fmt, hss_dtype dt, int32_t m, int32_t n, const void* W, int64_t k,
+                     int32_t* row_ptr, int32_t* col_idx, void* values, void* nm_values,
+                     uint32_t* nm_meta, void* residual, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  if (!valid_fmt(fmt) || !valid_dtype(dt) || m <= 0 || n <= 0) return HSS_ERR_INVALID_ARG;
+  const int64_t mn = (int64_t)m * n;
+  if (mn >= kLimit || W == nullptr) return HSS_ERR_INVALID_ARG;
+  const size_t wbytes = (size_t)mn * dsize(dt);
+  if (residual && overlap(W, wbytes, residual, wbytes)) return HSS_ERR_INVALID_ARG;
+  if (fmt == HSS_FMT_CSR) {
+    if (k < 0 || k > mn) return HSS_ERR_INVALID_ARG;
+    if (!row_ptr || (k > 0 && (!col_idx || !values))) return HSS_ERR_INVALID_ARG;
+    if (nm_values || nm_meta) return HSS_ERR_INVALID_ARG;
+  } else {
+    if (n % 4 != 0) return HSS_ERR_INVALID_ARG;
+    if (k != -1 && k != mn / 2) return HSS_ERR_INVALID_ARG;
+    if (!nm_values || !nm_meta) return HSS_ERR_INVALID_ARG;
+    if (row_ptr || col_idx || values) return HSS_ERR_INVALID_ARG;
+  }
+  const size_t need = hss::split_ws_bytes(fmt, m);
+  if (!ws || ws_bytes < need) return HSS_ERR_WORKSPACE;
+  if (fmt == HSS_FMT_CSR)
+    return hss::launch_split_csr(dt, m, n, W, k, row_ptr, col_idx, values, residual, ws, stream);
+  return hss::launch_split_24(dt, m, n, W, nm_values, nm_meta, residual, ws, stream);
+}
+
+hss_status hss_get_error(const void* ws, hipStream_t stream) {
+  if (!ws) return HSS_ERR_INVALID_ARG;
+  if (hipStreamSynchronize(stream) != hipSuccess) return HSS_ERR_HIP;
+  uint32_t err = 0;
+  if (hipMemcpy(&err, ws, sizeof(err), hipMemcpyDeviceToHost) != hipSuccess) return HSS_ERR_HIP;
+  return err ? HSS_ERR_NONFINITE : HSS_OK;
+}
+
+static hss_status check_matrix(const hss_matrix* A, int32_t b) {
+  if (!A || !valid_fmt(A->fmt) || !valid_dtype(A->dtype) || A->reserved != 0)
+    return HSS_ERR_INVALID_ARG;
+  const int64_t m = A->m, n = A->n, r = A->r;
+  if (m <= 0 || n <= 0 || r < 0 || b < 1) return HSS_ERR_INVALID_ARG;
+  if (m * n >= kLimit || (int64_t)b * m >= kLimit || (int64_t)b * n >= kLimit ||
+      r * (m + n) >= kLimit)
+    return HSS_ERR_INVALID_ARG;
+  if (r > 0 && (!A->U || !A->Vt)) return HSS_ERR_INVALID_ARG;
+  if (A->fmt == HSS_FMT_CSR) {
+    if (A->nnz < 0 || A->nnz > m * n || !A->row_ptr) return HSS_ERR_INVALID_ARG;
+    if (A->nnz > 0 && (!A->col_idx || !A->values)) return HSS_ERR_INVALID_ARG;
+  } else {
+    if (n % 4 != 0 || !A->nm_values || !A->nm_meta) return HSS_ERR_INVALID_ARG;
+  }
+  return HSS_OK;
+}
+
+hss_status hss_apply_workspace_size(const hss_matrix* A, int32_t b, size_t* bytes) {
+  if (!bytes) return HSS_ERR_INVALID_ARG;
+  hss_status st = check_matrix(A, b);
+  if (st != HSS_OK) return st;
+  *bytes = hss::apply_ws_bytes(A, b);
+  return HSS_OK;
+}
+
+hss_status hss_apply(const hss_matrix* A, int32_t b, const void* X, void* Y, void* ws,
+                     size_t ws_bytes, hipStream_t stream) {
+  hss_status st = check_matrix(A, b);
+  if (st != HSS_OK) return st;
+  if (!X || !Y) return HSS_ERR_INVALID_ARG;
+  const size_t es = dsize(A->dtype);
+  if (overlap(X, (size_t)b * A->n * es, Y, (size_t)b * A->m * es)) return HSS_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < hss::apply_ws_bytes(A, b)) return HSS_ERR_WORKSPACE;
+  return hss::launch_apply(A, b, X, Y, ws, stream);
+}
+
+}  // extern "C"

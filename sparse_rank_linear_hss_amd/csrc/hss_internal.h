@@ -1,0 +1,100 @@
+// Internal helpers shared by the HSS kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hss.h"
+
+#define HSS_WAVE 64
+
+namespace hss {
+
+// Native 16-byte vector (usable with the nontemporal load/store builtins).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Storage types.  Weights/activations travel as raw bits: uint32_t for fp32,
+// uint16_t for bf16.  Arithmetic is always fp32.
+// ---------------------------------------------------------------------------
+template <int DT> struct Elem;
+template <> struct Elem<HSS_F32> {
+  using bits_t = uint32_t;
+  static constexpr uint32_t key_mask = 0x7fffffffu;  // |w| as an unsigned order
+  static constexpr uint32_t key_inf = 0x7f800000u;   // keys >= this: Inf / NaN
+  static constexpr int key_bits = 31;
+  __device__ __forceinline__ static float to_f(uint32_t b) { return __uint_as_float(b); }
+};
+template <> struct Elem<HSS_BF16> {
+  using bits_t = uint16_t;
+  static constexpr uint32_t key_mask = 0x7fffu;
+  static constexpr uint32_t key_inf = 0x7f80u;
+  static constexpr int key_bits = 15;
+  __device__ __forceinline__ static float to_f(uint32_t b) { return __uint_as_float(b << 16); }
+};
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ---------------------------------------------------------------------------
+// Wave-level helpers (64 lanes).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, HSS_WAVE);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, HSS_WAVE);
+  return v;
+}
+
+// Exclusive prefix sum across the wave's lanes.
+__device__ __forceinline__ uint32_t wave_excl_scan_u32(uint32_t v) {
+  const int lane = lane_id();
+  uint32_t incl = v;
+#pragma unroll
+  for (int off = 1; off < HSS_WAVE; off <<= 1) {
+    uint32_t t = __shfl_up(incl, off, HSS_WAVE);
+    if (lane >= off) incl += t;
+  }
+  return incl - v;
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int lane = lane_id();
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+template <typename T>
+__device__ __forceinline__ T uniform(T v) {
+  return (T)__builtin_amdgcn_readfirstlane((int)v);
+}
+
+}  // namespace hss
+
+// Host-side launchers (defined in the .hip files).
+namespace hss {
+hss_status launch_split_csr(int dt, int m, int n, const void* W, int64_t k, int32_t* row_ptr,
+                            int32_t* col_idx, void* values, void* residual, void* ws,
+                            hipStream_t stream);
+hss_status launch_split_24(int dt, int m, int n, const void* W, void* nm_values, uint32_t* nm_meta,
+                           void* residual, void* ws, hipStream_t stream);
+size_t split_ws_bytes(int fmt, int m);
+
+size_t apply_ws_bytes(const hss_matrix* A, int b);
+hss_status launch_apply(const hss_matrix* A, int b, const void* X, void* Y, void* ws,
+                        hipStream_t stream);
+}  // namespace hss

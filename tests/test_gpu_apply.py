@@ -1,0 +1,171 @@
+"""GPU parity of hss_apply against the CPU oracle.
+
+Bar: every output within tol * N[c, i], N = sum_j |A_ij X_cj| (A = S + U V^T
+built in fp64 from the stored operands); tol = 1e-5 for fp32, 8e-3 for bf16
+inputs with fp32 accumulation and bf16 output.  The sparse part S always comes
+from the oracle's own split of the seeded W (never from the GPU split)."""
+import numpy as np
+import pytest
+
+import hss_synth as syn
+import oracle as O
+from _cases import dt_of, oracle_split, to_dev, to_host, weight
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def H():
+    import sparse_rank_linear_hss_amd as h
+    return h
+
+
+def _tdt(dtype):
+    import torch
+    return torch.float32 if dtype == O.F32 else torch.bfloat16
+
+
+def _raw(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _matrix(H, fmt, dtype, m, n, ref, U, V):
+    """Device HSSMatrix from the oracle's split arrays and storage-typed U, V."""
+    Ud = to_dev(U, dtype) if U.shape[1] > 0 else None
+    Vtd = to_dev(np.ascontiguousarray(V.T), dtype) if V.shape[1] > 0 else None
+    if fmt == "csr":
+        k = len(ref["col_idx"])
+        return H.HSSMatrix("csr", m, n, _tdt(dtype), U=Ud, Vt=Vtd, row_ptr=_raw(ref["row_ptr"]),
+                           col_idx=_raw(ref["col_idx"]) if k else None,
+                           values=to_dev(ref["values"], dtype) if k else None, nnz=k)
+    return H.HSSMatrix("2:4", m, n, _tdt(dtype), U=Ud, Vt=Vtd, nm_values=to_dev(ref["nm_values"], dtype),
+                       nm_meta=_raw(ref["nm_meta"].view(np.int32)))
+
+
+def _dense_S(fmt, dtype, m, n, ref):
+    if fmt == "csr":
+        return O.dense_from_csr(m, n, ref["row_ptr"], ref["col_idx"], ref["values"], dtype)
+    return O.dense_from_24(m, n, ref["nm_values"], ref["nm_meta"], dtype)
+
+
+def _factors(m, n, r, dtype, seed):
+    if r == 0:
+        st = np.float32 if dtype == O.F32 else np.uint16
+        return np.zeros((m, 0), st), np.zeros((n, 0), st)
+    return syn.factors(m, n, r, dtype, seed)
+
+
+def _check(Y_dev, dtype, Yref, N):
+    err = O.max_normalised_error(O.widen(to_host(Y_dev), dtype), Yref, N)
+    assert err <= O.TOL[dtype], f"max normalised error {err:.3e} > {O.TOL[dtype]}"
+    return err
+
+
+SMALL = [
+    # (fmt, m, n, r, b)
+    ("csr", 1, 1, 0, 1), ("csr", 5, 13, 2, 3), ("csr", 64, 64, 8, 1), ("csr", 65, 129, 7, 16),
+    ("csr", 130, 1000, 64, 17), ("csr", 1000, 37, 5, 2), ("csr", 96, 4100, 33, 8),
+    ("csr", 257, 512, 1, 33), ("csr", 300, 640, 128, 64),
+    ("2:4", 1, 4, 0, 1), ("2:4", 5, 36, 3, 2), ("2:4", 64, 4096, 16, 1), ("2:4", 65, 128, 7, 9),
+    ("2:4", 33, 100, 5, 16), ("2:4", 128, 512, 64, 64),
+]
+
+
+@pytest.mark.parametrize("dtype", [O.F32, O.BF16])
+@pytest.mark.parametrize("case", SMALL, ids=[f"{c[0]}-{c[1]}x{c[2]}-r{c[3]}-b{c[4]}" for c in SMALL])
+def test_apply_small(H, dtype, case):
+    fmt, m, n, r, b = case
+    seed = m * 7 + n * 3 + r + b
+    W = syn.random_matrix(m, n, dtype, seed=seed, kind="t3")
+    ref = O.split_csr(W, dtype, O.topk_count(m, n, 5, 100)) if fmt == "csr" else O.split_24(W, dtype)
+    U, V = _factors(m, n, r, dtype, seed)
+    X = syn.random_matrix(b, n, dtype, seed=seed + 1, kind="normal", scale=1.0)
+    S64 = _dense_S(fmt, dtype, m, n, ref)
+    U64, V64, X64 = O.widen(U, dtype), O.widen(V, dtype), O.widen(X, dtype)
+    Yref, N = O.apply_factored(S64, U64, V64, X64), O.normaliser(S64, U64, V64, X64)
+    A = _matrix(H, fmt, dtype, m, n, ref, U, V)
+    Xd = to_dev(X, dtype)
+    Y1 = H.hss_apply(A, Xd)
+    _check(Y1, dtype, Yref, N)
+    Y2 = H.hss_apply(A, Xd)
+    assert O.bits_equal(to_host(Y1), to_host(Y2))                  # deterministic
+    ws = A.workspace(b)
+    assert int(ws[:256].abs().sum().item()) == 0                   # control words left at zero
+
+
+@pytest.mark.parametrize("dtype", [O.F32, O.BF16])
+def test_apply_empty_sparse_part(H, dtype):
+    m, n, r, b = 70, 96, 6, 5
+    W = syn.random_matrix(m, n, dtype, seed=3, kind="t3")
+    ref = O.split_csr(W, dtype, 0)
+    U, V = _factors(m, n, r, dtype, 5)
+    X = syn.random_matrix(b, n, dtype, seed=4, kind="normal", scale=1.0)
+    S64 = np.zeros((m, n))
+    U64, V64, X64 = O.widen(U, dtype), O.widen(V, dtype), O.widen(X, dtype)
+    Y = H.hss_apply(_matrix(H, "csr", dtype, m, n, ref, U, V), to_dev(X, dtype))
+    _check(Y, dtype, O.apply_factored(S64, U64, V64, X64), O.normaliser(S64, U64, V64, X64))
+
+
+def test_apply_config1_true_svd(H):
+    """1024 x 1024 fp32 workload end to end on the oracle's side: top 5 %, +0
+    residual, rank-64 truncated SVD, factors cast to fp32; GPU apply at b=1."""
+    c = syn.CONFIGS[1]
+    W = weight(1)
+    ref = oracle_split(1)
+    U64, V64, _ = O.truncated_svd(O.widen(ref["residual"], O.F32), c.rank[0])
+    U, V = O.narrow(U64, O.F32), O.narrow(V64, O.F32)
+    X = syn.activations(c, 1)
+    S64 = _dense_S("csr", O.F32, 1024, 1024, ref)
+    Uw, Vw, Xw = O.widen(U, O.F32), O.widen(V, O.F32), O.widen(X, O.F32)
+    Yref, N = O.apply_factored(S64, Uw, Vw, Xw), O.normaliser(S64, Uw, Vw, Xw)
+    Y = H.hss_apply(_matrix(H, "csr", O.F32, 1024, 1024, ref, U, V), to_dev(X, O.F32))
+    _check(Y, O.F32, Yref, N)
+
+
+def _sampled_check(H, cfg, which, b, rows, step=0):
+    c = syn.CONFIGS[cfg]
+    dtype = dt_of(c.dtype)
+    m, n = c.shapes[which]
+    r = c.rank[which]
+    ref = oracle_split(cfg, which)
+    U, V = syn.factors(m, n, r, dtype, c.seed, which)
+    X = syn.activations(c, b, which, step)
+    A = _matrix(H, "csr" if c.fmt == "csr" else "2:4", dtype, m, n, ref, U, V)
+    Y = to_host(H.hss_apply(A, to_dev(X, dtype)))
+    if rows is None:
+        rows = np.arange(m)
+    if c.fmt == "csr":
+        S_rows = O.csr_rows_dense(rows, n, ref["row_ptr"], ref["col_idx"], ref["values"], dtype)
+    else:
+        S_rows = O.dense_from_24(len(rows), n, ref["nm_values"][rows], ref["nm_meta"][rows], dtype)
+    Yref, N = O.apply_rows(S_rows, O.widen(U, dtype)[rows], O.widen(V, dtype), O.widen(X, dtype))
+    err = O.max_normalised_error(O.widen(Y[:, rows], dtype), Yref, N)
+    assert err <= O.TOL[dtype], f"max normalised error {err:.3e}"
+
+
+@pytest.mark.parametrize("b", [1, 16])
+def test_apply_config2_full(H, b):
+    _sampled_check(H, 2, 0, b, None)
+
+
+@pytest.mark.parametrize("b", [1, 8, 64])
+def test_apply_config3_sampled(H, b):
+    rows = np.random.default_rng(b).choice(11008, size=512, replace=False)
+    rows.sort()
+    _sampled_check(H, 3, 0, b, rows)
+
+
+@pytest.mark.parametrize("which", [0, 4, 6])
+def test_apply_config4_sampled(H, which):
+    m = syn.CONFIGS[4].shapes[which][0]
+    rows = np.random.default_rng(which).choice(m, size=384, replace=False)
+    rows.sort()
+    for step in range(2):
+        _sampled_check(H, 4, which, 1, rows, step)
+
+
+def test_apply_config5_sampled(H):
+    rows = np.random.default_rng(5).choice(8192, size=96, replace=False)
+    rows.sort()
+    _sampled_check(H, 5, 0, 2048, rows)
