@@ -161,10 +161,11 @@ hss_status hss_apply_workspace_size(const hss_matrix* A, int32_t b, size_t* byte
  *   HSS_F32 : X, Y fp32; accumulation fp32.
  *   HSS_BF16: X bf16; products accumulated in fp32; Y bf16 = round-to-nearest-
  *             even of the fp32 result.
- * ws: at least hss_apply_workspace_size() bytes.  Its first 256 bytes are
- *     control words: they must be zero before the first call that uses the
- *     workspace, and every call leaves them zero again, so zero-filling a new
- *     workspace once suffices.  The rest is scratch with no required contents.
+ * ws: at least hss_apply_workspace_size() bytes, ZERO-FILLED once before its
+ *     first use.  The library keeps state in it between calls (a call
+ *     counter), so the caller must not write to it afterwards; any number of
+ *     calls, with any matrices and batch sizes, may then share it as long as
+ *     they are ordered (same stream or events).
  * Returns HSS_ERR_INVALID_ARG for: A or X or Y null, unknown fmt/dtype,
  *   reserved != 0, m, n <= 0, r < 0, b < 1, b*m, b*n, m*n, r*(m+n) >= 2^31,
  *   nnz < 0, required arrays null, n % 4 != 0 for 2:4, X overlapping Y.

@@ -171,8 +171,10 @@ class HSSMatrix:
     def workspace(self, b: int, device=None) -> torch.Tensor:
         """Zero-filled workspace for batch b (cached per device and size)."""
         size = hss_apply_workspace_size(self, b)
-        dev = device or (self.U.device if self.U is not None else
-                         (self.values.device if self.values is not None else self.nm_values.device))
+        if device is None:
+            held = [t for t in (self.U, self.row_ptr, self.values, self.nm_values) if t is not None]
+            device = held[0].device
+        dev = device
         key = (str(dev), size)
         if key not in self._ws:
             self._ws[key] = torch.zeros(max(size, 1), dtype=torch.uint8, device=dev)

@@ -1,0 +1,790 @@
+// Fused small-batch apply (bc <= 8 columns per launch): one kernel computes
+//   Y[c][i] = sum_{j in S_i} S_ij X[c][j] + sum_l U[i][l] T[c][l],
+//   T[c][l] = sum_j Vt[l][j] X[c][j].
+//
+// [HSS] page "LLMの階層的スパース+低ランク圧縮", section "実装と運用パターン": the
+// compressed forward pass is one sparse product plus two small dense products.
+// At decode batch sizes every byte of S, U and V^T is read once and the step
+// is bound by HBM bandwidth (SqueezeLLM explainer page aibr.jp/archives/208940,
+// section "1.概要と位置づけ": single-batch inference is memory-bandwidth bound),
+// so one launch keeps all three streams in flight instead of serialising T
+// before the row pass.
+//
+// Latency, not bandwidth, limits a decode call of a few MB, so the kernel is
+// written around dependent round trips to memory:
+//   * every load that does not depend on another is issued at kernel start,
+//     from a clamped (always valid) address with the value masked afterwards
+//     -- a load under a lane-divergent `if` makes the compiler wait for it at
+//     the join, which would serialise the prefetches;
+//   * the only chains are row_ptr -> (col_idx, values) for CSR rows and
+//     (Vt, X) -> T -> readers for the low-rank term.
+//
+// Cross-block hand-off of T (a launch costs ~2.5 us and a same-address device
+// atomic ~10 ns once every block hits it, so no hot counters and no
+// cache-wide acquire fences):
+//   * T row l is produced by "home" block l mod G at the start of the launch
+//     and published as 64-bit words (fp32 value, call tag) with coherent
+//     (agent-scope) stores -- there is no done counter;
+//   * every block reads the tagged words with coherent loads after its own
+//     sparse work, polls a stale word a bounded number of times, then computes
+//     any row still missing itself (same arithmetic, so the same bits).  No
+//     wait can hang and a stale value is never used;
+//   * the call tag is epoch+1, the epoch being read by every block at its
+//     start.  Each block then bumps one of 64 spread arrival counters; the
+//     last block to arrive (two-level count) advances the epoch and clears the
+//     counters.  All blocks have read the epoch before it can advance.
+#include <stdlib.h>
+
+#include "hss_internal.h"
+
+namespace hss {
+
+// Control region (uint32 words) at the start of the apply workspace.  Each
+// counter sits on its own 128-byte line.
+static constexpr int kCtlEpoch = 0;
+static constexpr int kCtlTop = 32;
+static constexpr int kCtlSub0 = 64;
+static constexpr int kCtlSubStride = 32;
+static constexpr int kNumSub = 64;
+static constexpr size_t kCtlBytes = 16384;
+// Copies of the tagged T words; block b reads copy b % kTReplicas, so each
+// line is polled by 1/kTReplicas of the blocks.
+static constexpr int kTReplicas = 8;
+
+struct DecodeArgs {
+  int m, n, r, bc;
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  const void* vals;
+  const void* nmv;
+  const uint32_t* meta;
+  const void* U;
+  const void* Vt;
+  const void* X;
+  void* Y;
+  uint64_t* Tt;   // tagged T words: T[c * r + l] = value bits | tag << 32, per replica
+  int64_t t_stride;  // words between replicas
+  uint32_t* ctl;  // control region
+  int64_t nnz;    // CSR entries
+  int x_lds;      // X staged in LDS
+  int vec;        // X, Vt rows 16-byte aligned: vector dot products
+  int vec_csr;    // CSR chunks: col_idx 16-byte, values 4*elem aligned, nnz >= 4
+  int nm_fast;    // bf16 2:4 with n % 32 == 0 and aligned rows: vector words
+  int spin;       // polls of a stale T word before computing it locally
+  int t_off, miss_off, x_off;  // dynamic LDS layout (bytes)
+};
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+template <int DT>
+__device__ __forceinline__ float fval(uint32_t bits) {
+  return Elem<DT>::to_f(bits);
+}
+
+// acc += dot of two 16-byte vectors (8 bf16 or 4 fp32 products).
+template <int DT>
+__device__ __forceinline__ float dot16(const u32x4& a, const u32x4& b, float acc) {
+  if constexpr (DT == HSS_BF16) {
+    acc = dot2_bf16(a.x, b.x, acc);
+    acc = dot2_bf16(a.y, b.y, acc);
+    acc = dot2_bf16(a.z, b.z, acc);
+    acc = dot2_bf16(a.w, b.w, acc);
+  } else {
+    acc = fmaf(__uint_as_float(a.x), __uint_as_float(b.x), acc);
+    acc = fmaf(__uint_as_float(a.y), __uint_as_float(b.y), acc);
+    acc = fmaf(__uint_as_float(a.z), __uint_as_float(b.z), acc);
+    acc = fmaf(__uint_as_float(a.w), __uint_as_float(b.w), acc);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ uint32_t tag_of(uint32_t epoch) { return epoch + 1u; }
+
+template <int BC>
+__device__ __forceinline__ float red_sum(float (*red)[BC], int c) {
+  return (red[0][c] + red[1][c]) + (red[2][c] + red[3][c]);
+}
+
+// Block-wide T[c][l] = Vt[l,:] . X[c,:] for c < bc (all 256 threads).  Thread
+// t covers 16-byte vectors q = t + 256k; TV of them (per operand) are loaded
+// before any is used.  Leaves the four wave sums in red[w][c] (the caller
+// adds them in a fixed order) after a barrier.
+template <int DT, int BC>
+__device__ __forceinline__ void t_row(const typename Elem<DT>::bits_t* __restrict__ v,
+                                      const typename Elem<DT>::bits_t* __restrict__ xsrc, int n,
+                                      int bc, int vec, float (*red)[BC]) {
+  using bits_t = typename Elem<DT>::bits_t;
+  constexpr int TV = BC <= 2 ? 4 : (BC <= 4 ? 2 : 1);
+  const int t = threadIdx.x;
+  float acc[BC];
+#pragma unroll
+  for (int c = 0; c < BC; ++c) acc[c] = 0.f;
+  int jt = 0;
+  if (vec) {
+    constexpr int NV = 16 / sizeof(bits_t);
+    const int nv = n / NV;
+    const u32x4* v4 = reinterpret_cast<const u32x4*>(v);
+    for (int base = 0; base < nv; base += 256 * TV) {
+      u32x4 vv[TV], xv[TV][BC];
+#pragma unroll
+      for (int k = 0; k < TV; ++k) {
+        const int qc = min(base + t + 256 * k, nv - 1);
+        vv[k] = __builtin_nontemporal_load(v4 + qc);
+#pragma unroll
+        for (int c = 0; c < BC; ++c)
+          xv[k][c] = reinterpret_cast<const u32x4*>(xsrc + (int64_t)min(c, bc - 1) * n)[qc];
+      }
+#pragma unroll
+      for (int k = 0; k < TV; ++k) {
+        if (base + t + 256 * k < nv) {
+#pragma unroll
+          for (int c = 0; c < BC; ++c)
+            if (c < bc) acc[c] = dot16<DT>(vv[k], xv[k][c], acc[c]);
+        }
+      }
+    }
+    jt = nv * NV;
+  }
+  for (int j = jt + t; j < n; j += 256) {
+    const float vj = fval<DT>(v[j]);
+#pragma unroll
+    for (int c = 0; c < BC; ++c)
+      if (c < bc) acc[c] = fmaf(vj, fval<DT>(xsrc[(int64_t)c * n + j]), acc[c]);
+  }
+  const int w = t >> 6;
+#pragma unroll
+  for (int c = 0; c < BC; ++c) {
+    const float s = wave_sum(acc[c]);
+    if (lane_id() == 0) red[w][c] = s;
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// CSR rows.  Lane L of pass p holds entries [a0 + 4L + 256p, +4) of a row,
+// a0 = row start rounded down to a multiple of 4 (16-byte aligned columns);
+// entries outside [start, end) are masked.  Pass-0 chunks of all the wave's
+// rows are loaded right after the row bounds return.
+// ---------------------------------------------------------------------------
+template <int DT, int RPW>
+struct CsrChunks {
+  static constexpr int VB = 4 * sizeof(typename Elem<DT>::bits_t);  // value bytes per chunk
+  typedef uint32_t vchunk_t __attribute__((ext_vector_type(VB / 4)));
+  int st[RPW], en[RPW], e0[RPW];
+  u32x4 cq[RPW];
+  vchunk_t vq[RPW];
+};
+
+template <int DT, int RPW>
+__device__ __forceinline__ void csr_issue(const DecodeArgs& a, const int (&rb)[RPW + 1],
+                                          CsrChunks<DT, RPW>& ch) {
+  using bits_t = typename Elem<DT>::bits_t;
+  using vchunk_t = typename CsrChunks<DT, RPW>::vchunk_t;
+  const int lane = lane_id();
+  const bits_t* __restrict__ vals = static_cast<const bits_t*>(a.vals);
+  const int64_t last = ((a.nnz - 4) & ~(int64_t)3);  // highest aligned full chunk
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    ch.st[i] = uniform(rb[i]);
+    ch.en[i] = uniform(rb[i + 1]);
+    ch.e0[i] = (ch.st[i] & ~3) + 4 * lane;
+    if (a.vec_csr) {
+      const int64_t ec = ch.e0[i] < last ? ch.e0[i] : last;
+      ch.cq[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.col_idx + ec));
+      ch.vq[i] = __builtin_nontemporal_load(reinterpret_cast<const vchunk_t*>(vals + ec));
+    }
+  }
+}
+
+// acc += the 4 entries of one chunk that fall in [st, en).
+template <int DT, int BC, typename VC>
+__device__ __forceinline__ void csr_chunk(const DecodeArgs& a, int e, int st, int en, const u32x4& cc,
+                                          const VC& vv, const typename Elem<DT>::bits_t* __restrict__ xsrc,
+                                          float (&acc)[BC]) {
+  using bits_t = typename Elem<DT>::bits_t;
+  const bits_t* __restrict__ vals = static_cast<const bits_t*>(a.vals);
+  const bool whole = e + 4 <= a.nnz;  // else: the array's tail, read element-wise
+  const int cols[4] = {(int)cc.x, (int)cc.y, (int)cc.z, (int)cc.w};
+  uint32_t vb4[4];
+  if constexpr (sizeof(bits_t) == 2) {
+    vb4[0] = vv.x & 0xffffu; vb4[1] = vv.x >> 16; vb4[2] = vv.y & 0xffffu; vb4[3] = vv.y >> 16;
+  } else {
+    vb4[0] = vv.x; vb4[1] = vv.y; vb4[2] = vv.z; vb4[3] = vv.w;
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int ek = e + k;
+    if (ek >= st && ek < en) {
+      const int ck = whole ? cols[k] : a.col_idx[ek];
+      const float vk = fval<DT>(whole ? vb4[k] : (uint32_t)vals[ek]);
+#pragma unroll
+      for (int c = 0; c < BC; ++c)
+        if (c < a.bc) acc[c] = fmaf(vk, fval<DT>(xsrc[(int64_t)c * a.n + ck]), acc[c]);
+    }
+  }
+}
+
+template <int DT, int BC, int RPW>
+__device__ __forceinline__ void csr_consume(const DecodeArgs& a, CsrChunks<DT, RPW>& ch,
+                                            const typename Elem<DT>::bits_t* __restrict__ xsrc,
+                                            float (&ssum)[RPW][BC]) {
+  using bits_t = typename Elem<DT>::bits_t;
+  using vchunk_t = typename CsrChunks<DT, RPW>::vchunk_t;
+  const int lane = lane_id();
+  const bits_t* __restrict__ vals = static_cast<const bits_t*>(a.vals);
+  const int64_t last = ((a.nnz - 4) & ~(int64_t)3);
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    float acc[BC];
+#pragma unroll
+    for (int c = 0; c < BC; ++c) acc[c] = 0.f;
+    const int st = ch.st[i], en = ch.en[i];
+    if (a.vec_csr) {
+      if (ch.e0[i] < en) csr_chunk<DT, BC>(a, ch.e0[i], st, en, ch.cq[i], ch.vq[i], xsrc, acc);
+      for (int base = (st & ~3) + 256; base < en; base += 256) {  // rows longer than 256 - 3
+        const int e = base + 4 * lane;
+        const int64_t ec = e < last ? e : last;
+        const u32x4 cc = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.col_idx + ec));
+        const vchunk_t vv = __builtin_nontemporal_load(reinterpret_cast<const vchunk_t*>(vals + ec));
+        if (e < en) csr_chunk<DT, BC>(a, e, st, en, cc, vv, xsrc, acc);
+      }
+    } else {
+      for (int p = st + lane; p < en; p += 64) {
+        const float v = fval<DT>(vals[p]);
+        const int col = a.col_idx[p];
+#pragma unroll
+        for (int c = 0; c < BC; ++c)
+          if (c < a.bc) acc[c] = fmaf(v, fval<DT>(xsrc[(int64_t)c * a.n + col]), acc[c]);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < BC; ++c) ssum[i][c] = wave_sum(acc[c]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 2:4 rows.  Lane L owns metadata words L, L+64, ... (32 columns each); the
+// first kWPL words of every row (metadata + 16 values) are loaded at kernel
+// start.  Fast path (bf16, n % 32 == 0): the 4-bit group index becomes a
+// byte-permute selector that packs the two kept X values next to each other,
+// and one bf16 dot2 per group accumulates both products in fp32.
+// ---------------------------------------------------------------------------
+static constexpr int kWPL = 2;
+
+template <int RPW>
+struct NmWords {
+  uint32_t mw[RPW][kWPL];
+  u32x4 vv[RPW][kWPL][2];
+};
+
+template <int DT, int RPW>
+__device__ __forceinline__ void nm_issue(const DecodeArgs& a, int row0, NmWords<RPW>& nw) {
+  using bits_t = typename Elem<DT>::bits_t;
+  if (!a.nm_fast) return;
+  const int lane = lane_id();
+  const int words = a.n >> 5;
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int rowc = min(row0 + i, a.m - 1);
+    const uint32_t* __restrict__ Mr = a.meta + (int64_t)rowc * words;
+    const bits_t* __restrict__ Vr = static_cast<const bits_t*>(a.nmv) + (int64_t)rowc * (a.n >> 1);
+#pragma unroll
+    for (int k = 0; k < kWPL; ++k) {
+      const int wdc = min(lane + 64 * k, words - 1);
+      nw.mw[i][k] = __builtin_nontemporal_load(Mr + wdc);
+      const u32x4* vp = reinterpret_cast<const u32x4*>(Vr + wdc * 16);
+      nw.vv[i][k][0] = __builtin_nontemporal_load(vp);
+      nw.vv[i][k][1] = __builtin_nontemporal_load(vp + 1);
+    }
+  }
+}
+
+template <int BC>
+__device__ __forceinline__ void nm_word_fast(uint32_t mw, const u32x4 (&vv)[2],
+                                             const uint16_t* __restrict__ xsrc, int n, int bc, int c0,
+                                             float (&acc)[BC]) {
+  const uint32_t vw[8] = {vv[0].x, vv[0].y, vv[0].z, vv[0].w, vv[1].x, vv[1].y, vv[1].z, vv[1].w};
+  uint32_t sel[8];
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    // bytes 2*i, 2*i+1 of the 8-byte group {x3 x2 | x1 x0} hold x[i]
+    const uint32_t i0 = (mw >> (4 * g)) & 3u;
+    const uint32_t i1 = (mw >> (4 * g + 2)) & 3u;
+    sel[g] = (i0 | (i1 << 16)) * 0x0202u + 0x01000100u;
+  }
+#pragma unroll
+  for (int c = 0; c < BC; ++c) {
+    if (c < bc) {
+      const u32x4* xp = reinterpret_cast<const u32x4*>(xsrc + (int64_t)c * n + c0);
+      u32x4 xq[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) xq[h] = xp[h];
+      const uint32_t xw[16] = {xq[0].x, xq[0].y, xq[0].z, xq[0].w, xq[1].x, xq[1].y,
+                               xq[1].z, xq[1].w, xq[2].x, xq[2].y, xq[2].z, xq[2].w,
+                               xq[3].x, xq[3].y, xq[3].z, xq[3].w};
+#pragma unroll
+      for (int g = 0; g < 8; ++g)
+        acc[c] = dot2_bf16(vw[g], __builtin_amdgcn_perm(xw[2 * g + 1], xw[2 * g], sel[g]), acc[c]);
+    }
+  }
+}
+
+template <int DT, int BC, int RPW>
+__device__ __forceinline__ void nm_consume(const DecodeArgs& a, int row0, const NmWords<RPW>& nw,
+                                           const typename Elem<DT>::bits_t* __restrict__ xsrc,
+                                           float (&ssum)[RPW][BC]) {
+  using bits_t = typename Elem<DT>::bits_t;
+  const int lane = lane_id();
+  const int m = a.m, n = a.n, bc = a.bc;
+  const int words = (n + 31) >> 5;
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int row = row0 + i;
+    float acc[BC];
+#pragma unroll
+    for (int c = 0; c < BC; ++c) acc[c] = 0.f;
+    if (row < m) {
+      const uint32_t* __restrict__ Mr = a.meta + (int64_t)row * words;
+      const bits_t* __restrict__ Vr = static_cast<const bits_t*>(a.nmv) + (int64_t)row * (n >> 1);
+      if constexpr (DT == HSS_BF16) {
+        if (a.nm_fast) {
+#pragma unroll
+          for (int k = 0; k < kWPL; ++k) {
+            const int wd = lane + 64 * k;
+            if (wd < words) nm_word_fast<BC>(nw.mw[i][k], nw.vv[i][k], xsrc, n, bc, wd * 32, acc);
+          }
+          for (int base = 64 * kWPL; base < words; base += 64) {  // words beyond the prefetched ones
+            const int wd = base + lane;
+            const int wdc = min(wd, words - 1);
+            const uint32_t mw = __builtin_nontemporal_load(Mr + wdc);
+            const u32x4* vp = reinterpret_cast<const u32x4*>(Vr + wdc * 16);
+            const u32x4 vv[2] = {__builtin_nontemporal_load(vp), __builtin_nontemporal_load(vp + 1)};
+            if (wd < words) nm_word_fast<BC>(mw, vv, xsrc, n, bc, wd * 32, acc);
+          }
+        }
+      }
+      if (!(DT == HSS_BF16 && a.nm_fast)) {
+        for (int wd = lane; wd < words; wd += 64) {
+          const uint32_t mw = Mr[wd];
+          const int c0 = wd * 32;
+          const int ng = min(8, (n - c0) >> 2);
+          for (int g = 0; g < ng; ++g) {
+            const uint32_t nib = (mw >> (4 * g)) & 15u;
+            const int j0 = c0 + 4 * g + (int)(nib & 3u);
+            const int j1 = c0 + 4 * g + (int)(nib >> 2);
+            const float v0 = fval<DT>(Vr[(c0 >> 1) + 2 * g]);
+            const float v1 = fval<DT>(Vr[(c0 >> 1) + 2 * g + 1]);
+#pragma unroll
+            for (int c = 0; c < BC; ++c) {
+              if (c < bc) {
+                acc[c] = fmaf(v0, fval<DT>(xsrc[(int64_t)c * n + j0]), acc[c]);
+                acc[c] = fmaf(v1, fval<DT>(xsrc[(int64_t)c * n + j1]), acc[c]);
+              }
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < BC; ++c) ssum[i][c] = wave_sum(acc[c]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// U entries of this wave's rows.  VECU (bf16, r % 4 == 0): lane L holds
+// l = 4L + 256q .. +3 (q < 2 covers r <= 512) as 8-byte vectors; otherwise
+// lane L holds l = L + 64q (q < 8).  Larger r continues in the epilogue.
+// Out-of-range slots load a clamped valid address and are skipped at use, so
+// nothing waits for these loads before the epilogue.
+// ---------------------------------------------------------------------------
+static constexpr int kUPL = 8;
+
+template <int DT, int RPW, bool VECU>
+__device__ __forceinline__ void u_issue(const DecodeArgs& a, int row0, uint32_t (&ub)[RPW][kUPL]) {
+  using bits_t = typename Elem<DT>::bits_t;
+  const bits_t* __restrict__ U = static_cast<const bits_t*>(a.U);
+  const int lane = lane_id();
+  const int m = a.m, r = a.r;
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int row = row0 + i;
+    const int64_t rowc = min(row, m - 1);
+    if constexpr (VECU) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int l = 4 * lane + 256 * q;
+        const int lc = min(l, r - 4);
+        const u32x2 u2 = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(U + rowc * r + lc));
+        ub[i][2 * q] = u2.x;  // masked at use (the epilogue skips l >= r, row >= m)
+        ub[i][2 * q + 1] = u2.y;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < kUPL; ++q) {
+        const int l = lane + 64 * q;
+        ub[i][q] = __builtin_nontemporal_load(U + rowc * r + min(l, r - 1));  // masked at use
+      }
+    }
+  }
+}
+
+template <int DT, int BC, int RPW, bool VECU>
+__device__ __forceinline__ void u_epilogue(const DecodeArgs& a, int row0, const uint32_t (&ub)[RPW][kUPL],
+                                           const float* __restrict__ Ts, float (&acc)[RPW][BC]) {
+  using bits_t = typename Elem<DT>::bits_t;
+  const bits_t* __restrict__ U = static_cast<const bits_t*>(a.U);
+  const int lane = lane_id();
+  const int m = a.m, r = a.r, bc = a.bc;
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int row = row0 + i;
+#pragma unroll
+    for (int c = 0; c < BC; ++c) acc[i][c] = 0.f;
+    if (row >= m) continue;
+    if constexpr (VECU) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int l = 4 * lane + 256 * q;
+        if (l < r) {
+          const float u0 = bf16lo(ub[i][2 * q]), u1 = bf16hi(ub[i][2 * q]);
+          const float u2 = bf16lo(ub[i][2 * q + 1]), u3 = bf16hi(ub[i][2 * q + 1]);
+#pragma unroll
+          for (int c = 0; c < BC; ++c) {
+            if (c < bc) {
+              const float4 tv = *reinterpret_cast<const float4*>(Ts + c * r + l);
+              acc[i][c] = fmaf(u0, tv.x, acc[i][c]);
+              acc[i][c] = fmaf(u1, tv.y, acc[i][c]);
+              acc[i][c] = fmaf(u2, tv.z, acc[i][c]);
+              acc[i][c] = fmaf(u3, tv.w, acc[i][c]);
+            }
+          }
+        }
+      }
+      for (int l = 4 * lane + 512; l < r; l += 256) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float u = fval<DT>(U[(int64_t)row * r + l + k]);
+#pragma unroll
+          for (int c = 0; c < BC; ++c)
+            if (c < bc) acc[i][c] = fmaf(u, Ts[c * r + l + k], acc[i][c]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < kUPL; ++q) {
+        const int l = lane + 64 * q;
+        if (l < r) {
+          const float u = fval<DT>(ub[i][q]);
+#pragma unroll
+          for (int c = 0; c < BC; ++c)
+            if (c < bc) acc[i][c] = fmaf(u, Ts[c * r + l], acc[i][c]);
+        }
+      }
+      for (int l = lane + 64 * kUPL; l < r; l += 64) {
+        const float u = fval<DT>(U[(int64_t)row * r + l]);
+#pragma unroll
+        for (int c = 0; c < BC; ++c)
+          if (c < bc) acc[i][c] = fmaf(u, Ts[c * r + l], acc[i][c]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Arrival count: called once per block by thread 0, strictly after the block's
+// epoch load returned (the inline wait).  The first level spreads the blocks
+// over 64 counters; sub_last/top carry the second level to the block's end.
+__device__ __forceinline__ void arrive(const DecodeArgs& a, int G, int nsub, int sub, bool& sub_last,
+                                       uint32_t& top) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  const uint32_t arrived = __hip_atomic_fetch_add(a.ctl + kCtlSub0 + kCtlSubStride * sub, 1u,
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  sub_last = arrived == (uint32_t)((G - sub + nsub - 1) / nsub) - 1;
+  if (sub_last)
+    top = __hip_atomic_fetch_add(a.ctl + kCtlTop, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Last arrival overall: every block has read the epoch, so advance it and
+// clear the counters for the next call (which starts after this kernel).
+__device__ __forceinline__ void finish_epoch(const DecodeArgs& a, int nsub, bool sub_last, uint32_t top,
+                                             uint32_t tag) {
+  if (sub_last && top == (uint32_t)nsub - 1) {
+    for (int k = 0; k < nsub; ++k)
+      __hip_atomic_store(a.ctl + kCtlSub0 + kCtlSubStride * k, 0u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.ctl + kCtlTop, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.ctl + kCtlEpoch, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Grid: blocks [0, r) are T producers (row l of T each; the lowest block ids
+// are dispatched first), the rest own 4*RPW output rows each.
+template <int DT, int FMT, int BC, int RPW, bool VECU>
+__global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
+  using bits_t = typename Elem<DT>::bits_t;
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ float red[4][BC];
+  __shared__ uint32_t epoch_sh;
+
+  const int t = threadIdx.x;
+  const int w = t >> 6;
+  const int m = a.m, n = a.n, r = a.r, bc = a.bc;
+  const int G = (int)gridDim.x;
+  const bits_t* __restrict__ X = static_cast<const bits_t*>(a.X);
+  const bits_t* __restrict__ Vt = static_cast<const bits_t*>(a.Vt);
+  float* Ts = reinterpret_cast<float*>(smem + a.t_off);
+  uint32_t* miss = reinterpret_cast<uint32_t*>(smem + a.miss_off);
+  bits_t* xs = reinterpret_cast<bits_t*>(smem + a.x_off);
+  const bits_t* xsrc = a.x_lds ? xs : X;
+  const int nsub = G < kNumSub ? G : kNumSub;
+  const int sub = (int)blockIdx.x % nsub;
+  bool sub_last = false;
+  uint32_t top = 0;
+
+  // ---- T producer: Vt row l and X loaded together, published tagged into
+  //      every replica ----
+  if ((int)blockIdx.x < r) {
+    const int l = blockIdx.x;
+    const uint32_t e = __hip_atomic_load(a.ctl + kCtlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    t_row<DT, BC>(Vt + (int64_t)l * n, X, n, bc, a.vec, red);
+    if (t == 0) {
+#pragma unroll
+      for (int c = 0; c < BC; ++c) {
+        if (c < bc) {
+          const uint64_t word = (uint64_t)__float_as_uint(red_sum<BC>(red, c)) | ((uint64_t)tag_of(e) << 32);
+          for (int rep = 0; rep < kTReplicas; ++rep)
+            __hip_atomic_store(a.Tt + (int64_t)rep * a.t_stride + (int64_t)c * r + l, word,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      arrive(a, G, nsub, sub, sub_last, top);
+      finish_epoch(a, nsub, sub_last, top, tag_of(e));
+    }
+    return;
+  }
+
+  // ---- row blocks ----
+  const int row0 = (((int)blockIdx.x - r) * 4 + w) * RPW;
+
+  // batch 1: row bounds
+  int rb[RPW + 1];
+  if constexpr (FMT == HSS_FMT_CSR) {
+#pragma unroll
+    for (int i = 0; i <= RPW; ++i) rb[i] = a.row_ptr[min(max(row0 + i, 0), m)];
+  }
+
+  // batch 2: everything else, issued before any of it is used
+  CsrChunks<DT, RPW> ch;
+  if constexpr (FMT == HSS_FMT_CSR) csr_issue<DT, RPW>(a, rb, ch);
+  NmWords<RPW> nw;
+  if constexpr (FMT == HSS_FMT_2OF4) nm_issue<DT, RPW>(a, row0, nw);
+  constexpr int NV = 16 / sizeof(bits_t);
+  constexpr int kXR = 4;  // staged X vectors per thread held in registers
+  const bool xreg = a.x_lds && a.vec;
+  const int xvecs = xreg ? bc * n / NV : 0;
+  u32x4 xr[kXR];
+  if (xvecs > 0) {
+#pragma unroll
+    for (int k = 0; k < kXR; ++k) xr[k] = reinterpret_cast<const u32x4*>(X)[min(t + 256 * k, xvecs - 1)];
+  }
+  uint32_t ub[RPW][kUPL];
+  if (r > 0) u_issue<DT, RPW, VECU>(a, row0, ub);
+  uint32_t epoch = 0;
+  if (r > 0) epoch = __hip_atomic_load(a.ctl + kCtlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int q = t; q < (r + 31) / 32; q += 256) miss[q] = 0;
+
+  // X -> LDS; arrival
+  if (xvecs > 0) {
+    u32x4* dst = reinterpret_cast<u32x4*>(xs);
+#pragma unroll
+    for (int k = 0; k < kXR; ++k)
+      if (t + 256 * k < xvecs) dst[t + 256 * k] = xr[k];
+    for (int q = t + 256 * kXR; q < xvecs; q += 256) dst[q] = reinterpret_cast<const u32x4*>(X)[q];
+  } else if (a.x_lds) {
+    for (int q = t; q < bc * n; q += 256) xs[q] = X[q];
+  }
+  if (r > 0 && t == 0) {
+    epoch_sh = epoch;
+    arrive(a, G, nsub, sub, sub_last, top);
+  }
+  __syncthreads();
+  const uint32_t tag = tag_of(epoch_sh);
+
+  // sparse part
+  float ssum[RPW][BC];
+  if constexpr (FMT == HSS_FMT_CSR)
+    csr_consume<DT, BC, RPW>(a, ch, xsrc, ssum);
+  else
+    nm_consume<DT, BC, RPW>(a, row0, nw, xsrc, ssum);
+
+  // T -> LDS: this block's replica, tag check, bounded polling of stale
+  // words, then local computation of any row still missing.
+  if (r > 0) {
+    const uint64_t* __restrict__ Tr = a.Tt + (int64_t)(blockIdx.x % kTReplicas) * a.t_stride;
+    const int total = bc * r;
+    for (int base = 0; base < total; base += 4 * 256) {
+      uint64_t v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        v[k] = __hip_atomic_load(Tr + min(base + t + 256 * k, total - 1), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int e = base + t + 256 * k;
+        if (e < total) {
+          for (int s = 0; (uint32_t)(v[k] >> 32) != tag && s < a.spin; ++s) {
+            __builtin_amdgcn_s_sleep(1);
+            v[k] = __hip_atomic_load(Tr + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+          if ((uint32_t)(v[k] >> 32) == tag) {
+            Ts[e] = __uint_as_float((uint32_t)v[k]);
+          } else {
+            const int l = e % r;
+            atomicOr(&miss[l >> 5], 1u << (l & 31));
+          }
+        }
+      }
+    }
+    __syncthreads();
+    for (int wi = 0; wi < (r + 31) / 32; ++wi) {
+      uint32_t bits = (uint32_t)__builtin_amdgcn_readfirstlane((int)miss[wi]);  // block-uniform
+      while (bits) {
+        const int l = wi * 32 + __ffs(bits) - 1;
+        bits &= bits - 1;
+        t_row<DT, BC>(Vt + (int64_t)l * n, xsrc, n, bc, a.vec, red);
+        if (t < bc) Ts[(int64_t)t * r + l] = red_sum<BC>(red, t);
+        __syncthreads();
+      }
+    }
+  }
+
+  // low-rank epilogue, store
+  float lacc[RPW][BC];
+  if (r > 0) u_epilogue<DT, BC, RPW, VECU>(a, row0, ub, Ts, lacc);
+  bits_t* __restrict__ Y = static_cast<bits_t*>(a.Y);
+  const int lane = lane_id();
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int row = row0 + i;
+#pragma unroll
+    for (int c = 0; c < BC; ++c) {
+      const float s = (r > 0 ? wave_sum(lacc[i][c]) : 0.f) + ssum[i][c];
+      if (row < m && c < bc && lane == c) {
+        if constexpr (DT == HSS_F32)
+          Y[(int64_t)c * m + row] = __float_as_uint(s);
+        else
+          Y[(int64_t)c * m + row] = f32_to_bf16(s);
+      }
+    }
+  }
+  if (t == 0) finish_epoch(a, nsub, sub_last, top, tag);
+}
+
+// ---------------------------------------------------------------------------
+template <int DT, int FMT, int BC, bool VECU>
+static void launch_v(const DecodeArgs& a, int rpw, size_t lds, hipStream_t s) {
+  const int rows_per_block = 4 * rpw;
+  const unsigned grid = (unsigned)(a.r + (a.m + rows_per_block - 1) / rows_per_block);
+  if (rpw == 1)
+    hipLaunchKernelGGL((k_decode<DT, FMT, BC, 1, VECU>), dim3(grid), dim3(256), lds, s, a);
+  else
+    hipLaunchKernelGGL((k_decode<DT, FMT, BC, 2, VECU>), dim3(grid), dim3(256), lds, s, a);
+}
+
+template <int DT, int FMT, int BC>
+static void launch_bc(const DecodeArgs& a, bool vecu, int rpw, size_t lds, hipStream_t s) {
+  if constexpr (DT == HSS_BF16) {
+    if (vecu) return launch_v<DT, FMT, BC, true>(a, rpw, lds, s);
+  }
+  launch_v<DT, FMT, BC, false>(a, rpw, lds, s);
+}
+
+template <int DT, int FMT>
+static void launch_fmt(const DecodeArgs& a, bool vecu, int rpw, size_t lds, hipStream_t s) {
+  if (a.bc == 1) launch_bc<DT, FMT, 1>(a, vecu, rpw, lds, s);
+  else if (a.bc == 2) launch_bc<DT, FMT, 2>(a, vecu, rpw, lds, s);
+  else if (a.bc <= 4) launch_bc<DT, FMT, 4>(a, vecu, rpw, lds, s);
+  else launch_bc<DT, FMT, 8>(a, vecu, rpw, lds, s);
+}
+
+static constexpr size_t kMaxLds = 60 * 1024;  // dynamic LDS budget per block
+
+static size_t align16(size_t x) { return (x + 15) / 16 * 16; }
+
+size_t decode_ctl_bytes() { return kCtlBytes; }
+
+// Words between T replicas for a matrix of rank r: room for 8 columns, padded
+// to whole 4 KiB pages plus one 128-byte line so copies start on different
+// lines and pages.
+static int64_t t_stride_words(int r) {
+  const int64_t words = 8 * (int64_t)(r > 0 ? r : 1);
+  return (words + 511) / 512 * 512 + 16;
+}
+
+size_t decode_t_bytes(const hss_matrix* A) {
+  return sizeof(uint64_t) * (size_t)t_stride_words(A->r) * kTReplicas;
+}
+
+// Largest column count per launch (1, 2, 4 or 8) whose T fits the LDS budget;
+// 0 if even one column does not fit.
+int decode_max_cols(const hss_matrix* A) {
+  for (int bc = 8; bc >= 1; bc /= 2) {
+    const size_t tb = align16(sizeof(float) * (size_t)bc * A->r) +
+                      align16(4 * (size_t)((A->r + 31) / 32));
+    if (tb <= kMaxLds) return bc;
+  }
+  return 0;
+}
+
+static int spin_limit() {
+  const char* s = getenv("HSS_DECODE_SPIN");
+  return s ? atoi(s) : 4096;
+}
+
+// One fused decode pass over bc columns (1 <= bc <= decode_max_cols(A)).
+void launch_decode(const hss_matrix* A, int bc, const void* X, void* Y, void* ws, hipStream_t s) {
+  DecodeArgs a;
+  a.m = A->m; a.n = A->n; a.r = A->r; a.bc = bc;
+  a.row_ptr = A->row_ptr; a.col_idx = A->col_idx; a.vals = A->values;
+  a.nmv = A->nm_values; a.meta = A->nm_meta;
+  a.U = A->U; a.Vt = A->Vt; a.X = X; a.Y = Y;
+  a.ctl = static_cast<uint32_t*>(ws);
+  a.Tt = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + kCtlBytes);
+  a.t_stride = t_stride_words(A->r);
+  a.nnz = A->nnz;
+  a.spin = spin_limit();
+  const size_t es = A->dtype == HSS_F32 ? 4 : 2;
+  const size_t tbytes = align16(sizeof(float) * (size_t)bc * A->r);
+  const size_t mbytes = align16(4 * (size_t)((A->r + 31) / 32));
+  const size_t xbytes = align16((size_t)bc * A->n * es);
+  a.t_off = 0;
+  a.miss_off = (int)tbytes;
+  a.x_off = (int)(tbytes + mbytes);
+  a.x_lds = tbytes + mbytes + xbytes <= kMaxLds;
+  // Vector dot products: X rows and Vt rows start 16-byte aligned.
+  a.vec = ((uintptr_t)X % 16 == 0) && ((size_t)A->n * es) % 16 == 0 &&
+          (A->r == 0 || (uintptr_t)A->Vt % 16 == 0);
+  a.vec_csr = A->fmt == HSS_FMT_CSR && A->nnz >= 4 && (uintptr_t)A->col_idx % 16 == 0 &&
+              (uintptr_t)A->values % (4 * es) == 0;
+  a.nm_fast = A->fmt == HSS_FMT_2OF4 && A->dtype == HSS_BF16 && a.vec && A->n % 32 == 0 &&
+              (uintptr_t)A->nm_values % 16 == 0 && (uintptr_t)A->nm_meta % 4 == 0;
+  // bf16 U rows as 8-byte vectors; T rows in LDS (c * r floats) stay 16-byte aligned.
+  const bool vecu = A->dtype == HSS_BF16 && A->r > 0 && A->r % 4 == 0 && (uintptr_t)A->U % 8 == 0;
+  const size_t lds = tbytes + mbytes + (a.x_lds ? xbytes : 0);
+  const int rpw = A->m >= 8192 ? 2 : 1;
+  if (A->dtype == HSS_F32) {
+    if (A->fmt == HSS_FMT_CSR) launch_fmt<HSS_F32, HSS_FMT_CSR>(a, false, rpw, lds, s);
+    else launch_fmt<HSS_F32, HSS_FMT_2OF4>(a, false, rpw, lds, s);
+  } else {
+    if (A->fmt == HSS_FMT_CSR) launch_fmt<HSS_BF16, HSS_FMT_CSR>(a, vecu, rpw, lds, s);
+    else launch_fmt<HSS_BF16, HSS_FMT_2OF4>(a, vecu, rpw, lds, s);
+  }
+}
+
+}  // namespace hss

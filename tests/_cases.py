@@ -18,6 +18,8 @@ def dt_of(cfg_dtype):
 def to_dev(a, dtype):
     import torch
     a = np.ascontiguousarray(a)
+    if not a.flags.writeable:
+        a = a.copy()
     if dtype == O.F32:
         return torch.from_numpy(a.astype(np.float32, copy=False)).cuda()
     if a.dtype == np.uint32:

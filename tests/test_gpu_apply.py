@@ -90,8 +90,6 @@ def test_apply_small(H, dtype, case):
     _check(Y1, dtype, Yref, N)
     Y2 = H.hss_apply(A, Xd)
     assert O.bits_equal(to_host(Y1), to_host(Y2))                  # deterministic
-    ws = A.workspace(b)
-    assert int(ws[:256].abs().sum().item()) == 0                   # control words left at zero
 
 
 @pytest.mark.parametrize("dtype", [O.F32, O.BF16])
@@ -169,3 +167,53 @@ def test_apply_config5_sampled(H):
     rows = np.random.default_rng(5).choice(8192, size=96, replace=False)
     rows.sort()
     _sampled_check(H, 5, 0, 2048, rows)
+
+
+@pytest.mark.parametrize("fmt,dtype,b", [("csr", O.BF16, 1), ("csr", O.F32, 3), ("2:4", O.BF16, 8),
+                                         ("2:4", O.F32, 2)])
+def test_apply_local_fallback_is_bitwise_identical(H, monkeypatch, fmt, dtype, b):
+    """With a zero poll budget every block computes the T rows it finds stale
+    itself; the result must be bit-identical to the normal hand-off."""
+    m, n, r = 300, 512, 40
+    W = syn.random_matrix(m, n, dtype, seed=21, kind="t3")
+    ref = O.split_csr(W, dtype, O.topk_count(m, n, 5, 100)) if fmt == "csr" else O.split_24(W, dtype)
+    U, V = _factors(m, n, r, dtype, 22)
+    X = syn.random_matrix(b, n, dtype, seed=23, kind="normal", scale=1.0)
+    A = _matrix(H, fmt, dtype, m, n, ref, U, V)
+    Xd = to_dev(X, dtype)
+    Y_normal = to_host(H.hss_apply(A, Xd))
+    monkeypatch.setenv("HSS_DECODE_SPIN", "0")
+    Y_local = to_host(H.hss_apply(A, Xd))
+    monkeypatch.delenv("HSS_DECODE_SPIN")
+    assert O.bits_equal(Y_normal, Y_local)
+    S64 = _dense_S(fmt, dtype, m, n, ref)
+    U64, V64, X64 = O.widen(U, dtype), O.widen(V, dtype), O.widen(X, dtype)
+    err = O.max_normalised_error(O.widen(Y_local, dtype), O.apply_factored(S64, U64, V64, X64),
+                                 O.normaliser(S64, U64, V64, X64))
+    assert err <= O.TOL[dtype]
+
+
+def test_apply_shared_workspace_many_calls(H):
+    """One workspace shared by two matrices of different shape, rank and batch,
+    called alternately many times: every result equals the one from a fresh
+    workspace (the call tags never let a stale T row through)."""
+    import torch
+    dtype = O.BF16
+    mats, xs, expect = [], [], []
+    for (m, n, r, b, seed) in [(200, 256, 24, 1, 31), (96, 512, 70, 5, 32)]:
+        W = syn.random_matrix(m, n, dtype, seed=seed, kind="t3")
+        ref = O.split_csr(W, dtype, O.topk_count(m, n, 5, 100))
+        U, V = _factors(m, n, r, dtype, seed)
+        A = _matrix(H, "csr", dtype, m, n, ref, U, V)
+        X = [to_dev(syn.random_matrix(b, n, dtype, seed=seed + 100 + i, kind="normal", scale=1.0), dtype)
+             for i in range(3)]
+        mats.append(A)
+        xs.append(X)
+        expect.append([to_host(H.hss_apply(A, x)) for x in X])     # each with its own workspace
+    size = max(H.hss_apply_workspace_size(A, x[0].shape[0]) for A, x in zip(mats, xs))
+    ws = torch.zeros(size, dtype=torch.uint8, device="cuda")
+    for it in range(40):
+        k = it % 2
+        i = (it // 2) % 3
+        Y = H.hss_apply(mats[k], xs[k][i], ws=ws)
+        assert O.bits_equal(to_host(Y), expect[k][i]), (it, k, i)
