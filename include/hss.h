@@ -131,7 +131,8 @@ hss_status hss_get_error(const void* ws, hipStream_t stream);
  * The compressed matrix.  All arrays are device memory in `dtype` unless
  * stated.  r = 0 means no low-rank term (U, Vt ignored).
  *   fmt == HSS_FMT_CSR:  row_ptr int32[m+1], col_idx int32[nnz] (each row's
- *     columns in [0, n), any order), values dtype[nnz]; nnz = row_ptr[m].
+ *     columns in [0, n), strictly ascending -- the order hss_split writes),
+ *     values dtype[nnz]; nnz = row_ptr[m].
  *     The nm_* fields are ignored.
  *   fmt == HSS_FMT_2OF4: nm_values dtype[m*n/2], nm_meta uint32[m*ceil(n/32)]
  *     in the layout hss_split writes; CSR fields ignored.
@@ -166,6 +167,9 @@ hss_status hss_apply_workspace_size(const hss_matrix* A, int32_t b, size_t* byte
  *     counter), so the caller must not write to it afterwards; any number of
  *     calls, with any matrices and batch sizes, may then share it as long as
  *     they are ordered (same stream or events).
+ * Execution: bf16 with b >= 16 runs on the matrix cores (T^T = X V and Y =
+ * [X | T^T] [S | U]^T as MFMA GEMMs with fp32 accumulation; T is rounded to
+ * bf16 once, between the two); otherwise one fused kernel per 8 columns.
  * Returns HSS_ERR_INVALID_ARG for: A or X or Y null, unknown fmt/dtype,
  *   reserved != 0, m, n <= 0, r < 0, b < 1, b*m, b*n, m*n, r*(m+n) >= 2^31,
  *   nnz < 0, required arrays null, n % 4 != 0 for 2:4, X overlapping Y.
