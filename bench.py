@@ -1,20 +1,30 @@
 #!/usr/bin/env python3
 """Throughput of the sparse + low-rank (HSS) linear layer on one MI355X.
 
-Workload (one step = one hss_apply, i.e. one decode token): the 4096 x 4096
-bf16 attention-projection shape with Student-t (nu = 3) x 0.02 weights and
-0.5 % outliers x20; S = top 5 % by |w| in CSR (838,860 bf16 values, int32
+Headline workload (one step = one hss_apply = one decode token): the 4096 x
+4096 bf16 attention-projection shape with Student-t (nu = 3) x 0.02 weights
+and 0.5 % outliers x20; S = top 5 % by |w| in CSR (838,860 bf16 values, int32
 columns), low-rank factors of rank 256; X ~ N(0, 1) bf16, batch 1.  S comes
 from this library's own hss_split of the seeded W; the factors are seeded
-stand-ins with a truncated SVD's shapes and scale.
+stand-ins with a truncated SVD's shapes and scale (the factorisation is
+offline and its values do not change the work).
 
-Cold-HBM protocol: the compressed operands (CSR arrays, U, V^T) are replicated
-into enough distinct device copies that one pass over them spans >= 1 GiB
-(4x the 256 MB last-level cache); consecutive steps use consecutive copies.
+Cold-HBM protocol: the compressed operands (CSR arrays, U, V^T) are
+replicated into enough distinct device copies that one pass over them spans
+>= 1 GiB (4x the 256 MB last-level cache); consecutive steps use consecutive
+copies.  The timed steps are replayed from a HIP graph (decode loops are
+launch-bound; the kernels keep their cross-call state on the device, so
+replays are exact); the plain stream-launch rate is reported beside it.
 
-Prints ONE JSON line.  `value` = tokens/s of the timed steps; `roofline`
-prices the apply's compressed-weight bytes against the 8 TB/s HBM peak;
-`cpu_baseline` times the fp64 CPU oracle on a bounded sample.
+Also measured in the same run (extra JSON keys): the same layer at batch 16,
+the 11008 x 4096 2:4 layer at batch 1/8/64, one decoder layer's seven
+projections per decode token, the 8192^2 prefill at batch 2048 (with the
+low-rank GEMMs alone for their matrix-core throughput), and hss_split.
+
+Prints ONE JSON line.  `value` = decode tokens/s of the timed steps;
+`roofline` prices the apply kernel's compressed-weight bytes against the
+8 TB/s HBM peak; `cpu_baseline` times the fp64 CPU oracle on a bounded
+sample.
 """
 from __future__ import annotations
 
@@ -27,7 +37,9 @@ import time
 
 METRIC = "sparse+low-rank linear tokens/s + compressed-weight GB/s (% HBM peak), 1 GPU"
 HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
 ROOT = os.path.dirname(os.path.abspath(__file__))
+GIB = float(1 << 30)
 
 
 def _args():
@@ -38,7 +50,7 @@ def _args():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the CPU-oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--rotation-bytes", type=float, default=float(1 << 30))
+    ap.add_argument("--only-headline", action="store_true", help="skip the other workloads")
     return ap.parse_args()
 
 
@@ -48,34 +60,105 @@ def _bf16(a):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def _time_applies(H, mats, xs, ys, ws, steps, warmup):
-    """Average ms per hss_apply over `steps` calls, rotating matrices and inputs.
-    Events are recorded on the stream the library launches on."""
+def _log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class Layer:
+    """One compressed matrix and its rotation copies on the device."""
+
+    def __init__(self, H, W, fmt, frac, r, seed, which=0, rotation_bytes=GIB):
+        import torch
+        import hss_synth as syn
+        m, n = W.shape
+        self.m, self.n, self.r = m, n, r
+        self.split = H.hss_split(W, fmt, frac=frac)
+        U, V = syn.factors(m, n, r, "bf16", seed, which)
+        self.U, self.Vt = _bf16(U), _bf16(V.T)
+        if fmt == "csr":
+            self.w_bytes = self.split.k * (2 + 4) + 4 * (m + 1) + (m + n) * r * 2
+        else:
+            self.w_bytes = m * n // 2 * 2 + m * ((n + 31) // 32) * 4 + (m + n) * r * 2
+        self.copies = max(1, math.ceil(rotation_bytes / self.w_bytes))
+        self.mats = []
+        sp = self.split
+        for _ in range(self.copies):
+            if fmt == "csr":
+                self.mats.append(H.HSSMatrix("csr", m, n, torch.bfloat16, U=self.U.clone(), Vt=self.Vt.clone(),
+                                             row_ptr=sp.row_ptr.clone(), col_idx=sp.col_idx.clone(),
+                                             values=sp.values.clone(), nnz=sp.k))
+            else:
+                self.mats.append(H.HSSMatrix("2:4", m, n, torch.bfloat16, U=self.U.clone(), Vt=self.Vt.clone(),
+                                             nm_values=sp.nm_values.clone(), nm_meta=sp.nm_meta.clone()))
+
+    def flops(self, b):
+        nnz = self.split.k
+        return 2.0 * b * (nnz + self.r * (self.m + self.n))
+
+
+def _time(fn, steps, warmup):
+    """Average ms per call of fn(i) over `steps` calls (HIP events on the
+    current stream, which is the one the library launches on)."""
     import torch
-    s = torch.cuda.current_stream()
-    nm, nx = len(mats), len(xs)
     for i in range(warmup):
-        H.hss_apply(mats[i % nm], xs[i % nx], ys[i % len(ys)], ws)
+        fn(i)
     torch.cuda.synchronize()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record(s)
+    t0.record()
     for i in range(steps):
-        H.hss_apply(mats[i % nm], xs[i % nx], ys[i % len(ys)], ws)
-    t1.record(s)
+        fn(i)
+    t1.record()
     torch.cuda.synchronize()
     return t0.elapsed_time(t1) / steps
 
 
+def _time_graph(fn, steps, warmup, reps=3):
+    """Capture `steps` calls of fn(i) into one HIP graph, replay it `reps`
+    times (after a warm-up replay), return ms per call."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / (steps * reps)
+
+
+def _apply_loop(H, layer, xs, ys, ws, rotate=True):
+    mats = layer.mats if rotate else layer.mats[:1]
+
+    def fn(i):
+        H.hss_apply(mats[i % len(mats)], xs[i % len(xs)], ys[i % len(ys)], ws)
+    return fn
+
+
+def _acts(cfg, b, which, count, m):
+    import torch
+    import hss_synth as syn
+    xs = [_bf16(syn.activations(cfg, b, which, step)) for step in range(count)]
+    ys = [torch.empty((b, m), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    return xs, ys
+
+
 def _cpu_baseline(cfg, W, U, V, seconds):
     """fp64 oracle factored apply, b = 1, on this host's cores."""
-    import numpy as np
     import oracle as O
+    import hss_synth as syn
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    import hss_synth as syn
     m, n = W.shape
     k = O.topk_count(m, n, *cfg.frac)
     t_split = time.perf_counter()
@@ -106,82 +189,149 @@ def main():
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     sys.path.insert(0, ROOT)
-    import numpy as np
     import torch
 
     import hss_synth as syn
     import sparse_rank_linear_hss_amd as H
 
     torch.cuda.set_device(0)
-    cfg = syn.CONFIGS[2]
-    m, n = cfg.shapes[0]
-    r = cfg.rank[0]
-    W = syn.weight(cfg)
-    Wd = _bf16(W)
+    out = {}
 
-    # --- stage 1 on the GPU (timed separately; done once per weight) ---
-    sp = H.hss_split(Wd, "csr", frac=cfg.frac)
-    torch.cuda.synchronize()
+    # ---------------- headline: 4096^2 CSR 5 %, rank 256, decode ----------------
+    cfg = syn.CONFIGS[2]
+    W_np = syn.weight(cfg)
+    W = _bf16(W_np)
+    L = Layer(H, W, "csr", cfg.frac, cfg.rank[0], cfg.seed)
+    m, n = L.m, L.n
+    nnz_head, bytes_head, copies_head = L.split.k, L.w_bytes, L.copies
+    _log(f"4096^2 layer ready: nnz={nnz_head}, {copies_head} rotation copies")
+    ws = L.mats[0].workspace(16)
+    xs, ys = _acts(cfg, 1, 0, 16, m)
+    steps = args.steps
+    ms_graph = _time_graph(_apply_loop(H, L, xs, ys, ws), steps, args.warmup)
+    ms_stream = _time(_apply_loop(H, L, xs, ys, ws), steps, args.warmup)
+    ms_hot = _time_graph(_apply_loop(H, L, xs, ys, ws, rotate=False), steps, args.warmup)
+    gbs = bytes_head / (ms_graph * 1e-3) / 1e9
+    headline = {"ms_graph": ms_graph, "ms_stream": ms_stream, "ms_hot_graph": ms_hot,
+                "gbs_stream": bytes_head / (ms_stream * 1e-3) / 1e9, "rotation_copies": copies_head}
+    # split (offline, once per weight)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    split_ms = []
+    sms = []
     for _ in range(5):
         e0.record()
-        H.hss_split(Wd, "csr", frac=cfg.frac, check_finite=False)
+        H.hss_split(W, "csr", frac=cfg.frac, check_finite=False)
         e1.record()
         torch.cuda.synchronize()
-        split_ms.append(e0.elapsed_time(e1))
-    split_ms = sorted(split_ms)[len(split_ms) // 2]
-    nnz = sp.k
+        sms.append(e0.elapsed_time(e1))
+    split_ms = sorted(sms)[2]
 
-    U, V = syn.factors(m, n, r, "bf16", cfg.seed)
-    Ud, Vtd = _bf16(U), _bf16(V.T)
-    w_bytes = nnz * (2 + 4) + 4 * (m + 1) + (m + n) * r * 2        # compressed weights / apply
-    copies = max(1, math.ceil(args.rotation_bytes / w_bytes))
-    mats = []
-    for _ in range(copies):
-        mats.append(H.HSSMatrix("csr", m, n, torch.bfloat16, U=Ud.clone(), Vt=Vtd.clone(),
-                                row_ptr=sp.row_ptr.clone(), col_idx=sp.col_idx.clone(),
-                                values=sp.values.clone(), nnz=nnz))
-    results = {}
-    for b in cfg.batches:
-        xs = [_bf16(syn.activations(cfg, b, 0, step)) for step in range(16)]
-        ys = [torch.empty((b, m), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
-        ws = mats[0].workspace(b)
-        steps = args.steps if b == 1 else max(1, args.steps // 4)
-        cold = _time_applies(H, mats, xs, ys, ws, steps, args.warmup)
-        hot = _time_applies(H, mats[:1], xs, ys, ws, steps, args.warmup)
-        results[b] = {"ms_cold": cold, "ms_hot": hot}
+    extra = {}
+    if not args.only_headline:
+        # same layer, batch 16 (matrix cores)
+        xs16, ys16 = _acts(cfg, 16, 0, 4, m)
+        ms16 = _time_graph(_apply_loop(H, L, xs16, ys16, ws), max(1, steps // 4), 20)
+        extra["csr4096_b16"] = {"ms": ms16, "tokens_per_s": 16 / (ms16 * 1e-3),
+                                "gbs": bytes_head / (ms16 * 1e-3) / 1e9}
+        del L
+        torch.cuda.empty_cache()
 
-    b1 = results[1]["ms_cold"]
-    gbs = w_bytes / (b1 * 1e-3) / 1e9
+        # 11008 x 4096 2:4, rank 64, b = 1, 8, 64
+        c3 = syn.CONFIGS[3]
+        W3 = _bf16(syn.weight(c3))
+        L3 = Layer(H, W3, "2:4", c3.frac, c3.rank[0], c3.seed)
+        _log(f"2:4 layer ready: {L3.copies} rotation copies")
+        ws3 = L3.mats[0].workspace(64)
+        r3 = {}
+        for b in c3.batches:
+            xs3, ys3 = _acts(c3, b, 0, 4, L3.m)
+            ms3 = _time_graph(_apply_loop(H, L3, xs3, ys3, ws3), max(1, steps // 8), 20)
+            r3[f"b{b}"] = {"ms": ms3, "tokens_per_s": b / (ms3 * 1e-3),
+                           "gbs": L3.w_bytes / (ms3 * 1e-3) / 1e9,
+                           "hbm_frac": L3.w_bytes / (ms3 * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        extra["nm24_11008x4096"] = dict(r3, w_bytes=L3.w_bytes)
+        del L3, W3
+        torch.cuda.empty_cache()
+
+        # decoder layer: 7 projections per token, b = 1
+        c4 = syn.CONFIGS[4]
+        projs = []
+        for which in range(7):
+            Wp = _bf16(syn.weight(c4, which))
+            projs.append(Layer(H, Wp, "csr", c4.frac, c4.rank[which], c4.seed, which,
+                               rotation_bytes=GIB / 7))
+            del Wp
+        tok_bytes = sum(p.w_bytes for p in projs)
+        _log(f"decoder layer ready: {tok_bytes} compressed bytes per token")
+        ws4 = projs[0].mats[0].workspace(1)
+        xs4 = [[_bf16(syn.activations(c4, 1, w, s)) for s in range(4)] for w in range(7)]
+        ys4 = [torch.empty((1, p.m), dtype=torch.bfloat16, device="cuda") for p in projs]
+
+        def layer_step(i):
+            for w, p in enumerate(projs):
+                H.hss_apply(p.mats[i % len(p.mats)], xs4[w][i % 4], ys4[w], ws4)
+        ms4 = _time_graph(layer_step, c4.tokens, 5)
+        extra["decoder_layer_7proj"] = {"ms_per_token": ms4, "tokens_per_s": 1 / (ms4 * 1e-3),
+                                        "gbs": tok_bytes / (ms4 * 1e-3) / 1e9, "bytes_per_token": tok_bytes,
+                                        "tokens": c4.tokens}
+        del projs
+        torch.cuda.empty_cache()
+
+        # prefill: 8192^2 CSR 3 %, rank 512, b = 2048
+        c5 = syn.CONFIGS[5]
+        W5 = _bf16(syn.weight(c5))
+        L5 = Layer(H, W5, "csr", c5.frac, c5.rank[0], c5.seed, rotation_bytes=GIB / 4)
+        _log(f"8192^2 layer ready: {L5.copies} rotation copies")
+        b = c5.batches[0]
+        ws5 = L5.mats[0].workspace(b)
+        xs5, ys5 = _acts(c5, b, 0, 2, L5.m)
+        ms5 = _time(_apply_loop(H, L5, xs5, ys5, ws5), 10, 3)
+        # the low-rank products alone (same matrix with an empty S): their MFMA rate
+        lr = [H.HSSMatrix("csr", L5.m, L5.n, torch.bfloat16, U=mat.U, Vt=mat.Vt,
+                          row_ptr=torch.zeros(L5.m + 1, dtype=torch.int32, device="cuda"), nnz=0)
+              for mat in L5.mats]
+        lr_layer = type("LR", (), {"mats": lr})
+        ms5_lr = _time(_apply_loop(H, lr_layer, xs5, ys5, ws5), 10, 3)
+        lr_flops = 2.0 * b * L5.r * (L5.m + L5.n)
+        dense_equiv = 2.0 * b * L5.m * L5.n
+        extra["prefill_8192sq_b2048"] = {
+            "ms": ms5, "tokens_per_s": b / (ms5 * 1e-3),
+            "useful_tflops": L5.flops(b) / (ms5 * 1e-3) / 1e12,
+            "lowrank_only_ms": ms5_lr,
+            "lowrank_tflops": lr_flops / (ms5_lr * 1e-3) / 1e12,
+            "lowrank_mfma_frac": lr_flops / (ms5_lr * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "dense_equiv_tflops": dense_equiv / (ms5 * 1e-3) / 1e12}
+        del L5, lr, W5
+        torch.cuda.empty_cache()
+
     out = {
         "metric": METRIC,
-        "value": 1.0 / (b1 * 1e-3),
+        "value": 1.0 / (ms_graph * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
-        "ms_per_step": b1,
+        "ms_per_step": ms_graph,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "4096x4096 bf16, Student-t(3) x0.02 + 0.5% outliers x20, top-5% CSR "
-                               "(838,860 nnz) + rank-256 factors, decode b=1, cold HBM rotation",
-                   "m": m, "n": n, "nnz": nnz, "rank": r, "batch": 1, "rotation_copies": copies},
+                               "(838,860 nnz) + rank-256 factors, decode b=1, cold HBM rotation, HIP-graph replay",
+                   "m": m, "n": n, "nnz": nnz_head, "rank": cfg.rank[0], "batch": 1},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "hss_apply CSR decode (all kernels of one apply)",
-                     "algorithmic_bytes_per_launch": w_bytes},
+                     "kernel": "k_decode (one launch per decode token)",
+                     "algorithmic_bytes_per_launch": bytes_head},
         "compressed_gbs": gbs,
-        "batch16": {"ms_cold": results[16]["ms_cold"], "tokens_per_s": 16 / (results[16]["ms_cold"] * 1e-3),
-                    "gbs": (w_bytes + 0) / (results[16]["ms_cold"] * 1e-3) / 1e9},
-        "hot_cache": {"b1_ms": results[1]["ms_hot"], "b16_ms": results[16]["ms_hot"]},
-        "split": {"ms": split_ms, "w_read_gbs": m * n * 2 / (split_ms * 1e-3) / 1e9},
+        "headline_detail": headline,
+        "split_ms": split_ms,
+        "split_w_read_gbs": m * n * 2 / (split_ms * 1e-3) / 1e9,
     }
+    out.update(extra)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = _cpu_baseline(cfg, W, U, V, args.cpu_seconds)
+        U, V = syn.factors(m, n, cfg.rank[0], "bf16", cfg.seed)
+        out["cpu_baseline"] = _cpu_baseline(cfg, W_np, U, V, args.cpu_seconds)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

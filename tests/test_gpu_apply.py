@@ -217,3 +217,34 @@ def test_apply_shared_workspace_many_calls(H):
         i = (it // 2) % 3
         Y = H.hss_apply(mats[k], xs[k][i], ws=ws)
         assert O.bits_equal(to_host(Y), expect[k][i]), (it, k, i)
+
+
+@pytest.mark.parametrize("fmt,b", [("csr", 1), ("csr", 5), ("2:4", 1), ("csr", 32), ("2:4", 64)])
+def test_apply_graph_replay_matches_eager(H, fmt, b):
+    """hss_apply captured into a HIP graph: every replay (with eager calls on
+    the same workspace in between) reproduces the eager result bit for bit."""
+    import torch
+    dtype = O.BF16
+    m, n, r = 200, 256, 48
+    W = syn.random_matrix(m, n, dtype, seed=41, kind="t3")
+    ref = O.split_csr(W, dtype, O.topk_count(m, n, 5, 100)) if fmt == "csr" else O.split_24(W, dtype)
+    U, V = _factors(m, n, r, dtype, 42)
+    A = _matrix(H, fmt, dtype, m, n, ref, U, V)
+    xs = [to_dev(syn.random_matrix(b, n, dtype, seed=43 + i, kind="normal", scale=1.0), dtype) for i in range(3)]
+    ys = [torch.empty((b, m), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    ws = A.workspace(b)
+    expect = [to_host(H.hss_apply(A, x, ws=ws)) for x in xs]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for x, y in zip(xs, ys):
+            H.hss_apply(A, x, y, ws)
+    for rep in range(4):
+        for y in ys:
+            y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(3):
+            assert O.bits_equal(to_host(ys[i]), expect[i]), (rep, i)
+        # eager work on the same workspace between replays
+        assert O.bits_equal(to_host(H.hss_apply(A, xs[rep % 3], ws=ws)), expect[rep % 3])
