@@ -51,6 +51,9 @@ def _args():
                     help="budget of the CPU-oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-headline", action="store_true", help="skip the other workloads")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run three plain 256 MiB device-to-device copies (a known-size "
+                         "reference for hardware byte counters)")
     return ap.parse_args()
 
 
@@ -196,6 +199,13 @@ def main():
 
     torch.cuda.set_device(0)
     out = {}
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---------------- headline: 4096^2 CSR 5 %, rank 256, decode ----------------
     cfg = syn.CONFIGS[2]
