@@ -67,6 +67,7 @@ struct DecodeArgs {
   uint32_t* ctl;  // control region
   int64_t nnz;    // CSR entries
   int x_lds;      // X staged in LDS
+  int x_pad;      // staged X padded (16 bytes after every 64), for the 2:4 fast path
   int vec;        // X, Vt rows 16-byte aligned: vector dot products
   int vec_csr;    // CSR chunks: col_idx 16-byte, values 4*elem aligned, nnz >= 4
   int nm_fast;    // bf16 2:4 with n % 32 == 0 and aligned rows: vector words
@@ -113,8 +114,11 @@ __device__ __forceinline__ float red_sum(float (*red)[BC], int c) {
 
 // Block-wide T[c][l] = Vt[l,:] . X[c,:] for c < bc (all 256 threads).  Thread
 // t covers 16-byte vectors q = t + 256k; TV of them (per operand) are loaded
-// before any is used.  Leaves the four wave sums in red[w][c] (the caller
-// adds them in a fixed order) after a barrier.
+// before any is used.  Slots past the end load vector 0 (one address for the
+// whole wave, a single request) and are skipped at use; clamping them to the
+// last vector instead would send every block to the same L2 line.  Leaves
+// the four wave sums in red[w][c] (the caller adds them in a fixed order)
+// after a barrier.
 template <int DT, int BC>
 __device__ __forceinline__ void t_row(const typename Elem<DT>::bits_t* __restrict__ v,
                                       const typename Elem<DT>::bits_t* __restrict__ xsrc, int n,
@@ -134,11 +138,14 @@ __device__ __forceinline__ void t_row(const typename Elem<DT>::bits_t* __restric
       u32x4 vv[TV], xv[TV][BC];
 #pragma unroll
       for (int k = 0; k < TV; ++k) {
-        const int qc = min(base + t + 256 * k, nv - 1);
-        vv[k] = __builtin_nontemporal_load(v4 + qc);
+        if (base + 256 * k < nv) {  // block-uniform: skip slices wholly past the end
+          const int q = base + t + 256 * k;
+          const int qc = q < nv ? q : 0;
+          vv[k] = __builtin_nontemporal_load(v4 + qc);
 #pragma unroll
-        for (int c = 0; c < BC; ++c)
-          xv[k][c] = reinterpret_cast<const u32x4*>(xsrc + (int64_t)min(c, bc - 1) * n)[qc];
+          for (int c = 0; c < BC; ++c)
+            if (c < bc) xv[k][c] = reinterpret_cast<const u32x4*>(xsrc + (int64_t)c * n)[qc];
+        }
       }
 #pragma unroll
       for (int k = 0; k < TV; ++k) {
@@ -170,7 +177,10 @@ __device__ __forceinline__ void t_row(const typename Elem<DT>::bits_t* __restric
 // CSR rows.  Lane L of pass p holds entries [a0 + 4L + 256p, +4) of a row,
 // a0 = row start rounded down to a multiple of 4 (16-byte aligned columns);
 // entries outside [start, end) are masked.  Pass-0 chunks of all the wave's
-// rows are loaded right after the row bounds return.
+// rows are loaded right after the row bounds return.  The array's last
+// partial chunk (nnz % 4 entries) cannot be read as a vector; lanes 0..3
+// load its entries one by one at kernel start (clamped, so always valid) and
+// the chunk reads them back with readlane -- no load sits in the consume path.
 // ---------------------------------------------------------------------------
 template <int DT, int RPW>
 struct CsrChunks {
@@ -179,7 +189,17 @@ struct CsrChunks {
   int st[RPW], en[RPW], e0[RPW];
   u32x4 cq[RPW];
   vchunk_t vq[RPW];
+  uint32_t tcol, tval;  // lane k < 4: entry (nnz & ~3) + k of the array tail
 };
+
+template <int DT, int RPW>
+__device__ __forceinline__ void csr_tail_issue(const DecodeArgs& a, CsrChunks<DT, RPW>& ch) {
+  using bits_t = typename Elem<DT>::bits_t;
+  const int64_t e = (a.nnz & ~(int64_t)3) + (lane_id() & 3);
+  const int64_t ec = e < a.nnz - 1 ? e : a.nnz - 1;
+  ch.tcol = (uint32_t)__builtin_nontemporal_load(a.col_idx + ec);
+  ch.tval = (uint32_t)__builtin_nontemporal_load(static_cast<const bits_t*>(a.vals) + ec);
+}
 
 template <int DT, int RPW>
 __device__ __forceinline__ void csr_issue(const DecodeArgs& a, const int (&rb)[RPW + 1],
@@ -202,14 +222,23 @@ __device__ __forceinline__ void csr_issue(const DecodeArgs& a, const int (&rb)[R
   }
 }
 
-// acc += the 4 entries of one chunk that fall in [st, en).
+// One chunk (entries e..e+3): the four X values are gathered with no branch
+// (entries outside [st, en) read column 0) so the LDS reads go out back to
+// back; csr_chunk_fma then adds the in-range products, in entry order.
+template <int DT, int BC>
+struct ChunkX {
+  uint32_t vb[4];   // value bits
+  bool in[4];       // entry in [st, en)
+  float x[4][BC];   // gathered X
+};
+
 template <int DT, int BC, typename VC>
-__device__ __forceinline__ void csr_chunk(const DecodeArgs& a, int e, int st, int en, const u32x4& cc,
-                                          const VC& vv, const typename Elem<DT>::bits_t* __restrict__ xsrc,
-                                          float (&acc)[BC]) {
+__device__ __forceinline__ void csr_chunk_gather(const DecodeArgs& a, int e, int st, int en, const u32x4& cc,
+                                                 const VC& vv, uint32_t tcol, uint32_t tval,
+                                                 const typename Elem<DT>::bits_t* __restrict__ xsrc,
+                                                 ChunkX<DT, BC>& g) {
   using bits_t = typename Elem<DT>::bits_t;
-  const bits_t* __restrict__ vals = static_cast<const bits_t*>(a.vals);
-  const bool whole = e + 4 <= a.nnz;  // else: the array's tail, read element-wise
+  const bool whole = e + 4 <= a.nnz;  // else: the array's tail, from lanes 0..3
   const int cols[4] = {(int)cc.x, (int)cc.y, (int)cc.z, (int)cc.w};
   uint32_t vb4[4];
   if constexpr (sizeof(bits_t) == 2) {
@@ -220,12 +249,25 @@ __device__ __forceinline__ void csr_chunk(const DecodeArgs& a, int e, int st, in
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int ek = e + k;
-    if (ek >= st && ek < en) {
-      const int ck = whole ? cols[k] : a.col_idx[ek];
-      const float vk = fval<DT>(whole ? vb4[k] : (uint32_t)vals[ek]);
+    g.in[k] = ek >= st && ek < en;
+    const int ck = whole ? cols[k] : __builtin_amdgcn_readlane((int)tcol, k);
+    g.vb[k] = whole ? vb4[k] : (uint32_t)__builtin_amdgcn_readlane((int)tval, k);
+    const int cx = g.in[k] ? ck : 0;
 #pragma unroll
-      for (int c = 0; c < BC; ++c)
-        if (c < a.bc) acc[c] = fmaf(vk, fval<DT>(xsrc[(int64_t)c * a.n + ck]), acc[c]);
+    for (int c = 0; c < BC; ++c)
+      g.x[k][c] = fval<DT>(xsrc[(int64_t)min(c, a.bc - 1) * a.n + cx]);
+  }
+}
+
+template <int DT, int BC>
+__device__ __forceinline__ void csr_chunk_fma(const ChunkX<DT, BC>& g, float (&acc)[BC]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float vk = fval<DT>(g.vb[k]);
+#pragma unroll
+    for (int c = 0; c < BC; ++c) {
+      const float f = fmaf(vk, g.x[k][c], acc[c]);
+      acc[c] = g.in[k] ? f : acc[c];
     }
   }
 }
@@ -239,6 +281,20 @@ __device__ __forceinline__ void csr_consume(const DecodeArgs& a, CsrChunks<DT, R
   const int lane = lane_id();
   const bits_t* __restrict__ vals = static_cast<const bits_t*>(a.vals);
   const int64_t last = ((a.nnz - 4) & ~(int64_t)3);
+  float accs[RPW][BC];
+  if (a.vec_csr) {
+    // first chunks of all rows: every gather first, then the products
+    ChunkX<DT, BC> g[RPW];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i)
+      csr_chunk_gather<DT, BC>(a, ch.e0[i], ch.st[i], ch.en[i], ch.cq[i], ch.vq[i], ch.tcol, ch.tval, xsrc, g[i]);
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+#pragma unroll
+      for (int c = 0; c < BC; ++c) accs[i][c] = 0.f;
+      csr_chunk_fma<DT, BC>(g[i], accs[i]);
+    }
+  }
 #pragma unroll
   for (int i = 0; i < RPW; ++i) {
     float acc[BC];
@@ -246,13 +302,16 @@ __device__ __forceinline__ void csr_consume(const DecodeArgs& a, CsrChunks<DT, R
     for (int c = 0; c < BC; ++c) acc[c] = 0.f;
     const int st = ch.st[i], en = ch.en[i];
     if (a.vec_csr) {
-      if (ch.e0[i] < en) csr_chunk<DT, BC>(a, ch.e0[i], st, en, ch.cq[i], ch.vq[i], xsrc, acc);
+#pragma unroll
+      for (int c = 0; c < BC; ++c) acc[c] = accs[i][c];
       for (int base = (st & ~3) + 256; base < en; base += 256) {  // rows longer than 256 - 3
         const int e = base + 4 * lane;
         const int64_t ec = e < last ? e : last;
         const u32x4 cc = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.col_idx + ec));
         const vchunk_t vv = __builtin_nontemporal_load(reinterpret_cast<const vchunk_t*>(vals + ec));
-        if (e < en) csr_chunk<DT, BC>(a, e, st, en, cc, vv, xsrc, acc);
+        ChunkX<DT, BC> gl;
+        csr_chunk_gather<DT, BC>(a, e, st, en, cc, vv, ch.tcol, ch.tval, xsrc, gl);
+        csr_chunk_fma<DT, BC>(gl, acc);
       }
     } else {
       for (int p = st + lane; p < en; p += 64) {
@@ -305,10 +364,22 @@ __device__ __forceinline__ void nm_issue(const DecodeArgs& a, int row0, NmWords<
   }
 }
 
-template <int BC>
-__device__ __forceinline__ void nm_word_fast(uint32_t mw, const u32x4 (&vv)[2],
-                                             const uint16_t* __restrict__ xsrc, int n, int bc, int c0,
-                                             float (&acc)[BC]) {
+// X chunk of one 2:4 word (32 columns) of batch column c: four 16-byte
+// vectors, from the padded LDS copy (pad: 16 bytes after every 64, so the
+// lanes' 64-byte-strided reads fall on distinct banks) or from global X.
+__device__ __forceinline__ void nm_xload(const uint16_t* __restrict__ xsrc, int n, int c, int c0, int pad,
+                                         u32x4 (&xq)[4]) {
+  const int64_t v = ((int64_t)c * n + c0) >> 3;  // a multiple of 4
+  const u32x4* xp = reinterpret_cast<const u32x4*>(xsrc) + (pad ? v + (v >> 2) : v);
+#pragma unroll
+  for (int h = 0; h < 4; ++h) xq[h] = xp[h];
+}
+
+// acc += the word's 16 products with one column's X chunk (8 groups of 4
+// columns, 2 kept values each), groups in ascending order; nothing is added
+// unless `valid`.
+__device__ __forceinline__ void nm_word_dot(uint32_t mw, const u32x4 (&vv)[2], const u32x4 (&xq)[4],
+                                            bool valid, float& acc) {
   const uint32_t vw[8] = {vv[0].x, vv[0].y, vv[0].z, vv[0].w, vv[1].x, vv[1].y, vv[1].z, vv[1].w};
   uint32_t sel[8];
 #pragma unroll
@@ -318,23 +389,16 @@ __device__ __forceinline__ void nm_word_fast(uint32_t mw, const u32x4 (&vv)[2],
     const uint32_t i1 = (mw >> (4 * g + 2)) & 3u;
     sel[g] = (i0 | (i1 << 16)) * 0x0202u + 0x01000100u;
   }
+  const uint32_t xw[16] = {xq[0].x, xq[0].y, xq[0].z, xq[0].w, xq[1].x, xq[1].y, xq[1].z, xq[1].w,
+                           xq[2].x, xq[2].y, xq[2].z, xq[2].w, xq[3].x, xq[3].y, xq[3].z, xq[3].w};
+  float f = acc;
 #pragma unroll
-  for (int c = 0; c < BC; ++c) {
-    if (c < bc) {
-      const u32x4* xp = reinterpret_cast<const u32x4*>(xsrc + (int64_t)c * n + c0);
-      u32x4 xq[4];
-#pragma unroll
-      for (int h = 0; h < 4; ++h) xq[h] = xp[h];
-      const uint32_t xw[16] = {xq[0].x, xq[0].y, xq[0].z, xq[0].w, xq[1].x, xq[1].y,
-                               xq[1].z, xq[1].w, xq[2].x, xq[2].y, xq[2].z, xq[2].w,
-                               xq[3].x, xq[3].y, xq[3].z, xq[3].w};
-#pragma unroll
-      for (int g = 0; g < 8; ++g)
-        acc[c] = dot2_bf16(vw[g], __builtin_amdgcn_perm(xw[2 * g + 1], xw[2 * g], sel[g]), acc[c]);
-    }
-  }
+  for (int g = 0; g < 8; ++g) f = dot2_bf16(vw[g], __builtin_amdgcn_perm(xw[2 * g + 1], xw[2 * g], sel[g]), f);
+  acc = valid ? f : acc;
 }
 
+// Fast path: lane L owns words L + 64k of every row of the wave, so the X
+// chunk of a word (per batch column) is read once and used for all RPW rows.
 template <int DT, int BC, int RPW>
 __device__ __forceinline__ void nm_consume(const DecodeArgs& a, int row0, const NmWords<RPW>& nw,
                                            const typename Elem<DT>::bits_t* __restrict__ xsrc,
@@ -343,33 +407,58 @@ __device__ __forceinline__ void nm_consume(const DecodeArgs& a, int row0, const 
   const int lane = lane_id();
   const int m = a.m, n = a.n, bc = a.bc;
   const int words = (n + 31) >> 5;
+  float acc[RPW][BC];
 #pragma unroll
-  for (int i = 0; i < RPW; ++i) {
-    const int row = row0 + i;
-    float acc[BC];
+  for (int i = 0; i < RPW; ++i)
 #pragma unroll
-    for (int c = 0; c < BC; ++c) acc[c] = 0.f;
-    if (row < m) {
-      const uint32_t* __restrict__ Mr = a.meta + (int64_t)row * words;
-      const bits_t* __restrict__ Vr = static_cast<const bits_t*>(a.nmv) + (int64_t)row * (n >> 1);
-      if constexpr (DT == HSS_BF16) {
-        if (a.nm_fast) {
+    for (int c = 0; c < BC; ++c) acc[i][c] = 0.f;
+  if constexpr (DT == HSS_BF16) {
+    if (a.nm_fast) {
+      const uint16_t* __restrict__ x16 = reinterpret_cast<const uint16_t*>(xsrc);
 #pragma unroll
-          for (int k = 0; k < kWPL; ++k) {
-            const int wd = lane + 64 * k;
-            if (wd < words) nm_word_fast<BC>(nw.mw[i][k], nw.vv[i][k], xsrc, n, bc, wd * 32, acc);
-          }
-          for (int base = 64 * kWPL; base < words; base += 64) {  // words beyond the prefetched ones
-            const int wd = base + lane;
-            const int wdc = min(wd, words - 1);
-            const uint32_t mw = __builtin_nontemporal_load(Mr + wdc);
-            const u32x4* vp = reinterpret_cast<const u32x4*>(Vr + wdc * 16);
-            const u32x4 vv[2] = {__builtin_nontemporal_load(vp), __builtin_nontemporal_load(vp + 1)};
-            if (wd < words) nm_word_fast<BC>(mw, vv, xsrc, n, bc, wd * 32, acc);
-          }
+      for (int k = 0; k < kWPL; ++k) {
+        const int wd = lane + 64 * k;
+        const bool wv = wd < words;
+#pragma unroll
+        for (int c = 0; c < BC; ++c) {
+          u32x4 xq[4];
+          nm_xload(x16, n, min(c, bc - 1), (wv ? wd : 0) * 32, a.x_pad, xq);
+#pragma unroll
+          for (int i = 0; i < RPW; ++i) nm_word_dot(nw.mw[i][k], nw.vv[i][k], xq, wv, acc[i][c]);
         }
       }
-      if (!(DT == HSS_BF16 && a.nm_fast)) {
+      for (int base = 64 * kWPL; base < words; base += 64) {  // words beyond the prefetched ones
+        const int wd = base + lane;
+        const bool wv = wd < words;
+        const int wdc = wv ? wd : words - 1;
+        uint32_t mw[RPW];
+        u32x4 vv[RPW][2];
+#pragma unroll
+        for (int i = 0; i < RPW; ++i) {
+          const int64_t rowc = min(row0 + i, m - 1);
+          mw[i] = __builtin_nontemporal_load(a.meta + rowc * words + wdc);
+          const u32x4* vp = reinterpret_cast<const u32x4*>(static_cast<const bits_t*>(a.nmv) +
+                                                           rowc * (n >> 1) + wdc * 16);
+          vv[i][0] = __builtin_nontemporal_load(vp);
+          vv[i][1] = __builtin_nontemporal_load(vp + 1);
+        }
+#pragma unroll
+        for (int c = 0; c < BC; ++c) {
+          u32x4 xq[4];
+          nm_xload(x16, n, min(c, bc - 1), wdc * 32, a.x_pad, xq);
+#pragma unroll
+          for (int i = 0; i < RPW; ++i) nm_word_dot(mw[i], vv[i], xq, wv, acc[i][c]);
+        }
+      }
+    }
+  }
+  if (!(DT == HSS_BF16 && a.nm_fast)) {
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int row = row0 + i;
+      if (row < m) {
+        const uint32_t* __restrict__ Mr = a.meta + (int64_t)row * words;
+        const bits_t* __restrict__ Vr = static_cast<const bits_t*>(a.nmv) + (int64_t)row * (n >> 1);
         for (int wd = lane; wd < words; wd += 64) {
           const uint32_t mw = Mr[wd];
           const int c0 = wd * 32;
@@ -383,25 +472,28 @@ __device__ __forceinline__ void nm_consume(const DecodeArgs& a, int row0, const 
 #pragma unroll
             for (int c = 0; c < BC; ++c) {
               if (c < bc) {
-                acc[c] = fmaf(v0, fval<DT>(xsrc[(int64_t)c * n + j0]), acc[c]);
-                acc[c] = fmaf(v1, fval<DT>(xsrc[(int64_t)c * n + j1]), acc[c]);
+                acc[i][c] = fmaf(v0, fval<DT>(xsrc[(int64_t)c * n + j0]), acc[i][c]);
+                acc[i][c] = fmaf(v1, fval<DT>(xsrc[(int64_t)c * n + j1]), acc[i][c]);
               }
             }
           }
         }
       }
     }
-#pragma unroll
-    for (int c = 0; c < BC; ++c) ssum[i][c] = wave_sum(acc[c]);
   }
+#pragma unroll
+  for (int i = 0; i < RPW; ++i)
+#pragma unroll
+    for (int c = 0; c < BC; ++c) ssum[i][c] = wave_sum(acc[i][c]);
 }
 
 // ---------------------------------------------------------------------------
 // U entries of this wave's rows.  VECU (bf16, r % 4 == 0): lane L holds
 // l = 4L + 256q .. +3 (q < 2 covers r <= 512) as 8-byte vectors; otherwise
 // lane L holds l = L + 64q (q < 8).  Larger r continues in the epilogue.
-// Out-of-range slots load a clamped valid address and are skipped at use, so
-// nothing waits for these loads before the epilogue.
+// Out-of-range slots load a clamped valid address (one per wave) and are
+// skipped at use: a load under a branch would be copied into its merged
+// value right away, making the wave wait for it there.
 // ---------------------------------------------------------------------------
 static constexpr int kUPL = 8;
 
@@ -419,7 +511,7 @@ __device__ __forceinline__ void u_issue(const DecodeArgs& a, int row0, uint32_t 
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int l = 4 * lane + 256 * q;
-        const int lc = min(l, r - 4);
+        const int lc = min(l, r - 4);  // past the row: one address per wave
         const u32x2 u2 = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(U + rowc * r + lc));
         ub[i][2 * q] = u2.x;  // masked at use (the epilogue skips l >= r, row >= m)
         ub[i][2 * q + 1] = u2.y;
@@ -448,22 +540,26 @@ __device__ __forceinline__ void u_epilogue(const DecodeArgs& a, int row0, const 
     for (int c = 0; c < BC; ++c) acc[i][c] = 0.f;
     if (row >= m) continue;
     if constexpr (VECU) {
+      // T reads first (clamped index, no branch), then the masked products
+      float4 tv[2][BC];
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        const int l = 4 * lane + 256 * q;
-        if (l < r) {
-          const float u0 = bf16lo(ub[i][2 * q]), u1 = bf16hi(ub[i][2 * q]);
-          const float u2 = bf16lo(ub[i][2 * q + 1]), u3 = bf16hi(ub[i][2 * q + 1]);
+        const int lc = min(4 * lane + 256 * q, r - 4);
 #pragma unroll
-          for (int c = 0; c < BC; ++c) {
-            if (c < bc) {
-              const float4 tv = *reinterpret_cast<const float4*>(Ts + c * r + l);
-              acc[i][c] = fmaf(u0, tv.x, acc[i][c]);
-              acc[i][c] = fmaf(u1, tv.y, acc[i][c]);
-              acc[i][c] = fmaf(u2, tv.z, acc[i][c]);
-              acc[i][c] = fmaf(u3, tv.w, acc[i][c]);
-            }
-          }
+        for (int c = 0; c < BC; ++c) tv[q][c] = *reinterpret_cast<const float4*>(Ts + min(c, bc - 1) * r + lc);
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const bool in = 4 * lane + 256 * q < r;
+        const float u0 = bf16lo(ub[i][2 * q]), u1 = bf16hi(ub[i][2 * q]);
+        const float u2 = bf16lo(ub[i][2 * q + 1]), u3 = bf16hi(ub[i][2 * q + 1]);
+#pragma unroll
+        for (int c = 0; c < BC; ++c) {
+          float f = fmaf(u0, tv[q][c].x, acc[i][c]);
+          f = fmaf(u1, tv[q][c].y, f);
+          f = fmaf(u2, tv[q][c].z, f);
+          f = fmaf(u3, tv[q][c].w, f);
+          acc[i][c] = in ? f : acc[i][c];
         }
       }
       for (int l = 4 * lane + 512; l < r; l += 256) {
@@ -476,14 +572,21 @@ __device__ __forceinline__ void u_epilogue(const DecodeArgs& a, int row0, const 
         }
       }
     } else {
+      float tq[kUPL][BC];
 #pragma unroll
       for (int q = 0; q < kUPL; ++q) {
-        const int l = lane + 64 * q;
-        if (l < r) {
-          const float u = fval<DT>(ub[i][q]);
+        const int lc = min(lane + 64 * q, r - 1);
 #pragma unroll
-          for (int c = 0; c < BC; ++c)
-            if (c < bc) acc[i][c] = fmaf(u, Ts[c * r + l], acc[i][c]);
+        for (int c = 0; c < BC; ++c) tq[q][c] = Ts[min(c, bc - 1) * r + lc];
+      }
+#pragma unroll
+      for (int q = 0; q < kUPL; ++q) {
+        const bool in = lane + 64 * q < r;
+        const float u = fval<DT>(ub[i][q]);
+#pragma unroll
+        for (int c = 0; c < BC; ++c) {
+          const float f = fmaf(u, tq[q][c], acc[i][c]);
+          acc[i][c] = in ? f : acc[i][c];
         }
       }
       for (int l = lane + 64 * kUPL; l < r; l += 64) {
@@ -497,21 +600,43 @@ __device__ __forceinline__ void u_epilogue(const DecodeArgs& a, int row0, const 
 }
 
 // ---------------------------------------------------------------------------
-// Arrival count: called once per block by thread 0, strictly after the block's
-// epoch load returned (the inline wait).  The first level spreads the blocks
-// over 64 counters; sub_last/top carry the second level to the block's end.
-__device__ __forceinline__ void arrive(const DecodeArgs& a, int G, int nsub, int sub, bool& sub_last,
-                                       uint32_t& top) {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  const uint32_t arrived = __hip_atomic_fetch_add(a.ctl + kCtlSub0 + kCtlSubStride * sub, 1u,
-                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  sub_last = arrived == (uint32_t)((G - sub + nsub - 1) / nsub) - 1;
-  if (sub_last)
-    top = __hip_atomic_fetch_add(a.ctl + kCtlTop, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Arrival count, in three stages so that no atomic round trip sits on a
+// block's critical path.  Thread 0 of every block:
+//   arrive_issue  once its epoch load has returned, bumps one of the 64
+//                 spread counters.  An empty asm that reads the epoch register
+//                 and yields an opaque zero offset orders the add after that
+//                 load and keeps the compiler from rewriting the single-lane
+//                 add as a wave scan that waits for the result at once;
+//   arrive_check  later, reads that result; the last arrival on a spread
+//                 counter bumps the top counter;
+//   finish_epoch  at the block's end, the last arrival overall (every block
+//                 has read the epoch) clears the counters and advances the
+//                 epoch for the next call, which starts after this kernel.
+// ---------------------------------------------------------------------------
+// The call epoch, read coherently at device scope (from L2): caches above L2
+// are not guaranteed to be clean between launches.
+__device__ __forceinline__ uint32_t load_epoch(const DecodeArgs& a) {
+  return __hip_atomic_load(a.ctl + kCtlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Last arrival overall: every block has read the epoch, so advance it and
-// clear the counters for the next call (which starts after this kernel).
+__device__ __forceinline__ uint32_t arrive_issue(const DecodeArgs& a, int sub, uint32_t epoch) {
+  uint32_t off = 0;
+  asm volatile("" : "+v"(off) : "v"(epoch));
+  return __hip_atomic_fetch_add(a.ctl + kCtlSub0 + kCtlSubStride * sub + off, 1u, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ bool arrive_check(const DecodeArgs& a, int G, int nsub, int sub, uint32_t arrived,
+                                             uint32_t& top) {
+  const bool sub_last = arrived == (uint32_t)((G - sub + nsub - 1) / nsub) - 1;
+  if (sub_last) {
+    uint32_t off = 0;
+    asm volatile("" : "+v"(off));  // opaque: keeps the add a plain single-lane atomic
+    top = __hip_atomic_fetch_add(a.ctl + kCtlTop + off, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return sub_last;
+}
+
 __device__ __forceinline__ void finish_epoch(const DecodeArgs& a, int nsub, bool sub_last, uint32_t top,
                                              uint32_t tag) {
   if (sub_last && top == (uint32_t)nsub - 1) {
@@ -525,15 +650,34 @@ __device__ __forceinline__ void finish_epoch(const DecodeArgs& a, int nsub, bool
 
 // Grid: blocks [0, r) are T producers (row l of T each; the lowest block ids
 // are dispatched first), the rest own 4*RPW output rows each.
-template <int DT, int FMT, int BC, int RPW, bool VECU>
-__global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
+//
+// FAST instances are launched only when r > 0, X is staged through registers
+// into LDS in one pass, and the sparse operand takes its vector path; with
+// those flags fixed at compile time every load of the prologue is issued
+// unconditionally, so the compiler can count outstanding loads exactly and
+// never waits for the (dependent, slowest) sparse loads before it must.
+static constexpr int kXR = 4;      // staged X vectors per thread held in registers
+static constexpr int kXRFast = 2;  // FAST: exactly this many, no branches (bc * n <= 4096 bf16)
+
+template <int DT, int FMT, int BC, int RPW, bool VECU, bool FAST>
+__global__ __launch_bounds__(256) void k_decode(DecodeArgs a_in) {
   using bits_t = typename Elem<DT>::bits_t;
+  DecodeArgs a = a_in;
+  if constexpr (FAST) {
+    a.x_lds = 1;
+    a.vec = 1;
+    a.vec_csr = FMT == HSS_FMT_CSR;
+    a.nm_fast = FMT == HSS_FMT_2OF4;
+    a.x_pad = FMT == HSS_FMT_2OF4;
+    __builtin_assume(a.r > 0);
+    __builtin_assume(a.bc * a.n > 0 && a.bc * a.n <= 256 * kXRFast * (16 / (int)sizeof(bits_t)));
+  }
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ float red[4][BC];
   __shared__ uint32_t epoch_sh;
 
   const int t = threadIdx.x;
-  const int w = t >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave index, uniform
   const int m = a.m, n = a.n, r = a.r, bc = a.bc;
   const int G = (int)gridDim.x;
   const bits_t* __restrict__ X = static_cast<const bits_t*>(a.X);
@@ -544,16 +688,15 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
   const bits_t* xsrc = a.x_lds ? xs : X;
   const int nsub = G < kNumSub ? G : kNumSub;
   const int sub = (int)blockIdx.x % nsub;
-  bool sub_last = false;
-  uint32_t top = 0;
 
   // ---- T producer: Vt row l and X loaded together, published tagged into
   //      every replica ----
   if ((int)blockIdx.x < r) {
     const int l = blockIdx.x;
-    const uint32_t e = __hip_atomic_load(a.ctl + kCtlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t e = load_epoch(a);
     t_row<DT, BC>(Vt + (int64_t)l * n, X, n, bc, a.vec, red);
     if (t == 0) {
+      const uint32_t arrived = arrive_issue(a, sub, e);
 #pragma unroll
       for (int c = 0; c < BC; ++c) {
         if (c < bc) {
@@ -563,58 +706,103 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
-      arrive(a, G, nsub, sub, sub_last, top);
+      uint32_t top = 0;
+      const bool sub_last = arrive_check(a, G, nsub, sub, arrived, top);
       finish_epoch(a, nsub, sub_last, top, tag_of(e));
     }
     return;
   }
 
   // ---- row blocks ----
-  const int row0 = (((int)blockIdx.x - r) * 4 + w) * RPW;
+  const int row0 = (((int)blockIdx.x - r) * 4 + w) * RPW;  // wave-uniform
 
-  // batch 1: row bounds
+  // row bounds: uniform addresses, scalar loads (own counter, so waiting for
+  // them does not wait for the vector loads below)
   int rb[RPW + 1];
   if constexpr (FMT == HSS_FMT_CSR) {
 #pragma unroll
-    for (int i = 0; i <= RPW; ++i) rb[i] = a.row_ptr[min(max(row0 + i, 0), m)];
+    for (int i = 0; i <= RPW; ++i) rb[i] = a.row_ptr[min(row0 + i, m)];
   }
 
-  // batch 2: everything else, issued before any of it is used
-  CsrChunks<DT, RPW> ch;
-  if constexpr (FMT == HSS_FMT_CSR) csr_issue<DT, RPW>(a, rb, ch);
-  NmWords<RPW> nw;
-  if constexpr (FMT == HSS_FMT_2OF4) nm_issue<DT, RPW>(a, row0, nw);
-  constexpr int NV = 16 / sizeof(bits_t);
-  constexpr int kXR = 4;  // staged X vectors per thread held in registers
-  const bool xreg = a.x_lds && a.vec;
-  const int xvecs = xreg ? bc * n / NV : 0;
-  u32x4 xr[kXR];
-  if (xvecs > 0) {
-#pragma unroll
-    for (int k = 0; k < kXR; ++k) xr[k] = reinterpret_cast<const u32x4*>(X)[min(t + 256 * k, xvecs - 1)];
-  }
+  // vector loads that depend on nothing: epoch, U rows, 2:4 words
+  uint32_t epoch = 0;
+  if (r > 0) epoch = load_epoch(a);
   uint32_t ub[RPW][kUPL];
   if (r > 0) u_issue<DT, RPW, VECU>(a, row0, ub);
-  uint32_t epoch = 0;
-  if (r > 0) epoch = __hip_atomic_load(a.ctl + kCtlEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  for (int q = t; q < (r + 31) / 32; q += 256) miss[q] = 0;
+  NmWords<RPW> nw;
+  if constexpr (FMT == HSS_FMT_2OF4) nm_issue<DT, RPW>(a, row0, nw);
+  CsrChunks<DT, RPW> ch;
+  if constexpr (FMT == HSS_FMT_CSR) {
+    if (a.vec_csr) csr_tail_issue<DT, RPW>(a, ch);
+  }
 
-  // X -> LDS; arrival
-  if (xvecs > 0) {
+  // CSR chunks: the one dependent load
+  if constexpr (FMT == HSS_FMT_CSR) csr_issue<DT, RPW>(a, rb, ch);
+
+  // X for LDS, issued last: writing it to LDS waits for every load above,
+  // all of which the sparse part needs right after the barrier anyway.
+  constexpr int NV = 16 / sizeof(bits_t);
+  const bool xreg = a.x_lds && a.vec;
+  const int xvecs = xreg ? bc * n / NV : 0;
+  constexpr int XR = FAST ? kXRFast : kXR;
+  if constexpr (FAST) __builtin_assume(xvecs > 0 && xvecs <= 256 * XR);
+  // Lanes past the end read vector 0: one address for the whole wave (a
+  // single request, served from L1), where clamping to the last vector would
+  // pile every block onto one L2 line.  FAST loads its XR vectors with no
+  // branch at all (a branch around them makes the compiler hold several
+  // times the registers there).
+  u32x4 xr[XR];
+  if (FAST || xvecs > 0) {
+#pragma unroll
+    for (int k = 0; k < XR; ++k) {
+      if (FAST || 256 * k < xvecs) {  // block-uniform
+        const int q = t + 256 * k;
+        xr[k] = reinterpret_cast<const u32x4*>(X)[q < xvecs ? q : 0];
+      }
+    }
+  }
+
+  if (r > 0 && t == 0) epoch_sh = epoch;
+  {
     u32x4* dst = reinterpret_cast<u32x4*>(xs);
 #pragma unroll
-    for (int k = 0; k < kXR; ++k)
-      if (t + 256 * k < xvecs) dst[t + 256 * k] = xr[k];
-    for (int q = t + 256 * kXR; q < xvecs; q += 256) dst[q] = reinterpret_cast<const u32x4*>(X)[q];
+    for (int k = 0; k < XR; ++k) {
+      const int q = t + 256 * k;
+      if (q < xvecs) dst[a.x_pad ? q + (q >> 2) : q] = xr[k];
+    }
+  }
+  for (int q = t; q < (r + 31) / 32; q += 256) miss[q] = 0;
+  if (xvecs > 0) {
+    u32x4* dst = reinterpret_cast<u32x4*>(xs);
+    for (int q = t + 256 * XR; q < xvecs; q += 256)
+      dst[a.x_pad ? q + (q >> 2) : q] = reinterpret_cast<const u32x4*>(X)[q];
   } else if (a.x_lds) {
     for (int q = t; q < bc * n; q += 256) xs[q] = X[q];
   }
-  if (r > 0 && t == 0) {
-    epoch_sh = epoch;
-    arrive(a, G, nsub, sub, sub_last, top);
-  }
+  // Arrival right before the barrier: every load above has returned (X went
+  // last), so nothing later waits for this atomic by accident.
+  uint32_t arrived = 0;
+  if (r > 0 && t == 0) arrived = arrive_issue(a, sub, epoch);
   __syncthreads();
   const uint32_t tag = tag_of(epoch_sh);
+
+  // T words, first pass.  FAST: issued now and read after the sparse part,
+  // which then has no memory wait that could catch them (its operands all
+  // arrived before the barrier).  The loads take no branch -- a load under a
+  // branch is copied into its merged value at once, which waits for it --
+  // so slots past the end re-read a word this block reads anyway.  A word
+  // still stale here is re-read below.
+  constexpr int kTW = FAST ? 2 : 4;
+  const uint64_t* __restrict__ Tr = a.Tt + (int64_t)(blockIdx.x % kTReplicas) * a.t_stride;
+  const int ttotal = bc * r;
+  uint64_t tv[kTW];
+  if constexpr (FAST) {
+#pragma unroll
+    for (int k = 0; k < kTW; ++k) {
+      const int e = t + 256 * k;
+      tv[k] = __hip_atomic_load(Tr + (e < ttotal ? e : e % ttotal), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
 
   // sparse part
   float ssum[RPW][BC];
@@ -623,27 +811,35 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
   else
     nm_consume<DT, BC, RPW>(a, row0, nw, xsrc, ssum);
 
-  // T -> LDS: this block's replica, tag check, bounded polling of stale
-  // words, then local computation of any row still missing.
+  bool sub_last = false;
+  uint32_t top = 0;
+  if (r > 0 && t == 0) sub_last = arrive_check(a, G, nsub, sub, arrived, top);
+
+  // T -> LDS: this block's replica (other passes read after the sparse part,
+  // when the producers, dispatched first, have normally published), tag
+  // check, bounded polling of stale words, then local computation of any row
+  // still missing.
   if (r > 0) {
-    const uint64_t* __restrict__ Tr = a.Tt + (int64_t)(blockIdx.x % kTReplicas) * a.t_stride;
-    const int total = bc * r;
-    for (int base = 0; base < total; base += 4 * 256) {
-      uint64_t v[4];
+    for (int base = 0; base < ttotal; base += kTW * 256) {
+      if (!FAST || base > 0) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        v[k] = __hip_atomic_load(Tr + min(base + t + 256 * k, total - 1), __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
+        for (int k = 0; k < kTW; ++k) {
+          const int e = base + t + 256 * k;
+          tv[k] = __hip_atomic_load(Tr + (e < ttotal ? e : e % ttotal), __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      for (int k = 0; k < kTW; ++k) {
         const int e = base + t + 256 * k;
-        if (e < total) {
-          for (int s = 0; (uint32_t)(v[k] >> 32) != tag && s < a.spin; ++s) {
+        if (e < ttotal) {
+          uint64_t v = tv[k];
+          for (int s = 0; (uint32_t)(v >> 32) != tag && s < a.spin; ++s) {
             __builtin_amdgcn_s_sleep(1);
-            v[k] = __hip_atomic_load(Tr + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            v = __hip_atomic_load(Tr + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
-          if ((uint32_t)(v[k] >> 32) == tag) {
-            Ts[e] = __uint_as_float((uint32_t)v[k]);
+          if ((uint32_t)(v >> 32) == tag) {
+            Ts[e] = __uint_as_float((uint32_t)v);
           } else {
             const int l = e % r;
             atomicOr(&miss[l >> 5], 1u << (l & 31));
@@ -657,7 +853,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
       while (bits) {
         const int l = wi * 32 + __ffs(bits) - 1;
         bits &= bits - 1;
-        t_row<DT, BC>(Vt + (int64_t)l * n, xsrc, n, bc, a.vec, red);
+        t_row<DT, BC>(Vt + (int64_t)l * n, a.x_pad ? X : xsrc, n, bc, a.vec, red);
         if (t < bc) Ts[(int64_t)t * r + l] = red_sum<BC>(red, t);
         __syncthreads();
       }
@@ -688,29 +884,40 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a) {
 
 // ---------------------------------------------------------------------------
 template <int DT, int FMT, int BC, bool VECU>
-static void launch_v(const DecodeArgs& a, int rpw, size_t lds, hipStream_t s) {
+static void launch_v(const DecodeArgs& a, bool fast, int rpw, size_t lds, hipStream_t s) {
   const int rows_per_block = 4 * rpw;
   const unsigned grid = (unsigned)(a.r + (a.m + rows_per_block - 1) / rows_per_block);
+  if constexpr (DT == HSS_BF16) {
+    if (fast) {
+      if (rpw == 1)
+        hipLaunchKernelGGL((k_decode<DT, FMT, BC, 1, VECU, true>), dim3(grid), dim3(256), lds, s, a);
+      else if (rpw == 4)
+        hipLaunchKernelGGL((k_decode<DT, FMT, BC, 4, VECU, true>), dim3(grid), dim3(256), lds, s, a);
+      else
+        hipLaunchKernelGGL((k_decode<DT, FMT, BC, 2, VECU, true>), dim3(grid), dim3(256), lds, s, a);
+      return;
+    }
+  }
   if (rpw == 1)
-    hipLaunchKernelGGL((k_decode<DT, FMT, BC, 1, VECU>), dim3(grid), dim3(256), lds, s, a);
-  else
-    hipLaunchKernelGGL((k_decode<DT, FMT, BC, 2, VECU>), dim3(grid), dim3(256), lds, s, a);
+    hipLaunchKernelGGL((k_decode<DT, FMT, BC, 1, VECU, false>), dim3(grid), dim3(256), lds, s, a);
+  else  // 2 (four rows per wave are launched FAST only)
+    hipLaunchKernelGGL((k_decode<DT, FMT, BC, 2, VECU, false>), dim3(grid), dim3(256), lds, s, a);
 }
 
 template <int DT, int FMT, int BC>
-static void launch_bc(const DecodeArgs& a, bool vecu, int rpw, size_t lds, hipStream_t s) {
+static void launch_bc(const DecodeArgs& a, bool vecu, bool fast, int rpw, size_t lds, hipStream_t s) {
   if constexpr (DT == HSS_BF16) {
-    if (vecu) return launch_v<DT, FMT, BC, true>(a, rpw, lds, s);
+    if (vecu) return launch_v<DT, FMT, BC, true>(a, fast, rpw, lds, s);
   }
-  launch_v<DT, FMT, BC, false>(a, rpw, lds, s);
+  launch_v<DT, FMT, BC, false>(a, fast, rpw, lds, s);
 }
 
 template <int DT, int FMT>
-static void launch_fmt(const DecodeArgs& a, bool vecu, int rpw, size_t lds, hipStream_t s) {
-  if (a.bc == 1) launch_bc<DT, FMT, 1>(a, vecu, rpw, lds, s);
-  else if (a.bc == 2) launch_bc<DT, FMT, 2>(a, vecu, rpw, lds, s);
-  else if (a.bc <= 4) launch_bc<DT, FMT, 4>(a, vecu, rpw, lds, s);
-  else launch_bc<DT, FMT, 8>(a, vecu, rpw, lds, s);
+static void launch_fmt(const DecodeArgs& a, bool vecu, bool fast, int rpw, size_t lds, hipStream_t s) {
+  if (a.bc == 1) launch_bc<DT, FMT, 1>(a, vecu, fast, rpw, lds, s);
+  else if (a.bc == 2) launch_bc<DT, FMT, 2>(a, vecu, fast, rpw, lds, s);
+  else if (a.bc <= 4) launch_bc<DT, FMT, 4>(a, vecu, fast, rpw, lds, s);
+  else launch_bc<DT, FMT, 8>(a, vecu, fast, rpw, lds, s);
 }
 
 static constexpr size_t kMaxLds = 60 * 1024;  // dynamic LDS budget per block
@@ -762,11 +969,16 @@ void launch_decode(const hss_matrix* A, int bc, const void* X, void* Y, void* ws
   const size_t es = A->dtype == HSS_F32 ? 4 : 2;
   const size_t tbytes = align16(sizeof(float) * (size_t)bc * A->r);
   const size_t mbytes = align16(4 * (size_t)((A->r + 31) / 32));
-  const size_t xbytes = align16((size_t)bc * A->n * es);
+  const bool nm_fast = A->fmt == HSS_FMT_2OF4 && A->dtype == HSS_BF16 && ((uintptr_t)X % 16 == 0) &&
+                       A->n % 32 == 0 && (uintptr_t)A->nm_values % 16 == 0 && (uintptr_t)A->nm_meta % 4 == 0 &&
+                       (A->r == 0 || (uintptr_t)A->Vt % 16 == 0);
+  // the 2:4 fast path reads 64-byte X chunks at a 64-byte lane stride: pad them
+  const size_t xbytes = align16((size_t)bc * A->n * es * (nm_fast ? 5 : 4) / 4);
   a.t_off = 0;
   a.miss_off = (int)tbytes;
   a.x_off = (int)(tbytes + mbytes);
   a.x_lds = tbytes + mbytes + xbytes <= kMaxLds;
+  a.x_pad = nm_fast && a.x_lds;
   // Vector dot products: X rows and Vt rows start 16-byte aligned.
   a.vec = ((uintptr_t)X % 16 == 0) && ((size_t)A->n * es) % 16 == 0 &&
           (A->r == 0 || (uintptr_t)A->Vt % 16 == 0);
@@ -777,13 +989,20 @@ void launch_decode(const hss_matrix* A, int bc, const void* X, void* Y, void* ws
   // bf16 U rows as 8-byte vectors; T rows in LDS (c * r floats) stay 16-byte aligned.
   const bool vecu = A->dtype == HSS_BF16 && A->r > 0 && A->r % 4 == 0 && (uintptr_t)A->U % 8 == 0;
   const size_t lds = tbytes + mbytes + (a.x_lds ? xbytes : 0);
-  const int rpw = A->m >= 8192 ? 2 : 1;
+  const bool fast = A->dtype == HSS_BF16 && A->r > 0 && a.x_lds && a.vec &&
+                    (size_t)bc * A->n / 8 <= 256 * (size_t)kXRFast &&
+                    (A->fmt == HSS_FMT_CSR ? a.vec_csr : a.nm_fast);
+  // Rows per wave: more rows per block means fewer copies of X staged through
+  // L2 into LDS and fewer blocks queueing loads on each CU (measured best:
+  // 2 for 4096 rows, 4 for 11008 rows); small matrices keep one row per wave
+  // for parallelism.  Four rows per wave exist only as FAST instances.
+  const int rpw = A->m >= 8192 ? (fast ? 4 : 2) : (A->m >= 2048 ? 2 : 1);
   if (A->dtype == HSS_F32) {
-    if (A->fmt == HSS_FMT_CSR) launch_fmt<HSS_F32, HSS_FMT_CSR>(a, false, rpw, lds, s);
-    else launch_fmt<HSS_F32, HSS_FMT_2OF4>(a, false, rpw, lds, s);
+    if (A->fmt == HSS_FMT_CSR) launch_fmt<HSS_F32, HSS_FMT_CSR>(a, false, false, rpw, lds, s);
+    else launch_fmt<HSS_F32, HSS_FMT_2OF4>(a, false, false, rpw, lds, s);
   } else {
-    if (A->fmt == HSS_FMT_CSR) launch_fmt<HSS_BF16, HSS_FMT_CSR>(a, vecu, rpw, lds, s);
-    else launch_fmt<HSS_BF16, HSS_FMT_2OF4>(a, vecu, rpw, lds, s);
+    if (A->fmt == HSS_FMT_CSR) launch_fmt<HSS_BF16, HSS_FMT_CSR>(a, vecu, fast, rpw, lds, s);
+    else launch_fmt<HSS_BF16, HSS_FMT_2OF4>(a, vecu, fast, rpw, lds, s);
   }
 }
 

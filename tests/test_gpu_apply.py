@@ -69,6 +69,9 @@ SMALL = [
     ("csr", 257, 512, 1, 33), ("csr", 300, 640, 128, 64),
     ("2:4", 1, 4, 0, 1), ("2:4", 5, 36, 3, 2), ("2:4", 64, 4096, 16, 1), ("2:4", 65, 128, 7, 9),
     ("2:4", 33, 100, 5, 16), ("2:4", 128, 512, 64, 64),
+    # ragged row counts in the 2- and 4-rows-per-wave regimes (m >= 2048, m >= 8192)
+    ("csr", 2053, 256, 16, 1), ("csr", 2049, 64, 9, 3), ("csr", 8195, 64, 12, 2),
+    ("2:4", 8197, 128, 8, 1), ("2:4", 8197, 128, 8, 5), ("2:4", 2050, 64, 6, 2),
 ]
 
 
