@@ -57,6 +57,26 @@ def _args():
     return ap.parse_args()
 
 
+def _measured_traffic():
+    """HBM bytes per launch of the headline kernel as two hardware-counter runs
+    measured them (profiles/k_decode_csr4096_b1_hbm_counters.txt), or None when
+    the kernel's sources have changed since (the stored hash no longer matches)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "k_decode_csr4096_b1_hbm_counters.txt")
+    try:
+        lines = open(path).read().splitlines()
+    except OSError:
+        return None
+    fields = {ln.split(":", 1)[0].split(" ")[0]: ln.rsplit(":", 1)[1].strip()
+              for ln in lines if ln.startswith(("traffic_bytes_per_launch", "source_sha256"))}
+    csrc = os.path.join(ROOT, "sparse_rank_linear_hss_amd", "csrc")
+    h = hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read()
+                                for f in ("decode.hip", "hss_internal.h"))).hexdigest()
+    if fields.get("source_sha256") != h or "traffic_bytes_per_launch" not in fields:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
+
+
 def _bf16(a):
     import numpy as np
     import torch
@@ -330,7 +350,8 @@ def main():
                                "(838,860 nnz) + rank-256 factors, decode b=1, cold HBM rotation, HIP-graph replay",
                    "m": m, "n": n, "nnz": nnz_head, "rank": cfg.rank[0], "batch": 1},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": _measured_traffic(),
+                     "traffic_unit": "HBM bytes per launch (FETCH_SIZE x read scale + WRITE_SIZE x write scale)",
                      "kernel": "k_decode (one launch per decode token)",
                      "algorithmic_bytes_per_launch": bytes_head},
         "compressed_gbs": gbs,
