@@ -276,6 +276,136 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Large tiles for big batches (prefill): 256 (M) x 128 (N) per block, each
+// wave a 128 x 64 quarter (4 x 2 MFMA blocks, 128 accumulators), K in stages
+// of 64 through one padded LDS buffer, the next stage's global loads in
+// flight during the current stage's MFMA loop.  The wave tile reads 6 KiB of
+// LDS per 8 MFMAs (the 64 x 64 tiles above: 4 KiB per 4), and a block is
+// small enough (55 KiB LDS) for two to share a CU.  Dense operands whose rows
+// allow 16-byte loads (K % 8 == 0).
+// ---------------------------------------------------------------------------
+static constexpr int kGM = 256, kGN = 128, kGK = 64;
+static constexpr int kGStride = kGK + 8;  // bf16 per LDS row (16-byte pad: conflict-free fragment reads)
+
+struct BigRegs {
+  u32x4 a[8], b[4];
+};
+
+// Stage s: segment 1 (A1, B1) for s < nst1, else segment 2.  Thread t holds
+// A vectors q = t + 256 i (row q / 8, columns 8 (q % 8) ..) and B likewise.
+__device__ __forceinline__ void big_load(BigRegs& r, const GemmArgs& g, int nst1, int s, int m0, int n0) {
+  const int t = threadIdx.x;
+  const bool seg1 = s < nst1;
+  const int k0 = (seg1 ? s : s - nst1) * kGK;
+  const int K = seg1 ? g.K1 : g.K2;
+  const uint16_t* __restrict__ A = seg1 ? g.A1 : g.A2;
+  const uint16_t* __restrict__ B = seg1 ? g.B1 : g.B2;
+  const int64_t lda = seg1 ? g.lda1 : g.lda2, ldb = seg1 ? g.ldb1 : g.ldb2;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int q = t + 256 * i;
+    const int kk = min(k0 + (q & 7) * 8, K - 8);
+    r.a[i] = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(A + (int64_t)min(m0 + (q >> 3), g.M - 1) * lda + kk));
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = t + 256 * i;
+    const int kk = min(k0 + (q & 7) * 8, K - 8);
+    r.b[i] = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(B + (int64_t)min(n0 + (q >> 3), g.N - 1) * ldb + kk));
+  }
+}
+
+__device__ __forceinline__ void big_store(uint16_t* __restrict__ As, uint16_t* __restrict__ Bs, const BigRegs& r,
+                                          const GemmArgs& g, int nst1, int s, int m0, int n0) {
+  const int t = threadIdx.x;
+  const bool seg1 = s < nst1;
+  const int k0 = (seg1 ? s : s - nst1) * kGK;
+  const int K = seg1 ? g.K1 : g.K2;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int q = t + 256 * i, row = q >> 3, kq = (q & 7) * 8;
+    *reinterpret_cast<u32x4*>(As + row * kGStride + kq) = (k0 + kq < K && m0 + row < g.M) ? r.a[i] : z;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = t + 256 * i, row = q >> 3, kq = (q & 7) * 8;
+    *reinterpret_cast<u32x4*>(Bs + row * kGStride + kq) = (k0 + kq < K && n0 + row < g.N) ? r.b[i] : z;
+  }
+}
+
+__global__ __launch_bounds__(256, 2) void k_gemm_big(GemmArgs g) {
+  __shared__ __align__(16) uint16_t As[kGM * kGStride];
+  __shared__ __align__(16) uint16_t Bs[kGN * kGStride];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int wm = w >> 1, wn = w & 1;
+  const int m0 = blockIdx.x * kGM, n0 = blockIdx.y * kGN;
+  const int nst1 = (g.K1 + kGK - 1) / kGK;
+  const int nst = nst1 + (g.K2 + kGK - 1) / kGK;
+  const int s_begin = blockIdx.z * g.chunks_per_split;
+  const int s_end = min(s_begin + g.chunks_per_split, nst);
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  BigRegs r;
+  if (s_begin < s_end) big_load(r, g, nst1, s_begin, m0, n0);
+  for (int s = s_begin; s < s_end; ++s) {
+    __syncthreads();  // the previous stage's fragment reads are done
+    big_store(As, Bs, r, g, nst1, s, m0, n0);
+    __syncthreads();
+    if (s + 1 < s_end) big_load(r, g, nst1, s + 1, m0, n0);
+#pragma unroll
+    for (int ks = 0; ks < kGK / 16; ++ks) {
+      const int kk = ks * 16 + 8 * (lane >> 5);
+      bf16x8 af[4], bfr[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        af[i] = *reinterpret_cast<const bf16x8*>(As + (wm * 128 + i * 32 + (lane & 31)) * kGStride + kk);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8*>(Bs + (wn * 64 + j * 32 + (lane & 31)) * kGStride + kk);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + wn * 64 + j * 32 + (lane & 31);
+      if (n >= g.N) continue;
+#pragma unroll
+      for (int vg = 0; vg < 4; ++vg) {
+        const int m = m0 + wm * 128 + i * 32 + 8 * vg + 4 * (lane >> 5);
+        if (g.out_mode == OUT_BF16) {
+          uint16_t* C = static_cast<uint16_t*>(g.C) + (int64_t)n * g.ldc;
+#pragma unroll
+          for (int p = 0; p < 4; ++p)
+            if (m + p < g.M) C[m + p] = f32_to_bf16(acc[i][j][4 * vg + p]);
+        } else {
+          float* C = static_cast<float*>(g.C) + (int64_t)blockIdx.z * g.N * g.ldc + (int64_t)n * g.ldc;
+#pragma unroll
+          for (int p = 0; p < 4; ++p)
+            if (m + p < g.M) C[m + p] = acc[i][j][4 * vg + p];
+        }
+      }
+    }
+  }
+}
+
 // Dense bf16 copy D (m x n, row-major) of a CSR matrix, one wave per row:
 // the row is zeroed with 16-byte stores, a fence waits for those stores, then
 // the lanes scatter the row's entries (no other wave touches the row).
@@ -326,28 +456,55 @@ static int choose_splits(int tiles, int nch) {
   return s;
 }
 
+// Kernel choice for one GEMM (M x N outputs, K = K1 + K2): the large-tile
+// kernel for dense 16-byte-aligned operands and N >= 256, else k_gemm<BN>.
+struct GemmCfg {
+  bool big;
+  int bn, splits;
+};
+
+static GemmCfg gemm_cfg(int M, int N, int K1, int K2, bool big_ok) {
+  GemmCfg c;
+  c.big = big_ok && N >= 256;
+  if (c.big) {
+    c.bn = kGN;
+    c.splits = choose_splits(cdiv(M, kGM) * cdiv(N, kGN), cdiv(K1, kGK) + cdiv(K2, kGK));
+  } else {
+    c.bn = batch_tile(N);
+    c.splits = choose_splits(cdiv(M, kBM) * cdiv(N, c.bn), cdiv(K1, kKC) + cdiv(K2, kKC));
+  }
+  return c;
+}
+
+// fp32 partials of one GEMM: enough for either kernel choice (operand
+// alignment, which decides between them, is known only at launch).
+static size_t gemm_part_bytes(int M, int N, int K1, int K2) {
+  size_t mx = 0;
+  for (int big = 0; big < 2; ++big) {
+    const GemmCfg c = gemm_cfg(M, N, K1, K2, big);
+    if (c.splits > 1) mx = std::max(mx, sizeof(float) * (size_t)c.splits * N * M);
+  }
+  return mx;
+}
+
 struct MfmaPlan {
-  int r, b, bn;
-  int t_splits, y_splits;
   size_t tb_off, dense_off, part_off, total;
 };
 
+static bool csr_empty(const hss_matrix* A) { return A->fmt == HSS_FMT_CSR && A->nnz == 0; }
+
 static MfmaPlan plan_mfma(const hss_matrix* A, int b) {
   MfmaPlan p;
-  p.r = A->r; p.b = b; p.bn = batch_tile(b);
   const int m = A->m, n = A->n, r = A->r;
-  const int tn = cdiv(b, p.bn);
-  p.t_splits = r > 0 ? choose_splits(cdiv(r, kBM) * tn, cdiv(n, kKC)) : 0;
-  const int nch_y = cdiv(n, kKC) + (r > 0 ? cdiv(r, kKC) : 0);
-  p.y_splits = choose_splits(cdiv(m, kBM) * tn, nch_y);
+  const int k1 = csr_empty(A) ? 0 : n;
   size_t off = 0;
   p.tb_off = off;    off += align256(sizeof(uint16_t) * (size_t)b * (r > 0 ? r : 1));
   p.dense_off = off;
-  if (A->fmt == HSS_FMT_CSR) off += align256(sizeof(uint16_t) * (size_t)m * n);
+  if (A->fmt == HSS_FMT_CSR && k1 > 0) off += align256(sizeof(uint16_t) * (size_t)m * n);
   p.part_off = off;
-  const size_t part_t = p.t_splits > 1 ? sizeof(float) * (size_t)p.t_splits * b * r : 0;
-  const size_t part_y = p.y_splits > 1 ? sizeof(float) * (size_t)p.y_splits * b * m : 0;
-  off += align256(part_t > part_y ? part_t : part_y);
+  const size_t part_t = r > 0 ? gemm_part_bytes(r, b, n, 0) : 0;
+  const size_t part_y = gemm_part_bytes(m, b, k1, r);
+  off += align256(std::max(part_t, part_y));
   p.total = off;
   return p;
 }
@@ -371,27 +528,33 @@ static void launch_gemm_bn(const GemmArgs& g, int amode, int splits, hipStream_t
     hipLaunchKernelGGL((k_gemm<BN, A_DENSE>), grid, dim3(256), 0, s, g);
 }
 
-static void run_gemm(GemmArgs g, int amode, int bn, int splits, float* part, hipStream_t s) {
-  g.chunks_per_split = cdiv(g.nch, splits);
+static int aligned16(const void* p, int64_t ld) { return ((uintptr_t)p % 16 == 0) && (ld % 8 == 0); }
+
+static void run_gemm(GemmArgs g, int amode, float* part, hipStream_t s) {
+  const bool big_ok = amode == A_DENSE && (g.K1 == 0 || (g.vec_a1 && g.vec_b1)) &&
+                      (g.K2 == 0 || (g.vec_a2 && g.vec_b2));
+  const GemmCfg c = gemm_cfg(g.M, g.N, g.K1, g.K2, big_ok);
+  g.chunks_per_split = cdiv(g.nch, c.splits);
+  if (c.big) g.chunks_per_split = cdiv(cdiv(g.K1, kGK) + cdiv(g.K2, kGK), c.splits);
   void* final_out = g.C;
   const int64_t final_ldc = g.ldc;
   const int final_bf16 = g.out_mode == OUT_BF16;
-  if (splits > 1) {
+  if (c.splits > 1) {
     g.C = part;
     g.out_mode = OUT_PARTIAL;
   }
-  if (bn == 32) launch_gemm_bn<32>(g, amode, splits, s);
-  else if (bn == 64) launch_gemm_bn<64>(g, amode, splits, s);
-  else launch_gemm_bn<128>(g, amode, splits, s);
-  if (splits > 1) {
+  if (c.big)
+    hipLaunchKernelGGL(k_gemm_big, dim3(cdiv(g.M, kGM), cdiv(g.N, kGN), c.splits), dim3(256), 0, s, g);
+  else if (c.bn == 32) launch_gemm_bn<32>(g, amode, c.splits, s);
+  else if (c.bn == 64) launch_gemm_bn<64>(g, amode, c.splits, s);
+  else launch_gemm_bn<128>(g, amode, c.splits, s);
+  if (c.splits > 1) {
     const int64_t total = (int64_t)g.N * final_ldc;
     const unsigned grid = (unsigned)std::min<int64_t>((total + 255) / 256, 4096);
-    hipLaunchKernelGGL(k_reduce, dim3(grid), dim3(256), 0, s, part, splits, g.M, g.N, final_ldc, final_out,
+    hipLaunchKernelGGL(k_reduce, dim3(grid), dim3(256), 0, s, part, c.splits, g.M, g.N, final_ldc, final_out,
                        final_bf16);
   }
 }
-
-static int aligned16(const void* p, int64_t ld) { return ((uintptr_t)p % 16 == 0) && (ld % 8 == 0); }
 
 hss_status launch_mfma(const hss_matrix* A, int b, const void* X, void* Y, void* ws, hipStream_t s) {
   const MfmaPlan p = plan_mfma(A, b);
@@ -402,10 +565,10 @@ hss_status launch_mfma(const hss_matrix* A, int b, const void* X, void* Y, void*
   const int m = A->m, n = A->n, r = A->r;
   const uint16_t* Xb = static_cast<const uint16_t*>(X);
   const bool csr = A->fmt == HSS_FMT_CSR;
-  const unsigned row_blocks = (unsigned)cdiv(m, 4);
+  const bool s_empty = csr_empty(A);  // segment 1 has no work
 
-  if (csr)
-    hipLaunchKernelGGL(k_csr_densify, dim3(row_blocks), dim3(256), 0, s, A->row_ptr, A->col_idx,
+  if (csr && !s_empty)
+    hipLaunchKernelGGL(k_csr_densify, dim3((unsigned)cdiv(m, 4)), dim3(256), 0, s, A->row_ptr, A->col_idx,
                        static_cast<const uint16_t*>(A->values), m, n, Sd);
   // T^T (b x r) = X . Vt^T
   if (r > 0) {
@@ -417,12 +580,12 @@ hss_status launch_mfma(const hss_matrix* A, int b, const void* X, void* Y, void*
     g.C = Tb; g.ldc = r; g.out_mode = OUT_BF16;
     g.vec_a1 = aligned16(g.A1, n) && n % 8 == 0;
     g.vec_b1 = aligned16(Xb, n) && n % 8 == 0;
-    run_gemm(g, A_DENSE, p.bn, p.t_splits, part, s);
+    run_gemm(g, A_DENSE, part, s);
   }
   // Y (b x m) = [X | T^T] . [S | U]^T
   GemmArgs g = {};
-  g.M = m; g.N = b; g.K1 = n; g.K2 = r;
-  g.nch1 = cdiv(n, kKC);
+  g.M = m; g.N = b; g.K1 = s_empty ? 0 : n; g.K2 = r;
+  g.nch1 = cdiv(g.K1, kKC);
   g.nch = g.nch1 + (r > 0 ? cdiv(r, kKC) : 0);
   g.B1 = Xb; g.ldb1 = n;
   g.vec_b1 = aligned16(Xb, n) && n % 8 == 0;
@@ -442,7 +605,7 @@ hss_status launch_mfma(const hss_matrix* A, int b, const void* X, void* Y, void*
     g.vec_b2 = aligned16(Tb, r) && r % 8 == 0;
   }
   g.C = Y; g.ldc = m; g.out_mode = OUT_BF16;
-  run_gemm(g, amode, p.bn, p.y_splits, part, s);
+  run_gemm(g, amode, part, s);
   return hipGetLastError() == hipSuccess ? HSS_OK : HSS_ERR_HIP;
 }
 

@@ -72,6 +72,8 @@ SMALL = [
     # ragged row counts in the 2- and 4-rows-per-wave regimes (m >= 2048, m >= 8192)
     ("csr", 2053, 256, 16, 1), ("csr", 2049, 64, 9, 3), ("csr", 8195, 64, 12, 2),
     ("2:4", 8197, 128, 8, 1), ("2:4", 8197, 128, 8, 5), ("2:4", 2050, 64, 6, 2),
+    # large batches: 256 x 128 tiles (ragged M and N, K tails not a multiple of the stage)
+    ("csr", 300, 640, 128, 300), ("csr", 257, 1000, 72, 260), ("2:4", 100, 256, 16, 256),
 ]
 
 
@@ -95,9 +97,11 @@ def test_apply_small(H, dtype, case):
     assert O.bits_equal(to_host(Y1), to_host(Y2))                  # deterministic
 
 
-@pytest.mark.parametrize("dtype", [O.F32, O.BF16])
-def test_apply_empty_sparse_part(H, dtype):
-    m, n, r, b = 70, 96, 6, 5
+@pytest.mark.parametrize("dtype,b,r", [(O.F32, 5, 6), (O.BF16, 5, 6), (O.BF16, 32, 16), (O.BF16, 300, 0)])
+def test_apply_empty_sparse_part(H, dtype, b, r):
+    """k = 0: a pure low-rank product (matrix-core batches skip the sparse
+    segment); with r = 0 too the output is exactly zero."""
+    m, n = 70, 96
     W = syn.random_matrix(m, n, dtype, seed=3, kind="t3")
     ref = O.split_csr(W, dtype, 0)
     U, V = _factors(m, n, r, dtype, 5)
