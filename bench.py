@@ -18,8 +18,10 @@ replays are exact); the plain stream-launch rate is reported beside it.
 
 Also measured in the same run (extra JSON keys): the same layer at batch 16,
 the 11008 x 4096 2:4 layer at batch 1/8/64, one decoder layer's seven
-projections per decode token, the 8192^2 prefill at batch 2048 (with the
-low-rank GEMMs alone for their matrix-core throughput), and hss_split.
+projections per decode token (q/k/v and gate/up as grouped applies, so four
+launches per token; the seven-launch order beside it), the 8192^2 prefill at
+batch 2048 (with the low-rank GEMMs alone for their matrix-core throughput),
+and hss_split.
 
 Prints ONE JSON line.  `value` = decode tokens/s of the timed steps;
 `roofline` prices the apply kernel's compressed-weight bytes against the
@@ -292,17 +294,32 @@ def main():
             del Wp
         tok_bytes = sum(p.w_bytes for p in projs)
         _log(f"decoder layer ready: {tok_bytes} compressed bytes per token")
-        ws4 = projs[0].mats[0].workspace(1)
-        xs4 = [[_bf16(syn.activations(c4, 1, w, s)) for s in range(4)] for w in range(7)]
+        # q, k, v read the same input, as do gate and up: 4 launches per token
+        # (grouped); the 7-launch order is timed as well.
+        groups = [[0, 1, 2], [3], [4, 5], [6]]
+        ws4 = torch.zeros(max(H.hss_apply_group_workspace_size([projs[w].mats[0] for w in grp], 1)
+                              for grp in groups), dtype=torch.uint8, device="cuda")
+        xin = [[_bf16(syn.activations(c4, 1, grp[0], s)) for s in range(4)] for grp in groups]
         ys4 = [torch.empty((1, p.m), dtype=torch.bfloat16, device="cuda") for p in projs]
 
         def layer_step(i):
-            for w, p in enumerate(projs):
-                H.hss_apply(p.mats[i % len(p.mats)], xs4[w][i % 4], ys4[w], ws4)
+            for gi, grp in enumerate(groups):
+                mats = [projs[w].mats[i % len(projs[w].mats)] for w in grp]
+                if len(grp) == 1:
+                    H.hss_apply(mats[0], xin[gi][i % 4], ys4[grp[0]], ws4)
+                else:
+                    H.hss_apply_group(mats, xin[gi][i % 4], [ys4[w] for w in grp], ws4)
+
+        def layer_step_7(i):
+            for gi, grp in enumerate(groups):
+                for w in grp:
+                    H.hss_apply(projs[w].mats[i % len(projs[w].mats)], xin[gi][i % 4], ys4[w], ws4)
         ms4 = _time_graph(layer_step, c4.tokens, 5)
+        ms4_7 = _time_graph(layer_step_7, c4.tokens, 5)
         extra["decoder_layer_7proj"] = {"ms_per_token": ms4, "tokens_per_s": 1 / (ms4 * 1e-3),
                                         "gbs": tok_bytes / (ms4 * 1e-3) / 1e9, "bytes_per_token": tok_bytes,
-                                        "tokens": c4.tokens}
+                                        "tokens": c4.tokens, "launches_per_token": 4,
+                                        "ms_per_token_7_launches": ms4_7}
         del projs
         torch.cuda.empty_cache()
 

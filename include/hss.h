@@ -43,7 +43,7 @@ extern "C" {
 #endif
 
 #define HSS_VERSION_MAJOR 1
-#define HSS_VERSION_MINOR 0
+#define HSS_VERSION_MINOR 1
 
 typedef enum {
   HSS_OK = 0,
@@ -169,7 +169,9 @@ hss_status hss_apply_workspace_size(const hss_matrix* A, int32_t b, size_t* byte
  *     they are ordered (same stream or events).
  * Execution: bf16 with b >= 16 runs on the matrix cores (T^T = X V and Y =
  * [X | T^T] [S | U]^T as MFMA GEMMs with fp32 accumulation; T is rounded to
- * bf16 once, between the two); otherwise one fused kernel per 8 columns.
+ * bf16 once, between the two; a CSR S is first expanded into a dense bf16
+ * copy inside the workspace, so the workspace then holds m*n*2 more bytes);
+ * otherwise one fused kernel per 8 columns.
  * Returns HSS_ERR_INVALID_ARG for: A or X or Y null, unknown fmt/dtype,
  *   reserved != 0, m, n <= 0, r < 0, b < 1, b*m, b*n, m*n, r*(m+n) >= 2^31,
  *   nnz < 0, required arrays null, n % 4 != 0 for 2:4, X overlapping Y.
@@ -178,6 +180,31 @@ hss_status hss_apply_workspace_size(const hss_matrix* A, int32_t b, size_t* byte
  */
 hss_status hss_apply(const hss_matrix* A, int32_t b, const void* X, void* Y, void* ws,
                      size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Grouped apply: G matrices that read the same X, e.g. the q, k and v
+ * projections of one attention block, or gate and up of one MLP block
+ * ([HSS] implementation-patterns section: the compressed layers run layer by
+ * layer; these share their input).
+ * ------------------------------------------------------------------------
+ * Y[g] (b x A[g]->m) = X (b x n) times (S_g + U_g V_g^T)^T for g < G, with
+ * exactly the arithmetic of hss_apply on each matrix.  In the decode regime
+ * (everything hss_apply runs in its fused kernel) all G matrices go through
+ * ONE launch per pass of up to 8 columns instead of G; on the matrix cores
+ * the matrices are applied one after another.
+ *   1 <= G <= HSS_MAX_GROUP; every A[g] valid for hss_apply with batch b, all
+ *   with the same n, dtype and fmt (m, r and the arrays may differ).
+ *   Y[g] device outputs, pairwise disjoint and disjoint from X.
+ *   ws: at least hss_apply_group_workspace_size() bytes, zero-filled once,
+ *   the same state rules as hss_apply (it may also serve hss_apply calls).
+ * Returns HSS_ERR_INVALID_ARG for: A, X or Y null, G out of range, any matrix
+ *   invalid, mismatched n/dtype/fmt, overlapping outputs; HSS_ERR_WORKSPACE for
+ *   a null or short workspace; HSS_ERR_HIP if a launch fails.
+ */
+#define HSS_MAX_GROUP 4
+hss_status hss_apply_group_workspace_size(const hss_matrix* const* A, int32_t G, int32_t b, size_t* bytes);
+hss_status hss_apply_group(const hss_matrix* const* A, int32_t G, int32_t b, const void* X, void* const* Y,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

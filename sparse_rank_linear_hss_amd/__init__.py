@@ -23,7 +23,8 @@ from ._lib import (HSS_BF16, HSS_ERR_NONFINITE, HSS_F32, HSS_FMT_2OF4, HSS_FMT_C
 
 __all__ = [
     "hss_version", "hss_topk_count", "hss_split_workspace_size", "hss_split", "hss_get_error",
-    "hss_apply_workspace_size", "hss_apply", "HSSMatrix", "SplitResult", "HSSError",
+    "hss_apply_workspace_size", "hss_apply", "hss_apply_group_workspace_size", "hss_apply_group",
+    "HSSMatrix", "SplitResult", "HSSError",
     "LIB_PATH", "status_string",
 ]
 
@@ -202,3 +203,34 @@ def hss_apply(A: HSSMatrix, X: torch.Tensor, Y: Optional[torch.Tensor] = None,
     check(lib.hss_apply(ctypes.byref(A.struct), b, _ptr(X), _ptr(Y), _ptr(ws), ws.numel(),
                         _stream(dev)), "hss_apply")
     return Y
+
+
+def _group_structs(As):
+    arr = (ctypes.POINTER(HssMatrixStruct) * len(As))(*[ctypes.pointer(A.struct) for A in As])
+    return arr
+
+
+def hss_apply_group_workspace_size(As, b: int) -> int:
+    out = ctypes.c_size_t(0)
+    check(lib.hss_apply_group_workspace_size(_group_structs(As), len(As), int(b), ctypes.byref(out)),
+          "hss_apply_group_workspace_size")
+    return int(out.value)
+
+
+def hss_apply_group(As, X: torch.Tensor, Ys=None, ws: Optional[torch.Tensor] = None):
+    """Y_g = X (S_g + U_g V_g^T)^T for every matrix of As (same n, dtype and
+    format), in one launch per decode pass; returns the list of Y_g."""
+    dev = _dev(X)
+    As = list(As)
+    for A in As:
+        if X.dim() != 2 or X.shape[1] != A.n or not X.is_contiguous() or X.dtype != A.dtype:
+            raise ValueError("X must be a contiguous b x n tensor of every matrix's dtype")
+    b = X.shape[0]
+    if Ys is None:
+        Ys = [torch.empty((b, A.m), dtype=A.dtype, device=dev) for A in As]
+    if ws is None:
+        ws = torch.zeros(hss_apply_group_workspace_size(As, b), dtype=torch.uint8, device=dev)
+    yp = (ctypes.c_void_p * len(As))(*[_ptr(Y) for Y in Ys])
+    check(lib.hss_apply_group(_group_structs(As), len(As), b, _ptr(X), yp, _ptr(ws), ws.numel(),
+                              _stream(dev)), "hss_apply_group")
+    return Ys

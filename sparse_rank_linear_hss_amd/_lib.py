@@ -60,6 +60,10 @@ def _load():
         "hss_apply_workspace_size": (ctypes.c_int, [P(HssMatrixStruct), c_int32, P(c_size_t)]),
         "hss_apply": (ctypes.c_int, [P(HssMatrixStruct), c_int32, c_void_p, c_void_p, c_void_p,
                                      c_size_t, c_void_p]),
+        "hss_apply_group_workspace_size": (ctypes.c_int, [P(P(HssMatrixStruct)), c_int32, c_int32,
+                                                          P(c_size_t)]),
+        "hss_apply_group": (ctypes.c_int, [P(P(HssMatrixStruct)), c_int32, c_int32, c_void_p, P(c_void_p),
+                                           c_void_p, c_size_t, c_void_p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

@@ -16,6 +16,8 @@
 namespace hss {
 
 void launch_decode(const hss_matrix* A, int bc, const void* X, void* Y, void* ws, hipStream_t s);
+void launch_decode_group(const hss_matrix* const* A, int G, int bc, const void* X, void* const* Y, void* ws,
+                         hipStream_t s);
 size_t decode_ctl_bytes();
 size_t decode_t_bytes(const hss_matrix* A);
 int decode_max_cols(const hss_matrix* A);
@@ -46,6 +48,46 @@ hss_status launch_apply(const hss_matrix* A, int b, const void* X, void* Y, void
     const int bc = b - c0 < cols ? b - c0 : cols;
     launch_decode(A, bc, static_cast<const char*>(X) + (size_t)c0 * A->n * es,
                   static_cast<char*>(Y) + (size_t)c0 * A->m * es, ws, stream);
+  }
+  return hipGetLastError() == hipSuccess ? HSS_OK : HSS_ERR_HIP;
+}
+
+// Grouped apply of G matrices sharing X.  Decode batches: one fused launch
+// per pass over all G matrices (their T words side by side after the control
+// region).  Matrix-core batches: one apply per matrix, in order.
+size_t apply_group_ws_bytes(const hss_matrix* const* A, int G, int b) {
+  size_t dec = 0, one = 0;
+  for (int g = 0; g < G; ++g) {
+    dec += decode_t_bytes(A[g]);
+    const size_t a = apply_ws_bytes(A[g], b) - decode_ctl_bytes();
+    one = one > a ? one : a;
+  }
+  return decode_ctl_bytes() + (dec > one ? dec : one);
+}
+
+hss_status launch_apply_group(const hss_matrix* const* A, int G, int b, const void* X, void* const* Y, void* ws,
+                              hipStream_t stream) {
+  bool any_mfma = false;
+  for (int g = 0; g < G; ++g) any_mfma = any_mfma || mfma_supported(A[g], b);
+  if (any_mfma) {
+    for (int g = 0; g < G; ++g) {
+      const hss_status st = launch_apply(A[g], b, X, Y[g], ws, stream);
+      if (st != HSS_OK) return st;
+    }
+    return HSS_OK;
+  }
+  const size_t es = A[0]->dtype == HSS_F32 ? 4 : 2;
+  int cols = kDecodeCols;
+  for (int g = 0; g < G; ++g) {
+    const int c = decode_max_cols(A[g]);
+    cols = cols < c ? cols : c;
+  }
+  if (cols == 0) return HSS_ERR_UNSUPPORTED;
+  for (int c0 = 0; c0 < b; c0 += cols) {
+    const int bc = b - c0 < cols ? b - c0 : cols;
+    void* Yc[8];
+    for (int g = 0; g < G; ++g) Yc[g] = static_cast<char*>(Y[g]) + (size_t)c0 * A[g]->m * es;
+    launch_decode_group(A, G, bc, static_cast<const char*>(X) + (size_t)c0 * A[0]->n * es, Yc, ws, stream);
   }
   return hipGetLastError() == hipSuccess ? HSS_OK : HSS_ERR_HIP;
 }

@@ -75,6 +75,18 @@ struct DecodeArgs {
   int t_off, miss_off, x_off;  // dynamic LDS layout (bytes)
 };
 
+// Several matrices that share X in one launch (at most kMaxGroup): the grid is
+// the producer blocks of every matrix, then the row blocks of every matrix.
+// One launch, so one epoch and one arrival count; each matrix has its own T
+// words.
+static constexpr int kMaxGroup = HSS_MAX_GROUP;
+struct GroupArgs {
+  DecodeArgs a[kMaxGroup];
+  int G;
+  int prod_start[kMaxGroup + 1];  // producer blocks of matrix g: [prod_start[g], prod_start[g + 1])
+  int row_start[kMaxGroup + 1];   // row blocks of matrix g (after all producers)
+};
+
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -660,9 +672,19 @@ static constexpr int kXR = 4;      // staged X vectors per thread held in regist
 static constexpr int kXRFast = 2;  // FAST: exactly this many, no branches (bc * n <= 4096 bf16)
 
 template <int DT, int FMT, int BC, int RPW, bool VECU, bool FAST>
-__global__ __launch_bounds__(256) void k_decode(DecodeArgs a_in) {
+__global__ __launch_bounds__(256) void k_decode(GroupArgs ga) {
   using bits_t = typename Elem<DT>::bits_t;
-  DecodeArgs a = a_in;
+  // this block's matrix and its index among that matrix's producer or row blocks
+  const int bid = blockIdx.x;
+  const bool producer = bid < ga.prod_start[ga.G];
+  int gi = 0;
+  if (producer) {
+    while (gi + 1 < ga.G && bid >= ga.prod_start[gi + 1]) ++gi;
+  } else {
+    while (gi + 1 < ga.G && bid >= ga.row_start[gi + 1]) ++gi;
+  }
+  const int local = bid - (producer ? ga.prod_start[gi] : ga.row_start[gi]);
+  DecodeArgs a = ga.a[gi];
   if constexpr (FAST) {
     a.x_lds = 1;
     a.vec = 1;
@@ -691,8 +713,8 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a_in) {
 
   // ---- T producer: Vt row l and X loaded together, published tagged into
   //      every replica ----
-  if ((int)blockIdx.x < r) {
-    const int l = blockIdx.x;
+  if (producer) {
+    const int l = local;
     const uint32_t e = load_epoch(a);
     t_row<DT, BC>(Vt + (int64_t)l * n, X, n, bc, a.vec, red);
     if (t == 0) {
@@ -714,7 +736,7 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a_in) {
   }
 
   // ---- row blocks ----
-  const int row0 = (((int)blockIdx.x - r) * 4 + w) * RPW;  // wave-uniform
+  const int row0 = (local * 4 + w) * RPW;  // wave-uniform
 
   // row bounds: uniform addresses, scalar loads (own counter, so waiting for
   // them does not wait for the vector loads below)
@@ -884,40 +906,39 @@ __global__ __launch_bounds__(256) void k_decode(DecodeArgs a_in) {
 
 // ---------------------------------------------------------------------------
 template <int DT, int FMT, int BC, bool VECU>
-static void launch_v(const DecodeArgs& a, bool fast, int rpw, size_t lds, hipStream_t s) {
-  const int rows_per_block = 4 * rpw;
-  const unsigned grid = (unsigned)(a.r + (a.m + rows_per_block - 1) / rows_per_block);
+static void launch_v(const GroupArgs& ga, unsigned grid, bool fast, int rpw, size_t lds, hipStream_t s) {
   if constexpr (DT == HSS_BF16) {
     if (fast) {
       if (rpw == 1)
-        hipLaunchKernelGGL((k_decode<DT, FMT, BC, 1, VECU, true>), dim3(grid), dim3(256), lds, s, a);
+        hipLaunchKernelGGL((k_decode<DT, FMT, BC, 1, VECU, true>), dim3(grid), dim3(256), lds, s, ga);
       else if (rpw == 4)
-        hipLaunchKernelGGL((k_decode<DT, FMT, BC, 4, VECU, true>), dim3(grid), dim3(256), lds, s, a);
+        hipLaunchKernelGGL((k_decode<DT, FMT, BC, 4, VECU, true>), dim3(grid), dim3(256), lds, s, ga);
       else
-        hipLaunchKernelGGL((k_decode<DT, FMT, BC, 2, VECU, true>), dim3(grid), dim3(256), lds, s, a);
+        hipLaunchKernelGGL((k_decode<DT, FMT, BC, 2, VECU, true>), dim3(grid), dim3(256), lds, s, ga);
       return;
     }
   }
   if (rpw == 1)
-    hipLaunchKernelGGL((k_decode<DT, FMT, BC, 1, VECU, false>), dim3(grid), dim3(256), lds, s, a);
+    hipLaunchKernelGGL((k_decode<DT, FMT, BC, 1, VECU, false>), dim3(grid), dim3(256), lds, s, ga);
   else  // 2 (four rows per wave are launched FAST only)
-    hipLaunchKernelGGL((k_decode<DT, FMT, BC, 2, VECU, false>), dim3(grid), dim3(256), lds, s, a);
+    hipLaunchKernelGGL((k_decode<DT, FMT, BC, 2, VECU, false>), dim3(grid), dim3(256), lds, s, ga);
 }
 
 template <int DT, int FMT, int BC>
-static void launch_bc(const DecodeArgs& a, bool vecu, bool fast, int rpw, size_t lds, hipStream_t s) {
+static void launch_bc(const GroupArgs& ga, unsigned grid, bool vecu, bool fast, int rpw, size_t lds, hipStream_t s) {
   if constexpr (DT == HSS_BF16) {
-    if (vecu) return launch_v<DT, FMT, BC, true>(a, fast, rpw, lds, s);
+    if (vecu) return launch_v<DT, FMT, BC, true>(ga, grid, fast, rpw, lds, s);
   }
-  launch_v<DT, FMT, BC, false>(a, fast, rpw, lds, s);
+  launch_v<DT, FMT, BC, false>(ga, grid, fast, rpw, lds, s);
 }
 
 template <int DT, int FMT>
-static void launch_fmt(const DecodeArgs& a, bool vecu, bool fast, int rpw, size_t lds, hipStream_t s) {
-  if (a.bc == 1) launch_bc<DT, FMT, 1>(a, vecu, fast, rpw, lds, s);
-  else if (a.bc == 2) launch_bc<DT, FMT, 2>(a, vecu, fast, rpw, lds, s);
-  else if (a.bc <= 4) launch_bc<DT, FMT, 4>(a, vecu, fast, rpw, lds, s);
-  else launch_bc<DT, FMT, 8>(a, vecu, fast, rpw, lds, s);
+static void launch_fmt(const GroupArgs& ga, unsigned grid, int bc, bool vecu, bool fast, int rpw, size_t lds,
+                       hipStream_t s) {
+  if (bc == 1) launch_bc<DT, FMT, 1>(ga, grid, vecu, fast, rpw, lds, s);
+  else if (bc == 2) launch_bc<DT, FMT, 2>(ga, grid, vecu, fast, rpw, lds, s);
+  else if (bc <= 4) launch_bc<DT, FMT, 4>(ga, grid, vecu, fast, rpw, lds, s);
+  else launch_bc<DT, FMT, 8>(ga, grid, vecu, fast, rpw, lds, s);
 }
 
 static constexpr size_t kMaxLds = 60 * 1024;  // dynamic LDS budget per block
@@ -954,15 +975,24 @@ static int spin_limit() {
   return s ? atoi(s) : 4096;
 }
 
-// One fused decode pass over bc columns (1 <= bc <= decode_max_cols(A)).
-void launch_decode(const hss_matrix* A, int bc, const void* X, void* Y, void* ws, hipStream_t s) {
+// Arguments of one matrix of a decode pass, and the per-matrix launch
+// properties the group has to agree on.
+struct MatrixLaunch {
   DecodeArgs a;
+  size_t lds;
+  bool vecu, fast;
+  int rpw;
+};
+
+static MatrixLaunch matrix_launch(const hss_matrix* A, int bc, const void* X, void* Y, uint32_t* ctl, uint64_t* Tt) {
+  MatrixLaunch L;
+  DecodeArgs& a = L.a;
   a.m = A->m; a.n = A->n; a.r = A->r; a.bc = bc;
   a.row_ptr = A->row_ptr; a.col_idx = A->col_idx; a.vals = A->values;
   a.nmv = A->nm_values; a.meta = A->nm_meta;
   a.U = A->U; a.Vt = A->Vt; a.X = X; a.Y = Y;
-  a.ctl = static_cast<uint32_t*>(ws);
-  a.Tt = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + kCtlBytes);
+  a.ctl = ctl;
+  a.Tt = Tt;
   a.t_stride = t_stride_words(A->r);
   a.nnz = A->nnz;
   a.spin = spin_limit();
@@ -987,23 +1017,62 @@ void launch_decode(const hss_matrix* A, int bc, const void* X, void* Y, void* ws
   a.nm_fast = A->fmt == HSS_FMT_2OF4 && A->dtype == HSS_BF16 && a.vec && A->n % 32 == 0 &&
               (uintptr_t)A->nm_values % 16 == 0 && (uintptr_t)A->nm_meta % 4 == 0;
   // bf16 U rows as 8-byte vectors; T rows in LDS (c * r floats) stay 16-byte aligned.
-  const bool vecu = A->dtype == HSS_BF16 && A->r > 0 && A->r % 4 == 0 && (uintptr_t)A->U % 8 == 0;
-  const size_t lds = tbytes + mbytes + (a.x_lds ? xbytes : 0);
-  const bool fast = A->dtype == HSS_BF16 && A->r > 0 && a.x_lds && a.vec &&
-                    (size_t)bc * A->n / 8 <= 256 * (size_t)kXRFast &&
-                    (A->fmt == HSS_FMT_CSR ? a.vec_csr : a.nm_fast);
+  L.vecu = A->dtype == HSS_BF16 && A->r > 0 && A->r % 4 == 0 && (uintptr_t)A->U % 8 == 0;
+  L.lds = tbytes + mbytes + (a.x_lds ? xbytes : 0);
+  L.fast = A->dtype == HSS_BF16 && A->r > 0 && a.x_lds && a.vec &&
+           (size_t)bc * A->n / 8 <= 256 * (size_t)kXRFast &&
+           (A->fmt == HSS_FMT_CSR ? a.vec_csr : a.nm_fast);
   // Rows per wave: more rows per block means fewer copies of X staged through
   // L2 into LDS and fewer blocks queueing loads on each CU (measured best:
   // 2 for 4096 rows, 4 for 11008 rows); small matrices keep one row per wave
   // for parallelism.  Four rows per wave exist only as FAST instances.
-  const int rpw = A->m >= 8192 ? (fast ? 4 : 2) : (A->m >= 2048 ? 2 : 1);
-  if (A->dtype == HSS_F32) {
-    if (A->fmt == HSS_FMT_CSR) launch_fmt<HSS_F32, HSS_FMT_CSR>(a, false, false, rpw, lds, s);
-    else launch_fmt<HSS_F32, HSS_FMT_2OF4>(a, false, false, rpw, lds, s);
-  } else {
-    if (A->fmt == HSS_FMT_CSR) launch_fmt<HSS_BF16, HSS_FMT_CSR>(a, vecu, fast, rpw, lds, s);
-    else launch_fmt<HSS_BF16, HSS_FMT_2OF4>(a, vecu, fast, rpw, lds, s);
+  L.rpw = A->m >= 8192 ? 4 : (A->m >= 2048 ? 2 : 1);
+  return L;
+}
+
+// One fused decode pass over bc columns (1 <= bc <= decode_max_cols of every
+// matrix) for G matrices sharing X (same n, dtype and format); Y[g] is
+// matrix g's output.  The T words of matrix g follow those of matrix g - 1.
+void launch_decode_group(const hss_matrix* const* A, int G, int bc, const void* X, void* const* Y, void* ws,
+                         hipStream_t s) {
+  GroupArgs ga = {};
+  ga.G = G;
+  uint32_t* ctl = static_cast<uint32_t*>(ws);
+  char* tw = static_cast<char*>(ws) + kCtlBytes;
+  size_t lds = 0;
+  bool vecu = true, fast = true;
+  int rpw = 4;
+  MatrixLaunch L[kMaxGroup];
+  for (int g = 0; g < G; ++g) {
+    L[g] = matrix_launch(A[g], bc, X, Y[g], ctl, reinterpret_cast<uint64_t*>(tw));
+    tw += decode_t_bytes(A[g]);
+    lds = lds > L[g].lds ? lds : L[g].lds;
+    vecu = vecu && L[g].vecu;
+    fast = fast && L[g].fast;
+    rpw = rpw < L[g].rpw ? rpw : L[g].rpw;
   }
+  if (!fast && rpw > 2) rpw = 2;
+  ga.prod_start[0] = 0;
+  for (int g = 0; g < G; ++g) {
+    ga.a[g] = L[g].a;
+    ga.prod_start[g + 1] = ga.prod_start[g] + A[g]->r;
+  }
+  ga.row_start[0] = ga.prod_start[G];
+  for (int g = 0; g < G; ++g) ga.row_start[g + 1] = ga.row_start[g] + (A[g]->m + 4 * rpw - 1) / (4 * rpw);
+  for (int g = G; g < kMaxGroup; ++g) { ga.prod_start[g + 1] = ga.prod_start[G]; ga.row_start[g + 1] = ga.row_start[G]; }
+  const unsigned grid = (unsigned)ga.row_start[G];
+  const int dt = A[0]->dtype, fmt = A[0]->fmt;
+  if (dt == HSS_F32) {
+    if (fmt == HSS_FMT_CSR) launch_fmt<HSS_F32, HSS_FMT_CSR>(ga, grid, bc, false, false, rpw, lds, s);
+    else launch_fmt<HSS_F32, HSS_FMT_2OF4>(ga, grid, bc, false, false, rpw, lds, s);
+  } else {
+    if (fmt == HSS_FMT_CSR) launch_fmt<HSS_BF16, HSS_FMT_CSR>(ga, grid, bc, vecu, fast, rpw, lds, s);
+    else launch_fmt<HSS_BF16, HSS_FMT_2OF4>(ga, grid, bc, vecu, fast, rpw, lds, s);
+  }
+}
+
+void launch_decode(const hss_matrix* A, int bc, const void* X, void* Y, void* ws, hipStream_t s) {
+  launch_decode_group(&A, 1, bc, X, &Y, ws, s);
 }
 
 }  // namespace hss

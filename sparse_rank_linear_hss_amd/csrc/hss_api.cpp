@@ -123,4 +123,40 @@ hss_status hss_apply(const hss_matrix* A, int32_t b, const void* X, void* Y, voi
   return hss::launch_apply(A, b, X, Y, ws, stream);
 }
 
+static hss_status check_group(const hss_matrix* const* A, int32_t G, int32_t b) {
+  if (!A || G < 1 || G > HSS_MAX_GROUP) return HSS_ERR_INVALID_ARG;
+  for (int g = 0; g < G; ++g) {
+    const hss_status st = check_matrix(A[g], b);
+    if (st != HSS_OK) return st;
+    if (A[g]->n != A[0]->n || A[g]->dtype != A[0]->dtype || A[g]->fmt != A[0]->fmt) return HSS_ERR_INVALID_ARG;
+  }
+  return HSS_OK;
+}
+
+hss_status hss_apply_group_workspace_size(const hss_matrix* const* A, int32_t G, int32_t b, size_t* bytes) {
+  if (!bytes) return HSS_ERR_INVALID_ARG;
+  const hss_status st = check_group(A, G, b);
+  if (st != HSS_OK) return st;
+  *bytes = hss::apply_group_ws_bytes(A, G, b);
+  return HSS_OK;
+}
+
+hss_status hss_apply_group(const hss_matrix* const* A, int32_t G, int32_t b, const void* X, void* const* Y,
+                           void* ws, size_t ws_bytes, hipStream_t stream) {
+  hss_status st = check_group(A, G, b);
+  if (st != HSS_OK) return st;
+  if (!X || !Y) return HSS_ERR_INVALID_ARG;
+  const size_t es = dsize(A[0]->dtype);
+  const size_t xbytes = (size_t)b * A[0]->n * es;
+  for (int g = 0; g < G; ++g) {
+    if (!Y[g]) return HSS_ERR_INVALID_ARG;
+    const size_t yb = (size_t)b * A[g]->m * es;
+    if (overlap(X, xbytes, Y[g], yb)) return HSS_ERR_INVALID_ARG;
+    for (int h = 0; h < g; ++h)
+      if (overlap(Y[h], (size_t)b * A[h]->m * es, Y[g], yb)) return HSS_ERR_INVALID_ARG;
+  }
+  if (!ws || ws_bytes < hss::apply_group_ws_bytes(A, G, b)) return HSS_ERR_WORKSPACE;
+  return hss::launch_apply_group(A, G, b, X, Y, ws, stream);
+}
+
 }  // extern "C"

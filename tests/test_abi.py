@@ -26,6 +26,7 @@ def hl():
 def test_header_declares_the_boundary():
     names = _declared()
     for must in ("hss_split", "hss_apply", "hss_split_workspace_size", "hss_apply_workspace_size",
+                 "hss_apply_group", "hss_apply_group_workspace_size",
                  "hss_get_error", "hss_topk_count", "hss_status_string", "hss_version"):
         assert must in names
 
@@ -37,7 +38,7 @@ def test_library_exports_every_declared_symbol(hl):
 
 
 def test_version_and_strings(hl):
-    assert hl.hss_version() == 100
+    assert hl.hss_version() == 101
     for code in range(6):
         assert hl.status_string(code).startswith("HSS_")
 
@@ -132,3 +133,36 @@ def test_apply_rejects_bad_arguments(hl):
     assert lib.hss_apply_workspace_size(ctypes.byref(_matrix(hl, r=0, U=None, Vt=None)), 1,
                                         ctypes.byref(sz)) == 0
     assert sz.value >= 256
+
+
+def _group(hl, mats, b=1, X=FAKE + 8192, Ys=None, ws=FAKE * 16, wsb=1 << 20):
+    lib = hl._lib.lib
+    arr = (ctypes.POINTER(hl._lib.HssMatrixStruct) * max(1, len(mats)))(*[ctypes.pointer(m) for m in mats])
+    if Ys is None:
+        Ys = [FAKE * 32 + i * 65536 for i in range(len(mats))]
+    yp = (ctypes.c_void_p * max(1, len(Ys)))(*Ys)
+    return lib.hss_apply_group(arr, len(mats), b, X, yp, ws, wsb, None)
+
+
+def test_apply_group_rejects_bad_arguments(hl):
+    INV, WS = hl._lib.HSS_ERR_INVALID_ARG, hl._lib.HSS_ERR_WORKSPACE
+    lib = hl._lib.lib
+    a, b2 = _matrix(hl), _matrix(hl, m=40)
+    assert lib.hss_apply_group(None, 1, 1, FAKE, None, FAKE, 1 << 20, None) == INV
+    assert _group(hl, []) == INV                                        # G = 0
+    assert _group(hl, [a] * 5) == INV                                   # G > HSS_MAX_GROUP
+    assert _group(hl, [a, _matrix(hl, n=64)]) == INV                    # n differs
+    assert _group(hl, [a, _matrix(hl, dtype=0)]) == INV                 # dtype differs
+    assert _group(hl, [a, _matrix(hl, fmt=1, nm_values=FAKE, nm_meta=FAKE)]) == INV  # format differs
+    assert _group(hl, [a, _matrix(hl, r=-1)]) == INV                    # an invalid member
+    assert _group(hl, [a, b2], X=None) == INV
+    assert _group(hl, [a, b2], Ys=[FAKE * 32, None]) == INV
+    assert _group(hl, [a, b2], Ys=[FAKE * 32, FAKE * 32 + 8]) == INV    # outputs overlap
+    assert _group(hl, [a, b2], X=FAKE * 32 + 4) == INV                  # X overlaps an output
+    assert _group(hl, [a, b2], ws=None) == WS
+    assert _group(hl, [a, b2], wsb=8) == WS
+    sz1, sz2 = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    arr = (ctypes.POINTER(hl._lib.HssMatrixStruct) * 2)(ctypes.pointer(a), ctypes.pointer(b2))
+    assert lib.hss_apply_group_workspace_size(arr, 2, 1, ctypes.byref(sz2)) == 0
+    assert lib.hss_apply_workspace_size(ctypes.byref(a), 1, ctypes.byref(sz1)) == 0
+    assert sz2.value >= sz1.value

@@ -255,3 +255,66 @@ def test_apply_graph_replay_matches_eager(H, fmt, b):
             assert O.bits_equal(to_host(ys[i]), expect[i]), (rep, i)
         # eager work on the same workspace between replays
         assert O.bits_equal(to_host(H.hss_apply(A, xs[rep % 3], ws=ws)), expect[rep % 3])
+
+
+GROUPS = [
+    # (fmt, [(m, r), ...], n, b)
+    ("csr", [(200, 16), (64, 8), (300, 12)], 256, 1),
+    ("csr", [(130, 7), (130, 0), (65, 33)], 96, 3),
+    ("csr", [(2100, 16), (333, 4)], 64, 8),
+    ("2:4", [(300, 8), (300, 8)], 128, 1),
+    ("2:4", [(70, 5), (33, 16), (129, 4)], 64, 5),
+    ("csr", [(150, 16), (90, 8)], 256, 16),
+]
+
+
+@pytest.mark.parametrize("dtype", [O.F32, O.BF16])
+@pytest.mark.parametrize("case", GROUPS, ids=[f"{c[0]}-g{len(c[1])}-n{c[2]}-b{c[3]}" for c in GROUPS])
+def test_apply_group(H, dtype, case):
+    """hss_apply_group: every output within the oracle bound, and bit-equal to
+    hss_apply of the same matrix on the same X."""
+    fmt, shapes, n, b = case
+    X = syn.random_matrix(b, n, dtype, seed=n + b, kind="normal", scale=1.0)
+    Xd = to_dev(X, dtype)
+    mats, refs = [], []
+    for i, (m, r) in enumerate(shapes):
+        W = syn.random_matrix(m, n, dtype, seed=100 + 7 * i + m, kind="t3")
+        ref = O.split_csr(W, dtype, O.topk_count(m, n, 5, 100)) if fmt == "csr" else O.split_24(W, dtype)
+        U, V = _factors(m, n, r, dtype, 200 + i)
+        mats.append(_matrix(H, fmt, dtype, m, n, ref, U, V))
+        S64 = _dense_S(fmt, dtype, m, n, ref)
+        Uw, Vw, Xw = O.widen(U, dtype), O.widen(V, dtype), O.widen(X, dtype)
+        refs.append((O.apply_factored(S64, Uw, Vw, Xw), O.normaliser(S64, Uw, Vw, Xw)))
+    Ys = H.hss_apply_group(mats, Xd)
+    for A, Y, (Yref, N) in zip(mats, Ys, refs):
+        _check(Y, dtype, Yref, N)
+        assert O.bits_equal(to_host(Y), to_host(H.hss_apply(A, Xd)))
+
+
+def test_apply_group_graph_replay(H):
+    """A captured grouped apply replays to the eager result, with eager calls
+    on the same workspace in between."""
+    import torch
+    dtype, n, b = O.BF16, 256, 1
+    mats = []
+    for i, (m, r) in enumerate([(400, 16), (256, 32), (256, 32)]):
+        W = syn.random_matrix(m, n, dtype, seed=500 + i, kind="t3")
+        ref = O.split_csr(W, dtype, O.topk_count(m, n, 5, 100))
+        U, V = _factors(m, n, r, dtype, 600 + i)
+        mats.append(_matrix(H, "csr", dtype, m, n, ref, U, V))
+    xs = [to_dev(syn.random_matrix(b, n, dtype, seed=700 + i, kind="normal", scale=1.0), dtype) for i in range(2)]
+    ws = torch.zeros(H.hss_apply_group_workspace_size(mats, b), dtype=torch.uint8, device="cuda")
+    ys = [[torch.empty((b, A.m), dtype=torch.bfloat16, device="cuda") for A in mats] for _ in xs]
+    expect = [[to_host(y) for y in H.hss_apply_group(mats, x, ws=ws)] for x in xs]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for x, y in zip(xs, ys):
+            H.hss_apply_group(mats, x, y, ws)
+    for rep in range(4):
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(len(xs)):
+            for j in range(len(mats)):
+                assert O.bits_equal(to_host(ys[i][j]), expect[i][j]), (rep, i, j)
+        assert O.bits_equal(to_host(H.hss_apply(mats[0], xs[rep % 2], ws=ws)), expect[rep % 2][0])
