@@ -74,35 +74,55 @@ __global__ void k_split_init(uint32_t* ws, int64_t k) {
 
 // Histogram of digit (key >> shift) & 255 over keys whose bits above
 // shift+8 equal the prefix.  VEC: use 16-byte loads (W 16-byte aligned).
+// Trained (and synthetic heavy-tailed) weights put almost every key of the
+// top digit -- essentially the exponent -- into one or two bins, so a single
+// LDS histogram would serialise whole waves on one address: lane l counts
+// into copy l % 32 instead (copies 257 words apart, so the copies of a bin
+// sit in different banks), and the copies are summed at the end.
+static constexpr int kHistCopies = 32, kHistStride = 257;
+
 template <int DT, bool VEC>
 __global__ __launch_bounds__(256) void k_split_hist(const typename Elem<DT>::bits_t* __restrict__ W,
                                                     int64_t count, uint32_t* __restrict__ ws,
                                                     int shift, int first) {
   using E = Elem<DT>;
-  __shared__ uint32_t h[256];
+  __shared__ uint32_t h[kHistCopies * kHistStride];
   if (ws[W_REM] == 0) return;  // k == 0: uniform across the grid
   const uint32_t prefix = ws[W_PREFIX];
   const int hs = shift + 8;
-  h[threadIdx.x] = 0;
+  for (int i = threadIdx.x; i < kHistCopies * kHistStride; i += 256) h[i] = 0;
   __syncthreads();
+  uint32_t* hc = h + (lane_id() & (kHistCopies - 1)) * kHistStride;
   bool bad = false;
   auto visit = [&](uint32_t bits) {
     const uint32_t key = bits & E::key_mask;
     bad |= first && key >= E::key_inf;
     const uint32_t hi = hs >= 32 ? 0u : (key >> hs);
-    if (hi == prefix) atomicAdd(&h[(key >> shift) & 255u], 1u);
+    if (hi == prefix) atomicAdd(&hc[(key >> shift) & 255u], 1u);
   };
   const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   if (VEC) {
     constexpr int NV = VecLoad<DT>::N;
+    constexpr int U = 4;  // vectors in flight per thread
     const int64_t nvec = count / NV;
     const u32x4* W4 = reinterpret_cast<const u32x4*>(W);
-    for (int64_t v = tid; v < nvec; v += stride) {
-      uint32_t e[NV];
-      VecLoad<DT>::unpack(__builtin_nontemporal_load(W4 + v), e);
+    for (int64_t v0 = tid; v0 < nvec; v0 += U * stride) {
+      u32x4 raw[U];
 #pragma unroll
-      for (int q = 0; q < NV; ++q) visit(e[q]);
+      for (int u = 0; u < U; ++u) {
+        const int64_t v = v0 + u * stride;
+        raw[u] = __builtin_nontemporal_load(W4 + (v < nvec ? v : v0));
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (v0 + u * stride < nvec) {
+          uint32_t e[NV];
+          VecLoad<DT>::unpack(raw[u], e);
+#pragma unroll
+          for (int q = 0; q < NV; ++q) visit(e[q]);
+        }
+      }
     }
     for (int64_t i = nvec * NV + tid; i < count; i += stride) visit(W[i]);
   } else {
@@ -110,26 +130,34 @@ __global__ __launch_bounds__(256) void k_split_hist(const typename Elem<DT>::bit
   }
   if (bad) atomicOr(&ws[W_ERR], 1u);
   __syncthreads();
-  const uint32_t c = h[threadIdx.x];
+  uint32_t c = 0;
+  for (int k = 0; k < kHistCopies; ++k) c += h[k * kHistStride + threadIdx.x];
   if (c) atomicAdd(&ws[W_HIST + threadIdx.x], c);
 }
 
-// Walk the 256-bin histogram from the top; fix the digit of the k-th key.
-__global__ void k_split_pick(uint32_t* __restrict__ ws, int last) {
-  __shared__ uint32_t hs[256];
-  const int t = threadIdx.x;
+// Fix the digit of the k-th largest key: the largest digit d whose suffix
+// count S(d) = sum of bins >= d reaches the remaining rank (digit 0 if none
+// does).  Thread t holds bin 255 - t; an inclusive scan over t gives S(255 - t)
+// and the first thread whose scan reaches the rank (or the last thread) owns
+// the digit; keys above it: S(d + 1).  One block of 256 threads.
+__global__ __launch_bounds__(256) void k_split_pick(uint32_t* __restrict__ ws, int last) {
+  __shared__ uint32_t wsum[4];
+  const int t = threadIdx.x, lane = lane_id(), w = t >> 6;
   const uint32_t rem = ws[W_REM];
   if (rem == 0) return;  // k == 0
-  hs[t] = ws[W_HIST + t];
-  ws[W_HIST + t] = 0;  // ready for the next digit
+  const uint32_t v = ws[W_HIST + 255 - t];
+  ws[W_HIST + 255 - t] = 0;  // ready for the next digit
+  const uint32_t ex = wave_excl_scan_u32(v);
+  if (lane == HSS_WAVE - 1) wsum[w] = ex + v;
   __syncthreads();
-  if (t == 0) {
-    uint32_t above = 0;
-    int d = 255;
-    for (; d > 0; --d) {
-      if (above + hs[d] >= rem) break;
-      above += hs[d];
-    }
+  uint32_t base = 0;
+  for (int k = 0; k < w; ++k) base += wsum[k];
+  const uint32_t incl = base + ex + v;
+  const bool reach = incl >= rem || t == 255;
+  const bool prev = t > 0 && (incl - v >= rem);  // an earlier thread reached it already
+  if (reach && !prev) {
+    const int d = 255 - t;
+    const uint32_t above = incl - v;
     const uint32_t prefix = (ws[W_PREFIX] << 8) | (uint32_t)d;
     ws[W_PREFIX] = prefix;
     ws[W_CGT] += above;
@@ -159,12 +187,25 @@ __global__ __launch_bounds__(256) void k_split_rowcount(const typename Elem<DT>:
   };
   if (VEC) {
     constexpr int NV = VecLoad<DT>::N;
+    constexpr int U = 4;  // vectors in flight per lane
+    const int nvec = n / NV;
     const u32x4* W4 = reinterpret_cast<const u32x4*>(Wr);
-    for (int v = lane; v < n / NV; v += HSS_WAVE) {
-      uint32_t e[NV];
-      VecLoad<DT>::unpack(__builtin_nontemporal_load(W4 + v), e);
+    for (int v0 = lane; v0 < nvec; v0 += U * HSS_WAVE) {
+      u32x4 raw[U];
 #pragma unroll
-      for (int q = 0; q < NV; ++q) visit(e[q]);
+      for (int u = 0; u < U; ++u) {
+        const int v = v0 + u * HSS_WAVE;
+        raw[u] = __builtin_nontemporal_load(W4 + (v < nvec ? v : v0));
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (v0 + u * HSS_WAVE < nvec) {
+          uint32_t e[NV];
+          VecLoad<DT>::unpack(raw[u], e);
+#pragma unroll
+          for (int q = 0; q < NV; ++q) visit(e[q]);
+        }
+      }
     }
   } else {
     for (int j = lane; j < n; j += HSS_WAVE) visit(Wr[j]);
@@ -395,7 +436,8 @@ static hss_status split_csr_t(int m, int n, const void* Wv, int64_t k, int32_t* 
   // Digits of the key, most significant first: f32 keys have 31 bits
   // (shifts 24, 16, 8, 0), bf16 keys 15 bits (shifts 8, 0).
   const int top = Elem<DT>::key_bits > 16 ? 24 : 8;
-  const unsigned hgrid = grid_for(count, 256 * VecLoad<DT>::N, 2048);
+  // ~16 vectors per thread: enough work to amortise the 32-copy histogram per block
+  const unsigned hgrid = grid_for(count, 256 * 16 * VecLoad<DT>::N, 512);
   for (int shift = top; shift >= 0; shift -= 8) {
     if (vec_all)
       hipLaunchKernelGGL((k_split_hist<DT, true>), dim3(hgrid), dim3(256), 0, s, W, count, ws, shift,
