@@ -167,7 +167,8 @@ hss_status hss_apply_workspace_size(const hss_matrix* A, int32_t b, size_t* byte
  *     counter), so the caller must not write to it afterwards; any number of
  *     calls, with any matrices and batch sizes, may then share it as long as
  *     they are ordered (same stream or events).
- * Execution: bf16 with b >= 16 runs on the matrix cores (T^T = X V and Y =
+ * Execution: bf16 with b >= 16 (2:4) or b >= 24 (CSR) runs on the matrix
+ * cores (T^T = X V and Y =
  * [X | T^T] [S | U]^T as MFMA GEMMs with fp32 accumulation; T is rounded to
  * bf16 once, between the two; a CSR S is first expanded into a dense bf16
  * copy inside the workspace, so the workspace then holds m*n*2 more bytes);

@@ -8,9 +8,9 @@
 //   decode (decode.hip)  up to 8 columns per launch: one fused kernel that
 //                        streams S, U and V^T once (HBM-bound regime); fp32
 //                        and narrow batches.
-//   mfma (mfma.hip)      bf16 with b >= 16: the low-rank products are dense
-//                        contractions and run on the matrix cores, with S
-//                        densified chunk by chunk into the same GEMM.
+//   mfma (mfma.hip)      bf16 with b >= 16 (2:4) or b >= 24 (CSR): the
+//                        low-rank products are dense contractions and run on
+//                        the matrix cores, S expanded into the same GEMM.
 #include "hss_internal.h"
 
 namespace hss {

@@ -669,6 +669,7 @@ __device__ __forceinline__ void finish_epoch(const DecodeArgs& a, int nsub, bool
 // unconditionally, so the compiler can count outstanding loads exactly and
 // never waits for the (dependent, slowest) sparse loads before it must.
 static constexpr int kXR = 4;      // staged X vectors per thread held in registers
+static constexpr size_t kMaxLdsAll = 112 * 1024;  // dynamic LDS a decode block may request
 static constexpr int kXRFast = 2;  // FAST: exactly this many, no branches (bc * n <= 4096 bf16)
 
 template <int DT, int FMT, int BC, int RPW, bool VECU, bool FAST>
@@ -905,23 +906,36 @@ __global__ __launch_bounds__(256) void k_decode(GroupArgs ga) {
 }
 
 // ---------------------------------------------------------------------------
+// Launch one instance; more than 64 KiB of dynamic LDS (wide batches: X for
+// 8 columns) must be allowed per kernel first, once.
+template <int DT, int FMT, int BC, int RPW, bool VECU, bool FAST>
+static void launch_k(const GroupArgs& ga, unsigned grid, size_t lds, hipStream_t s) {
+  static bool big_lds = false;
+  if (lds > 64 * 1024 && !big_lds) {
+    hipFuncSetAttribute(reinterpret_cast<const void*>(&k_decode<DT, FMT, BC, RPW, VECU, FAST>),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLdsAll);
+    big_lds = true;
+  }
+  hipLaunchKernelGGL((k_decode<DT, FMT, BC, RPW, VECU, FAST>), dim3(grid), dim3(256), lds, s, ga);
+}
+
 template <int DT, int FMT, int BC, bool VECU>
 static void launch_v(const GroupArgs& ga, unsigned grid, bool fast, int rpw, size_t lds, hipStream_t s) {
   if constexpr (DT == HSS_BF16) {
     if (fast) {
       if (rpw == 1)
-        hipLaunchKernelGGL((k_decode<DT, FMT, BC, 1, VECU, true>), dim3(grid), dim3(256), lds, s, ga);
+        launch_k<DT, FMT, BC, 1, VECU, true>(ga, grid, lds, s);
       else if (rpw == 4)
-        hipLaunchKernelGGL((k_decode<DT, FMT, BC, 4, VECU, true>), dim3(grid), dim3(256), lds, s, ga);
+        launch_k<DT, FMT, BC, 4, VECU, true>(ga, grid, lds, s);
       else
-        hipLaunchKernelGGL((k_decode<DT, FMT, BC, 2, VECU, true>), dim3(grid), dim3(256), lds, s, ga);
+        launch_k<DT, FMT, BC, 2, VECU, true>(ga, grid, lds, s);
       return;
     }
   }
   if (rpw == 1)
-    hipLaunchKernelGGL((k_decode<DT, FMT, BC, 1, VECU, false>), dim3(grid), dim3(256), lds, s, ga);
+    launch_k<DT, FMT, BC, 1, VECU, false>(ga, grid, lds, s);
   else  // 2 (four rows per wave are launched FAST only)
-    hipLaunchKernelGGL((k_decode<DT, FMT, BC, 2, VECU, false>), dim3(grid), dim3(256), lds, s, ga);
+    launch_k<DT, FMT, BC, 2, VECU, false>(ga, grid, lds, s);
 }
 
 template <int DT, int FMT, int BC>
@@ -941,7 +955,14 @@ static void launch_fmt(const GroupArgs& ga, unsigned grid, int bc, bool vecu, bo
   else launch_bc<DT, FMT, 8>(ga, grid, vecu, fast, rpw, lds, s);
 }
 
-static constexpr size_t kMaxLds = 60 * 1024;  // dynamic LDS budget per block
+// Dynamic LDS budget per block.  CSR gathers X at random columns, so X goes
+// to LDS even for 8 columns (64 KiB at n = 4096); 2:4 reads X in contiguous
+// 64-byte chunks that caches serve well, and a large LDS request would halve
+// the blocks per CU, so it keeps the smaller budget (measured: 8 columns of
+// the 11008 x 4096 2:4 layer 45 us with X from cache, 72 us through LDS).
+static constexpr size_t kMaxLdsCsr = 100 * 1024;
+static constexpr size_t kMaxLdsNm = 60 * 1024;
+static size_t max_lds(const hss_matrix* A) { return A->fmt == HSS_FMT_CSR ? kMaxLdsCsr : kMaxLdsNm; }
 
 static size_t align16(size_t x) { return (x + 15) / 16 * 16; }
 
@@ -965,7 +986,7 @@ int decode_max_cols(const hss_matrix* A) {
   for (int bc = 8; bc >= 1; bc /= 2) {
     const size_t tb = align16(sizeof(float) * (size_t)bc * A->r) +
                       align16(4 * (size_t)((A->r + 31) / 32));
-    if (tb <= kMaxLds) return bc;
+    if (tb <= max_lds(A)) return bc;
   }
   return 0;
 }
@@ -1007,7 +1028,7 @@ static MatrixLaunch matrix_launch(const hss_matrix* A, int bc, const void* X, vo
   a.t_off = 0;
   a.miss_off = (int)tbytes;
   a.x_off = (int)(tbytes + mbytes);
-  a.x_lds = tbytes + mbytes + xbytes <= kMaxLds;
+  a.x_lds = tbytes + mbytes + xbytes <= max_lds(A);
   a.x_pad = nm_fast && a.x_lds;
   // Vector dot products: X rows and Vt rows start 16-byte aligned.
   a.vec = ((uintptr_t)X % 16 == 0) && ((size_t)A->n * es) % 16 == 0 &&
