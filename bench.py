@@ -16,7 +16,8 @@ copies.  The timed steps are replayed from a HIP graph (decode loops are
 launch-bound; the kernels keep their cross-call state on the device, so
 replays are exact); the plain stream-launch rate is reported beside it.
 
-Also measured in the same run (extra JSON keys): the same layer at batch 16,
+Also measured in the same run (extra JSON keys): the same layer with 16-bit
+column indices and at batch 16,
 the 11008 x 4096 2:4 layer at batch 1/8/64, one decoder layer's seven
 projections per decode token (q/k/v and gate/up as grouped applies, so four
 launches per token; the seven-launch order beside it), the 8192^2 prefill at
@@ -259,7 +260,15 @@ def main():
 
     extra = {}
     if not args.only_headline:
-        # same layer, batch 16 (matrix cores)
+        # same layer with 16-bit column indices (4 instead of 6 bytes per entry)
+        L16 = type("L16", (), {"mats": [A.with_col16() for A in L.mats]})
+        bytes16 = nnz_head * (2 + 2) + 4 * (m + 1) + (m + n) * cfg.rank[0] * 2
+        ms16c = _time_graph(_apply_loop(H, L16, xs, ys, ws), steps, args.warmup)
+        extra["csr4096_b1_col16"] = {"ms": ms16c, "tokens_per_s": 1 / (ms16c * 1e-3),
+                                     "gbs": bytes16 / (ms16c * 1e-3) / 1e9, "bytes_per_apply": bytes16}
+        del L16
+
+        # same layer, batch 16
         xs16, ys16 = _acts(cfg, 16, 0, 4, m)
         ms16 = _time_graph(_apply_loop(H, L, xs16, ys16, ws), max(1, steps // 4), 20)
         extra["csr4096_b16"] = {"ms": ms16, "tokens_per_s": 16 / (ms16 * 1e-3),

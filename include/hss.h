@@ -43,7 +43,7 @@ extern "C" {
 #endif
 
 #define HSS_VERSION_MAJOR 1
-#define HSS_VERSION_MINOR 1
+#define HSS_VERSION_MINOR 2
 
 typedef enum {
   HSS_OK = 0,
@@ -136,15 +136,21 @@ hss_status hss_get_error(const void* ws, hipStream_t stream);
  *     The nm_* fields are ignored.
  *   fmt == HSS_FMT_2OF4: nm_values dtype[m*n/2], nm_meta uint32[m*ceil(n/32)]
  *     in the layout hss_split writes; CSR fields ignored.
+ *   flags & HSS_COL16: col_idx points to uint16[nnz] columns instead of
+ *     int32 (n <= 65536), 2 bytes per entry less to read ([HSS] implementation
+ *     section: narrower indices for the stored sparse part).  Convert the
+ *     int32 columns hss_split writes with hss_csr_cols_to_u16.
  *   U  dtype[m*r]  row-major m x r.
  *   Vt dtype[r*n]  row-major r x n, i.e. the n x r factor V stored
  *                  column-major, so that V^T x reads contiguous rows.
  */
+#define HSS_COL16 1
+
 typedef struct hss_matrix {
   int32_t fmt;   /* hss_format */
   int32_t dtype; /* hss_dtype  */
   int32_t m, n, r;
-  int32_t reserved; /* must be 0 */
+  int32_t flags;    /* 0, or HSS_COL16 (CSR only: col_idx holds uint16 columns) */
   int64_t nnz;      /* CSR: row_ptr[m] (>= 0); 2:4: ignored */
   const int32_t* row_ptr;
   const int32_t* col_idx;
@@ -154,6 +160,14 @@ typedef struct hss_matrix {
   const void* U;
   const void* Vt;
 } hss_matrix;
+
+/* out[i] = (uint16) col_idx[i] for i < nnz, on `stream`: the 16-bit column
+ * array of an HSS_COL16 matrix.  Requires 0 < n <= 65536 (every column fits);
+ * col_idx and out must not overlap.  Returns HSS_ERR_INVALID_ARG for bad
+ * arguments (nnz < 0, n out of range, null arrays with nnz > 0), HSS_ERR_HIP if
+ * the launch fails. */
+hss_status hss_csr_cols_to_u16(const int32_t* col_idx, int64_t nnz, int32_t n, uint16_t* out,
+                               hipStream_t stream);
 
 /* Workspace bytes hss_apply needs for this matrix and batch size. */
 hss_status hss_apply_workspace_size(const hss_matrix* A, int32_t b, size_t* bytes);
@@ -174,7 +188,8 @@ hss_status hss_apply_workspace_size(const hss_matrix* A, int32_t b, size_t* byte
  * copy inside the workspace, so the workspace then holds m*n*2 more bytes);
  * otherwise one fused kernel per 8 columns.
  * Returns HSS_ERR_INVALID_ARG for: A or X or Y null, unknown fmt/dtype,
- *   reserved != 0, m, n <= 0, r < 0, b < 1, b*m, b*n, m*n, r*(m+n) >= 2^31,
+ *   unknown flags (or HSS_COL16 with a 2:4 matrix or n > 65536),
+ *   m, n <= 0, r < 0, b < 1, b*m, b*n, m*n, r*(m+n) >= 2^31,
  *   nnz < 0, required arrays null, n % 4 != 0 for 2:4, X overlapping Y.
  *   HSS_ERR_WORKSPACE for a null or short workspace.  HSS_ERR_HIP if a launch
  *   fails.

@@ -18,12 +18,13 @@ from typing import Optional
 
 import torch
 
-from ._lib import (HSS_BF16, HSS_ERR_NONFINITE, HSS_F32, HSS_FMT_2OF4, HSS_FMT_CSR, HSS_OK,
+from ._lib import (HSS_BF16, HSS_COL16, HSS_ERR_NONFINITE, HSS_F32, HSS_FMT_2OF4, HSS_FMT_CSR, HSS_OK,
                    HSSError, HssMatrixStruct, LIB_PATH, check, lib, status_string)
 
 __all__ = [
     "hss_version", "hss_topk_count", "hss_split_workspace_size", "hss_split", "hss_get_error",
     "hss_apply_workspace_size", "hss_apply", "hss_apply_group_workspace_size", "hss_apply_group",
+    "hss_csr_cols_to_u16", "HSS_COL16",
     "HSSMatrix", "SplitResult", "HSSError",
     "LIB_PATH", "status_string",
 ]
@@ -133,11 +134,14 @@ class HSSMatrix:
     """Compressed matrix S + U V^T in device memory; keeps its tensors alive.
 
     U: m x r row-major.  The factor V (n x r) is held as Vt (r x n row-major,
-    i.e. V column-major), the layout the library reads."""
+    i.e. V column-major), the layout the library reads.  CSR col_idx is
+    int32, or 16-bit (a torch.int16 tensor holding the uint16 columns, n <=
+    65536, see hss_csr_cols_to_u16) -- the matrix then carries HSS_COL16."""
 
     def __init__(self, fmt, m, n, dtype, U=None, Vt=None, row_ptr=None, col_idx=None, values=None,
                  nnz=None, nm_values=None, nm_meta=None):
         self.fmt = _FMT[fmt]
+        self.flags = HSS_COL16 if (col_idx is not None and col_idx.dtype == torch.int16) else 0
         self.m, self.n = int(m), int(n)
         self.dtype = dtype
         self.U, self.Vt = U, Vt
@@ -151,7 +155,7 @@ class HSSMatrix:
         self._ws = {}
         s = HssMatrixStruct()
         s.fmt, s.dtype = self.fmt, _DT[dtype]
-        s.m, s.n, s.r, s.reserved = self.m, self.n, self.r, 0
+        s.m, s.n, s.r, s.flags = self.m, self.n, self.r, self.flags
         s.nnz = self.nnz
         s.row_ptr, s.col_idx, s.values = _ptr(row_ptr), _ptr(col_idx), _ptr(values)
         s.nm_values, s.nm_meta = _ptr(nm_values), _ptr(nm_meta)
@@ -168,6 +172,16 @@ class HSSMatrix:
             return cls("csr", sp.m, sp.n, dtype, U=U, Vt=Vt, row_ptr=sp.row_ptr,
                        col_idx=sp.col_idx, values=sp.values, nnz=sp.k)
         return cls("2:4", sp.m, sp.n, dtype, U=U, Vt=Vt, nm_values=sp.nm_values, nm_meta=sp.nm_meta)
+
+    def with_col16(self) -> "HSSMatrix":
+        """The same CSR matrix with 16-bit columns (converted on the device)."""
+        if self.fmt != HSS_FMT_CSR:
+            raise ValueError("16-bit columns are a CSR option")
+        c16 = hss_csr_cols_to_u16(self.col_idx, self.n) if self.nnz > 0 else None
+        return HSSMatrix("csr", self.m, self.n, self.dtype, U=self.U, Vt=self.Vt, row_ptr=self.row_ptr,
+                         col_idx=c16 if c16 is not None else torch.zeros(0, dtype=torch.int16,
+                                                                           device=self.row_ptr.device),
+                         values=self.values, nnz=self.nnz)
 
     def workspace(self, b: int, device=None) -> torch.Tensor:
         """Zero-filled workspace for batch b (cached per device and size)."""
@@ -234,3 +248,15 @@ def hss_apply_group(As, X: torch.Tensor, Ys=None, ws: Optional[torch.Tensor] = N
     check(lib.hss_apply_group(_group_structs(As), len(As), b, _ptr(X), yp, _ptr(ws), ws.numel(),
                               _stream(dev)), "hss_apply_group")
     return Ys
+
+
+def hss_csr_cols_to_u16(col_idx: torch.Tensor, n: int) -> torch.Tensor:
+    """16-bit copy of int32 CSR columns (n <= 65536), as a torch.int16 tensor
+    holding the uint16 bit patterns."""
+    dev = _dev(col_idx)
+    if col_idx.dtype != torch.int32 or not col_idx.is_contiguous():
+        raise ValueError("col_idx must be a contiguous int32 tensor")
+    out = torch.empty(col_idx.numel(), dtype=torch.int16, device=dev)
+    check(lib.hss_csr_cols_to_u16(_ptr(col_idx), col_idx.numel(), int(n), _ptr(out), _stream(dev)),
+          "hss_csr_cols_to_u16")
+    return out

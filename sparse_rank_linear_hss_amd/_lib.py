@@ -19,6 +19,7 @@ HSS_F32 = 0
 HSS_BF16 = 1
 HSS_FMT_CSR = 0
 HSS_FMT_2OF4 = 1
+HSS_COL16 = 1  # hss_matrix.flags: CSR col_idx holds uint16 columns
 
 c_int32, c_int64, c_size_t, c_void_p = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
 
@@ -27,7 +28,7 @@ class HssMatrixStruct(ctypes.Structure):
     """Mirror of struct hss_matrix in include/hss.h."""
     _fields_ = [
         ("fmt", c_int32), ("dtype", c_int32),
-        ("m", c_int32), ("n", c_int32), ("r", c_int32), ("reserved", c_int32),
+        ("m", c_int32), ("n", c_int32), ("r", c_int32), ("flags", c_int32),
         ("nnz", c_int64),
         ("row_ptr", c_void_p), ("col_idx", c_void_p), ("values", c_void_p),
         ("nm_values", c_void_p), ("nm_meta", c_void_p),
@@ -44,7 +45,7 @@ class HSSError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m sparse_rank_linear_hss_amd.build` "
+            f"{LIB_PATH} is missing: build it with `python sparse_rank_linear_hss_amd/build.py` "
             "(hipcc, gfx950). There is no non-HIP fallback.")
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER
@@ -60,6 +61,7 @@ def _load():
         "hss_apply_workspace_size": (ctypes.c_int, [P(HssMatrixStruct), c_int32, P(c_size_t)]),
         "hss_apply": (ctypes.c_int, [P(HssMatrixStruct), c_int32, c_void_p, c_void_p, c_void_p,
                                      c_size_t, c_void_p]),
+        "hss_csr_cols_to_u16": (ctypes.c_int, [c_void_p, c_int64, c_int32, c_void_p, c_void_p]),
         "hss_apply_group_workspace_size": (ctypes.c_int, [P(P(HssMatrixStruct)), c_int32, c_int32,
                                                           P(c_size_t)]),
         "hss_apply_group": (ctypes.c_int, [P(P(HssMatrixStruct)), c_int32, c_int32, c_void_p, P(c_void_p),

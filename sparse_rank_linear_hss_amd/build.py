@@ -1,6 +1,7 @@
 """Build libhss.so (the C-ABI library) in-tree with hipcc for gfx950.
 
-    python -m sparse_rank_linear_hss_amd.build        # or: python sparse_rank_linear_hss_amd/build.py
+    python sparse_rank_linear_hss_amd/build.py   (standalone: it does not import the package,
+                                                 which loads the library it builds)
 
 Each source compiles to an object in _build/ (in parallel), then one link
 step writes sparse_rank_linear_hss_amd/libhss.so next to this file.

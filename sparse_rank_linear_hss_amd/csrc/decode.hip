@@ -54,7 +54,8 @@ static constexpr int kTReplicas = 8;
 struct DecodeArgs {
   int m, n, r, bc;
   const int32_t* row_ptr;
-  const int32_t* col_idx;
+  const int32_t* col_idx;  // 32-bit columns, or
+  const uint16_t* col16;   // 16-bit columns (FMT == kFmtCsr16)
   const void* vals;
   const void* nmv;
   const uint32_t* meta;
@@ -89,6 +90,29 @@ struct GroupArgs {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Kernel format: HSS_FMT_CSR (32-bit columns), HSS_FMT_2OF4, or CSR with
+// 16-bit columns (n <= 65536: 4 instead of 6 bytes per bf16 entry).
+static constexpr int kFmtCsr16 = 2;
+template <int FMT> constexpr bool is_csr = FMT != HSS_FMT_2OF4;
+
+// Columns of entries ec .. ec + 3 (ec a multiple of 4), as a 16-byte (32-bit
+// columns) or 8-byte (16-bit columns) vector load.
+template <int FMT>
+__device__ __forceinline__ u32x4 col_chunk(const DecodeArgs& a, int64_t ec) {
+  if constexpr (FMT == kFmtCsr16) {
+    const u32x2 c = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(a.col16 + ec));
+    return u32x4{c.x & 0xffffu, c.x >> 16, c.y & 0xffffu, c.y >> 16};
+  } else {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.col_idx + ec));
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ int col_at(const DecodeArgs& a, int64_t p) {
+  if constexpr (FMT == kFmtCsr16) return a.col16[p];
+  else return a.col_idx[p];
+}
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
@@ -204,16 +228,19 @@ struct CsrChunks {
   uint32_t tcol, tval;  // lane k < 4: entry (nnz & ~3) + k of the array tail
 };
 
-template <int DT, int RPW>
+template <int DT, int FMT, int RPW>
 __device__ __forceinline__ void csr_tail_issue(const DecodeArgs& a, CsrChunks<DT, RPW>& ch) {
   using bits_t = typename Elem<DT>::bits_t;
   const int64_t e = (a.nnz & ~(int64_t)3) + (lane_id() & 3);
   const int64_t ec = e < a.nnz - 1 ? e : a.nnz - 1;
-  ch.tcol = (uint32_t)__builtin_nontemporal_load(a.col_idx + ec);
+  if constexpr (FMT == kFmtCsr16)
+    ch.tcol = (uint32_t)__builtin_nontemporal_load(a.col16 + ec);
+  else
+    ch.tcol = (uint32_t)__builtin_nontemporal_load(a.col_idx + ec);
   ch.tval = (uint32_t)__builtin_nontemporal_load(static_cast<const bits_t*>(a.vals) + ec);
 }
 
-template <int DT, int RPW>
+template <int DT, int FMT, int RPW>
 __device__ __forceinline__ void csr_issue(const DecodeArgs& a, const int (&rb)[RPW + 1],
                                           CsrChunks<DT, RPW>& ch) {
   using bits_t = typename Elem<DT>::bits_t;
@@ -228,7 +255,7 @@ __device__ __forceinline__ void csr_issue(const DecodeArgs& a, const int (&rb)[R
     ch.e0[i] = (ch.st[i] & ~3) + 4 * lane;
     if (a.vec_csr) {
       const int64_t ec = ch.e0[i] < last ? ch.e0[i] : last;
-      ch.cq[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.col_idx + ec));
+      ch.cq[i] = col_chunk<FMT>(a, ec);
       ch.vq[i] = __builtin_nontemporal_load(reinterpret_cast<const vchunk_t*>(vals + ec));
     }
   }
@@ -284,7 +311,7 @@ __device__ __forceinline__ void csr_chunk_fma(const ChunkX<DT, BC>& g, float (&a
   }
 }
 
-template <int DT, int BC, int RPW>
+template <int DT, int FMT, int BC, int RPW>
 __device__ __forceinline__ void csr_consume(const DecodeArgs& a, CsrChunks<DT, RPW>& ch,
                                             const typename Elem<DT>::bits_t* __restrict__ xsrc,
                                             float (&ssum)[RPW][BC]) {
@@ -319,7 +346,7 @@ __device__ __forceinline__ void csr_consume(const DecodeArgs& a, CsrChunks<DT, R
       for (int base = (st & ~3) + 256; base < en; base += 256) {  // rows longer than 256 - 3
         const int e = base + 4 * lane;
         const int64_t ec = e < last ? e : last;
-        const u32x4 cc = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.col_idx + ec));
+        const u32x4 cc = col_chunk<FMT>(a, ec);
         const vchunk_t vv = __builtin_nontemporal_load(reinterpret_cast<const vchunk_t*>(vals + ec));
         ChunkX<DT, BC> gl;
         csr_chunk_gather<DT, BC>(a, e, st, en, cc, vv, ch.tcol, ch.tval, xsrc, gl);
@@ -328,7 +355,7 @@ __device__ __forceinline__ void csr_consume(const DecodeArgs& a, CsrChunks<DT, R
     } else {
       for (int p = st + lane; p < en; p += 64) {
         const float v = fval<DT>(vals[p]);
-        const int col = a.col_idx[p];
+        const int col = col_at<FMT>(a, p);
 #pragma unroll
         for (int c = 0; c < BC; ++c)
           if (c < a.bc) acc[c] = fmaf(v, fval<DT>(xsrc[(int64_t)c * a.n + col]), acc[c]);
@@ -689,7 +716,7 @@ __global__ __launch_bounds__(256) void k_decode(GroupArgs ga) {
   if constexpr (FAST) {
     a.x_lds = 1;
     a.vec = 1;
-    a.vec_csr = FMT == HSS_FMT_CSR;
+    a.vec_csr = is_csr<FMT>;
     a.nm_fast = FMT == HSS_FMT_2OF4;
     a.x_pad = FMT == HSS_FMT_2OF4;
     __builtin_assume(a.r > 0);
@@ -742,7 +769,7 @@ __global__ __launch_bounds__(256) void k_decode(GroupArgs ga) {
   // row bounds: uniform addresses, scalar loads (own counter, so waiting for
   // them does not wait for the vector loads below)
   int rb[RPW + 1];
-  if constexpr (FMT == HSS_FMT_CSR) {
+  if constexpr (is_csr<FMT>) {
 #pragma unroll
     for (int i = 0; i <= RPW; ++i) rb[i] = a.row_ptr[min(row0 + i, m)];
   }
@@ -755,12 +782,12 @@ __global__ __launch_bounds__(256) void k_decode(GroupArgs ga) {
   NmWords<RPW> nw;
   if constexpr (FMT == HSS_FMT_2OF4) nm_issue<DT, RPW>(a, row0, nw);
   CsrChunks<DT, RPW> ch;
-  if constexpr (FMT == HSS_FMT_CSR) {
-    if (a.vec_csr) csr_tail_issue<DT, RPW>(a, ch);
+  if constexpr (is_csr<FMT>) {
+    if (a.vec_csr) csr_tail_issue<DT, FMT, RPW>(a, ch);
   }
 
   // CSR chunks: the one dependent load
-  if constexpr (FMT == HSS_FMT_CSR) csr_issue<DT, RPW>(a, rb, ch);
+  if constexpr (is_csr<FMT>) csr_issue<DT, FMT, RPW>(a, rb, ch);
 
   // X for LDS, issued last: writing it to LDS waits for every load above,
   // all of which the sparse part needs right after the barrier anyway.
@@ -829,8 +856,8 @@ __global__ __launch_bounds__(256) void k_decode(GroupArgs ga) {
 
   // sparse part
   float ssum[RPW][BC];
-  if constexpr (FMT == HSS_FMT_CSR)
-    csr_consume<DT, BC, RPW>(a, ch, xsrc, ssum);
+  if constexpr (is_csr<FMT>)
+    csr_consume<DT, FMT, BC, RPW>(a, ch, xsrc, ssum);
   else
     nm_consume<DT, BC, RPW>(a, row0, nw, xsrc, ssum);
 
@@ -963,6 +990,7 @@ static void launch_fmt(const GroupArgs& ga, unsigned grid, int bc, bool vecu, bo
 static constexpr size_t kMaxLdsCsr = 100 * 1024;
 static constexpr size_t kMaxLdsNm = 60 * 1024;
 static size_t max_lds(const hss_matrix* A) { return A->fmt == HSS_FMT_CSR ? kMaxLdsCsr : kMaxLdsNm; }
+static bool col16_of(const hss_matrix* A) { return A->fmt == HSS_FMT_CSR && (A->flags & HSS_COL16); }
 
 static size_t align16(size_t x) { return (x + 15) / 16 * 16; }
 
@@ -1009,7 +1037,9 @@ static MatrixLaunch matrix_launch(const hss_matrix* A, int bc, const void* X, vo
   MatrixLaunch L;
   DecodeArgs& a = L.a;
   a.m = A->m; a.n = A->n; a.r = A->r; a.bc = bc;
-  a.row_ptr = A->row_ptr; a.col_idx = A->col_idx; a.vals = A->values;
+  a.row_ptr = A->row_ptr; a.vals = A->values;
+  a.col_idx = col16_of(A) ? nullptr : A->col_idx;
+  a.col16 = col16_of(A) ? reinterpret_cast<const uint16_t*>(A->col_idx) : nullptr;
   a.nmv = A->nm_values; a.meta = A->nm_meta;
   a.U = A->U; a.Vt = A->Vt; a.X = X; a.Y = Y;
   a.ctl = ctl;
@@ -1033,7 +1063,7 @@ static MatrixLaunch matrix_launch(const hss_matrix* A, int bc, const void* X, vo
   // Vector dot products: X rows and Vt rows start 16-byte aligned.
   a.vec = ((uintptr_t)X % 16 == 0) && ((size_t)A->n * es) % 16 == 0 &&
           (A->r == 0 || (uintptr_t)A->Vt % 16 == 0);
-  a.vec_csr = A->fmt == HSS_FMT_CSR && A->nnz >= 4 && (uintptr_t)A->col_idx % 16 == 0 &&
+  a.vec_csr = A->fmt == HSS_FMT_CSR && A->nnz >= 4 && (uintptr_t)A->col_idx % (col16_of(A) ? 8 : 16) == 0 &&
               (uintptr_t)A->values % (4 * es) == 0;
   a.nm_fast = A->fmt == HSS_FMT_2OF4 && A->dtype == HSS_BF16 && a.vec && A->n % 32 == 0 &&
               (uintptr_t)A->nm_values % 16 == 0 && (uintptr_t)A->nm_meta % 4 == 0;
@@ -1082,12 +1112,14 @@ void launch_decode_group(const hss_matrix* const* A, int G, int bc, const void* 
   for (int g = 0; g < G; ++g) ga.row_start[g + 1] = ga.row_start[g] + (A[g]->m + 4 * rpw - 1) / (4 * rpw);
   for (int g = G; g < kMaxGroup; ++g) { ga.prod_start[g + 1] = ga.prod_start[G]; ga.row_start[g + 1] = ga.row_start[G]; }
   const unsigned grid = (unsigned)ga.row_start[G];
-  const int dt = A[0]->dtype, fmt = A[0]->fmt;
+  const int dt = A[0]->dtype, fmt = col16_of(A[0]) ? kFmtCsr16 : A[0]->fmt;
   if (dt == HSS_F32) {
     if (fmt == HSS_FMT_CSR) launch_fmt<HSS_F32, HSS_FMT_CSR>(ga, grid, bc, false, false, rpw, lds, s);
+    else if (fmt == kFmtCsr16) launch_fmt<HSS_F32, kFmtCsr16>(ga, grid, bc, false, false, rpw, lds, s);
     else launch_fmt<HSS_F32, HSS_FMT_2OF4>(ga, grid, bc, false, false, rpw, lds, s);
   } else {
     if (fmt == HSS_FMT_CSR) launch_fmt<HSS_BF16, HSS_FMT_CSR>(ga, grid, bc, vecu, fast, rpw, lds, s);
+    else if (fmt == kFmtCsr16) launch_fmt<HSS_BF16, kFmtCsr16>(ga, grid, bc, vecu, fast, rpw, lds, s);
     else launch_fmt<HSS_BF16, HSS_FMT_2OF4>(ga, grid, bc, vecu, fast, rpw, lds, s);
   }
 }

@@ -87,8 +87,9 @@ hss_status hss_get_error(const void* ws, hipStream_t stream) {
 }
 
 static hss_status check_matrix(const hss_matrix* A, int32_t b) {
-  if (!A || !valid_fmt(A->fmt) || !valid_dtype(A->dtype) || A->reserved != 0)
+  if (!A || !valid_fmt(A->fmt) || !valid_dtype(A->dtype) || (A->flags & ~HSS_COL16) != 0)
     return HSS_ERR_INVALID_ARG;
+  if ((A->flags & HSS_COL16) && (A->fmt != HSS_FMT_CSR || A->n > 65536)) return HSS_ERR_INVALID_ARG;
   const int64_t m = A->m, n = A->n, r = A->r;
   if (m <= 0 || n <= 0 || r < 0 || b < 1) return HSS_ERR_INVALID_ARG;
   if (m * n >= kLimit || (int64_t)b * m >= kLimit || (int64_t)b * n >= kLimit ||
@@ -102,6 +103,14 @@ static hss_status check_matrix(const hss_matrix* A, int32_t b) {
     if (n % 4 != 0 || !A->nm_values || !A->nm_meta) return HSS_ERR_INVALID_ARG;
   }
   return HSS_OK;
+}
+
+hss_status hss_csr_cols_to_u16(const int32_t* col_idx, int64_t nnz, int32_t n, uint16_t* out,
+                               hipStream_t stream) {
+  if (nnz < 0 || n <= 0 || n > 65536) return HSS_ERR_INVALID_ARG;
+  if (nnz == 0) return HSS_OK;
+  if (!col_idx || !out || overlap(col_idx, (size_t)nnz * 4, out, (size_t)nnz * 2)) return HSS_ERR_INVALID_ARG;
+  return hss::launch_cols_to_u16(col_idx, nnz, out, stream);
 }
 
 hss_status hss_apply_workspace_size(const hss_matrix* A, int32_t b, size_t* bytes) {
@@ -128,7 +137,9 @@ static hss_status check_group(const hss_matrix* const* A, int32_t G, int32_t b) 
   for (int g = 0; g < G; ++g) {
     const hss_status st = check_matrix(A[g], b);
     if (st != HSS_OK) return st;
-    if (A[g]->n != A[0]->n || A[g]->dtype != A[0]->dtype || A[g]->fmt != A[0]->fmt) return HSS_ERR_INVALID_ARG;
+    if (A[g]->n != A[0]->n || A[g]->dtype != A[0]->dtype || A[g]->fmt != A[0]->fmt ||
+        A[g]->flags != A[0]->flags)
+      return HSS_ERR_INVALID_ARG;
   }
   return HSS_OK;
 }

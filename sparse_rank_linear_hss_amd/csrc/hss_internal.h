@@ -115,6 +115,7 @@ size_t apply_ws_bytes(const hss_matrix* A, int b);
 hss_status launch_apply(const hss_matrix* A, int b, const void* X, void* Y, void* ws,
                         hipStream_t stream);
 size_t apply_group_ws_bytes(const hss_matrix* const* A, int G, int b);
+hss_status launch_cols_to_u16(const int32_t* col_idx, int64_t nnz, uint16_t* out, hipStream_t stream);
 hss_status launch_apply_group(const hss_matrix* const* A, int G, int b, const void* X, void* const* Y, void* ws,
                               hipStream_t stream);
 }  // namespace hss

@@ -410,8 +410,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(GemmArgs g) {
 // the row is zeroed with 16-byte stores, a fence waits for those stores, then
 // the lanes scatter the row's entries (no other wave touches the row).
 // Segment 1 of the batched apply then reads S as a dense operand.
+template <typename COL>
 __global__ __launch_bounds__(256) void k_csr_densify(const int32_t* __restrict__ row_ptr,
-                                                     const int32_t* __restrict__ col_idx,
+                                                     const COL* __restrict__ col_idx,
                                                      const uint16_t* __restrict__ vals, int m, int n,
                                                      uint16_t* __restrict__ D) {
   const int lane = threadIdx.x & 63;
@@ -570,9 +571,15 @@ hss_status launch_mfma(const hss_matrix* A, int b, const void* X, void* Y, void*
   const bool csr = A->fmt == HSS_FMT_CSR;
   const bool s_empty = csr_empty(A);  // segment 1 has no work
 
-  if (csr && !s_empty)
-    hipLaunchKernelGGL(k_csr_densify, dim3((unsigned)cdiv(m, 4)), dim3(256), 0, s, A->row_ptr, A->col_idx,
-                       static_cast<const uint16_t*>(A->values), m, n, Sd);
+  if (csr && !s_empty) {
+    const dim3 grid((unsigned)cdiv(m, 4));
+    const uint16_t* vals = static_cast<const uint16_t*>(A->values);
+    if (A->flags & HSS_COL16)
+      hipLaunchKernelGGL(k_csr_densify<uint16_t>, grid, dim3(256), 0, s, A->row_ptr,
+                         reinterpret_cast<const uint16_t*>(A->col_idx), vals, m, n, Sd);
+    else
+      hipLaunchKernelGGL(k_csr_densify<int32_t>, grid, dim3(256), 0, s, A->row_ptr, A->col_idx, vals, m, n, Sd);
+  }
   // T^T (b x r) = X . Vt^T
   if (r > 0) {
     GemmArgs g = {};

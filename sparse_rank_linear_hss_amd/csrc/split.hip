@@ -462,6 +462,18 @@ static hss_status split_csr_t(int m, int n, const void* Wv, int64_t k, int32_t* 
   return hipGetLastError() == hipSuccess ? HSS_OK : HSS_ERR_HIP;
 }
 
+// 16-bit copy of CSR columns (every column < 65536 by the caller's check).
+__global__ __launch_bounds__(256) void k_cols_to_u16(const int32_t* __restrict__ col, int64_t nnz,
+                                                     uint16_t* __restrict__ out) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nnz; i += stride) out[i] = (uint16_t)col[i];
+}
+
+hss_status launch_cols_to_u16(const int32_t* col_idx, int64_t nnz, uint16_t* out, hipStream_t stream) {
+  hipLaunchKernelGGL(k_cols_to_u16, dim3(grid_for(nnz, 256 * 4, 4096)), dim3(256), 0, stream, col_idx, nnz, out);
+  return hipGetLastError() == hipSuccess ? HSS_OK : HSS_ERR_HIP;
+}
+
 hss_status launch_split_csr(int dt, int m, int n, const void* W, int64_t k, int32_t* row_ptr,
                             int32_t* col_idx, void* values, void* residual, void* ws,
                             hipStream_t stream) {

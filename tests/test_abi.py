@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(hl):
 
 
 def test_version_and_strings(hl):
-    assert hl.hss_version() == 101
+    assert hl.hss_version() == 102
     for code in range(6):
         assert hl.status_string(code).startswith("HSS_")
 
@@ -94,7 +94,7 @@ def test_split_workspace_size(hl):
 
 def _matrix(hl, **kw):
     s = hl._lib.HssMatrixStruct()
-    s.fmt, s.dtype, s.m, s.n, s.r, s.reserved, s.nnz = 0, 1, 16, 32, 4, 0, 10
+    s.fmt, s.dtype, s.m, s.n, s.r, s.flags, s.nnz = 0, 1, 16, 32, 4, 0, 10
     s.row_ptr = s.col_idx = s.values = FAKE
     s.U, s.Vt = FAKE, FAKE + 4096
     for k, v in kw.items():
@@ -112,7 +112,9 @@ def test_apply_rejects_bad_arguments(hl):
     assert lib.hss_apply(None, 1, FAKE, FAKE * 2, FAKE * 3, 1 << 20, None) == INV
     assert _apply(hl, _matrix(hl, fmt=5)) == INV
     assert _apply(hl, _matrix(hl, dtype=3)) == INV
-    assert _apply(hl, _matrix(hl, reserved=1)) == INV
+    assert _apply(hl, _matrix(hl, flags=2)) == INV                  # unknown flag
+    assert _apply(hl, _matrix(hl, fmt=1, flags=1, nm_values=FAKE, nm_meta=FAKE)) == INV  # COL16 on 2:4
+    assert _apply(hl, _matrix(hl, flags=1, n=65537)) == INV         # COL16 needs n <= 65536
     assert _apply(hl, _matrix(hl, m=0)) == INV
     assert _apply(hl, _matrix(hl, r=-1)) == INV
     assert _apply(hl, _matrix(hl), b=0) == INV

@@ -318,3 +318,47 @@ def test_apply_group_graph_replay(H):
             for j in range(len(mats)):
                 assert O.bits_equal(to_host(ys[i][j]), expect[i][j]), (rep, i, j)
         assert O.bits_equal(to_host(H.hss_apply(mats[0], xs[rep % 2], ws=ws)), expect[rep % 2][0])
+
+
+COL16 = [
+    # (m, n, r, b): every decode regime, the matrix-core densify and the large tile
+    (300, 640, 128, 1), (130, 1000, 64, 3), (2053, 256, 16, 1), (8195, 64, 12, 2), (96, 4104, 33, 8),
+    (257, 512, 8, 24), (300, 640, 128, 300), (5, 13, 2, 3),
+]
+
+
+@pytest.mark.parametrize("dtype", [O.F32, O.BF16])
+@pytest.mark.parametrize("case", COL16, ids=[f"{c[0]}x{c[1]}-r{c[2]}-b{c[3]}" for c in COL16])
+def test_apply_col16(H, dtype, case):
+    """16-bit CSR columns: the same result bit for bit as 32-bit columns, and
+    within the oracle bound."""
+    m, n, r, b = case
+    W = syn.random_matrix(m, n, dtype, seed=900 + m + n, kind="t3")
+    ref = O.split_csr(W, dtype, O.topk_count(m, n, 5, 100))
+    U, V = _factors(m, n, r, dtype, 901)
+    X = syn.random_matrix(b, n, dtype, seed=902 + b, kind="normal", scale=1.0)
+    A32 = _matrix(H, "csr", dtype, m, n, ref, U, V)
+    A16 = A32.with_col16()
+    assert A16.struct.flags == H.HSS_COL16
+    assert np.array_equal(to_host(A16.col_idx).view(np.uint16).astype(np.int64), ref["col_idx"].astype(np.int64))
+    Xd = to_dev(X, dtype)
+    Y16, Y32 = H.hss_apply(A16, Xd), H.hss_apply(A32, Xd)
+    assert O.bits_equal(to_host(Y16), to_host(Y32))
+    S64 = _dense_S("csr", dtype, m, n, ref)
+    Uw, Vw, Xw = O.widen(U, dtype), O.widen(V, dtype), O.widen(X, dtype)
+    _check(Y16, dtype, O.apply_factored(S64, Uw, Vw, Xw), O.normaliser(S64, Uw, Vw, Xw))
+
+
+def test_apply_group_col16(H):
+    dtype, n, b = O.BF16, 256, 1
+    X = to_dev(syn.random_matrix(b, n, dtype, seed=77, kind="normal", scale=1.0), dtype)
+    mats = []
+    for i, (m, r) in enumerate([(200, 16), (64, 8)]):
+        W = syn.random_matrix(m, n, dtype, seed=78 + i, kind="t3")
+        ref = O.split_csr(W, dtype, O.topk_count(m, n, 5, 100))
+        U, V = _factors(m, n, r, dtype, 80 + i)
+        mats.append(_matrix(H, "csr", dtype, m, n, ref, U, V))
+    y32 = H.hss_apply_group(mats, X)
+    y16 = H.hss_apply_group([A.with_col16() for A in mats], X)
+    for a, c in zip(y32, y16):
+        assert O.bits_equal(to_host(a), to_host(c))
