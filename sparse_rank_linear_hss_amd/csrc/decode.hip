@@ -143,19 +143,26 @@ __device__ __forceinline__ float dot16(const u32x4& a, const u32x4& b, float acc
 
 __device__ __forceinline__ uint32_t tag_of(uint32_t epoch) { return epoch + 1u; }
 
-template <int BC>
+// Sum of the NW per-wave partials red[w][c] in a fixed order (NW = 4, 8 or 16).
+template <int BC, int NW>
 __device__ __forceinline__ float red_sum(float (*red)[BC], int c) {
-  return (red[0][c] + red[1][c]) + (red[2][c] + red[3][c]);
+  float s = (red[0][c] + red[1][c]) + (red[2][c] + red[3][c]);
+  if constexpr (NW >= 8) s += (red[4][c] + red[5][c]) + (red[6][c] + red[7][c]);
+  if constexpr (NW == 16) {
+    s += ((red[8][c] + red[9][c]) + (red[10][c] + red[11][c])) +
+         ((red[12][c] + red[13][c]) + (red[14][c] + red[15][c]));
+  }
+  return s;
 }
 
-// Block-wide T[c][l] = Vt[l,:] . X[c,:] for c < bc (all 256 threads).  Thread
-// t covers 16-byte vectors q = t + 256k; TV of them (per operand) are loaded
+// Block-wide T[c][l] = Vt[l,:] . X[c,:] for c < bc (all NT threads).  Thread
+// t covers 16-byte vectors q = t + NT*k; TV of them (per operand) are loaded
 // before any is used.  Slots past the end load vector 0 (one address for the
 // whole wave, a single request) and are skipped at use; clamping them to the
 // last vector instead would send every block to the same L2 line.  Leaves
-// the four wave sums in red[w][c] (the caller adds them in a fixed order)
-// after a barrier.
-template <int DT, int BC>
+// the NT/64 wave sums in red[w][c] (the caller adds them with red_sum) after a
+// barrier.
+template <int DT, int BC, int NT>
 __device__ __forceinline__ void t_row(const typename Elem<DT>::bits_t* __restrict__ v,
                                       const typename Elem<DT>::bits_t* __restrict__ xsrc, int n,
                                       int bc, int vec, float (*red)[BC]) {
@@ -170,12 +177,12 @@ __device__ __forceinline__ void t_row(const typename Elem<DT>::bits_t* __restric
     constexpr int NV = 16 / sizeof(bits_t);
     const int nv = n / NV;
     const u32x4* v4 = reinterpret_cast<const u32x4*>(v);
-    for (int base = 0; base < nv; base += 256 * TV) {
+    for (int base = 0; base < nv; base += NT * TV) {
       u32x4 vv[TV], xv[TV][BC];
 #pragma unroll
       for (int k = 0; k < TV; ++k) {
-        if (base + 256 * k < nv) {  // block-uniform: skip slices wholly past the end
-          const int q = base + t + 256 * k;
+        if (base + NT * k < nv) {  // block-uniform: skip slices wholly past the end
+          const int q = base + t + NT * k;
           const int qc = q < nv ? q : 0;
           vv[k] = __builtin_nontemporal_load(v4 + qc);
 #pragma unroll
@@ -185,7 +192,7 @@ __device__ __forceinline__ void t_row(const typename Elem<DT>::bits_t* __restric
       }
 #pragma unroll
       for (int k = 0; k < TV; ++k) {
-        if (base + t + 256 * k < nv) {
+        if (base + t + NT * k < nv) {
 #pragma unroll
           for (int c = 0; c < BC; ++c)
             if (c < bc) acc[c] = dot16<DT>(vv[k], xv[k][c], acc[c]);
@@ -194,7 +201,7 @@ __device__ __forceinline__ void t_row(const typename Elem<DT>::bits_t* __restric
     }
     jt = nv * NV;
   }
-  for (int j = jt + t; j < n; j += 256) {
+  for (int j = jt + t; j < n; j += NT) {
     const float vj = fval<DT>(v[j]);
 #pragma unroll
     for (int c = 0; c < BC; ++c)
@@ -695,13 +702,30 @@ __device__ __forceinline__ void finish_epoch(const DecodeArgs& a, int nsub, bool
 // those flags fixed at compile time every load of the prologue is issued
 // unconditionally, so the compiler can count outstanding loads exactly and
 // never waits for the (dependent, slowest) sparse loads before it must.
+//
+// MERGED instances (one CSR matrix, one column, FAST) have no producer
+// blocks: kMergedThreads-thread blocks, no more than there are CUs (all
+// resident at once), each own 8*RPW rows and also produce T row `local`
+// (r <= blocks).  The epoch, X and that Vt row are loaded first; each wave
+// adds its share of the row's dot product as soon as they return, and the
+// last wave to do so (an LDS counter) publishes the row.  The block's CSR
+// chunks are requested only then, so they do not queue ahead of the Vt rows
+// that every block waits for.  X is staged once per block of 8 waves instead
+// of once per 4, and the T reads after the barrier find the CU's load queue
+// nearly empty.  (Measured on the 4096^2 layer: 512 threads beat 1024, whose
+// 4096 waves take ~1 us to launch, delaying the last T rows.)
 static constexpr int kXR = 4;      // staged X vectors per thread held in registers
 static constexpr size_t kMaxLdsAll = 112 * 1024;  // dynamic LDS a decode block may request
 static constexpr int kXRFast = 2;  // FAST: exactly this many, no branches (bc * n <= 4096 bf16)
+static constexpr int kMergedThreads = 512;  // MERGED block size
 
-template <int DT, int FMT, int BC, int RPW, bool VECU, bool FAST>
-__global__ __launch_bounds__(256) void k_decode(GroupArgs ga) {
+template <int DT, int FMT, int BC, int RPW, bool VECU, bool FAST, int MNT>
+__global__ __launch_bounds__(MNT > 0 ? MNT : 256) void k_decode(GroupArgs ga) {
   using bits_t = typename Elem<DT>::bits_t;
+  constexpr bool MERGED = MNT > 0;  // producers merged into MNT-thread row blocks
+  static_assert(!MERGED || (FAST && BC == 1), "merged producers: one column, FAST only");
+  constexpr int NT = MERGED ? MNT : 256;  // threads per block
+  constexpr int NW = NT / 64;              // waves per block
   // this block's matrix and its index among that matrix's producer or row blocks
   const int bid = blockIdx.x;
   const bool producer = bid < ga.prod_start[ga.G];
@@ -722,9 +746,14 @@ __global__ __launch_bounds__(256) void k_decode(GroupArgs ga) {
     __builtin_assume(a.r > 0);
     __builtin_assume(a.bc * a.n > 0 && a.bc * a.n <= 256 * kXRFast * (16 / (int)sizeof(bits_t)));
   }
+  if constexpr (MERGED) {
+    a.bc = 1;
+    __builtin_assume(a.r <= ga.row_start[gi + 1] - ga.row_start[gi]);
+  }
   extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ float red[4][BC];
+  __shared__ float red[NW][BC];
   __shared__ uint32_t epoch_sh;
+  __shared__ uint32_t tdone_sh;  // MERGED: waves that have added their share of the T row
 
   const int t = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave index, uniform
@@ -744,13 +773,14 @@ __global__ __launch_bounds__(256) void k_decode(GroupArgs ga) {
   if (producer) {
     const int l = local;
     const uint32_t e = load_epoch(a);
-    t_row<DT, BC>(Vt + (int64_t)l * n, X, n, bc, a.vec, red);
+    t_row<DT, BC, NT>(Vt + (int64_t)l * n, X, n, bc, a.vec, red);
     if (t == 0) {
       const uint32_t arrived = arrive_issue(a, sub, e);
 #pragma unroll
       for (int c = 0; c < BC; ++c) {
         if (c < bc) {
-          const uint64_t word = (uint64_t)__float_as_uint(red_sum<BC>(red, c)) | ((uint64_t)tag_of(e) << 32);
+          const uint64_t word =
+              (uint64_t)__float_as_uint(red_sum<BC, NW>(red, c)) | ((uint64_t)tag_of(e) << 32);
           for (int rep = 0; rep < kTReplicas; ++rep)
             __hip_atomic_store(a.Tt + (int64_t)rep * a.t_stride + (int64_t)c * r + l, word,
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -764,7 +794,8 @@ __global__ __launch_bounds__(256) void k_decode(GroupArgs ga) {
   }
 
   // ---- row blocks ----
-  const int row0 = (local * 4 + w) * RPW;  // wave-uniform
+  const int row0 = (local * NW + w) * RPW;  // wave-uniform
+  if (MERGED && t == 0) tdone_sh = 0;
 
   // row bounds: uniform addresses, scalar loads (own counter, so waiting for
   // them does not wait for the vector loads below)
@@ -774,9 +805,42 @@ __global__ __launch_bounds__(256) void k_decode(GroupArgs ga) {
     for (int i = 0; i <= RPW; ++i) rb[i] = a.row_ptr[min(row0 + i, m)];
   }
 
-  // vector loads that depend on nothing: epoch, U rows, 2:4 words
+  constexpr int NV = 16 / sizeof(bits_t);
+  const bool xreg = a.x_lds && a.vec;
+  const int xvecs = xreg ? bc * n / NV : 0;
+  constexpr int XR = MERGED ? 1 : (FAST ? kXRFast : kXR);
+  if constexpr (FAST) __builtin_assume(xvecs > 0 && xvecs <= NT * XR);
+  u32x4 xr[XR];
+  // Lanes past the end read vector 0: one address for the whole wave (a
+  // single request, served from L1), where clamping to the last vector would
+  // pile every block onto one L2 line.  FAST loads its XR vectors with no
+  // branch at all (a branch around them makes the compiler hold several
+  // times the registers there).
+  auto x_issue = [&]() {
+    if (FAST || xvecs > 0) {
+#pragma unroll
+      for (int k = 0; k < XR; ++k) {
+        if (FAST || NT * k < xvecs) {  // block-uniform
+          const int q = t + NT * k;
+          xr[k] = reinterpret_cast<const u32x4*>(X)[q < xvecs ? q : 0];
+        }
+      }
+    }
+  };
+
+  // MERGED: the epoch, X and this block's Vt row go out first, so the T row
+  // can be published as soon as they return (loads return in issue order).
   uint32_t epoch = 0;
-  if (r > 0) epoch = load_epoch(a);
+  u32x4 vt;
+  const int tl = local < r ? local : 0;  // blocks past r load row 0 and publish nothing
+  if constexpr (MERGED) {
+    epoch = load_epoch(a);
+    x_issue();
+    vt = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Vt + (int64_t)tl * n) + (t < xvecs ? t : 0));
+  }
+
+  // vector loads that depend on nothing: epoch, U rows, 2:4 words
+  if (!MERGED && r > 0) epoch = load_epoch(a);
   uint32_t ub[RPW][kUPL];
   if (r > 0) u_issue<DT, RPW, VECU>(a, row0, ub);
   NmWords<RPW> nw;
@@ -786,30 +850,36 @@ __global__ __launch_bounds__(256) void k_decode(GroupArgs ga) {
     if (a.vec_csr) csr_tail_issue<DT, FMT, RPW>(a, ch);
   }
 
-  // CSR chunks: the one dependent load
-  if constexpr (is_csr<FMT>) csr_issue<DT, FMT, RPW>(a, rb, ch);
+  // CSR chunks: the one dependent load (MERGED: after the T row is out)
+  if constexpr (is_csr<FMT> && !MERGED) csr_issue<DT, FMT, RPW>(a, rb, ch);
 
-  // X for LDS, issued last: writing it to LDS waits for every load above,
-  // all of which the sparse part needs right after the barrier anyway.
-  constexpr int NV = 16 / sizeof(bits_t);
-  const bool xreg = a.x_lds && a.vec;
-  const int xvecs = xreg ? bc * n / NV : 0;
-  constexpr int XR = FAST ? kXRFast : kXR;
-  if constexpr (FAST) __builtin_assume(xvecs > 0 && xvecs <= 256 * XR);
-  // Lanes past the end read vector 0: one address for the whole wave (a
-  // single request, served from L1), where clamping to the last vector would
-  // pile every block onto one L2 line.  FAST loads its XR vectors with no
-  // branch at all (a branch around them makes the compiler hold several
-  // times the registers there).
-  u32x4 xr[XR];
-  if (FAST || xvecs > 0) {
-#pragma unroll
-    for (int k = 0; k < XR; ++k) {
-      if (FAST || 256 * k < xvecs) {  // block-uniform
-        const int q = t + 256 * k;
-        xr[k] = reinterpret_cast<const u32x4*>(X)[q < xvecs ? q : 0];
-      }
+  // X for LDS, issued last otherwise: writing it to LDS waits for every load
+  // above, all of which the sparse part needs right after the barrier anyway.
+  if constexpr (!MERGED) x_issue();
+
+  if constexpr (MERGED) {
+    // this wave's share of T row tl (X vector t times Vt vector t), then the
+    // last wave publishes the fixed-order sum of all shares.  The barrier
+    // only orders the counter's reset before its increments; it does not
+    // wait for the loads in flight.
+    __syncthreads();
+    const float p = wave_sum(t < xvecs ? dot16<DT>(vt, xr[0], 0.f) : 0.f);
+    uint32_t done = 0;
+    if (lane_id() == 0) {
+      red[w][0] = p;
+      asm volatile("" ::: "memory");  // the share is written before the count (LDS keeps a wave's order)
+      done = __hip_atomic_fetch_add(&tdone_sh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
+    done = (uint32_t)__builtin_amdgcn_readlane((int)done, 0);
+    if (done == (uint32_t)NW - 1 && local < r) {
+      asm volatile("" ::: "memory");
+      const uint64_t word = (uint64_t)__float_as_uint(red_sum<BC, NW>(red, 0)) | ((uint64_t)tag_of(epoch) << 32);
+      const int rep = lane_id();
+      if (rep < kTReplicas)
+        __hip_atomic_store(a.Tt + (int64_t)rep * a.t_stride + local, word, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if constexpr (is_csr<FMT>) csr_issue<DT, FMT, RPW>(a, rb, ch);
   }
 
   if (r > 0 && t == 0) epoch_sh = epoch;
@@ -817,17 +887,17 @@ __global__ __launch_bounds__(256) void k_decode(GroupArgs ga) {
     u32x4* dst = reinterpret_cast<u32x4*>(xs);
 #pragma unroll
     for (int k = 0; k < XR; ++k) {
-      const int q = t + 256 * k;
+      const int q = t + NT * k;
       if (q < xvecs) dst[a.x_pad ? q + (q >> 2) : q] = xr[k];
     }
   }
-  for (int q = t; q < (r + 31) / 32; q += 256) miss[q] = 0;
+  for (int q = t; q < (r + 31) / 32; q += NT) miss[q] = 0;
   if (xvecs > 0) {
     u32x4* dst = reinterpret_cast<u32x4*>(xs);
-    for (int q = t + 256 * XR; q < xvecs; q += 256)
+    for (int q = t + NT * XR; q < xvecs; q += NT)
       dst[a.x_pad ? q + (q >> 2) : q] = reinterpret_cast<const u32x4*>(X)[q];
   } else if (a.x_lds) {
-    for (int q = t; q < bc * n; q += 256) xs[q] = X[q];
+    for (int q = t; q < bc * n; q += NT) xs[q] = X[q];
   }
   // Arrival right before the barrier: every load above has returned (X went
   // last), so nothing later waits for this atomic by accident.
@@ -842,14 +912,14 @@ __global__ __launch_bounds__(256) void k_decode(GroupArgs ga) {
   // branch is copied into its merged value at once, which waits for it --
   // so slots past the end re-read a word this block reads anyway.  A word
   // still stale here is re-read below.
-  constexpr int kTW = FAST ? 2 : 4;
+  constexpr int kTW = MERGED ? 1 : (FAST ? 2 : 4);
   const uint64_t* __restrict__ Tr = a.Tt + (int64_t)(blockIdx.x % kTReplicas) * a.t_stride;
   const int ttotal = bc * r;
   uint64_t tv[kTW];
   if constexpr (FAST) {
 #pragma unroll
     for (int k = 0; k < kTW; ++k) {
-      const int e = t + 256 * k;
+      const int e = t + NT * k;
       tv[k] = __hip_atomic_load(Tr + (e < ttotal ? e : e % ttotal), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
@@ -870,18 +940,18 @@ __global__ __launch_bounds__(256) void k_decode(GroupArgs ga) {
   // check, bounded polling of stale words, then local computation of any row
   // still missing.
   if (r > 0) {
-    for (int base = 0; base < ttotal; base += kTW * 256) {
+    for (int base = 0; base < ttotal; base += kTW * NT) {
       if (!FAST || base > 0) {
 #pragma unroll
         for (int k = 0; k < kTW; ++k) {
-          const int e = base + t + 256 * k;
+          const int e = base + t + NT * k;
           tv[k] = __hip_atomic_load(Tr + (e < ttotal ? e : e % ttotal), __ATOMIC_RELAXED,
                                     __HIP_MEMORY_SCOPE_AGENT);
         }
       }
 #pragma unroll
       for (int k = 0; k < kTW; ++k) {
-        const int e = base + t + 256 * k;
+        const int e = base + t + NT * k;
         if (e < ttotal) {
           uint64_t v = tv[k];
           for (int s = 0; (uint32_t)(v >> 32) != tag && s < a.spin; ++s) {
@@ -903,8 +973,8 @@ __global__ __launch_bounds__(256) void k_decode(GroupArgs ga) {
       while (bits) {
         const int l = wi * 32 + __ffs(bits) - 1;
         bits &= bits - 1;
-        t_row<DT, BC>(Vt + (int64_t)l * n, a.x_pad ? X : xsrc, n, bc, a.vec, red);
-        if (t < bc) Ts[(int64_t)t * r + l] = red_sum<BC>(red, t);
+        t_row<DT, BC, NT>(Vt + (int64_t)l * n, a.x_pad ? X : xsrc, n, bc, a.vec, red);
+        if (t < bc) Ts[(int64_t)t * r + l] = red_sum<BC, NW>(red, t);
         __syncthreads();
       }
     }
@@ -932,23 +1002,54 @@ __global__ __launch_bounds__(256) void k_decode(GroupArgs ga) {
   if (t == 0) finish_epoch(a, nsub, sub_last, top, tag);
 }
 
+// Compute units of the current device, cached per device.
+static int cu_count() {
+  static int cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) cache[dev] = v;
+  }
+  return cache[dev];
+}
+
+// HSS_DECODE_MERGED=0 keeps separate producer blocks (a diagnostic switch).
+static bool merged_enabled() {
+  const char* s = getenv("HSS_DECODE_MERGED");
+  return !(s && s[0] == '0');
+}
+
 // ---------------------------------------------------------------------------
 // Launch one instance; more than 64 KiB of dynamic LDS (wide batches: X for
 // 8 columns) must be allowed per kernel first, once.
-template <int DT, int FMT, int BC, int RPW, bool VECU, bool FAST>
+template <int DT, int FMT, int BC, int RPW, bool VECU, bool FAST, int MNT = 0>
 static void launch_k(const GroupArgs& ga, unsigned grid, size_t lds, hipStream_t s) {
   static bool big_lds = false;
   if (lds > 64 * 1024 && !big_lds) {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(&k_decode<DT, FMT, BC, RPW, VECU, FAST>),
+    hipFuncSetAttribute(reinterpret_cast<const void*>(&k_decode<DT, FMT, BC, RPW, VECU, FAST, MNT>),
                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLdsAll);
     big_lds = true;
   }
-  hipLaunchKernelGGL((k_decode<DT, FMT, BC, RPW, VECU, FAST>), dim3(grid), dim3(256), lds, s, ga);
+  hipLaunchKernelGGL((k_decode<DT, FMT, BC, RPW, VECU, FAST, MNT>), dim3(grid), dim3(MNT > 0 ? MNT : 256), lds, s,
+                     ga);
 }
 
 template <int DT, int FMT, int BC, bool VECU>
-static void launch_v(const GroupArgs& ga, unsigned grid, bool fast, int rpw, size_t lds, hipStream_t s) {
+static void launch_v(const GroupArgs& ga, unsigned grid, bool fast, bool merged, int rpw, size_t lds,
+                     hipStream_t s) {
   if constexpr (DT == HSS_BF16) {
+    if constexpr (BC == 1 && VECU && is_csr<FMT>) {
+      if (merged) {
+        if (rpw == 1)
+          launch_k<DT, FMT, 1, 1, true, true, kMergedThreads>(ga, grid, lds, s);
+        else if (rpw == 4)
+          launch_k<DT, FMT, 1, 4, true, true, kMergedThreads>(ga, grid, lds, s);
+        else
+          launch_k<DT, FMT, 1, 2, true, true, kMergedThreads>(ga, grid, lds, s);
+        return;
+      }
+    }
     if (fast) {
       if (rpw == 1)
         launch_k<DT, FMT, BC, 1, VECU, true>(ga, grid, lds, s);
@@ -966,20 +1067,21 @@ static void launch_v(const GroupArgs& ga, unsigned grid, bool fast, int rpw, siz
 }
 
 template <int DT, int FMT, int BC>
-static void launch_bc(const GroupArgs& ga, unsigned grid, bool vecu, bool fast, int rpw, size_t lds, hipStream_t s) {
+static void launch_bc(const GroupArgs& ga, unsigned grid, bool vecu, bool fast, bool merged, int rpw, size_t lds,
+                      hipStream_t s) {
   if constexpr (DT == HSS_BF16) {
-    if (vecu) return launch_v<DT, FMT, BC, true>(ga, grid, fast, rpw, lds, s);
+    if (vecu) return launch_v<DT, FMT, BC, true>(ga, grid, fast, merged, rpw, lds, s);
   }
-  launch_v<DT, FMT, BC, false>(ga, grid, fast, rpw, lds, s);
+  launch_v<DT, FMT, BC, false>(ga, grid, fast, false, rpw, lds, s);
 }
 
 template <int DT, int FMT>
-static void launch_fmt(const GroupArgs& ga, unsigned grid, int bc, bool vecu, bool fast, int rpw, size_t lds,
-                       hipStream_t s) {
-  if (bc == 1) launch_bc<DT, FMT, 1>(ga, grid, vecu, fast, rpw, lds, s);
-  else if (bc == 2) launch_bc<DT, FMT, 2>(ga, grid, vecu, fast, rpw, lds, s);
-  else if (bc <= 4) launch_bc<DT, FMT, 4>(ga, grid, vecu, fast, rpw, lds, s);
-  else launch_bc<DT, FMT, 8>(ga, grid, vecu, fast, rpw, lds, s);
+static void launch_fmt(const GroupArgs& ga, unsigned grid, int bc, bool vecu, bool fast, bool merged, int rpw,
+                       size_t lds, hipStream_t s) {
+  if (bc == 1) launch_bc<DT, FMT, 1>(ga, grid, vecu, fast, merged, rpw, lds, s);
+  else if (bc == 2) launch_bc<DT, FMT, 2>(ga, grid, vecu, fast, false, rpw, lds, s);
+  else if (bc <= 4) launch_bc<DT, FMT, 4>(ga, grid, vecu, fast, false, rpw, lds, s);
+  else launch_bc<DT, FMT, 8>(ga, grid, vecu, fast, false, rpw, lds, s);
 }
 
 // Dynamic LDS budget per block.  CSR gathers X at random columns, so X goes
@@ -1047,6 +1149,7 @@ static MatrixLaunch matrix_launch(const hss_matrix* A, int bc, const void* X, vo
   a.t_stride = t_stride_words(A->r);
   a.nnz = A->nnz;
   a.spin = spin_limit();
+
   const size_t es = A->dtype == HSS_F32 ? 4 : 2;
   const size_t tbytes = align16(sizeof(float) * (size_t)bc * A->r);
   const size_t mbytes = align16(4 * (size_t)((A->r + 31) / 32));
@@ -1103,24 +1206,40 @@ void launch_decode_group(const hss_matrix* const* A, int G, int bc, const void* 
     rpw = rpw < L[g].rpw ? rpw : L[g].rpw;
   }
   if (!fast && rpw > 2) rpw = 2;
+  // One column of one matrix: producers merged into 1024-thread row blocks
+  // when, with the fewest rows per wave that allow it, there are at most as
+  // many blocks as CUs (all resident at once) and at least r of them.
+  bool merged = false;
+  if (G == 1 && bc == 1 && fast && vecu && A[0]->fmt == HSS_FMT_CSR && merged_enabled()) {
+    const int cus = cu_count();
+    const int mw = kMergedThreads / 64;
+    for (int rp = 1; rp <= 4 && !merged; rp *= 2) {
+      const int nb = (A[0]->m + mw * rp - 1) / (mw * rp);
+      if (nb <= cus && A[0]->r <= nb) {
+        merged = true;
+        rpw = rp;
+      }
+    }
+  }
   ga.prod_start[0] = 0;
   for (int g = 0; g < G; ++g) {
     ga.a[g] = L[g].a;
-    ga.prod_start[g + 1] = ga.prod_start[g] + A[g]->r;
+    ga.prod_start[g + 1] = ga.prod_start[g] + (merged ? 0 : A[g]->r);
   }
   ga.row_start[0] = ga.prod_start[G];
-  for (int g = 0; g < G; ++g) ga.row_start[g + 1] = ga.row_start[g] + (A[g]->m + 4 * rpw - 1) / (4 * rpw);
+  const int rows_per_block = (merged ? kMergedThreads / 64 : 4) * rpw;
+  for (int g = 0; g < G; ++g) ga.row_start[g + 1] = ga.row_start[g] + (A[g]->m + rows_per_block - 1) / rows_per_block;
   for (int g = G; g < kMaxGroup; ++g) { ga.prod_start[g + 1] = ga.prod_start[G]; ga.row_start[g + 1] = ga.row_start[G]; }
   const unsigned grid = (unsigned)ga.row_start[G];
   const int dt = A[0]->dtype, fmt = col16_of(A[0]) ? kFmtCsr16 : A[0]->fmt;
   if (dt == HSS_F32) {
-    if (fmt == HSS_FMT_CSR) launch_fmt<HSS_F32, HSS_FMT_CSR>(ga, grid, bc, false, false, rpw, lds, s);
-    else if (fmt == kFmtCsr16) launch_fmt<HSS_F32, kFmtCsr16>(ga, grid, bc, false, false, rpw, lds, s);
-    else launch_fmt<HSS_F32, HSS_FMT_2OF4>(ga, grid, bc, false, false, rpw, lds, s);
+    if (fmt == HSS_FMT_CSR) launch_fmt<HSS_F32, HSS_FMT_CSR>(ga, grid, bc, false, false, false, rpw, lds, s);
+    else if (fmt == kFmtCsr16) launch_fmt<HSS_F32, kFmtCsr16>(ga, grid, bc, false, false, false, rpw, lds, s);
+    else launch_fmt<HSS_F32, HSS_FMT_2OF4>(ga, grid, bc, false, false, false, rpw, lds, s);
   } else {
-    if (fmt == HSS_FMT_CSR) launch_fmt<HSS_BF16, HSS_FMT_CSR>(ga, grid, bc, vecu, fast, rpw, lds, s);
-    else if (fmt == kFmtCsr16) launch_fmt<HSS_BF16, kFmtCsr16>(ga, grid, bc, vecu, fast, rpw, lds, s);
-    else launch_fmt<HSS_BF16, HSS_FMT_2OF4>(ga, grid, bc, vecu, fast, rpw, lds, s);
+    if (fmt == HSS_FMT_CSR) launch_fmt<HSS_BF16, HSS_FMT_CSR>(ga, grid, bc, vecu, fast, merged, rpw, lds, s);
+    else if (fmt == kFmtCsr16) launch_fmt<HSS_BF16, kFmtCsr16>(ga, grid, bc, vecu, fast, merged, rpw, lds, s);
+    else launch_fmt<HSS_BF16, HSS_FMT_2OF4>(ga, grid, bc, vecu, fast, merged, rpw, lds, s);
   }
 }
 

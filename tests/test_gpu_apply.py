@@ -74,6 +74,10 @@ SMALL = [
     ("2:4", 8197, 128, 8, 1), ("2:4", 8197, 128, 8, 5), ("2:4", 2050, 64, 6, 2),
     # large batches: 256 x 128 tiles (ragged M and N, K tails not a multiple of the stage)
     ("csr", 300, 640, 128, 300), ("csr", 257, 1000, 72, 260), ("2:4", 100, 256, 16, 256),
+    # one CSR column, bf16: T producers merged into 512-thread row blocks (r <= blocks <= CUs),
+    # with a ragged last block, r equal to the block count, blocks past r, 1, 2 and 4 rows per wave
+    ("csr", 1030, 512, 40, 1), ("csr", 4096, 1024, 256, 1), ("csr", 100, 128, 4, 1),
+    ("csr", 7990, 256, 60, 1), ("csr", 2047, 64, 252, 1), ("2:4", 2100, 256, 16, 1),
 ]
 
 
@@ -176,12 +180,14 @@ def test_apply_config5_sampled(H):
     _sampled_check(H, 5, 0, 2048, rows)
 
 
-@pytest.mark.parametrize("fmt,dtype,b", [("csr", O.BF16, 1), ("csr", O.F32, 3), ("2:4", O.BF16, 8),
-                                         ("2:4", O.F32, 2)])
-def test_apply_local_fallback_is_bitwise_identical(H, monkeypatch, fmt, dtype, b):
+@pytest.mark.parametrize("fmt,dtype,b,m", [("csr", O.BF16, 1, 300), ("csr", O.F32, 3, 300), ("2:4", O.BF16, 8, 300),
+                                           ("2:4", O.F32, 2, 300), ("csr", O.BF16, 1, 1030),
+                                           ("2:4", O.BF16, 1, 1030)])
+def test_apply_local_fallback_is_bitwise_identical(H, monkeypatch, fmt, dtype, b, m):
     """With a zero poll budget every block computes the T rows it finds stale
-    itself; the result must be bit-identical to the normal hand-off."""
-    m, n, r = 300, 512, 40
+    itself; the result must be bit-identical to the normal hand-off (m = 1030
+    at one bf16 CSR column: the T rows come from the row blocks themselves)."""
+    n, r = 512, 40
     W = syn.random_matrix(m, n, dtype, seed=21, kind="t3")
     ref = O.split_csr(W, dtype, O.topk_count(m, n, 5, 100)) if fmt == "csr" else O.split_24(W, dtype)
     U, V = _factors(m, n, r, dtype, 22)
@@ -226,13 +232,14 @@ def test_apply_shared_workspace_many_calls(H):
         assert O.bits_equal(to_host(Y), expect[k][i]), (it, k, i)
 
 
-@pytest.mark.parametrize("fmt,b", [("csr", 1), ("csr", 5), ("2:4", 1), ("csr", 32), ("2:4", 64)])
-def test_apply_graph_replay_matches_eager(H, fmt, b):
+@pytest.mark.parametrize("fmt,b,m", [("csr", 1, 200), ("csr", 5, 200), ("2:4", 1, 200), ("csr", 32, 200),
+                                     ("2:4", 64, 200), ("csr", 1, 1030), ("2:4", 1, 1030)])
+def test_apply_graph_replay_matches_eager(H, fmt, b, m):
     """hss_apply captured into a HIP graph: every replay (with eager calls on
     the same workspace in between) reproduces the eager result bit for bit."""
     import torch
     dtype = O.BF16
-    m, n, r = 200, 256, 48
+    n, r = 256, 48
     W = syn.random_matrix(m, n, dtype, seed=41, kind="t3")
     ref = O.split_csr(W, dtype, O.topk_count(m, n, 5, 100)) if fmt == "csr" else O.split_24(W, dtype)
     U, V = _factors(m, n, r, dtype, 42)
