@@ -703,28 +703,27 @@ __device__ __forceinline__ void finish_epoch(const DecodeArgs& a, int nsub, bool
 // unconditionally, so the compiler can count outstanding loads exactly and
 // never waits for the (dependent, slowest) sparse loads before it must.
 //
-// MERGED instances (one CSR matrix, one column, FAST) have no producer
-// blocks: kMergedThreads-thread blocks, no more than there are CUs (all
-// resident at once), each own 8*RPW rows and also produce T row `local`
-// (r <= blocks).  The epoch, X and that Vt row are loaded first; each wave
-// adds its share of the row's dot product as soon as they return, and the
-// last wave to do so (an LDS counter) publishes the row.  The block's CSR
-// chunks are requested only then, so they do not queue ahead of the Vt rows
-// that every block waits for.  X is staged once per block of 8 waves instead
-// of once per 4, and the T reads after the barrier find the CU's load queue
-// nearly empty.  (Measured on the 4096^2 layer: 512 threads beat 1024, whose
-// 4096 waves take ~1 us to launch, delaying the last T rows.)
+// MERGED instances (CSR, one column, FAST; MTR > 0) have no producer blocks:
+// kMergedThreads-thread blocks, at most one per CU, own 8*RPW rows each, and block `local` of a matrix with nb blocks also produces T rows
+// local + nb*i (i < MTR, while below r).  The epoch, X and those Vt rows are
+// loaded first; each wave adds its share of the rows' dot products as soon as
+// they return, and the last wave to do so (an LDS counter) publishes them.
+// The block's CSR chunks are requested only then, so they do not queue ahead
+// of the Vt rows that every block waits for.  X is staged once per block of 8
+// waves instead of once per 4, and the T reads after the barrier find the
+// CU's load queue nearly empty.  (Measured on the 4096^2 layer: 512 threads
+// beat 1024, whose 4096 waves take ~1 us to launch, delaying the last T rows.)
 static constexpr int kXR = 4;      // staged X vectors per thread held in registers
 static constexpr size_t kMaxLdsAll = 112 * 1024;  // dynamic LDS a decode block may request
 static constexpr int kXRFast = 2;  // FAST: exactly this many, no branches (bc * n <= 4096 bf16)
 static constexpr int kMergedThreads = 512;  // MERGED block size
 
-template <int DT, int FMT, int BC, int RPW, bool VECU, bool FAST, int MNT>
-__global__ __launch_bounds__(MNT > 0 ? MNT : 256) void k_decode(GroupArgs ga) {
+template <int DT, int FMT, int BC, int RPW, bool VECU, bool FAST, int MTR>
+__global__ __launch_bounds__(MTR > 0 ? kMergedThreads : 256) void k_decode(GroupArgs ga) {
   using bits_t = typename Elem<DT>::bits_t;
-  constexpr bool MERGED = MNT > 0;  // producers merged into MNT-thread row blocks
-  static_assert(!MERGED || (FAST && BC == 1), "merged producers: one column, FAST only");
-  constexpr int NT = MERGED ? MNT : 256;  // threads per block
+  constexpr bool MERGED = MTR > 0;  // producers merged into the row blocks, MTR T rows each at most
+  static_assert(!MERGED || (FAST && BC == 1 && is_csr<FMT>), "merged producers: one CSR column, FAST only");
+  constexpr int NT = MERGED ? kMergedThreads : 256;  // threads per block
   constexpr int NW = NT / 64;              // waves per block
   // this block's matrix and its index among that matrix's producer or row blocks
   const int bid = blockIdx.x;
@@ -746,14 +745,16 @@ __global__ __launch_bounds__(MNT > 0 ? MNT : 256) void k_decode(GroupArgs ga) {
     __builtin_assume(a.r > 0);
     __builtin_assume(a.bc * a.n > 0 && a.bc * a.n <= 256 * kXRFast * (16 / (int)sizeof(bits_t)));
   }
+  const int nb = ga.row_start[gi + 1] - ga.row_start[gi];  // row blocks of this matrix
   if constexpr (MERGED) {
     a.bc = 1;
-    __builtin_assume(a.r <= ga.row_start[gi + 1] - ga.row_start[gi]);
+    __builtin_assume(a.r <= MTR * nb);
   }
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ float red[NW][BC];
   __shared__ uint32_t epoch_sh;
-  __shared__ uint32_t tdone_sh;  // MERGED: waves that have added their share of the T row
+  __shared__ uint32_t tdone_sh;  // MERGED: waves that have added their shares of the T rows
+  __shared__ float tred[MERGED ? MTR : 1][NW][1];  // MERGED: per-wave shares of each T row
 
   const int t = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave index, uniform
@@ -828,15 +829,21 @@ __global__ __launch_bounds__(MNT > 0 ? MNT : 256) void k_decode(GroupArgs ga) {
     }
   };
 
-  // MERGED: the epoch, X and this block's Vt row go out first, so the T row
+  // MERGED: the epoch, X and this block's Vt rows go out first, so its T rows
   // can be published as soon as they return (loads return in issue order).
+  // Slots past r load row l % r (a valid row, not the same one for every
+  // block) and publish nothing.
   uint32_t epoch = 0;
-  u32x4 vt;
-  const int tl = local < r ? local : 0;  // blocks past r load row 0 and publish nothing
+  u32x4 vt[MERGED ? MTR : 1];
   if constexpr (MERGED) {
     epoch = load_epoch(a);
     x_issue();
-    vt = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Vt + (int64_t)tl * n) + (t < xvecs ? t : 0));
+#pragma unroll
+    for (int i = 0; i < MTR; ++i) {
+      const int l = local + nb * i;
+      const int lc = l < r ? l : l % r;
+      vt[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Vt + (int64_t)lc * n) + (t < xvecs ? t : 0));
+    }
   }
 
   // vector loads that depend on nothing: epoch, U rows, 2:4 words
@@ -858,28 +865,34 @@ __global__ __launch_bounds__(MNT > 0 ? MNT : 256) void k_decode(GroupArgs ga) {
   if constexpr (!MERGED) x_issue();
 
   if constexpr (MERGED) {
-    // this wave's share of T row tl (X vector t times Vt vector t), then the
-    // last wave publishes the fixed-order sum of all shares.  The barrier
-    // only orders the counter's reset before its increments; it does not
-    // wait for the loads in flight.
+    // this wave's shares of the block's T rows (X vector t times Vt vector
+    // t; the same arithmetic as t_row, so a row computed again locally has
+    // the same bits), then the last wave publishes the fixed-order sums.
+    // The barrier only orders the counter's reset before its increments; it
+    // does not wait for the loads in flight.
     __syncthreads();
-    const float p = wave_sum(t < xvecs ? dot16<DT>(vt, xr[0], 0.f) : 0.f);
+    float p[MTR];
+#pragma unroll
+    for (int i = 0; i < MTR; ++i) p[i] = wave_sum(t < xvecs ? dot16<DT>(vt[i], xr[0], 0.f) : 0.f);
     uint32_t done = 0;
     if (lane_id() == 0) {
-      red[w][0] = p;
-      asm volatile("" ::: "memory");  // the share is written before the count (LDS keeps a wave's order)
+#pragma unroll
+      for (int i = 0; i < MTR; ++i) tred[i][w][0] = p[i];
+      asm volatile("" ::: "memory");  // the shares are written before the count (LDS keeps a wave's order)
       done = __hip_atomic_fetch_add(&tdone_sh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     done = (uint32_t)__builtin_amdgcn_readlane((int)done, 0);
-    if (done == (uint32_t)NW - 1 && local < r) {
+    if (done == (uint32_t)NW - 1) {
       asm volatile("" ::: "memory");
-      const uint64_t word = (uint64_t)__float_as_uint(red_sum<BC, NW>(red, 0)) | ((uint64_t)tag_of(epoch) << 32);
-      const int rep = lane_id();
-      if (rep < kTReplicas)
-        __hip_atomic_store(a.Tt + (int64_t)rep * a.t_stride + local, word, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+      // lane 8i + k writes replica k of row i
+      const int i = lane_id() / kTReplicas, rep = lane_id() % kTReplicas;
+      const int l = local + nb * i;
+      if (i < MTR && l < r) {
+        const uint64_t word = (uint64_t)__float_as_uint(red_sum<1, NW>(tred[i], 0)) | ((uint64_t)tag_of(epoch) << 32);
+        __hip_atomic_store(a.Tt + (int64_t)rep * a.t_stride + l, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
-    if constexpr (is_csr<FMT>) csr_issue<DT, FMT, RPW>(a, rb, ch);
+    csr_issue<DT, FMT, RPW>(a, rb, ch);
   }
 
   if (r > 0 && t == 0) epoch_sh = epoch;
@@ -1023,30 +1036,37 @@ static bool merged_enabled() {
 // ---------------------------------------------------------------------------
 // Launch one instance; more than 64 KiB of dynamic LDS (wide batches: X for
 // 8 columns) must be allowed per kernel first, once.
-template <int DT, int FMT, int BC, int RPW, bool VECU, bool FAST, int MNT = 0>
+template <int DT, int FMT, int BC, int RPW, bool VECU, bool FAST, int MTR = 0>
 static void launch_k(const GroupArgs& ga, unsigned grid, size_t lds, hipStream_t s) {
   static bool big_lds = false;
   if (lds > 64 * 1024 && !big_lds) {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(&k_decode<DT, FMT, BC, RPW, VECU, FAST, MNT>),
+    hipFuncSetAttribute(reinterpret_cast<const void*>(&k_decode<DT, FMT, BC, RPW, VECU, FAST, MTR>),
                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLdsAll);
     big_lds = true;
   }
-  hipLaunchKernelGGL((k_decode<DT, FMT, BC, RPW, VECU, FAST, MNT>), dim3(grid), dim3(MNT > 0 ? MNT : 256), lds, s,
-                     ga);
+  hipLaunchKernelGGL((k_decode<DT, FMT, BC, RPW, VECU, FAST, MTR>), dim3(grid), dim3(MTR > 0 ? kMergedThreads : 256),
+                     lds, s, ga);
+}
+
+template <int DT, int FMT, int RPW, bool VECU>
+static void launch_merged_tr(const GroupArgs& ga, unsigned grid, int mtr, size_t lds, hipStream_t s) {
+  if (mtr == 1) launch_k<DT, FMT, 1, RPW, VECU, true, 1>(ga, grid, lds, s);
+  else if (mtr == 2) launch_k<DT, FMT, 1, RPW, VECU, true, 2>(ga, grid, lds, s);
+  else launch_k<DT, FMT, 1, RPW, VECU, true, 4>(ga, grid, lds, s);
 }
 
 template <int DT, int FMT, int BC, bool VECU>
-static void launch_v(const GroupArgs& ga, unsigned grid, bool fast, bool merged, int rpw, size_t lds,
+static void launch_v(const GroupArgs& ga, unsigned grid, bool fast, int mtr, int rpw, size_t lds,
                      hipStream_t s) {
   if constexpr (DT == HSS_BF16) {
-    if constexpr (BC == 1 && VECU && is_csr<FMT>) {
-      if (merged) {
+    if constexpr (BC == 1 && is_csr<FMT>) {
+      if (mtr > 0) {
         if (rpw == 1)
-          launch_k<DT, FMT, 1, 1, true, true, kMergedThreads>(ga, grid, lds, s);
+          launch_merged_tr<DT, FMT, 1, VECU>(ga, grid, mtr, lds, s);
         else if (rpw == 4)
-          launch_k<DT, FMT, 1, 4, true, true, kMergedThreads>(ga, grid, lds, s);
+          launch_merged_tr<DT, FMT, 4, VECU>(ga, grid, mtr, lds, s);
         else
-          launch_k<DT, FMT, 1, 2, true, true, kMergedThreads>(ga, grid, lds, s);
+          launch_merged_tr<DT, FMT, 2, VECU>(ga, grid, mtr, lds, s);
         return;
       }
     }
@@ -1067,21 +1087,21 @@ static void launch_v(const GroupArgs& ga, unsigned grid, bool fast, bool merged,
 }
 
 template <int DT, int FMT, int BC>
-static void launch_bc(const GroupArgs& ga, unsigned grid, bool vecu, bool fast, bool merged, int rpw, size_t lds,
+static void launch_bc(const GroupArgs& ga, unsigned grid, bool vecu, bool fast, int mtr, int rpw, size_t lds,
                       hipStream_t s) {
   if constexpr (DT == HSS_BF16) {
-    if (vecu) return launch_v<DT, FMT, BC, true>(ga, grid, fast, merged, rpw, lds, s);
+    if (vecu) return launch_v<DT, FMT, BC, true>(ga, grid, fast, mtr, rpw, lds, s);
   }
-  launch_v<DT, FMT, BC, false>(ga, grid, fast, false, rpw, lds, s);
+  launch_v<DT, FMT, BC, false>(ga, grid, fast, mtr, rpw, lds, s);
 }
 
 template <int DT, int FMT>
-static void launch_fmt(const GroupArgs& ga, unsigned grid, int bc, bool vecu, bool fast, bool merged, int rpw,
+static void launch_fmt(const GroupArgs& ga, unsigned grid, int bc, bool vecu, bool fast, int mtr, int rpw,
                        size_t lds, hipStream_t s) {
-  if (bc == 1) launch_bc<DT, FMT, 1>(ga, grid, vecu, fast, merged, rpw, lds, s);
-  else if (bc == 2) launch_bc<DT, FMT, 2>(ga, grid, vecu, fast, false, rpw, lds, s);
-  else if (bc <= 4) launch_bc<DT, FMT, 4>(ga, grid, vecu, fast, false, rpw, lds, s);
-  else launch_bc<DT, FMT, 8>(ga, grid, vecu, fast, false, rpw, lds, s);
+  if (bc == 1) launch_bc<DT, FMT, 1>(ga, grid, vecu, fast, mtr, rpw, lds, s);
+  else if (bc == 2) launch_bc<DT, FMT, 2>(ga, grid, vecu, fast, 0, rpw, lds, s);
+  else if (bc <= 4) launch_bc<DT, FMT, 4>(ga, grid, vecu, fast, 0, rpw, lds, s);
+  else launch_bc<DT, FMT, 8>(ga, grid, vecu, fast, 0, rpw, lds, s);
 }
 
 // Dynamic LDS budget per block.  CSR gathers X at random columns, so X goes
@@ -1184,6 +1204,33 @@ static MatrixLaunch matrix_launch(const hss_matrix* A, int bc, const void* X, vo
   return L;
 }
 
+// Merged producers for one CSR column (bf16, FAST): the fewest rows per wave
+// (1, 2 or 4) whose blocks, 8*RPW rows each, number at most the CUs (each
+// block waits for T rows that other blocks produce, so all must be resident;
+// measured: with 2-3 merged blocks per CU the 3-matrix q/k/v launch of the
+// decoder layer is slower than with separate producers), with at most 4 T
+// rows per block (r <= 4 * blocks of each matrix).  Returns the T rows per
+// block (1, 2 or 4; 0: not merged) and sets rpw.
+static int merged_plan(const hss_matrix* const* A, int G, int bc, bool fast_bf16, int fmt, int& rpw) {
+  if (bc != 1 || !fast_bf16 || fmt == HSS_FMT_2OF4 || !merged_enabled()) return 0;
+  const int cus = cu_count();
+  constexpr int mw = kMergedThreads / 64;
+  for (int rp = 1; rp <= 4; rp *= 2) {
+    int blocks = 0, tr = 0;
+    for (int g = 0; g < G; ++g) {
+      const int nb = (A[g]->m + mw * rp - 1) / (mw * rp);
+      blocks += nb;
+      const int t = (A[g]->r + nb - 1) / nb;
+      tr = tr > t ? tr : t;
+    }
+    if (tr <= 4 && blocks <= cus) {
+      rpw = rp;
+      return tr <= 1 ? 1 : (tr <= 2 ? 2 : 4);
+    }
+  }
+  return 0;
+}
+
 // One fused decode pass over bc columns (1 <= bc <= decode_max_cols of every
 // matrix) for G matrices sharing X (same n, dtype and format); Y[g] is
 // matrix g's output.  The T words of matrix g follow those of matrix g - 1.
@@ -1206,21 +1253,9 @@ void launch_decode_group(const hss_matrix* const* A, int G, int bc, const void* 
     rpw = rpw < L[g].rpw ? rpw : L[g].rpw;
   }
   if (!fast && rpw > 2) rpw = 2;
-  // One column of one matrix: producers merged into 1024-thread row blocks
-  // when, with the fewest rows per wave that allow it, there are at most as
-  // many blocks as CUs (all resident at once) and at least r of them.
-  bool merged = false;
-  if (G == 1 && bc == 1 && fast && vecu && A[0]->fmt == HSS_FMT_CSR && merged_enabled()) {
-    const int cus = cu_count();
-    const int mw = kMergedThreads / 64;
-    for (int rp = 1; rp <= 4 && !merged; rp *= 2) {
-      const int nb = (A[0]->m + mw * rp - 1) / (mw * rp);
-      if (nb <= cus && A[0]->r <= nb) {
-        merged = true;
-        rpw = rp;
-      }
-    }
-  }
+  const int dt = A[0]->dtype, fmt = col16_of(A[0]) ? kFmtCsr16 : A[0]->fmt;
+  const int mtr = merged_plan(A, G, bc, fast && dt == HSS_BF16, fmt, rpw);
+  const bool merged = mtr > 0;
   ga.prod_start[0] = 0;
   for (int g = 0; g < G; ++g) {
     ga.a[g] = L[g].a;
@@ -1231,15 +1266,14 @@ void launch_decode_group(const hss_matrix* const* A, int G, int bc, const void* 
   for (int g = 0; g < G; ++g) ga.row_start[g + 1] = ga.row_start[g] + (A[g]->m + rows_per_block - 1) / rows_per_block;
   for (int g = G; g < kMaxGroup; ++g) { ga.prod_start[g + 1] = ga.prod_start[G]; ga.row_start[g + 1] = ga.row_start[G]; }
   const unsigned grid = (unsigned)ga.row_start[G];
-  const int dt = A[0]->dtype, fmt = col16_of(A[0]) ? kFmtCsr16 : A[0]->fmt;
   if (dt == HSS_F32) {
-    if (fmt == HSS_FMT_CSR) launch_fmt<HSS_F32, HSS_FMT_CSR>(ga, grid, bc, false, false, false, rpw, lds, s);
-    else if (fmt == kFmtCsr16) launch_fmt<HSS_F32, kFmtCsr16>(ga, grid, bc, false, false, false, rpw, lds, s);
-    else launch_fmt<HSS_F32, HSS_FMT_2OF4>(ga, grid, bc, false, false, false, rpw, lds, s);
+    if (fmt == HSS_FMT_CSR) launch_fmt<HSS_F32, HSS_FMT_CSR>(ga, grid, bc, false, false, 0, rpw, lds, s);
+    else if (fmt == kFmtCsr16) launch_fmt<HSS_F32, kFmtCsr16>(ga, grid, bc, false, false, 0, rpw, lds, s);
+    else launch_fmt<HSS_F32, HSS_FMT_2OF4>(ga, grid, bc, false, false, 0, rpw, lds, s);
   } else {
-    if (fmt == HSS_FMT_CSR) launch_fmt<HSS_BF16, HSS_FMT_CSR>(ga, grid, bc, vecu, fast, merged, rpw, lds, s);
-    else if (fmt == kFmtCsr16) launch_fmt<HSS_BF16, kFmtCsr16>(ga, grid, bc, vecu, fast, merged, rpw, lds, s);
-    else launch_fmt<HSS_BF16, HSS_FMT_2OF4>(ga, grid, bc, vecu, fast, merged, rpw, lds, s);
+    if (fmt == HSS_FMT_CSR) launch_fmt<HSS_BF16, HSS_FMT_CSR>(ga, grid, bc, vecu, fast, mtr, rpw, lds, s);
+    else if (fmt == kFmtCsr16) launch_fmt<HSS_BF16, kFmtCsr16>(ga, grid, bc, vecu, fast, mtr, rpw, lds, s);
+    else launch_fmt<HSS_BF16, HSS_FMT_2OF4>(ga, grid, bc, vecu, fast, mtr, rpw, lds, s);
   }
 }
 

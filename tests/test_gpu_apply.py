@@ -78,6 +78,10 @@ SMALL = [
     # with a ragged last block, r equal to the block count, blocks past r, 1, 2 and 4 rows per wave
     ("csr", 1030, 512, 40, 1), ("csr", 4096, 1024, 256, 1), ("csr", 100, 128, 4, 1),
     ("csr", 7990, 256, 60, 1), ("csr", 2047, 64, 252, 1), ("2:4", 2100, 256, 16, 1),
+    # ... and 2 or 4 T rows per block (r up to 4x the blocks)
+    ("csr", 2048, 256, 400, 1), ("csr", 1024, 128, 500, 1),
+    # ... with r % 4 != 0 (U rows read element by element)
+    ("csr", 1030, 512, 41, 1), ("csr", 2050, 256, 409, 1),
 ]
 
 
@@ -182,11 +186,12 @@ def test_apply_config5_sampled(H):
 
 @pytest.mark.parametrize("fmt,dtype,b,m", [("csr", O.BF16, 1, 300), ("csr", O.F32, 3, 300), ("2:4", O.BF16, 8, 300),
                                            ("2:4", O.F32, 2, 300), ("csr", O.BF16, 1, 1030),
-                                           ("2:4", O.BF16, 1, 1030)])
+                                           ("2:4", O.BF16, 1, 1030), ("csr", O.BF16, 1, 100)])
 def test_apply_local_fallback_is_bitwise_identical(H, monkeypatch, fmt, dtype, b, m):
     """With a zero poll budget every block computes the T rows it finds stale
-    itself; the result must be bit-identical to the normal hand-off (m = 1030
-    at one bf16 CSR column: the T rows come from the row blocks themselves)."""
+    itself; the result must be bit-identical to the normal hand-off (one bf16
+    CSR column: the T rows come from the row blocks themselves, 4, 2 and 1 per
+    block at m = 100, 300 and 1030)."""
     n, r = 512, 40
     W = syn.random_matrix(m, n, dtype, seed=21, kind="t3")
     ref = O.split_csr(W, dtype, O.topk_count(m, n, 5, 100)) if fmt == "csr" else O.split_24(W, dtype)
@@ -272,6 +277,12 @@ GROUPS = [
     ("2:4", [(300, 8), (300, 8)], 128, 1),
     ("2:4", [(70, 5), (33, 16), (129, 4)], 64, 5),
     ("csr", [(150, 16), (90, 8)], 256, 16),
+    # one bf16 column: T producers merged into the row blocks, 2 and 4 T rows per block (and a
+    # group with more blocks than CUs at every row count per wave: separate producers)
+    ("csr", [(1000, 200), (600, 100)], 512, 1),
+    ("csr", [(512, 200), (256, 100), (300, 4)], 256, 1),
+    ("csr", [(4096, 64), (4096, 64), (4090, 64)], 128, 1),
+    ("csr", [(1000, 201), (600, 99)], 512, 1),
 ]
 
 
