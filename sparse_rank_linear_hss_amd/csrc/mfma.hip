@@ -29,6 +29,17 @@
 namespace hss {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 (lo in the low half) with gfx950's packed
+// conversion: round to nearest even, NaN stays NaN -- the same bits as
+// f32_to_bf16 for every other input, in one instruction instead of six.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 enum : int { A_DENSE = 0, A_NM24 = 1 };
@@ -406,6 +417,206 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(GemmArgs g) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// 256 x 256 tiles for large batches (prefill): 4 waves, each a 128 x 128
+// quarter (4 x 4 MFMA blocks, 256 fp32 accumulators per lane), so a wave
+// reads 8 fragments from LDS per 16 MFMAs.  K runs in stages of 32: each
+// stage is loaded into registers (buffer loads: one 32-bit offset per row,
+// rows past the end read as zeros) while the one before it is computed,
+// written to the other of two LDS buffers, and costs one barrier.  Rows of a stage are 64
+// bytes; chunk c (8 bf16) of row r sits at slot c ^ ((r >> 1) & 3), so both
+// the stores (4 lanes per row) and the fragment reads (8 consecutive rows
+// per 8 lanes) hit 8 distinct 16-byte bank groups.  Needs K1 and K2
+// multiples of 32 and 16-byte aligned rows.
+// ---------------------------------------------------------------------------
+static constexpr int kHM = 256, kHN = 256, kHK = 32;
+static constexpr int kHStage = (kHM + kHN) * kHK;  // bf16 per LDS buffer: A rows, then B rows
+
+struct HRegs {
+  u32x4 a[4], b[4];  // thread t: chunks q = t + 256 i (row q / 4, chunk q % 4) of A and of B
+};
+
+// The four operands as buffer resources (32-bit offsets, one register per
+// row instead of a 64-bit pointer; rows past the end read as zeros).
+struct HOps {
+  __amdgpu_buffer_rsrc_t a1, b1, a2, b2;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t h_rsrc(const uint16_t* p, int rows, int64_t ld) {
+  const int64_t bytes = p ? (int64_t)rows * ld * 2 : 0;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p), 0, (int)bytes, 0x00020000);
+}
+
+// Stage s: rows r0 + (t >> 2) + 64 i, columns k0 + 8 (t & 3) .. of A and B.
+__device__ __forceinline__ void h_load(HRegs& r, const GemmArgs& g, const HOps& ops, int nst1, int s, int m0,
+                                       int n0) {
+  const int t = threadIdx.x;
+  const bool seg1 = s < nst1;
+  const int k0 = (seg1 ? s : s - nst1) * kHK;
+  const int lda = (int)(seg1 ? g.lda1 : g.lda2), ldb = (int)(seg1 ? g.ldb1 : g.ldb2);
+  const uint32_t koff = 2u * (uint32_t)(k0 + 8 * (t & 3));
+  const uint32_t arow = 2u * (uint32_t)(m0 + (t >> 2)) * (uint32_t)lda + koff;
+  const uint32_t brow = 2u * (uint32_t)(n0 + (t >> 2)) * (uint32_t)ldb + koff;
+  const uint32_t astep = 128u * (uint32_t)lda, bstep = 128u * (uint32_t)ldb;  // 64 rows
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r.a[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(seg1 ? ops.a1 : ops.a2, arow + i * astep, 0, 0));
+    r.b[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(seg1 ? ops.b1 : ops.b2, brow + i * bstep, 0, 0));
+  }
+}
+
+__device__ __forceinline__ void h_store(uint16_t* __restrict__ buf, const HRegs& r) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = t + 256 * i, row = q >> 2, c = q & 3;
+    const int off = row * kHK + 8 * (c ^ ((row >> 1) & 3));
+    *reinterpret_cast<u32x4*>(buf + off) = r.a[i];
+    *reinterpret_cast<u32x4*>(buf + kHM * kHK + off) = r.b[i];
+  }
+}
+
+// The MFMAs of one stage.
+__device__ __forceinline__ void h_compute(const uint16_t* __restrict__ buf, int wm, int wn, f32x16 (&acc)[4][4]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int ks = 0; ks < kHK / 16; ++ks) {
+    const int c = 2 * ks + (lane >> 5);
+    bf16x8 af[4], bfr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = wm * 128 + 32 * i + (lane & 31);
+      af[i] = *reinterpret_cast<const bf16x8*>(buf + row * kHK + 8 * (c ^ ((row >> 1) & 3)));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = wn * 128 + 32 * j + (lane & 31);
+      bfr[j] = *reinterpret_cast<const bf16x8*>(buf + kHM * kHK + row * kHK + 8 * (c ^ ((row >> 1) & 3)));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+__global__ __launch_bounds__(256, 1) void k_gemm_h(GemmArgs g) {
+  __shared__ __align__(16) uint16_t hb0[kHStage], hb1[kHStage];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wm = w >> 1, wn = w & 1;
+  const int m0 = blockIdx.x * kHM, n0 = blockIdx.y * kHN;
+  const int nst1 = g.K1 / kHK;
+  const int nst = nst1 + g.K2 / kHK;
+  const int s_begin = blockIdx.z * g.chunks_per_split;
+  const int s_end = min(s_begin + g.chunks_per_split, nst);
+  // An AGPR named in an (empty) asm makes the compiler treat the kernel as
+  // one that uses AGPRs, so the MFMAs keep their 256 accumulators there;
+  // otherwise they are selected with VGPR accumulators, which do not fit.
+  asm volatile("" ::: "a0");
+  HOps ops;
+  ops.a1 = h_rsrc(g.A1, g.M, g.lda1);
+  ops.b1 = h_rsrc(g.B1, g.N, g.ldb1);
+  ops.a2 = h_rsrc(g.A2, g.M, g.lda2);
+  ops.b2 = h_rsrc(g.B2, g.N, g.ldb2);
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  // Stage s_begin + d sits in LDS buffer d % 2.  The registers hold the
+  // stage after the one being computed; loads past the end reload the last
+  // stage (unconditional, so the compiler keeps one copy of the staging
+  // registers), and its store fills a buffer nobody reads.
+  if (s_begin < s_end) {
+    const int last = s_end - 1;
+    HRegs r;
+    h_load(r, g, ops, nst1, s_begin, m0, n0);
+    h_store(hb0, r);
+    h_load(r, g, ops, nst1, min(s_begin + 1, last), m0, n0);
+    __syncthreads();
+    for (int s = s_begin; s < s_end; ++s) {
+      const int odd = (s - s_begin) & 1;
+      h_compute(odd ? hb1 : hb0, wm, wn, acc);
+      h_store(odd ? hb0 : hb1, r);
+      h_load(r, g, ops, nst1, min(s + 2, last), m0, n0);
+      __syncthreads();
+    }
+  }
+
+  // Output.  bf16: each wave stages 32 columns n x its 128 rows m of C at a
+  // time in its own 8 KiB of LDS (16-byte chunk cm of row n at cm ^ (n % 16)),
+  // then writes every row n as 256 contiguous bytes in 16-byte stores.
+  // fp32 partials: 16-byte stores of 4 consecutive m straight from the
+  // accumulators.
+  const int mw0 = m0 + wm * 128, nw0 = n0 + wn * 128;
+  if (g.out_mode == OUT_BF16) {
+    uint16_t* stage = hb0 + w * 4096;  // hb0 is free: the loop ended on a barrier
+    uint16_t* C = static_cast<uint16_t*>(g.C);
+    const bool vec_out = ((uintptr_t)C % 16 == 0) && (g.ldc % 8 == 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int nl = lane & 31, h = lane >> 5;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int vg = 0; vg < 4; ++vg) {
+          const int cm = 4 * i + vg;
+          u32x2 v2;
+          v2.x = pack_bf16x2(acc[i][j][4 * vg], acc[i][j][4 * vg + 1]);
+          v2.y = pack_bf16x2(acc[i][j][4 * vg + 2], acc[i][j][4 * vg + 3]);
+          *reinterpret_cast<u32x2*>(stage + nl * 128 + 8 * (cm ^ (nl & 15)) + 4 * h) = v2;
+        }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int nl2 = 4 * q + (lane >> 4), cm = lane & 15;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stage + nl2 * 128 + 8 * (cm ^ (nl2 & 15)));
+        const int n = nw0 + 32 * j + nl2, m = mw0 + 8 * cm;
+        if (n < g.N) {
+          uint16_t* dst = C + (int64_t)n * g.ldc + m;
+          if (vec_out && m + 8 <= g.M) {
+            *reinterpret_cast<u32x4*>(dst) = v;
+          } else {
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (m + e < g.M) dst[e] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+          }
+        }
+      }
+    }
+  } else {
+    float* C = static_cast<float*>(g.C) + (int64_t)blockIdx.z * g.N * g.ldc;
+    const bool vec_out = ((uintptr_t)C % 16 == 0) && (g.ldc % 4 == 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = nw0 + j * 32 + (lane & 31);
+        if (n >= g.N) continue;
+#pragma unroll
+        for (int vg = 0; vg < 4; ++vg) {
+          const int m = mw0 + i * 32 + 8 * vg + 4 * (lane >> 5);
+          float* dst = C + (int64_t)n * g.ldc + m;
+          if (vec_out && m + 4 <= g.M) {
+            float4 v;
+            v.x = acc[i][j][4 * vg]; v.y = acc[i][j][4 * vg + 1];
+            v.z = acc[i][j][4 * vg + 2]; v.w = acc[i][j][4 * vg + 3];
+            *reinterpret_cast<float4*>(dst) = v;
+          } else {
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+              if (m + p < g.M) dst[p] = acc[i][j][4 * vg + p];
+          }
+        }
+      }
+  }
+}
+
 // Dense bf16 copy D (m x n, row-major) of a CSR matrix, one wave per row:
 // the row is zeroed with 16-byte stores, a fence waits for those stores, then
 // the lanes scatter the row's entries (no other wave touches the row).
@@ -457,32 +668,40 @@ static int choose_splits(int tiles, int nch) {
   return s;
 }
 
-// Kernel choice for one GEMM (M x N outputs, K = K1 + K2): the large-tile
-// kernel for dense 16-byte-aligned operands and N >= 256, else k_gemm<BN>.
+// Kernel choice for one GEMM (M x N outputs, K = K1 + K2): 256 x 256 tiles
+// (k_gemm_h) for dense 16-byte-aligned operands with K segments in whole
+// stages of 32 and M, N >= 256; else 256 x 128 tiles (k_gemm_big) for dense
+// aligned operands and N >= 256; else k_gemm<BN>.
+enum : int { G_SMALL = 0, G_BIG = 1, G_H = 2 };
 struct GemmCfg {
-  bool big;
+  int kind;
   int bn, splits;
 };
 
-static GemmCfg gemm_cfg(int M, int N, int K1, int K2, bool big_ok) {
+static GemmCfg gemm_cfg(int M, int N, int K1, int K2, bool big_ok, bool h_ok) {
   GemmCfg c;
-  c.big = big_ok && N >= 256;
-  if (c.big) {
+  if (h_ok && M >= kHM && N >= kHN && K1 % kHK == 0 && K2 % kHK == 0) {
+    c.kind = G_H;
+    c.bn = kHN;
+    c.splits = choose_splits(cdiv(M, kHM) * cdiv(N, kHN), K1 / kHK + K2 / kHK);
+  } else if (big_ok && N >= 256) {
+    c.kind = G_BIG;
     c.bn = kGN;
     c.splits = choose_splits(cdiv(M, kGM) * cdiv(N, kGN), cdiv(K1, kGK) + cdiv(K2, kGK));
   } else {
+    c.kind = G_SMALL;
     c.bn = batch_tile(N);
     c.splits = choose_splits(cdiv(M, kBM) * cdiv(N, c.bn), cdiv(K1, kKC) + cdiv(K2, kKC));
   }
   return c;
 }
 
-// fp32 partials of one GEMM: enough for either kernel choice (operand
+// fp32 partials of one GEMM: enough for every kernel choice (operand
 // alignment, which decides between them, is known only at launch).
 static size_t gemm_part_bytes(int M, int N, int K1, int K2) {
   size_t mx = 0;
-  for (int big = 0; big < 2; ++big) {
-    const GemmCfg c = gemm_cfg(M, N, K1, K2, big);
+  for (int kind = 0; kind < 3; ++kind) {
+    const GemmCfg c = gemm_cfg(M, N, K1, K2, kind >= G_BIG, kind == G_H);
     if (c.splits > 1) mx = std::max(mx, sizeof(float) * (size_t)c.splits * N * M);
   }
   return mx;
@@ -534,12 +753,18 @@ static void launch_gemm_bn(const GemmArgs& g, int amode, int splits, hipStream_t
 
 static int aligned16(const void* p, int64_t ld) { return ((uintptr_t)p % 16 == 0) && (ld % 8 == 0); }
 
+// Operand rows * ld bf16 fit the 32-bit byte offsets of k_gemm_h's buffer loads.
+static bool fits_u31(int rows, int64_t ld) { return (int64_t)rows * ld * 2 < ((int64_t)1 << 31); }
+
 static void run_gemm(GemmArgs g, int amode, float* part, hipStream_t s) {
   const bool big_ok = amode == A_DENSE && (g.K1 == 0 || (g.vec_a1 && g.vec_b1)) &&
                       (g.K2 == 0 || (g.vec_a2 && g.vec_b2));
-  const GemmCfg c = gemm_cfg(g.M, g.N, g.K1, g.K2, big_ok);
+  const bool h_ok = big_ok && (g.K1 == 0 || (fits_u31(g.M, g.lda1) && fits_u31(g.N, g.ldb1))) &&
+                    (g.K2 == 0 || (fits_u31(g.M, g.lda2) && fits_u31(g.N, g.ldb2)));
+  const GemmCfg c = gemm_cfg(g.M, g.N, g.K1, g.K2, big_ok, h_ok);
   g.chunks_per_split = cdiv(g.nch, c.splits);
-  if (c.big) g.chunks_per_split = cdiv(cdiv(g.K1, kGK) + cdiv(g.K2, kGK), c.splits);
+  if (c.kind == G_BIG) g.chunks_per_split = cdiv(cdiv(g.K1, kGK) + cdiv(g.K2, kGK), c.splits);
+  if (c.kind == G_H) g.chunks_per_split = cdiv(g.K1 / kHK + g.K2 / kHK, c.splits);
   void* final_out = g.C;
   const int64_t final_ldc = g.ldc;
   const int final_bf16 = g.out_mode == OUT_BF16;
@@ -547,7 +772,9 @@ static void run_gemm(GemmArgs g, int amode, float* part, hipStream_t s) {
     g.C = part;
     g.out_mode = OUT_PARTIAL;
   }
-  if (c.big)
+  if (c.kind == G_H)
+    hipLaunchKernelGGL(k_gemm_h, dim3(cdiv(g.M, kHM), cdiv(g.N, kHN), c.splits), dim3(256), 0, s, g);
+  else if (c.kind == G_BIG)
     hipLaunchKernelGGL(k_gemm_big, dim3(cdiv(g.M, kGM), cdiv(g.N, kGN), c.splits), dim3(256), 0, s, g);
   else if (c.bn == 32) launch_gemm_bn<32>(g, amode, c.splits, s);
   else if (c.bn == 64) launch_gemm_bn<64>(g, amode, c.splits, s);

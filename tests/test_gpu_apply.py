@@ -74,6 +74,9 @@ SMALL = [
     ("2:4", 8197, 128, 8, 1), ("2:4", 8197, 128, 8, 5), ("2:4", 2050, 64, 6, 2),
     # large batches: 256 x 128 tiles (ragged M and N, K tails not a multiple of the stage)
     ("csr", 300, 640, 128, 300), ("csr", 257, 1000, 72, 260), ("2:4", 100, 256, 16, 256),
+    # 256 x 256 tiles: ragged M and N, split-K ranges across the S | U segment boundary,
+    # odd stage counts per split
+    ("csr", 520, 512, 256, 512), ("csr", 300, 224, 32, 260), ("csr", 256, 160, 64, 256),
     # one CSR column, bf16: T producers merged into 512-thread row blocks (r <= blocks <= CUs),
     # with a ragged last block, r equal to the block count, blocks past r, 1, 2 and 4 rows per wave
     ("csr", 1030, 512, 40, 1), ("csr", 4096, 1024, 256, 1), ("csr", 100, 128, 4, 1),
