@@ -60,6 +60,7 @@ struct GemmArgs {
   const uint16_t* B2;  int64_t ldb2;   // N x K2
   void* C; int64_t ldc; int out_mode;  // C[n * ldc + m]; partials: + z * N * ldc
   int vec_a1, vec_b1, vec_a2, vec_b2;  // 16-byte loads allowed (K % 8 == 0, aligned rows)
+  int tiles_m, tiles_n;                // k_gemm_h: tiles per dimension (1-D grid of tiles_m * tiles_n * splits)
 };
 
 // Wave layout of a kBM x BN tile: WM x WN waves, each a (FM x FN) grid of
@@ -418,22 +419,29 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
-// 256 x 256 tiles for large batches (prefill): 4 waves, each a 128 x 128
-// quarter (4 x 4 MFMA blocks, 256 fp32 accumulators per lane), so a wave
+// Large tiles for big batches (prefill), k_gemm_h<FM, FN>: 4 waves, each a
+// (32 FM) x (32 FN) part (FM x FN MFMA blocks) of a (64 FM) x (64 FN) tile;
+// FM = FN = 4 gives 256 x 256 tiles with 128 x 128 per wave, where a wave
 // reads 8 fragments from LDS per 16 MFMAs.  K runs in stages of 32: each
 // stage is loaded into registers (buffer loads: one 32-bit offset per row,
 // rows past the end read as zeros) while the one before it is computed,
-// written to the other of two LDS buffers, and costs one barrier.  Rows of a stage are 64
-// bytes; chunk c (8 bf16) of row r sits at slot c ^ ((r >> 1) & 3), so both
-// the stores (4 lanes per row) and the fragment reads (8 consecutive rows
-// per 8 lanes) hit 8 distinct 16-byte bank groups.  Needs K1 and K2
+// written to the other of two LDS buffers, and costs one barrier.  Rows of a
+// stage are 64 bytes; chunk c (8 bf16) of row r sits at slot c ^ ((r >> 1) & 3),
+// so both the stores (4 lanes per row) and the fragment reads (8 consecutive
+// rows per 8 lanes) hit 8 distinct 16-byte bank groups.  Needs K1 and K2
 // multiples of 32 and 16-byte aligned rows.
 // ---------------------------------------------------------------------------
-static constexpr int kHM = 256, kHN = 256, kHK = 32;
-static constexpr int kHStage = (kHM + kHN) * kHK;  // bf16 per LDS buffer: A rows, then B rows
+static constexpr int kHK = 32;
 
+template <int FM, int FN>
+struct HTile {
+  static constexpr int TM = 64 * FM, TN = 64 * FN;  // block tile
+  static constexpr int STAGE = (TM + TN) * kHK;      // bf16 per LDS buffer: A rows, then B rows
+};
+
+template <int FM, int FN>
 struct HRegs {
-  u32x4 a[4], b[4];  // thread t: chunks q = t + 256 i (row q / 4, chunk q % 4) of A and of B
+  u32x4 a[FM], b[FN];  // thread t: chunks q = t + 256 i (row q / 4, chunk q % 4) of A and of B
 };
 
 // The four operands as buffer resources (32-bit offsets, one register per
@@ -448,7 +456,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t h_rsrc(const uint16_t* p, int 
 }
 
 // Stage s: rows r0 + (t >> 2) + 64 i, columns k0 + 8 (t & 3) .. of A and B.
-__device__ __forceinline__ void h_load(HRegs& r, const GemmArgs& g, const HOps& ops, int nst1, int s, int m0,
+template <int FM, int FN>
+__device__ __forceinline__ void h_load(HRegs<FM, FN>& r, const GemmArgs& g, const HOps& ops, int nst1, int s, int m0,
                                        int n0) {
   const int t = threadIdx.x;
   const bool seg1 = s < nst1;
@@ -459,59 +468,88 @@ __device__ __forceinline__ void h_load(HRegs& r, const GemmArgs& g, const HOps& 
   const uint32_t brow = 2u * (uint32_t)(n0 + (t >> 2)) * (uint32_t)ldb + koff;
   const uint32_t astep = 128u * (uint32_t)lda, bstep = 128u * (uint32_t)ldb;  // 64 rows
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < FM; ++i)
     r.a[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(seg1 ? ops.a1 : ops.a2, arow + i * astep, 0, 0));
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
     r.b[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(seg1 ? ops.b1 : ops.b2, brow + i * bstep, 0, 0));
-  }
 }
 
-__device__ __forceinline__ void h_store(uint16_t* __restrict__ buf, const HRegs& r) {
+template <int FM, int FN>
+__device__ __forceinline__ void h_store(uint16_t* __restrict__ buf, const HRegs<FM, FN>& r) {
   const int t = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = t + 256 * i, row = q >> 2, c = q & 3;
-    const int off = row * kHK + 8 * (c ^ ((row >> 1) & 3));
-    *reinterpret_cast<u32x4*>(buf + off) = r.a[i];
-    *reinterpret_cast<u32x4*>(buf + kHM * kHK + off) = r.b[i];
+  for (int i = 0; i < FM; ++i) {
+    const int row = (t >> 2) + 64 * i, c = t & 3;
+    *reinterpret_cast<u32x4*>(buf + row * kHK + 8 * (c ^ ((row >> 1) & 3))) = r.a[i];
+  }
+#pragma unroll
+  for (int i = 0; i < FN; ++i) {
+    const int row = (t >> 2) + 64 * i, c = t & 3;
+    *reinterpret_cast<u32x4*>(buf + HTile<FM, FN>::TM * kHK + row * kHK + 8 * (c ^ ((row >> 1) & 3))) = r.b[i];
   }
 }
 
 // The MFMAs of one stage.
-__device__ __forceinline__ void h_compute(const uint16_t* __restrict__ buf, int wm, int wn, f32x16 (&acc)[4][4]) {
+template <int FM, int FN>
+__device__ __forceinline__ void h_compute(const uint16_t* __restrict__ buf, int wm, int wn, f32x16 (&acc)[FM][FN]) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int ks = 0; ks < kHK / 16; ++ks) {
     const int c = 2 * ks + (lane >> 5);
-    bf16x8 af[4], bfr[4];
+    bf16x8 af[FM], bfr[FN];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = wm * 128 + 32 * i + (lane & 31);
+    for (int i = 0; i < FM; ++i) {
+      const int row = wm * 32 * FM + 32 * i + (lane & 31);
       af[i] = *reinterpret_cast<const bf16x8*>(buf + row * kHK + 8 * (c ^ ((row >> 1) & 3)));
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = wn * 128 + 32 * j + (lane & 31);
-      bfr[j] = *reinterpret_cast<const bf16x8*>(buf + kHM * kHK + row * kHK + 8 * (c ^ ((row >> 1) & 3)));
+    for (int j = 0; j < FN; ++j) {
+      const int row = wn * 32 * FN + 32 * j + (lane & 31);
+      bfr[j] = *reinterpret_cast<const bf16x8*>(buf + HTile<FM, FN>::TM * kHK + row * kHK + 8 * (c ^ ((row >> 1) & 3)));
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < FN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
   }
 }
 
-__global__ __launch_bounds__(256, 1) void k_gemm_h(GemmArgs g) {
-  __shared__ __align__(16) uint16_t hb0[kHStage], hb1[kHStage];
+// Tile of block b in a 1-D grid of G = tiles_m * tiles_n * splits blocks.
+// Blocks are dealt to the 8 XCDs round robin (b % 8), each XCD with its own
+// L2, so each XCD gets a contiguous range of tile numbers (when G % 8 == 0),
+// and tile numbers run down groups of 8 tiles along M before moving along N
+// (split z outermost): the blocks of one XCD then share their A and B slabs
+// in its L2 instead of each fetching them from memory.
+__device__ __forceinline__ void h_tile_of(int b, int tiles_m, int tiles_n, int G, int& tm, int& tn, int& tz) {
+  const int t = G % 8 == 0 ? (b % 8) * (G / 8) + b / 8 : b;
+  const int per_z = tiles_m * tiles_n;
+  tz = t / per_z;
+  const int u = t - tz * per_z;
+  const int group = 8 * tiles_n;  // tiles in a group of 8 M-tiles
+  const int first_m = (u / group) * 8;
+  const int gm = min(tiles_m - first_m, 8);
+  const int v = u - (u / group) * group;
+  tm = first_m + v % gm;
+  tn = v / gm;
+}
+
+template <int FM, int FN>
+__global__ __launch_bounds__(256, (FM * FN >= 16 ? 1 : 2)) void k_gemm_h(GemmArgs g) {
+  using TL = HTile<FM, FN>;
+  __shared__ __align__(16) uint16_t hb0[TL::STAGE], hb1[TL::STAGE];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w >> 1, wn = w & 1;
-  const int m0 = blockIdx.x * kHM, n0 = blockIdx.y * kHN;
+  int tm, tn, tz;
+  h_tile_of(blockIdx.x, g.tiles_m, g.tiles_n, (int)gridDim.x, tm, tn, tz);
+  const int m0 = tm * TL::TM, n0 = tn * TL::TN;
   const int nst1 = g.K1 / kHK;
   const int nst = nst1 + g.K2 / kHK;
-  const int s_begin = blockIdx.z * g.chunks_per_split;
+  const int s_begin = tz * g.chunks_per_split;
   const int s_end = min(s_begin + g.chunks_per_split, nst);
   // An AGPR named in an (empty) asm makes the compiler treat the kernel as
-  // one that uses AGPRs, so the MFMAs keep their 256 accumulators there;
+  // one that uses AGPRs, so the MFMAs keep their accumulators there;
   // otherwise they are selected with VGPR accumulators, which do not fit.
   asm volatile("" ::: "a0");
   HOps ops;
@@ -520,11 +558,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_h(GemmArgs g) {
   ops.a2 = h_rsrc(g.A2, g.M, g.lda2);
   ops.b2 = h_rsrc(g.B2, g.N, g.ldb2);
 
-  f32x16 acc[4][4];
+  f32x16 acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
@@ -534,47 +572,50 @@ __global__ __launch_bounds__(256, 1) void k_gemm_h(GemmArgs g) {
   // registers), and its store fills a buffer nobody reads.
   if (s_begin < s_end) {
     const int last = s_end - 1;
-    HRegs r;
-    h_load(r, g, ops, nst1, s_begin, m0, n0);
-    h_store(hb0, r);
-    h_load(r, g, ops, nst1, min(s_begin + 1, last), m0, n0);
+    HRegs<FM, FN> r;
+    h_load<FM, FN>(r, g, ops, nst1, s_begin, m0, n0);
+    h_store<FM, FN>(hb0, r);
+    h_load<FM, FN>(r, g, ops, nst1, min(s_begin + 1, last), m0, n0);
     __syncthreads();
     for (int s = s_begin; s < s_end; ++s) {
       const int odd = (s - s_begin) & 1;
-      h_compute(odd ? hb1 : hb0, wm, wn, acc);
-      h_store(odd ? hb0 : hb1, r);
-      h_load(r, g, ops, nst1, min(s + 2, last), m0, n0);
+      h_compute<FM, FN>(odd ? hb1 : hb0, wm, wn, acc);
+      h_store<FM, FN>(odd ? hb0 : hb1, r);
+      h_load<FM, FN>(r, g, ops, nst1, min(s + 2, last), m0, n0);
       __syncthreads();
     }
   }
 
-  // Output.  bf16: each wave stages 32 columns n x its 128 rows m of C at a
-  // time in its own 8 KiB of LDS (16-byte chunk cm of row n at cm ^ (n % 16)),
-  // then writes every row n as 256 contiguous bytes in 16-byte stores.
-  // fp32 partials: 16-byte stores of 4 consecutive m straight from the
-  // accumulators.
-  const int mw0 = m0 + wm * 128, nw0 = n0 + wn * 128;
+  // Output.  bf16: each wave stages 32 columns n x its 32 FM rows m of C at
+  // a time in its own part of LDS (16-byte chunk cm of row n at
+  // cm ^ (n % 4 FM)), then writes every row n as 64 FM contiguous bytes in
+  // 16-byte stores.  fp32 partials: 16-byte stores of 4 consecutive m
+  // straight from the accumulators.
+  const int mw0 = m0 + wm * 32 * FM, nw0 = n0 + wn * 32 * FN;
   if (g.out_mode == OUT_BF16) {
-    uint16_t* stage = hb0 + w * 4096;  // hb0 is free: the loop ended on a barrier
+    constexpr int CH = 4 * FM;       // 16-byte chunks per staged row
+    constexpr int RPI = 64 / CH;     // rows per read instruction
+    static_assert(4 * 32 * 32 * FM <= TL::STAGE, "staging fits one LDS buffer");
+    uint16_t* stage = hb0 + w * 32 * 32 * FM;  // hb0 is free: the loop ended on a barrier
     uint16_t* C = static_cast<uint16_t*>(g.C);
     const bool vec_out = ((uintptr_t)C % 16 == 0) && (g.ldc % 8 == 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < FN; ++j) {
       const int nl = lane & 31, h = lane >> 5;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int vg = 0; vg < 4; ++vg) {
           const int cm = 4 * i + vg;
           u32x2 v2;
           v2.x = pack_bf16x2(acc[i][j][4 * vg], acc[i][j][4 * vg + 1]);
           v2.y = pack_bf16x2(acc[i][j][4 * vg + 2], acc[i][j][4 * vg + 3]);
-          *reinterpret_cast<u32x2*>(stage + nl * 128 + 8 * (cm ^ (nl & 15)) + 4 * h) = v2;
+          *reinterpret_cast<u32x2*>(stage + nl * 8 * CH + 8 * (cm ^ (nl % CH)) + 4 * h) = v2;
         }
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int nl2 = 4 * q + (lane >> 4), cm = lane & 15;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(stage + nl2 * 128 + 8 * (cm ^ (nl2 & 15)));
+      for (int q = 0; q < 32 / RPI; ++q) {
+        const int nl2 = RPI * q + lane / CH, cm = lane % CH;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stage + nl2 * 8 * CH + 8 * (cm ^ (nl2 % CH)));
         const int n = nw0 + 32 * j + nl2, m = mw0 + 8 * cm;
         if (n < g.N) {
           uint16_t* dst = C + (int64_t)n * g.ldc + m;
@@ -590,12 +631,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_h(GemmArgs g) {
       }
     }
   } else {
-    float* C = static_cast<float*>(g.C) + (int64_t)blockIdx.z * g.N * g.ldc;
+    float* C = static_cast<float*>(g.C) + (int64_t)tz * g.N * g.ldc;
     const bool vec_out = ((uintptr_t)C % 16 == 0) && (g.ldc % 4 == 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < FN; ++j) {
         const int n = nw0 + j * 32 + (lane & 31);
         if (n >= g.N) continue;
 #pragma unroll
@@ -661,34 +702,44 @@ static inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 // Batch tile: the smallest of 32, 64, 128 that covers b (larger b tiles by 128).
 static int batch_tile(int b) { return b <= 32 ? 32 : (b <= 64 ? 64 : 128); }
 
-// Splits so that tiles * splits reaches ~256 blocks, at least 2 chunks each.
-static int choose_splits(int tiles, int nch) {
+// Splits so that tiles * splits reaches ~`target` blocks, at least 2 chunks each.
+static int choose_splits(int tiles, int nch, int target = 256) {
   int s = 1;
-  while (tiles * s < 256 && s * 2 <= nch / 2) s *= 2;
+  while (tiles * s < target && s * 2 <= nch / 2) s *= 2;
   return s;
 }
 
-// Kernel choice for one GEMM (M x N outputs, K = K1 + K2): 256 x 256 tiles
-// (k_gemm_h) for dense 16-byte-aligned operands with K segments in whole
-// stages of 32 and M, N >= 256; else 256 x 128 tiles (k_gemm_big) for dense
-// aligned operands and N >= 256; else k_gemm<BN>.
+// Kernel choice for one GEMM (M x N outputs, K = K1 + K2): k_gemm_h for
+// dense 16-byte-aligned operands with K segments in whole stages of 32 and
+// M, N >= 128 -- 128 x 256 tiles when there are at least 64 of them, else
+// 128 x 128, with K split until there are ~512 blocks (two per CU); else
+// 256 x 128 tiles (k_gemm_big) for dense aligned operands and N >= 256; else
+// k_gemm<BN>.  Measured on the 8192^2 rank-512 layer at b = 2048: the
+// 2048 x 8192 products take 23 us (K 512) and 238 us (K 8704, 49 % of the
+// bf16 MFMA peak) with 128 x 256 tiles, 26 and 249 us with 256 x 256; the
+// 2048 x 512 one (K 8192) 37 us with 128 x 128 tiles split 8 ways.
 enum : int { G_SMALL = 0, G_BIG = 1, G_H = 2 };
 struct GemmCfg {
   int kind;
   int bn, splits;
+  int fm, fn;  // k_gemm_h tile: (64 fm) x (64 fn)
 };
 
 static GemmCfg gemm_cfg(int M, int N, int K1, int K2, bool big_ok, bool h_ok) {
   GemmCfg c;
-  if (h_ok && M >= kHM && N >= kHN && K1 % kHK == 0 && K2 % kHK == 0) {
+  if (h_ok && M >= 128 && N >= 128 && K1 % kHK == 0 && K2 % kHK == 0) {
     c.kind = G_H;
-    c.bn = kHN;
-    c.splits = choose_splits(cdiv(M, kHM) * cdiv(N, kHN), K1 / kHK + K2 / kHK);
+    c.fm = 2;
+    c.fn = N >= 256 && cdiv(M, 128) * cdiv(N, 256) >= 64 ? 4 : 2;
+    c.bn = 64 * c.fn;
+    c.splits = choose_splits(cdiv(M, 64 * c.fm) * cdiv(N, 64 * c.fn), K1 / kHK + K2 / kHK, 512);
   } else if (big_ok && N >= 256) {
+    c.fm = c.fn = 0;
     c.kind = G_BIG;
     c.bn = kGN;
     c.splits = choose_splits(cdiv(M, kGM) * cdiv(N, kGN), cdiv(K1, kGK) + cdiv(K2, kGK));
   } else {
+    c.fm = c.fn = 0;
     c.kind = G_SMALL;
     c.bn = batch_tile(N);
     c.splits = choose_splits(cdiv(M, kBM) * cdiv(N, c.bn), cdiv(K1, kKC) + cdiv(K2, kKC));
@@ -772,8 +823,15 @@ static void run_gemm(GemmArgs g, int amode, float* part, hipStream_t s) {
     g.C = part;
     g.out_mode = OUT_PARTIAL;
   }
-  if (c.kind == G_H)
-    hipLaunchKernelGGL(k_gemm_h, dim3(cdiv(g.M, kHM), cdiv(g.N, kHN), c.splits), dim3(256), 0, s, g);
+  if (c.kind == G_H) {
+    g.tiles_m = cdiv(g.M, 64 * c.fm);
+    g.tiles_n = cdiv(g.N, 64 * c.fn);
+    const dim3 grid((unsigned)(g.tiles_m * g.tiles_n * c.splits));
+    if (c.fn == 4)
+      hipLaunchKernelGGL((k_gemm_h<2, 4>), grid, dim3(256), 0, s, g);
+    else
+      hipLaunchKernelGGL((k_gemm_h<2, 2>), grid, dim3(256), 0, s, g);
+  }
   else if (c.kind == G_BIG)
     hipLaunchKernelGGL(k_gemm_big, dim3(cdiv(g.M, kGM), cdiv(g.N, kGN), c.splits), dim3(256), 0, s, g);
   else if (c.bn == 32) launch_gemm_bn<32>(g, amode, c.splits, s);
