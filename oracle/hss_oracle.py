@@ -25,6 +25,11 @@ Sources (web pages; section names as printed on each page)
             into one sparse product plus two small dense products.
 [HASSLE]  aibr.jp/archives/82335 (explainer of HASSLE-free), section
           "3.中核となる技術的要素": N:M sparsity as the GPU-friendly structure.
+[SQZ]     aibr.jp/archives/208940 (explainer of SqueezeLLM), section
+          "3.中核となる技術的要素": the dense-and-sparse decomposition W = D + S
+          (the rare outliers kept exactly in a CSR matrix S, the dense rest D
+          quantised with non-uniform levels); section "4.有効性の検証方法と成果":
+          the sparse part is about 0.5 % of the weights.
 
 Readings where the pages are silent (each is listed in the design notes):
 * k = floor(m*n*num/den) in exact integer arithmetic (the worked example
@@ -37,6 +42,13 @@ Readings where the pages are silent (each is listed in the design notes):
 * Stage 2 is one truncated SVD of the whole residual at rank r, with the
   singular values folded into U (U = U_r diag(s_r), V = V_r).
 * The residual equals W with the kept positions set to +0 (no subtraction).
+* Dense-and-sparse: S = the top 0.5 % by |w| (k = floor(m*n*5/1000)), D = the
+  residual; each row of D is quantised to 2^bits levels by unweighted 1-D
+  k-means (the pages' sensitivity weights need gradients from data, which
+  this path has none of), started at quantiles of the distinct values, ties
+  to the lower level; levels are stored in the weight's type and every code is the nearest
+  stored level.  4-bit codes are packed two per byte, the even column in the
+  low nibble.
 
 Storage conventions (the same ones the C library documents):
   fp32 values are numpy.float32; bf16 values are their bit patterns in
@@ -315,3 +327,101 @@ def apply_rows(S_rows64, U_rows64, V64, X64):
     """Y[:, rows] and N[:, rows] from the dense rows of S and the rows of U."""
     A_rows = S_rows64 + U_rows64 @ V64.T
     return X64 @ A_rows.T, np.abs(X64) @ np.abs(A_rows).T
+
+
+# ---------------------------------------------------------------------------
+# Dense-and-sparse variant W = D + S  ([SQZ] section "3.中核となる技術的要素":
+# the few outliers stay exact in a sparse CSR matrix, the dense remainder is
+# quantised with non-uniform levels)
+# ---------------------------------------------------------------------------
+
+def outlier_count(m, n):
+    """Outliers kept in S: 0.5 % of the weights, floor(m*n*5/1000)."""
+    return topk_count(m, n, 5, 1000)
+
+
+def kmeans_1d(v64, K, max_iter=200):
+    """K-level quantiser of the values v by Lloyd's algorithm.
+
+    Start: with u the sorted distinct values, centroid k is u[floor((k + 1/2)
+    * |u| / K)] (the middle of the k-th of K equal bins of distinct values; with
+    at most K distinct values every one of them is a starting centroid, so the
+    result is exact).  Step: every value goes to its nearest centroid (ties to
+    the lower index); every non-empty cluster's centroid moves to the mean of
+    its values, an empty one stays.  Stops when no assignment changes.
+    Returns (centroids fp64[K], codes int[n])."""
+    v = np.asarray(v64, dtype=np.float64).reshape(-1)
+    if v.size == 0:
+        return np.zeros(K), np.zeros(0, dtype=np.int64)
+    u = np.unique(v)
+    c = u[(2 * np.arange(K) + 1) * u.size // (2 * K)].astype(np.float64)
+    codes = None
+    for _ in range(max_iter):
+        new = np.argmin(np.abs(v[:, None] - c[None, :]), axis=1)   # first minimum: lower index
+        if codes is not None and np.array_equal(new, codes):
+            break
+        codes = new
+        for k in range(K):
+            members = v[codes == k]
+            if members.size:
+                c[k] = members.mean()
+    return c, codes
+
+
+def nearest_level(v64, levels64):
+    """Index of the nearest level for each value (ties to the lower index)."""
+    v = np.asarray(v64, dtype=np.float64)
+    return np.argmin(np.abs(v[..., None] - np.asarray(levels64)[None, :]), axis=-1)
+
+
+def quantize_rows(D, dtype, bits=4):
+    """Per-row non-uniform quantisation of D (m x n, stored type).
+
+    Returns (lut, codes): lut m x 2^bits in the stored type (the row's k-means
+    centroids, rounded), codes m x n uint8 = index of the nearest stored level."""
+    m, n = D.shape
+    K = 1 << int(bits)
+    D64 = widen(D, dtype)
+    lut = np.zeros((m, K), dtype=np.float32 if dtype == F32 else np.uint16)
+    codes = np.zeros((m, n), dtype=np.uint8)
+    for i in range(m):
+        c, _ = kmeans_1d(D64[i], K)
+        lut[i] = narrow(c, dtype)
+        codes[i] = nearest_level(D64[i], widen(lut[i], dtype))
+    return lut, codes
+
+
+def pack_nibbles(codes):
+    """4-bit codes m x n (n even) -> bytes m x n/2: byte j = code[2j] | code[2j+1] << 4."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    if codes.shape[-1] % 2 or np.any(codes > 15):
+        raise ValueError("4-bit codes need an even row length and values < 16")
+    return (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_nibbles(packed, n):
+    """Inverse of pack_nibbles."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    out = np.zeros(packed.shape[:-1] + (n,), dtype=np.uint8)
+    out[..., 0::2] = packed & 0xF
+    out[..., 1::2] = packed >> 4
+    return out
+
+
+def dense_from_codes(codes, lut, dtype):
+    """fp64 dequantised D: D[i, j] = lut[i, codes[i, j]] (stored level, widened)."""
+    L = widen(lut, dtype)
+    rows = np.arange(L.shape[0])[:, None]
+    return L[rows, np.asarray(codes, dtype=np.int64)]
+
+
+def split_dense_sparse(W, dtype, k=None, bits=4):
+    """Dense-and-sparse form of W: the k outliers (default 0.5 %) as CSR, the
+    residual quantised per row.  Returns dict(row_ptr, col_idx, values, lut,
+    codes, codes_packed, residual, mask)."""
+    m, n = W.shape
+    s = split_csr(W, dtype, outlier_count(m, n) if k is None else k)
+    lut, codes = quantize_rows(s["residual"], dtype, bits)
+    s.update(lut=lut, codes=codes, codes_packed=pack_nibbles(codes) if bits == 4 else None)
+    return s
+

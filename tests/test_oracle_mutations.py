@@ -118,6 +118,53 @@ def _residual_keeps_values(W, mask):
     return np.array(W, copy=True)
 
 
+def _pack_nibbles_swapped(codes):
+    codes = np.asarray(codes, dtype=np.uint8)
+    return (codes[..., 1::2] | (codes[..., 0::2] << 4)).astype(np.uint8)
+
+
+_orig_kmeans = H.kmeans_1d
+
+
+def _kmeans_ties_high(v64, K, max_iter=200):
+    v = np.asarray(v64, dtype=np.float64).reshape(-1)
+    u = np.unique(v)
+    c = u[(2 * np.arange(K) + 1) * u.size // (2 * K)].astype(np.float64)
+    codes = None
+    for _ in range(max_iter):
+        d = np.abs(v[:, None] - c[None, :])[:, ::-1]
+        new = (K - 1) - np.argmin(d, axis=1)             # last minimum: upper index
+        if codes is not None and np.array_equal(new, codes):
+            break
+        codes = new
+        for k in range(K):
+            if np.any(codes == k):
+                c[k] = v[codes == k].mean()
+    return c, codes
+
+
+def _kmeans_one_step(v64, K, max_iter=200):
+    return _orig_kmeans(v64, K, max_iter=1)
+
+
+def _quantize_no_reassign(D, dtype, bits=4):
+    m, n = D.shape
+    K = 1 << bits
+    D64 = H.widen(D, dtype)
+    lut = np.zeros((m, K), dtype=np.float32 if dtype == H.F32 else np.uint16)
+    codes = np.zeros((m, n), dtype=np.uint8)
+    for i in range(m):
+        c, cd = _orig_kmeans(D64[i], K)
+        lut[i] = H.narrow(c, dtype)
+        codes[i] = cd                                    # codes of the unrounded levels
+    return lut, codes
+
+
+def _dense_from_codes_row0_lut(codes, lut, dtype):
+    L = H.widen(lut, dtype)
+    return L[0][np.asarray(codes, dtype=np.int64)]       # one row's levels for every row
+
+
 CASES = [
     ("apply_factored", _apply_no_lowrank,
      [P.test_apply_hand_example, lambda: [P.test_apply_factored_equals_dense(s) for s in range(5)]]),
@@ -141,6 +188,14 @@ CASES = [
     ("csr_from_mask", _csr_cols_descending,
      [lambda: P.test_csr_matches_scipy(H.F32), lambda: P.test_csr_roundtrip_and_residual("t3")]),
     ("residual", _residual_keeps_values, [lambda: P.test_csr_roundtrip_and_residual("t3")]),
+    ("pack_nibbles", _pack_nibbles_swapped, [P.test_pack_nibbles_hand_and_roundtrip]),
+    ("kmeans_1d", _kmeans_ties_high, [P.test_kmeans_hand_tie_rule]),
+    ("kmeans_1d", _kmeans_one_step,
+     [lambda: [P.test_kmeans_fixed_point_and_not_worse_than_start(s) for s in range(3)]]),
+    ("quantize_rows", _quantize_no_reassign,
+     [lambda: P.test_quantize_rows_codes_are_nearest_stored_level(H.BF16)]),
+    ("dense_from_codes", _dense_from_codes_row0_lut,
+     [P.test_dense_sparse_apply_histogram_form, P.test_quantize_rows_few_distinct_values_is_exact]),
 ]
 
 

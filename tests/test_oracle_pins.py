@@ -358,3 +358,120 @@ def test_bf16_narrowing_matches_torch():
     assert np.array_equal(mine, ref)
     assert np.array_equal(syn.f32_to_bf16_bits(a.astype(np.float32)), ref)
     assert np.array_equal(O.widen(mine, O.BF16), torch.from_numpy(ref.view(np.int16)).view(torch.bfloat16).double().numpy())
+
+
+# ---------------------------------------------------------------------------
+# Dense-and-sparse variant (SqueezeLLM explainer, section "3.中核となる技術的要素")
+# ---------------------------------------------------------------------------
+
+def test_kmeans_hand_tie_rule():
+    g = json.load(open(os.path.join(GOLDEN, "kmeans_hand.json")))
+    c, codes = O.kmeans_1d(np.array(g["values"], dtype=np.float64), g["K"])
+    assert np.allclose(c, g["centroids"], rtol=0, atol=1e-15)
+    assert codes.tolist() == g["codes"]
+
+
+def test_kmeans_recovers_separated_clusters():
+    """16 tight, equally large clusters far apart (all values distinct): each
+    starting quantile falls in its own cluster, so the levels are the cluster means and the codes the
+    cluster labels (centres ascending).  (With unequal sizes Lloyd's algorithm
+    may settle with two levels in one cluster: a local optimum.)"""
+    rng = np.random.default_rng(7)
+    centres = np.arange(16) * 10.0 - 75.0
+    sizes = np.full(16, 7)
+    vals, labels = [], []
+    for k, (c0, sz) in enumerate(zip(centres, sizes)):
+        vals.append(c0 + rng.uniform(-0.1, 0.1, size=sz))
+        labels.append(np.full(sz, k))
+    vals, labels = np.concatenate(vals), np.concatenate(labels)
+    perm = rng.permutation(vals.size)
+    vals, labels = vals[perm], labels[perm]
+    c, codes = O.kmeans_1d(vals, 16)
+    assert np.array_equal(codes, labels)
+    for k in range(16):
+        assert abs(c[k] - vals[labels == k].sum() / (labels == k).sum()) < 1e-12
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_kmeans_fixed_point_and_not_worse_than_start(seed):
+    rng = np.random.default_rng(seed)
+    v = rng.standard_t(3, size=300) * 0.02
+    K = 16
+    c, codes = O.kmeans_1d(v, K)
+    d = np.abs(v[:, None] - c[None, :])
+    # every value sits at a nearest level, the first one on ties
+    assert np.all(d[np.arange(v.size), codes] <= d.min(axis=1))
+    first = np.array([int(np.flatnonzero(row == row.min())[0]) for row in d])
+    assert np.array_equal(codes, first)
+    # every non-empty level is the mean of its values
+    for k in range(K):
+        if np.any(codes == k):
+            assert abs(c[k] - np.sum(v[codes == k]) / np.sum(codes == k)) < 1e-15 + 1e-12 * abs(c[k])
+    # Lloyd never increases the squared error of its starting quantiser
+    u = np.unique(v)
+    c0 = u[[(2 * k + 1) * u.size // (2 * K) for k in range(K)]]
+    sse0 = np.sum(np.min((v[:, None] - c0[None, :]) ** 2, axis=1))
+    sse = np.sum((v - c[codes]) ** 2)
+    assert sse <= sse0 + 1e-18
+
+
+@pytest.mark.parametrize("dtype", [O.F32, O.BF16])
+def test_quantize_rows_codes_are_nearest_stored_level(dtype):
+    W = syn.random_matrix(24, 64, dtype, seed=5, kind="t3")
+    lut, codes = O.quantize_rows(W, dtype, 4)
+    L, D = O.widen(lut, dtype), O.widen(W, dtype)
+    for i in range(W.shape[0]):
+        d = np.abs(D[i][:, None] - L[i][None, :])
+        first = np.array([int(np.flatnonzero(row == row.min())[0]) for row in d])
+        assert np.array_equal(codes[i].astype(np.int64), first)
+
+
+def test_quantize_rows_few_distinct_values_is_exact():
+    rng = np.random.default_rng(3)
+    levels = np.sort(rng.standard_normal(16)).astype(np.float32)
+    W = levels[rng.integers(0, 16, size=(10, 48))]
+    W[0, :] = levels[3]                 # a row with one distinct value
+    W[1, :] = levels[rng.integers(0, 5, size=48)]
+    lut, codes = O.quantize_rows(W, O.F32, 4)
+    assert O.bits_equal(O.narrow(O.dense_from_codes(codes, lut, O.F32), O.F32), W)
+
+
+def test_pack_nibbles_hand_and_roundtrip():
+    g = json.load(open(os.path.join(GOLDEN, "dq4_pack_hand.json")))
+    packed = O.pack_nibbles(np.array([g["codes"]], dtype=np.uint8))
+    assert packed[0].tolist() == g["bytes"]
+    rng = np.random.default_rng(1)
+    codes = rng.integers(0, 16, size=(5, 38)).astype(np.uint8)
+    assert np.array_equal(O.unpack_nibbles(O.pack_nibbles(codes), 38), codes)
+
+
+def test_dense_sparse_split_invariants():
+    assert O.outlier_count(4096, 4096) == 83886     # 0.5 % of 16,777,216, floored
+    W = syn.random_matrix(40, 64, O.BF16, seed=11, kind="t3")
+    d = O.split_dense_sparse(W, O.BF16)
+    k = O.outlier_count(40, 64)
+    assert k == 12 and len(d["col_idx"]) == k
+    S = O.dense_from_csr(40, 64, d["row_ptr"], d["col_idx"], d["values"], O.BF16)
+    R = O.widen(d["residual"], O.BF16)
+    assert np.array_equal(S + R, O.widen(W, O.BF16))             # W = S + D exactly
+    a = np.abs(O.widen(W, O.BF16))
+    assert a[S != 0].min() >= a[S == 0].max() if np.any(S != 0) else True
+    assert d["codes"].max() < 16 and d["codes_packed"].shape == (40, 32)
+
+
+def test_dense_sparse_apply_histogram_form():
+    """y_i = sum_k lut[i, k] * (sum of x_j over the columns j coded k) + (S x)_i:
+    the grouped sum equals the dense product with the dequantised D."""
+    m, n = 12, 40
+    W = syn.random_matrix(m, n, O.F32, seed=4, kind="t3")
+    d = O.split_dense_sparse(W, O.F32)
+    X = syn.random_matrix(3, n, O.F32, seed=6, kind="normal", scale=1.0).astype(np.float64)
+    S = O.dense_from_csr(m, n, d["row_ptr"], d["col_idx"], d["values"], O.F32)
+    Dq = O.dense_from_codes(d["codes"], d["lut"], O.F32)
+    Y = O.apply_factored(S + Dq, np.zeros((m, 0)), np.zeros((n, 0)), X)
+    L = O.widen(d["lut"], O.F32)
+    for c in range(3):
+        for i in range(m):
+            grouped = sum(L[i, k] * X[c, d["codes"][i] == k].sum() for k in range(16))
+            sparse = sum(S[i, j] * X[c, j] for j in range(n))
+            assert abs(Y[c, i] - (grouped + sparse)) <= 1e-12 * (1 + abs(Y[c, i]))
