@@ -17,8 +17,9 @@ launch-bound; the kernels keep their cross-call state on the device, so
 replays are exact); the plain stream-launch rate is reported beside it.
 
 Also measured in the same run (extra JSON keys): the same layer with 16-bit
-column indices and at batch 16,
-the 11008 x 4096 2:4 layer at batch 1/8/64, one decoder layer's seven
+column indices and at batch 16, its dense-and-sparse form (0.5 % outliers in
+CSR plus a 4-bit quantised dense part, stand-in codes and levels) at batch 1
+and 8, the 11008 x 4096 2:4 layer at batch 1/8/64, one decoder layer's seven
 projections per decode token (q/k/v and gate/up as grouped applies, so four
 launches per token; the seven-launch order beside it), the 8192^2 prefill at
 batch 2048 (with the low-rank GEMMs alone for their matrix-core throughput),
@@ -274,6 +275,31 @@ def main():
         extra["csr4096_b16"] = {"ms": ms16, "tokens_per_s": 16 / (ms16 * 1e-3),
                                 "gbs": bytes_head / (ms16 * 1e-3) / 1e9}
         del L
+        torch.cuda.empty_cache()
+
+        # dense-and-sparse form of the same weight: 0.5 % outliers in CSR (this
+        # library's split) + a 4-bit quantised dense part (seeded stand-in codes
+        # and levels), decode b = 1 and 8, cold rotation
+        spo = H.hss_split(W, "csr", frac=(5, 1000))
+        codes, levels = syn.quantised_standin(m, n, "bf16", cfg.seed)
+        codes_d = torch.from_numpy(codes).cuda()
+        levels_d = _bf16(levels)
+        bytes_dq = m * n // 2 + m * 16 * 2 + spo.k * (2 + 4) + 4 * (m + 1)
+        dq_copies = max(1, math.ceil(GIB / bytes_dq))
+        dq_mats = [H.HSSMatrix("csr", m, n, torch.bfloat16, row_ptr=spo.row_ptr.clone(),
+                               col_idx=spo.col_idx.clone(), values=spo.values.clone(), nnz=spo.k,
+                               dq_codes=codes_d.clone(), dq_levels=levels_d.clone())
+                   for _ in range(dq_copies)]
+        LDQ = type("LDQ", (), {"mats": dq_mats})
+        dq = {"bytes_per_apply": bytes_dq, "outliers": spo.k, "rotation_copies": dq_copies}
+        for bq in (1, 8):
+            xq, yq = _acts(cfg, bq, 0, 4, m)
+            msq = _time_graph(_apply_loop(H, LDQ, xq, yq, ws), max(1, steps // (1 if bq == 1 else 4)),
+                              args.warmup)
+            dq[f"b{bq}"] = {"ms": msq, "tokens_per_s": bq / (msq * 1e-3), "gbs": bytes_dq / (msq * 1e-3) / 1e9,
+                            "hbm_frac": bytes_dq / (msq * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        extra["dense_sparse_4096_q4"] = dq
+        del dq_mats, LDQ, codes_d, levels_d, spo
         torch.cuda.empty_cache()
 
         # 11008 x 4096 2:4, rank 64, b = 1, 8, 64

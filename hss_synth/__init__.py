@@ -42,7 +42,7 @@ __all__ = [
 ]
 
 # Stream tags (second entry of the SeedSequence entropy list).
-_TAG_W, _TAG_OUT, _TAG_X, _TAG_FAC, _TAG_SMALL = 0, 1, 2, 3, 4
+_TAG_W, _TAG_OUT, _TAG_X, _TAG_FAC, _TAG_SMALL, _TAG_DQ = 0, 1, 2, 3, 4, 5
 
 
 class Config:
@@ -162,6 +162,18 @@ def factors(m: int, n: int, r: int, dtype: str, seed: int, which: int = 0, sigma
     s = top * np.linspace(1.0, 0.5, num=max(r, 1))[:r]
     u = rng.standard_normal((m, r)) * (s / np.sqrt(m))[None, :]
     return _store(u, dtype).reshape(m, r), _store(v, dtype).reshape(n, r)
+
+
+def quantised_standin(m: int, n: int, dtype: str, seed: int, sigma_w: float = 0.02):
+    """Stand-in 4-bit quantised dense part: codes m x n/2 bytes (two uniform
+    random 4-bit codes per byte) and per-row levels m x 16 (16 sorted N(0,
+    sigma_w^2) draws), with the shapes and scale a k-means of a weight row
+    gives.  Used where quantising a full-size matrix would cost minutes of CPU;
+    the apply step's cost and its error bound do not depend on the values."""
+    rng = _rng(seed, _TAG_DQ, m, n)
+    codes = rng.integers(0, 256, size=(m, n // 2), dtype=np.uint8)
+    levels = np.sort(rng.standard_normal((m, 16)) * sigma_w, axis=1)
+    return codes, _store(levels, dtype).reshape(m, 16)
 
 
 _KINDS = ("t3", "normal", "ties", "equal", "zeros", "ints")

@@ -16,6 +16,10 @@
  *            sparse product plus two small dense products.
  *   [HASSLE] aibr.jp/archives/82335, section "3.中核となる技術的要素": N:M
  *            (here 2:4) structured sparsity as the GPU-friendly form of S.
+ *   [SQZ]    aibr.jp/archives/208940 (SqueezeLLM explainer), section
+ *            "3.中核となる技術的要素": the dense-and-sparse decomposition W = D + S,
+ *            the rare outliers kept exactly as a sparse (CSR) matrix and the
+ *            dense rest quantised with non-uniform levels.
  *
  * Conventions shared by every call
  *   - Every pointer is a caller-owned DEVICE pointer unless stated otherwise.
@@ -43,7 +47,7 @@ extern "C" {
 #endif
 
 #define HSS_VERSION_MAJOR 1
-#define HSS_VERSION_MINOR 2
+#define HSS_VERSION_MINOR 3
 
 typedef enum {
   HSS_OK = 0,
@@ -143,8 +147,18 @@ hss_status hss_get_error(const void* ws, hipStream_t stream);
  *   U  dtype[m*r]  row-major m x r.
  *   Vt dtype[r*n]  row-major r x n, i.e. the n x r factor V stored
  *                  column-major, so that V^T x reads contiguous rows.
+ *   flags & HSS_DQ4: a quantised dense part D is added to the layer
+ *     ([SQZ] dense-and-sparse: W ~= D + S with S the outliers, e.g. the top
+ *     0.5 % by |w| from hss_split, and D the residual quantised offline):
+ *       dq_codes  uint8[m*n/2]  row i, byte j holds the 4-bit codes of
+ *                 columns 2j (low nibble) and 2j+1 (high nibble);
+ *       dq_levels dtype[m*16]   row i's 16 levels;
+ *       D[i][j] = dq_levels[16 i + code(i, j)].
+ *     Requires fmt == HSS_FMT_CSR, n even and r == 0 (a dense part together
+ *     with a low-rank term returns HSS_ERR_UNSUPPORTED).
  */
 #define HSS_COL16 1
+#define HSS_DQ4 2
 
 typedef struct hss_matrix {
   int32_t fmt;   /* hss_format */
@@ -159,6 +173,8 @@ typedef struct hss_matrix {
   const uint32_t* nm_meta;
   const void* U;
   const void* Vt;
+  const uint8_t* dq_codes; /* HSS_DQ4 only (else ignored) */
+  const void* dq_levels;   /* HSS_DQ4 only (else ignored) */
 } hss_matrix;
 
 /* out[i] = (uint16) col_idx[i] for i < nnz, on `stream`: the 16-bit column
@@ -172,7 +188,8 @@ hss_status hss_csr_cols_to_u16(const int32_t* col_idx, int64_t nnz, int32_t n, u
 /* Workspace bytes hss_apply needs for this matrix and batch size. */
 hss_status hss_apply_workspace_size(const hss_matrix* A, int32_t b, size_t* bytes);
 
-/* Y (b x m, row-major) = X (b x n, row-major) times (S + U V^T)^T.
+/* Y (b x m, row-major) = X (b x n, row-major) times (S + U V^T)^T, plus the
+ * quantised dense part D for HSS_DQ4 matrices: X (S + D)^T.
  *   HSS_F32 : X, Y fp32; accumulation fp32.
  *   HSS_BF16: X bf16; products accumulated in fp32; Y bf16 = round-to-nearest-
  *             even of the fp32 result.
@@ -186,9 +203,12 @@ hss_status hss_apply_workspace_size(const hss_matrix* A, int32_t b, size_t* byte
  * [X | T^T] [S | U]^T as MFMA GEMMs with fp32 accumulation; T is rounded to
  * bf16 once, between the two; a CSR S is first expanded into a dense bf16
  * copy inside the workspace, so the workspace then holds m*n*2 more bytes);
- * otherwise one fused kernel per 8 columns.
+ * otherwise one fused kernel per 8 columns.  HSS_DQ4 matrices always run the
+ * fused dense-and-sparse kernel (up to 8 columns per pass; no workspace:
+ * hss_apply_workspace_size returns 0 and ws may be NULL).
  * Returns HSS_ERR_INVALID_ARG for: A or X or Y null, unknown fmt/dtype,
- *   unknown flags (or HSS_COL16 with a 2:4 matrix or n > 65536),
+ *   unknown flags (or HSS_COL16 with a 2:4 matrix or n > 65536; HSS_DQ4 with
+ *   a 2:4 matrix, odd n or null dq arrays),
  *   m, n <= 0, r < 0, b < 1, b*m, b*n, m*n, r*(m+n) >= 2^31,
  *   nnz < 0, required arrays null, n % 4 != 0 for 2:4, X overlapping Y.
  *   HSS_ERR_WORKSPACE for a null or short workspace.  HSS_ERR_HIP if a launch

@@ -18,13 +18,13 @@ from typing import Optional
 
 import torch
 
-from ._lib import (HSS_BF16, HSS_COL16, HSS_ERR_NONFINITE, HSS_F32, HSS_FMT_2OF4, HSS_FMT_CSR, HSS_OK,
+from ._lib import (HSS_BF16, HSS_COL16, HSS_DQ4, HSS_ERR_NONFINITE, HSS_F32, HSS_FMT_2OF4, HSS_FMT_CSR, HSS_OK,
                    HSSError, HssMatrixStruct, LIB_PATH, check, lib, status_string)
 
 __all__ = [
     "hss_version", "hss_topk_count", "hss_split_workspace_size", "hss_split", "hss_get_error",
     "hss_apply_workspace_size", "hss_apply", "hss_apply_group_workspace_size", "hss_apply_group",
-    "hss_csr_cols_to_u16", "HSS_COL16",
+    "hss_csr_cols_to_u16", "HSS_COL16", "HSS_DQ4",
     "HSSMatrix", "SplitResult", "HSSError",
     "LIB_PATH", "status_string",
 ]
@@ -131,17 +131,26 @@ def hss_get_error(ws: torch.Tensor) -> int:
 
 
 class HSSMatrix:
-    """Compressed matrix S + U V^T in device memory; keeps its tensors alive.
+    """Compressed matrix S + U V^T (or S + D) in device memory; keeps its tensors alive.
 
     U: m x r row-major.  The factor V (n x r) is held as Vt (r x n row-major,
     i.e. V column-major), the layout the library reads.  CSR col_idx is
     int32, or 16-bit (a torch.int16 tensor holding the uint16 columns, n <=
-    65536, see hss_csr_cols_to_u16) -- the matrix then carries HSS_COL16."""
+    65536, see hss_csr_cols_to_u16) -- the matrix then carries HSS_COL16.
+    dq_codes (uint8, m x n/2: the 4-bit codes of columns 2j and 2j+1 in the
+    low and high nibble of byte j) with dq_levels (m x 16, the matrix dtype)
+    add the quantised dense part D of the dense-and-sparse form (HSS_DQ4)."""
 
     def __init__(self, fmt, m, n, dtype, U=None, Vt=None, row_ptr=None, col_idx=None, values=None,
-                 nnz=None, nm_values=None, nm_meta=None):
+                 nnz=None, nm_values=None, nm_meta=None, dq_codes=None, dq_levels=None):
         self.fmt = _FMT[fmt]
         self.flags = HSS_COL16 if (col_idx is not None and col_idx.dtype == torch.int16) else 0
+        if dq_codes is not None:
+            assert dq_codes.dtype == torch.uint8 and dq_codes.is_contiguous() and dq_codes.numel() == m * n // 2
+            assert dq_levels is not None and dq_levels.dtype == dtype and dq_levels.is_contiguous()
+            assert dq_levels.numel() == m * 16
+            self.flags |= HSS_DQ4
+        self.dq_codes, self.dq_levels = dq_codes, dq_levels
         self.m, self.n = int(m), int(n)
         self.dtype = dtype
         self.U, self.Vt = U, Vt
@@ -160,6 +169,7 @@ class HSSMatrix:
         s.row_ptr, s.col_idx, s.values = _ptr(row_ptr), _ptr(col_idx), _ptr(values)
         s.nm_values, s.nm_meta = _ptr(nm_values), _ptr(nm_meta)
         s.U, s.Vt = (_ptr(U), _ptr(Vt)) if self.r > 0 else (None, None)
+        s.dq_codes, s.dq_levels = _ptr(dq_codes), _ptr(dq_levels)
         self.struct = s
 
     @classmethod
@@ -181,13 +191,13 @@ class HSSMatrix:
         return HSSMatrix("csr", self.m, self.n, self.dtype, U=self.U, Vt=self.Vt, row_ptr=self.row_ptr,
                          col_idx=c16 if c16 is not None else torch.zeros(0, dtype=torch.int16,
                                                                            device=self.row_ptr.device),
-                         values=self.values, nnz=self.nnz)
+                         values=self.values, nnz=self.nnz, dq_codes=self.dq_codes, dq_levels=self.dq_levels)
 
     def workspace(self, b: int, device=None) -> torch.Tensor:
         """Zero-filled workspace for batch b (cached per device and size)."""
         size = hss_apply_workspace_size(self, b)
         if device is None:
-            held = [t for t in (self.U, self.row_ptr, self.values, self.nm_values) if t is not None]
+            held = [t for t in (self.U, self.row_ptr, self.values, self.nm_values, self.dq_codes) if t is not None]
             device = held[0].device
         dev = device
         key = (str(dev), size)

@@ -20,6 +20,7 @@ HSS_BF16 = 1
 HSS_FMT_CSR = 0
 HSS_FMT_2OF4 = 1
 HSS_COL16 = 1  # hss_matrix.flags: CSR col_idx holds uint16 columns
+HSS_DQ4 = 2    # hss_matrix.flags: a 4-bit quantised dense part (dq_codes, dq_levels)
 
 c_int32, c_int64, c_size_t, c_void_p = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
 
@@ -33,6 +34,7 @@ class HssMatrixStruct(ctypes.Structure):
         ("row_ptr", c_void_p), ("col_idx", c_void_p), ("values", c_void_p),
         ("nm_values", c_void_p), ("nm_meta", c_void_p),
         ("U", c_void_p), ("Vt", c_void_p),
+        ("dq_codes", c_void_p), ("dq_levels", c_void_p),
     ]
 
 

@@ -11,6 +11,9 @@
 //   mfma (mfma.hip)      bf16 with b >= 16 (2:4) or b >= 24 (CSR): the
 //                        low-rank products are dense contractions and run on
 //                        the matrix cores, S expanded into the same GEMM.
+//   dense-and-sparse     HSS_DQ4 matrices (decode.hip, k_decode_dq): the
+//                        quantised dense part and the CSR outliers, up to 8
+//                        columns per pass, no workspace.
 #include "hss_internal.h"
 
 namespace hss {
@@ -21,6 +24,9 @@ void launch_decode_group(const hss_matrix* const* A, int G, int bc, const void* 
 size_t decode_ctl_bytes();
 size_t decode_t_bytes(const hss_matrix* A);
 int decode_max_cols(const hss_matrix* A);
+int decode_dq_max_cols(const hss_matrix* A);
+void launch_decode_dq(const hss_matrix* A, int bc, const void* X, void* Y, hipStream_t s);
+static bool is_dq(const hss_matrix* A) { return (A->flags & HSS_DQ4) != 0; }
 
 static constexpr int kDecodeCols = 8;
 
@@ -32,6 +38,7 @@ hss_status launch_mfma(const hss_matrix* A, int b, const void* X, void* Y, void*
 // control region persists between calls; everything after it is per-call
 // scratch, so both paths can share one workspace.
 size_t apply_ws_bytes(const hss_matrix* A, int b) {
+  if (is_dq(A)) return 0;
   const size_t dec = decode_t_bytes(A);
   const size_t mf = mfma_supported(A, b) ? mfma_ws_bytes(A, b) : 0;
   return decode_ctl_bytes() + (dec > mf ? dec : mf);
@@ -39,6 +46,17 @@ size_t apply_ws_bytes(const hss_matrix* A, int b) {
 
 hss_status launch_apply(const hss_matrix* A, int b, const void* X, void* Y, void* ws,
                         hipStream_t stream) {
+  if (is_dq(A)) {
+    const size_t es = A->dtype == HSS_F32 ? 4 : 2;
+    const int cols = decode_dq_max_cols(A);
+    if (cols == 0) return HSS_ERR_UNSUPPORTED;
+    for (int c0 = 0; c0 < b; c0 += cols) {
+      const int bc = b - c0 < cols ? b - c0 : cols;
+      launch_decode_dq(A, bc, static_cast<const char*>(X) + (size_t)c0 * A->n * es,
+                       static_cast<char*>(Y) + (size_t)c0 * A->m * es, stream);
+    }
+    return hipGetLastError() == hipSuccess ? HSS_OK : HSS_ERR_HIP;
+  }
   if (mfma_supported(A, b))
     return launch_mfma(A, b, X, Y, static_cast<char*>(ws) + decode_ctl_bytes(), stream);
   const size_t es = A->dtype == HSS_F32 ? 4 : 2;
@@ -58,6 +76,7 @@ hss_status launch_apply(const hss_matrix* A, int b, const void* X, void* Y, void
 size_t apply_group_ws_bytes(const hss_matrix* const* A, int G, int b) {
   size_t dec = 0, one = 0;
   for (int g = 0; g < G; ++g) {
+    if (is_dq(A[g])) continue;  // the dense-and-sparse kernel uses no workspace
     dec += decode_t_bytes(A[g]);
     const size_t a = apply_ws_bytes(A[g], b) - decode_ctl_bytes();
     one = one > a ? one : a;
@@ -67,8 +86,8 @@ size_t apply_group_ws_bytes(const hss_matrix* const* A, int G, int b) {
 
 hss_status launch_apply_group(const hss_matrix* const* A, int G, int b, const void* X, void* const* Y, void* ws,
                               hipStream_t stream) {
-  bool any_mfma = false;
-  for (int g = 0; g < G; ++g) any_mfma = any_mfma || mfma_supported(A[g], b);
+  bool any_mfma = false;  // (or dense-and-sparse: those run one by one too)
+  for (int g = 0; g < G; ++g) any_mfma = any_mfma || mfma_supported(A[g], b) || is_dq(A[g]);
   if (any_mfma) {
     for (int g = 0; g < G; ++g) {
       const hss_status st = launch_apply(A[g], b, X, Y[g], ws, stream);

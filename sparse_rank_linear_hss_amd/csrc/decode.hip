@@ -1281,4 +1281,269 @@ void launch_decode(const hss_matrix* A, int bc, const void* X, void* Y, void* ws
   launch_decode_group(&A, 1, bc, X, &Y, ws, s);
 }
 
+// ---------------------------------------------------------------------------
+// Dense-and-sparse apply (HSS_DQ4 matrices):
+//   Y[c][i] = sum_{j in S_i} S_ij X[c][j] + sum_j D(i, j) X[c][j],
+//   D(i, j) = levels[i][code(i, j)],
+// [SQZ] page aibr.jp/archives/208940, section "3.中核となる技術的要素": the
+// dense part, quantised with non-uniform levels, and the outliers in CSR are
+// multiplied side by side.  The codes (4 bits per weight) are the dominant
+// stream; every byte holds the codes of two adjacent columns, so one lookup
+// in a 256-entry table of level pairs (rebuilt per row from the row's 16
+// levels, in the wave's own LDS) gives both weights, and one dot2 (bf16) or
+// two FMAs (fp32) with the matching X pair from LDS accumulates them.
+//
+// Block: 4 waves, RPW rows per wave.  Lane L owns 16-byte code chunks
+// L + 64 k of each row (32 columns each); the first kDqPre chunks of every
+// row are requested at kernel start with the CSR chunks, the rest inside the
+// loop.  X (bc columns) is staged in LDS for both parts.
+// ---------------------------------------------------------------------------
+static constexpr int kDqPre = 2;
+
+struct DqArgs {
+  DecodeArgs a;          // m, n, bc, X, Y and the CSR outliers (r = 0)
+  const uint8_t* codes;  // m x n/2 bytes
+  const void* levels;    // m x 16, storage type
+  int vec_codes;         // rows of codes 16-byte aligned (n % 32 == 0, aligned base)
+  int tab_off;           // dynamic LDS byte offset of the 4 per-wave tables
+};
+
+template <int DT> struct DqEntry;  // one table entry: levels of (low, high) nibble
+template <> struct DqEntry<HSS_BF16> { using t = uint32_t; };
+template <> struct DqEntry<HSS_F32> { using t = u32x2; };
+
+// acc += (lo, hi) . (x[2p], x[2p + 1]) for one code byte.
+template <int DT>
+__device__ __forceinline__ float dq_pair(const typename DqEntry<DT>::t& e, uint32_t x0, uint32_t x1, float acc) {
+  if constexpr (DT == HSS_BF16) {
+    return dot2_bf16(e, x0, acc);  // x0 holds both bf16 x values
+  } else {
+    acc = fmaf(__uint_as_float(e.x), __uint_as_float(x0), acc);
+    return fmaf(__uint_as_float(e.y), __uint_as_float(x1), acc);
+  }
+}
+
+// One 16-byte code chunk q (columns 32 q .. 32 q + 31) of one row: 16 table
+// lookups, then the products with every column of X.  `valid` bytes of the
+// chunk belong to the row (a row's last chunk may be partial).
+template <int DT, int BC>
+__device__ __forceinline__ void dq_chunk(const u32x4& cw, int q, int valid, const typename DqEntry<DT>::t* tab,
+                                         const typename Elem<DT>::bits_t* xs, int n, int bc, float (&acc)[BC]) {
+  using E = typename DqEntry<DT>::t;
+  const uint32_t w4[4] = {cw.x, cw.y, cw.z, cw.w};
+  E e[16];
+#pragma unroll
+  for (int b = 0; b < 16; ++b) e[b] = tab[(w4[b >> 2] >> (8 * (b & 3))) & 0xffu];
+#pragma unroll
+  for (int c = 0; c < BC; ++c) {
+    if (c >= bc) break;
+    const typename Elem<DT>::bits_t* xr = xs + (int64_t)c * n + 32 * q;
+    if constexpr (DT == HSS_BF16) {
+      const u32x4* xv = reinterpret_cast<const u32x4*>(xr);  // 32 bf16 = 4 x 16 bytes
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const u32x4 x4 = xv[v];
+        const uint32_t xw[4] = {x4.x, x4.y, x4.z, x4.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int b = 4 * v + t;
+          const float f = dq_pair<DT>(e[b], xw[t], 0u, acc[c]);
+          acc[c] = b < valid ? f : acc[c];
+        }
+      }
+    } else {
+      const u32x4* xv = reinterpret_cast<const u32x4*>(xr);  // 32 fp32 = 8 x 16 bytes
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const u32x4 x4 = xv[v];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int b = 2 * v + t;
+          const float f = dq_pair<DT>(e[b], t ? x4.z : x4.x, t ? x4.w : x4.y, acc[c]);
+          acc[c] = b < valid ? f : acc[c];
+        }
+      }
+    }
+  }
+}
+
+template <int DT, int FMT, int BC, int RPW>
+__global__ __launch_bounds__(256) void k_decode_dq(DqArgs q) {
+  using bits_t = typename Elem<DT>::bits_t;
+  using E = typename DqEntry<DT>::t;
+  const DecodeArgs& a = q.a;
+  extern __shared__ __align__(16) unsigned char smem[];
+  bits_t* xs = reinterpret_cast<bits_t*>(smem + a.x_off);
+  const int t = threadIdx.x, lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  E* tab = reinterpret_cast<E*>(smem + q.tab_off) + w * 256;
+  const int m = a.m, n = a.n, bc = a.bc;
+  const int row0 = ((int)blockIdx.x * 4 + w) * RPW;
+  const int nb = n >> 1;                 // code bytes per row
+  const int nch = (nb + 15) >> 4;        // 16-byte chunks per row
+  const bits_t* __restrict__ X = static_cast<const bits_t*>(a.X);
+  const bits_t* __restrict__ L = static_cast<const bits_t*>(q.levels);
+
+  // CSR outliers: row bounds (scalar), chunk loads
+  int rb[RPW + 1];
+#pragma unroll
+  for (int i = 0; i <= RPW; ++i) rb[i] = a.row_ptr[min(row0 + i, m)];
+  CsrChunks<DT, RPW> ch;
+  if (a.vec_csr) csr_tail_issue<DT, FMT, RPW>(a, ch);
+  // levels (lane k % 16 holds level k % 16 of each row) and the first code chunks
+  uint32_t lv[RPW];
+  u32x4 cpre[RPW][kDqPre];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int64_t rowc = min(row0 + i, m - 1);
+    lv[i] = (uint32_t)L[rowc * 16 + (lane & 15)];
+#pragma unroll
+    for (int k = 0; k < kDqPre; ++k) {
+      const int cq = min(lane + 64 * k, nch - 1);
+      if (q.vec_codes)
+        cpre[i][k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(q.codes + rowc * nb) + cq);
+      else
+        cpre[i][k] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  csr_issue<DT, FMT, RPW>(a, rb, ch);
+
+  // X -> LDS
+  constexpr int NV = 16 / sizeof(bits_t);
+  if (a.vec) {
+    for (int v = t; v < bc * n / NV; v += 256)
+      reinterpret_cast<u32x4*>(xs)[v] = reinterpret_cast<const u32x4*>(X)[v];
+  } else {
+    for (int v = t; v < bc * n; v += 256) xs[v] = X[v];
+  }
+  __syncthreads();
+
+  // sparse part
+  float ssum[RPW][BC];
+  csr_consume<DT, FMT, BC, RPW>(a, ch, xs, ssum);
+
+  bits_t* __restrict__ Y = static_cast<bits_t*>(a.Y);
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int row = row0 + i;
+    const int64_t rowc = min(row, m - 1);
+    // table of level pairs: entry e = (level[e & 15], level[e >> 4]); lane L
+    // writes entries 4L .. 4L + 3 (the same high level, low levels 4(L & 3) + u)
+    {
+      const uint32_t hi = (uint32_t)__shfl((int)lv[i], lane >> 2, 64);
+      uint32_t lo[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) lo[u] = (uint32_t)__shfl((int)lv[i], 4 * (lane & 3) + u, 64);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if constexpr (DT == HSS_BF16)
+          tab[4 * lane + u] = (lo[u] & 0xffffu) | (hi << 16);
+        else
+          tab[4 * lane + u] = u32x2{lo[u], hi};
+      }
+    }
+    float acc[BC];
+#pragma unroll
+    for (int c = 0; c < BC; ++c) acc[c] = 0.f;
+    if (q.vec_codes) {
+#pragma unroll
+      for (int k = 0; k < kDqPre; ++k) {
+        const int cq = lane + 64 * k;
+        if (cq < nch) dq_chunk<DT, BC>(cpre[i][k], cq, min(16, nb - 16 * cq), tab, xs, n, bc, acc);
+      }
+      for (int cq = lane + 64 * kDqPre; cq < nch; cq += 64) {
+        const u32x4 cw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(q.codes + rowc * nb) + cq);
+        dq_chunk<DT, BC>(cw, cq, min(16, nb - 16 * cq), tab, xs, n, bc, acc);
+      }
+    } else {
+      // unaligned rows: bytes one at a time
+      for (int cq = lane; cq < nch; cq += 64) {
+        uint32_t w4[4] = {0u, 0u, 0u, 0u};
+        const int valid = min(16, nb - 16 * cq);
+        for (int b = 0; b < valid; ++b) w4[b >> 2] |= (uint32_t)q.codes[rowc * nb + 16 * cq + b] << (8 * (b & 3));
+        dq_chunk<DT, BC>(u32x4{w4[0], w4[1], w4[2], w4[3]}, cq, valid, tab, xs, n, bc, acc);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < BC; ++c) {
+      const float s = wave_sum(acc[c]) + ssum[i][c];
+      if (row < m && c < bc && lane == c) {
+        if constexpr (DT == HSS_F32)
+          Y[(int64_t)c * m + row] = __float_as_uint(s);
+        else
+          Y[(int64_t)c * m + row] = f32_to_bf16(s);
+      }
+    }
+  }
+}
+
+// Largest column count per dense-and-sparse pass whose staged X fits 96 KiB;
+// one column when n % 8 != 0 (the 16-byte X reads of later columns would be
+// misaligned).
+int decode_dq_max_cols(const hss_matrix* A) {
+  const size_t es = A->dtype == HSS_F32 ? 4 : 2;
+  if (A->n % 8 != 0) return 1;
+  for (int bc = 8; bc >= 1; bc /= 2)
+    if (align16((size_t)bc * A->n * es) <= 96 * 1024) return bc;
+  return 0;
+}
+
+template <int DT, int FMT, int BC, int RPW>
+static void launch_dq_k(const DqArgs& q, unsigned grid, size_t lds, hipStream_t s) {
+  static bool big_lds = false;
+  if (lds > 64 * 1024 && !big_lds) {
+    hipFuncSetAttribute(reinterpret_cast<const void*>(&k_decode_dq<DT, FMT, BC, RPW>),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, 112 * 1024);
+    big_lds = true;
+  }
+  hipLaunchKernelGGL((k_decode_dq<DT, FMT, BC, RPW>), dim3(grid), dim3(256), lds, s, q);
+}
+
+template <int DT, int FMT, int BC>
+static void launch_dq_rpw(const DqArgs& q, unsigned grid, int rpw, size_t lds, hipStream_t s) {
+  if (rpw == 2) launch_dq_k<DT, FMT, BC, 2>(q, grid, lds, s);
+  else launch_dq_k<DT, FMT, BC, 1>(q, grid, lds, s);
+}
+
+template <int DT, int FMT>
+static void launch_dq_bc(const DqArgs& q, unsigned grid, int bc, int rpw, size_t lds, hipStream_t s) {
+  if (bc == 1) launch_dq_rpw<DT, FMT, 1>(q, grid, rpw, lds, s);
+  else if (bc == 2) launch_dq_rpw<DT, FMT, 2>(q, grid, rpw, lds, s);
+  else if (bc <= 4) launch_dq_rpw<DT, FMT, 4>(q, grid, rpw, lds, s);
+  else launch_dq_rpw<DT, FMT, 8>(q, grid, rpw, lds, s);
+}
+
+// One dense-and-sparse pass over bc (<= decode_dq_max_cols) columns.
+void launch_decode_dq(const hss_matrix* A, int bc, const void* X, void* Y, hipStream_t s) {
+  DqArgs q = {};
+  DecodeArgs& a = q.a;
+  const size_t es = A->dtype == HSS_F32 ? 4 : 2;
+  a.m = A->m; a.n = A->n; a.r = 0; a.bc = bc;
+  a.row_ptr = A->row_ptr; a.vals = A->values;
+  a.col_idx = col16_of(A) ? nullptr : A->col_idx;
+  a.col16 = col16_of(A) ? reinterpret_cast<const uint16_t*>(A->col_idx) : nullptr;
+  a.X = X; a.Y = Y;
+  a.nnz = A->nnz;
+  a.x_lds = 1;
+  a.vec = ((uintptr_t)X % 16 == 0) && ((size_t)A->n * es) % 16 == 0;
+  a.vec_csr = A->nnz >= 4 && (uintptr_t)A->col_idx % (col16_of(A) ? 8 : 16) == 0 &&
+              (uintptr_t)A->values % (4 * es) == 0;
+  a.x_off = 0;
+  q.codes = A->dq_codes;
+  q.levels = A->dq_levels;
+  q.vec_codes = A->n % 32 == 0 && (uintptr_t)A->dq_codes % 16 == 0;
+  q.tab_off = (int)align16((size_t)bc * A->n * es);
+  const size_t lds = (size_t)q.tab_off + 4 * 256 * (A->dtype == HSS_F32 ? 8 : 4);
+  const int rpw = A->m >= 2048 ? 2 : 1;
+  const unsigned grid = (unsigned)((A->m + 4 * rpw - 1) / (4 * rpw));
+  const int fmt = col16_of(A) ? kFmtCsr16 : HSS_FMT_CSR;
+  if (A->dtype == HSS_F32) {
+    if (fmt == kFmtCsr16) launch_dq_bc<HSS_F32, kFmtCsr16>(q, grid, bc, rpw, lds, s);
+    else launch_dq_bc<HSS_F32, HSS_FMT_CSR>(q, grid, bc, rpw, lds, s);
+  } else {
+    if (fmt == kFmtCsr16) launch_dq_bc<HSS_BF16, kFmtCsr16>(q, grid, bc, rpw, lds, s);
+    else launch_dq_bc<HSS_BF16, HSS_FMT_CSR>(q, grid, bc, rpw, lds, s);
+  }
+}
+
 }  // namespace hss

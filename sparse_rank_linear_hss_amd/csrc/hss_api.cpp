@@ -87,11 +87,15 @@ hss_status hss_get_error(const void* ws, hipStream_t stream) {
 }
 
 static hss_status check_matrix(const hss_matrix* A, int32_t b) {
-  if (!A || !valid_fmt(A->fmt) || !valid_dtype(A->dtype) || (A->flags & ~HSS_COL16) != 0)
+  if (!A || !valid_fmt(A->fmt) || !valid_dtype(A->dtype) || (A->flags & ~(HSS_COL16 | HSS_DQ4)) != 0)
     return HSS_ERR_INVALID_ARG;
   if ((A->flags & HSS_COL16) && (A->fmt != HSS_FMT_CSR || A->n > 65536)) return HSS_ERR_INVALID_ARG;
   const int64_t m = A->m, n = A->n, r = A->r;
   if (m <= 0 || n <= 0 || r < 0 || b < 1) return HSS_ERR_INVALID_ARG;
+  if (A->flags & HSS_DQ4) {
+    if (A->fmt != HSS_FMT_CSR || n % 2 != 0 || !A->dq_codes || !A->dq_levels) return HSS_ERR_INVALID_ARG;
+    if (r > 0) return HSS_ERR_UNSUPPORTED;
+  }
   if (m * n >= kLimit || (int64_t)b * m >= kLimit || (int64_t)b * n >= kLimit ||
       r * (m + n) >= kLimit)
     return HSS_ERR_INVALID_ARG;
@@ -128,7 +132,8 @@ hss_status hss_apply(const hss_matrix* A, int32_t b, const void* X, void* Y, voi
   if (!X || !Y) return HSS_ERR_INVALID_ARG;
   const size_t es = dsize(A->dtype);
   if (overlap(X, (size_t)b * A->n * es, Y, (size_t)b * A->m * es)) return HSS_ERR_INVALID_ARG;
-  if (!ws || ws_bytes < hss::apply_ws_bytes(A, b)) return HSS_ERR_WORKSPACE;
+  const size_t need = hss::apply_ws_bytes(A, b);
+  if ((need > 0 && !ws) || ws_bytes < need) return HSS_ERR_WORKSPACE;
   return hss::launch_apply(A, b, X, Y, ws, stream);
 }
 

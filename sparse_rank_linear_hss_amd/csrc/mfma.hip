@@ -784,6 +784,7 @@ static MfmaPlan plan_mfma(const hss_matrix* A, int b) {
 // decode passes with X in LDS beat densifying S -- measured 43 vs 49 us on
 // the 4096 x 4096 5 % layer).
 bool mfma_supported(const hss_matrix* A, int b) {
+  if (A->flags & HSS_DQ4) return false;  // dense-and-sparse: its own fused kernel
   if (A->dtype != HSS_BF16 || b < (A->fmt == HSS_FMT_CSR ? 24 : 16)) return false;
   if (A->fmt == HSS_FMT_CSR && A->n % 8 != 0) return false;  // dense copy written in 16-byte rows
   if (A->fmt == HSS_FMT_2OF4 && (A->n % 32 != 0 || (uintptr_t)A->nm_values % 16 || (uintptr_t)A->nm_meta % 4))

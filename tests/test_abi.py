@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(hl):
 
 
 def test_version_and_strings(hl):
-    assert hl.hss_version() == 102
+    assert hl.hss_version() == 103
     for code in range(6):
         assert hl.status_string(code).startswith("HSS_")
 
@@ -112,7 +112,18 @@ def test_apply_rejects_bad_arguments(hl):
     assert lib.hss_apply(None, 1, FAKE, FAKE * 2, FAKE * 3, 1 << 20, None) == INV
     assert _apply(hl, _matrix(hl, fmt=5)) == INV
     assert _apply(hl, _matrix(hl, dtype=3)) == INV
-    assert _apply(hl, _matrix(hl, flags=2)) == INV                  # unknown flag
+    assert _apply(hl, _matrix(hl, flags=4)) == INV                  # unknown flag
+    # dense-and-sparse (HSS_DQ4): arrays required, CSR only, n even, no low-rank term
+    assert _apply(hl, _matrix(hl, flags=2, r=0, U=None, Vt=None)) == INV
+    assert _apply(hl, _matrix(hl, flags=2, r=0, U=None, Vt=None, dq_codes=FAKE)) == INV
+    assert _apply(hl, _matrix(hl, flags=2, r=0, U=None, Vt=None, dq_codes=FAKE, dq_levels=FAKE, fmt=1,
+                              nm_values=FAKE, nm_meta=FAKE)) == INV
+    assert _apply(hl, _matrix(hl, flags=2, r=0, U=None, Vt=None, dq_codes=FAKE, dq_levels=FAKE, n=31)) == INV
+    assert _apply(hl, _matrix(hl, flags=2, dq_codes=FAKE, dq_levels=FAKE)) == hl._lib.HSS_ERR_UNSUPPORTED
+    dq_sz = ctypes.c_size_t(1)
+    assert lib.hss_apply_workspace_size(ctypes.byref(_matrix(hl, flags=2, r=0, U=None, Vt=None, dq_codes=FAKE,
+                                                             dq_levels=FAKE)), 7, ctypes.byref(dq_sz)) == 0
+    assert dq_sz.value == 0                                         # the dense-and-sparse kernel needs none
     assert _apply(hl, _matrix(hl, fmt=1, flags=1, nm_values=FAKE, nm_meta=FAKE)) == INV  # COL16 on 2:4
     assert _apply(hl, _matrix(hl, flags=1, n=65537)) == INV         # COL16 needs n <= 65536
     assert _apply(hl, _matrix(hl, m=0)) == INV
