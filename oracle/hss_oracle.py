@@ -25,6 +25,12 @@ Sources (web pages; section names as printed on each page)
             into one sparse product plus two small dense products.
 [HASSLE]  aibr.jp/archives/82335 (explainer of HASSLE-free), section
           "3.中核となる技術的要素": N:M sparsity as the GPU-friendly structure.
+          section "順列と階層的整列" (permutation and hierarchical alignment; its
+          vision rewrite "置換と階層的整列"): the concentration ratio rho =
+          (sum of |W| over the diagonal blocks) / (sum of |W|); a Reverse
+          Cuthill-McKee order of rows and columns pulls large |w| towards the
+          diagonal; the factorisation works on a 2 x 2 block partition, the
+          off-diagonal blocks at a low rank (8), the diagonal ones higher (32).
 [SQZ]     aibr.jp/archives/208940 (explainer of SqueezeLLM), section
           "3.中核となる技術的要素": the dense-and-sparse decomposition W = D + S
           (the rare outliers kept exactly in a CSR matrix S, the dense rest D
@@ -46,9 +52,20 @@ Readings where the pages are silent (each is listed in the design notes):
   residual; each row of D is quantised to 2^bits levels by unweighted 1-D
   k-means (the pages' sensitivity weights need gradients from data, which
   this path has none of), started at quantiles of the distinct values, ties
-  to the lower level; levels are stored in the weight's type and every code is the nearest
-  stored level.  4-bit codes are packed two per byte, the even column in the
-  low nibble.
+  to the lower level; levels are stored in the weight's type and every code
+  is the nearest stored level.  4-bit codes are packed two per byte, the even
+  column in the low nibble.
+* Hierarchical variant (one level, as the 512 x 512 example describes): the
+  2 x 2 blocks split rows at m1 = m // 2 and columns at n1 = n // 2; rho
+  counts the two diagonal blocks.  RCM works on the symmetric graph of the
+  stage-1 support (edge i - j when S has (i, j) or (j, i), i != j) of a
+  square matrix: components in order of their lowest-degree (then lowest
+  index) unvisited node, breadth-first, each node's unvisited neighbours
+  queued by (degree, index) ascending; the visit order reversed.  perm[i] is
+  the original index at position i; the permuted matrix is W'[i, j] =
+  W[perm[i], perm[j]].  S stays in the original order (stage 1 before the
+  permutation); each block of the permuted residual gets its own truncated
+  SVD.
 
 Storage conventions (the same ones the C library documents):
   fp32 values are numpy.float32; bf16 values are their bit patterns in
@@ -424,4 +441,130 @@ def split_dense_sparse(W, dtype, k=None, bits=4):
     lut, codes = quantize_rows(s["residual"], dtype, bits)
     s.update(lut=lut, codes=codes, codes_packed=pack_nibbles(codes) if bits == 4 else None)
     return s
+
+
+# ---------------------------------------------------------------------------
+# Hierarchical variant ([HSS] section "順列と階層的整列"): concentration ratio,
+# Reverse Cuthill-McKee order, 2 x 2 block low-rank factors
+# ---------------------------------------------------------------------------
+
+def concentration_ratio(W, dtype, perm=None):
+    """rho = sum |W'| over the two diagonal blocks / sum |W'|, W' = W with rows
+    and columns in the order perm (identity when None); blocks split at
+    m // 2 and n // 2.  0 for an all-zero matrix."""
+    a = magnitudes(W, dtype)
+    if perm is not None:
+        p = np.asarray(perm, dtype=np.int64)
+        a = a[p][:, p]
+    m, n = a.shape
+    m1, n1 = m // 2, n // 2
+    total = a.sum()
+    if total == 0:
+        return 0.0
+    return float((a[:m1, :n1].sum() + a[m1:, n1:].sum()) / total)
+
+
+def rcm_graph(n, row_ptr, col_idx):
+    """Neighbour sets of the symmetric graph of a square CSR pattern (i != j)."""
+    nbr = [set() for _ in range(n)]
+    for i in range(n):
+        for p in range(int(row_ptr[i]), int(row_ptr[i + 1])):
+            j = int(col_idx[p])
+            if j != i:
+                nbr[i].add(j)
+                nbr[j].add(i)
+    return nbr
+
+
+def rcm_order(n, row_ptr, col_idx):
+    """Reverse Cuthill-McKee order of the pattern (module notes):
+    perm[i] = original index placed at position i."""
+    nbr = rcm_graph(n, row_ptr, col_idx)
+    deg = [len(s) for s in nbr]
+    seen = [False] * n
+    order = []
+    while len(order) < n:
+        start = min((v for v in range(n) if not seen[v]), key=lambda v: (deg[v], v))
+        seen[start] = True
+        queue = [start]
+        head = 0
+        while head < len(queue):
+            u = queue[head]
+            head += 1
+            for v in sorted((v for v in nbr[u] if not seen[v]), key=lambda v: (deg[v], v)):
+                seen[v] = True
+                queue.append(v)
+        order.extend(queue)
+    return np.array(order[::-1], dtype=np.int32)
+
+
+def bandwidth(n, row_ptr, col_idx, perm=None):
+    """max |pos(i) - pos(j)| over the pattern's entries, positions after perm."""
+    pos = np.arange(n) if perm is None else np.argsort(np.asarray(perm))
+    bw = 0
+    for i in range(n):
+        for p in range(int(row_ptr[i]), int(row_ptr[i + 1])):
+            bw = max(bw, abs(int(pos[i]) - int(pos[int(col_idx[p])])))
+    return bw
+
+
+def hier_factors(R64p, r_diag, r_off):
+    """Truncated SVD of each block of the (permuted) residual, blocks split at
+    m // 2 and n // 2: rank r_diag on the diagonal blocks, r_off off it (each
+    capped at the block's smaller side).  Returns {(bi, bj): (U, V)}, U
+    (block rows) x r and V (block columns) x r, U carrying the singular values."""
+    R64p = np.asarray(R64p, dtype=np.float64)
+    m, n = R64p.shape
+    rows = [(0, m // 2), (m // 2, m)]
+    cols = [(0, n // 2), (n // 2, n)]
+    out = {}
+    for bi in range(2):
+        for bj in range(2):
+            blk = R64p[rows[bi][0]:rows[bi][1], cols[bj][0]:cols[bj][1]]
+            r = min(r_diag if bi == bj else r_off, min(blk.shape))
+            U, V, _ = truncated_svd(blk, r)
+            out[(bi, bj)] = (U, V)
+    return out
+
+
+def hier_param_count(k, m, n, r_diag, r_off):
+    """Stored parameters: k sparse values plus, per block, (rows + cols) * rank."""
+    m1, n1 = m // 2, n // 2
+    m2, n2 = m - m1, n - n1
+    return int(k) + (m1 + n1 + m2 + n2) * r_diag + (m1 + n2 + m2 + n1) * r_off
+
+
+def hier_lowrank_dense(blocks, perm, m, n):
+    """The block low-rank term as a dense m x n matrix in the original order:
+    block (bi, bj) of the permuted matrix is U V^T, and permuted position
+    (i, j) is original (perm[i], perm[j]) (identity when perm is None; then
+    m and n may differ)."""
+    Lp = np.zeros((m, n))
+    for (bi, bj), (U, V) in blocks.items():
+        r0, r1 = (0, m // 2) if bi == 0 else (m // 2, m)
+        c0, c1 = (0, n // 2) if bj == 0 else (n // 2, n)
+        Lp[r0:r1, c0:c1] = U @ V.T
+    if perm is None:
+        return Lp
+    p = np.asarray(perm, dtype=np.int64)
+    L = np.zeros((m, n))
+    L[np.ix_(p, p)] = Lp
+    return L
+
+
+def hier_apply(S64, blocks, perm, X64):
+    """Y = X S^T + the block low-rank term applied through its factors: x' =
+    x[perm], y'_block_rows += (x'_block_cols V) U^T, y[perm] += y'."""
+    m, n = S64.shape
+    p = np.arange(n) if perm is None else np.asarray(perm, dtype=np.int64)
+    Xp = X64[:, p]
+    Yp = np.zeros((X64.shape[0], m))
+    for (bi, bj), (U, V) in blocks.items():
+        r0, r1 = (0, m // 2) if bi == 0 else (m // 2, m)
+        c0, c1 = (0, n // 2) if bj == 0 else (n // 2, n)
+        Yp[:, r0:r1] += (Xp[:, c0:c1] @ V) @ U.T
+    Y = X64 @ S64.T
+    q = np.arange(m) if perm is None else np.asarray(perm, dtype=np.int64)
+    Y[:, q] += Yp
+    return Y
 

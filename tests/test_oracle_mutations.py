@@ -165,6 +165,68 @@ def _dense_from_codes_row0_lut(codes, lut, dtype):
     return L[0][np.asarray(codes, dtype=np.int64)]       # one row's levels for every row
 
 
+_orig_rcm = H.rcm_order
+
+
+def _rcm_not_reversed(n, row_ptr, col_idx):
+    return _orig_rcm(n, row_ptr, col_idx)[::-1].copy()
+
+
+def _rcm_ties_high(n, row_ptr, col_idx):
+    nbr = H.rcm_graph(n, row_ptr, col_idx)
+    deg = [len(x) for x in nbr]
+    seen, order = [False] * n, []
+    while len(order) < n:
+        start = min((v for v in range(n) if not seen[v]), key=lambda v: (deg[v], -v))
+        seen[start] = True
+        queue, head = [start], 0
+        while head < len(queue):
+            u = queue[head]
+            head += 1
+            for v in sorted((v for v in nbr[u] if not seen[v]), key=lambda v: (deg[v], -v)):
+                seen[v] = True
+                queue.append(v)
+        order.extend(queue)
+    return np.array(order[::-1], dtype=np.int32)
+
+
+def _rho_off_diagonal(W, dtype, perm=None):
+    a = H.magnitudes(W, dtype)
+    if perm is not None:
+        p = np.asarray(perm, dtype=np.int64)
+        a = a[p][:, p]
+    m, n = a.shape
+    t = a.sum()
+    return 0.0 if t == 0 else float((a[:m // 2, n // 2:].sum() + a[m // 2:, :n // 2].sum()) / t)
+
+
+def _hier_factors_split_shifted(R64p, r_diag, r_off):
+    R64p = np.asarray(R64p, dtype=np.float64)
+    m, n = R64p.shape
+    rows = [(0, m // 2 + 1), (m // 2 + 1, m)]
+    cols = [(0, n // 2), (n // 2, n)]
+    out = {}
+    for bi in range(2):
+        for bj in range(2):
+            blk = R64p[rows[bi][0]:rows[bi][1], cols[bj][0]:cols[bj][1]]
+            r = min(r_diag if bi == bj else r_off, min(blk.shape))
+            U, V, _ = H.truncated_svd(blk, r)
+            out[(bi, bj)] = (U, V)
+    return out
+
+
+def _hier_apply_perm_inverted(S64, blocks, perm, X64):
+    m, n = S64.shape
+    p = np.arange(n) if perm is None else np.asarray(perm, dtype=np.int64)
+    Xp = X64[:, p]
+    Yp = np.zeros((X64.shape[0], m))
+    for (bi, bj), (U, V) in blocks.items():
+        r0, r1 = (0, m // 2) if bi == 0 else (m // 2, m)
+        c0, c1 = (0, n // 2) if bj == 0 else (n // 2, n)
+        Yp[:, r0:r1] += (Xp[:, c0:c1] @ V) @ U.T
+    return X64 @ S64.T + Yp[:, p]                         # y = y'[perm] instead of y[perm] = y'
+
+
 CASES = [
     ("apply_factored", _apply_no_lowrank,
      [P.test_apply_hand_example, lambda: [P.test_apply_factored_equals_dense(s) for s in range(5)]]),
@@ -196,6 +258,11 @@ CASES = [
      [lambda: P.test_quantize_rows_codes_are_nearest_stored_level(H.BF16)]),
     ("dense_from_codes", _dense_from_codes_row0_lut,
      [P.test_dense_sparse_apply_histogram_form, P.test_quantize_rows_few_distinct_values_is_exact]),
+    ("rcm_order", _rcm_not_reversed, [P.test_rcm_hand_example]),
+    ("rcm_order", _rcm_ties_high, [P.test_rcm_hand_example]),
+    ("concentration_ratio", _rho_off_diagonal, [P.test_concentration_ratio_closed_forms]),
+    ("hier_factors", _hier_factors_split_shifted, [P.test_hier_full_rank_reproduces_residual_and_eckart_young]),
+    ("hier_apply", _hier_apply_perm_inverted, [lambda: P.test_hier_apply_equals_dense(True)]),
 ]
 
 

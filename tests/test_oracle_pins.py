@@ -475,3 +475,109 @@ def test_dense_sparse_apply_histogram_form():
             grouped = sum(L[i, k] * X[c, d["codes"][i] == k].sum() for k in range(16))
             sparse = sum(S[i, j] * X[c, j] for j in range(n))
             assert abs(Y[c, i] - (grouped + sparse)) <= 1e-12 * (1 + abs(Y[c, i]))
+
+
+# ---------------------------------------------------------------------------
+# Hierarchical variant ([HSS] section "順列と階層的整列")
+# ---------------------------------------------------------------------------
+
+def test_concentration_ratio_closed_forms():
+    # constant blocks: diagonal quadrants |a|, off-diagonal |b| -> rho = (m1 n1 + m2 n2) a / (that + rest)
+    m, n = 7, 5
+    m1, n1 = 3, 2
+    W = np.full((m, n), -3.0, dtype=np.float32)
+    W[:m1, :n1] = 2.0
+    W[m1:, n1:] = 2.0
+    diag = 2.0 * (m1 * n1 + (m - m1) * (n - n1))
+    off = 3.0 * (m1 * (n - n1) + (m - m1) * n1)
+    assert abs(O.concentration_ratio(W, O.F32) - diag / (diag + off)) < 1e-15
+    # block-diagonal -> 1; all zero -> 0
+    B = np.zeros((6, 6), dtype=np.float32)
+    B[:3, :3] = 1.5
+    B[3:, 3:] = -0.5
+    assert O.concentration_ratio(B, O.F32) == 1.0
+    assert O.concentration_ratio(np.zeros((4, 4), np.float32), O.F32) == 0.0
+    # a scrambled matrix measured in the order that unscrambles it
+    sigma = np.random.default_rng(2).permutation(6)
+    Wsc = B[np.argsort(sigma)][:, np.argsort(sigma)]   # Wsc[sigma[i], sigma[j]] = B[i, j]
+    assert O.concentration_ratio(Wsc, O.F32, perm=sigma) == 1.0
+
+
+def test_rcm_hand_example():
+    g = json.load(open(os.path.join(GOLDEN, "rcm_hand.json")))
+    assert O.rcm_order(g["n"], g["row_ptr"], g["col_idx"]).tolist() == g["perm"]
+
+
+def _csr_of_edges(n, edges):
+    rows = [[] for _ in range(n)]
+    for a, b in edges:
+        rows[a].append(b)
+    rp, ci = [0], []
+    for i in range(n):
+        ci += sorted(rows[i])
+        rp.append(len(ci))
+    return rp, ci
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_rcm_recovers_a_scrambled_path(seed):
+    n = 9 + seed
+    q = np.random.default_rng(seed).permutation(n)
+    rp, ci = _csr_of_edges(n, [(int(q[t]), int(q[t + 1])) for t in range(n - 1)])
+    perm = O.rcm_order(n, rp, ci)
+    assert sorted(perm.tolist()) == list(range(n))
+    assert O.bandwidth(n, rp, ci, perm) == 1
+    assert O.bandwidth(n, rp, ci) > 1
+
+
+def test_rcm_keeps_components_contiguous():
+    # two scrambled paths on interleaved node sets, plus an isolated node
+    n = 11
+    a, b = [0, 2, 4, 6, 8], [1, 3, 5, 7, 9]
+    rp, ci = _csr_of_edges(n, [(a[t], a[t + 1]) for t in range(4)] + [(b[t + 1], b[t]) for t in range(4)])
+    perm = O.rcm_order(n, rp, ci).tolist()
+    pos = {v: i for i, v in enumerate(perm)}
+    for comp in (a, b, [10]):
+        ps = sorted(pos[v] for v in comp)
+        assert ps == list(range(ps[0], ps[0] + len(comp)))
+    assert O.bandwidth(n, rp, ci, np.array(perm)) == 1
+
+
+def test_hier_full_rank_reproduces_residual_and_eckart_young():
+    rng = np.random.default_rng(4)
+    m = n = 13                                   # odd: blocks 6 and 7
+    R = rng.standard_normal((m, n))
+    full = O.hier_factors(R, 7, 7)
+    assert np.max(np.abs(O.hier_lowrank_dense(full, None, m, n) - R)) < 1e-12
+    low = O.hier_factors(R, 4, 2)
+    rows, cols = [(0, 6), (6, 13)], [(0, 6), (6, 13)]
+    for (bi, bj), (U, V) in low.items():
+        blk = R[rows[bi][0]:rows[bi][1], cols[bj][0]:cols[bj][1]]
+        r = 4 if bi == bj else 2
+        assert U.shape == (blk.shape[0], r) and V.shape == (blk.shape[1], r)
+        s = np.linalg.svd(blk, compute_uv=False)
+        assert abs(np.linalg.norm(blk - U @ V.T) - np.sqrt(np.sum(s[r:] ** 2))) < 1e-10
+
+
+def test_hier_param_count_512_example():
+    # the pages' 512 x 512 example: diagonal blocks rank 32, off-diagonal rank 8 (no S)
+    assert O.hier_param_count(0, 512, 512, 32, 8) == (256 + 256) * 32 * 2 + (256 + 256) * 8 * 2 == 40960
+    assert O.hier_param_count(10, 5, 3, 2, 1) == 10 + (2 + 1 + 3 + 2) * 2 + (2 + 2 + 3 + 1) * 1
+
+
+@pytest.mark.parametrize("permuted", [False, True])
+def test_hier_apply_equals_dense(permuted):
+    rng = np.random.default_rng(8)
+    m = n = 11
+    S = np.where(rng.random((m, n)) < 0.2, rng.standard_normal((m, n)), 0.0)
+    R = rng.standard_normal((m, n))
+    perm = rng.permutation(n) if permuted else None
+    Rp = R if perm is None else R[perm][:, perm]
+    blocks = O.hier_factors(Rp, 3, 1)
+    X = rng.standard_normal((4, n))
+    A = S + O.hier_lowrank_dense(blocks, perm, m, n)
+    Y = O.hier_apply(S, blocks, perm, X)
+    assert np.max(np.abs(Y - X @ A.T)) < 1e-12 * (1 + np.max(np.abs(Y)))
+    # with full ranks the permuted low-rank term is R itself, back in the original order
+    fullb = O.hier_factors(Rp, 6, 6)
+    assert np.max(np.abs(O.hier_lowrank_dense(fullb, perm, m, n) - R)) < 1e-12
