@@ -17,7 +17,9 @@ launch-bound; the kernels keep their cross-call state on the device, so
 replays are exact); the plain stream-launch rate is reported beside it.
 
 Also measured in the same run (extra JSON keys): the same layer with 16-bit
-column indices and at batch 16, its dense-and-sparse form (0.5 % outliers in
+column indices and at batch 16, its hierarchical form (Reverse
+Cuthill-McKee order of S's support, concentration ratio, 2 x 2 block
+factors of ranks 96 / 32 packed to rank 256) at batch 1, its dense-and-sparse form (0.5 % outliers in
 CSR plus a 4-bit quantised dense part, stand-in codes and levels) at batch 1
 and 8, the 11008 x 4096 2:4 layer at batch 1/8/64, one decoder layer's seven
 projections per decode token (q/k/v and gate/up as grouped applies, so four
@@ -274,6 +276,48 @@ def main():
         ms16 = _time_graph(_apply_loop(H, L, xs16, ys16, ws), max(1, steps // 4), 20)
         extra["csr4096_b16"] = {"ms": ms16, "tokens_per_s": 16 / (ms16 * 1e-3),
                                 "gbs": bytes_head / (ms16 * 1e-3) / 1e9}
+
+        # hierarchical form: RCM order of S's support (host), concentration
+        # ratio before / after it, 2 x 2 block factors (seeded stand-ins,
+        # ranks 96 diagonal / 32 off, so R = 256 as in the flat layer) packed
+        # into flat factors, decode b = 1 with the headline's rotation
+        import numpy as np
+        rp_h = L.split.row_ptr.cpu().numpy()
+        ci_h = L.split.col_idx.cpu().numpy()
+        t0 = time.perf_counter()
+        perm = H.hss_rcm_order(rp_h, ci_h, n)
+        rcm_ms = (time.perf_counter() - t0) * 1e3
+        pos = np.empty(n, dtype=np.int64)
+        pos[perm] = np.arange(n)
+        rows_h = np.repeat(np.arange(m), np.diff(rp_h))
+        bw = [int(np.abs(rows_h - ci_h).max()), int(np.abs(pos[rows_h] - pos[ci_h]).max())]
+        perm_d = torch.from_numpy(perm).cuda()
+        rho = [float(H.hss_concentration(W)[0]), float(H.hss_concentration(W, perm_d)[0])]
+        rd, ro = 96, 32
+        hU, hVt = [], []
+        for blk in range(4):
+            rb = rd if blk in (0, 3) else ro
+            Ub, Vb = syn.factors(m // 2, n // 2, rb, "bf16", cfg.seed, 10 + blk)
+            hU.append(_bf16(Ub))
+            hVt.append(_bf16(np.ascontiguousarray(Vb.T)))
+        e0.record()
+        Ucat, Vtcat = H.hss_hier_pack(hU, hVt, m, n, perm_d)
+        e1.record()
+        torch.cuda.synchronize()
+        pack_ms = e0.elapsed_time(e1)
+        sp = L.split
+        h_mats = [H.HSSMatrix("csr", m, n, torch.bfloat16, U=Ucat.clone(), Vt=Vtcat.clone(),
+                              row_ptr=sp.row_ptr.clone(), col_idx=sp.col_idx.clone(), values=sp.values.clone(),
+                              nnz=sp.k) for _ in range(copies_head)]
+        LH = type("LH", (), {"mats": h_mats})
+        msh = _time_graph(_apply_loop(H, LH, xs, ys, ws), steps, args.warmup)
+        R_h = 2 * (rd + ro)
+        extra["hier2x2_4096_b1"] = {
+            "ms": msh, "tokens_per_s": 1 / (msh * 1e-3), "gbs": bytes_head / (msh * 1e-3) / 1e9,
+            "ranks_diag_off": [rd, ro], "packed_rank": R_h,
+            "factor_bytes_compact": (m + n) * (rd + ro) * 2, "factor_bytes_stored": (m + n) * R_h * 2,
+            "rcm_host_ms": rcm_ms, "pack_ms": pack_ms, "rho_identity_rcm": rho, "bandwidth_identity_rcm": bw}
+        del h_mats, LH, Ucat, Vtcat, hU, hVt, perm_d
         del L
         torch.cuda.empty_cache()
 

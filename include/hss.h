@@ -242,6 +242,65 @@ hss_status hss_apply_group_workspace_size(const hss_matrix* const* A, int32_t G,
 hss_status hss_apply_group(const hss_matrix* const* A, int32_t G, int32_t b, const void* X, void* const* Y,
                            void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Hierarchical variant ([HSS] section "順列と階層的整列", vision rewrite
+ * "置換と階層的整列"): reorder rows and columns so that the large weights sit
+ * near the diagonal, measure how much magnitude the diagonal blocks hold,
+ * and factor the residual block by block (a higher rank on the two diagonal
+ * blocks than off them).  One level of 2 x 2 blocks: rows split at m / 2,
+ * columns at n / 2.
+ * ------------------------------------------------------------------------
+ *
+ * hss_rcm_order: Reverse Cuthill-McKee order of a square n x n sparsity
+ *   pattern given as CSR in HOST memory (e.g. the support of S from
+ *   hss_split), computed on the host, synchronously.  Graph: i - j when the
+ *   pattern has (i, j) or (j, i), i != j.  Each component is walked
+ *   breadth-first from its unvisited node of lowest degree (then lowest
+ *   index), a node's unvisited neighbours are queued by (degree, index)
+ *   ascending, and the whole visit order is reversed.
+ *   perm (HOST int32[n], out): perm[i] = the original index at position i;
+ *   the permuted matrix is W'[i][j] = W[perm[i]][perm[j]].
+ *   HSS_ERR_INVALID_ARG: n < 1, null arrays, row_ptr[0] != 0, decreasing
+ *   row_ptr, a column outside [0, n).
+ */
+hss_status hss_rcm_order(int32_t n, const int32_t* row_ptr, const int32_t* col_idx, int32_t* perm);
+
+/* hss_concentration: rho of W (m x n, dtype, device) in the order perm
+ *   (device int32[n], a permutation of [0, n); m == n; NULL = identity):
+ *     out[0] = rho = out[1] / out[2] (0 if out[2] == 0),
+ *     out[1] = sum of |W'[i][j]| over the diagonal blocks (i < m/2 and
+ *              j < n/2, or i >= m/2 and j >= n/2),
+ *     out[2] = sum of |W|,
+ *   out = 3 device doubles, W' = W with rows and columns in the order perm.
+ *   Sums in fp64 in a fixed order (the same bits every call).
+ *   ws: at least hss_concentration_workspace_size() bytes (no state kept).
+ *   HSS_ERR_INVALID_ARG: bad dtype or size, null W or out, perm with m != n;
+ *   HSS_ERR_WORKSPACE; HSS_ERR_HIP. */
+hss_status hss_concentration_workspace_size(int32_t m, int32_t n, size_t* bytes);
+hss_status hss_concentration(hss_dtype dt, int32_t m, int32_t n, const void* W, const int32_t* perm, double* out,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* hss_hier_pack: flat factors of the 2 x 2 block low-rank term, for the
+ *   ordinary apply.  Block b = (bi, bj), in the order 00, 01, 10, 11, is
+ *   U[b] (device, (rows of half bi) x r[b], row-major) times Vt[b] (device,
+ *   r[b] x (columns of half bj), row-major) on the matrix permuted by perm
+ *   (device int32[n], a permutation; m == n; NULL = identity).  Writes
+ *     U_cat  (device, m x R, row-major) and Vt_cat (device, R x n), R = sum r[b],
+ *   such that U_cat Vt_cat is the block term in the ORIGINAL order:
+ *     U_cat[perm[i]][o_b + l] = U[b][i'][l] for the two blocks of i's row
+ *     half (i' = i, or i - m/2), Vt_cat[o_b + l][perm[j]] = Vt[b][l][j'] for
+ *     the columns j of block b's column half, zero elsewhere (o_b = r[0] +
+ *     ... + r[b-1]).  A matrix with U = U_cat, Vt = Vt_cat and r = R then
+ *     applies S + (block term) with hss_apply; the zeros double the factor
+ *     bytes the blocks themselves hold.
+ *   r, U, Vt: HOST arrays of 4 (the U and Vt entries are device pointers).
+ *   A permutation entry outside [0, n) is skipped.
+ *   HSS_ERR_INVALID_ARG: bad dtype, m or n < 2, r[b] < 0 or larger than its
+ *   block's smaller side, null arrays, perm with m != n, m*R or R*n >= 2^31;
+ *   HSS_ERR_HIP. */
+hss_status hss_hier_pack(hss_dtype dt, int32_t m, int32_t n, const int32_t* r, const void* const* U,
+                         const void* const* Vt, const int32_t* perm, void* U_cat, void* Vt_cat, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,6 +25,7 @@ __all__ = [
     "hss_version", "hss_topk_count", "hss_split_workspace_size", "hss_split", "hss_get_error",
     "hss_apply_workspace_size", "hss_apply", "hss_apply_group_workspace_size", "hss_apply_group",
     "hss_csr_cols_to_u16", "HSS_COL16", "HSS_DQ4",
+    "hss_rcm_order", "hss_concentration", "hss_hier_pack",
     "HSSMatrix", "SplitResult", "HSSError",
     "LIB_PATH", "status_string",
 ]
@@ -270,3 +271,65 @@ def hss_csr_cols_to_u16(col_idx: torch.Tensor, n: int) -> torch.Tensor:
     check(lib.hss_csr_cols_to_u16(_ptr(col_idx), col_idx.numel(), int(n), _ptr(out), _stream(dev)),
           "hss_csr_cols_to_u16")
     return out
+
+
+# ---------------------------------------------------------------------------
+# Hierarchical variant
+# ---------------------------------------------------------------------------
+
+def hss_rcm_order(row_ptr, col_idx, n: int):
+    """Reverse Cuthill-McKee order of a square CSR pattern (host arrays, or
+    tensors copied to the host): numpy int32 perm, perm[i] = original index
+    at position i."""
+    import numpy as np
+    rp = np.ascontiguousarray(row_ptr.cpu().numpy() if isinstance(row_ptr, torch.Tensor) else row_ptr, dtype=np.int32)
+    ci = np.ascontiguousarray(col_idx.cpu().numpy() if isinstance(col_idx, torch.Tensor) else col_idx, dtype=np.int32)
+    perm = np.zeros(int(n), dtype=np.int32)
+    check(lib.hss_rcm_order(int(n), rp.ctypes.data, ci.ctypes.data if ci.size else None, perm.ctypes.data),
+          "hss_rcm_order")
+    return perm
+
+
+def hss_concentration(W: torch.Tensor, perm: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Device float64 tensor [rho, diagonal-block |W| sum, total |W| sum] of W
+    (rows and columns in the order perm, a device int32 permutation)."""
+    dev = _dev(W)
+    if W.dim() != 2 or not W.is_contiguous() or W.dtype not in _DT:
+        raise ValueError("W must be a contiguous 2-D fp32 or bf16 tensor")
+    m, n = W.shape
+    size = ctypes.c_size_t(0)
+    check(lib.hss_concentration_workspace_size(m, n, ctypes.byref(size)), "hss_concentration_workspace_size")
+    ws = torch.empty(size.value, dtype=torch.uint8, device=dev)
+    out = torch.empty(3, dtype=torch.float64, device=dev)
+    if perm is not None and (perm.dtype != torch.int32 or perm.numel() != n or not perm.is_contiguous()):
+        raise ValueError("perm must be a contiguous int32 tensor of n entries")
+    check(lib.hss_concentration(_DT[W.dtype], m, n, _ptr(W), _ptr(perm), _ptr(out), _ptr(ws), ws.numel(),
+                                _stream(dev)), "hss_concentration")
+    return out
+
+
+def hss_hier_pack(U, Vt, m: int, n: int, perm: Optional[torch.Tensor] = None):
+    """Flat factors (U_cat m x R, Vt_cat R x n) of the 2 x 2 block low-rank
+    term with blocks U[b] Vt[b], b in the order 00, 01, 10, 11, on the matrix
+    permuted by perm (device int32 or None)."""
+    dtype = next(u.dtype for u in U if u is not None)
+    dev = next(u.device for u in U if u is not None)
+    r = [0 if u is None else int(u.shape[1]) for u in U]
+    R = sum(r)
+    Ucat = torch.empty((m, R), dtype=dtype, device=dev)
+    Vtcat = torch.empty((R, n), dtype=dtype, device=dev)
+    rows, cols = (m // 2, m - m // 2), (n // 2, n - n // 2)
+    for b, (u, v) in enumerate(zip(U, Vt)):
+        if u is None:
+            continue
+        if not u.is_contiguous() or not v.is_contiguous() or u.dtype != dtype or v.dtype != dtype:
+            raise ValueError("blocks must be contiguous tensors of one dtype")
+        if tuple(u.shape) != (rows[b >> 1], r[b]) or tuple(v.shape) != (r[b], cols[b & 1]):
+            raise ValueError(f"block {b}: U {tuple(u.shape)} / Vt {tuple(v.shape)} do not fit a {m} x {n} matrix")
+    r_arr = (ctypes.c_int32 * 4)(*r)
+    u_arr = (ctypes.c_void_p * 4)(*[_ptr(u) for u in U])
+    v_arr = (ctypes.c_void_p * 4)(*[_ptr(v) for v in Vt])
+    check(lib.hss_hier_pack(_DT[dtype], int(m), int(n), r_arr, u_arr, v_arr, _ptr(perm), _ptr(Ucat), _ptr(Vtcat),
+                            _stream(dev)), "hss_hier_pack")
+    return Ucat, Vtcat
+

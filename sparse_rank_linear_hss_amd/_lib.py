@@ -68,6 +68,12 @@ def _load():
                                                           P(c_size_t)]),
         "hss_apply_group": (ctypes.c_int, [P(P(HssMatrixStruct)), c_int32, c_int32, c_void_p, P(c_void_p),
                                            c_void_p, c_size_t, c_void_p]),
+        "hss_rcm_order": (ctypes.c_int, [c_int32, c_void_p, c_void_p, c_void_p]),
+        "hss_concentration_workspace_size": (ctypes.c_int, [c_int32, c_int32, P(c_size_t)]),
+        "hss_concentration": (ctypes.c_int, [ctypes.c_int, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
+                                             c_void_p, c_size_t, c_void_p]),
+        "hss_hier_pack": (ctypes.c_int, [ctypes.c_int, c_int32, c_int32, P(c_int32), P(c_void_p), P(c_void_p),
+                                         c_void_p, c_void_p, c_void_p, c_void_p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

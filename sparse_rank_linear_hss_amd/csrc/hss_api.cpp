@@ -176,3 +176,49 @@ hss_status hss_apply_group(const hss_matrix* const* A, int32_t G, int32_t b, con
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Hierarchical variant
+// ---------------------------------------------------------------------------
+hss_status hss_rcm_order(int32_t n, const int32_t* row_ptr, const int32_t* col_idx, int32_t* perm) {
+  if (n < 1 || !row_ptr || !perm || row_ptr[0] != 0) return HSS_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < n; ++i)
+    if (row_ptr[i + 1] < row_ptr[i]) return HSS_ERR_INVALID_ARG;
+  const int64_t nnz = row_ptr[n];
+  if (nnz > 0 && !col_idx) return HSS_ERR_INVALID_ARG;
+  for (int64_t p = 0; p < nnz; ++p)
+    if (col_idx[p] < 0 || col_idx[p] >= n) return HSS_ERR_INVALID_ARG;
+  return hss::rcm_order_host(n, row_ptr, col_idx, perm);
+}
+
+hss_status hss_concentration_workspace_size(int32_t m, int32_t n, size_t* bytes) {
+  if (!bytes || m < 1 || n < 1 || (int64_t)m * n >= kLimit) return HSS_ERR_INVALID_ARG;
+  *bytes = hss::concentration_ws_bytes(n);
+  return HSS_OK;
+}
+
+hss_status hss_concentration(hss_dtype dt, int32_t m, int32_t n, const void* W, const int32_t* perm, double* out,
+                             void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!valid_dtype(dt) || m < 1 || n < 1 || (int64_t)m * n >= kLimit || !W || !out) return HSS_ERR_INVALID_ARG;
+  if (perm && m != n) return HSS_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < hss::concentration_ws_bytes(n)) return HSS_ERR_WORKSPACE;
+  return hss::launch_concentration(dt, m, n, W, perm, out, ws, stream);
+}
+
+hss_status hss_hier_pack(hss_dtype dt, int32_t m, int32_t n, const int32_t* r, const void* const* U,
+                         const void* const* Vt, const int32_t* perm, void* U_cat, void* Vt_cat, hipStream_t stream) {
+  if (!valid_dtype(dt) || m < 2 || n < 2 || !r || !U || !Vt) return HSS_ERR_INVALID_ARG;
+  if (perm && m != n) return HSS_ERR_INVALID_ARG;
+  const int32_t rows[2] = {m / 2, m - m / 2}, cols[2] = {n / 2, n - n / 2};
+  int64_t R = 0;
+  for (int b = 0; b < 4; ++b) {
+    const int32_t lim = std::min(rows[b >> 1], cols[b & 1]);
+    if (r[b] < 0 || r[b] > lim) return HSS_ERR_INVALID_ARG;
+    if (r[b] > 0 && (!U[b] || !Vt[b])) return HSS_ERR_INVALID_ARG;
+    R += r[b];
+  }
+  if (R > 0 && (!U_cat || !Vt_cat)) return HSS_ERR_INVALID_ARG;
+  if ((int64_t)m * R >= kLimit || R * (int64_t)n >= kLimit) return HSS_ERR_INVALID_ARG;
+  return hss::launch_hier_pack(dt, m, n, r, U, Vt, perm, U_cat, Vt_cat, stream);
+}
+

@@ -118,4 +118,10 @@ size_t apply_group_ws_bytes(const hss_matrix* const* A, int G, int b);
 hss_status launch_cols_to_u16(const int32_t* col_idx, int64_t nnz, uint16_t* out, hipStream_t stream);
 hss_status launch_apply_group(const hss_matrix* const* A, int G, int b, const void* X, void* const* Y, void* ws,
                               hipStream_t stream);
+hss_status rcm_order_host(int n, const int32_t* row_ptr, const int32_t* col_idx, int32_t* perm);
+size_t concentration_ws_bytes(int n);
+hss_status launch_concentration(int dt, int m, int n, const void* W, const int32_t* perm, double* out, void* ws,
+                                hipStream_t s);
+hss_status launch_hier_pack(int dt, int m, int n, const int32_t* r, const void* const* U, const void* const* Vt,
+                            const int32_t* perm, void* Ucat, void* Vtcat, hipStream_t s);
 }  // namespace hss

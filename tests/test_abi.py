@@ -27,7 +27,8 @@ def test_header_declares_the_boundary():
     names = _declared()
     for must in ("hss_split", "hss_apply", "hss_split_workspace_size", "hss_apply_workspace_size",
                  "hss_apply_group", "hss_apply_group_workspace_size",
-                 "hss_get_error", "hss_topk_count", "hss_status_string", "hss_version"):
+                 "hss_get_error", "hss_topk_count", "hss_status_string", "hss_version",
+                 "hss_rcm_order", "hss_concentration", "hss_concentration_workspace_size", "hss_hier_pack"):
         assert must in names
 
 
@@ -179,3 +180,36 @@ def test_apply_group_rejects_bad_arguments(hl):
     assert lib.hss_apply_group_workspace_size(arr, 2, 1, ctypes.byref(sz2)) == 0
     assert lib.hss_apply_workspace_size(ctypes.byref(a), 1, ctypes.byref(sz1)) == 0
     assert sz2.value >= sz1.value
+
+
+def test_hierarchical_entry_points_reject_bad_arguments(hl):
+    INV, WS = hl._lib.HSS_ERR_INVALID_ARG, hl._lib.HSS_ERR_WORKSPACE
+    lib = hl._lib.lib
+    sz = ctypes.c_size_t(0)
+    assert lib.hss_concentration_workspace_size(16, 24, ctypes.byref(sz)) == 0 and sz.value >= 4 * 24
+    assert lib.hss_concentration_workspace_size(0, 24, ctypes.byref(sz)) == INV
+    big = 1 << 22
+
+    def conc(dt=1, m=16, n=16, W=FAKE, perm=None, out=FAKE * 2, ws=FAKE * 3, wsb=big):
+        return lib.hss_concentration(dt, m, n, W, perm, out, ws, wsb, None)
+    assert conc(dt=7) == INV
+    assert conc(m=0) == INV
+    assert conc(W=None) == INV
+    assert conc(out=None) == INV
+    assert conc(n=24, perm=FAKE * 4) == INV                    # a permutation needs a square matrix
+    assert conc(ws=None) == WS
+    assert conc(wsb=64) == WS
+
+    def pack(dt=1, m=16, n=16, r=(2, 1, 1, 2), U=(FAKE,) * 4, Vt=(FAKE,) * 4, perm=None, Uc=FAKE * 5, Vc=FAKE * 6):
+        ra = (ctypes.c_int32 * 4)(*r)
+        ua = (ctypes.c_void_p * 4)(*U)
+        va = (ctypes.c_void_p * 4)(*Vt)
+        return lib.hss_hier_pack(dt, m, n, ra, ua, va, perm, Uc, Vc, None)
+    assert pack(dt=5) == INV
+    assert pack(m=1) == INV
+    assert pack(r=(9, 0, 0, 0)) == INV                         # rank above the block's smaller side
+    assert pack(r=(-1, 0, 0, 0)) == INV
+    assert pack(U=(None, FAKE, FAKE, FAKE)) == INV             # block 0 has rank 2 but no factor
+    assert pack(Uc=None) == INV
+    assert pack(n=20, perm=FAKE) == INV
+    assert pack(r=(0, 0, 0, 0), U=(None,) * 4, Vt=(None,) * 4, Uc=None, Vc=None) == 0   # nothing to pack
