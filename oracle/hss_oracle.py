@@ -67,6 +67,11 @@ Readings where the pages are silent (each is listed in the design notes):
   permutation); each block of the permuted residual gets its own truncated
   SVD.
 
+* Backward: the pages give dS, dU and dV; the input gradient dX = G A is
+  added, since a layer's backward pass needs it.  dS is restricted to S's
+  stored positions (its pattern is fixed).  S^T's CSR orders each row's
+  entries by original row.
+
 Storage conventions (the same ones the C library documents):
   fp32 values are numpy.float32; bf16 values are their bit patterns in
   numpy.uint16.  Matrices are row-major.  W is m x n (out x in), X is b x n,
@@ -568,3 +573,49 @@ def hier_apply(S64, blocks, perm, X64):
     Y[:, q] += Yp
     return Y
 
+
+
+# ---------------------------------------------------------------------------
+# Backward pass ([HSS] section "実装と運用パターン", the backward formulas: the
+# gradients of S, U and V are computed separately, S's restricted to its
+# stored positions).  With Y = X A^T, A = S + U V^T and G = dL/dY (b x m):
+#   dA = G^T X (m x n), dS = dA on S's support, dU = dA V, dV = dA^T U,
+# and the input gradient dX = G A (the layer's backward needs it too; the
+# pages' formulas are written in the in x out orientation, these are the
+# same quantities in this module's out x in one).
+# ---------------------------------------------------------------------------
+
+def csr_row_of_entry(m, row_ptr):
+    """Row index of every stored entry, in storage order."""
+    return np.repeat(np.arange(m, dtype=np.int64), np.diff(np.asarray(row_ptr, dtype=np.int64)))
+
+
+def csr_transpose(m, n, row_ptr, col_idx):
+    """S^T's CSR pattern (n rows) and perm with values_t = values[perm]:
+    the stored entries ordered by (column, row)."""
+    rows = csr_row_of_entry(m, row_ptr)
+    cols = np.asarray(col_idx, dtype=np.int64)
+    perm = np.lexsort((rows, cols))
+    row_ptr_t = np.zeros(n + 1, dtype=np.int64)
+    np.add.at(row_ptr_t, cols + 1, 1)
+    return np.cumsum(row_ptr_t).astype(np.int32), rows[perm].astype(np.int32), perm.astype(np.int64)
+
+
+def backward(m, n, row_ptr, col_idx, S64, U64, V64, X64, G64):
+    """fp64 gradients of L with dL/dY = G: dX (b x n), dS (values, storage
+    order), dU (m x r), dV (n x r)."""
+    dA = G64.T @ X64
+    rows = csr_row_of_entry(m, row_ptr)
+    dS = dA[rows, np.asarray(col_idx, dtype=np.int64)]
+    return {"dX": G64 @ (S64 + U64 @ V64.T), "dS": dS, "dU": dA @ V64, "dV": dA.T @ U64}
+
+
+def backward_normalisers(m, n, row_ptr, col_idx, S64, U64, V64, X64, G64):
+    """Per-output scales of the gradients' error bounds (the same sums with
+    every term's magnitude): dS_p ~ sum_c |G_ci X_cj|, dU ~ |G|^T |X| |V|,
+    dV ~ |X|^T |G| |U|, dX ~ |G| |S + U V^T|."""
+    aG, aX = np.abs(G64), np.abs(X64)
+    rows = csr_row_of_entry(m, row_ptr)
+    NS = (aG.T @ aX)[rows, np.asarray(col_idx, dtype=np.int64)]
+    return {"dX": aG @ np.abs(S64 + U64 @ V64.T), "dS": NS, "dU": aG.T @ (aX @ np.abs(V64)),
+            "dV": aX.T @ (aG @ np.abs(U64))}

@@ -28,6 +28,41 @@ def _fails(*tests):
     return False
 
 
+_orig_backward = H.backward
+_orig_csr_transpose = H.csr_transpose
+
+
+def _backward_dU_uses_U(m, n, rp, ci, S, U, V, X, G):
+    g = _orig_backward(m, n, rp, ci, S, U, V, X, G)
+    g["dU"] = (G.T @ X) @ np.resize(U, V.shape)                 # U where V belongs
+    return g
+
+
+def _backward_dX_no_lowrank(m, n, rp, ci, S, U, V, X, G):
+    g = _orig_backward(m, n, rp, ci, S, U, V, X, G)
+    g["dX"] = G @ S
+    return g
+
+
+def _backward_sign_flipped(m, n, rp, ci, S, U, V, X, G):
+    g = _orig_backward(m, n, rp, ci, S, U, V, X, G)
+    g["dV"] = -g["dV"]
+    return g
+
+
+def _backward_dS_transposed_index(m, n, rp, ci, S, U, V, X, G):
+    g = _orig_backward(m, n, rp, ci, S, U, V, X, G)
+    dA = G.T @ X
+    rows = H.csr_row_of_entry(m, rp)
+    g["dS"] = dA[np.asarray(ci) % m, rows % n]                  # row and column swapped
+    return g
+
+
+def _csr_transpose_row_major_order(m, n, rp, ci):
+    rpt, cit, perm = _orig_csr_transpose(m, n, rp, ci)
+    return rpt, cit, np.arange(len(perm))                          # storage order kept
+
+
 def _apply_no_lowrank(S, U, V, X):
     return X @ S.T
 
@@ -263,6 +298,11 @@ CASES = [
     ("concentration_ratio", _rho_off_diagonal, [P.test_concentration_ratio_closed_forms]),
     ("hier_factors", _hier_factors_split_shifted, [P.test_hier_full_rank_reproduces_residual_and_eckart_young]),
     ("hier_apply", _hier_apply_perm_inverted, [lambda: P.test_hier_apply_equals_dense(True)]),
+    ("backward", _backward_dU_uses_U, [lambda: P.test_backward_matches_exact_finite_differences(0)]),
+    ("backward", _backward_dX_no_lowrank, [lambda: P.test_backward_matches_exact_finite_differences(0)]),
+    ("backward", _backward_sign_flipped, [lambda: P.test_backward_matches_exact_finite_differences(0)]),
+    ("backward", _backward_dS_transposed_index, [P.test_backward_one_hot_upstream_and_full_support_brute_force]),
+    ("csr_transpose", _csr_transpose_row_major_order, [P.test_csr_transpose_is_the_transposed_matrix]),
 ]
 
 

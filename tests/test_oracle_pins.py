@@ -581,3 +581,111 @@ def test_hier_apply_equals_dense(permuted):
     # with full ranks the permuted low-rank term is R itself, back in the original order
     fullb = O.hier_factors(Rp, 6, 6)
     assert np.max(np.abs(O.hier_lowrank_dense(fullb, perm, m, n) - R)) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# Backward: gradients of S (on its support), U, V and the input
+# ---------------------------------------------------------------------------
+
+def _bw_case(m=7, n=9, r=3, b=4, density=0.3, seed=0):
+    rng = np.random.default_rng(seed)
+    mask = rng.random((m, n)) < density
+    S = np.where(mask, rng.standard_normal((m, n)), 0.0)
+    rows, cols = np.nonzero(mask)
+    row_ptr = np.concatenate([[0], np.cumsum(np.bincount(rows, minlength=m))]).astype(np.int32)
+    return (row_ptr, cols.astype(np.int32), S, rng.standard_normal((m, r)), rng.standard_normal((n, r)),
+            rng.standard_normal((b, n)), rng.standard_normal((b, m)))
+
+
+def _loss(G, S, U, V, X):
+    return float(np.sum(G * O.apply_factored(S, U, V, X)))
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_backward_matches_exact_finite_differences(seed):
+    """L = sum(G * Y) is linear in each of S's stored values, U, V and X, so
+    L(theta + E) - L(theta) = <grad, E> exactly (up to rounding), with L
+    evaluated through the forward apply."""
+    m, n = 7, 9
+    rp, ci, S, U, V, X, G = _bw_case(m, n, seed=seed)
+    g = O.backward(m, n, rp, ci, S, U, V, X, G)
+    rng = np.random.default_rng(100 + seed)
+    L0 = _loss(G, S, U, V, X)
+    rows = O.csr_row_of_entry(m, rp)
+    Es = rng.standard_normal(len(ci))
+    S2 = S.copy()
+    S2[rows, ci] += Es
+    for delta, expect in (
+        (_loss(G, S2, U, V, X) - L0, g["dS"] @ Es),
+        (_loss(G, S, U + (EU := rng.standard_normal(U.shape)), V, X) - L0, np.sum(g["dU"] * EU)),
+        (_loss(G, S, U, V + (EV := rng.standard_normal(V.shape)), X) - L0, np.sum(g["dV"] * EV)),
+        (_loss(G, S, U, V, X + (EX := rng.standard_normal(X.shape))) - L0, np.sum(g["dX"] * EX)),
+    ):
+        assert abs(delta - expect) <= 1e-9 * (1 + abs(expect))
+
+
+def test_backward_euler_identities():
+    """Each part of L is homogeneous of degree 1 in each parameter: <dS, s> is
+    the sparse part of L, <dU, U> = <dV, V> its low-rank part, <dX, X> all of it."""
+    m, n = 6, 11
+    rp, ci, S, U, V, X, G = _bw_case(m, n, r=4, b=5, seed=3)
+    g = O.backward(m, n, rp, ci, S, U, V, X, G)
+    Ls = float(np.sum(G * (X @ S.T)))
+    Ll = float(np.sum(G * ((X @ V) @ U.T)))
+    vals = S[O.csr_row_of_entry(m, rp), ci]
+    assert np.isclose(g["dS"] @ vals, Ls, rtol=1e-12, atol=1e-12)
+    assert np.isclose(np.sum(g["dU"] * U), Ll, rtol=1e-12, atol=1e-12)
+    assert np.isclose(np.sum(g["dV"] * V), Ll, rtol=1e-12, atol=1e-12)
+    assert np.isclose(np.sum(g["dX"] * X), Ls + Ll, rtol=1e-12, atol=1e-12)
+
+
+def test_backward_one_hot_upstream_and_full_support_brute_force():
+    """G = one entry (c, i): dX is row i of A in batch row c only, dU is X_c V in
+    row i only, dV is X_c^T U_i.  With every position stored, dS is the
+    brute-force double loop sum_c G_ci X_cj."""
+    m, n, b = 5, 4, 3
+    rp, ci, S, U, V, X, _ = _bw_case(m, n, b=b, density=1.1, seed=4)   # every position stored
+    G = np.zeros((b, m))
+    G[1, 3] = 1.0
+    g = O.backward(m, n, rp, ci, S, U, V, X, G)
+    A = S + U @ V.T
+    expect_dX = np.zeros((b, n))
+    expect_dX[1] = A[3]
+    assert np.allclose(g["dX"], expect_dX, rtol=0, atol=1e-14)
+    expect_dU = np.zeros_like(U)
+    expect_dU[3] = X[1] @ V
+    assert np.allclose(g["dU"], expect_dU, rtol=0, atol=1e-14)
+    assert np.allclose(g["dV"], np.outer(X[1], U[3]), rtol=0, atol=1e-14)
+    G = np.random.default_rng(5).standard_normal((b, m))
+    g = O.backward(m, n, rp, ci, S, U, V, X, G)
+    brute = [sum(G[c, i] * X[c, j] for c in range(b)) for i in range(m) for j in range(n)]
+    assert np.allclose(g["dS"], brute, rtol=1e-13, atol=1e-13)
+
+
+def test_backward_normalisers_bound_the_gradients():
+    m, n = 8, 6
+    rp, ci, S, U, V, X, G = _bw_case(m, n, seed=6)
+    g = O.backward(m, n, rp, ci, S, U, V, X, G)
+    N = O.backward_normalisers(m, n, rp, ci, S, U, V, X, G)
+    for k in g:
+        assert np.all(np.abs(g[k]) <= N[k] * (1 + 1e-12) + 1e-15), k
+    # with nonnegative inputs there is no cancellation: the bound is attained
+    p = [np.abs(a) for a in (S, U, V, X, G)]
+    g = O.backward(m, n, rp, ci, *p)
+    N = O.backward_normalisers(m, n, rp, ci, *p)
+    for k in g:
+        assert np.allclose(g[k], N[k], rtol=1e-12), k
+
+
+def test_csr_transpose_is_the_transposed_matrix():
+    m, n = 9, 7
+    rp, ci, S, *_ = _bw_case(m, n, density=0.4, seed=7)
+    vals = S[O.csr_row_of_entry(m, rp), ci]
+    rpt, cit, perm = O.csr_transpose(m, n, rp, ci)
+    St = np.zeros((n, m))
+    for j in range(n):
+        seg = slice(rpt[j], rpt[j + 1])
+        assert np.all(np.diff(cit[seg]) > 0)                         # original rows ascending
+        St[j, cit[seg]] = vals[perm][seg]
+    assert np.array_equal(St, S.T)
+    assert sorted(perm.tolist()) == list(range(len(ci)))
