@@ -17,7 +17,9 @@ launch-bound; the kernels keep their cross-call state on the device, so
 replays are exact); the plain stream-launch rate is reported beside it.
 
 Also measured in the same run (extra JSON keys): the same layer with 16-bit
-column indices and at batch 16, its hierarchical form (Reverse
+column indices and at batch 16, its batched routes side by side (fused decode
+passes, gather SpMM, densified S on the matrix cores; b = 8 .. 256), its
+hierarchical form (Reverse
 Cuthill-McKee order of S's support, concentration ratio, 2 x 2 block
 factors of ranks 96 / 32 packed to rank 256) at batch 1, its dense-and-sparse form (0.5 % outliers in
 CSR plus a 4-bit quantised dense part, stand-in codes and levels) at batch 1
@@ -271,11 +273,26 @@ def main():
                                      "gbs": bytes16 / (ms16c * 1e-3) / 1e9, "bytes_per_apply": bytes16}
         del L16
 
-        # same layer, batch 16
+        # same layer, batch 16 (the default route: gather SpMM)
         xs16, ys16 = _acts(cfg, 16, 0, 4, m)
         ms16 = _time_graph(_apply_loop(H, L, xs16, ys16, ws), max(1, steps // 4), 20)
         extra["csr4096_b16"] = {"ms": ms16, "tokens_per_s": 16 / (ms16 * 1e-3),
                                 "gbs": bytes_head / (ms16 * 1e-3) / 1e9}
+        # batched CSR routes side by side (HSS_CSR_BATCH_ROUTE forces one):
+        # fused decode passes, gather SpMM, S densified for the matrix cores
+        routes = {}
+        for bq in (8, 16, 64, 128, 256):
+            wsq = L.mats[0].workspace(bq)
+            xq, yq = _acts(cfg, bq, 0, 4, m)
+            row = {}
+            for route in ("decode", "spmm", "densify"):
+                if (route == "decode" and bq > 64) or (route == "densify" and bq < 24):
+                    continue
+                os.environ["HSS_CSR_BATCH_ROUTE"] = route
+                row[route] = _time_graph(_apply_loop(H, L, xq, yq, wsq), max(1, steps // 10), 10) * 1e3
+            os.environ.pop("HSS_CSR_BATCH_ROUTE")
+            routes[f"b{bq}_us"] = row
+        extra["csr4096_batch_routes"] = routes
 
         # hierarchical form: RCM order of S's support (host), concentration
         # ratio before / after it, 2 x 2 block factors (seeded stand-ins,

@@ -47,7 +47,7 @@ extern "C" {
 #endif
 
 #define HSS_VERSION_MAJOR 1
-#define HSS_VERSION_MINOR 3
+#define HSS_VERSION_MINOR 4
 
 typedef enum {
   HSS_OK = 0,
@@ -198,12 +198,17 @@ hss_status hss_apply_workspace_size(const hss_matrix* A, int32_t b, size_t* byte
  *     counter), so the caller must not write to it afterwards; any number of
  *     calls, with any matrices and batch sizes, may then share it as long as
  *     they are ordered (same stream or events).
- * Execution: bf16 with b >= 16 (2:4) or b >= 24 (CSR) runs on the matrix
- * cores (T^T = X V and Y =
- * [X | T^T] [S | U]^T as MFMA GEMMs with fp32 accumulation; T is rounded to
- * bf16 once, between the two; a CSR S is first expanded into a dense bf16
- * copy inside the workspace, so the workspace then holds m*n*2 more bytes);
- * otherwise one fused kernel per 8 columns.  HSS_DQ4 matrices always run the
+ * Execution: bf16 2:4 with b >= 16, and bf16 CSR with b > 128, run on the
+ * matrix cores (T^T = X V and Y = [X | T^T] [S | U]^T as MFMA GEMMs with
+ * fp32 accumulation; T is rounded to bf16 once, between the two; a CSR S is
+ * first expanded into a dense bf16 copy inside the workspace, so the
+ * workspace then holds m*n*2 more bytes).  bf16 CSR with 8 <= b <= 128 runs
+ * the gather SpMM (T = X V rounded to bf16 once, X^T staged in the
+ * workspace, then every stored entry gathers its X^T row; fp32
+ * accumulation).  Otherwise one fused kernel per 8 columns.  The
+ * environment variable HSS_CSR_BATCH_ROUTE = decode | spmm | densify forces
+ * a bf16 CSR call onto that route where the route supports the matrix (for
+ * comparing them); the workspace size covers every route.  HSS_DQ4 matrices always run the
  * fused dense-and-sparse kernel (up to 8 columns per pass; no workspace:
  * hss_apply_workspace_size returns 0 and ws may be NULL).
  * Returns HSS_ERR_INVALID_ARG for: A or X or Y null, unknown fmt/dtype,
@@ -300,6 +305,60 @@ hss_status hss_concentration(hss_dtype dt, int32_t m, int32_t n, const void* W, 
  *   HSS_ERR_HIP. */
 hss_status hss_hier_pack(hss_dtype dt, int32_t m, int32_t n, const int32_t* r, const void* const* U,
                          const void* const* Vt, const int32_t* perm, void* U_cat, void* Vt_cat, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Backward pass ([HSS] section "実装と運用パターン", the backward formulas):
+ * the gradients of S, U and V are computed separately, S's restricted to
+ * its stored positions.  With Y = X A^T, A = S + U V^T and G = dL/dY
+ * (b x m): dA = G^T X, dS = dA on S's support, dU = dA V, dV = dA^T U.
+ * The input gradient dX = G A is the forward apply of the transposed layer
+ * A^T = S^T + V U^T, built with hss_csr_transpose, hss_gather_values and
+ * hss_transpose and applied with hss_apply.
+ * ------------------------------------------------------------------------
+ *
+ * hss_grad: parameter gradients of a bf16 CSR layer (device arrays):
+ *   X (b x n) and G (b x m) bf16, row-major;
+ *   dS  (fp32[nnz], out; NULL = skip): dS[p] = sum_c G[c][i] X[c][col_idx[p]]
+ *        for the stored entry p in row i, in S's storage order;
+ *   dU  (fp32, m x r row-major, out; NULL = skip) = G^T (X V);
+ *   dVt (fp32, r x n row-major, out; NULL = skip) = (G U)^T X, the gradient
+ *        of the stored V^T.
+ *   X V and G U are rounded to bf16 once (matrix-core GEMMs with fp32
+ *   accumulation); every sum over the batch accumulates in fp32.  The same
+ *   inputs give the same bits on every call.
+ *   ws: at least hss_grad_workspace_size() bytes (no state kept).
+ *   HSS_ERR_UNSUPPORTED: a 2:4, fp32 or dense-and-sparse layer, or
+ *   n * round8(b) * 2 or m * round8(b) * 2 >= 2^31.  HSS_ERR_INVALID_ARG: as
+ *   hss_apply, plus null X or G, or an output overlapping X, G or another
+ *   output.  HSS_ERR_WORKSPACE; HSS_ERR_HIP. */
+hss_status hss_grad_workspace_size(const hss_matrix* A, int32_t b, size_t* bytes);
+hss_status hss_grad(const hss_matrix* A, int32_t b, const void* X, const void* G, float* dS, float* dU, float* dVt,
+                    void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* hss_csr_transpose: the CSR pattern of S^T (n x m) from S's (m x n), in
+ *   HOST memory, computed on the host, synchronously (once per pattern):
+ *   row_ptr_t (int32[n+1]) and col_idx_t (int32[nnz]) with each row's
+ *   entries ordered by original row; perm (int32[nnz]): entry q of S^T is
+ *   entry perm[q] of S.
+ *   HSS_ERR_INVALID_ARG: m or n < 1, null arrays, row_ptr[0] != 0,
+ *   decreasing row_ptr, a column outside [0, n). */
+hss_status hss_csr_transpose(int32_t m, int32_t n, const int32_t* row_ptr, const int32_t* col_idx, int32_t* row_ptr_t,
+                             int32_t* col_idx_t, int32_t* perm);
+
+/* hss_gather_values: values_t[q] = values[perm[q]] for q < nnz (device
+ *   arrays, bits copied): S^T's values after each change of S's.
+ *   perm must hold indices in [0, nnz).
+ *   HSS_ERR_INVALID_ARG: bad dtype, nnz < 0 or >= 2^31, null arrays with
+ *   nnz > 0, values overlapping values_t.  HSS_ERR_HIP. */
+hss_status hss_gather_values(hss_dtype dt, int64_t nnz, const void* values, const int32_t* perm, void* values_t,
+                             hipStream_t stream);
+
+/* hss_transpose: dst (cols x rows, row-major) = src (rows x cols,
+ *   row-major)^T, device arrays, bits copied (U^T and V for the transposed
+ *   layer: its U is V = (stored V^T)^T, its V^T is U^T).
+ *   HSS_ERR_INVALID_ARG: bad dtype, rows or cols < 1, rows * cols >= 2^31,
+ *   rows > 2,097,120, null or overlapping arrays.  HSS_ERR_HIP. */
+hss_status hss_transpose(hss_dtype dt, int32_t rows, int32_t cols, const void* src, void* dst, hipStream_t stream);
 
 #ifdef __cplusplus
 }

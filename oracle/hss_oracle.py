@@ -619,3 +619,16 @@ def backward_normalisers(m, n, row_ptr, col_idx, S64, U64, V64, X64, G64):
     NS = (aG.T @ aX)[rows, np.asarray(col_idx, dtype=np.int64)]
     return {"dX": aG @ np.abs(S64 + U64 @ V64.T), "dS": NS, "dU": aG.T @ (aX @ np.abs(V64)),
             "dV": aX.T @ (aG @ np.abs(U64))}
+
+
+def backward_sampled(rows, cols, ent_rows, ent_cols, U64, V64, X64, G64):
+    """The same gradients on a sample, for full-size checks: dU's rows
+    `rows` (= G[:, rows]^T X V), dV's rows `cols` (= X[:, cols]^T G U) and dS
+    at the positions (ent_rows[e], ent_cols[e]) (= sum_c G[c, i] X[c, j]),
+    each with its error-bound scale (the same sums of magnitudes)."""
+    aG, aX = np.abs(G64), np.abs(X64)
+    XV, GU = X64 @ V64, G64 @ U64
+    dS = np.sum(G64[:, ent_rows] * X64[:, ent_cols], axis=0)
+    NS = np.sum(aG[:, ent_rows] * aX[:, ent_cols], axis=0)
+    return {"dU": G64[:, rows].T @ XV, "dV": X64[:, cols].T @ GU, "dS": dS,
+            "NU": aG[:, rows].T @ (aX @ np.abs(V64)), "NV": aX[:, cols].T @ (aG @ np.abs(U64)), "NS": NS}

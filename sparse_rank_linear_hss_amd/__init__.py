@@ -26,6 +26,7 @@ __all__ = [
     "hss_apply_workspace_size", "hss_apply", "hss_apply_group_workspace_size", "hss_apply_group",
     "hss_csr_cols_to_u16", "HSS_COL16", "HSS_DQ4",
     "hss_rcm_order", "hss_concentration", "hss_hier_pack",
+    "hss_grad", "hss_csr_transpose", "hss_gather_values", "hss_transpose", "hss_transposed_layer", "hss_backward",
     "HSSMatrix", "SplitResult", "HSSError",
     "LIB_PATH", "status_string",
 ]
@@ -333,3 +334,96 @@ def hss_hier_pack(U, Vt, m: int, n: int, perm: Optional[torch.Tensor] = None):
                             _stream(dev)), "hss_hier_pack")
     return Ucat, Vtcat
 
+
+
+# ---------------------------------------------------------------------------
+# Backward pass
+# ---------------------------------------------------------------------------
+
+def hss_grad(A: HSSMatrix, X: torch.Tensor, G: torch.Tensor, dS=True, dU=True, dVt=True,
+             ws: Optional[torch.Tensor] = None) -> dict:
+    """Parameter gradients of a bf16 CSR layer for the upstream gradient G
+    (b x m): fp32 dS (S's stored values, storage order), dU (m x r) and dVt
+    (r x n, the gradient of the stored V^T).  Pass False to skip one."""
+    dev = _dev(X)
+    if X.dim() != 2 or X.shape[1] != A.n or not X.is_contiguous() or X.dtype != A.dtype:
+        raise ValueError("X must be a contiguous b x n tensor of the matrix dtype")
+    b = X.shape[0]
+    if G.shape != (b, A.m) or not G.is_contiguous() or G.dtype != A.dtype:
+        raise ValueError("G must be a contiguous b x m tensor of the matrix dtype")
+    out = {}
+    if dS:
+        out["dS"] = torch.empty(A.nnz, dtype=torch.float32, device=dev)
+    if dU:
+        out["dU"] = torch.empty((A.m, A.r), dtype=torch.float32, device=dev)
+    if dVt:
+        out["dVt"] = torch.empty((A.r, A.n), dtype=torch.float32, device=dev)
+    if ws is None:
+        size = ctypes.c_size_t(0)
+        check(lib.hss_grad_workspace_size(ctypes.byref(A.struct), b, ctypes.byref(size)), "hss_grad_workspace_size")
+        ws = torch.empty(size.value, dtype=torch.uint8, device=dev)
+    check(lib.hss_grad(ctypes.byref(A.struct), b, _ptr(X), _ptr(G), _ptr(out.get("dS")), _ptr(out.get("dU")),
+                       _ptr(out.get("dVt")), _ptr(ws), ws.numel(), _stream(dev)), "hss_grad")
+    return out
+
+
+def hss_csr_transpose(row_ptr, col_idx, m: int, n: int):
+    """S^T's CSR pattern (host int32 row_ptr_t, col_idx_t) and perm (entry q of
+    S^T is entry perm[q] of S), computed on the host."""
+    import numpy as np
+    rp = np.ascontiguousarray(row_ptr.cpu().numpy() if isinstance(row_ptr, torch.Tensor) else row_ptr, dtype=np.int32)
+    ci = np.ascontiguousarray(col_idx.cpu().numpy() if isinstance(col_idx, torch.Tensor) else col_idx, dtype=np.int32)
+    nnz = int(rp[m])
+    rpt = np.zeros(int(n) + 1, dtype=np.int32)
+    cit = np.zeros(max(nnz, 1), dtype=np.int32)
+    perm = np.zeros(max(nnz, 1), dtype=np.int32)
+    check(lib.hss_csr_transpose(int(m), int(n), rp.ctypes.data, ci.ctypes.data if nnz else None, rpt.ctypes.data,
+                                cit.ctypes.data, perm.ctypes.data), "hss_csr_transpose")
+    return rpt, cit[:nnz], perm[:nnz]
+
+
+def hss_gather_values(values: torch.Tensor, perm: torch.Tensor) -> torch.Tensor:
+    """values[perm] on the device (bits copied)."""
+    out = torch.empty(perm.numel(), dtype=values.dtype, device=values.device)
+    check(lib.hss_gather_values(_DT[values.dtype], perm.numel(), _ptr(values), _ptr(perm), _ptr(out),
+                                _stream(values.device)), "hss_gather_values")
+    return out
+
+
+def hss_transpose(t: torch.Tensor) -> torch.Tensor:
+    """A contiguous 2-D fp32 / bf16 device tensor transposed by the library."""
+    rows, cols = t.shape
+    out = torch.empty((cols, rows), dtype=t.dtype, device=t.device)
+    check(lib.hss_transpose(_DT[t.dtype], rows, cols, _ptr(t), _ptr(out), _stream(t.device)), "hss_transpose")
+    return out
+
+
+def hss_transposed_layer(A: HSSMatrix) -> HSSMatrix:
+    """A^T = S^T + V U^T as an HSSMatrix (n x m): S^T's pattern from the host
+    transpose, its values gathered on the device, U' = V and V'^T = U^T from
+    the stored factors.  hss_apply(A^T, G) is the input gradient G A."""
+    if A.fmt != HSS_FMT_CSR or A.flags & HSS_DQ4:
+        raise ValueError("the transposed layer is built for CSR layers")
+    dev = A.row_ptr.device
+    cols = A.col_idx.to(torch.int32) if A.flags & HSS_COL16 else A.col_idx
+    if A.flags & HSS_COL16:
+        cols = cols & 0xFFFF
+    rpt, cit, perm = hss_csr_transpose(A.row_ptr, cols if A.nnz else torch.zeros(0, dtype=torch.int32), A.m, A.n)
+    perm_d = torch.from_numpy(perm).to(dev)
+    vals = hss_gather_values(A.values, perm_d) if A.nnz else None
+    U2 = hss_transpose(A.Vt) if A.r > 0 else None
+    Vt2 = hss_transpose(A.U) if A.r > 0 else None
+    At = HSSMatrix("csr", A.n, A.m, A.dtype, U=U2, Vt=Vt2, row_ptr=torch.from_numpy(rpt).to(dev),
+                   col_idx=torch.from_numpy(cit).to(dev) if A.nnz else None, values=vals, nnz=A.nnz)
+    At.perm_from_s = perm_d
+    return At
+
+
+def hss_backward(A: HSSMatrix, X: torch.Tensor, G: torch.Tensor, At: Optional[HSSMatrix] = None) -> dict:
+    """dX (b x n, the layer dtype) = G A through the transposed layer, and
+    the fp32 parameter gradients dS, dU, dVt of hss_grad."""
+    if At is None:
+        At = hss_transposed_layer(A)
+    out = hss_grad(A, X, G)
+    out["dX"] = hss_apply(At, G)
+    return out

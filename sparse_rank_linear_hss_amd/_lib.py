@@ -74,6 +74,12 @@ def _load():
                                              c_void_p, c_size_t, c_void_p]),
         "hss_hier_pack": (ctypes.c_int, [ctypes.c_int, c_int32, c_int32, P(c_int32), P(c_void_p), P(c_void_p),
                                          c_void_p, c_void_p, c_void_p, c_void_p]),
+        "hss_grad_workspace_size": (ctypes.c_int, [P(HssMatrixStruct), c_int32, P(c_size_t)]),
+        "hss_grad": (ctypes.c_int, [P(HssMatrixStruct), c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                    c_void_p, c_size_t, c_void_p]),
+        "hss_csr_transpose": (ctypes.c_int, [c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+        "hss_gather_values": (ctypes.c_int, [ctypes.c_int, c_int64, c_void_p, c_void_p, c_void_p, c_void_p]),
+        "hss_transpose": (ctypes.c_int, [ctypes.c_int, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

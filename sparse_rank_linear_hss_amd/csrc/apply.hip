@@ -8,12 +8,22 @@
 //   decode (decode.hip)  up to 8 columns per launch: one fused kernel that
 //                        streams S, U and V^T once (HBM-bound regime); fp32
 //                        and narrow batches.
-//   mfma (mfma.hip)      bf16 with b >= 16 (2:4) or b >= 24 (CSR): the
+//   mfma (mfma.hip)      bf16 with b >= 16 (2:4) or b > 128 (CSR): the
 //                        low-rank products are dense contractions and run on
 //                        the matrix cores, S expanded into the same GEMM.
 //   dense-and-sparse     HSS_DQ4 matrices (decode.hip, k_decode_dq): the
 //                        quantised dense part and the CSR outliers, up to 8
 //                        columns per pass, no workspace.
+//   gather SpMM          bf16 CSR from 8 to 128 columns (and beyond where S
+//   (spmm.hip)           cannot be densified): S read once, X^T rows
+//                        gathered per entry, T from a small prologue.
+//
+// The environment variable HSS_CSR_BATCH_ROUTE = decode | spmm | densify
+// forces the route of a bf16 CSR batch (where that route supports it), for
+// measuring one against another.
+#include <cstdlib>
+#include <cstring>
+
 #include "hss_internal.h"
 
 namespace hss {
@@ -34,14 +44,45 @@ bool mfma_supported(const hss_matrix* A, int b);
 size_t mfma_ws_bytes(const hss_matrix* A, int b);
 hss_status launch_mfma(const hss_matrix* A, int b, const void* X, void* Y, void* ws, hipStream_t s);
 
+bool spmm_supported(const hss_matrix* A, int b);
+size_t spmm_ws_bytes(const hss_matrix* A, int b);
+hss_status launch_spmm(const hss_matrix* A, int b, const void* X, void* Y, void* ws, hipStream_t s);
+
+enum Route { R_DECODE = 0, R_SPMM = 1, R_MFMA = 2 };
+
+// Default batch range of the gather SpMM for bf16 CSR: below it the fused
+// decode passes, above it S densified for the matrix cores.  Measured on the
+// 4096 x 4096 5 % rank-256 layer (decode / densify vs gather): b = 4 decode
+// 12.9 vs 19.7 us; b = 8 decode 21.3 vs 17.9 us; b = 16 42.1 vs 23.7 us;
+// b = 64 169 / 58.5 vs 45.7 us; b = 128 densify 64.9 vs 56.4 us; b = 256
+// densify 74.8 vs 77.2 us.  The 8192 x 8192 3 % rank-512 layer agrees:
+// b = 64 densify 137 vs 87 us, b = 128 156 vs 139 us, b = 256 164 vs 203 us.
+static constexpr int kSpmmMinCols = 8, kSpmmMaxCols = 128;
+
+static Route batch_route(const hss_matrix* A, int b) {
+  const bool sp = spmm_supported(A, b), mf = mfma_supported(A, b);
+  if (const char* e = std::getenv("HSS_CSR_BATCH_ROUTE")) {
+    if (!std::strcmp(e, "decode")) return R_DECODE;
+    if (!std::strcmp(e, "spmm") && sp) return R_SPMM;
+    if (!std::strcmp(e, "densify") && mf) return R_MFMA;
+  }
+  if (sp && b >= kSpmmMinCols && (b <= kSpmmMaxCols || !mf)) return R_SPMM;
+  if (mf) return R_MFMA;
+  return R_DECODE;
+}
+
 // Layout: [decode control region | decode T words or MFMA buffers].  The
 // control region persists between calls; everything after it is per-call
 // scratch, so both paths can share one workspace.
 size_t apply_ws_bytes(const hss_matrix* A, int b) {
   if (is_dq(A)) return 0;
+  // every route the call may take (the route can be forced at call time)
   const size_t dec = decode_t_bytes(A);
   const size_t mf = mfma_supported(A, b) ? mfma_ws_bytes(A, b) : 0;
-  return decode_ctl_bytes() + (dec > mf ? dec : mf);
+  const size_t sp = spmm_supported(A, b) ? spmm_ws_bytes(A, b) : 0;
+  size_t mx = dec > mf ? dec : mf;
+  mx = mx > sp ? mx : sp;
+  return decode_ctl_bytes() + mx;
 }
 
 hss_status launch_apply(const hss_matrix* A, int b, const void* X, void* Y, void* ws,
@@ -57,8 +98,9 @@ hss_status launch_apply(const hss_matrix* A, int b, const void* X, void* Y, void
     }
     return hipGetLastError() == hipSuccess ? HSS_OK : HSS_ERR_HIP;
   }
-  if (mfma_supported(A, b))
-    return launch_mfma(A, b, X, Y, static_cast<char*>(ws) + decode_ctl_bytes(), stream);
+  const Route route = batch_route(A, b);
+  if (route == R_MFMA) return launch_mfma(A, b, X, Y, static_cast<char*>(ws) + decode_ctl_bytes(), stream);
+  if (route == R_SPMM) return launch_spmm(A, b, X, Y, static_cast<char*>(ws) + decode_ctl_bytes(), stream);
   const size_t es = A->dtype == HSS_F32 ? 4 : 2;
   const int cols = decode_max_cols(A);
   if (cols == 0) return HSS_ERR_UNSUPPORTED;
@@ -87,7 +129,7 @@ size_t apply_group_ws_bytes(const hss_matrix* const* A, int G, int b) {
 hss_status launch_apply_group(const hss_matrix* const* A, int G, int b, const void* X, void* const* Y, void* ws,
                               hipStream_t stream) {
   bool any_mfma = false;  // (or dense-and-sparse: those run one by one too)
-  for (int g = 0; g < G; ++g) any_mfma = any_mfma || mfma_supported(A[g], b) || is_dq(A[g]);
+  for (int g = 0; g < G; ++g) any_mfma = any_mfma || batch_route(A[g], b) != R_DECODE || is_dq(A[g]);
   if (any_mfma) {
     for (int g = 0; g < G; ++g) {
       const hss_status st = launch_apply(A[g], b, X, Y[g], ws, stream);

@@ -4,6 +4,17 @@
 
 #include "hss_internal.h"
 
+namespace hss {  // grad.hip
+size_t grad_ws_bytes(const hss_matrix* A, int b);
+hss_status launch_grad(const hss_matrix* A, int b, const void* X, const void* G, float* dS, float* dU, float* dVt,
+                       void* ws, hipStream_t s);
+hss_status csr_transpose_host(int m, int n, const int32_t* row_ptr, const int32_t* col_idx, int32_t* row_ptr_t,
+                              int32_t* col_idx_t, int32_t* perm);
+hss_status launch_gather_values(int dt, int64_t nnz, const void* values, const int32_t* perm, void* values_t,
+                                hipStream_t s);
+hss_status launch_transpose(int dt, int rows, int cols, const void* src, void* dst, hipStream_t s);
+}  // namespace hss
+
 namespace {
 
 constexpr int64_t kLimit = (int64_t)1 << 31;  // arrays must have fewer elements
@@ -222,3 +233,74 @@ hss_status hss_hier_pack(hss_dtype dt, int32_t m, int32_t n, const int32_t* r, c
   return hss::launch_hier_pack(dt, m, n, r, U, Vt, perm, U_cat, Vt_cat, stream);
 }
 
+// ---------------------------------------------------------------------------
+// Backward pass
+// ---------------------------------------------------------------------------
+static hss_status check_grad(const hss_matrix* A, int32_t b) {
+  hss_status st = check_matrix(A, b);
+  if (st != HSS_OK) return st;
+  if (A->fmt != HSS_FMT_CSR || A->dtype != HSS_BF16 || (A->flags & HSS_DQ4)) return HSS_ERR_UNSUPPORTED;
+  const int64_t ldt = ((int64_t)b + 7) / 8 * 8;
+  if ((int64_t)A->n * ldt * 2 >= kLimit || (int64_t)A->m * ldt * 2 >= kLimit) return HSS_ERR_UNSUPPORTED;
+  return HSS_OK;
+}
+
+hss_status hss_grad_workspace_size(const hss_matrix* A, int32_t b, size_t* bytes) {
+  if (!bytes) return HSS_ERR_INVALID_ARG;
+  const hss_status st = check_grad(A, b);
+  if (st != HSS_OK) return st;
+  *bytes = hss::grad_ws_bytes(A, b);
+  return HSS_OK;
+}
+
+hss_status hss_grad(const hss_matrix* A, int32_t b, const void* X, const void* G, float* dS, float* dU, float* dVt,
+                    void* ws, size_t ws_bytes, hipStream_t stream) {
+  const hss_status st = check_grad(A, b);
+  if (st != HSS_OK) return st;
+  if (!X || !G) return HSS_ERR_INVALID_ARG;
+  const int64_t m = A->m, n = A->n, r = A->r;
+  const size_t xb = (size_t)b * n * 2, gb = (size_t)b * m * 2;
+  const size_t sb = (size_t)A->nnz * 4, ub = (size_t)m * r * 4, vb = (size_t)r * n * 4;
+  const void* outs[3] = {dS, dU, dVt};
+  const size_t ob[3] = {sb, ub, vb};
+  for (int k = 0; k < 3; ++k) {
+    if (!outs[k] || ob[k] == 0) continue;
+    if (overlap(outs[k], ob[k], X, xb) || overlap(outs[k], ob[k], G, gb)) return HSS_ERR_INVALID_ARG;
+    for (int q = k + 1; q < 3; ++q)
+      if (outs[q] && ob[q] && overlap(outs[k], ob[k], outs[q], ob[q])) return HSS_ERR_INVALID_ARG;
+  }
+  const size_t need = hss::grad_ws_bytes(A, b);
+  if (!ws || ws_bytes < need) return HSS_ERR_WORKSPACE;
+  return hss::launch_grad(A, b, X, G, dS, dU, dVt, ws, stream);
+}
+
+hss_status hss_csr_transpose(int32_t m, int32_t n, const int32_t* row_ptr, const int32_t* col_idx, int32_t* row_ptr_t,
+                             int32_t* col_idx_t, int32_t* perm) {
+  if (m < 1 || n < 1 || !row_ptr || !row_ptr_t || row_ptr[0] != 0) return HSS_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < m; ++i)
+    if (row_ptr[i + 1] < row_ptr[i]) return HSS_ERR_INVALID_ARG;
+  const int64_t nnz = row_ptr[m];
+  if (nnz > 0 && (!col_idx || !col_idx_t || !perm)) return HSS_ERR_INVALID_ARG;
+  for (int64_t p = 0; p < nnz; ++p)
+    if (col_idx[p] < 0 || col_idx[p] >= n) return HSS_ERR_INVALID_ARG;
+  return hss::csr_transpose_host(m, n, row_ptr, col_idx, row_ptr_t, col_idx_t, perm);
+}
+
+hss_status hss_gather_values(hss_dtype dt, int64_t nnz, const void* values, const int32_t* perm, void* values_t,
+                             hipStream_t stream) {
+  if (!valid_dtype(dt) || nnz < 0 || nnz >= kLimit) return HSS_ERR_INVALID_ARG;
+  if (nnz == 0) return HSS_OK;
+  if (!values || !perm || !values_t) return HSS_ERR_INVALID_ARG;
+  const size_t vb = (size_t)nnz * dsize(dt);
+  if (overlap(values, vb, values_t, vb)) return HSS_ERR_INVALID_ARG;
+  return hss::launch_gather_values(dt, nnz, values, perm, values_t, stream);
+}
+
+hss_status hss_transpose(hss_dtype dt, int32_t rows, int32_t cols, const void* src, void* dst, hipStream_t stream) {
+  if (!valid_dtype(dt) || rows < 1 || cols < 1 || (int64_t)rows * cols >= kLimit || !src || !dst)
+    return HSS_ERR_INVALID_ARG;
+  if ((rows + 31) / 32 > 65535) return HSS_ERR_INVALID_ARG;
+  const size_t bytes = (size_t)rows * cols * dsize(dt);
+  if (overlap(src, bytes, dst, bytes)) return HSS_ERR_INVALID_ARG;
+  return hss::launch_transpose(dt, rows, cols, src, dst, stream);
+}

@@ -846,6 +846,63 @@ static void run_gemm(GemmArgs g, int amode, float* part, hipStream_t s) {
   }
 }
 
+// T (b x r, bf16, row c = X[c] . V) on the matrix cores; `part` holds at
+// least t_gemm_part_bytes(A, b) bytes of split-K partials.
+void launch_t_gemm(const hss_matrix* A, int b, const void* X, uint16_t* Tb, float* part, hipStream_t s) {
+  const int n = A->n, r = A->r;
+  const uint16_t* Xb = static_cast<const uint16_t*>(X);
+  GemmArgs g = {};
+  g.M = r; g.N = b; g.K1 = n; g.K2 = 0;
+  g.nch1 = g.nch = cdiv(n, kKC);
+  g.A1 = static_cast<const uint16_t*>(A->Vt); g.lda1 = n;
+  g.B1 = Xb; g.ldb1 = n;
+  g.C = Tb; g.ldc = r; g.out_mode = OUT_BF16;
+  g.vec_a1 = aligned16(g.A1, n) && n % 8 == 0;
+  g.vec_b1 = aligned16(Xb, n) && n % 8 == 0;
+  run_gemm(g, A_DENSE, part, s);
+}
+
+// T transposed: Tt[l * ldt + c] = (X V)[c][l] (r x b, row stride ldt >= b;
+// columns past b are not written), the GEMM with X as the M operand.
+void launch_tt_gemm(const hss_matrix* A, int b, const void* X, uint16_t* Tt, int ldt, float* part, hipStream_t s) {
+  const int n = A->n, r = A->r;
+  const uint16_t* Xb = static_cast<const uint16_t*>(X);
+  GemmArgs g = {};
+  g.M = b; g.N = r; g.K1 = n; g.K2 = 0;
+  g.nch1 = g.nch = cdiv(n, kKC);
+  g.A1 = Xb; g.lda1 = n;
+  g.B1 = static_cast<const uint16_t*>(A->Vt); g.ldb1 = n;
+  g.C = Tt; g.ldc = ldt; g.out_mode = OUT_BF16;
+  g.vec_a1 = aligned16(Xb, n) && n % 8 == 0;
+  g.vec_b1 = aligned16(g.B1, n) && n % 8 == 0;
+  run_gemm(g, A_DENSE, part, s);
+}
+
+size_t t_gemm_part_bytes(const hss_matrix* A, int b) { return A->r > 0 ? gemm_part_bytes(A->r, b, A->n, 0) : 0; }
+// A general bf16 GEMM on the matrix cores: C[n * ldc + m] = sum_k A[m][k]
+// B[n][k] for m < M, n < N, k < K (A: M rows, B: N rows, both K-contiguous
+// with strides lda, ldb), fp32 accumulation, stored as bf16 (RNE) or fp32.
+// `part` holds at least gemm_bf16_part_bytes(M, N, K, ldc) bytes.
+void launch_gemm_bf16(int M, int N, int K, const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, void* C,
+                      int64_t ldc, bool out_bf16, float* part, hipStream_t s) {
+  GemmArgs g = {};
+  g.M = M; g.N = N; g.K1 = K; g.K2 = 0;
+  g.nch1 = g.nch = cdiv(K, kKC);
+  g.A1 = A; g.lda1 = lda;
+  g.B1 = B; g.ldb1 = ldb;
+  g.C = C; g.ldc = ldc; g.out_mode = out_bf16 ? OUT_BF16 : OUT_F32;
+  g.vec_a1 = aligned16(A, lda) && K % 8 == 0;
+  g.vec_b1 = aligned16(B, ldb) && K % 8 == 0;
+  run_gemm(g, A_DENSE, part, s);
+}
+
+size_t gemm_bf16_part_bytes(int M, int N, int K, int64_t ldc) { return gemm_part_bytes(M, N, K, 0) / M * ldc; }
+
+// Partials are laid out with the output's row stride ldt (>= b).
+size_t tt_gemm_part_bytes(const hss_matrix* A, int b, int ldt) {
+  return A->r > 0 ? gemm_part_bytes(b, A->r, A->n, 0) / b * ldt : 0;
+}
+
 hss_status launch_mfma(const hss_matrix* A, int b, const void* X, void* Y, void* ws, hipStream_t s) {
   const MfmaPlan p = plan_mfma(A, b);
   char* base = static_cast<char*>(ws);
@@ -867,17 +924,7 @@ hss_status launch_mfma(const hss_matrix* A, int b, const void* X, void* Y, void*
       hipLaunchKernelGGL(k_csr_densify<int32_t>, grid, dim3(256), 0, s, A->row_ptr, A->col_idx, vals, m, n, Sd);
   }
   // T^T (b x r) = X . Vt^T
-  if (r > 0) {
-    GemmArgs g = {};
-    g.M = r; g.N = b; g.K1 = n; g.K2 = 0;
-    g.nch1 = g.nch = cdiv(n, kKC);
-    g.A1 = static_cast<const uint16_t*>(A->Vt); g.lda1 = n;
-    g.B1 = Xb; g.ldb1 = n;
-    g.C = Tb; g.ldc = r; g.out_mode = OUT_BF16;
-    g.vec_a1 = aligned16(g.A1, n) && n % 8 == 0;
-    g.vec_b1 = aligned16(Xb, n) && n % 8 == 0;
-    run_gemm(g, A_DENSE, part, s);
-  }
+  if (r > 0) launch_t_gemm(A, b, X, Tb, part, s);
   // Y (b x m) = [X | T^T] . [S | U]^T
   GemmArgs g = {};
   g.M = m; g.N = b; g.K1 = s_empty ? 0 : n; g.K2 = r;

@@ -28,7 +28,8 @@ def test_header_declares_the_boundary():
     for must in ("hss_split", "hss_apply", "hss_split_workspace_size", "hss_apply_workspace_size",
                  "hss_apply_group", "hss_apply_group_workspace_size",
                  "hss_get_error", "hss_topk_count", "hss_status_string", "hss_version",
-                 "hss_rcm_order", "hss_concentration", "hss_concentration_workspace_size", "hss_hier_pack"):
+                 "hss_rcm_order", "hss_concentration", "hss_concentration_workspace_size", "hss_hier_pack",
+                 "hss_grad", "hss_grad_workspace_size", "hss_csr_transpose", "hss_gather_values", "hss_transpose"):
         assert must in names
 
 
@@ -39,7 +40,7 @@ def test_library_exports_every_declared_symbol(hl):
 
 
 def test_version_and_strings(hl):
-    assert hl.hss_version() == 103
+    assert hl.hss_version() == 104
     for code in range(6):
         assert hl.status_string(code).startswith("HSS_")
 
@@ -213,3 +214,33 @@ def test_hierarchical_entry_points_reject_bad_arguments(hl):
     assert pack(Uc=None) == INV
     assert pack(n=20, perm=FAKE) == INV
     assert pack(r=(0, 0, 0, 0), U=(None,) * 4, Vt=(None,) * 4, Uc=None, Vc=None) == 0   # nothing to pack
+
+
+def test_backward_entry_points_reject_bad_arguments(hl):
+    INV, WS, UNS = hl._lib.HSS_ERR_INVALID_ARG, hl._lib.HSS_ERR_WORKSPACE, hl._lib.HSS_ERR_UNSUPPORTED
+    lib = hl._lib.lib
+
+    def grad(s, b=4, X=FAKE * 64, G=FAKE * 96, dS=FAKE * 128, dU=FAKE * 160, dVt=FAKE * 192, ws=FAKE * 224,
+             wsb=1 << 24):
+        return lib.hss_grad(ctypes.byref(s), b, X, G, dS, dU, dVt, ws, wsb, None)
+    assert grad(_matrix(hl, dtype=0)) == UNS                            # fp32 layer
+    assert grad(_matrix(hl, fmt=1, nm_values=FAKE, nm_meta=FAKE)) == UNS  # 2:4 layer
+    assert grad(_matrix(hl, m=0)) == INV
+    assert grad(_matrix(hl), b=0) == INV
+    assert grad(_matrix(hl), X=None) == INV
+    assert grad(_matrix(hl), G=None) == INV
+    assert grad(_matrix(hl), dU=FAKE * 64 + 8) == INV                   # output overlaps X
+    assert grad(_matrix(hl), dVt=FAKE * 128 + 4) == INV                 # two outputs overlap
+    assert grad(_matrix(hl), ws=None) == WS
+    assert grad(_matrix(hl), wsb=64) == WS
+    sz = ctypes.c_size_t(0)
+    assert lib.hss_grad_workspace_size(ctypes.byref(_matrix(hl)), 4, ctypes.byref(sz)) == 0 and sz.value > 0
+    assert lib.hss_gather_values(1, -1, FAKE, FAKE * 2, FAKE * 3, None) == INV
+    assert lib.hss_gather_values(7, 4, FAKE, FAKE * 2, FAKE * 3, None) == INV
+    assert lib.hss_gather_values(1, 4, FAKE, None, FAKE * 3, None) == INV
+    assert lib.hss_gather_values(1, 4, FAKE, FAKE * 2, FAKE + 2, None) == INV   # overlapping values
+    assert lib.hss_gather_values(1, 0, None, None, None, None) == 0             # nothing to do
+    assert lib.hss_transpose(1, 0, 4, FAKE, FAKE * 2, None) == INV
+    assert lib.hss_transpose(9, 4, 4, FAKE, FAKE * 2, None) == INV
+    assert lib.hss_transpose(1, 4, 4, FAKE, FAKE + 8, None) == INV             # overlapping
+    assert lib.hss_transpose(1, 2_200_000, 2, FAKE, FAKE * 64, None) == INV    # too many rows for the grid

@@ -71,3 +71,33 @@ def test_rcm_rejects_bad_arguments(H):
     assert call([0, 1, 1], [5], 2) == INV                  # column out of range
     assert call([0, 1, 1], [-1], 2) == INV
     assert lib.hss_rcm_order(2, None, None, perm.ctypes.data) == INV
+
+
+@pytest.mark.parametrize("m,n,density,seed", [(1, 1, 1.0, 0), (7, 5, 0.4, 1), (60, 90, 0.05, 2), (300, 41, 0.2, 3),
+                                              (33, 33, 0.0, 4)])
+def test_csr_transpose_matches_oracle(H, m, n, density, seed):
+    """The library's host transpose of a CSR pattern is the oracle's: same
+    S^T pattern, same permutation (bit-exact)."""
+    rng = np.random.default_rng(seed)
+    mask = rng.random((m, n)) < density
+    rp, ci = _csr(mask)
+    rpt, cit, perm = H.hss_csr_transpose(rp, ci, m, n)
+    ort, oct_, operm = O.csr_transpose(m, n, rp, ci)
+    assert np.array_equal(rpt, ort) and np.array_equal(cit, oct_) and np.array_equal(perm, operm)
+
+
+def test_csr_transpose_rejects_bad_arguments(H):
+    lib, INV = H._lib.lib, H._lib.HSS_ERR_INVALID_ARG
+    out = np.zeros(8, dtype=np.int32)
+
+    def call(rp, ci, m, n):
+        rp = np.asarray(rp, dtype=np.int32)
+        ci = np.asarray(ci, dtype=np.int32)
+        return lib.hss_csr_transpose(m, n, rp.ctypes.data, ci.ctypes.data, out.ctypes.data, out.ctypes.data,
+                                     out.ctypes.data)
+    assert call([0, 1, 2], [0, 1], 2, 2) == 0
+    assert call([0, 1, 2], [0, 1], 0, 2) == INV
+    assert call([0, 1, 2], [0, 1], 2, 0) == INV
+    assert call([1, 1, 2], [0, 1], 2, 2) == INV
+    assert call([0, 2, 1], [0, 1], 2, 2) == INV
+    assert call([0, 1, 2], [0, 2], 2, 2) == INV                  # column outside [0, n)

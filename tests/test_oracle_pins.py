@@ -689,3 +689,19 @@ def test_csr_transpose_is_the_transposed_matrix():
         St[j, cit[seg]] = vals[perm][seg]
     assert np.array_equal(St, S.T)
     assert sorted(perm.tolist()) == list(range(len(ci)))
+
+
+def test_backward_sampled_equals_full():
+    m, n = 10, 8
+    rp, ci, S, U, V, X, G = _bw_case(m, n, r=3, b=6, seed=8)
+    g = O.backward(m, n, rp, ci, S, U, V, X, G)
+    N = O.backward_normalisers(m, n, rp, ci, S, U, V, X, G)
+    rows, cols = np.array([0, 3, 9]), np.array([1, 7])
+    er = O.csr_row_of_entry(m, rp)
+    pick = np.array([0, len(ci) // 2, len(ci) - 1])
+    smp = O.backward_sampled(rows, cols, er[pick], ci[pick], U, V, X, G)
+    assert np.allclose(smp["dU"], g["dU"][rows], rtol=1e-12, atol=1e-12)
+    assert np.allclose(smp["dV"], g["dV"][cols], rtol=1e-12, atol=1e-12)
+    assert np.allclose(smp["dS"], g["dS"][pick], rtol=1e-12, atol=1e-12)
+    assert np.allclose(smp["NU"], N["dU"][rows]) and np.allclose(smp["NV"], N["dV"][cols])
+    assert np.allclose(smp["NS"], N["dS"][pick])
