@@ -27,7 +27,8 @@ and 8, the 11008 x 4096 2:4 layer at batch 1/8/64, one decoder layer's seven
 projections per decode token (q/k/v and gate/up as grouped applies, so four
 launches per token; the seven-launch order beside it), the 8192^2 prefill at
 batch 2048 (with the low-rank GEMMs alone for their matrix-core throughput),
-and hss_split.
+a training step on the 8192^2 layer at b = 2048 (forward, hss_grad and the
+transposed layer's apply for the input gradient), and hss_split.
 
 Prints ONE JSON line.  `value` = decode tokens/s of the timed steps;
 `roofline` prices the apply kernel's compressed-weight bytes against the
@@ -37,6 +38,7 @@ sample.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import math
 import os
@@ -443,6 +445,36 @@ def main():
             "lowrank_tflops": lr_flops / (ms5_lr * 1e-3) / 1e12,
             "lowrank_mfma_frac": lr_flops / (ms5_lr * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
             "dense_equiv_tflops": dense_equiv / (ms5 * 1e-3) / 1e12}
+
+        # training step on the same layer, b = 2048: forward, parameter
+        # gradients (hss_grad) and the input gradient (forward apply of the
+        # transposed layer); S^T's pattern is built once on the host, its
+        # values are gathered on the device every step
+        A5 = L5.mats[0]
+        t0 = time.perf_counter()
+        At5 = H.hss_transposed_layer(A5)
+        torch.cuda.synchronize()
+        at_ms = (time.perf_counter() - t0) * 1e3
+        gs5 = [_bf16(syn.random_matrix(b, L5.m, "bf16", seed=70 + i, kind="normal", scale=1.0)) for i in range(2)]
+        gsz = ctypes.c_size_t(0)
+        H._lib.check(H._lib.lib.hss_grad_workspace_size(ctypes.byref(A5.struct), b, ctypes.byref(gsz)), "ws")
+        gws = torch.empty(gsz.value, dtype=torch.uint8, device="cuda")
+        wst = At5.workspace(b)
+        dxs = torch.empty((b, L5.n), dtype=torch.bfloat16, device="cuda")
+        ms_fwd = _time(lambda i: H.hss_apply(A5, xs5[i % 2], ys5[i % 2], ws5), 10, 3)
+        ms_grad = _time(lambda i: H.hss_grad(A5, xs5[i % 2], gs5[i % 2], ws=gws), 10, 3)
+        ms_dx = _time(lambda i: H.hss_apply(At5, gs5[i % 2], dxs, wst), 10, 3)
+        ms_gather = _time(lambda i: H.hss_gather_values(A5.values, At5.perm_from_s), 10, 3)
+        grad_flops = 2.0 * b * (2 * L5.r * (L5.m + L5.n) + L5.split.k)
+        step_ms = ms_fwd + ms_grad + ms_dx + ms_gather
+        step_flops = 2 * L5.flops(b) + grad_flops
+        extra["train_8192sq_b2048"] = {
+            "step_ms": step_ms, "tokens_per_s": b / (step_ms * 1e-3),
+            "useful_tflops": step_flops / (step_ms * 1e-3) / 1e12,
+            "forward_ms": ms_fwd, "grad_ms": ms_grad, "grad_useful_tflops": grad_flops / (ms_grad * 1e-3) / 1e12,
+            "dX_ms": ms_dx, "gather_values_ms": ms_gather, "transposed_layer_setup_ms": at_ms,
+            "note": "one copy of the weights (compute-bound shape; no rotation)"}
+        del At5, gs5, gws, wst, dxs, A5
         del L5, lr, W5
         torch.cuda.empty_cache()
 

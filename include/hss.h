@@ -325,7 +325,11 @@ hss_status hss_hier_pack(hss_dtype dt, int32_t m, int32_t n, const int32_t* r, c
  *        of the stored V^T.
  *   X V and G U are rounded to bf16 once (matrix-core GEMMs with fp32
  *   accumulation); every sum over the batch accumulates in fp32.  The same
- *   inputs give the same bits on every call.
+ *   inputs give the same bits on every call.  dS is a sampled product on
+ *   the vector units below 512 columns; from 512 on, the dense G^T X on the
+ *   matrix cores (its m*n fp32 values in the workspace) then a gather
+ *   (HSS_GRAD_DS_ROUTE = sparse | dense forces one; query the workspace
+ *   size with the same setting).
  *   ws: at least hss_grad_workspace_size() bytes (no state kept).
  *   HSS_ERR_UNSUPPORTED: a 2:4, fp32 or dense-and-sparse layer, or
  *   n * round8(b) * 2 or m * round8(b) * 2 >= 2^31.  HSS_ERR_INVALID_ARG: as

@@ -12,13 +12,16 @@
 //   P^T = (G U)^T   r x ldt   GEMM: A = G (b x m), B = U^T (r x m)
 //   dU  = G^T T     m x r     GEMM over the batch: A = T^T, B = G^T (m x ldt)
 //   dV^T = P^T X    r x n     GEMM over the batch: A = X^T (n x ldt), B = P^T
-//   dS_p = sum_c G[c][i_p] X[c][j_p]                  k_sddmm (vector units)
+//   dS_p = sum_c G[c][i_p] X[c][j_p]                  k_sddmm (vector units), or
+//          for large batches dA = G^T X on the matrix cores, then k_ds_gather
 //
 // The input gradient dX = G A is the forward apply of A^T = S^T + V U^T:
 // hss_csr_transpose (S^T's pattern, once per pattern, on the host),
 // hss_gather_values (its values, on the device) and hss_transpose (U^T and
 // V from the stored factors) build it; hss_apply then runs on it.
 #include <algorithm>
+#include <cstdlib>
+#include <cstring>
 #include <vector>
 
 #include "hss_internal.h"
@@ -36,16 +39,19 @@ static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 static int round8(int x) { return (x + 7) & ~7; }
 
 // ---------------------------------------------------------------------------
-// dS: one wave per row i; each stored entry's dot product over the batch is
-// split across LP lanes (16 bytes = 8 batch values of G^T[i] and X^T[j] per
-// lane and step), the 64 / LP lane groups taking every (64 / LP)-th entry.
-// The LP partial sums meet in an xor butterfly (fixed order).
+// dS, sparse form: one wave per row i; each stored entry's dot product over
+// the batch is split across LP lanes (16 bytes = 8 batch values of G^T[i]
+// and X^T[j] per lane and step), the 64 / LP lane groups taking entries
+// p0 + s + SL u (u < 4: four entries in flight, sharing the G^T piece).  The
+// LP partial sums meet in an xor butterfly (fixed order).
 // ---------------------------------------------------------------------------
+static constexpr int kSdUnroll = 4;
+
 template <int LP, typename CT>
 __global__ __launch_bounds__(256) void k_sddmm(const int32_t* __restrict__ row_ptr, const CT* __restrict__ col,
                                                const uint16_t* __restrict__ Gt, const uint16_t* __restrict__ Xt,
                                                int m, int n, int ldt, float* __restrict__ dS) {
-  constexpr int SL = 64 / LP;
+  constexpr int SL = 64 / LP, UE = kSdUnroll;
   const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (i >= m) return;  // wave-uniform
   const int lane = lane_id(), q0 = lane % LP, s = lane / LP;
@@ -56,23 +62,54 @@ __global__ __launch_bounds__(256) void k_sddmm(const int32_t* __restrict__ row_p
   // reads zeros instead of memory past X^T
   const __amdgpu_buffer_rsrc_t rx =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Xt), 0, (int)((int64_t)n * ldt * 2), 0x00020000);
-  for (int64_t p0 = rs; p0 < re; p0 += SL) {
-    const int64_t p = p0 + s;
-    const bool on = p < re;
-    const int j = on ? (int)col[p] : 0;
-    float acc = 0.f;
+  for (int64_t p0 = rs + s; p0 < re; p0 += SL * UE) {
+    int j[UE];
+    float acc[UE];
+#pragma unroll
+    for (int u = 0; u < UE; ++u) {
+      const int64_t p = p0 + u * SL;
+      j[u] = p < re ? (int)col[p] : 0;
+      acc[u] = 0.f;
+    }
     for (int q = q0; q < pieces; q += LP) {
       const u32x4 gv = *reinterpret_cast<const u32x4*>(grow + 8 * q);
-      const u32x4 xv =
-          __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (j * ldt + 8 * q) * 2, 0, 0));
-      acc = fmaf(bf16lo(gv.x), bf16lo(xv.x), acc); acc = fmaf(bf16hi(gv.x), bf16hi(xv.x), acc);
-      acc = fmaf(bf16lo(gv.y), bf16lo(xv.y), acc); acc = fmaf(bf16hi(gv.y), bf16hi(xv.y), acc);
-      acc = fmaf(bf16lo(gv.z), bf16lo(xv.z), acc); acc = fmaf(bf16hi(gv.z), bf16hi(xv.z), acc);
-      acc = fmaf(bf16lo(gv.w), bf16lo(xv.w), acc); acc = fmaf(bf16hi(gv.w), bf16hi(xv.w), acc);
+      u32x4 xv[UE];
+#pragma unroll
+      for (int u = 0; u < UE; ++u)
+        xv[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, (j[u] * ldt + 8 * q) * 2, 0, 0));
+      const float g[8] = {bf16lo(gv.x), bf16hi(gv.x), bf16lo(gv.y), bf16hi(gv.y),
+                          bf16lo(gv.z), bf16hi(gv.z), bf16lo(gv.w), bf16hi(gv.w)};
+#pragma unroll
+      for (int u = 0; u < UE; ++u) {
+        float t = acc[u];
+        t = fmaf(g[0], bf16lo(xv[u].x), t); t = fmaf(g[1], bf16hi(xv[u].x), t);
+        t = fmaf(g[2], bf16lo(xv[u].y), t); t = fmaf(g[3], bf16hi(xv[u].y), t);
+        t = fmaf(g[4], bf16lo(xv[u].z), t); t = fmaf(g[5], bf16hi(xv[u].z), t);
+        t = fmaf(g[6], bf16lo(xv[u].w), t); t = fmaf(g[7], bf16hi(xv[u].w), t);
+        acc[u] = t;
+      }
     }
 #pragma unroll
-    for (int off = 1; off < LP; off <<= 1) acc += __shfl_xor(acc, off, 64);
-    if (on && q0 == 0) dS[p] = acc;
+    for (int u = 0; u < UE; ++u) {
+#pragma unroll
+      for (int off = 1; off < LP; off <<= 1) acc[u] += __shfl_xor(acc[u], off, 64);
+      const int64_t p = p0 + u * SL;
+      if (p < re && q0 == 0) dS[p] = acc[u];
+    }
+  }
+}
+
+// dS, dense form: dS[p] = dA[i][col_idx[p]] from dA = G^T X (m x n fp32,
+// computed on the matrix cores); one wave per row, coalesced along the row.
+template <typename CT>
+__global__ __launch_bounds__(256) void k_ds_gather(const int32_t* __restrict__ row_ptr, const CT* __restrict__ col,
+                                                   const float* __restrict__ dA, int m, int n, float* __restrict__ dS) {
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (i >= m) return;
+  const float* __restrict__ row = dA + (int64_t)i * n;
+  for (int64_t p = row_ptr[i] + lane_id(); p < row_ptr[i + 1]; p += 64) {
+    const int j = (int)col[p];
+    dS[p] = (j >= 0 && j < n) ? row[j] : 0.f;
   }
 }
 
@@ -94,9 +131,22 @@ static void launch_sddmm_ct(int lp, const int32_t* rp, const CT* col, const uint
 // ---------------------------------------------------------------------------
 // Workspace: X^T, G^T, U^T, T^T, P^T and the GEMMs' split-K partials.
 // ---------------------------------------------------------------------------
+// dS route: the dense form from this batch on (or HSS_GRAD_DS_ROUTE =
+// sparse | dense).  Measured on the 8192 x 8192 3 % layer: see the design
+// notes' backward table.
+static constexpr int kDenseDsMinB = 512;
+
+static bool ds_dense(int b) {
+  if (const char* e = getenv("HSS_GRAD_DS_ROUTE")) {
+    if (!strcmp(e, "sparse")) return false;
+    if (!strcmp(e, "dense")) return true;
+  }
+  return b >= kDenseDsMinB;
+}
+
 struct GradPlan {
   int ldt, ldu;
-  size_t xt, gt, ut, tt, pt, part, total;
+  size_t xt, gt, ut, tt, pt, da, part, total;
 };
 
 static GradPlan plan_grad(const hss_matrix* A, int b) {
@@ -110,6 +160,7 @@ static GradPlan plan_grad(const hss_matrix* A, int b) {
   p.ut = off; off += al256((size_t)(r > 0 ? r : 1) * p.ldu * 2);
   p.tt = off; off += al256((size_t)(r > 0 ? r : 1) * p.ldt * 2);
   p.pt = off; off += al256((size_t)(r > 0 ? r : 1) * p.ldt * 2);
+  p.da = off; off += ds_dense(b) ? al256((size_t)m * n * 4) : 0;
   size_t part = 0;
   if (r > 0) {
     part = std::max(part, tt_gemm_part_bytes(A, b, p.ldt));
@@ -117,6 +168,7 @@ static GradPlan plan_grad(const hss_matrix* A, int b) {
     part = std::max(part, gemm_bf16_part_bytes(r, m, b, r));      // dU
     part = std::max(part, gemm_bf16_part_bytes(n, r, b, n));      // dV^T
   }
+  if (ds_dense(b)) part = std::max(part, gemm_bf16_part_bytes(n, m, b, n));  // dA
   p.part = off; off += al256(part);
   p.total = off;
   return p;
@@ -149,7 +201,16 @@ hss_status launch_grad(const hss_matrix* A, int b, const void* X, const void* G,
     launch_gemm_bf16(b, r, m, Gb, m, Ut, p.ldu, Pt, p.ldt, true, part, s);
     launch_gemm_bf16(n, r, b, Xt, p.ldt, Pt, p.ldt, dVt, n, false, part, s);
   }
-  if (want_s) {
+  if (want_s && ds_dense(b)) {
+    float* dA = reinterpret_cast<float*>(base + p.da);
+    launch_gemm_bf16(n, m, b, Xt, p.ldt, Gt, p.ldt, dA, n, false, part, s);
+    const dim3 grid((unsigned)((m + 3) / 4));
+    if (A->flags & HSS_COL16)
+      hipLaunchKernelGGL(k_ds_gather<uint16_t>, grid, dim3(256), 0, s, A->row_ptr,
+                         reinterpret_cast<const uint16_t*>(A->col_idx), dA, m, n, dS);
+    else
+      hipLaunchKernelGGL(k_ds_gather<int32_t>, grid, dim3(256), 0, s, A->row_ptr, A->col_idx, dA, m, n, dS);
+  } else if (want_s) {
     int lp = 1;
     while (lp < 64 && lp * 2 <= (p.ldt >> 3)) lp *= 2;
     if (A->flags & HSS_COL16)

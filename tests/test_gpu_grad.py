@@ -171,3 +171,20 @@ def test_backward_8192_layer_sampled(H):
     A_cols = S_cols + U64 @ V64[cols].T
     dX_ref, NX = G64 @ A_cols, np.abs(G64) @ np.abs(A_cols)
     _within(O.widen(to_host(out["dX"]), DT)[:, cols], dX_ref, NX, "dX")
+
+
+@pytest.mark.parametrize("route,b", [("dense", 16), ("sparse", 600), ("dense", 5)])
+def test_ds_routes_forced(H, monkeypatch, route, b):
+    """Both forms of dS (the sampled product and the dense G^T X plus gather)
+    on the other side of their default batch threshold."""
+    m, n, r = 130, 264, 8
+    A, ref, S64, U64, V64 = _layer(H, m, n, r, 55 + b)
+    X = syn.random_matrix(b, n, DT, seed=56, kind="normal", scale=1.0)
+    G = syn.random_matrix(b, m, DT, seed=57, kind="normal", scale=1.0)
+    X64, G64 = O.widen(X, DT), O.widen(G, DT)
+    g = O.backward(m, n, ref["row_ptr"], ref["col_idx"], S64, U64, V64, X64, G64)
+    N = O.backward_normalisers(m, n, ref["row_ptr"], ref["col_idx"], S64, U64, V64, X64, G64)
+    monkeypatch.setenv("HSS_GRAD_DS_ROUTE", route)
+    out = H.hss_grad(A, to_dev(X, DT), to_dev(G, DT))
+    _within(out["dS"].cpu().numpy(), g["dS"], N["dS"], "dS")
+    _within(out["dU"].cpu().numpy(), g["dU"], N["dU"], "dU")
