@@ -120,16 +120,31 @@ __global__ __launch_bounds__(256) void k_rho_partial(const typename Elem<DT>::bi
   }
 }
 
-__global__ void k_rho_final(const double* __restrict__ part, int blocks, double* out) {
-  if (threadIdx.x != 0) return;
+// 64 threads: thread t adds partials t, t + 64, ... in order, then a fixed
+// pairwise tree through LDS; the same bits on every call.
+__global__ __launch_bounds__(64) void k_rho_final(const double* __restrict__ part, int blocks, double* out) {
+  __shared__ double sd[64], st[64];
+  const int t = threadIdx.x;
   double d = 0.0, a = 0.0;
-  for (int b = 0; b < blocks; ++b) {
+  for (int b = t; b < blocks; b += 64) {
     d += part[2 * b];
     a += part[2 * b + 1];
   }
-  out[0] = a > 0.0 ? d / a : 0.0;
-  out[1] = d;
-  out[2] = a;
+  sd[t] = d;
+  st[t] = a;
+  __syncthreads();
+  for (int s = 32; s > 0; s >>= 1) {
+    if (t < s) {
+      sd[t] += sd[t + s];
+      st[t] += st[t + s];
+    }
+    __syncthreads();
+  }
+  if (t == 0) {
+    out[0] = st[0] > 0.0 ? sd[0] / st[0] : 0.0;
+    out[1] = sd[0];
+    out[2] = st[0];
+  }
 }
 
 size_t concentration_ws_bytes(int n) { return sizeof(double) * 2 * kRhoBlocks + sizeof(int32_t) * (size_t)n; }
