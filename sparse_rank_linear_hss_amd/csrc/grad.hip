@@ -65,10 +65,12 @@ __global__ __launch_bounds__(256) void k_sddmm(const int32_t* __restrict__ row_p
   for (int64_t p0 = rs + s; p0 < re; p0 += SL * UE) {
     int j[UE];
     float acc[UE];
+    // unconditional loads (past the row: its last entry again, dropped at the
+    // store), so the four are in flight together
 #pragma unroll
     for (int u = 0; u < UE; ++u) {
       const int64_t p = p0 + u * SL;
-      j[u] = p < re ? (int)col[p] : 0;
+      j[u] = (int)col[p < re ? p : re - 1];
       acc[u] = 0.f;
     }
     for (int q = q0; q < pieces; q += LP) {

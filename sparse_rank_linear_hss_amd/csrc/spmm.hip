@@ -35,7 +35,7 @@ static constexpr int kSpWaves = 8;            // rows (waves) per block
 static constexpr int kSpLdsMax = 64 * 1024;   // LDS for the T tile
 static constexpr int kSpMaxG = 8;             // batch tile <= 64 columns
 static constexpr int kSpDepth = 4;            // entries per lane in flight
-static constexpr int kSpVecMaxB = 16;         // T on the vector units up to this batch
+static constexpr int kSpVecMaxB = 64;         // T on the vector units up to this batch
 
 static size_t align256_(size_t x) { return (x + 255) & ~(size_t)255; }
 static int cdiv_(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
@@ -106,21 +106,25 @@ __global__ __launch_bounds__(256) void k_spmm_prep(const uint16_t* __restrict__ 
 #pragma unroll
     for (int cc = 0; cc < 16; ++cc) acc[cc] = 0.f;
     if constexpr (VEC) {
+      // all 17 loads of a step are unconditional (rows past b re-read row
+      // b - 1 and are dropped after), so they are in flight together: a load
+      // under a branch would be waited for inside it
       for (int j = 8 * threadIdx.x; j < n; j += 8 * 256) {
         const u32x4 vv = *reinterpret_cast<const u32x4*>(vrow + j);
+        u32x4 xx[16];
+#pragma unroll
+        for (int cc = 0; cc < 16; ++cc)
+          xx[cc] = *reinterpret_cast<const u32x4*>(X + (int64_t)min(cb + cc, b - 1) * n + j);
         const float vf[8] = {bf16lo(vv.x), bf16hi(vv.x), bf16lo(vv.y), bf16hi(vv.y),
                              bf16lo(vv.z), bf16hi(vv.z), bf16lo(vv.w), bf16hi(vv.w)};
 #pragma unroll
         for (int cc = 0; cc < 16; ++cc) {
-          if (cb + cc < b) {
-            const u32x4 xx = *reinterpret_cast<const u32x4*>(X + (int64_t)(cb + cc) * n + j);
-            float t = acc[cc];
-            t = fmaf(vf[0], bf16lo(xx.x), t); t = fmaf(vf[1], bf16hi(xx.x), t);
-            t = fmaf(vf[2], bf16lo(xx.y), t); t = fmaf(vf[3], bf16hi(xx.y), t);
-            t = fmaf(vf[4], bf16lo(xx.z), t); t = fmaf(vf[5], bf16hi(xx.z), t);
-            t = fmaf(vf[6], bf16lo(xx.w), t); t = fmaf(vf[7], bf16hi(xx.w), t);
-            acc[cc] = t;
-          }
+          float t = acc[cc];
+          t = fmaf(vf[0], bf16lo(xx[cc].x), t); t = fmaf(vf[1], bf16hi(xx[cc].x), t);
+          t = fmaf(vf[2], bf16lo(xx[cc].y), t); t = fmaf(vf[3], bf16hi(xx[cc].y), t);
+          t = fmaf(vf[4], bf16lo(xx[cc].z), t); t = fmaf(vf[5], bf16hi(xx[cc].z), t);
+          t = fmaf(vf[6], bf16lo(xx[cc].w), t); t = fmaf(vf[7], bf16hi(xx[cc].w), t);
+          acc[cc] = t;
         }
       }
     } else {
