@@ -179,16 +179,17 @@ __device__ __forceinline__ void t_row(const typename Elem<DT>::bits_t* __restric
     const u32x4* v4 = reinterpret_cast<const u32x4*>(v);
     for (int base = 0; base < nv; base += NT * TV) {
       u32x4 vv[TV], xv[TV][BC];
+      // every load unconditional (past the end: vector 0; past bc: column
+      // bc - 1), so they are all in flight together -- a load under a branch
+      // is waited for inside it
 #pragma unroll
       for (int k = 0; k < TV; ++k) {
-        if (base + NT * k < nv) {  // block-uniform: skip slices wholly past the end
-          const int q = base + t + NT * k;
-          const int qc = q < nv ? q : 0;
-          vv[k] = __builtin_nontemporal_load(v4 + qc);
+        const int q = base + t + NT * k;
+        const int qc = q < nv ? q : 0;
+        vv[k] = __builtin_nontemporal_load(v4 + qc);
 #pragma unroll
-          for (int c = 0; c < BC; ++c)
-            if (c < bc) xv[k][c] = reinterpret_cast<const u32x4*>(xsrc + (int64_t)c * n)[qc];
-        }
+        for (int c = 0; c < BC; ++c)
+          xv[k][c] = reinterpret_cast<const u32x4*>(xsrc + (int64_t)min(c, bc - 1) * n)[qc];
       }
 #pragma unroll
       for (int k = 0; k < TV; ++k) {
@@ -906,9 +907,23 @@ __global__ __launch_bounds__(MTR > 0 ? kMergedThreads : 256) void k_decode(Group
   }
   for (int q = t; q < (r + 31) / 32; q += NT) miss[q] = 0;
   if (xvecs > 0) {
+    // the rest of X, four vectors per thread in flight per step (unconditional
+    // loads, past the end of X: vector 0)
     u32x4* dst = reinterpret_cast<u32x4*>(xs);
-    for (int q = t + NT * XR; q < xvecs; q += NT)
-      dst[a.x_pad ? q + (q >> 2) : q] = reinterpret_cast<const u32x4*>(X)[q];
+    const u32x4* X4 = reinterpret_cast<const u32x4*>(X);
+    for (int q0 = t + NT * XR; q0 < xvecs; q0 += 4 * NT) {
+      u32x4 v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int q = q0 + NT * k;
+        v[k] = X4[q < xvecs ? q : 0];
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int q = q0 + NT * k;
+        if (q < xvecs) dst[a.x_pad ? q + (q >> 2) : q] = v[k];
+      }
+    }
   } else if (a.x_lds) {
     for (int q = t; q < bc * n; q += NT) xs[q] = X[q];
   }
@@ -1408,11 +1423,25 @@ __global__ __launch_bounds__(256) void k_decode_dq(DqArgs q) {
   }
   csr_issue<DT, FMT, RPW>(a, rb, ch);
 
-  // X -> LDS
+  // X -> LDS, four vectors per thread in flight per step (unconditional
+  // loads; past the end of X: vector 0)
   constexpr int NV = 16 / sizeof(bits_t);
   if (a.vec) {
-    for (int v = t; v < bc * n / NV; v += 256)
-      reinterpret_cast<u32x4*>(xs)[v] = reinterpret_cast<const u32x4*>(X)[v];
+    const int xv = bc * n / NV;
+    const u32x4* X4 = reinterpret_cast<const u32x4*>(X);
+    for (int v0 = t; v0 < xv; v0 += 4 * 256) {
+      u32x4 vv[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int v = v0 + 256 * k;
+        vv[k] = X4[v < xv ? v : 0];
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int v = v0 + 256 * k;
+        if (v < xv) reinterpret_cast<u32x4*>(xs)[v] = vv[k];
+      }
+    }
   } else {
     for (int v = t; v < bc * n; v += 256) xs[v] = X[v];
   }
