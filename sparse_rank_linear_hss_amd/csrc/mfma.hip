@@ -538,6 +538,7 @@ __device__ __forceinline__ void h_tile_of(int b, int tiles_m, int tiles_n, int G
 template <int FM, int FN>
 __global__ __launch_bounds__(256, (FM * FN >= 16 ? 1 : 2)) void k_gemm_h(GemmArgs g) {
   using TL = HTile<FM, FN>;
+  constexpr bool DEEP = FM * FN < 8;  // two stages in registers
   __shared__ __align__(16) uint16_t hb0[TL::STAGE], hb1[TL::STAGE];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w >> 1, wn = w & 1;
@@ -566,11 +567,35 @@ __global__ __launch_bounds__(256, (FM * FN >= 16 ? 1 : 2)) void k_gemm_h(GemmArg
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  // Stage s_begin + d sits in LDS buffer d % 2.  The registers hold the
-  // stage after the one being computed; loads past the end reload the last
-  // stage (unconditional, so the compiler keeps one copy of the staging
-  // registers), and its store fills a buffer nobody reads.
-  if (s_begin < s_end) {
+  // Stage s_begin + d sits in LDS buffer d % 2.  Two register sets hold the
+  // next two stages, so every stage's loads have two stages of MFMA work to
+  // land in (one was not enough to cover a memory round trip on the short-K
+  // products).  Loads past the end reload the last stage (unconditional, so
+  // the compiler keeps one copy of each register set), and their stores fill
+  // a buffer nobody reads.
+  if (DEEP && s_begin < s_end) {
+    const int last = s_end - 1;
+    HRegs<FM, FN> r0, r1;
+    h_load<FM, FN>(r0, g, ops, nst1, s_begin, m0, n0);
+    h_store<FM, FN>(hb0, r0);
+    h_load<FM, FN>(r0, g, ops, nst1, min(s_begin + 1, last), m0, n0);
+    h_load<FM, FN>(r1, g, ops, nst1, min(s_begin + 2, last), m0, n0);
+    __syncthreads();
+    for (int s = s_begin; s < s_end; s += 2) {
+      // stage s in hb0, s + 1 in r0, s + 2 in r1
+      h_compute<FM, FN>(hb0, wm, wn, acc);
+      h_store<FM, FN>(hb1, r0);
+      h_load<FM, FN>(r0, g, ops, nst1, min(s + 3, last), m0, n0);
+      __syncthreads();
+      if (s + 1 >= s_end) break;  // block-uniform
+      h_compute<FM, FN>(hb1, wm, wn, acc);
+      h_store<FM, FN>(hb0, r1);
+      h_load<FM, FN>(r1, g, ops, nst1, min(s + 4, last), m0, n0);
+      __syncthreads();
+    }
+  } else if (!DEEP && s_begin < s_end) {
+    // one register set (the 128 x 256 tile: a second set does not fit
+    // beside its 128 accumulators at two blocks per CU)
     const int last = s_end - 1;
     HRegs<FM, FN> r;
     h_load<FM, FN>(r, g, ops, nst1, s_begin, m0, n0);
