@@ -218,7 +218,7 @@ def main():
     args = _args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     sys.path.insert(0, ROOT)
@@ -238,7 +238,7 @@ def main():
         del src, dst
 
     # ---------------- headline: 4096^2 CSR 5 %, rank 256, decode ----------------
-    cfg = syn.CONFIGS[2]
+    cfg = syn.WORKLOADS["csr4096"]
     W_np = syn.weight(cfg)
     W = _bf16(W_np)
     L = Layer(H, W, "csr", cfg.frac, cfg.rank[0], cfg.seed)
@@ -366,14 +366,14 @@ def main():
         torch.cuda.empty_cache()
 
         # 11008 x 4096 2:4, rank 64, b = 1, 8, 64
-        c3 = syn.CONFIGS[3]
-        W3 = _bf16(syn.weight(c3))
-        L3 = Layer(H, W3, "2:4", c3.frac, c3.rank[0], c3.seed)
+        wl_nm = syn.WORKLOADS["nm24_11008x4096"]
+        W3 = _bf16(syn.weight(wl_nm))
+        L3 = Layer(H, W3, "2:4", wl_nm.frac, wl_nm.rank[0], wl_nm.seed)
         _log(f"2:4 layer ready: {L3.copies} rotation copies")
         ws3 = L3.mats[0].workspace(64)
         r3 = {}
-        for b in c3.batches:
-            xs3, ys3 = _acts(c3, b, 0, 4, L3.m)
+        for b in wl_nm.batches:
+            xs3, ys3 = _acts(wl_nm, b, 0, 4, L3.m)
             ms3 = _time_graph(_apply_loop(H, L3, xs3, ys3, ws3), max(1, steps // 8), 20)
             r3[f"b{b}"] = {"ms": ms3, "tokens_per_s": b / (ms3 * 1e-3),
                            "gbs": L3.w_bytes / (ms3 * 1e-3) / 1e9,
@@ -383,11 +383,11 @@ def main():
         torch.cuda.empty_cache()
 
         # decoder layer: 7 projections per token, b = 1
-        c4 = syn.CONFIGS[4]
+        wl_dl = syn.WORKLOADS["decoder_layer"]
         projs = []
         for which in range(7):
-            Wp = _bf16(syn.weight(c4, which))
-            projs.append(Layer(H, Wp, "csr", c4.frac, c4.rank[which], c4.seed, which,
+            Wp = _bf16(syn.weight(wl_dl, which))
+            projs.append(Layer(H, Wp, "csr", wl_dl.frac, wl_dl.rank[which], wl_dl.seed, which,
                                rotation_bytes=GIB / 7))
             del Wp
         tok_bytes = sum(p.w_bytes for p in projs)
@@ -397,7 +397,7 @@ def main():
         groups = [[0, 1, 2], [3], [4, 5], [6]]
         ws4 = torch.zeros(max(H.hss_apply_group_workspace_size([projs[w].mats[0] for w in grp], 1)
                               for grp in groups), dtype=torch.uint8, device="cuda")
-        xin = [[_bf16(syn.activations(c4, 1, grp[0], s)) for s in range(4)] for grp in groups]
+        xin = [[_bf16(syn.activations(wl_dl, 1, grp[0], s)) for s in range(4)] for grp in groups]
         ys4 = [torch.empty((1, p.m), dtype=torch.bfloat16, device="cuda") for p in projs]
 
         def layer_step(i):
@@ -412,23 +412,23 @@ def main():
             for gi, grp in enumerate(groups):
                 for w in grp:
                     H.hss_apply(projs[w].mats[i % len(projs[w].mats)], xin[gi][i % 4], ys4[w], ws4)
-        ms4 = _time_graph(layer_step, c4.tokens, 5)
-        ms4_7 = _time_graph(layer_step_7, c4.tokens, 5)
+        ms4 = _time_graph(layer_step, wl_dl.tokens, 5)
+        ms4_7 = _time_graph(layer_step_7, wl_dl.tokens, 5)
         extra["decoder_layer_7proj"] = {"ms_per_token": ms4, "tokens_per_s": 1 / (ms4 * 1e-3),
                                         "gbs": tok_bytes / (ms4 * 1e-3) / 1e9, "bytes_per_token": tok_bytes,
-                                        "tokens": c4.tokens, "launches_per_token": 4,
+                                        "tokens": wl_dl.tokens, "launches_per_token": 4,
                                         "ms_per_token_7_launches": ms4_7}
         del projs
         torch.cuda.empty_cache()
 
         # prefill: 8192^2 CSR 3 %, rank 512, b = 2048
-        c5 = syn.CONFIGS[5]
-        W5 = _bf16(syn.weight(c5))
-        L5 = Layer(H, W5, "csr", c5.frac, c5.rank[0], c5.seed, rotation_bytes=GIB / 4)
+        wl_pf = syn.WORKLOADS["csr8192_prefill"]
+        W5 = _bf16(syn.weight(wl_pf))
+        L5 = Layer(H, W5, "csr", wl_pf.frac, wl_pf.rank[0], wl_pf.seed, rotation_bytes=GIB / 4)
         _log(f"8192^2 layer ready: {L5.copies} rotation copies")
-        b = c5.batches[0]
+        b = wl_pf.batches[0]
         ws5 = L5.mats[0].workspace(b)
-        xs5, ys5 = _acts(c5, b, 0, 2, L5.m)
+        xs5, ys5 = _acts(wl_pf, b, 0, 2, L5.m)
         ms5 = _time(_apply_loop(H, L5, xs5, ys5, ws5), 10, 3)
         # the low-rank products alone (same matrix with an empty S): their MFMA rate
         lr = [H.HSSMatrix("csr", L5.m, L5.n, torch.bfloat16, U=mat.U, Vt=mat.Vt,

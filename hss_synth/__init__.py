@@ -5,7 +5,7 @@ none of the method's arithmetic (no top-k, no factorisation, no products), so
 both the CPU oracle's tests and the GPU path's tests/bench can take their
 inputs from it without sharing any of the computation under test.
 
-Workloads follow the five configurations the layer is measured on: Llama-class
+The workloads (WORKLOADS, keyed by name) are the five the layer is measured on: Llama-class
 projection shapes with heavy-tailed (Student-t, nu = 3) or Gaussian weights,
 optionally with 0.5 % outliers scaled x20 -- the heavy-tailed magnitude
 histogram that the HSS page ("LLMの階層的スパース+低ランク圧縮", section
@@ -31,8 +31,8 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "CONFIGS",
-    "Config",
+    "WORKLOADS",
+    "Workload",
     "f32_to_bf16_bits",
     "bf16_bits_to_f32",
     "weight",
@@ -45,12 +45,12 @@ __all__ = [
 _TAG_W, _TAG_OUT, _TAG_X, _TAG_FAC, _TAG_SMALL, _TAG_DQ = 0, 1, 2, 3, 4, 5
 
 
-class Config:
+class Workload:
     """One measured workload (shapes, dtype, distribution, S format, rank, batches)."""
 
-    def __init__(self, idx, name, shapes, dtype, dist, scale, outliers, fmt, frac, rank, batches,
+    def __init__(self, key, name, shapes, dtype, dist, scale, outliers, fmt, frac, rank, batches,
                  seed, tokens=None, proj_names=None):
-        self.idx = idx
+        self.key = key
         self.name = name
         self.shapes = list(shapes)        # list of (m, n): out features x in features
         self.dtype = dtype                # "f32" | "bf16"
@@ -66,27 +66,31 @@ class Config:
         self.proj_names = proj_names or [f"w{i}" for i in range(len(self.shapes))]
 
     def __repr__(self):
-        return f"Config({self.idx}, {self.name})"
+        return f"Workload({self.key!r}, {self.name})"
 
 
 _L = (4096, 4096)
 _UP = (11008, 4096)
 _DOWN = (4096, 11008)
 
-CONFIGS = {
-    1: Config(1, "1024x1024 f32, top 5% CSR, rank 64, b=1", [(1024, 1024)], "f32", "t3", 0.02,
-              False, "csr", (5, 100), [64], (1,), seed=0),
-    2: Config(2, "4096x4096 bf16 + 0.5% outliers, top 5% CSR, rank 256, b=1,16", [_L], "bf16",
-              "t3", 0.02, True, "csr", (5, 100), [256], (1, 16), seed=1),
-    3: Config(3, "11008x4096 bf16 + 0.5% outliers, 2:4, rank 64, b=1,8,64", [_UP], "bf16",
-              "normal", 0.02, True, "2:4", (1, 2), [64], (1, 8, 64), seed=2),
+WORKLOADS = {
+    "csr1024_f32": Workload(
+        "csr1024_f32", "1024x1024 f32, top 5% CSR, rank 64, b=1", [(1024, 1024)], "f32", "t3", 0.02,
+        False, "csr", (5, 100), [64], (1,), seed=0),
+    "csr4096": Workload(
+        "csr4096", "4096x4096 bf16 + 0.5% outliers, top 5% CSR, rank 256, b=1,16", [_L], "bf16",
+        "t3", 0.02, True, "csr", (5, 100), [256], (1, 16), seed=1),
+    "nm24_11008x4096": Workload(
+        "nm24_11008x4096", "11008x4096 bf16 + 0.5% outliers, 2:4, rank 64, b=1,8,64", [_UP], "bf16",
+        "normal", 0.02, True, "2:4", (1, 2), [64], (1, 8, 64), seed=2),
     # Seven projections of one decoder layer; rank = 10 % of min(m, n), floored: 409.
-    4: Config(4, "decoder layer q,k,v,o,gate,up,down bf16, top 3% CSR, rank 409, 256 tokens",
-              [_L, _L, _L, _L, _UP, _UP, _DOWN], "bf16", "t3", 0.02, False, "csr", (3, 100),
-              [409] * 7, (1,), seed=3, tokens=256,
-              proj_names=["q", "k", "v", "o", "gate", "up", "down"]),
-    5: Config(5, "8192x8192 bf16, top 3% CSR, rank 512, prefill b=2048", [(8192, 8192)], "bf16",
-              "t3", 0.015, False, "csr", (3, 100), [512], (2048,), seed=4),
+    "decoder_layer": Workload(
+        "decoder_layer", "decoder layer q,k,v,o,gate,up,down bf16, top 3% CSR, rank 409, 256 tokens",
+        [_L, _L, _L, _L, _UP, _UP, _DOWN], "bf16", "t3", 0.02, False, "csr", (3, 100),
+        [409] * 7, (1,), seed=3, tokens=256, proj_names=["q", "k", "v", "o", "gate", "up", "down"]),
+    "csr8192_prefill": Workload(
+        "csr8192_prefill", "8192x8192 bf16, top 3% CSR, rank 512, prefill b=2048", [(8192, 8192)], "bf16",
+        "t3", 0.015, False, "csr", (3, 100), [512], (2048,), seed=4),
 }
 
 
@@ -122,8 +126,8 @@ def _student_t3(rng, size):
     return rng.standard_t(3, size=size)
 
 
-def weight(cfg: Config, which: int = 0):
-    """W (m x n, row-major) of projection ``which`` of ``cfg``, in the config's storage type."""
+def weight(cfg: Workload, which: int = 0):
+    """W (m x n, row-major) of projection ``which`` of ``cfg``, in the workload's storage type."""
     m, n = cfg.shapes[which]
     rng = _rng(cfg.seed, _TAG_W, which)
     if cfg.dist == "t3":
@@ -140,7 +144,7 @@ def weight(cfg: Config, which: int = 0):
     return _store(w, cfg.dtype).reshape(m, n)
 
 
-def activations(cfg: Config, b: int, which: int = 0, step: int = 0):
+def activations(cfg: Workload, b: int, which: int = 0, step: int = 0):
     """X (b x n, row-major) ~ N(0, 1) for projection ``which`` at decode step ``step``."""
     n = cfg.shapes[which][1]
     x = _rng(cfg.seed, _TAG_X, which, step, b).standard_normal(b * n)

@@ -52,7 +52,7 @@ extern "C" {
 typedef enum {
   HSS_OK = 0,
   HSS_ERR_INVALID_ARG = 1, /* bad size, null pointer, aliasing, unknown enum          */
-  HSS_ERR_UNSUPPORTED = 2, /* valid request this build does not implement            */
+  HSS_ERR_UNSUPPORTED = 2, /* valid request the library does not implement          */
   HSS_ERR_WORKSPACE = 3,   /* workspace pointer null or smaller than *_workspace_size */
   HSS_ERR_NONFINITE = 4,   /* device-side: a NaN/Inf weight was seen by hss_split     */
   HSS_ERR_HIP = 5          /* a HIP runtime call or kernel launch failed              */

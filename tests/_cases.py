@@ -41,16 +41,16 @@ def meta_to_dev(meta):
 
 
 @functools.lru_cache(maxsize=None)
-def weight(cfg_idx, which=0):
-    w = syn.weight(syn.CONFIGS[cfg_idx], which)
+def weight(wl, which=0):
+    w = syn.weight(syn.WORKLOADS[wl], which)
     w.setflags(write=False)
     return w
 
 
 @functools.lru_cache(maxsize=None)
-def oracle_split(cfg_idx, which=0):
-    cfg = syn.CONFIGS[cfg_idx]
-    W = weight(cfg_idx, which)
+def oracle_split(wl, which=0):
+    cfg = syn.WORKLOADS[wl]
+    W = weight(wl, which)
     dt = dt_of(cfg.dtype)
     if cfg.fmt == "2:4":
         return O.split_24(W, dt)

@@ -123,12 +123,12 @@ def test_apply_empty_sparse_part(H, dtype, b, r):
     _check(Y, dtype, O.apply_factored(S64, U64, V64, X64), O.normaliser(S64, U64, V64, X64))
 
 
-def test_apply_config1_true_svd(H):
+def test_apply_csr1024_f32_true_svd(H):
     """1024 x 1024 fp32 workload end to end on the oracle's side: top 5 %, +0
     residual, rank-64 truncated SVD, factors cast to fp32; GPU apply at b=1."""
-    c = syn.CONFIGS[1]
-    W = weight(1)
-    ref = oracle_split(1)
+    c = syn.WORKLOADS["csr1024_f32"]
+    W = weight("csr1024_f32")
+    ref = oracle_split("csr1024_f32")
     U64, V64, _ = O.truncated_svd(O.widen(ref["residual"], O.F32), c.rank[0])
     U, V = O.narrow(U64, O.F32), O.narrow(V64, O.F32)
     X = syn.activations(c, 1)
@@ -140,7 +140,7 @@ def test_apply_config1_true_svd(H):
 
 
 def _sampled_check(H, cfg, which, b, rows, step=0):
-    c = syn.CONFIGS[cfg]
+    c = syn.WORKLOADS[cfg]
     dtype = dt_of(c.dtype)
     m, n = c.shapes[which]
     r = c.rank[which]
@@ -161,30 +161,30 @@ def _sampled_check(H, cfg, which, b, rows, step=0):
 
 
 @pytest.mark.parametrize("b", [1, 16])
-def test_apply_config2_full(H, b):
-    _sampled_check(H, 2, 0, b, None)
+def test_apply_csr4096_full(H, b):
+    _sampled_check(H, "csr4096", 0, b, None)
 
 
 @pytest.mark.parametrize("b", [1, 8, 64])
-def test_apply_config3_sampled(H, b):
+def test_apply_nm24_11008x4096_sampled(H, b):
     rows = np.random.default_rng(b).choice(11008, size=512, replace=False)
     rows.sort()
-    _sampled_check(H, 3, 0, b, rows)
+    _sampled_check(H, "nm24_11008x4096", 0, b, rows)
 
 
 @pytest.mark.parametrize("which", [0, 4, 6])
-def test_apply_config4_sampled(H, which):
-    m = syn.CONFIGS[4].shapes[which][0]
+def test_apply_decoder_layer_sampled(H, which):
+    m = syn.WORKLOADS["decoder_layer"].shapes[which][0]
     rows = np.random.default_rng(which).choice(m, size=384, replace=False)
     rows.sort()
     for step in range(2):
-        _sampled_check(H, 4, which, 1, rows, step)
+        _sampled_check(H, "decoder_layer", which, 1, rows, step)
 
 
-def test_apply_config5_sampled(H):
+def test_apply_csr8192_prefill_sampled(H):
     rows = np.random.default_rng(5).choice(8192, size=96, replace=False)
     rows.sort()
-    _sampled_check(H, 5, 0, 2048, rows)
+    _sampled_check(H, "csr8192_prefill", 0, 2048, rows)
 
 
 @pytest.mark.parametrize("fmt,dtype,b,m", [("csr", O.BF16, 1, 300), ("csr", O.F32, 3, 300), ("2:4", O.BF16, 8, 300),

@@ -109,7 +109,7 @@ def test_dq_apply_full_size_sampled(H):
     """4096 x 4096 bf16 with 0.5 % outliers (the oracle's split of the 4096^2
     weight) and stand-in 4-bit codes and levels; rows checked one by one."""
     import torch
-    cfg = syn.CONFIGS[2]
+    cfg = syn.WORKLOADS["csr4096"]
     m, n = cfg.shapes[0]
     W = syn.weight(cfg)
     s = O.split_csr(W, O.BF16, O.outlier_count(m, n))

@@ -138,10 +138,10 @@ def test_backward_8192_layer_sampled(H):
     shape): dU and dV on sampled rows, dS on sampled entries, dX on sampled
     columns."""
     import torch
-    c = syn.CONFIGS[5]
+    c = syn.WORKLOADS["csr8192_prefill"]
     m, n = c.shapes[0]
     r = c.rank[0]
-    ref = oracle_split(5)
+    ref = oracle_split("csr8192_prefill")
     U, V = syn.factors(m, n, r, DT, c.seed)
     A = H.HSSMatrix("csr", m, n, torch.bfloat16, U=to_dev(U, DT), Vt=to_dev(np.ascontiguousarray(V.T), DT),
                     row_ptr=_raw(ref["row_ptr"]), col_idx=_raw(ref["col_idx"]), values=to_dev(ref["values"], DT),

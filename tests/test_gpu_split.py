@@ -45,9 +45,9 @@ def test_split_csr_small(H, dtype, shape):
             _assert_csr_equal(sp, O.split_csr(W, dtype, k), dtype)
 
 
-@pytest.mark.parametrize("cfg", [1, 2])
-def test_split_csr_config_vs_oracle(H, cfg):
-    c = syn.CONFIGS[cfg]
+@pytest.mark.parametrize("cfg", ["csr1024_f32", "csr4096"])
+def test_split_csr_workload_vs_oracle(H, cfg):
+    c = syn.WORKLOADS[cfg]
     W = weight(cfg)
     dtype = dt_of(c.dtype)
     ref = oracle_split(cfg)
@@ -58,11 +58,11 @@ def test_split_csr_config_vs_oracle(H, cfg):
     assert np.array_equal(to_host(sp2.col_idx), ref["col_idx"])
 
 
-@pytest.mark.parametrize("cfg,which", [(4, i) for i in range(7)] + [(5, 0)])
-def test_split_csr_config_properties(H, cfg, which):
+@pytest.mark.parametrize("cfg,which", [("decoder_layer", i) for i in range(7)] + [("csr8192_prefill", 0)])
+def test_split_csr_workload_properties(H, cfg, which):
     """Full-size decoder-layer and 8192^2 splits: the defining properties of
     the top-k set (which make it unique) checked on every entry."""
-    c = syn.CONFIGS[cfg]
+    c = syn.WORKLOADS[cfg]
     W = weight(cfg, which)
     dtype = dt_of(c.dtype)
     m, n = W.shape
@@ -89,11 +89,11 @@ def test_split_24_small(H, dtype, shape):
         _assert_24_equal(sp, O.split_24(W, dtype))
 
 
-def test_split_24_config3_vs_oracle(H):
-    c = syn.CONFIGS[3]
-    W = weight(3)
+def test_split_24_nm24_11008x4096_vs_oracle(H):
+    c = syn.WORKLOADS["nm24_11008x4096"]
+    W = weight("nm24_11008x4096")
     sp = H.hss_split(to_dev(W, O.BF16), "2:4", residual=True)
-    _assert_24_equal(sp, oracle_split(3))
+    _assert_24_equal(sp, oracle_split("nm24_11008x4096"))
 
 
 @pytest.mark.parametrize("fmt", ["csr", "2:4"])

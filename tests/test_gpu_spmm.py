@@ -132,11 +132,11 @@ def test_spmm_group_equals_single_applies(H, monkeypatch, b):
         _check(Y, S64, U64, V64, O.widen(X, DT))
 
 
-def _full(H, cfg_idx, b, rows, route, monkeypatch):
-    c = syn.CONFIGS[cfg_idx]
+def _full(H, wl, b, rows, route, monkeypatch):
+    c = syn.WORKLOADS[wl]
     m, n = c.shapes[0]
     r = c.rank[0]
-    ref = oracle_split(cfg_idx)
+    ref = oracle_split(wl)
     U, V = syn.factors(m, n, r, DT, c.seed)
     import torch
     A = H.HSSMatrix("csr", m, n, torch.bfloat16, U=to_dev(U, DT), Vt=to_dev(np.ascontiguousarray(V.T), DT),
@@ -155,11 +155,11 @@ def _full(H, cfg_idx, b, rows, route, monkeypatch):
 def test_spmm_4096_layer_sampled(H, monkeypatch, b):
     """The 4096 x 4096 top-5 % rank-256 layer on the gather route."""
     rows = np.sort(np.random.default_rng(b).choice(4096, size=256, replace=False))
-    _full(H, 2, b, rows, "spmm", monkeypatch)
+    _full(H, "csr4096", b, rows, "spmm", monkeypatch)
 
 
 def test_spmm_8192_prefill_sampled(H, monkeypatch):
     """The 8192 x 8192 top-3 % rank-512 layer at b = 2048 on the gather route
     (32 batch tiles of 64 columns)."""
     rows = np.sort(np.random.default_rng(9).choice(8192, size=64, replace=False))
-    _full(H, 5, 2048, rows, "spmm", monkeypatch)
+    _full(H, "csr8192_prefill", 2048, rows, "spmm", monkeypatch)

@@ -62,10 +62,10 @@ def test_topk_count_is_floor_in_integers():
     assert O.topk_count(7, 1, 0, 100) == 0
 
 
-def test_config1_oracle_reproduces_worked_example():
+def test_csr1024_oracle_reproduces_worked_example():
     """The first workload is the worked example's shape: the oracle's split and
     factor shapes must give the printed parameter total."""
-    cfg = syn.CONFIGS[1]
+    cfg = syn.WORKLOADS["csr1024_f32"]
     W = syn.weight(cfg)
     m, n = W.shape
     k = O.topk_count(m, n, *cfg.frac)
@@ -101,8 +101,8 @@ def test_topk_matches_brute_force(kind, dtype, shape):
         assert np.array_equal(O.topk_mask(W, dtype, k), _brute_topk(W, dtype, k)), k
 
 
-def test_topk_invariants_config1():
-    cfg = syn.CONFIGS[1]
+def test_topk_invariants_csr1024():
+    cfg = syn.WORKLOADS["csr1024_f32"]
     W = syn.weight(cfg)
     k = O.topk_count(*W.shape, *cfg.frac)
     mask = O.topk_mask(W, O.F32, k)
