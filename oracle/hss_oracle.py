@@ -632,3 +632,17 @@ def backward_sampled(rows, cols, ent_rows, ent_cols, U64, V64, X64, G64):
     NS = np.sum(aG[:, ent_rows] * aX[:, ent_cols], axis=0)
     return {"dU": G64[:, rows].T @ XV, "dV": X64[:, cols].T @ GU, "dS": dS,
             "NU": aG[:, rows].T @ (aX @ np.abs(V64)), "NV": aX[:, cols].T @ (aG @ np.abs(U64)), "NS": NS}
+
+
+def nm24_pattern(m, n, nm_meta):
+    """The stored positions of a 2:4 matrix as a CSR pattern, in storage order
+    (entry 2g + s of row i is the s-th kept column of group g), so that its
+    values array is nm_values flattened: row_ptr[i] = i n / 2."""
+    meta = np.asarray(nm_meta, dtype=np.uint32).reshape(m, -1)
+    cols = np.zeros((m, n // 2), dtype=np.int64)
+    for g in range(n // 4):
+        nib = (meta[:, g // 8] >> np.uint32(4 * (g % 8))) & np.uint32(0xF)
+        cols[:, 2 * g] = 4 * g + (nib & 3)
+        cols[:, 2 * g + 1] = 4 * g + ((nib >> 2) & 3)
+    row_ptr = (np.arange(m + 1, dtype=np.int64) * (n // 2)).astype(np.int32)
+    return row_ptr, cols.reshape(-1).astype(np.int32)

@@ -28,6 +28,14 @@ def _fails(*tests):
     return False
 
 
+_orig_nm24_pattern = H.nm24_pattern
+
+
+def _nm24_pattern_slots_swapped(m, n, nm_meta):
+    rp, ci = _orig_nm24_pattern(m, n, nm_meta)
+    return rp, ci.reshape(-1, 2)[:, ::-1].reshape(-1).copy()     # the pair's columns in the wrong order
+
+
 _orig_backward = H.backward
 _orig_csr_transpose = H.csr_transpose
 
@@ -303,6 +311,7 @@ CASES = [
     ("backward", _backward_sign_flipped, [lambda: P.test_backward_matches_exact_finite_differences(0)]),
     ("backward", _backward_dS_transposed_index, [P.test_backward_one_hot_upstream_and_full_support_brute_force]),
     ("csr_transpose", _csr_transpose_row_major_order, [P.test_csr_transpose_is_the_transposed_matrix]),
+    ("nm24_pattern", _nm24_pattern_slots_swapped, [P.test_nm24_pattern_is_the_mask_in_storage_order]),
 ]
 
 

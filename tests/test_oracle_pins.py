@@ -705,3 +705,16 @@ def test_backward_sampled_equals_full():
     assert np.allclose(smp["dS"], g["dS"][pick], rtol=1e-12, atol=1e-12)
     assert np.allclose(smp["NU"], N["dU"][rows]) and np.allclose(smp["NV"], N["dV"][cols])
     assert np.allclose(smp["NS"], N["dS"][pick])
+
+
+def test_nm24_pattern_is_the_mask_in_storage_order():
+    """The 2:4 pattern as CSR: the kept positions row-major (ascending within
+    each group), and with the stored values it rebuilds the same matrix."""
+    W = syn.random_matrix(6, 40, O.BF16, seed=21, kind="ties")
+    s = O.split_24(W, O.BF16)
+    rp, ci = O.nm24_pattern(6, 40, s["nm_meta"])
+    rows, cols = np.nonzero(s["mask"])
+    assert np.array_equal(rp, np.arange(7) * 20)
+    assert np.array_equal(ci, cols) and np.array_equal(O.csr_row_of_entry(6, rp), rows)
+    assert np.array_equal(O.dense_from_csr(6, 40, rp, ci, s["nm_values"].reshape(-1), O.BF16),
+                          O.dense_from_24(6, 40, s["nm_values"], s["nm_meta"], O.BF16))
