@@ -316,10 +316,12 @@ hss_status hss_hier_pack(hss_dtype dt, int32_t m, int32_t n, const int32_t* r, c
  * hss_transpose and applied with hss_apply.
  * ------------------------------------------------------------------------
  *
- * hss_grad: parameter gradients of a bf16 CSR layer (device arrays):
+ * hss_grad: parameter gradients of a bf16 layer, CSR or 2:4 (device arrays):
  *   X (b x n) and G (b x m) bf16, row-major;
- *   dS  (fp32[nnz], out; NULL = skip): dS[p] = sum_c G[c][i] X[c][col_idx[p]]
- *        for the stored entry p in row i, in S's storage order;
+ *   dS  (fp32, out; NULL = skip): dS[p] = sum_c G[c][i] X[c][j] for the
+ *        stored entry p (row i, column j), in S's storage order: nnz values
+ *        for CSR; m * n / 2 for 2:4, laid out as nm_values (entry 2g + s of
+ *        row i is the s-th kept column of group g);
  *   dU  (fp32, m x r row-major, out; NULL = skip) = G^T (X V);
  *   dVt (fp32, r x n row-major, out; NULL = skip) = (G U)^T X, the gradient
  *        of the stored V^T.
@@ -331,13 +333,23 @@ hss_status hss_hier_pack(hss_dtype dt, int32_t m, int32_t n, const int32_t* r, c
  *   (HSS_GRAD_DS_ROUTE = sparse | dense forces one; query the workspace
  *   size with the same setting).
  *   ws: at least hss_grad_workspace_size() bytes (no state kept).
- *   HSS_ERR_UNSUPPORTED: a 2:4, fp32 or dense-and-sparse layer, or
+ *   HSS_ERR_UNSUPPORTED: an fp32 or dense-and-sparse layer, or
  *   n * round8(b) * 2 or m * round8(b) * 2 >= 2^31.  HSS_ERR_INVALID_ARG: as
  *   hss_apply, plus null X or G, or an output overlapping X, G or another
  *   output.  HSS_ERR_WORKSPACE; HSS_ERR_HIP. */
 hss_status hss_grad_workspace_size(const hss_matrix* A, int32_t b, size_t* bytes);
 hss_status hss_grad(const hss_matrix* A, int32_t b, const void* X, const void* G, float* dS, float* dU, float* dVt,
                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* hss_nm24_to_csr: the stored positions of a 2:4 matrix (m x n, nm_meta as
+ *   in hss_matrix) as a CSR pattern on the device: row_ptr (int32[m+1]) =
+ *   i n / 2, col_idx (int32[m n / 2]) in storage order, so that nm_values is
+ *   its values array (a valid CSR: columns ascend within each row).  The
+ *   transposed layer of a 2:4 layer starts from it.
+ *   HSS_ERR_INVALID_ARG: m < 1, n < 4 or n % 4 != 0, m * n >= 2^31, null or
+ *   overlapping arrays.  HSS_ERR_HIP. */
+hss_status hss_nm24_to_csr(int32_t m, int32_t n, const uint32_t* nm_meta, int32_t* row_ptr, int32_t* col_idx,
+                           hipStream_t stream);
 
 /* hss_csr_transpose: the CSR pattern of S^T (n x m) from S's (m x n), in
  *   HOST memory, computed on the host, synchronously (once per pattern):

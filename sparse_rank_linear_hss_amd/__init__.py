@@ -27,6 +27,7 @@ __all__ = [
     "hss_csr_cols_to_u16", "HSS_COL16", "HSS_DQ4",
     "hss_rcm_order", "hss_concentration", "hss_hier_pack",
     "hss_grad", "hss_csr_transpose", "hss_gather_values", "hss_transpose", "hss_transposed_layer", "hss_backward",
+    "hss_nm24_to_csr",
     "HSSMatrix", "SplitResult", "HSSError",
     "LIB_PATH", "status_string",
 ]
@@ -342,9 +343,10 @@ def hss_hier_pack(U, Vt, m: int, n: int, perm: Optional[torch.Tensor] = None):
 
 def hss_grad(A: HSSMatrix, X: torch.Tensor, G: torch.Tensor, dS=True, dU=True, dVt=True,
              ws: Optional[torch.Tensor] = None) -> dict:
-    """Parameter gradients of a bf16 CSR layer for the upstream gradient G
-    (b x m): fp32 dS (S's stored values, storage order), dU (m x r) and dVt
-    (r x n, the gradient of the stored V^T).  Pass False to skip one."""
+    """Parameter gradients of a bf16 layer (CSR or 2:4) for the upstream
+    gradient G (b x m): fp32 dS (S's stored values, storage order: nnz for
+    CSR, m x n/2 laid out as nm_values for 2:4), dU (m x r) and dVt (r x n,
+    the gradient of the stored V^T).  Pass False to skip one."""
     dev = _dev(X)
     if X.dim() != 2 or X.shape[1] != A.n or not X.is_contiguous() or X.dtype != A.dtype:
         raise ValueError("X must be a contiguous b x n tensor of the matrix dtype")
@@ -353,7 +355,8 @@ def hss_grad(A: HSSMatrix, X: torch.Tensor, G: torch.Tensor, dS=True, dU=True, d
         raise ValueError("G must be a contiguous b x m tensor of the matrix dtype")
     out = {}
     if dS:
-        out["dS"] = torch.empty(A.nnz, dtype=torch.float32, device=dev)
+        stored = A.m * (A.n // 2) if A.fmt == HSS_FMT_2OF4 else A.nnz
+        out["dS"] = torch.empty(stored, dtype=torch.float32, device=dev)
     if dU:
         out["dU"] = torch.empty((A.m, A.r), dtype=torch.float32, device=dev)
     if dVt:
@@ -398,23 +401,40 @@ def hss_transpose(t: torch.Tensor) -> torch.Tensor:
     return out
 
 
+def hss_nm24_to_csr(A: HSSMatrix):
+    """The stored positions of a 2:4 matrix as a device CSR pattern (row_ptr,
+    col_idx) in storage order: its values array is nm_values flattened."""
+    dev = A.nm_meta.device
+    rp = torch.empty(A.m + 1, dtype=torch.int32, device=dev)
+    ci = torch.empty(A.m * (A.n // 2), dtype=torch.int32, device=dev)
+    check(lib.hss_nm24_to_csr(A.m, A.n, _ptr(A.nm_meta), _ptr(rp), _ptr(ci), _stream(dev)), "hss_nm24_to_csr")
+    return rp, ci
+
+
 def hss_transposed_layer(A: HSSMatrix) -> HSSMatrix:
-    """A^T = S^T + V U^T as an HSSMatrix (n x m): S^T's pattern from the host
-    transpose, its values gathered on the device, U' = V and V'^T = U^T from
-    the stored factors.  hss_apply(A^T, G) is the input gradient G A."""
-    if A.fmt != HSS_FMT_CSR or A.flags & HSS_DQ4:
-        raise ValueError("the transposed layer is built for CSR layers")
-    dev = A.row_ptr.device
-    cols = A.col_idx.to(torch.int32) if A.flags & HSS_COL16 else A.col_idx
-    if A.flags & HSS_COL16:
-        cols = cols & 0xFFFF
-    rpt, cit, perm = hss_csr_transpose(A.row_ptr, cols if A.nnz else torch.zeros(0, dtype=torch.int32), A.m, A.n)
+    """A^T = S^T + V U^T as an HSSMatrix (n x m, CSR): S^T's pattern from the
+    host transpose (of the 2:4 positions for a 2:4 layer), its values
+    gathered on the device, U' = V and V'^T = U^T from the stored factors.
+    hss_apply(A^T, G) is the input gradient G A."""
+    if A.flags & HSS_DQ4:
+        raise ValueError("the transposed layer is built for CSR and 2:4 layers")
+    if A.fmt == HSS_FMT_2OF4:
+        dev = A.nm_meta.device
+        row_ptr, cols = hss_nm24_to_csr(A)
+        values, nnz = A.nm_values.reshape(-1), A.m * (A.n // 2)
+    else:
+        dev = A.row_ptr.device
+        row_ptr, values, nnz = A.row_ptr, A.values, A.nnz
+        cols = A.col_idx.to(torch.int32) if A.flags & HSS_COL16 else A.col_idx
+        if A.flags & HSS_COL16:
+            cols = cols & 0xFFFF
+    rpt, cit, perm = hss_csr_transpose(row_ptr, cols if nnz else torch.zeros(0, dtype=torch.int32), A.m, A.n)
     perm_d = torch.from_numpy(perm).to(dev)
-    vals = hss_gather_values(A.values, perm_d) if A.nnz else None
+    vals = hss_gather_values(values, perm_d) if nnz else None
     U2 = hss_transpose(A.Vt) if A.r > 0 else None
     Vt2 = hss_transpose(A.U) if A.r > 0 else None
     At = HSSMatrix("csr", A.n, A.m, A.dtype, U=U2, Vt=Vt2, row_ptr=torch.from_numpy(rpt).to(dev),
-                   col_idx=torch.from_numpy(cit).to(dev) if A.nnz else None, values=vals, nnz=A.nnz)
+                   col_idx=torch.from_numpy(cit).to(dev) if nnz else None, values=vals, nnz=nnz)
     At.perm_from_s = perm_d
     return At
 

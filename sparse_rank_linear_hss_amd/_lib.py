@@ -80,6 +80,7 @@ def _load():
         "hss_csr_transpose": (ctypes.c_int, [c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
         "hss_gather_values": (ctypes.c_int, [ctypes.c_int, c_int64, c_void_p, c_void_p, c_void_p, c_void_p]),
         "hss_transpose": (ctypes.c_int, [ctypes.c_int, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
+        "hss_nm24_to_csr": (ctypes.c_int, [c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

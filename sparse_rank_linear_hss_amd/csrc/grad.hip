@@ -47,16 +47,54 @@ static int round8(int x) { return (x + 7) & ~7; }
 // ---------------------------------------------------------------------------
 static constexpr int kSdUnroll = 4;
 
-template <int LP, typename CT>
-__global__ __launch_bounds__(256) void k_sddmm(const int32_t* __restrict__ row_ptr, const CT* __restrict__ col,
-                                               const uint16_t* __restrict__ Gt, const uint16_t* __restrict__ Xt,
-                                               int m, int n, int ldt, float* __restrict__ dS) {
+// S's stored positions: CSR (int32 or 16-bit columns) or 2:4 (row i holds
+// n / 2 entries, entry 2g + s the s-th kept column of group g, from the
+// nibble at bits 4 (g % 8) of metadata word g / 8).
+enum : int { PAT_CSR32 = 0, PAT_CSR16 = 1, PAT_NM24 = 2 };
+
+struct SPattern {
+  const int32_t* row_ptr;  // CSR
+  const void* col;         // CSR columns
+  const uint32_t* meta;    // 2:4 metadata, m x ceil(n / 32)
+  int n;
+};
+
+template <int PAT>
+__device__ __forceinline__ void pat_row(const SPattern& P, int i, int64_t& rs, int64_t& re) {
+  if constexpr (PAT == PAT_NM24) {
+    rs = (int64_t)i * (P.n >> 1);
+    re = rs + (P.n >> 1);
+  } else {
+    rs = P.row_ptr[i];
+    re = P.row_ptr[i + 1];
+  }
+}
+
+template <int PAT>
+__device__ __forceinline__ int pat_col(const SPattern& P, int i, int64_t rs, int64_t p) {
+  if constexpr (PAT == PAT_CSR32) {
+    return static_cast<const int32_t*>(P.col)[p];
+  } else if constexpr (PAT == PAT_CSR16) {
+    return static_cast<const uint16_t*>(P.col)[p];
+  } else {
+    const int q = (int)(p - rs), g = q >> 1;
+    const uint32_t w = P.meta[(int64_t)i * ((P.n + 31) >> 5) + (g >> 3)];
+    const uint32_t nib = (w >> (4 * (g & 7))) & 15u;
+    return 4 * g + (int)((q & 1) ? (nib >> 2) & 3u : nib & 3u);
+  }
+}
+
+template <int LP, int PAT>
+__global__ __launch_bounds__(256) void k_sddmm(SPattern P, const uint16_t* __restrict__ Gt,
+                                               const uint16_t* __restrict__ Xt, int m, int n, int ldt,
+                                               float* __restrict__ dS) {
   constexpr int SL = 64 / LP, UE = kSdUnroll;
   const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (i >= m) return;  // wave-uniform
   const int lane = lane_id(), q0 = lane % LP, s = lane / LP;
   const int pieces = ldt >> 3;
-  const int64_t rs = row_ptr[i], re = row_ptr[i + 1];
+  int64_t rs, re;
+  pat_row<PAT>(P, i, rs, re);
   const uint16_t* __restrict__ grow = Gt + (int64_t)i * ldt;
   // X^T through a bounded buffer resource: a column index outside [0, n)
   // reads zeros instead of memory past X^T
@@ -70,7 +108,7 @@ __global__ __launch_bounds__(256) void k_sddmm(const int32_t* __restrict__ row_p
 #pragma unroll
     for (int u = 0; u < UE; ++u) {
       const int64_t p = p0 + u * SL;
-      j[u] = (int)col[p < re ? p : re - 1];
+      j[u] = pat_col<PAT>(P, i, rs, p < re ? p : re - 1);
       acc[u] = 0.f;
     }
     for (int q = q0; q < pieces; q += LP) {
@@ -101,32 +139,57 @@ __global__ __launch_bounds__(256) void k_sddmm(const int32_t* __restrict__ row_p
   }
 }
 
-// dS, dense form: dS[p] = dA[i][col_idx[p]] from dA = G^T X (m x n fp32,
+// dS, dense form: dS[p] = dA[i][column of p] from dA = G^T X (m x n fp32,
 // computed on the matrix cores); one wave per row, coalesced along the row.
-template <typename CT>
-__global__ __launch_bounds__(256) void k_ds_gather(const int32_t* __restrict__ row_ptr, const CT* __restrict__ col,
-                                                   const float* __restrict__ dA, int m, int n, float* __restrict__ dS) {
+template <int PAT>
+__global__ __launch_bounds__(256) void k_ds_gather(SPattern P, const float* __restrict__ dA, int m, int n,
+                                                   float* __restrict__ dS) {
   const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (i >= m) return;
   const float* __restrict__ row = dA + (int64_t)i * n;
-  for (int64_t p = row_ptr[i] + lane_id(); p < row_ptr[i + 1]; p += 64) {
-    const int j = (int)col[p];
+  int64_t rs, re;
+  pat_row<PAT>(P, i, rs, re);
+  for (int64_t p = rs + lane_id(); p < re; p += 64) {
+    const int j = pat_col<PAT>(P, i, rs, p);
     dS[p] = (j >= 0 && j < n) ? row[j] : 0.f;
   }
 }
 
-template <typename CT>
-static void launch_sddmm_ct(int lp, const int32_t* rp, const CT* col, const uint16_t* Gt, const uint16_t* Xt, int m,
-                            int n, int ldt, float* dS, hipStream_t s) {
+// The CSR form of a 2:4 pattern (row_ptr[i] = i n / 2; columns from the
+// metadata), for building the transposed layer.
+__global__ __launch_bounds__(256) void k_nm_to_csr(const uint32_t* __restrict__ meta, int m, int n,
+                                                   int32_t* __restrict__ row_ptr, int32_t* __restrict__ col) {
+  SPattern P = {};
+  P.meta = meta;
+  P.n = n;
+  const int64_t total = (int64_t)m * (n >> 1);
+  for (int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x; p < total; p += (int64_t)gridDim.x * 256) {
+    const int i = (int)(p / (n >> 1));
+    col[p] = pat_col<PAT_NM24>(P, i, (int64_t)i * (n >> 1), p);
+  }
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i <= m; i += (int64_t)gridDim.x * 256)
+    row_ptr[i] = (int32_t)(i * (n >> 1));
+}
+
+hss_status launch_nm_to_csr(int m, int n, const uint32_t* meta, int32_t* row_ptr, int32_t* col, hipStream_t s) {
+  const int64_t total = (int64_t)m * (n >> 1);
+  const unsigned grid = (unsigned)std::min<int64_t>((total + 255) / 256, 8192);
+  hipLaunchKernelGGL(k_nm_to_csr, dim3(grid), dim3(256), 0, s, meta, m, n, row_ptr, col);
+  return hipGetLastError() == hipSuccess ? HSS_OK : HSS_ERR_HIP;
+}
+
+template <int PAT>
+static void launch_sddmm_pat(int lp, const SPattern& P, const uint16_t* Gt, const uint16_t* Xt, int m, int n, int ldt,
+                             float* dS, hipStream_t s) {
   const dim3 grid((unsigned)((m + 3) / 4)), block(256);
   switch (lp) {
-    case 1: hipLaunchKernelGGL((k_sddmm<1, CT>), grid, block, 0, s, rp, col, Gt, Xt, m, n, ldt, dS); break;
-    case 2: hipLaunchKernelGGL((k_sddmm<2, CT>), grid, block, 0, s, rp, col, Gt, Xt, m, n, ldt, dS); break;
-    case 4: hipLaunchKernelGGL((k_sddmm<4, CT>), grid, block, 0, s, rp, col, Gt, Xt, m, n, ldt, dS); break;
-    case 8: hipLaunchKernelGGL((k_sddmm<8, CT>), grid, block, 0, s, rp, col, Gt, Xt, m, n, ldt, dS); break;
-    case 16: hipLaunchKernelGGL((k_sddmm<16, CT>), grid, block, 0, s, rp, col, Gt, Xt, m, n, ldt, dS); break;
-    case 32: hipLaunchKernelGGL((k_sddmm<32, CT>), grid, block, 0, s, rp, col, Gt, Xt, m, n, ldt, dS); break;
-    default: hipLaunchKernelGGL((k_sddmm<64, CT>), grid, block, 0, s, rp, col, Gt, Xt, m, n, ldt, dS); break;
+    case 1: hipLaunchKernelGGL((k_sddmm<1, PAT>), grid, block, 0, s, P, Gt, Xt, m, n, ldt, dS); break;
+    case 2: hipLaunchKernelGGL((k_sddmm<2, PAT>), grid, block, 0, s, P, Gt, Xt, m, n, ldt, dS); break;
+    case 4: hipLaunchKernelGGL((k_sddmm<4, PAT>), grid, block, 0, s, P, Gt, Xt, m, n, ldt, dS); break;
+    case 8: hipLaunchKernelGGL((k_sddmm<8, PAT>), grid, block, 0, s, P, Gt, Xt, m, n, ldt, dS); break;
+    case 16: hipLaunchKernelGGL((k_sddmm<16, PAT>), grid, block, 0, s, P, Gt, Xt, m, n, ldt, dS); break;
+    case 32: hipLaunchKernelGGL((k_sddmm<32, PAT>), grid, block, 0, s, P, Gt, Xt, m, n, ldt, dS); break;
+    default: hipLaunchKernelGGL((k_sddmm<64, PAT>), grid, block, 0, s, P, Gt, Xt, m, n, ldt, dS); break;
   }
 }
 
@@ -191,7 +254,8 @@ hss_status launch_grad(const hss_matrix* A, int b, const void* X, const void* G,
   const int m = A->m, n = A->n, r = A->r;
   const uint16_t* Xb = static_cast<const uint16_t*>(X);
   const uint16_t* Gb = static_cast<const uint16_t*>(G);
-  const bool want_s = dS && A->nnz > 0, want_u = dU && r > 0, want_v = dVt && r > 0;
+  const int64_t stored = A->fmt == HSS_FMT_2OF4 ? (int64_t)m * (n / 2) : A->nnz;
+  const bool want_s = dS && stored > 0, want_u = dU && r > 0, want_v = dVt && r > 0;
   if (want_v || want_s) launch_xt(Xb, b, n, p.ldt, Xt, s);
   if (want_u || want_s) launch_xt(Gb, b, m, p.ldt, Gt, s);
   if (want_u) {
@@ -203,23 +267,33 @@ hss_status launch_grad(const hss_matrix* A, int b, const void* X, const void* G,
     launch_gemm_bf16(b, r, m, Gb, m, Ut, p.ldu, Pt, p.ldt, true, part, s);
     launch_gemm_bf16(n, r, b, Xt, p.ldt, Pt, p.ldt, dVt, n, false, part, s);
   }
-  if (want_s && ds_dense(b)) {
-    float* dA = reinterpret_cast<float*>(base + p.da);
-    launch_gemm_bf16(n, m, b, Xt, p.ldt, Gt, p.ldt, dA, n, false, part, s);
-    const dim3 grid((unsigned)((m + 3) / 4));
-    if (A->flags & HSS_COL16)
-      hipLaunchKernelGGL(k_ds_gather<uint16_t>, grid, dim3(256), 0, s, A->row_ptr,
-                         reinterpret_cast<const uint16_t*>(A->col_idx), dA, m, n, dS);
-    else
-      hipLaunchKernelGGL(k_ds_gather<int32_t>, grid, dim3(256), 0, s, A->row_ptr, A->col_idx, dA, m, n, dS);
-  } else if (want_s) {
-    int lp = 1;
-    while (lp < 64 && lp * 2 <= (p.ldt >> 3)) lp *= 2;
-    if (A->flags & HSS_COL16)
-      launch_sddmm_ct<uint16_t>(lp, A->row_ptr, reinterpret_cast<const uint16_t*>(A->col_idx), Gt, Xt, m, n, p.ldt,
-                                dS, s);
-    else
-      launch_sddmm_ct<int32_t>(lp, A->row_ptr, A->col_idx, Gt, Xt, m, n, p.ldt, dS, s);
+  if (want_s) {
+    SPattern P = {};
+    P.row_ptr = A->row_ptr;
+    P.col = A->col_idx;
+    P.meta = A->nm_meta;
+    P.n = n;
+    const int pat = A->fmt == HSS_FMT_2OF4 ? PAT_NM24 : ((A->flags & HSS_COL16) ? PAT_CSR16 : PAT_CSR32);
+    if (ds_dense(b)) {
+      float* dA = reinterpret_cast<float*>(base + p.da);
+      launch_gemm_bf16(n, m, b, Xt, p.ldt, Gt, p.ldt, dA, n, false, part, s);
+      const dim3 grid((unsigned)((m + 3) / 4));
+      if (pat == PAT_NM24)
+        hipLaunchKernelGGL(k_ds_gather<PAT_NM24>, grid, dim3(256), 0, s, P, dA, m, n, dS);
+      else if (pat == PAT_CSR16)
+        hipLaunchKernelGGL(k_ds_gather<PAT_CSR16>, grid, dim3(256), 0, s, P, dA, m, n, dS);
+      else
+        hipLaunchKernelGGL(k_ds_gather<PAT_CSR32>, grid, dim3(256), 0, s, P, dA, m, n, dS);
+    } else {
+      int lp = 1;
+      while (lp < 64 && lp * 2 <= (p.ldt >> 3)) lp *= 2;
+      if (pat == PAT_NM24)
+        launch_sddmm_pat<PAT_NM24>(lp, P, Gt, Xt, m, n, p.ldt, dS, s);
+      else if (pat == PAT_CSR16)
+        launch_sddmm_pat<PAT_CSR16>(lp, P, Gt, Xt, m, n, p.ldt, dS, s);
+      else
+        launch_sddmm_pat<PAT_CSR32>(lp, P, Gt, Xt, m, n, p.ldt, dS, s);
+    }
   }
   return hipGetLastError() == hipSuccess ? HSS_OK : HSS_ERR_HIP;
 }

@@ -13,6 +13,7 @@ hss_status csr_transpose_host(int m, int n, const int32_t* row_ptr, const int32_
 hss_status launch_gather_values(int dt, int64_t nnz, const void* values, const int32_t* perm, void* values_t,
                                 hipStream_t s);
 hss_status launch_transpose(int dt, int rows, int cols, const void* src, void* dst, hipStream_t s);
+hss_status launch_nm_to_csr(int m, int n, const uint32_t* meta, int32_t* row_ptr, int32_t* col, hipStream_t s);
 }  // namespace hss
 
 namespace {
@@ -239,7 +240,7 @@ hss_status hss_hier_pack(hss_dtype dt, int32_t m, int32_t n, const int32_t* r, c
 static hss_status check_grad(const hss_matrix* A, int32_t b) {
   hss_status st = check_matrix(A, b);
   if (st != HSS_OK) return st;
-  if (A->fmt != HSS_FMT_CSR || A->dtype != HSS_BF16 || (A->flags & HSS_DQ4)) return HSS_ERR_UNSUPPORTED;
+  if (A->dtype != HSS_BF16 || (A->flags & HSS_DQ4)) return HSS_ERR_UNSUPPORTED;
   const int64_t ldt = ((int64_t)b + 7) / 8 * 8;
   if ((int64_t)A->n * ldt * 2 >= kLimit || (int64_t)A->m * ldt * 2 >= kLimit) return HSS_ERR_UNSUPPORTED;
   return HSS_OK;
@@ -260,7 +261,8 @@ hss_status hss_grad(const hss_matrix* A, int32_t b, const void* X, const void* G
   if (!X || !G) return HSS_ERR_INVALID_ARG;
   const int64_t m = A->m, n = A->n, r = A->r;
   const size_t xb = (size_t)b * n * 2, gb = (size_t)b * m * 2;
-  const size_t sb = (size_t)A->nnz * 4, ub = (size_t)m * r * 4, vb = (size_t)r * n * 4;
+  const int64_t stored = A->fmt == HSS_FMT_2OF4 ? m * (n / 2) : A->nnz;
+  const size_t sb = (size_t)stored * 4, ub = (size_t)m * r * 4, vb = (size_t)r * n * 4;
   const void* outs[3] = {dS, dU, dVt};
   const size_t ob[3] = {sb, ub, vb};
   for (int k = 0; k < 3; ++k) {
@@ -303,4 +305,13 @@ hss_status hss_transpose(hss_dtype dt, int32_t rows, int32_t cols, const void* s
   const size_t bytes = (size_t)rows * cols * dsize(dt);
   if (overlap(src, bytes, dst, bytes)) return HSS_ERR_INVALID_ARG;
   return hss::launch_transpose(dt, rows, cols, src, dst, stream);
+}
+
+hss_status hss_nm24_to_csr(int32_t m, int32_t n, const uint32_t* nm_meta, int32_t* row_ptr, int32_t* col_idx,
+                           hipStream_t stream) {
+  if (m < 1 || n < 4 || n % 4 != 0 || (int64_t)m * n >= kLimit || !nm_meta || !row_ptr || !col_idx)
+    return HSS_ERR_INVALID_ARG;
+  const size_t cb = (size_t)m * (n / 2) * 4, rb = (size_t)(m + 1) * 4;
+  if (overlap(row_ptr, rb, col_idx, cb)) return HSS_ERR_INVALID_ARG;
+  return hss::launch_nm_to_csr(m, n, nm_meta, row_ptr, col_idx, stream);
 }

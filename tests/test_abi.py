@@ -29,7 +29,8 @@ def test_header_declares_the_boundary():
                  "hss_apply_group", "hss_apply_group_workspace_size",
                  "hss_get_error", "hss_topk_count", "hss_status_string", "hss_version",
                  "hss_rcm_order", "hss_concentration", "hss_concentration_workspace_size", "hss_hier_pack",
-                 "hss_grad", "hss_grad_workspace_size", "hss_csr_transpose", "hss_gather_values", "hss_transpose"):
+                 "hss_grad", "hss_grad_workspace_size", "hss_csr_transpose", "hss_gather_values", "hss_transpose",
+                 "hss_nm24_to_csr"):
         assert must in names
 
 
@@ -224,7 +225,7 @@ def test_backward_entry_points_reject_bad_arguments(hl):
              wsb=1 << 24):
         return lib.hss_grad(ctypes.byref(s), b, X, G, dS, dU, dVt, ws, wsb, None)
     assert grad(_matrix(hl, dtype=0)) == UNS                            # fp32 layer
-    assert grad(_matrix(hl, fmt=1, nm_values=FAKE, nm_meta=FAKE)) == UNS  # 2:4 layer
+    assert grad(_matrix(hl, flags=2, r=0, U=None, Vt=None, dq_codes=FAKE, dq_levels=FAKE)) == UNS  # D + S
     assert grad(_matrix(hl, m=0)) == INV
     assert grad(_matrix(hl), b=0) == INV
     assert grad(_matrix(hl), X=None) == INV
@@ -244,3 +245,7 @@ def test_backward_entry_points_reject_bad_arguments(hl):
     assert lib.hss_transpose(9, 4, 4, FAKE, FAKE * 2, None) == INV
     assert lib.hss_transpose(1, 4, 4, FAKE, FAKE + 8, None) == INV             # overlapping
     assert lib.hss_transpose(1, 2_200_000, 2, FAKE, FAKE * 64, None) == INV    # too many rows for the grid
+    assert lib.hss_nm24_to_csr(0, 8, FAKE, FAKE * 2, FAKE * 3, None) == INV
+    assert lib.hss_nm24_to_csr(4, 6, FAKE, FAKE * 2, FAKE * 3, None) == INV     # n % 4 != 0
+    assert lib.hss_nm24_to_csr(4, 8, None, FAKE * 2, FAKE * 3, None) == INV
+    assert lib.hss_nm24_to_csr(4, 8, FAKE, FAKE * 2, FAKE * 2 + 8, None) == INV  # overlapping outputs

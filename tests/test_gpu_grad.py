@@ -188,3 +188,42 @@ def test_ds_routes_forced(H, monkeypatch, route, b):
     out = H.hss_grad(A, to_dev(X, DT), to_dev(G, DT))
     _within(out["dS"].cpu().numpy(), g["dS"], N["dS"], "dS")
     _within(out["dU"].cpu().numpy(), g["dU"], N["dU"], "dU")
+
+
+def _layer24(H, m, n, r, seed):
+    import torch
+    W = syn.random_matrix(m, n, DT, seed=seed, kind="normal")
+    s = O.split_24(W, DT)
+    U, V = syn.factors(m, n, r, DT, seed)
+    A = H.HSSMatrix("2:4", m, n, torch.bfloat16, U=to_dev(U, DT), Vt=to_dev(np.ascontiguousarray(V.T), DT),
+                    nm_values=to_dev(s["nm_values"], DT), nm_meta=_raw(s["nm_meta"].view(np.int32)))
+    rp, ci = O.nm24_pattern(m, n, s["nm_meta"])
+    S64 = O.dense_from_24(m, n, s["nm_values"], s["nm_meta"], DT)
+    return A, s, rp, ci, S64, O.widen(U, DT), O.widen(V, DT)
+
+
+@pytest.mark.parametrize("m,n,r,b,route", [(40, 64, 8, 5, None), (130, 96, 16, 33, None), (70, 128, 4, 16, "dense"),
+                                           (64, 256, 16, 600, None), (64, 256, 16, 600, "sparse")])
+def test_backward_2of4_matches_oracle(H, monkeypatch, m, n, r, b, route):
+    """A 2:4 layer: dS laid out as nm_values, dU, dV, and dX through the
+    transposed layer built from the 2:4 positions."""
+    if route:
+        monkeypatch.setenv("HSS_GRAD_DS_ROUTE", route)
+    A, s, rp, ci, S64, U64, V64 = _layer24(H, m, n, r, 100 + m + b)
+    X = syn.random_matrix(b, n, DT, seed=101, kind="normal", scale=1.0)
+    G = syn.random_matrix(b, m, DT, seed=102, kind="normal", scale=1.0)
+    X64, G64 = O.widen(X, DT), O.widen(G, DT)
+    g = O.backward(m, n, rp, ci, S64, U64, V64, X64, G64)
+    N = O.backward_normalisers(m, n, rp, ci, S64, U64, V64, X64, G64)
+    out = H.hss_backward(A, to_dev(X, DT), to_dev(G, DT))
+    _within(out["dS"].cpu().numpy(), g["dS"], N["dS"], "dS")
+    _within(out["dU"].cpu().numpy(), g["dU"], N["dU"], "dU")
+    _within(out["dVt"].cpu().numpy().T, g["dV"], N["dV"], "dV")
+    _within(O.widen(to_host(out["dX"]), DT), g["dX"], N["dX"], "dX")
+
+
+def test_nm24_to_csr_is_the_oracle_pattern(H):
+    m, n = 33, 160
+    A, s, rp, ci, *_ = _layer24(H, m, n, 4, 7)
+    drp, dci = H.hss_nm24_to_csr(A)
+    assert np.array_equal(drp.cpu().numpy(), rp) and np.array_equal(dci.cpu().numpy(), ci)
