@@ -207,10 +207,11 @@ hss_status hss_apply_workspace_size(const hss_matrix* A, int32_t b, size_t* byte
  * workspace, then every stored entry gathers its X^T row; fp32
  * accumulation).  Otherwise one fused kernel per 8 columns.  The
  * environment variable HSS_CSR_BATCH_ROUTE = decode | spmm | densify forces
- * a bf16 CSR call onto that route where the route supports the matrix (for
- * comparing them); the workspace size covers every route.  HSS_DQ4 matrices always run the
- * fused dense-and-sparse kernel (up to 8 columns per pass; no workspace:
- * hss_apply_workspace_size returns 0 and ws may be NULL).
+ * a bf16 CSR call with b >= 2 onto that route where the route supports the
+ * matrix (for comparing them); the workspace size covers every route.
+ * HSS_DQ4 matrices always run the fused dense-and-sparse kernel (up to 8
+ * columns per pass; no workspace: hss_apply_workspace_size returns 0 and ws
+ * may be NULL).
  * Returns HSS_ERR_INVALID_ARG for: A or X or Y null, unknown fmt/dtype,
  *   unknown flags (or HSS_COL16 with a 2:4 matrix or n > 65536; HSS_DQ4 with
  *   a 2:4 matrix, odd n or null dq arrays),

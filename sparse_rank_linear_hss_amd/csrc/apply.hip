@@ -60,6 +60,7 @@ enum Route { R_DECODE = 0, R_SPMM = 1, R_MFMA = 2 };
 static constexpr int kSpmmMinCols = 8, kSpmmMaxCols = 128;
 
 static Route batch_route(const hss_matrix* A, int b) {
+  if (b < 2) return R_DECODE;  // one column: always the fused decode kernel (no environment lookup)
   const bool sp = spmm_supported(A, b), mf = mfma_supported(A, b);
   if (const char* e = std::getenv("HSS_CSR_BATCH_ROUTE")) {
     if (!std::strcmp(e, "decode")) return R_DECODE;
