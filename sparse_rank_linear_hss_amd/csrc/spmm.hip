@@ -160,6 +160,17 @@ __device__ __forceinline__ void fma8(float (&acc)[8], float v, const u32x4& x) {
   acc[7] = fmaf(v, bf16hi(x.w), acc[7]);
 }
 
+// acc += v x (8 columns) when on, else acc unchanged (a masked entry adds
+// nothing, whatever its x).
+__device__ __forceinline__ void fma8_if(float (&acc)[8], float v, const u32x4& x, bool on) {
+  float t[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) t[k] = acc[k];
+  fma8(t, v, x);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = on ? t[k] : acc[k];
+}
+
 template <typename CT>
 __device__ __forceinline__ int load_col(__amdgpu_buffer_rsrc_t rc, int64_t p) {
   if constexpr (sizeof(CT) == 4)
@@ -172,10 +183,37 @@ __device__ __forceinline__ int load_col(__amdgpu_buffer_rsrc_t rc, int64_t p) {
 // Dynamic LDS: r x 8G bf16 (T's tile, transposed).
 template <int G, typename CT>
 __global__ __launch_bounds__(kSpWaves * 64) void k_spmm(SpmmArgs a) {
-  constexpr int BT = 8 * G, S = 64 / G;
+  constexpr int BT = 8 * G, S = 64 / G, D = kSpDepth;
   extern __shared__ uint16_t ts[];
   const int c0 = blockIdx.y * BT;
   const int r = a.r;
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const int i = blockIdx.x * kSpWaves + wave;
+  const bool live = i < a.m;  // wave-uniform
+  const int g = lane % G, s = lane / G;
+
+  // This wave's row bounds, then the first D entries of each lane and the
+  // first D values of its U row, issued before the T tile's staging and
+  // barrier so that their round trips overlap it.  The loads are
+  // unconditional (buffer resources: past an array's end they read zeros;
+  // past the row they read entries of the next one, masked out below).
+  const int64_t rs = live ? a.row_ptr[i] : 0, re = live ? a.row_ptr[i + 1] : 0;
+  const __amdgpu_buffer_rsrc_t rc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.col), 0, (int)(a.nnz * sizeof(CT)), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.val), 0, (int)(a.nnz * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t ru =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.U), 0, (int)((int64_t)a.m * r * 2), 0x00020000);
+  int64_t p = rs + s;
+  int c1[D];
+  float v1[D], u1[D];
+#pragma unroll
+  for (int k = 0; k < D; ++k) {
+    c1[k] = load_col<CT>(rc, p + k * S);
+    v1[k] = bf16lo(__builtin_amdgcn_raw_buffer_load_b16(rv, (int)((p + k * S) * 2), 0, 0));
+    u1[k] = bf16lo(__builtin_amdgcn_raw_buffer_load_b16(ru, (int)(((int64_t)(live ? i : 0) * r + s + k * S) * 2), 0, 0));
+  }
+
   // T tile -> LDS: ts[l * BT + c] = T^T[l][c0 + c], 16-byte pieces, four
   // loads in flight per thread before their stores.  Columns at or past b
   // (inside the last 8-column piece, or a whole piece past ldt) feed only
@@ -202,39 +240,39 @@ __global__ __launch_bounds__(kSpWaves * 64) void k_spmm(SpmmArgs a) {
     }
   }
   __syncthreads();
-
-  const int wave = threadIdx.x >> 6, lane = lane_id();
-  const int i = blockIdx.x * kSpWaves + wave;
-  if (i >= a.m) return;  // wave-uniform; no barrier follows
-  const int g = lane % G, s = lane / G;
+  if (!live) return;  // no barrier follows
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 
-  // sparse part: entries p = rs + s + S t, four per lane in flight (the
-  // column loads, then the gathers), then the row's tail one at a time
-  const int64_t rs = a.row_ptr[i], re = a.row_ptr[i + 1];
+  // sparse part: entries p = rs + s + S t in order -- the prefetched D
+  // (masked past the row), then D per lane in flight (the column loads, then
+  // the gathers), then the row's tail one at a time
   if (re > rs) {
-    const __amdgpu_buffer_rsrc_t rc =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.col), 0, (int)(a.nnz * sizeof(CT)), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.val), 0, (int)(a.nnz * 2), 0x00020000);
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(a.Xt), 0, (int)((int64_t)a.n * a.ldt * 2), 0x00020000);
     const int xoff = (c0 + 8 * g) * 2;
-    int64_t p = rs + s;
-    for (; p + (kSpDepth - 1) * S < re; p += kSpDepth * S) {
-      int c[kSpDepth];
-      float v[kSpDepth];
+    {
+      u32x4 x[D];
 #pragma unroll
-      for (int k = 0; k < kSpDepth; ++k) {
+      for (int k = 0; k < D; ++k)
+        x[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, c1[k] * a.ldt * 2 + xoff, 0, 0));
+#pragma unroll
+      for (int k = 0; k < D; ++k) fma8_if(acc, v1[k], x[k], p + k * S < re);
+      p += D * S;
+    }
+    for (; p + (D - 1) * S < re; p += D * S) {
+      int c[D];
+      float v[D];
+#pragma unroll
+      for (int k = 0; k < D; ++k) {
         c[k] = load_col<CT>(rc, p + k * S);
         v[k] = bf16lo(__builtin_amdgcn_raw_buffer_load_b16(rv, (int)((p + k * S) * 2), 0, 0));
       }
-      u32x4 x[kSpDepth];
+      u32x4 x[D];
 #pragma unroll
-      for (int k = 0; k < kSpDepth; ++k)
+      for (int k = 0; k < D; ++k)
         x[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, c[k] * a.ldt * 2 + xoff, 0, 0));
 #pragma unroll
-      for (int k = 0; k < kSpDepth; ++k) fma8(acc, v[k], x[k]);
+      for (int k = 0; k < D; ++k) fma8(acc, v[k], x[k]);
     }
     for (; p < re; p += S) {
       const int c = load_col<CT>(rc, p);
@@ -243,20 +281,31 @@ __global__ __launch_bounds__(kSpWaves * 64) void k_spmm(SpmmArgs a) {
       fma8(acc, v, x);
     }
   }
-  // low-rank part: l = s + S t, U from memory, T from LDS
+  // low-rank part: l = s + S t in order, U from memory (the first D
+  // prefetched), T from LDS
   if (r > 0) {
-    const uint16_t* __restrict__ ur = a.U + (int64_t)i * r;
-    int l = s;
-    for (; l + (kSpDepth - 1) * S < r; l += kSpDepth * S) {
-      float u[kSpDepth];
-      u32x4 x[kSpDepth];
+    {
+      u32x4 x[D];
 #pragma unroll
-      for (int k = 0; k < kSpDepth; ++k) {
+      for (int k = 0; k < D; ++k) {
+        const int l = s + k * S;
+        x[k] = *reinterpret_cast<const u32x4*>(ts + (l < r ? l : r - 1) * BT + 8 * g);
+      }
+#pragma unroll
+      for (int k = 0; k < D; ++k) fma8_if(acc, u1[k], x[k], s + k * S < r);
+    }
+    const uint16_t* __restrict__ ur = a.U + (int64_t)i * r;
+    int l = s + D * S;
+    for (; l + (D - 1) * S < r; l += D * S) {
+      float u[D];
+      u32x4 x[D];
+#pragma unroll
+      for (int k = 0; k < D; ++k) {
         u[k] = bf16lo(ur[l + k * S]);
         x[k] = *reinterpret_cast<const u32x4*>(ts + (l + k * S) * BT + 8 * g);
       }
 #pragma unroll
-      for (int k = 0; k < kSpDepth; ++k) fma8(acc, u[k], x[k]);
+      for (int k = 0; k < D; ++k) fma8(acc, u[k], x[k]);
     }
     for (; l < r; l += S) fma8(acc, bf16lo(ur[l]), *reinterpret_cast<const u32x4*>(ts + l * BT + 8 * g));
   }
@@ -300,6 +349,7 @@ bool spmm_supported(const hss_matrix* A, int b) {
   if ((size_t)A->r * 8 * 2 > kSpLdsMax) return false;                    // T tile of 8 columns must fit
   if ((int64_t)A->n * spmm_ldt(b) * 2 >= ((int64_t)1 << 31)) return false; // 32-bit buffer offsets
   if (A->nnz * 4 >= ((int64_t)1 << 31)) return false;
+  if ((int64_t)A->m * A->r * 2 >= ((int64_t)1 << 31)) return false;  // U through a 32-bit buffer offset
   return true;
 }
 
