@@ -183,7 +183,10 @@ __device__ __forceinline__ int load_col(__amdgpu_buffer_rsrc_t rc, int64_t p) {
 // Dynamic LDS: r x 8G bf16 (T's tile, transposed).
 template <int G, typename CT>
 __global__ __launch_bounds__(kSpWaves * 64) void k_spmm(SpmmArgs a) {
-  constexpr int BT = 8 * G, S = 64 / G, D = kSpDepth;
+  // entries per lane in flight: 8 with 32 slots (16 columns: a 4096-wide
+  // 5 % row then needs one round of loads per lane; measured 17.0 -> 15.7
+  // us), else 4 (8 was slower at 32-128 columns)
+  constexpr int BT = 8 * G, S = 64 / G, D = G == 2 ? 2 * kSpDepth : kSpDepth;
   extern __shared__ uint16_t ts[];
   const int c0 = blockIdx.y * BT;
   const int r = a.r;
