@@ -55,9 +55,10 @@ def _check(Y_dev, dtype, Yref, N):
 
 CASES = [
     # (m, n, b, k): n % 32 == 0 (16-byte code chunks) and not (bytes one at a time), n % 8 != 0
-    # (one column per pass), several passes of 8 columns, ragged rows at 2 rows per wave, no outliers
+    # (one column per pass), several passes of 8 columns, ragged rows at 1 and 2 rows per wave
+    # (m >= 2048: one column, several), no outliers
     (64, 64, 1, None), (130, 96, 3, None), (257, 512, 8, None), (300, 1024, 17, None),
-    (2050, 256, 1, None), (40, 38, 2, None), (96, 4096, 1, None), (33, 128, 5, 0),
+    (2050, 256, 1, None), (2051, 256, 3, None), (40, 38, 2, None), (96, 4096, 1, None), (33, 128, 5, 0),
 ]
 
 
