@@ -202,7 +202,7 @@ hss_status hss_apply_workspace_size(const hss_matrix* A, int32_t b, size_t* byte
  * matrix cores (T^T = X V and Y = [X | T^T] [S | U]^T as MFMA GEMMs with
  * fp32 accumulation; T is rounded to bf16 once, between the two; a CSR S is
  * first expanded into a dense bf16 copy inside the workspace, so the
- * workspace then holds m*n*2 more bytes).  bf16 CSR with 8 <= b <= 128 runs
+ * workspace then holds m*n*2 more bytes).  bf16 CSR with 5 <= b <= 128 runs
  * the gather SpMM (T = X V rounded to bf16 once, X^T staged in the
  * workspace, then every stored entry gathers its X^T row; fp32
  * accumulation).  Otherwise one fused kernel per 8 columns.  The

@@ -14,7 +14,7 @@
 //   dense-and-sparse     HSS_DQ4 matrices (decode.hip, k_decode_dq): the
 //                        quantised dense part and the CSR outliers, up to 8
 //                        columns per pass, no workspace.
-//   gather SpMM          bf16 CSR from 8 to 128 columns (and beyond where S
+//   gather SpMM          bf16 CSR from 5 to 128 columns (and beyond where S
 //   (spmm.hip)           cannot be densified): S read once, X^T rows
 //                        gathered per entry, T from a small prologue.
 //
@@ -53,11 +53,12 @@ enum Route { R_DECODE = 0, R_SPMM = 1, R_MFMA = 2 };
 // Default batch range of the gather SpMM for bf16 CSR: below it the fused
 // decode passes, above it S densified for the matrix cores.  Measured on the
 // 4096 x 4096 5 % rank-256 layer (decode / densify vs gather): b = 4 decode
-// 12.9 vs 19.7 us; b = 8 decode 21.3 vs 17.9 us; b = 16 42.1 vs 23.7 us;
-// b = 64 169 / 58.5 vs 45.7 us; b = 128 densify 64.9 vs 56.4 us; b = 256
-// densify 74.8 vs 77.2 us.  The 8192 x 8192 3 % rank-512 layer agrees:
-// b = 64 densify 137 vs 87 us, b = 128 156 vs 139 us, b = 256 164 vs 203 us.
-static constexpr int kSpmmMinCols = 8, kSpmmMaxCols = 128;
+// 12.7 vs 13.0 us; b = 5 decode 16.6 vs 13.1 us; b = 8 decode 20.1 vs 13.6
+// us; b = 16 39.8 vs 15.7 us; b = 64 169 / 58.4 vs 36.7 us; b = 128 densify
+// 64.8 vs 57.3 us; b = 256 densify 74.6 vs 75.1 us.  The 8192 x 8192 3 %
+// rank-512 layer agrees: b = 64 densify 137 vs 85 us, b = 128 156 vs 139 us,
+// b = 256 164 vs 203 us.
+static constexpr int kSpmmMinCols = 5, kSpmmMaxCols = 128;
 
 static Route batch_route(const hss_matrix* A, int b) {
   if (b < 2) return R_DECODE;  // one column: always the fused decode kernel (no environment lookup)
