@@ -871,9 +871,9 @@ static void run_gemm(GemmArgs g, int amode, float* part, hipStream_t s) {
   }
 }
 
-// T (b x r, bf16, row c = X[c] . V) on the matrix cores; `part` holds at
-// least t_gemm_part_bytes(A, b) bytes of split-K partials.
-void launch_t_gemm(const hss_matrix* A, int b, const void* X, uint16_t* Tb, float* part, hipStream_t s) {
+// T (b x r, bf16, row c = X[c] . V) on the matrix cores; `part` holds the
+// split-K partials (sized by plan_mfma).
+static void launch_t_gemm(const hss_matrix* A, int b, const void* X, uint16_t* Tb, float* part, hipStream_t s) {
   const int n = A->n, r = A->r;
   const uint16_t* Xb = static_cast<const uint16_t*>(X);
   GemmArgs g = {};
@@ -903,7 +903,6 @@ void launch_tt_gemm(const hss_matrix* A, int b, const void* X, uint16_t* Tt, int
   run_gemm(g, A_DENSE, part, s);
 }
 
-size_t t_gemm_part_bytes(const hss_matrix* A, int b) { return A->r > 0 ? gemm_part_bytes(A->r, b, A->n, 0) : 0; }
 // A general bf16 GEMM on the matrix cores: C[n * ldc + m] = sum_k A[m][k]
 // B[n][k] for m < M, n < N, k < K (A: M rows, B: N rows, both K-contiguous
 // with strides lda, ldb), fp32 accumulation, stored as bf16 (RNE) or fp32.

@@ -22,7 +22,6 @@
 // slot partial sums are added by an xor butterfly in a fixed order, so the
 // result does not depend on scheduling.
 #include <algorithm>
-#include <cstdlib>
 
 #include "hss_internal.h"
 
