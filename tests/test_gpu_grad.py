@@ -227,3 +227,23 @@ def test_nm24_to_csr_is_the_oracle_pattern(H):
     A, s, rp, ci, *_ = _layer24(H, m, n, 4, 7)
     drp, dci = H.hss_nm24_to_csr(A)
     assert np.array_equal(drp.cpu().numpy(), rp) and np.array_equal(dci.cpu().numpy(), ci)
+
+
+def test_fp32_input_gradient_through_transposed_layer(H):
+    """An fp32 CSR layer (hss_grad is bf16-only): dX = G A still comes from
+    the transposed layer's apply, within the fp32 bar."""
+    import torch
+    m, n, r, b = 90, 70, 6, 4
+    W = syn.random_matrix(m, n, O.F32, seed=5, kind="t3")
+    ref = O.split_csr(W, O.F32, O.topk_count(m, n, 5, 100))
+    U, V = syn.factors(m, n, r, O.F32, 5)
+    A = H.HSSMatrix("csr", m, n, torch.float32, U=to_dev(U, O.F32), Vt=to_dev(np.ascontiguousarray(V.T), O.F32),
+                    row_ptr=_raw(ref["row_ptr"]), col_idx=_raw(ref["col_idx"]), values=to_dev(ref["values"], O.F32),
+                    nnz=len(ref["col_idx"]))
+    G = syn.random_matrix(b, m, O.F32, seed=6, kind="normal", scale=1.0)
+    dX = H.hss_apply(H.hss_transposed_layer(A), to_dev(G, O.F32)).cpu().numpy()
+    S64 = O.dense_from_csr(m, n, ref["row_ptr"], ref["col_idx"], ref["values"], O.F32)
+    A64 = S64 + O.widen(U, O.F32) @ O.widen(V, O.F32).T
+    G64 = O.widen(G, O.F32)
+    err = O.max_normalised_error(dX.astype(np.float64), G64 @ A64, np.abs(G64) @ np.abs(A64))
+    assert err <= O.TOL[O.F32], f"max normalised error {err:.3e}"
