@@ -37,7 +37,7 @@ Sources (web pages; section names as printed on each page)
           quantised with non-uniform levels); section "4.有効性の検証方法と成果":
           the sparse part is about 0.5 % of the weights.
 
-Readings where the pages are silent (each is listed in the design notes):
+Readings where the pages are silent or ambiguous:
 * k = floor(m*n*num/den) in exact integer arithmetic (the worked example
   prints 52,428 for 5 % of 1,048,576, i.e. floor).
 * Ties at the threshold go to the lower row-major linear index; exactly k
