@@ -60,6 +60,8 @@ CASES = [
     # (m, n, r, b): ragged shapes, batches below / at / across the 8-column padding and K tails
     (5, 13, 2, 3), (65, 129, 7, 9), (130, 1000, 64, 16), (257, 512, 1, 33), (300, 640, 128, 64),
     (100, 77, 5, 65), (520, 512, 256, 130), (64, 256, 16, 600), (2053, 256, 16, 5),
+    # one column: the reductions over the batch are GEMMs with K = 1
+    (40, 64, 4, 1),
 ]
 
 
@@ -203,6 +205,7 @@ def _layer24(H, m, n, r, seed):
 
 
 @pytest.mark.parametrize("m,n,r,b,route", [(40, 64, 8, 5, None), (130, 96, 16, 33, None), (70, 128, 4, 16, "dense"),
+                                           (36, 32, 4, 1, None),
                                            (64, 256, 16, 600, None), (64, 256, 16, 600, "sparse")])
 def test_backward_2of4_matches_oracle(H, monkeypatch, m, n, r, b, route):
     """A 2:4 layer: dS laid out as nm_values, dU, dV, and dX through the
