@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhss.so")
 ARCH = os.environ.get("HSS_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["hss_api.cpp", "split.hip", "apply.hip", "decode.hip", "mfma.hip", "hier.hip", "spmm.hip", "grad.hip"]
+SOURCES = ["hss_api.cpp", "split.hip", "apply.hip", "decode.hip", "mfma.hip", "hier.hip", "spmm.hip", "grad.hip", "nm_mma.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

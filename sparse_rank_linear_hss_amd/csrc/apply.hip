@@ -8,7 +8,7 @@
 //   decode (decode.hip)  up to 8 columns per launch: one fused kernel that
 //                        streams S, U and V^T once (HBM-bound regime); fp32
 //                        and narrow batches.
-//   mfma (mfma.hip)      bf16 with b >= 16 (2:4) or b > 128 (CSR): the
+//   mfma (mfma.hip)      bf16 2:4 beyond 64 columns, CSR beyond 128: the
 //                        low-rank products are dense contractions and run on
 //                        the matrix cores, S expanded into the same GEMM.
 //   dense-and-sparse     HSS_DQ4 matrices (decode.hip, k_decode_dq): the
@@ -17,10 +17,13 @@
 //   gather SpMM          bf16 CSR from 5 to 128 columns (and beyond where S
 //   (spmm.hip)           cannot be densified): S read once, X^T rows
 //                        gathered per entry, T from a small prologue.
+//   sparse matrix cores  bf16 2:4 from 3 to 64 columns (n % 128 == 0): S's
+//   (nm_mma.hip)         values and metadata fed to v_smfmac as stored, T
+//                        from a small prologue.
 //
-// The environment variable HSS_CSR_BATCH_ROUTE = decode | spmm | densify
-// forces the route of a bf16 CSR batch (where that route supports it), for
-// measuring one against another.
+// The environment variable HSS_CSR_BATCH_ROUTE = decode | spmm | densify |
+// smfmac forces the route of a bf16 batch (where that route supports it),
+// for measuring one against another.
 #include <cstdlib>
 #include <cstring>
 
@@ -48,7 +51,19 @@ bool spmm_supported(const hss_matrix* A, int b);
 size_t spmm_ws_bytes(const hss_matrix* A, int b);
 hss_status launch_spmm(const hss_matrix* A, int b, const void* X, void* Y, void* ws, hipStream_t s);
 
-enum Route { R_DECODE = 0, R_SPMM = 1, R_MFMA = 2 };
+bool nm_mma_supported(const hss_matrix* A, int b);
+size_t nm_mma_ws_bytes(const hss_matrix* A, int b);
+hss_status launch_nm_mma(const hss_matrix* A, int b, const void* X, void* Y, void* ws, hipStream_t s);
+
+enum Route { R_DECODE = 0, R_SPMM = 1, R_MFMA = 2, R_NM = 3 };
+
+// Default batch range of the 2:4 route on the sparse matrix cores (it runs
+// from 2 columns when forced).  Measured on the 11008 x 4096 rank-64 layer
+// (decode / densify vs sparse matrix cores, us): b = 2 decode 20.2 vs 21.9;
+// b = 3 decode 25.3 vs 22.1; b = 4 decode 27.4 vs 22.4; b = 8 decode 46.0 vs
+// 23.6; b = 16 densify 46.0 vs 26.7; b = 32 densify 48.5 vs 38.7; b = 64
+// densify 60.3 vs 57.3.
+static constexpr int kNmMinColsDefault = 3;
 
 // Default batch range of the gather SpMM for bf16 CSR: below it the fused
 // decode passes, above it S densified for the matrix cores.  Measured on the
@@ -60,14 +75,19 @@ enum Route { R_DECODE = 0, R_SPMM = 1, R_MFMA = 2 };
 // b = 256 164 vs 203 us.
 static constexpr int kSpmmMinCols = 5, kSpmmMaxCols = 128;
 
-static Route batch_route(const hss_matrix* A, int b) {
+// X: the call's input (the sparse matrix cores need it 16-byte aligned), or
+// null when sizing a workspace.
+static Route batch_route(const hss_matrix* A, int b, const void* X) {
   if (b < 2) return R_DECODE;  // one column: always the fused decode kernel (no environment lookup)
   const bool sp = spmm_supported(A, b), mf = mfma_supported(A, b);
+  const bool nm = nm_mma_supported(A, b) && (uintptr_t)X % 16 == 0;
   if (const char* e = std::getenv("HSS_CSR_BATCH_ROUTE")) {
     if (!std::strcmp(e, "decode")) return R_DECODE;
     if (!std::strcmp(e, "spmm") && sp) return R_SPMM;
     if (!std::strcmp(e, "densify") && mf) return R_MFMA;
+    if (!std::strcmp(e, "smfmac") && nm) return R_NM;
   }
+  if (nm && b >= kNmMinColsDefault) return R_NM;
   if (sp && b >= kSpmmMinCols && (b <= kSpmmMaxCols || !mf)) return R_SPMM;
   if (mf) return R_MFMA;
   return R_DECODE;
@@ -82,8 +102,10 @@ size_t apply_ws_bytes(const hss_matrix* A, int b) {
   const size_t dec = decode_t_bytes(A);
   const size_t mf = mfma_supported(A, b) ? mfma_ws_bytes(A, b) : 0;
   const size_t sp = spmm_supported(A, b) ? spmm_ws_bytes(A, b) : 0;
+  const size_t nm = nm_mma_supported(A, b) ? nm_mma_ws_bytes(A, b) : 0;
   size_t mx = dec > mf ? dec : mf;
   mx = mx > sp ? mx : sp;
+  mx = mx > nm ? mx : nm;
   return decode_ctl_bytes() + mx;
 }
 
@@ -100,7 +122,8 @@ hss_status launch_apply(const hss_matrix* A, int b, const void* X, void* Y, void
     }
     return hipGetLastError() == hipSuccess ? HSS_OK : HSS_ERR_HIP;
   }
-  const Route route = batch_route(A, b);
+  const Route route = batch_route(A, b, X);
+  if (route == R_NM) return launch_nm_mma(A, b, X, Y, static_cast<char*>(ws) + decode_ctl_bytes(), stream);
   if (route == R_MFMA) return launch_mfma(A, b, X, Y, static_cast<char*>(ws) + decode_ctl_bytes(), stream);
   if (route == R_SPMM) return launch_spmm(A, b, X, Y, static_cast<char*>(ws) + decode_ctl_bytes(), stream);
   const size_t es = A->dtype == HSS_F32 ? 4 : 2;
@@ -131,7 +154,7 @@ size_t apply_group_ws_bytes(const hss_matrix* const* A, int G, int b) {
 hss_status launch_apply_group(const hss_matrix* const* A, int G, int b, const void* X, void* const* Y, void* ws,
                               hipStream_t stream) {
   bool any_mfma = false;  // (or dense-and-sparse: those run one by one too)
-  for (int g = 0; g < G; ++g) any_mfma = any_mfma || batch_route(A[g], b) != R_DECODE || is_dq(A[g]);
+  for (int g = 0; g < G; ++g) any_mfma = any_mfma || batch_route(A[g], b, X) != R_DECODE || is_dq(A[g]);
   if (any_mfma) {
     for (int g = 0; g < G; ++g) {
       const hss_status st = launch_apply(A[g], b, X, Y[g], ws, stream);

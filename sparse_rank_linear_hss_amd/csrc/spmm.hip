@@ -6,7 +6,7 @@
 // W ~ S + U V^T.  Here, for b columns:
 //
 //   T^T = (X V)^T                   (r x ldt, bf16) k_spmm_prep on the vector
-//                                   units for b <= 16, else launch_tt_gemm on
+//                                   units for b <= 64, else launch_tt_gemm on
 //                                   the matrix cores
 //   X^T                             (n x ldt) a plain transpose (k_spmm_prep's
 //                                   other blocks, or k_xt)
@@ -80,16 +80,17 @@ __global__ __launch_bounds__(256) void k_xt(const uint16_t* __restrict__ X, int 
     xt_item(X, b, n, ldt, t, Xt);
 }
 
-// Prologue for b <= 16 in one launch.  Blocks 0 .. r-1: T^T row l = V^T[l] .
+// Prologue for b <= 64 in one launch.  Blocks 0 .. r-1: T^T row l = V^T[l] .
 // X^T (b values), the block's threads striding over n (8 columns per step
 // with 16-byte loads when VEC), 16 batch columns per pass; each column's sum
 // is reduced within waves by DPP and the four wave sums added in order, so
-// the result does not depend on scheduling; stored as bf16.  Blocks r and
-// up: X^T, as k_xt.
+// the result does not depend on scheduling; stored as bf16 at
+// T[l * sl + c * sc] (sl = ldt, sc = 1: T^T; sl = 1, sc = row stride: T).
+// Blocks r and up: X^T, as k_xt.
 template <bool VEC>
 __global__ __launch_bounds__(256) void k_spmm_prep(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Vt,
-                                                   int b, int n, int r, int ldt, uint16_t* __restrict__ Tt,
-                                                   uint16_t* __restrict__ Xt) {
+                                                   int b, int n, int r, int ldt, int sl, int sc,
+                                                   uint16_t* __restrict__ Tt, uint16_t* __restrict__ Xt) {
   if ((int)blockIdx.x >= r) {
     const int64_t total = (int64_t)n * (ldt >> 3);
     const int64_t nb = gridDim.x - r;
@@ -142,7 +143,8 @@ __global__ __launch_bounds__(256) void k_spmm_prep(const uint16_t* __restrict__ 
     __syncthreads();
     if (threadIdx.x < 16 && cb + (int)threadIdx.x < b) {
       const int cc = threadIdx.x;
-      Tt[(int64_t)l * ldt + cb + cc] = f32_to_bf16(((red[0][cc] + red[1][cc]) + red[2][cc]) + red[3][cc]);
+      Tt[(int64_t)l * sl + (int64_t)(cb + cc) * sc] =
+          f32_to_bf16(((red[0][cc] + red[1][cc]) + red[2][cc]) + red[3][cc]);
     }
     __syncthreads();
   }
@@ -405,11 +407,11 @@ hss_status launch_spmm(const hss_matrix* A, int b, const void* X, void* Y, void*
     if (grid > 0) {
       const uint16_t* Vt = static_cast<const uint16_t*>(A->Vt);
       if (vec)
-        hipLaunchKernelGGL(k_spmm_prep<true>, dim3(grid), dim3(256), 0, s, Xb, Vt, b, A->n, A->r, a.ldt,
-                           const_cast<uint16_t*>(a.Tt), const_cast<uint16_t*>(a.Xt));
+        hipLaunchKernelGGL(k_spmm_prep<true>, dim3(grid), dim3(256), 0, s, Xb, Vt, b, A->n, A->r, a.ldt, a.ldt,
+                           1, const_cast<uint16_t*>(a.Tt), const_cast<uint16_t*>(a.Xt));
       else
-        hipLaunchKernelGGL(k_spmm_prep<false>, dim3(grid), dim3(256), 0, s, Xb, Vt, b, A->n, A->r, a.ldt,
-                           const_cast<uint16_t*>(a.Tt), const_cast<uint16_t*>(a.Xt));
+        hipLaunchKernelGGL(k_spmm_prep<false>, dim3(grid), dim3(256), 0, s, Xb, Vt, b, A->n, A->r, a.ldt, a.ldt,
+                           1, const_cast<uint16_t*>(a.Tt), const_cast<uint16_t*>(a.Xt));
     }
   } else {
     if (xt_blocks > 0)
@@ -426,6 +428,21 @@ hss_status launch_spmm(const hss_matrix* A, int b, const void* X, void* Y, void*
     default: launch_spmm_g<8>(a, col16, s); break;
   }
   return hipGetLastError() == hipSuccess ? HSS_OK : HSS_ERR_HIP;
+}
+
+// T = X V (b x r, bf16, row c at T + c * ldt, ldt >= r) on the vector units
+// alone (k_spmm_prep's T blocks), b <= 64.
+void launch_t_vec(const hss_matrix* A, int b, const void* X, int ldt, uint16_t* T, hipStream_t s) {
+  if (A->r == 0) return;
+  const uint16_t* Xb = static_cast<const uint16_t*>(X);
+  const uint16_t* Vt = static_cast<const uint16_t*>(A->Vt);
+  const bool vec = A->n % 8 == 0 && (uintptr_t)X % 16 == 0 && (uintptr_t)A->Vt % 16 == 0;
+  if (vec)
+    hipLaunchKernelGGL(k_spmm_prep<true>, dim3(A->r), dim3(256), 0, s, Xb, Vt, b, A->n, A->r, 8, 1, ldt, T,
+                       static_cast<uint16_t*>(nullptr));
+  else
+    hipLaunchKernelGGL(k_spmm_prep<false>, dim3(A->r), dim3(256), 0, s, Xb, Vt, b, A->n, A->r, 8, 1, ldt, T,
+                       static_cast<uint16_t*>(nullptr));
 }
 
 }  // namespace hss

@@ -196,6 +196,7 @@ def test_apply_local_fallback_is_bitwise_identical(H, monkeypatch, fmt, dtype, b
     CSR column: the T rows come from the row blocks themselves, 4, 2 and 1 per
     block at m = 100, 300 and 1030)."""
     n, r = 512, 40
+    monkeypatch.setenv("HSS_CSR_BATCH_ROUTE", "decode")   # the fused kernel's hand-off is what is tested
     W = syn.random_matrix(m, n, dtype, seed=21, kind="t3")
     ref = O.split_csr(W, dtype, O.topk_count(m, n, 5, 100)) if fmt == "csr" else O.split_24(W, dtype)
     U, V = _factors(m, n, r, dtype, 22)
