@@ -59,10 +59,9 @@ enum Route { R_DECODE = 0, R_SPMM = 1, R_MFMA = 2, R_NM = 3 };
 
 // Default batch range of the 2:4 route on the sparse matrix cores (it runs
 // from 2 columns when forced).  Measured on the 11008 x 4096 rank-64 layer
-// (decode / densify vs sparse matrix cores, us): b = 2 decode 20.2 vs 21.9;
-// b = 3 decode 25.3 vs 22.1; b = 4 decode 27.4 vs 22.4; b = 8 decode 46.0 vs
-// 23.6; b = 16 densify 46.0 vs 26.7; b = 32 densify 48.5 vs 38.7; b = 64
-// densify 60.3 vs 57.3.
+// (decode / densify vs sparse matrix cores, us): b = 2 decode 20.2 vs 20.1;
+// b = 3 decode 25.3 vs 20.3; b = 8 decode 46.0 vs 21.3; b = 16 densify 46.0
+// vs 22.9; b = 32 densify 48.5 vs 31.2; b = 64 densify 60.1 vs 45.7.
 static constexpr int kNmMinColsDefault = 3;
 
 // Default batch range of the gather SpMM for bf16 CSR: below it the fused

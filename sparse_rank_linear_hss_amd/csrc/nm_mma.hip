@@ -30,15 +30,17 @@
 // 8h + 7, the word's bits 16h .. 16h + 15).  Inverting kappa, B half hb then
 // needs X columns 8 hb .. 8 hb + 7 and 16 + 8 hb .. 16 + 8 hb + 7 of the chunk.
 //
-// One block owns 32 rows; its 4 waves take the row's 128-column stages in
-// turn (wave w: stages w, w + 4, ...), two stages in flight per lane.  A
-// stage's values are loaded row-contiguous (each load instruction covers 8
-// whole 128-byte row segments) and passed through the wave's own LDS area
-// into the operand layout; X comes through a buffer resource (rows past b
-// read as zeros).  The low-rank part T U^T runs on the dense
-// v_mfma_f32_32x32x16_bf16 into the same accumulators (16 rank columns per
-// step, steps dealt round robin to the waves).  The 4 partial tiles are added
-// through LDS in wave order, so the result does not depend on scheduling.
+// One block owns 64 rows (two 32-row tiles, so each X piece it reads from
+// L2 serves both) and one 32-column tile of the batch; its 4 waves take the
+// rows' 128-column stages in turn (wave w: stages w, w + 4, ...), two stages
+// in flight per lane.  A stage's values are loaded row-contiguous (each load
+// instruction covers 8 whole 128-byte row segments) and passed through the
+// wave's own LDS area into the operand layout; X comes through a buffer
+// resource (rows past b read as zeros).  The low-rank part T U^T runs on the
+// dense v_mfma_f32_32x32x16_bf16 into the same accumulators (16 rank
+// columns per step, steps dealt round robin to the waves).  The 4 partial
+// tiles are added through LDS in wave order, so the result does not depend
+// on scheduling.
 #include "hss_internal.h"
 
 namespace hss {
@@ -50,7 +52,7 @@ typedef __bf16 nm_bf16x16 __attribute__((ext_vector_type(16)));
 typedef float nm_f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t nm_u32x8 __attribute__((ext_vector_type(8)));
 
-static constexpr int kNmBlockWaves = 4;         // waves per 32-row block
+static constexpr int kNmBlockWaves = 4;         // waves (turns at the stages) per block
 static constexpr int kNmStride = 36;            // LDS floats per column of a partial tile
 static constexpr int kNmMinCols = 2, kNmMaxCols = 64;
 // T on the vector units up to this many columns (k_spmm_prep's T blocks, one
@@ -58,6 +60,12 @@ static constexpr int kNmMinCols = 2, kNmMaxCols = 64;
 // k_nm_t's 4 blocks take 7.0 us), on the matrix cores above (b = 64: 9.8 us
 // against 16.5 us).
 static constexpr int kNmTVecMaxCols = 16;
+// 32-row tiles per block: X, read once per block from L2, serves 64 rows.
+// Measured on the 11008 x 4096 layer (one tile vs two, us): b = 2 22.0 vs
+// 20.2, b = 8 23.6 vs 21.4, b = 32 38.8 vs 31.3, b = 64 57.3 vs 45.6 (three
+// tiles need 250 VGPRs: one wave per SIMD; 8 waves per block: 23.0 us at
+// b = 8).
+static constexpr int kNmRowTiles = 2;
 
 static size_t align256_nm(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -75,17 +83,17 @@ struct NmArgs {
 // T's row stride: 16-byte rows.
 static int nm_tld(int r) { return (r + 7) & ~7; }
 
-// One stage of a lane: 4 chunks (128 columns) of its wave's 32 rows.  v:
-// the rows' values loaded row-contiguous (lane l: row 8 k + l / 8, bytes
-// 16 (l % 8) .. of the stage's 128-byte row segment, k = 0..3), so each load
-// instruction covers 8 whole 128-byte segments; mw: the 4 metadata words of
-// row l % 32; x: per 32-column tile j and chunk c, the two 16-byte pieces of
-// X row 32 j + l % 32 its B operand takes.
-template <int NT>
+// One stage of a lane: 4 chunks (128 columns) of its block's 32 RT rows.
+// v: the rows' values loaded row-contiguous (for row tile t, lane l: row
+// 32 t + 8 k + l / 8, bytes 16 (l % 8) .. of the stage's 128-byte row
+// segment, k = 0..3), so each load instruction covers 8 whole 128-byte row
+// segments; mw: the 4 metadata words of row 32 t + l % 32; x: per chunk c,
+// the two 16-byte pieces of X row 32 by + l % 32 its B operand takes.
+template <int RT>
 struct NmStage {
-  u32x4 v[4];
-  u32x4 mw;
-  u32x4 x[NT][4][2];
+  u32x4 v[RT][4];
+  u32x4 mw[RT];
+  u32x4 x[4][2];
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t nm_rsrc(const uint16_t* p, int64_t bytes) {
@@ -101,118 +109,126 @@ __device__ __forceinline__ u32x4 nm_bload(__amdgpu_buffer_rsrc_t r, uint32_t off
 static constexpr int kNmRowBytes = 144;
 static_assert(kNmRowBytes * 32 == 32 * kNmStride * 4, "staging area = the wave's reduction tile");
 
-// WV waves per 32-row block, each a contiguous range of its stages; D stages
-// in flight per lane; NT tiles of 32 columns.
-template <int NT, int D, int WV>
+// Block (bx, by): rows 32 RT bx .. (RT tiles of 32), batch columns 32 by ..
+// 32 by + 31.  WV waves take its 128-column stages in turn (wave w: stages
+// w, w + WV, ...); D stages in flight per lane.
+template <int RT, int D, int WV>
 __global__ __launch_bounds__(64 * WV) void k_nm_smfmac(NmArgs a) {
   constexpr int kNmWaves = WV, kNmThreads = 64 * WV;
   // Each wave's slice is its staging area during the main loop and its
-  // partial tile afterwards (only that wave touches it in between).
-  __shared__ __align__(16) float red[kNmWaves][32][kNmStride];
+  // partial tiles afterwards (only that wave touches it in between).
+  __shared__ __align__(16) float red[kNmWaves][32 * RT][kNmStride];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int i = lane & 31, h = lane >> 5;
-  const int row0 = blockIdx.x * 32;
-  const int row = min(row0 + i, a.m - 1);  // rows past m compute a copy of row m - 1, never stored
+  const int row0 = blockIdx.x * 32 * RT, c0 = blockIdx.y * 32;
   const int n = a.n, nst = n >> 7;         // 128-column stages (n % 128 == 0)
   const int per = (nst + kNmWaves - 1) / kNmWaves;  // stages per wave
-  // stage k of wave w: w + WV k, so the block's waves read adjacent 128-byte
-  // segments of the same rows together
   char* const stg = reinterpret_cast<char*>(&red[w][0][0]);
-
-  nm_f32x16 acc[NT];
+  int rows[RT];  // this lane's operand row of each tile (rows past m: a copy of row m - 1, never stored)
 #pragma unroll
-  for (int j = 0; j < NT; ++j) acc[j] = nm_f32x16{};
+  for (int t = 0; t < RT; ++t) rows[t] = min(row0 + 32 * t + i, a.m - 1);
+
+  nm_f32x16 acc[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) acc[t] = nm_f32x16{};
 
   // Low-rank part: step s covers rank columns 16 s .. 16 s + 15 (half h: 8 of
   // them).  Its loads go out first, so waiting for them waits for nothing else.
   // Rank columns past r are zeros on both sides.
   const int nus = (a.r + 15) >> 4;
-  const __amdgpu_buffer_rsrc_t rt = nm_rsrc(a.T, (int64_t)a.b * a.tld * 2);
-  auto u_load = [&](int s, u32x4& ua, u32x4 (&ub)[NT]) {
+  const __amdgpu_buffer_rsrc_t rtb = nm_rsrc(a.T, (int64_t)a.b * a.tld * 2);
+  auto u_load = [&](int s, u32x4 (&ua)[RT], u32x4& ub) {
     const int col = 16 * s + 8 * h;
     const int nv = min(max(a.r - col, 0), 8);  // valid columns of this half step
     const int cc = nv > 0 ? col : 0;
-    const uint16_t* up = a.U + (int64_t)row * a.r + cc;
-    if (a.uvec) {
-      ua = *reinterpret_cast<const u32x4*>(up);
-    } else {
-      uint32_t e[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) e[q] = up[q < nv ? q : 0];
-      ua = u32x4{e[0] | e[1] << 16, e[2] | e[3] << 16, e[4] | e[5] << 16, e[6] | e[7] << 16};
+    for (int t = 0; t < RT; ++t) {
+      const uint16_t* up = a.U + (int64_t)rows[t] * a.r + cc;
+      if (a.uvec) {
+        ua[t] = *reinterpret_cast<const u32x4*>(up);
+      } else {
+        uint32_t e[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) e[q] = up[q < nv ? q : 0];
+        ua[t] = u32x4{e[0] | e[1] << 16, e[2] | e[3] << 16, e[4] | e[5] << 16, e[6] | e[7] << 16};
+      }
     }
-#pragma unroll
-    for (int j = 0; j < NT; ++j)
-      ub[j] = nm_bload(rt, 2u * ((uint32_t)(32 * j + i) * (uint32_t)a.tld + (uint32_t)cc));
+    ub = nm_bload(rtb, 2u * ((uint32_t)(c0 + i) * (uint32_t)a.tld + (uint32_t)cc));
     if (nv < 8) {
       uint32_t mk[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) mk[q] = (2 * q < nv ? 0xffffu : 0u) | (2 * q + 1 < nv ? 0xffff0000u : 0u);
       const u32x4 m4 = {mk[0], mk[1], mk[2], mk[3]};
-      ua &= m4;
 #pragma unroll
-      for (int j = 0; j < NT; ++j) ub[j] &= m4;
+      for (int t = 0; t < RT; ++t) ua[t] &= m4;
+      ub &= m4;
     }
   };
-  auto u_mma = [&](const u32x4& ua, const u32x4 (&ub)[NT]) {
+  auto u_mma = [&](const u32x4 (&ua)[RT], const u32x4& ub) {
 #pragma unroll
-    for (int j = 0; j < NT; ++j)
-      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(nm_bf16x8, ua),
-                                                       __builtin_bit_cast(nm_bf16x8, ub[j]), acc[j], 0, 0, 0);
+    for (int t = 0; t < RT; ++t)
+      acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(nm_bf16x8, ua[t]),
+                                                       __builtin_bit_cast(nm_bf16x8, ub), acc[t], 0, 0, 0);
   };
-  u32x4 ua0, ub0[NT];
+  u32x4 ua0[RT], ub0;
   if (w < nus) u_load(w, ua0, ub0);  // wave-uniform
 
   // Sparse part.
   const __amdgpu_buffer_rsrc_t rx = nm_rsrc(a.X, (int64_t)a.b * n * 2);
   const int vr = lane >> 3, vb = 16 * (lane & 7);  // coalesced value loads: row 8 k + vr, byte vb
-  const char* __restrict__ vbase[4];
+  const char* __restrict__ vbase[RT][4];
+  const uint32_t* __restrict__ mrow[RT];
 #pragma unroll
-  for (int k = 0; k < 4; ++k)
-    vbase[k] = reinterpret_cast<const char*>(a.vals) + (int64_t)min(row0 + 8 * k + vr, a.m - 1) * n + vb;
-  const uint32_t* __restrict__ mrow = a.meta + (int64_t)row * (n >> 5);
-  uint32_t xo[NT];
+  for (int t = 0; t < RT; ++t) {
 #pragma unroll
-  for (int j = 0; j < NT; ++j) xo[j] = 2u * ((uint32_t)(32 * j + i) * (uint32_t)n + 8u * (uint32_t)h);
+    for (int k = 0; k < 4; ++k)
+      vbase[t][k] = reinterpret_cast<const char*>(a.vals) + (int64_t)min(row0 + 32 * t + 8 * k + vr, a.m - 1) * n + vb;
+    mrow[t] = a.meta + (int64_t)rows[t] * (n >> 5);
+  }
+  const uint32_t xo = 2u * ((uint32_t)(c0 + i) * (uint32_t)n + 8u * (uint32_t)h);
 
   // Stage k of this wave (clamped into the matrix: loads are unconditional).
-  auto issue = [&](NmStage<NT>& st, int k) {
+  auto issue = [&](NmStage<RT>& st, int k) {
     const int sg = min(w + kNmWaves * k, nst - 1);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) st.v[q] = *reinterpret_cast<const u32x4*>(vbase[q] + 128 * (int64_t)sg);
-    st.mw = *reinterpret_cast<const u32x4*>(mrow + 4 * sg);
+    for (int t = 0; t < RT; ++t) {
 #pragma unroll
-    for (int j = 0; j < NT; ++j)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint32_t o = xo[j] + 256u * (uint32_t)sg + 64u * (uint32_t)c;
-        st.x[j][c][0] = nm_bload(rx, o);
-        st.x[j][c][1] = nm_bload(rx, o + 32u);
-      }
-  };
-  auto consume = [&](const NmStage<NT>& st, bool ok) {
-    // the stage's rows into the staging area, then each chunk's A operand
-    // (row l % 32, the chunk's values 8 h .. 8 h + 7) back out
-#pragma unroll
-    for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4*>(stg + (8 * q + vr) * kNmRowBytes + vb) = st.v[q];
-    const uint32_t mwv[4] = {st.mw.x, st.mw.y, st.mw.z, st.mw.w};
+      for (int q = 0; q < 4; ++q) st.v[t][q] = *reinterpret_cast<const u32x4*>(vbase[t][q] + 128 * (int64_t)sg);
+      st.mw[t] = *reinterpret_cast<const u32x4*>(mrow[t] + 4 * sg);
+    }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      u32x4 av = *reinterpret_cast<const u32x4*>(stg + i * kNmRowBytes + 32 * c + 16 * h);
-      av = ok ? av : z;  // a stage past the range adds zeros
-      const int idx = (int)(mwv[c] >> (16 * h));
+      const uint32_t o = xo + 256u * (uint32_t)sg + 64u * (uint32_t)c;
+      st.x[c][0] = nm_bload(rx, o);
+      st.x[c][1] = nm_bload(rx, o + 32u);
+    }
+  };
+  auto consume = [&](const NmStage<RT>& st, bool ok) {
+    // the stage's rows into the staging area, then each chunk's A operand
+    // (row l % 32 of a tile, the chunk's values 8 h .. 8 h + 7) back out
 #pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const nm_u32x8 bx = {st.x[j][c][0].x, st.x[j][c][0].y, st.x[j][c][0].z, st.x[j][c][0].w,
-                             st.x[j][c][1].x, st.x[j][c][1].y, st.x[j][c][1].z, st.x[j][c][1].w};
-        acc[j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(__builtin_bit_cast(nm_bf16x8, av),
-                                                           __builtin_bit_cast(nm_bf16x16, bx), acc[j], idx, 0, 0);
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<u32x4*>(stg + (32 * t + 8 * q + vr) * kNmRowBytes + vb) = st.v[t][q];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const nm_u32x8 bx = {st.x[c][0].x, st.x[c][0].y, st.x[c][0].z, st.x[c][0].w,
+                           st.x[c][1].x, st.x[c][1].y, st.x[c][1].z, st.x[c][1].w};
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        u32x4 av = *reinterpret_cast<const u32x4*>(stg + (32 * t + i) * kNmRowBytes + 32 * c + 16 * h);
+        av = ok ? av : z;  // a stage past the range adds zeros
+        const uint32_t mwv[4] = {st.mw[t].x, st.mw[t].y, st.mw[t].z, st.mw[t].w};
+        const int idx = (int)(mwv[c] >> (16 * h));
+        acc[t] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(__builtin_bit_cast(nm_bf16x8, av),
+                                                           __builtin_bit_cast(nm_bf16x16, bx), acc[t], idx, 0, 0);
       }
     }
   };
 
-  NmStage<NT> st[D];
+  NmStage<RT> st[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) {
     issue(st[d], d);
@@ -232,30 +248,30 @@ __global__ __launch_bounds__(64 * WV) void k_nm_smfmac(NmArgs a) {
   }
   // further low-rank steps (r > 16 * waves)
   for (int s = w + kNmWaves; s < nus; s += kNmWaves) {
-    u32x4 ua, ub[NT];
+    u32x4 ua[RT], ub;
     u_load(s, ua, ub);
     u_mma(ua, ub);
   }
 
-  // Partial tiles added in wave order; column c of tile j to Y[c][row0 ..].
+  // Partial tiles added in wave order; column c0 + cc to Y[c0 + cc][row0 ..].
 #pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    if (j > 0) __syncthreads();
+  for (int t = 0; t < RT; ++t)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const float4 q = {acc[j][4 * g], acc[j][4 * g + 1], acc[j][4 * g + 2], acc[j][4 * g + 3]};
-      *reinterpret_cast<float4*>(&red[w][i][8 * g + 4 * h]) = q;
+      const float4 q = {acc[t][4 * g], acc[t][4 * g + 1], acc[t][4 * g + 2], acc[t][4 * g + 3]};
+      *reinterpret_cast<float4*>(&red[w][32 * t + i][8 * g + 4 * h]) = q;
     }
-    __syncthreads();
-    const int rr = threadIdx.x & 31;
-    for (int cc = threadIdx.x >> 5; cc < 32; cc += kNmThreads / 32) {
-      float sum = red[0][cc][rr];
+  __syncthreads();
+  const int rr = threadIdx.x & 31;
 #pragma unroll
-      for (int ww = 1; ww < kNmWaves; ++ww) sum += red[ww][cc][rr];
-      const int c = 32 * j + cc;
-      if (c < a.b && row0 + rr < a.m) a.Y[(int64_t)c * a.m + row0 + rr] = f32_to_bf16(sum);
+  for (int t = 0; t < RT; ++t)
+    for (int cc = threadIdx.x >> 5; cc < 32; cc += kNmThreads / 32) {
+      float sum = red[0][32 * t + cc][rr];
+#pragma unroll
+      for (int ww = 1; ww < kNmWaves; ++ww) sum += red[ww][32 * t + cc][rr];
+      const int c = c0 + cc, row = row0 + 32 * t + rr;
+      if (c < a.b && row < a.m) a.Y[(int64_t)c * a.m + row] = f32_to_bf16(sum);
     }
-  }
 }
 
 // T = X V for this route on the matrix cores, one block per 16 x 16 tile of
@@ -332,10 +348,10 @@ size_t nm_mma_ws_bytes(const hss_matrix* A, int b) {
   return A->r > 0 ? align256_nm(sizeof(uint16_t) * (size_t)b * nm_tld(A->r)) : 0;
 }
 
-template <int NT>
-static void launch_nm_nt(const NmArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)((a.m + 31) / 32));
-  hipLaunchKernelGGL((k_nm_smfmac<NT, 2, kNmBlockWaves>), grid, dim3(64 * kNmBlockWaves), 0, s, a);
+template <int RT>
+static void launch_nm_rt(const NmArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)((a.m + 32 * RT - 1) / (32 * RT)), (unsigned)((a.b + 31) / 32));
+  hipLaunchKernelGGL((k_nm_smfmac<RT, 2, kNmBlockWaves>), grid, dim3(64 * kNmBlockWaves), 0, s, a);
 }
 
 // X must be 16-byte aligned (the caller routes other X elsewhere).
@@ -361,10 +377,7 @@ hss_status launch_nm_mma(const hss_matrix* A, int b, const void* X, void* Y, voi
     const dim3 grid((unsigned)((A->r + 15) / 16), (unsigned)((b + 15) / 16));
     hipLaunchKernelGGL(k_nm_t, grid, dim3(64 * kNmTWaves), 0, s, t);
   }
-  if (b <= 32)
-    launch_nm_nt<1>(a, s);
-  else
-    launch_nm_nt<2>(a, s);
+  launch_nm_rt<kNmRowTiles>(a, s);
   return hipGetLastError() == hipSuccess ? HSS_OK : HSS_ERR_HIP;
 }
 
