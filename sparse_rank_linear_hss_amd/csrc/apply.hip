@@ -14,10 +14,10 @@
 //   dense-and-sparse     HSS_DQ4 matrices (decode.hip, k_decode_dq): the
 //                        quantised dense part and the CSR outliers, up to 8
 //                        columns per pass, no workspace.
-//   gather SpMM          bf16 CSR from 5 to 128 columns (and beyond where S
+//   gather SpMM          bf16 CSR from 3 to 128 columns (and beyond where S
 //   (spmm.hip)           cannot be densified): S read once, X^T rows
 //                        gathered per entry, T from a small prologue.
-//   sparse matrix cores  bf16 2:4 from 3 to 64 columns (n % 128 == 0): S's
+//   sparse matrix cores  bf16 2:4 from 2 to 64 columns (n % 128 == 0): S's
 //   (nm_mma.hip)         values and metadata fed to v_smfmac as stored, T
 //                        from a small prologue.
 //
@@ -57,22 +57,22 @@ hss_status launch_nm_mma(const hss_matrix* A, int b, const void* X, void* Y, voi
 
 enum Route { R_DECODE = 0, R_SPMM = 1, R_MFMA = 2, R_NM = 3 };
 
-// Default batch range of the 2:4 route on the sparse matrix cores (it runs
-// from 2 columns when forced).  Measured on the 11008 x 4096 rank-64 layer
-// (decode / densify vs sparse matrix cores, us): b = 2 decode 20.2 vs 20.1;
-// b = 3 decode 25.3 vs 20.3; b = 8 decode 46.0 vs 21.3; b = 16 densify 46.0
-// vs 22.9; b = 32 densify 48.5 vs 31.2; b = 64 densify 60.1 vs 45.7.
-static constexpr int kNmMinColsDefault = 3;
+// Default batch range of the 2:4 route on the sparse matrix cores.
+// Measured on the 11008 x 4096 rank-64 layer (decode / densify vs sparse
+// matrix cores, us): b = 2 decode 20.2 vs 18.3; b = 3 decode 25.3 vs 18.5;
+// b = 8 decode 46.0 vs 19.8; b = 16 densify 46.0 vs 23.0; b = 32 densify
+// 48.5 vs 31.2; b = 64 densify 60.1 vs 45.7.
+static constexpr int kNmMinColsDefault = 2;
 
 // Default batch range of the gather SpMM for bf16 CSR: below it the fused
 // decode passes, above it S densified for the matrix cores.  Measured on the
-// 4096 x 4096 5 % rank-256 layer (decode / densify vs gather): b = 4 decode
-// 12.7 vs 13.0 us; b = 5 decode 16.6 vs 13.1 us; b = 8 decode 20.1 vs 13.6
-// us; b = 16 39.8 vs 15.7 us; b = 64 169 / 58.4 vs 36.7 us; b = 128 densify
-// 64.8 vs 57.3 us; b = 256 densify 74.6 vs 75.1 us.  The 8192 x 8192 3 %
-// rank-512 layer agrees: b = 64 densify 137 vs 85 us, b = 128 156 vs 139 us,
-// b = 256 164 vs 203 us.
-static constexpr int kSpmmMinCols = 5, kSpmmMaxCols = 128;
+// 4096 x 4096 5 % rank-256 layer (decode / densify vs gather): b = 2 decode
+// 10.3 vs 11.1 us; b = 3 decode 12.2 vs 11.2 us; b = 4 decode 12.7 vs 11.3
+// us; b = 8 decode 20.1 vs 12.2 us; b = 16 39.8 vs 15.7 us; b = 64 169 /
+// 58.4 vs 36.7 us; b = 128 densify 64.8 vs 57.3 us; b = 256 densify 74.6 vs
+// 75.1 us.  The 8192 x 8192 3 % rank-512 layer agrees: b = 64 densify 137
+// vs 85 us, b = 128 156 vs 139 us, b = 256 164 vs 203 us.
+static constexpr int kSpmmMinCols = 3, kSpmmMaxCols = 128;
 
 // X: the call's input (the sparse matrix cores need it 16-byte aligned), or
 // null when sizing a workspace.

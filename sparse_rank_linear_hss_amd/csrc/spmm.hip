@@ -82,12 +82,13 @@ __global__ __launch_bounds__(256) void k_xt(const uint16_t* __restrict__ X, int 
 
 // Prologue for b <= 64 in one launch.  Blocks 0 .. r-1: T^T row l = V^T[l] .
 // X^T (b values), the block's threads striding over n (8 columns per step
-// with 16-byte loads when VEC), 16 batch columns per pass; each column's sum
+// with 16-byte loads when VEC), CB batch columns per pass (4, 8 or 16: one
+// X load per column and step); each column's sum
 // is reduced within waves by DPP and the four wave sums added in order, so
 // the result does not depend on scheduling; stored as bf16 at
 // T[l * sl + c * sc] (sl = ldt, sc = 1: T^T; sl = 1, sc = row stride: T).
 // Blocks r and up: X^T, as k_xt.
-template <bool VEC>
+template <bool VEC, int CB>
 __global__ __launch_bounds__(256) void k_spmm_prep(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Vt,
                                                    int b, int n, int r, int ldt, int sl, int sc,
                                                    uint16_t* __restrict__ Tt, uint16_t* __restrict__ Xt) {
@@ -101,24 +102,24 @@ __global__ __launch_bounds__(256) void k_spmm_prep(const uint16_t* __restrict__ 
   __shared__ float red[4][16];
   const int l = blockIdx.x, wave = threadIdx.x >> 6;
   const uint16_t* __restrict__ vrow = Vt + (int64_t)l * n;
-  for (int cb = 0; cb < b; cb += 16) {
-    float acc[16];
+  for (int cb = 0; cb < b; cb += CB) {
+    float acc[CB];
 #pragma unroll
-    for (int cc = 0; cc < 16; ++cc) acc[cc] = 0.f;
+    for (int cc = 0; cc < CB; ++cc) acc[cc] = 0.f;
     if constexpr (VEC) {
-      // all 17 loads of a step are unconditional (rows past b re-read row
+      // all CB + 1 loads of a step are unconditional (rows past b re-read row
       // b - 1 and are dropped after), so they are in flight together: a load
       // under a branch would be waited for inside it
       for (int j = 8 * threadIdx.x; j < n; j += 8 * 256) {
         const u32x4 vv = *reinterpret_cast<const u32x4*>(vrow + j);
-        u32x4 xx[16];
+        u32x4 xx[CB];
 #pragma unroll
-        for (int cc = 0; cc < 16; ++cc)
+        for (int cc = 0; cc < CB; ++cc)
           xx[cc] = *reinterpret_cast<const u32x4*>(X + (int64_t)min(cb + cc, b - 1) * n + j);
         const float vf[8] = {bf16lo(vv.x), bf16hi(vv.x), bf16lo(vv.y), bf16hi(vv.y),
                              bf16lo(vv.z), bf16hi(vv.z), bf16lo(vv.w), bf16hi(vv.w)};
 #pragma unroll
-        for (int cc = 0; cc < 16; ++cc) {
+        for (int cc = 0; cc < CB; ++cc) {
           float t = acc[cc];
           t = fmaf(vf[0], bf16lo(xx[cc].x), t); t = fmaf(vf[1], bf16hi(xx[cc].x), t);
           t = fmaf(vf[2], bf16lo(xx[cc].y), t); t = fmaf(vf[3], bf16hi(xx[cc].y), t);
@@ -131,17 +132,17 @@ __global__ __launch_bounds__(256) void k_spmm_prep(const uint16_t* __restrict__ 
       for (int j = threadIdx.x; j < n; j += 256) {
         const float vf = bf16lo(vrow[j]);
 #pragma unroll
-        for (int cc = 0; cc < 16; ++cc)
+        for (int cc = 0; cc < CB; ++cc)
           if (cb + cc < b) acc[cc] = fmaf(vf, bf16lo(X[(int64_t)(cb + cc) * n + j]), acc[cc]);
       }
     }
 #pragma unroll
-    for (int cc = 0; cc < 16; ++cc) {
+    for (int cc = 0; cc < CB; ++cc) {
       const float w = wave_sum(acc[cc]);
       if ((threadIdx.x & 63) == 0) red[wave][cc] = w;
     }
     __syncthreads();
-    if (threadIdx.x < 16 && cb + (int)threadIdx.x < b) {
+    if (threadIdx.x < CB && cb + (int)threadIdx.x < b) {
       const int cc = threadIdx.x;
       Tt[(int64_t)l * sl + (int64_t)(cb + cc) * sc] =
           f32_to_bf16(((red[0][cc] + red[1][cc]) + red[2][cc]) + red[3][cc]);
@@ -374,6 +375,27 @@ static SpmmPlan plan_spmm(const hss_matrix* A, int b) {
 
 size_t spmm_ws_bytes(const hss_matrix* A, int b) { return plan_spmm(A, b).total; }
 
+// k_spmm_prep with the pass width that fits b (fewer X loads per step for
+// narrow batches).
+template <bool VEC>
+static void launch_prep_v(unsigned grid, const uint16_t* X, const uint16_t* Vt, int b, int n, int r, int ldt, int sl,
+                          int sc, uint16_t* T, uint16_t* Xt, hipStream_t s) {
+  if (b <= 4)
+    hipLaunchKernelGGL((k_spmm_prep<VEC, 4>), dim3(grid), dim3(256), 0, s, X, Vt, b, n, r, ldt, sl, sc, T, Xt);
+  else if (b <= 8)
+    hipLaunchKernelGGL((k_spmm_prep<VEC, 8>), dim3(grid), dim3(256), 0, s, X, Vt, b, n, r, ldt, sl, sc, T, Xt);
+  else
+    hipLaunchKernelGGL((k_spmm_prep<VEC, 16>), dim3(grid), dim3(256), 0, s, X, Vt, b, n, r, ldt, sl, sc, T, Xt);
+}
+
+static void launch_prep(bool vec, unsigned grid, const uint16_t* X, const uint16_t* Vt, int b, int n, int r, int ldt,
+                        int sl, int sc, uint16_t* T, uint16_t* Xt, hipStream_t s) {
+  if (vec)
+    launch_prep_v<true>(grid, X, Vt, b, n, r, ldt, sl, sc, T, Xt, s);
+  else
+    launch_prep_v<false>(grid, X, Vt, b, n, r, ldt, sl, sc, T, Xt, s);
+}
+
 template <int G>
 static void launch_spmm_g(const SpmmArgs& a, bool col16, hipStream_t s) {
   const dim3 grid((unsigned)cdiv_(a.m, kSpWaves), (unsigned)cdiv_(a.b, 8 * G));
@@ -404,15 +426,9 @@ hss_status launch_spmm(const hss_matrix* A, int b, const void* X, void* Y, void*
     // T and X^T in one launch
     const bool vec = A->n % 8 == 0 && (uintptr_t)X % 16 == 0 && (A->r == 0 || (uintptr_t)A->Vt % 16 == 0);
     const unsigned grid = (unsigned)(A->r + xt_blocks);
-    if (grid > 0) {
-      const uint16_t* Vt = static_cast<const uint16_t*>(A->Vt);
-      if (vec)
-        hipLaunchKernelGGL(k_spmm_prep<true>, dim3(grid), dim3(256), 0, s, Xb, Vt, b, A->n, A->r, a.ldt, a.ldt,
-                           1, const_cast<uint16_t*>(a.Tt), const_cast<uint16_t*>(a.Xt));
-      else
-        hipLaunchKernelGGL(k_spmm_prep<false>, dim3(grid), dim3(256), 0, s, Xb, Vt, b, A->n, A->r, a.ldt, a.ldt,
-                           1, const_cast<uint16_t*>(a.Tt), const_cast<uint16_t*>(a.Xt));
-    }
+    if (grid > 0)
+      launch_prep(vec, grid, Xb, static_cast<const uint16_t*>(A->Vt), b, A->n, A->r, a.ldt, a.ldt, 1,
+                  const_cast<uint16_t*>(a.Tt), const_cast<uint16_t*>(a.Xt), s);
   } else {
     if (xt_blocks > 0)
       hipLaunchKernelGGL(k_xt, dim3((unsigned)std::min<int64_t>(cdiv_(work, 256), 4096)), dim3(256), 0, s, Xb, b,
@@ -437,12 +453,7 @@ void launch_t_vec(const hss_matrix* A, int b, const void* X, int ldt, uint16_t* 
   const uint16_t* Xb = static_cast<const uint16_t*>(X);
   const uint16_t* Vt = static_cast<const uint16_t*>(A->Vt);
   const bool vec = A->n % 8 == 0 && (uintptr_t)X % 16 == 0 && (uintptr_t)A->Vt % 16 == 0;
-  if (vec)
-    hipLaunchKernelGGL(k_spmm_prep<true>, dim3(A->r), dim3(256), 0, s, Xb, Vt, b, A->n, A->r, 8, 1, ldt, T,
-                       static_cast<uint16_t*>(nullptr));
-  else
-    hipLaunchKernelGGL(k_spmm_prep<false>, dim3(A->r), dim3(256), 0, s, Xb, Vt, b, A->n, A->r, 8, 1, ldt, T,
-                       static_cast<uint16_t*>(nullptr));
+  launch_prep(vec, (unsigned)A->r, Xb, Vt, b, A->n, A->r, 8, 1, ldt, T, nullptr, s);
 }
 
 }  // namespace hss

@@ -71,8 +71,7 @@ def test_smfmac_matches_oracle(H, monkeypatch, case):
     _check(Y1, S64, U64, V64, O.widen(X, DT))
     assert O.bits_equal(to_host(Y1), to_host(H.hss_apply(A, Xd)))      # deterministic
     monkeypatch.delenv("HSS_CSR_BATCH_ROUTE")
-    if b >= 3:                                                          # the default route from 3 to 64 columns
-        assert O.bits_equal(to_host(Y1), to_host(H.hss_apply(A, Xd)))
+    assert O.bits_equal(to_host(Y1), to_host(H.hss_apply(A, Xd)))      # the default route for 2..64 columns
 
 
 @pytest.mark.parametrize("b", [2, 16, 64])
