@@ -379,6 +379,21 @@ def main():
                            "gbs": L3.w_bytes / (ms3 * 1e-3) / 1e9,
                            "hbm_frac": L3.w_bytes / (ms3 * 1e-3) / 1e9 / HBM_PEAK_GBS}
         extra["nm24_11008x4096"] = dict(r3, w_bytes=L3.w_bytes)
+        # the same layer on each route the call can take (sparse matrix cores,
+        # fused decode passes, densified GEMM), us per call
+        routes3 = {}
+        for bq in (2, 8, 16, 64):
+            xq, yq = _acts(wl_nm, bq, 0, 4, L3.m)
+            wsq3 = L3.mats[0].workspace(bq)
+            row = {}
+            for route in ("smfmac", "decode", "densify"):
+                if (route == "decode" and bq > 8) or (route == "densify" and bq < 16):
+                    continue
+                os.environ["HSS_CSR_BATCH_ROUTE"] = route
+                row[route] = _time_graph(_apply_loop(H, L3, xq, yq, wsq3), max(1, steps // 10), 10) * 1e3
+            os.environ.pop("HSS_CSR_BATCH_ROUTE")
+            routes3[f"b{bq}_us"] = row
+        extra["nm24_11008x4096_batch_routes"] = routes3
         del L3, W3
         torch.cuda.empty_cache()
 
