@@ -56,7 +56,7 @@ static constexpr int kNmBlockWaves = 4;         // waves (turns at the stages) p
 static constexpr int kNmStride = 36;            // LDS floats per column of a partial tile
 static constexpr int kNmMinCols = 2, kNmMaxCols = 64;
 // T on the vector units up to this many columns (k_spmm_prep's T blocks, one
-// per rank row: 5.5 us on the 11008 x 4096 rank-64 layer at b = 2 .. 8, where
+// per rank row: 4.5 us on the 11008 x 4096 rank-64 layer at b = 2 .. 8, where
 // k_nm_t's 4 blocks take 7.0 us), on the matrix cores above (b = 64: 9.8 us
 // against 16.5 us).
 static constexpr int kNmTVecMaxCols = 16;
