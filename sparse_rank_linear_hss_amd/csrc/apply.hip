@@ -69,9 +69,10 @@ static constexpr int kNmMinColsDefault = 2;
 // 4096 x 4096 5 % rank-256 layer (decode / densify vs gather): b = 2 decode
 // 10.3 vs 11.1 us; b = 3 decode 12.2 vs 11.2 us; b = 4 decode 12.7 vs 11.3
 // us; b = 8 decode 20.1 vs 12.2 us; b = 16 39.8 vs 15.7 us; b = 64 169 /
-// 58.4 vs 36.7 us; b = 128 densify 64.8 vs 57.3 us; b = 256 densify 74.6 vs
-// 75.1 us.  The 8192 x 8192 3 % rank-512 layer agrees: b = 64 densify 137
-// vs 85 us, b = 128 156 vs 139 us, b = 256 164 vs 203 us.
+// 58.4 vs 33.1 us; b = 128 densify 64.8 vs 41.4 us; b = 256 densify 77.3 vs
+// 61.5 us.  The 8192 x 8192 3 % rank-512 layer: b = 64 densify 137 vs 74 us,
+// b = 128 156 vs 112 us, b = 256 164 vs 202 us (its U part, m r b on the
+// vector units, is 4 times the 4096^2 layer's), so the gather stops at 128.
 static constexpr int kSpmmMinCols = 3, kSpmmMaxCols = 128;
 
 // X: the call's input (the sparse matrix cores need it 16-byte aligned), or

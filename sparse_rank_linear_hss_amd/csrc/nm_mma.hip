@@ -287,8 +287,9 @@ typedef float nm_f32x4 __attribute__((ext_vector_type(4)));
 struct NmTArgs {
   const uint16_t* X;    // b x n
   const uint16_t* Vt;   // r x n
-  uint16_t* T;          // b x tld
-  int n, r, b, tld, kw; // kw: columns per wave (a multiple of 32)
+  uint16_t* T;          // (X V)[c][l] at T[c * sc + l * sl]
+  int n, r, b, sc, sl;
+  int kw;               // columns per wave (a multiple of 32)
 };
 
 // Operand layout of v_mfma_f32_16x16x32_bf16: A lane l holds row l % 16, K
@@ -328,8 +329,26 @@ __global__ __launch_bounds__(64 * kNmTWaves) void k_nm_t(NmTArgs a) {
 #pragma unroll
     for (int ww = 1; ww < kNmTWaves; ++ww) sum += tred[ww][c][l];
     const int cg = 16 * ct + c, lg = 16 * lt + l;
-    if (cg < a.b && lg < a.r) a.T[(int64_t)cg * a.tld + lg] = f32_to_bf16(sum);
+    if (cg < a.b && lg < a.r) a.T[(int64_t)cg * a.sc + (int64_t)lg * a.sl] = f32_to_bf16(sum);
   }
+}
+
+// T = X V on the matrix cores (k_nm_t) at T[c * sc + l * sl].  Needs n % 32
+// == 0 and 16-byte aligned X and V^T rows (t_mfma_supported), bf16, r > 0.
+bool t_mfma_supported(const hss_matrix* A, const void* X) {
+  return A->dtype == HSS_BF16 && A->r > 0 && A->n % 32 == 0 && (uintptr_t)X % 16 == 0 &&
+         (uintptr_t)A->Vt % 16 == 0 && (int64_t)A->r * A->n * 2 < ((int64_t)1 << 31);
+}
+
+void launch_t_mfma(const hss_matrix* A, int b, const void* X, uint16_t* T, int sl, int sc, hipStream_t s) {
+  NmTArgs t = {};
+  t.X = static_cast<const uint16_t*>(X);
+  t.Vt = static_cast<const uint16_t*>(A->Vt);
+  t.T = T;
+  t.n = A->n; t.r = A->r; t.b = b; t.sc = sc; t.sl = sl;
+  t.kw = (A->n / 32 + kNmTWaves - 1) / kNmTWaves * 32;
+  const dim3 grid((unsigned)((A->r + 15) / 16), (unsigned)((b + 15) / 16));
+  hipLaunchKernelGGL(k_nm_t, grid, dim3(64 * kNmTWaves), 0, s, t);
 }
 
 bool nm_mma_supported(const hss_matrix* A, int b) {
@@ -368,14 +387,7 @@ hss_status launch_nm_mma(const hss_matrix* A, int b, const void* X, void* Y, voi
   if (A->r > 0 && b <= kNmTVecMaxCols) {
     launch_t_vec(A, b, X, a.tld, static_cast<uint16_t*>(ws), s);
   } else if (A->r > 0) {
-    NmTArgs t = {};
-    t.X = a.X;
-    t.Vt = static_cast<const uint16_t*>(A->Vt);
-    t.T = static_cast<uint16_t*>(ws);
-    t.n = A->n; t.r = A->r; t.b = b; t.tld = a.tld;
-    t.kw = (A->n / 32 + kNmTWaves - 1) / kNmTWaves * 32;
-    const dim3 grid((unsigned)((A->r + 15) / 16), (unsigned)((b + 15) / 16));
-    hipLaunchKernelGGL(k_nm_t, grid, dim3(64 * kNmTWaves), 0, s, t);
+    launch_t_mfma(A, b, X, static_cast<uint16_t*>(ws), 1, a.tld, s);
   }
   launch_nm_rt<kNmRowTiles>(a, s);
   return hipGetLastError() == hipSuccess ? HSS_OK : HSS_ERR_HIP;

@@ -28,6 +28,8 @@
 namespace hss {
 
 void launch_tt_gemm(const hss_matrix* A, int b, const void* X, uint16_t* Tt, int ldt, float* part, hipStream_t s);
+bool t_mfma_supported(const hss_matrix* A, const void* X);
+void launch_t_mfma(const hss_matrix* A, int b, const void* X, uint16_t* T, int sl, int sc, hipStream_t s);
 size_t tt_gemm_part_bytes(const hss_matrix* A, int b, int ldt);
 
 static constexpr int kSpWaves = 8;            // rows (waves) per block
@@ -35,6 +37,7 @@ static constexpr int kSpLdsMax = 64 * 1024;   // LDS for the T tile
 static constexpr int kSpMaxG = 8;             // batch tile <= 64 columns
 static constexpr int kSpDepth = 4;            // entries per lane in flight
 static constexpr int kSpVecMaxB = 64;         // T on the vector units up to this batch
+static constexpr int kSpTMfmaMinB = 48;       // from this batch, T by k_nm_t where it can
 
 static size_t align256_(size_t x) { return (x + 255) & ~(size_t)255; }
 static int cdiv_(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
@@ -422,7 +425,13 @@ hss_status launch_spmm(const hss_matrix* A, int b, const void* X, void* Y, void*
   const uint16_t* Xb = static_cast<const uint16_t*>(X);
   const int64_t work = (int64_t)A->n * (a.ldt >> 3);
   const int xt_blocks = A->nnz > 0 ? (int)std::min<int64_t>(cdiv_(work, 256), 1024) : 0;
-  if (b <= kSpVecMaxB) {
+  if (b >= kSpTMfmaMinB && t_mfma_supported(A, X)) {
+    // T on the matrix cores, X^T by k_xt
+    launch_t_mfma(A, b, X, const_cast<uint16_t*>(a.Tt), a.ldt, 1, s);
+    if (xt_blocks > 0)
+      hipLaunchKernelGGL(k_xt, dim3((unsigned)std::min<int64_t>(cdiv_(work, 256), 4096)), dim3(256), 0, s, Xb, b,
+                         A->n, a.ldt, const_cast<uint16_t*>(a.Xt));
+  } else if (b <= kSpVecMaxB) {
     // T and X^T in one launch
     const bool vec = A->n % 8 == 0 && (uintptr_t)X % 16 == 0 && (A->r == 0 || (uintptr_t)A->Vt % 16 == 0);
     const unsigned grid = (unsigned)(A->r + xt_blocks);
