@@ -55,11 +55,13 @@ typedef uint32_t nm_u32x8 __attribute__((ext_vector_type(8)));
 static constexpr int kNmBlockWaves = 4;         // waves (turns at the stages) per block
 static constexpr int kNmStride = 36;            // LDS floats per column of a partial tile
 static constexpr int kNmMinCols = 2, kNmMaxCols = 64;
-// T on the vector units up to this many columns (k_spmm_prep's T blocks, one
-// per rank row: 4.5 us on the 11008 x 4096 rank-64 layer at b = 2 .. 8, where
-// k_nm_t's 4 blocks take 7.0 us), on the matrix cores above (b = 64: 9.8 us
-// against 16.5 us).
-static constexpr int kNmTVecMaxCols = 16;
+// T on the vector units (k_spmm_prep's T blocks, one per rank row and pass
+// of up to 16 columns, the passes side by side) while that takes at most
+// kNmTVecMaxBlocks blocks, else on the matrix cores (k_nm_t).  On the
+// 11008 x 4096 rank-64 layer the passes win at every batch: b = 2 .. 8
+// 4.5 us against 7.0; whole calls at b = 32 / 48 / 64 27.0 / 37.8 / 41.6 us
+// against 31.2 / 42.1 / 45.7.
+static constexpr int kNmTVecMaxBlocks = 1024;
 // 32-row tiles per block: X, read once per block from L2, serves 64 rows.
 // Measured on the 11008 x 4096 layer (one tile vs two, us): b = 2 22.0 vs
 // 20.2, b = 8 23.6 vs 21.4, b = 32 38.8 vs 31.3, b = 64 57.3 vs 45.6 (three
@@ -384,7 +386,7 @@ hss_status launch_nm_mma(const hss_matrix* A, int b, const void* X, void* Y, voi
   a.Y = static_cast<uint16_t*>(Y);
   a.m = A->m; a.n = A->n; a.r = A->r; a.b = b; a.tld = nm_tld(A->r);
   a.uvec = A->r % 8 == 0 && (uintptr_t)A->U % 16 == 0;
-  if (A->r > 0 && b <= kNmTVecMaxCols) {
+  if (A->r > 0 && ((int64_t)A->r * ((b + 15) / 16) <= kNmTVecMaxBlocks || !t_mfma_supported(A, X))) {
     launch_t_vec(A, b, X, a.tld, static_cast<uint16_t*>(ws), s);
   } else if (A->r > 0) {
     launch_t_mfma(A, b, X, static_cast<uint16_t*>(ws), 1, a.tld, s);

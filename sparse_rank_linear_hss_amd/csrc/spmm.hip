@@ -36,8 +36,12 @@ static constexpr int kSpWaves = 8;            // rows (waves) per block
 static constexpr int kSpLdsMax = 64 * 1024;   // LDS for the T tile
 static constexpr int kSpMaxG = 8;             // batch tile <= 64 columns
 static constexpr int kSpDepth = 4;            // entries per lane in flight
-static constexpr int kSpVecMaxB = 64;         // T on the vector units up to this batch
-static constexpr int kSpTMfmaMinB = 48;       // from this batch, T by k_nm_t where it can
+static constexpr int kSpVecMaxB = 64;         // T on the vector units up to this batch, and
+static constexpr int kPrepMaxTBlocks = 1024;  // while its passes take at most this many blocks;
+                                              // beyond, T by k_nm_t where it can
+// (4096^2 rank 256, passes of 16 columns side by side vs k_nm_t: b = 48 29.0
+// vs 33.5 us, b = 64 30.0 vs 33.1 us; 8192^2 rank 512, 2048 pass blocks at
+// b = 64: 77.7 vs 74.2 us.)
 
 static size_t align256_(size_t x) { return (x + 255) & ~(size_t)255; }
 static int cdiv_(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
@@ -96,6 +100,7 @@ __global__ __launch_bounds__(256) void k_spmm_prep(const uint16_t* __restrict__ 
                                                    int b, int n, int r, int ldt, int sl, int sc,
                                                    uint16_t* __restrict__ Tt, uint16_t* __restrict__ Xt) {
   if ((int)blockIdx.x >= r) {
+    if (blockIdx.y > 0) return;  // X^T once
     const int64_t total = (int64_t)n * (ldt >> 3);
     const int64_t nb = gridDim.x - r;
     for (int64_t t = (int64_t)(blockIdx.x - r) * 256 + threadIdx.x; t < total; t += nb * 256)
@@ -105,7 +110,8 @@ __global__ __launch_bounds__(256) void k_spmm_prep(const uint16_t* __restrict__ 
   __shared__ float red[4][16];
   const int l = blockIdx.x, wave = threadIdx.x >> 6;
   const uint16_t* __restrict__ vrow = Vt + (int64_t)l * n;
-  for (int cb = 0; cb < b; cb += CB) {
+  // pass blockIdx.y, and every gridDim.y-th after it
+  for (int cb = CB * (int)blockIdx.y; cb < b; cb += CB * (int)gridDim.y) {
     float acc[CB];
 #pragma unroll
     for (int cc = 0; cc < CB; ++cc) acc[cc] = 0.f;
@@ -381,22 +387,26 @@ size_t spmm_ws_bytes(const hss_matrix* A, int b) { return plan_spmm(A, b).total;
 // k_spmm_prep with the pass width that fits b (fewer X loads per step for
 // narrow batches).
 template <bool VEC>
-static void launch_prep_v(unsigned grid, const uint16_t* X, const uint16_t* Vt, int b, int n, int r, int ldt, int sl,
+static void launch_prep_v(dim3 grid, const uint16_t* X, const uint16_t* Vt, int b, int n, int r, int ldt, int sl,
                           int sc, uint16_t* T, uint16_t* Xt, hipStream_t s) {
   if (b <= 4)
-    hipLaunchKernelGGL((k_spmm_prep<VEC, 4>), dim3(grid), dim3(256), 0, s, X, Vt, b, n, r, ldt, sl, sc, T, Xt);
+    hipLaunchKernelGGL((k_spmm_prep<VEC, 4>), grid, dim3(256), 0, s, X, Vt, b, n, r, ldt, sl, sc, T, Xt);
   else if (b <= 8)
-    hipLaunchKernelGGL((k_spmm_prep<VEC, 8>), dim3(grid), dim3(256), 0, s, X, Vt, b, n, r, ldt, sl, sc, T, Xt);
+    hipLaunchKernelGGL((k_spmm_prep<VEC, 8>), grid, dim3(256), 0, s, X, Vt, b, n, r, ldt, sl, sc, T, Xt);
   else
-    hipLaunchKernelGGL((k_spmm_prep<VEC, 16>), dim3(grid), dim3(256), 0, s, X, Vt, b, n, r, ldt, sl, sc, T, Xt);
+    hipLaunchKernelGGL((k_spmm_prep<VEC, 16>), grid, dim3(256), 0, s, X, Vt, b, n, r, ldt, sl, sc, T, Xt);
 }
 
+// Grid: rank rows (then X^T blocks) along x, the passes of CB columns along
+// y, so a block computes one pass (the passes run side by side).
 static void launch_prep(bool vec, unsigned grid, const uint16_t* X, const uint16_t* Vt, int b, int n, int r, int ldt,
                         int sl, int sc, uint16_t* T, uint16_t* Xt, hipStream_t s) {
+  const int cb = b <= 4 ? 4 : (b <= 8 ? 8 : 16);
+  const dim3 g(grid, (unsigned)((b + cb - 1) / cb));
   if (vec)
-    launch_prep_v<true>(grid, X, Vt, b, n, r, ldt, sl, sc, T, Xt, s);
+    launch_prep_v<true>(g, X, Vt, b, n, r, ldt, sl, sc, T, Xt, s);
   else
-    launch_prep_v<false>(grid, X, Vt, b, n, r, ldt, sl, sc, T, Xt, s);
+    launch_prep_v<false>(g, X, Vt, b, n, r, ldt, sl, sc, T, Xt, s);
 }
 
 template <int G>
@@ -425,7 +435,8 @@ hss_status launch_spmm(const hss_matrix* A, int b, const void* X, void* Y, void*
   const uint16_t* Xb = static_cast<const uint16_t*>(X);
   const int64_t work = (int64_t)A->n * (a.ldt >> 3);
   const int xt_blocks = A->nnz > 0 ? (int)std::min<int64_t>(cdiv_(work, 256), 1024) : 0;
-  if (b >= kSpTMfmaMinB && t_mfma_supported(A, X)) {
+  const bool t_vec = b <= kSpVecMaxB && (int64_t)A->r * ((b + 15) / 16) <= kPrepMaxTBlocks;
+  if (!t_vec && t_mfma_supported(A, X)) {
     // T on the matrix cores, X^T by k_xt
     launch_t_mfma(A, b, X, const_cast<uint16_t*>(a.Tt), a.ldt, 1, s);
     if (xt_blocks > 0)
