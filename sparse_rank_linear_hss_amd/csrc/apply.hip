@@ -70,9 +70,10 @@ static constexpr int kNmMinColsDefault = 2;
 // 10.3 vs 11.1 us; b = 3 decode 12.2 vs 11.2 us; b = 4 decode 12.7 vs 11.3
 // us; b = 8 decode 20.1 vs 12.2 us; b = 16 39.8 vs 15.6 us; b = 32 densify
 // 52.8 vs 21.4 us; b = 64 169 / 58.4 vs 30.0 us; b = 128 densify 64.8 vs
-// 41.0 us; b = 256 densify 77.3 vs 61.5 us.  The 8192 x 8192 3 % rank-512 layer: b = 64 densify 137 vs 74 us,
-// b = 128 156 vs 112 us, b = 256 164 vs 202 us (its U part, m r b on the
-// vector units, is 4 times the 4096^2 layer's), so the gather stops at 128.
+// 41.0 us; b = 256 densify 77.3 vs 61.5 us.  The 8192 x 8192 3 % rank-512
+// layer: b = 64 densify 137 vs 68 us, b = 128 151 vs 102 us, b = 256 164 vs
+// 178 us (its U part, m r b on the vector units, is 4 times the 4096^2
+// layer's), so the gather stops at 128.
 static constexpr int kSpmmMinCols = 3, kSpmmMaxCols = 128;
 
 // X: the call's input (the sparse matrix cores need it 16-byte aligned), or

@@ -34,6 +34,7 @@ size_t tt_gemm_part_bytes(const hss_matrix* A, int b, int ldt);
 
 static constexpr int kSpWaves = 8;            // rows (waves) per block
 static constexpr int kSpLdsMax = 64 * 1024;   // LDS for the T tile
+static constexpr int kSpLdsPref = 32 * 1024;  // ... preferred (more blocks per CU)
 static constexpr int kSpMaxG = 8;             // batch tile <= 64 columns
 static constexpr int kSpDepth = 4;            // entries per lane in flight
 static constexpr int kSpVecMaxB = 64;         // T on the vector units up to this batch, and
@@ -349,9 +350,13 @@ void launch_xt(const uint16_t* X, int b, int n, int ldt, uint16_t* Xt, hipStream
 
 // Batch tile: the smallest of 8, 16, 32, 64 columns that covers b (64 beyond),
 // shrunk until T's tile fits the LDS budget.
+// Batch tile 8 G: the widest that covers b and whose T tile takes at most
+// kSpLdsPref of LDS (8192^2 rank 512, whose 64-column tile takes 64 KB: 4
+// tiles of 32 columns at b = 64 / 128 took 67.7 / 103 us against 74.1 / 112
+// with 2 / 1 tiles of 64; 4096^2 rank 256: 29.6 / 45.2 against 30.0 / 41.0).
 static int spmm_g(const hss_matrix* A, int b) {
   int g = b <= 8 ? 1 : (b <= 16 ? 2 : (b <= 32 ? 4 : kSpMaxG));
-  while (g > 1 && (size_t)A->r * 8 * g * 2 > kSpLdsMax) g >>= 1;
+  while (g > 1 && (size_t)A->r * 8 * g * 2 > kSpLdsPref) g >>= 1;
   return g;
 }
 
