@@ -60,16 +60,16 @@ enum Route { R_DECODE = 0, R_SPMM = 1, R_MFMA = 2, R_NM = 3 };
 // Default batch range of the 2:4 route on the sparse matrix cores.
 // Measured on the 11008 x 4096 rank-64 layer (decode / densify vs sparse
 // matrix cores, us): b = 2 decode 20.2 vs 18.3; b = 3 decode 25.3 vs 18.5;
-// b = 8 decode 46.0 vs 19.8; b = 16 densify 46.0 vs 23.0; b = 32 densify
-// 48.5 vs 26.9; b = 64 densify 60.1 vs 41.6.
+// b = 8 decode 46.0 vs 19.1; b = 16 densify 46.0 vs 20.7; b = 32 densify
+// 48.5 vs 25.8; b = 64 densify 60.1 vs 41.6.
 static constexpr int kNmMinColsDefault = 2;
 
 // Default batch range of the gather SpMM for bf16 CSR: below it the fused
 // decode passes, above it S densified for the matrix cores.  Measured on the
 // 4096 x 4096 5 % rank-256 layer (decode / densify vs gather): b = 2 decode
 // 10.3 vs 11.1 us; b = 3 decode 12.2 vs 11.2 us; b = 4 decode 12.7 vs 11.3
-// us; b = 8 decode 20.1 vs 12.2 us; b = 16 39.8 vs 15.6 us; b = 32 densify
-// 52.8 vs 21.4 us; b = 64 169 / 58.4 vs 30.0 us; b = 128 densify 64.8 vs
+// us; b = 8 decode 20.1 vs 11.7 us; b = 16 39.8 vs 14.3 us; b = 32 densify
+// 52.8 vs 20.7 us; b = 64 169 / 58.4 vs 30.0 us; b = 128 densify 64.8 vs
 // 41.0 us; b = 256 densify 77.3 vs 61.5 us.  The 8192 x 8192 3 % rank-512
 // layer: b = 64 densify 137 vs 68 us, b = 128 151 vs 102 us, b = 256 164 vs
 // 178 us (its U part, m r b on the vector units, is 4 times the 4096^2

@@ -46,6 +46,7 @@
 namespace hss {
 
 void launch_t_vec(const hss_matrix* A, int b, const void* X, int ldt, uint16_t* T, hipStream_t s);
+int64_t prep_t_blocks(int r, int b);
 
 typedef __bf16 nm_bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 nm_bf16x16 __attribute__((ext_vector_type(16)));
@@ -386,7 +387,7 @@ hss_status launch_nm_mma(const hss_matrix* A, int b, const void* X, void* Y, voi
   a.Y = static_cast<uint16_t*>(Y);
   a.m = A->m; a.n = A->n; a.r = A->r; a.b = b; a.tld = nm_tld(A->r);
   a.uvec = A->r % 8 == 0 && (uintptr_t)A->U % 16 == 0;
-  if (A->r > 0 && ((int64_t)A->r * ((b + 15) / 16) <= kNmTVecMaxBlocks || !t_mfma_supported(A, X))) {
+  if (A->r > 0 && (prep_t_blocks(A->r, b) <= kNmTVecMaxBlocks || !t_mfma_supported(A, X))) {
     launch_t_vec(A, b, X, a.tld, static_cast<uint16_t*>(ws), s);
   } else if (A->r > 0) {
     launch_t_mfma(A, b, X, static_cast<uint16_t*>(ws), 1, a.tld, s);

@@ -35,6 +35,7 @@ size_t tt_gemm_part_bytes(const hss_matrix* A, int b, int ldt);
 static constexpr int kSpWaves = 8;            // rows (waves) per block
 static constexpr int kSpLdsMax = 64 * 1024;   // LDS for the T tile
 static constexpr int kSpLdsPref = 32 * 1024;  // ... preferred (more blocks per CU)
+static constexpr int kPrepCb4MaxB = 16;       // T passes of 4 columns up to this batch
 static constexpr int kSpMaxG = 8;             // batch tile <= 64 columns
 static constexpr int kSpDepth = 4;            // entries per lane in flight
 static constexpr int kSpVecMaxB = 64;         // T on the vector units up to this batch, and
@@ -389,14 +390,20 @@ static SpmmPlan plan_spmm(const hss_matrix* A, int b) {
 
 size_t spmm_ws_bytes(const hss_matrix* A, int b) { return plan_spmm(A, b).total; }
 
-// k_spmm_prep with the pass width that fits b (fewer X loads per step for
-// narrow batches).
+// Columns per T pass of k_spmm_prep: narrower passes load fewer X rows per
+// step and run side by side.
+static int prep_cb(int b) { return b <= kPrepCb4MaxB ? 4 : (b <= 32 ? 8 : 16); }
+
+// Blocks the T passes of k_spmm_prep take for b columns.
+int64_t prep_t_blocks(int r, int b) { return (int64_t)r * ((b + prep_cb(b) - 1) / prep_cb(b)); }
+
+// k_spmm_prep with the pass width prep_cb(b).
 template <bool VEC>
 static void launch_prep_v(dim3 grid, const uint16_t* X, const uint16_t* Vt, int b, int n, int r, int ldt, int sl,
                           int sc, uint16_t* T, uint16_t* Xt, hipStream_t s) {
-  if (b <= 4)
+  if (prep_cb(b) == 4)
     hipLaunchKernelGGL((k_spmm_prep<VEC, 4>), grid, dim3(256), 0, s, X, Vt, b, n, r, ldt, sl, sc, T, Xt);
-  else if (b <= 8)
+  else if (prep_cb(b) == 8)
     hipLaunchKernelGGL((k_spmm_prep<VEC, 8>), grid, dim3(256), 0, s, X, Vt, b, n, r, ldt, sl, sc, T, Xt);
   else
     hipLaunchKernelGGL((k_spmm_prep<VEC, 16>), grid, dim3(256), 0, s, X, Vt, b, n, r, ldt, sl, sc, T, Xt);
@@ -406,7 +413,7 @@ static void launch_prep_v(dim3 grid, const uint16_t* X, const uint16_t* Vt, int 
 // y, so a block computes one pass (the passes run side by side).
 static void launch_prep(bool vec, unsigned grid, const uint16_t* X, const uint16_t* Vt, int b, int n, int r, int ldt,
                         int sl, int sc, uint16_t* T, uint16_t* Xt, hipStream_t s) {
-  const int cb = b <= 4 ? 4 : (b <= 8 ? 8 : 16);
+  const int cb = prep_cb(b);
   const dim3 g(grid, (unsigned)((b + cb - 1) / cb));
   if (vec)
     launch_prep_v<true>(g, X, Vt, b, n, r, ldt, sl, sc, T, Xt, s);
@@ -440,7 +447,7 @@ hss_status launch_spmm(const hss_matrix* A, int b, const void* X, void* Y, void*
   const uint16_t* Xb = static_cast<const uint16_t*>(X);
   const int64_t work = (int64_t)A->n * (a.ldt >> 3);
   const int xt_blocks = A->nnz > 0 ? (int)std::min<int64_t>(cdiv_(work, 256), 1024) : 0;
-  const bool t_vec = b <= kSpVecMaxB && (int64_t)A->r * ((b + 15) / 16) <= kPrepMaxTBlocks;
+  const bool t_vec = b <= kSpVecMaxB && prep_t_blocks(A->r, b) <= kPrepMaxTBlocks;
   if (!t_vec && t_mfma_supported(A, X)) {
     // T on the matrix cores, X^T by k_xt
     launch_t_mfma(A, b, X, const_cast<uint16_t*>(a.Tt), a.ldt, 1, s);
