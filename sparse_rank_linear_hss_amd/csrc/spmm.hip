@@ -36,6 +36,14 @@ static constexpr int kSpWaves = 8;            // rows (waves) per block
 static constexpr int kSpLdsMax = 64 * 1024;   // LDS for the T tile
 static constexpr int kSpLdsPref = 32 * 1024;  // ... preferred (more blocks per CU)
 static constexpr int kPrepCb4MaxB = 16;       // T passes of 4 columns up to this batch
+// k_spmm_prep's block: 512 threads (a 4096-column row in one step of 8
+// columns each, all its loads in flight together) while the T passes take
+// at most kPrepWideMaxBlocks blocks, else 256 (more blocks per CU).  11008 x
+// 4096 rank 64 (64 .. 256 pass blocks), whole 2:4 calls, 256 vs 512
+// threads: b = 2 18.3 vs 17.9 us, b = 32 25.8 vs 25.2 us; 4096^2 rank 256
+// (256 .. 1024 pass blocks), gather calls: b = 3 11.1 vs 10.9 us, b = 16
+// 14.3 vs 14.7 us, b = 64 30.0 vs 33.3 us.
+static constexpr int kPrepWideMaxBlocks = 256;
 static constexpr int kSpMaxG = 8;             // batch tile <= 64 columns
 static constexpr int kSpDepth = 4;            // entries per lane in flight
 static constexpr int kSpVecMaxB = 64;         // T on the vector units up to this batch, and
@@ -93,23 +101,24 @@ __global__ __launch_bounds__(256) void k_xt(const uint16_t* __restrict__ X, int 
 // X^T (b values), the block's threads striding over n (8 columns per step
 // with 16-byte loads when VEC), CB batch columns per pass (4, 8 or 16: one
 // X load per column and step); each column's sum
-// is reduced within waves by DPP and the four wave sums added in order, so
-// the result does not depend on scheduling; stored as bf16 at
+// is reduced within waves by DPP and the NTH / 64 wave sums added in order,
+// so the result does not depend on scheduling; stored as bf16 at
 // T[l * sl + c * sc] (sl = ldt, sc = 1: T^T; sl = 1, sc = row stride: T).
 // Blocks r and up: X^T, as k_xt.
-template <bool VEC, int CB>
-__global__ __launch_bounds__(256) void k_spmm_prep(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Vt,
+template <bool VEC, int CB, int NTH>
+__global__ __launch_bounds__(NTH) void k_spmm_prep(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Vt,
                                                    int b, int n, int r, int ldt, int sl, int sc,
                                                    uint16_t* __restrict__ Tt, uint16_t* __restrict__ Xt) {
   if ((int)blockIdx.x >= r) {
     if (blockIdx.y > 0) return;  // X^T once
     const int64_t total = (int64_t)n * (ldt >> 3);
     const int64_t nb = gridDim.x - r;
-    for (int64_t t = (int64_t)(blockIdx.x - r) * 256 + threadIdx.x; t < total; t += nb * 256)
+    for (int64_t t = (int64_t)(blockIdx.x - r) * NTH + threadIdx.x; t < total; t += nb * NTH)
       xt_item(X, b, n, ldt, t, Xt);
     return;
   }
-  __shared__ float red[4][16];
+  constexpr int kPrepWaves = NTH / 64;
+  __shared__ float red[kPrepWaves][16];
   const int l = blockIdx.x, wave = threadIdx.x >> 6;
   const uint16_t* __restrict__ vrow = Vt + (int64_t)l * n;
   // pass blockIdx.y, and every gridDim.y-th after it
@@ -121,7 +130,7 @@ __global__ __launch_bounds__(256) void k_spmm_prep(const uint16_t* __restrict__ 
       // all CB + 1 loads of a step are unconditional (rows past b re-read row
       // b - 1 and are dropped after), so they are in flight together: a load
       // under a branch would be waited for inside it
-      for (int j = 8 * threadIdx.x; j < n; j += 8 * 256) {
+      for (int j = 8 * threadIdx.x; j < n; j += 8 * NTH) {
         const u32x4 vv = *reinterpret_cast<const u32x4*>(vrow + j);
         u32x4 xx[CB];
 #pragma unroll
@@ -140,7 +149,7 @@ __global__ __launch_bounds__(256) void k_spmm_prep(const uint16_t* __restrict__ 
         }
       }
     } else {
-      for (int j = threadIdx.x; j < n; j += 256) {
+      for (int j = threadIdx.x; j < n; j += NTH) {
         const float vf = bf16lo(vrow[j]);
 #pragma unroll
         for (int cc = 0; cc < CB; ++cc)
@@ -155,8 +164,10 @@ __global__ __launch_bounds__(256) void k_spmm_prep(const uint16_t* __restrict__ 
     __syncthreads();
     if (threadIdx.x < CB && cb + (int)threadIdx.x < b) {
       const int cc = threadIdx.x;
-      Tt[(int64_t)l * sl + (int64_t)(cb + cc) * sc] =
-          f32_to_bf16(((red[0][cc] + red[1][cc]) + red[2][cc]) + red[3][cc]);
+      float sum = red[0][cc];
+#pragma unroll
+      for (int w = 1; w < kPrepWaves; ++w) sum += red[w][cc];
+      Tt[(int64_t)l * sl + (int64_t)(cb + cc) * sc] = f32_to_bf16(sum);
     }
     __syncthreads();
   }
@@ -398,15 +409,24 @@ static int prep_cb(int b) { return b <= kPrepCb4MaxB ? 4 : (b <= 32 ? 8 : 16); }
 int64_t prep_t_blocks(int r, int b) { return (int64_t)r * ((b + prep_cb(b) - 1) / prep_cb(b)); }
 
 // k_spmm_prep with the pass width prep_cb(b).
+template <bool VEC, int NTH>
+static void launch_prep_vn(dim3 grid, const uint16_t* X, const uint16_t* Vt, int b, int n, int r, int ldt, int sl,
+                           int sc, uint16_t* T, uint16_t* Xt, hipStream_t s) {
+  if (prep_cb(b) == 4)
+    hipLaunchKernelGGL((k_spmm_prep<VEC, 4, NTH>), grid, dim3(NTH), 0, s, X, Vt, b, n, r, ldt, sl, sc, T, Xt);
+  else if (prep_cb(b) == 8)
+    hipLaunchKernelGGL((k_spmm_prep<VEC, 8, NTH>), grid, dim3(NTH), 0, s, X, Vt, b, n, r, ldt, sl, sc, T, Xt);
+  else
+    hipLaunchKernelGGL((k_spmm_prep<VEC, 16, NTH>), grid, dim3(NTH), 0, s, X, Vt, b, n, r, ldt, sl, sc, T, Xt);
+}
+
 template <bool VEC>
 static void launch_prep_v(dim3 grid, const uint16_t* X, const uint16_t* Vt, int b, int n, int r, int ldt, int sl,
                           int sc, uint16_t* T, uint16_t* Xt, hipStream_t s) {
-  if (prep_cb(b) == 4)
-    hipLaunchKernelGGL((k_spmm_prep<VEC, 4>), grid, dim3(256), 0, s, X, Vt, b, n, r, ldt, sl, sc, T, Xt);
-  else if (prep_cb(b) == 8)
-    hipLaunchKernelGGL((k_spmm_prep<VEC, 8>), grid, dim3(256), 0, s, X, Vt, b, n, r, ldt, sl, sc, T, Xt);
+  if (prep_t_blocks(r, b) <= kPrepWideMaxBlocks)
+    launch_prep_vn<VEC, 512>(grid, X, Vt, b, n, r, ldt, sl, sc, T, Xt, s);
   else
-    hipLaunchKernelGGL((k_spmm_prep<VEC, 16>), grid, dim3(256), 0, s, X, Vt, b, n, r, ldt, sl, sc, T, Xt);
+    launch_prep_vn<VEC, 256>(grid, X, Vt, b, n, r, ldt, sl, sc, T, Xt, s);
 }
 
 // Grid: rank rows (then X^T blocks) along x, the passes of CB columns along
