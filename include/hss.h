@@ -198,10 +198,10 @@ hss_status hss_apply_workspace_size(const hss_matrix* A, int32_t b, size_t* byte
  *     counter), so the caller must not write to it afterwards; any number of
  *     calls, with any matrices and batch sizes, may then share it as long as
  *     they are ordered (same stream or events).
- * Execution: bf16 2:4 with 2 <= b <= 64 (n % 128 == 0, aligned arrays and
- * X) runs on the sparse matrix cores: S's stored values and 2-bit indices
- * are the operands of v_smfmac as they are, with fp32 accumulation, and T =
- * X V is rounded to bf16 once before U T is added.  bf16 2:4 beyond 64
+ * Execution: bf16 2:4 with 2 <= b <= 64 (n % 128 == 0; nm_values, nm_meta
+ * and X 16-byte aligned) runs on the sparse matrix cores: S's stored values
+ * and 2-bit indices are the operands of v_smfmac as they are, with fp32
+ * accumulation, and T = X V is rounded to bf16 once before U T is added.  bf16 2:4 beyond 64
  * columns, and bf16 CSR with b > 128, run on the matrix cores (T^T = X V and
  * Y = [X | T^T] [S | U]^T as MFMA GEMMs with fp32 accumulation; T is rounded
  * to bf16 once, between the two; a CSR S is first expanded into a dense bf16
@@ -209,8 +209,9 @@ hss_status hss_apply_workspace_size(const hss_matrix* A, int32_t b, size_t* byte
  * bf16 CSR with 3 <= b <= 128 runs the gather SpMM (T = X V rounded to bf16
  * once, X^T staged in the workspace, then every stored entry gathers its X^T
  * row; fp32 accumulation).  Otherwise one fused kernel per 8 columns.  On
- * the matrix-core routes the zeros of an expanded operand multiply X too, so
- * a NaN or infinity in X reaches every output of its batch row.  The
+ * the matrix-core routes (the sparse one included) zeros in an operand
+ * multiply X too, so a NaN or infinity in X can reach any output of its
+ * batch row.  The
  * environment variable HSS_CSR_BATCH_ROUTE = decode | spmm | densify |
  * smfmac forces a bf16 call with b >= 2 onto that route where the route
  * supports the matrix (for comparing them); the workspace size covers every
