@@ -1,44 +1,38 @@
 #!/usr/bin/env python3
 """Throughput of the sparse + low-rank (HSS) linear layer on one MI355X.
 
-Headline workload (one step = one hss_apply = one decode token): the 4096 x
-4096 bf16 attention-projection shape with Student-t (nu = 3) x 0.02 weights
-and 0.5 % outliers x20; S = top 5 % by |w| in CSR (838,860 bf16 values, int32
-columns), low-rank factors of rank 256; X ~ N(0, 1) bf16, batch 1.  S comes
-from this library's own hss_split of the seeded W; the factors are seeded
-stand-ins with a truncated SVD's shapes and scale (the factorisation is
-offline and its values do not change the work).
+Headline workload (one step = one decode token through one decoder layer):
+the seven projections of a Llama-7B-class decoder layer (q, k, v, o 4096 x
+4096; gate, up 11008 x 4096; down 4096 x 11008), bf16 Student-t (nu = 3) x
+0.02 weights, each S = the top 3 % by |w| in CSR (this library's hss_split of
+the seeded W) plus factors of rank 409 (10 % of min(m, n)); batch-1 decode.
+q/k/v and gate/up read the same input and run as grouped calls, so a token
+is four launches.  The factors are seeded stand-ins with a truncated SVD's
+shapes and scale (the factorisation is offline; its values do not change
+the work -- the parity tests run the oracle's real factors).
 
-Cold-HBM protocol: the compressed operands (CSR arrays, U, V^T) are
-replicated into enough distinct device copies that one pass over them spans
->= 1 GiB (4x the 256 MB last-level cache); consecutive steps use consecutive
-copies.  The timed steps are replayed from a HIP graph (decode loops are
-launch-bound; the kernels keep their cross-call state on the device, so
-replays are exact); the plain stream-launch rate is reported beside it.
+Cold-HBM protocol (every timed figure): the compressed operands are
+replicated into enough distinct device copies that a pass over them spans
+>= 1 GiB, and consecutive steps use consecutive copies.  Exactly K steps are
+captured into one HIP graph; before each timed replay a 1 GiB read-write
+flush evicts the 256 MB last-level cache, so the steps read HBM whatever K
+is.  Several trials give p10 / p50 / p90; `value` is from the median trial.
 
-Also measured in the same run (extra JSON keys): the same layer with 16-bit
-column indices and at batch 16, its batched routes side by side (fused decode
-passes, gather SpMM, densified S on the matrix cores; b = 8 .. 256), its
-hierarchical form (Reverse
-Cuthill-McKee order of S's support, concentration ratio, 2 x 2 block
-factors of ranks 96 / 32 packed to rank 256) at batch 1, its dense-and-sparse form (0.5 % outliers in
-CSR plus a 4-bit quantised dense part, stand-in codes and levels) at batch 1
-and 8, the 11008 x 4096 2:4 layer at batch 1/8/64, one decoder layer's seven
-projections per decode token (q/k/v and gate/up as grouped applies, so four
-launches per token; the seven-launch order beside it), the 8192^2 prefill at
-batch 2048 (with the low-rank GEMMs alone for their matrix-core throughput),
-a training step on the 8192^2 layer at b = 2048 (forward, hss_grad and the
-transposed layer's apply for the input gradient), and hss_split.
+Also measured (extra JSON keys, each with its own roofline): the 1024^2 fp32
+layer (b = 1); the 4096^2 5 % rank-256 layer at b = 1 and 16, its 16-bit
+column form, its batched routes side by side, its hierarchical and
+dense-and-sparse forms; the 11008 x 4096 2:4 layer at b = 1 / 8 / 64 and its
+routes; the 8192^2 prefill at b = 2048 with the low-rank GEMMs alone; a
+training step on that layer; hss_split.  `cpu_baseline` times the fp64 CPU
+oracle (CSR apply) on a bounded sample of the headline workload.
 
-Prints ONE JSON line.  `value` = decode tokens/s of the timed steps;
-`roofline` prices the apply kernel's compressed-weight bytes against the
-8 TB/s HBM peak; `cpu_baseline` times the fp64 CPU oracle on a bounded
-sample.
+Prints ONE JSON line.
 """
 from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import math
 import os
@@ -50,15 +44,17 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 ROOT = os.path.dirname(os.path.abspath(__file__))
 GIB = float(1 << 30)
+LAYER_GROUPS = [[0, 1, 2], [3], [4, 5], [6]]          # q k v | o | gate up | down
+GROUP_NAMES = ["qkv", "o", "gate_up", "down"]
 
 
 def _args():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="budget of the CPU-oracle baseline sample")
+    ap.add_argument("--steps", type=int, default=256, help="decode tokens per timed region")
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--trials", type=int, default=9, help="timed regions (for p10/p50/p90)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-headline", action="store_true", help="skip the other workloads")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -67,24 +63,31 @@ def _args():
     return ap.parse_args()
 
 
-def _measured_traffic():
-    """HBM bytes per launch of the headline kernel as two hardware-counter runs
-    measured them (profiles/k_decode_csr4096_b1_hbm_counters.txt), or None when
-    the kernel's sources have changed since (the stored hash no longer matches)."""
-    import hashlib
-    path = os.path.join(ROOT, "profiles", "k_decode_csr4096_b1_hbm_counters.txt")
+def _log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def _decode_source_hash():
+    csrc = os.path.join(ROOT, "sparse_rank_linear_hss_amd", "csrc")
+    names = sorted(f for f in os.listdir(csrc) if f.startswith("decode")) + ["hss_internal.h"]
+    return hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read() for f in names)).hexdigest()
+
+
+def _measured_traffic(kernel_key):
+    """HBM bytes per launch of a decode kernel as two hardware-counter runs
+    measured them (profiles/k_decode_hbm_counters.txt), or None when the
+    kernels' sources have changed since (the stored hash no longer matches)."""
+    path = os.path.join(ROOT, "profiles", "k_decode_hbm_counters.txt")
     try:
         lines = open(path).read().splitlines()
     except OSError:
         return None
-    fields = {ln.split(":", 1)[0].split(" ")[0]: ln.rsplit(":", 1)[1].strip()
-              for ln in lines if ln.startswith(("traffic_bytes_per_launch", "source_sha256"))}
-    csrc = os.path.join(ROOT, "sparse_rank_linear_hss_amd", "csrc")
-    h = hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read()
-                                for f in ("decode.hip", "hss_internal.h"))).hexdigest()
-    if fields.get("source_sha256") != h or "traffic_bytes_per_launch" not in fields:
+    fields = dict(ln.split(":", 1) for ln in lines if ":" in ln and not ln.startswith((" ", "#")))
+    fields = {k.strip(): v.strip() for k, v in fields.items()}
+    if fields.get("source_sha256") != _decode_source_hash():
         return None
-    return float(fields["traffic_bytes_per_launch"])
+    v = fields.get(f"traffic_bytes_per_launch[{kernel_key}]")
+    return float(v) if v else None
 
 
 def _bf16(a):
@@ -93,35 +96,46 @@ def _bf16(a):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def _log(msg):
-    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+def _dev(a, dtype):
+    import numpy as np
+    import torch
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    return _bf16(a)
+
+
+def _tdtype(dtype):
+    import torch
+    return torch.float32 if dtype == "f32" else torch.bfloat16
 
 
 class Layer:
-    """One compressed matrix and its rotation copies on the device."""
+    """One compressed matrix (this library's split of W, stand-in factors)
+    and its rotation copies on the device."""
 
-    def __init__(self, H, W, fmt, frac, r, seed, which=0, rotation_bytes=GIB):
-        import torch
+    def __init__(self, H, W, fmt, frac, r, seed, which=0, dtype="bf16", rotation_bytes=GIB, copies=None):
         import hss_synth as syn
         m, n = W.shape
-        self.m, self.n, self.r = m, n, r
+        es = 4 if dtype == "f32" else 2
+        self.m, self.n, self.r, self.dtype = m, n, r, dtype
         self.split = H.hss_split(W, fmt, frac=frac)
-        U, V = syn.factors(m, n, r, "bf16", seed, which)
-        self.U, self.Vt = _bf16(U), _bf16(V.T)
+        U, V = syn.factors(m, n, r, dtype, seed, which)
+        self.U, self.Vt = _dev(U, dtype), _dev(V.T, dtype)
         if fmt == "csr":
-            self.w_bytes = self.split.k * (2 + 4) + 4 * (m + 1) + (m + n) * r * 2
+            self.w_bytes = self.split.k * (es + 4) + 4 * (m + 1) + (m + n) * r * es
         else:
-            self.w_bytes = m * n // 2 * 2 + m * ((n + 31) // 32) * 4 + (m + n) * r * 2
-        self.copies = max(1, math.ceil(rotation_bytes / self.w_bytes))
-        self.mats = []
+            self.w_bytes = m * n // 2 * es + m * ((n + 31) // 32) * 4 + (m + n) * r * es
+        self.copies = copies if copies is not None else max(1, math.ceil(rotation_bytes / self.w_bytes))
         sp = self.split
+        td = _tdtype(dtype)
+        self.mats = []
         for _ in range(self.copies):
             if fmt == "csr":
-                self.mats.append(H.HSSMatrix("csr", m, n, torch.bfloat16, U=self.U.clone(), Vt=self.Vt.clone(),
+                self.mats.append(H.HSSMatrix("csr", m, n, td, U=self.U.clone(), Vt=self.Vt.clone(),
                                              row_ptr=sp.row_ptr.clone(), col_idx=sp.col_idx.clone(),
                                              values=sp.values.clone(), nnz=sp.k))
             else:
-                self.mats.append(H.HSSMatrix("2:4", m, n, torch.bfloat16, U=self.U.clone(), Vt=self.Vt.clone(),
+                self.mats.append(H.HSSMatrix("2:4", m, n, td, U=self.U.clone(), Vt=self.Vt.clone(),
                                              nm_values=sp.nm_values.clone(), nm_meta=sp.nm_meta.clone()))
 
     def flops(self, b):
@@ -129,106 +143,461 @@ class Layer:
         return 2.0 * b * (nnz + self.r * (self.m + self.n))
 
 
-def _time(fn, steps, warmup):
-    """Average ms per call of fn(i) over `steps` calls (HIP events on the
-    current stream, which is the one the library launches on)."""
-    import torch
-    for i in range(warmup):
-        fn(i)
-    torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for i in range(steps):
-        fn(i)
-    t1.record()
-    torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / steps
+class Timer:
+    """Cold-HBM timing of K steps: one HIP graph of exactly K calls fn(0 ..
+    K-1); warm-up calls continue the rotation (fn(K ..)); before each timed
+    replay a 1 GiB read-write flush evicts the last-level cache."""
 
+    def __init__(self, trials):
+        import torch
+        self.trials = trials
+        self.flush_buf = torch.zeros(int(GIB), dtype=torch.uint8, device="cuda")
 
-def _time_graph(fn, steps, warmup, reps=3):
-    """Capture `steps` calls of fn(i) into one HIP graph, replay it `reps`
-    times (after a warm-up replay), return ms per call."""
-    import torch
-    for i in range(warmup):
-        fn(i)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
+    def flush(self):
+        self.flush_buf.add_(1)
+
+    def graph(self, fn, steps, warmup):
+        """ms per step of every trial (a list)."""
+        import torch
+        for i in range(warmup):
+            fn(steps + i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                fn(i)
+        self.flush()
+        g.replay()                      # first replay: graph upload (untimed)
+        torch.cuda.synchronize()
+        out = []
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(self.trials):
+            self.flush()
+            torch.cuda.synchronize()
+            t0.record()
+            g.replay()
+            t1.record()
+            torch.cuda.synchronize()
+            out.append(t0.elapsed_time(t1) / steps)
+        del g
+        return out
+
+    def eager(self, fn, steps, warmup):
+        """ms per step of stream launches (no graph), one trial after a flush."""
+        import torch
+        for i in range(warmup):
+            fn(steps + i)
+        self.flush()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
         for i in range(steps):
             fn(i)
-    g.replay()
-    torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(reps):
-        g.replay()
-    t1.record()
-    torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / (steps * reps)
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
 
 
-def _apply_loop(H, layer, xs, ys, ws, rotate=True):
-    mats = layer.mats if rotate else layer.mats[:1]
+def _pct(v):
+    import numpy as np
+    return {"p10": float(np.percentile(v, 10)), "p50": float(np.percentile(v, 50)), "p90": float(np.percentile(v, 90))}
+
+
+def _hbm_roofline(bytes_per_launch, ms, kernel, traffic=None):
+    gbs = bytes_per_launch / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+            "traffic": traffic, "kernel": kernel, "algorithmic_bytes_per_launch": bytes_per_launch}
+
+
+def _apply_loop(H, layer, xs, ys, ws):
+    mats = layer.mats
 
     def fn(i):
         H.hss_apply(mats[i % len(mats)], xs[i % len(xs)], ys[i % len(ys)], ws)
     return fn
 
 
-def _acts(cfg, b, which, count, m):
+def _acts(cfg, b, which, count, m, dtype="bf16"):
     import torch
     import hss_synth as syn
-    xs = [_bf16(syn.activations(cfg, b, which, step)) for step in range(count)]
-    ys = [torch.empty((b, m), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    xs = [_dev(syn.activations(cfg, b, which, step), dtype) for step in range(count)]
+    ys = [torch.empty((b, m), dtype=_tdtype(dtype), device="cuda") for _ in range(2)]
     return xs, ys
 
 
-def _cpu_baseline(cfg, W, U, V, seconds):
-    """fp64 oracle factored apply, b = 1, on this host's cores."""
+# ---------------------------------------------------------------------------
+# Headline: one decoder layer, batch-1 decode
+# ---------------------------------------------------------------------------
+
+def _decoder_layer(H, timer, args):
+    import torch
+    import hss_synth as syn
+    wl = syn.WORKLOADS["decoder_layer"]
+    tok_bytes = 0
+    for (m, n), r in zip(wl.shapes, wl.rank):
+        tok_bytes += H.hss_topk_count(m, n, *wl.frac) * 6 + 4 * (m + 1) + (m + n) * r * 2
+    copies = max(1, math.ceil(GIB / tok_bytes))          # whole-layer copies: >= 1 GiB per rotation
+    projs = []
+    for which in range(7):
+        Wp = _bf16(syn.weight(wl, which))
+        projs.append(Layer(H, Wp, "csr", wl.frac, wl.rank[which], wl.seed, which, copies=copies))
+        del Wp
+    assert sum(p.w_bytes for p in projs) == tok_bytes
+    _log(f"decoder layer ready: {tok_bytes} compressed bytes per token, {copies} layer copies")
+    ws = H.apply_workspace(max(H.hss_apply_group_workspace_size([projs[w].mats[0] for w in grp], 1)
+                               for grp in LAYER_GROUPS), "cuda")
+    xin = [[_bf16(syn.activations(wl, 1, grp[0], s)) for s in range(4)] for grp in LAYER_GROUPS]
+    ys = [torch.empty((1, p.m), dtype=torch.bfloat16, device="cuda") for p in projs]
+    group_bytes = [sum(projs[w].w_bytes for w in grp) for grp in LAYER_GROUPS]
+
+    def call(gi, i):
+        grp = LAYER_GROUPS[gi]
+        mats = [projs[w].mats[i % copies] for w in grp]
+        if len(grp) == 1:
+            H.hss_apply(mats[0], xin[gi][i % 4], ys[grp[0]], ws)
+        else:
+            H.hss_apply_group(mats, xin[gi][i % 4], [ys[w] for w in grp], ws)
+
+    def step(i):
+        for gi in range(len(LAYER_GROUPS)):
+            call(gi, i)
+
+    def step_7(i):
+        for gi, grp in enumerate(LAYER_GROUPS):
+            for w in grp:
+                H.hss_apply(projs[w].mats[i % copies], xin[gi][i % 4], ys[w], ws)
+
+    K = args.steps
+    trials = timer.graph(step, K, args.warmup)
+    ms = sorted(trials)[len(trials) // 2]
+    # the config's own 256-token sequence, and the seven-launch order, for reference
+    seq = timer.graph(step, wl.tokens, 5) if K != wl.tokens else trials
+    ms7 = sorted(timer.graph(step_7, wl.tokens, 5))[len(trials) // 2]
+
+    # per-launch durations: HIP events around every launch on the library's
+    # stream (torch's current stream), the GPU queue pre-filled with flushes
+    # so that the events bracket the kernels and not the host's enqueue
+    ev_tokens = min(K, 32)
+    per = [[] for _ in LAYER_GROUPS]
+    for rep in range(max(1, math.ceil(K / ev_tokens))):
+        for _ in range(24):
+            timer.flush()
+        evs = []
+        for i in range(ev_tokens):
+            for gi in range(len(LAYER_GROUPS)):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                call(gi, rep * ev_tokens + i)
+                e1.record()
+                evs.append((gi, e0, e1))
+        torch.cuda.synchronize()
+        for gi, e0, e1 in evs:
+            per[gi].append(e0.elapsed_time(e1))
+    per_ms = [sorted(v)[len(v) // 2] for v in per]
+    launches = []
+    for gi, grp in enumerate(LAYER_GROUPS):
+        launches.append({"group": GROUP_NAMES[gi], "projections": [wl.proj_names[w] for w in grp],
+                         "algorithmic_bytes": group_bytes[gi], "us_median": per_ms[gi] * 1e3,
+                         "gbs": group_bytes[gi] / (per_ms[gi] * 1e-3) / 1e9,
+                         "hbm_frac": group_bytes[gi] / (per_ms[gi] * 1e-3) / 1e9 / HBM_PEAK_GBS})
+    dom = max(range(len(LAYER_GROUPS)), key=lambda g: per_ms[g])
+    roof = _hbm_roofline(group_bytes[dom], per_ms[dom], f"k_decode ({GROUP_NAMES[dom]} launch of the decoder layer)",
+                         _measured_traffic(f"decoder_layer.{GROUP_NAMES[dom]}"))
+    roof["launch_duration_us"] = per_ms[dom] * 1e3
+    roof["traffic_unit"] = "HBM bytes per launch (FETCH_SIZE x read scale + WRITE_SIZE x write scale)"
+    res = {"ms_per_token": ms, "trials_ms_per_token": trials, "ms_per_token_pct": _pct(trials),
+           "tokens_per_s": 1 / (ms * 1e-3), "bytes_per_token": tok_bytes,
+           "gbs": tok_bytes / (ms * 1e-3) / 1e9, "hbm_frac": tok_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "layer_copies": copies, "launches_per_token": len(LAYER_GROUPS), "launches": launches,
+           "seq256_ms_per_token_pct": _pct(seq), "ms_per_token_7_launches": ms7,
+           "stream_ms_per_token": timer.eager(step, K, 5)}
+    del projs
+    torch.cuda.empty_cache()
+    return res, roof
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle's CSR apply of the same decoder layer
+# ---------------------------------------------------------------------------
+
+def _cpu_model():
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _cpu_baseline(seconds):
+    import numpy as np
     import oracle as O
     import hss_synth as syn
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
-    m, n = W.shape
-    k = O.topk_count(m, n, *cfg.frac)
-    t_split = time.perf_counter()
-    ref = O.split_csr(W, O.BF16, k)
-    t_split = time.perf_counter() - t_split
-    S64 = O.dense_from_csr(m, n, ref["row_ptr"], ref["col_idx"], ref["values"], O.BF16)
-    U64, V64 = O.widen(U, O.BF16), O.widen(V, O.BF16)
-    xs = [O.widen(syn.activations(cfg, 1, 0, step), O.BF16) for step in range(8)]
-    O.apply_factored(S64, U64, V64, xs[0])  # first-touch
-    calls, t0 = 0, time.perf_counter()
-    while True:
-        O.apply_factored(S64, U64, V64, xs[calls % len(xs)])
-        calls += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or calls >= 100000:
-            break
-    return {"value": calls / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{calls} decode tokens (b=1) of the 4096x4096 top-5% CSR + rank-256 layer "
-                      f"through the fp64 oracle factored apply (dense S, BLAS), {el:.1f} s; "
-                      f"oracle split of the same W took {t_split:.1f} s (not in value)"}
+    from threadpoolctl import threadpool_limits
+    wl = syn.WORKLOADS["decoder_layer"]
+    cores = len(os.sched_getaffinity(0))
+    t_prep = time.perf_counter()
+    mats = []
+    for which in range(7):
+        W = syn.weight(wl, which)
+        m, n = W.shape
+        sp = O.split_csr(W, O.BF16, O.topk_count(m, n, *wl.frac))
+        U, V = syn.factors(m, n, wl.rank[which], "bf16", wl.seed, which)
+        mats.append((m, n, sp["row_ptr"], sp["col_idx"], sp["values"], O.widen(U, O.BF16), O.widen(V, O.BF16)))
+        del W, sp
+    xs = [[O.widen(syn.activations(wl, 1, grp[0], s), O.BF16) for s in range(4)] for grp in LAYER_GROUPS]
+    t_prep = time.perf_counter() - t_prep
+
+    def token(i):
+        for gi, grp in enumerate(LAYER_GROUPS):
+            for w in grp:
+                m, n, rp, ci, v, U64, V64 = mats[w]
+                O.apply_csr(m, n, rp, ci, v, O.BF16, U64, V64, xs[gi][i % 4])
+
+    def run(threads, budget):
+        with threadpool_limits(limits=threads):
+            token(0)
+            calls, t0 = 0, time.perf_counter()
+            while True:
+                token(calls)
+                calls += 1
+                el = time.perf_counter() - t0
+                if el >= budget or calls >= 100000:
+                    return calls, el
+    calls, el = run(cores, seconds)
+    calls1, el1 = run(1, seconds / 2)
+    tok_bytes = sum(len(mm[3]) * 6 + 4 * (mm[0] + 1) + (mm[0] + mm[1]) * mm[5].shape[1] * 2 for mm in mats)
+    return {"value": calls / el, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "cpu_model": _cpu_model(), "single_thread_tokens_per_s": calls1 / el1,
+            "gbs": tok_bytes * calls / el / 1e9,
+            "sample": f"{calls} decode tokens (b=1) of the decoder layer's 7 projections (top-3% CSR + rank 409) "
+                      f"through the fp64 oracle apply_csr (scipy.sparse CSR times x, plus (x V) U^T), "
+                      f"{el:.1f} s with BLAS at {cores} threads; {calls1} tokens in {el1:.1f} s at 1 thread; "
+                      f"oracle split of the 7 weights took {t_prep:.1f} s (not in value)"}
+
+
+# ---------------------------------------------------------------------------
+# Other workloads
+# ---------------------------------------------------------------------------
+
+def _single_layer(H, timer, args, key, b_list, ws_b, extra_routes=None):
+    import torch
+    import hss_synth as syn
+    wl = syn.WORKLOADS[key]
+    W = _dev(syn.weight(wl), wl.dtype)
+    L = Layer(H, W, "csr" if wl.fmt == "csr" else "2:4", wl.frac, wl.rank[0], wl.seed, dtype=wl.dtype)
+    _log(f"{key} ready: {L.copies} rotation copies")
+    ws = L.mats[0].workspace(ws_b)
+    out = {"w_bytes": L.w_bytes, "rotation_copies": L.copies}
+    for b in b_list:
+        xs, ys = _acts(wl, b, 0, 4, L.m, wl.dtype)
+        steps = max(8, args.steps if b == 1 else args.steps // 4)
+        trials = timer.graph(_apply_loop(H, L, xs, ys, ws), steps, args.warmup)
+        ms = sorted(trials)[len(trials) // 2]
+        out[f"b{b}"] = {"ms": ms, "ms_pct": _pct(trials), "tokens_per_s": b / (ms * 1e-3),
+                        "roofline": _hbm_roofline(L.w_bytes, ms, f"hss_apply b={b} (one call)")}
+    return L, W, ws, out
+
+
+def _routes(H, timer, L, wl, batches, routes, skip):
+    import hss_synth as syn
+    res = {}
+    for bq in batches:
+        wsq = L.mats[0].workspace(bq)
+        xq, yq = _acts(wl, bq, 0, 4, L.m)
+        row = {}
+        for route in routes:
+            if skip(route, bq):
+                continue
+            with H.option("batch_route", route):
+                row[route] = sorted(timer.graph(_apply_loop(H, L, xq, yq, wsq), 16, 4))[timer.trials // 2] * 1e3
+        res[f"b{bq}_us"] = row
+    return res
+
+
+def _others(H, timer, args, extra):
+    import numpy as np
+    import torch
+    import hss_synth as syn
+
+    # 1024^2 fp32, top 5 %, rank 64, b = 1 (launch-bound correctness scale)
+    L1, W1, _, r1 = _single_layer(H, timer, args, "csr1024_f32", [1], 1)
+    extra["csr1024_f32"] = r1
+    del L1, W1
+
+    # 4096^2 5 % + rank 256: b = 1, 16; 16-bit columns; routes; hierarchical; dense-and-sparse
+    wl = syn.WORKLOADS["csr4096"]
+    L, W, ws, r2 = _single_layer(H, timer, args, "csr4096", [1, 16], 16)
+    m, n = L.m, L.n
+    xs, ys = _acts(wl, 1, 0, 16, m)
+    L16 = type("L16", (), {"mats": [A.with_col16() for A in L.mats]})
+    bytes16 = L.split.k * (2 + 2) + 4 * (m + 1) + (m + n) * wl.rank[0] * 2
+    t16 = timer.graph(_apply_loop(H, L16, xs, ys, ws), args.steps, args.warmup)
+    ms16 = sorted(t16)[len(t16) // 2]
+    r2["b1_col16"] = {"ms": ms16, "tokens_per_s": 1 / (ms16 * 1e-3),
+                      "roofline": _hbm_roofline(bytes16, ms16, "hss_apply b=1, 16-bit columns")}
+    del L16
+    r2["batch_routes"] = _routes(H, timer, L, wl, (8, 16, 64, 128, 256), ("decode", "spmm", "densify"),
+                                 lambda rt, b: (rt == "decode" and b > 64) or (rt == "densify" and b < 24))
+    extra["csr4096"] = r2
+
+    # hierarchical form: RCM order of S's support (host), concentration ratio
+    # before / after it, 2 x 2 block factors (seeded stand-ins, ranks 96
+    # diagonal / 32 off: R = 256 as in the flat layer) packed into flat
+    # factors, decode b = 1
+    rp_h = L.split.row_ptr.cpu().numpy()
+    ci_h = L.split.col_idx.cpu().numpy()
+    t0 = time.perf_counter()
+    perm = H.hss_rcm_order(rp_h, ci_h, n)
+    rcm_ms = (time.perf_counter() - t0) * 1e3
+    pos = np.empty(n, dtype=np.int64)
+    pos[perm] = np.arange(n)
+    rows_h = np.repeat(np.arange(m), np.diff(rp_h))
+    bw = [int(np.abs(rows_h - ci_h).max()), int(np.abs(pos[rows_h] - pos[ci_h]).max())]
+    perm_d = torch.from_numpy(perm).cuda()
+    rho = [float(H.hss_concentration(W)[0]), float(H.hss_concentration(W, perm_d)[0])]
+    rd, ro = 96, 32
+    hU, hVt = [], []
+    for blk in range(4):
+        rb = rd if blk in (0, 3) else ro
+        Ub, Vb = syn.factors(m // 2, n // 2, rb, "bf16", wl.seed, 10 + blk)
+        hU.append(_bf16(Ub))
+        hVt.append(_bf16(np.ascontiguousarray(Vb.T)))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    Ucat, Vtcat = H.hss_hier_pack(hU, hVt, m, n, perm_d)
+    e1.record()
+    torch.cuda.synchronize()
+    pack_ms = e0.elapsed_time(e1)
+    sp = L.split
+    LH = type("LH", (), {"mats": [H.HSSMatrix("csr", m, n, torch.bfloat16, U=Ucat.clone(), Vt=Vtcat.clone(),
+                                              row_ptr=sp.row_ptr.clone(), col_idx=sp.col_idx.clone(),
+                                              values=sp.values.clone(), nnz=sp.k) for _ in range(L.copies)]})
+    th = timer.graph(_apply_loop(H, LH, xs, ys, ws), args.steps, args.warmup)
+    msh = sorted(th)[len(th) // 2]
+    R_h = 2 * (rd + ro)
+    extra["hier2x2_4096_b1"] = {
+        "ms": msh, "tokens_per_s": 1 / (msh * 1e-3), "ranks_diag_off": [rd, ro], "packed_rank": R_h,
+        "factor_bytes_compact": (m + n) * (rd + ro) * 2, "factor_bytes_stored": (m + n) * R_h * 2,
+        "rcm_host_ms": rcm_ms, "pack_ms": pack_ms, "rho_identity_rcm": rho, "bandwidth_identity_rcm": bw}
+    del LH, Ucat, Vtcat, hU, hVt, perm_d
+
+    # dense-and-sparse form of the same weight: 0.5 % outliers in CSR (this
+    # library's split) + a 4-bit quantised dense part (seeded stand-in codes
+    # and levels), decode b = 1 and 8
+    spo = H.hss_split(W, "csr", frac=(5, 1000))
+    codes, levels = syn.quantised_standin(m, n, "bf16", wl.seed)
+    codes_d, levels_d = torch.from_numpy(codes).cuda(), _bf16(levels)
+    bytes_dq = m * n // 2 + m * 16 * 2 + spo.k * (2 + 4) + 4 * (m + 1)
+    dq_copies = max(1, math.ceil(GIB / bytes_dq))
+    LDQ = type("LDQ", (), {"mats": [H.HSSMatrix("csr", m, n, torch.bfloat16, row_ptr=spo.row_ptr.clone(),
+                                                col_idx=spo.col_idx.clone(), values=spo.values.clone(), nnz=spo.k,
+                                                dq_codes=codes_d.clone(), dq_levels=levels_d.clone())
+                                   for _ in range(dq_copies)]})
+    dq = {"bytes_per_apply": bytes_dq, "outliers": spo.k, "rotation_copies": dq_copies}
+    for bq in (1, 8):
+        xq, yq = _acts(wl, bq, 0, 4, m)
+        tq = timer.graph(_apply_loop(H, LDQ, xq, yq, ws), max(8, args.steps // (1 if bq == 1 else 4)), args.warmup)
+        msq = sorted(tq)[len(tq) // 2]
+        dq[f"b{bq}"] = {"ms": msq, "tokens_per_s": bq / (msq * 1e-3),
+                        "roofline": _hbm_roofline(bytes_dq, msq, f"k_decode_dq b={bq}")}
+    extra["dense_sparse_4096_q4"] = dq
+    del LDQ, codes_d, levels_d, spo
+
+    # split (offline, once per weight)
+    sms = []
+    for _ in range(5):
+        e0.record()
+        H.hss_split(W, "csr", frac=wl.frac, check_finite=False)
+        e1.record()
+        torch.cuda.synchronize()
+        sms.append(e0.elapsed_time(e1))
+    split_ms = sorted(sms)[2]
+    extra["split_4096sq_bf16"] = {"ms": split_ms, "w_read_gbs": m * n * 2 / (split_ms * 1e-3) / 1e9}
+    del L, W
+    torch.cuda.empty_cache()
+
+    # 11008 x 4096 2:4, rank 64, b = 1, 8, 64, and its routes
+    wl3 = syn.WORKLOADS["nm24_11008x4096"]
+    L3, W3, _, r3 = _single_layer(H, timer, args, "nm24_11008x4096", list(wl3.batches), 64)
+    r3["batch_routes"] = _routes(H, timer, L3, wl3, (2, 8, 16, 64), ("smfmac", "decode", "densify"),
+                                 lambda rt, b: (rt == "decode" and b > 8) or (rt == "densify" and b < 16))
+    extra["nm24_11008x4096"] = r3
+    del L3, W3
+    torch.cuda.empty_cache()
+
+    # prefill: 8192^2 CSR 3 %, rank 512, b = 2048 (matrix cores; rotation keeps
+    # the densify's read of S honest), and the low-rank products alone
+    wl5 = syn.WORKLOADS["csr8192_prefill"]
+    W5 = _bf16(syn.weight(wl5))
+    L5 = Layer(H, W5, "csr", wl5.frac, wl5.rank[0], wl5.seed, rotation_bytes=GIB / 4)
+    _log(f"8192^2 layer ready: {L5.copies} rotation copies")
+    b = wl5.batches[0]
+    ws5 = L5.mats[0].workspace(b)
+    xs5, ys5 = _acts(wl5, b, 0, 2, L5.m)
+    t5 = timer.graph(_apply_loop(H, L5, xs5, ys5, ws5), 8, 2)
+    ms5 = sorted(t5)[len(t5) // 2]
+    lr = type("LR", (), {"mats": [H.HSSMatrix("csr", L5.m, L5.n, torch.bfloat16, U=mat.U, Vt=mat.Vt,
+                                              row_ptr=torch.zeros(L5.m + 1, dtype=torch.int32, device="cuda"),
+                                              nnz=0) for mat in L5.mats]})
+    t5l = timer.graph(_apply_loop(H, lr, xs5, ys5, ws5), 8, 2)
+    ms5_lr = sorted(t5l)[len(t5l) // 2]
+    lr_flops = 2.0 * b * L5.r * (L5.m + L5.n)
+    lr_tf = lr_flops / (ms5_lr * 1e-3) / 1e12
+    extra["prefill_8192sq_b2048"] = {
+        "ms": ms5, "ms_pct": _pct(t5), "tokens_per_s": b / (ms5 * 1e-3),
+        "useful_tflops": L5.flops(b) / (ms5 * 1e-3) / 1e12,
+        "dense_equiv_tflops": 2.0 * b * L5.m * L5.n / (ms5 * 1e-3) / 1e12,
+        "lowrank_only_ms": ms5_lr, "lowrank_tflops": lr_tf, "lowrank_mfma_frac": lr_tf / BF16_PEAK_TFLOPS,
+        "roofline": {"bound": "mfma", "achieved": lr_tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": lr_tf / BF16_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "low-rank products (T^T = X V, Y = T U^T) of one call with an empty S",
+                     "algorithmic_flops_per_call": lr_flops}}
+    del lr
+
+    # training step on the same layer, b = 2048: forward, parameter gradients
+    # (hss_grad) and the input gradient (apply of the transposed layer)
+    A5 = L5.mats[0]
+    t0 = time.perf_counter()
+    At5 = H.hss_transposed_layer(A5)
+    torch.cuda.synchronize()
+    at_ms = (time.perf_counter() - t0) * 1e3
+    gs5 = [_bf16(syn.random_matrix(b, L5.m, "bf16", seed=70 + i, kind="normal", scale=1.0)) for i in range(2)]
+    gsz = ctypes.c_size_t(0)
+    H._lib.check(H._lib.lib.hss_grad_workspace_size(ctypes.byref(A5.struct), b, ctypes.byref(gsz)), "ws")
+    gws = torch.empty(gsz.value, dtype=torch.uint8, device="cuda")
+    wst = At5.workspace(b)
+    dxs = torch.empty((b, L5.n), dtype=torch.bfloat16, device="cuda")
+    ms_fwd = timer.eager(lambda i: H.hss_apply(A5, xs5[i % 2], ys5[i % 2], ws5), 10, 3)
+    ms_grad = timer.eager(lambda i: H.hss_grad(A5, xs5[i % 2], gs5[i % 2], ws=gws), 10, 3)
+    ms_dx = timer.eager(lambda i: H.hss_apply(At5, gs5[i % 2], dxs, wst), 10, 3)
+    ms_gather = timer.eager(lambda i: H.hss_gather_values(A5.values, At5.perm_from_s), 10, 3)
+    grad_flops = 2.0 * b * (2 * L5.r * (L5.m + L5.n) + L5.split.k)
+    step_ms = ms_fwd + ms_grad + ms_dx + ms_gather
+    extra["train_8192sq_b2048"] = {
+        "step_ms": step_ms, "tokens_per_s": b / (step_ms * 1e-3),
+        "useful_tflops": (2 * L5.flops(b) + grad_flops) / (step_ms * 1e-3) / 1e12,
+        "forward_ms": ms_fwd, "grad_ms": ms_grad, "grad_useful_tflops": grad_flops / (ms_grad * 1e-3) / 1e12,
+        "dX_ms": ms_dx, "gather_values_ms": ms_gather, "transposed_layer_setup_ms": at_ms,
+        "note": "one copy of the weights (compute-bound shape), stream launches"}
+    del At5, gs5, gws, wst, dxs, A5, L5, W5
+    torch.cuda.empty_cache()
 
 
 def main():
     args = _args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: the library has no multi-GPU path "
-              "(run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
         sys.exit(2)
     sys.path.insert(0, ROOT)
     import torch
 
-    import hss_synth as syn
     import sparse_rank_linear_hss_amd as H
 
     torch.cuda.set_device(0)
-    out = {}
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -236,295 +605,39 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    timer = Timer(args.trials)
 
-    # ---------------- headline: 4096^2 CSR 5 %, rank 256, decode ----------------
-    cfg = syn.WORKLOADS["csr4096"]
-    W_np = syn.weight(cfg)
-    W = _bf16(W_np)
-    L = Layer(H, W, "csr", cfg.frac, cfg.rank[0], cfg.seed)
-    m, n = L.m, L.n
-    nnz_head, bytes_head, copies_head = L.split.k, L.w_bytes, L.copies
-    _log(f"4096^2 layer ready: nnz={nnz_head}, {copies_head} rotation copies")
-    ws = L.mats[0].workspace(16)
-    xs, ys = _acts(cfg, 1, 0, 16, m)
-    steps = args.steps
-    ms_graph = _time_graph(_apply_loop(H, L, xs, ys, ws), steps, args.warmup)
-    ms_stream = _time(_apply_loop(H, L, xs, ys, ws), steps, args.warmup)
-    ms_hot = _time_graph(_apply_loop(H, L, xs, ys, ws, rotate=False), steps, args.warmup)
-    gbs = bytes_head / (ms_graph * 1e-3) / 1e9
-    headline = {"ms_graph": ms_graph, "ms_stream": ms_stream, "ms_hot_graph": ms_hot,
-                "gbs_stream": bytes_head / (ms_stream * 1e-3) / 1e9, "rotation_copies": copies_head}
-    # split (offline, once per weight)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    sms = []
-    for _ in range(5):
-        e0.record()
-        H.hss_split(W, "csr", frac=cfg.frac, check_finite=False)
-        e1.record()
-        torch.cuda.synchronize()
-        sms.append(e0.elapsed_time(e1))
-    split_ms = sorted(sms)[2]
-
+    head, roof = _decoder_layer(H, timer, args)
     extra = {}
     if not args.only_headline:
-        # same layer with 16-bit column indices (4 instead of 6 bytes per entry)
-        L16 = type("L16", (), {"mats": [A.with_col16() for A in L.mats]})
-        bytes16 = nnz_head * (2 + 2) + 4 * (m + 1) + (m + n) * cfg.rank[0] * 2
-        ms16c = _time_graph(_apply_loop(H, L16, xs, ys, ws), steps, args.warmup)
-        extra["csr4096_b1_col16"] = {"ms": ms16c, "tokens_per_s": 1 / (ms16c * 1e-3),
-                                     "gbs": bytes16 / (ms16c * 1e-3) / 1e9, "bytes_per_apply": bytes16}
-        del L16
-
-        # same layer, batch 16 (the default route: gather SpMM)
-        xs16, ys16 = _acts(cfg, 16, 0, 4, m)
-        ms16 = _time_graph(_apply_loop(H, L, xs16, ys16, ws), max(1, steps // 4), 20)
-        extra["csr4096_b16"] = {"ms": ms16, "tokens_per_s": 16 / (ms16 * 1e-3),
-                                "gbs": bytes_head / (ms16 * 1e-3) / 1e9}
-        # batched CSR routes side by side (HSS_CSR_BATCH_ROUTE forces one):
-        # fused decode passes, gather SpMM, S densified for the matrix cores
-        routes = {}
-        for bq in (8, 16, 64, 128, 256):
-            wsq = L.mats[0].workspace(bq)
-            xq, yq = _acts(cfg, bq, 0, 4, m)
-            row = {}
-            for route in ("decode", "spmm", "densify"):
-                if (route == "decode" and bq > 64) or (route == "densify" and bq < 24):
-                    continue
-                os.environ["HSS_CSR_BATCH_ROUTE"] = route
-                row[route] = _time_graph(_apply_loop(H, L, xq, yq, wsq), max(1, steps // 10), 10) * 1e3
-            os.environ.pop("HSS_CSR_BATCH_ROUTE")
-            routes[f"b{bq}_us"] = row
-        extra["csr4096_batch_routes"] = routes
-
-        # hierarchical form: RCM order of S's support (host), concentration
-        # ratio before / after it, 2 x 2 block factors (seeded stand-ins,
-        # ranks 96 diagonal / 32 off, so R = 256 as in the flat layer) packed
-        # into flat factors, decode b = 1 with the headline's rotation
-        import numpy as np
-        rp_h = L.split.row_ptr.cpu().numpy()
-        ci_h = L.split.col_idx.cpu().numpy()
-        t0 = time.perf_counter()
-        perm = H.hss_rcm_order(rp_h, ci_h, n)
-        rcm_ms = (time.perf_counter() - t0) * 1e3
-        pos = np.empty(n, dtype=np.int64)
-        pos[perm] = np.arange(n)
-        rows_h = np.repeat(np.arange(m), np.diff(rp_h))
-        bw = [int(np.abs(rows_h - ci_h).max()), int(np.abs(pos[rows_h] - pos[ci_h]).max())]
-        perm_d = torch.from_numpy(perm).cuda()
-        rho = [float(H.hss_concentration(W)[0]), float(H.hss_concentration(W, perm_d)[0])]
-        rd, ro = 96, 32
-        hU, hVt = [], []
-        for blk in range(4):
-            rb = rd if blk in (0, 3) else ro
-            Ub, Vb = syn.factors(m // 2, n // 2, rb, "bf16", cfg.seed, 10 + blk)
-            hU.append(_bf16(Ub))
-            hVt.append(_bf16(np.ascontiguousarray(Vb.T)))
-        e0.record()
-        Ucat, Vtcat = H.hss_hier_pack(hU, hVt, m, n, perm_d)
-        e1.record()
-        torch.cuda.synchronize()
-        pack_ms = e0.elapsed_time(e1)
-        sp = L.split
-        h_mats = [H.HSSMatrix("csr", m, n, torch.bfloat16, U=Ucat.clone(), Vt=Vtcat.clone(),
-                              row_ptr=sp.row_ptr.clone(), col_idx=sp.col_idx.clone(), values=sp.values.clone(),
-                              nnz=sp.k) for _ in range(copies_head)]
-        LH = type("LH", (), {"mats": h_mats})
-        msh = _time_graph(_apply_loop(H, LH, xs, ys, ws), steps, args.warmup)
-        R_h = 2 * (rd + ro)
-        extra["hier2x2_4096_b1"] = {
-            "ms": msh, "tokens_per_s": 1 / (msh * 1e-3), "gbs": bytes_head / (msh * 1e-3) / 1e9,
-            "ranks_diag_off": [rd, ro], "packed_rank": R_h,
-            "factor_bytes_compact": (m + n) * (rd + ro) * 2, "factor_bytes_stored": (m + n) * R_h * 2,
-            "rcm_host_ms": rcm_ms, "pack_ms": pack_ms, "rho_identity_rcm": rho, "bandwidth_identity_rcm": bw}
-        del h_mats, LH, Ucat, Vtcat, hU, hVt, perm_d
-        del L
-        torch.cuda.empty_cache()
-
-        # dense-and-sparse form of the same weight: 0.5 % outliers in CSR (this
-        # library's split) + a 4-bit quantised dense part (seeded stand-in codes
-        # and levels), decode b = 1 and 8, cold rotation
-        spo = H.hss_split(W, "csr", frac=(5, 1000))
-        codes, levels = syn.quantised_standin(m, n, "bf16", cfg.seed)
-        codes_d = torch.from_numpy(codes).cuda()
-        levels_d = _bf16(levels)
-        bytes_dq = m * n // 2 + m * 16 * 2 + spo.k * (2 + 4) + 4 * (m + 1)
-        dq_copies = max(1, math.ceil(GIB / bytes_dq))
-        dq_mats = [H.HSSMatrix("csr", m, n, torch.bfloat16, row_ptr=spo.row_ptr.clone(),
-                               col_idx=spo.col_idx.clone(), values=spo.values.clone(), nnz=spo.k,
-                               dq_codes=codes_d.clone(), dq_levels=levels_d.clone())
-                   for _ in range(dq_copies)]
-        LDQ = type("LDQ", (), {"mats": dq_mats})
-        dq = {"bytes_per_apply": bytes_dq, "outliers": spo.k, "rotation_copies": dq_copies}
-        for bq in (1, 8):
-            xq, yq = _acts(cfg, bq, 0, 4, m)
-            msq = _time_graph(_apply_loop(H, LDQ, xq, yq, ws), max(1, steps // (1 if bq == 1 else 4)),
-                              args.warmup)
-            dq[f"b{bq}"] = {"ms": msq, "tokens_per_s": bq / (msq * 1e-3), "gbs": bytes_dq / (msq * 1e-3) / 1e9,
-                            "hbm_frac": bytes_dq / (msq * 1e-3) / 1e9 / HBM_PEAK_GBS}
-        extra["dense_sparse_4096_q4"] = dq
-        del dq_mats, LDQ, codes_d, levels_d, spo
-        torch.cuda.empty_cache()
-
-        # 11008 x 4096 2:4, rank 64, b = 1, 8, 64
-        wl_nm = syn.WORKLOADS["nm24_11008x4096"]
-        W3 = _bf16(syn.weight(wl_nm))
-        L3 = Layer(H, W3, "2:4", wl_nm.frac, wl_nm.rank[0], wl_nm.seed)
-        _log(f"2:4 layer ready: {L3.copies} rotation copies")
-        ws3 = L3.mats[0].workspace(64)
-        r3 = {}
-        for b in wl_nm.batches:
-            xs3, ys3 = _acts(wl_nm, b, 0, 4, L3.m)
-            ms3 = _time_graph(_apply_loop(H, L3, xs3, ys3, ws3), max(1, steps // 8), 20)
-            r3[f"b{b}"] = {"ms": ms3, "tokens_per_s": b / (ms3 * 1e-3),
-                           "gbs": L3.w_bytes / (ms3 * 1e-3) / 1e9,
-                           "hbm_frac": L3.w_bytes / (ms3 * 1e-3) / 1e9 / HBM_PEAK_GBS}
-        extra["nm24_11008x4096"] = dict(r3, w_bytes=L3.w_bytes)
-        # the same layer on each route the call can take (sparse matrix cores,
-        # fused decode passes, densified GEMM), us per call
-        routes3 = {}
-        for bq in (2, 8, 16, 64):
-            xq, yq = _acts(wl_nm, bq, 0, 4, L3.m)
-            wsq3 = L3.mats[0].workspace(bq)
-            row = {}
-            for route in ("smfmac", "decode", "densify"):
-                if (route == "decode" and bq > 8) or (route == "densify" and bq < 16):
-                    continue
-                os.environ["HSS_CSR_BATCH_ROUTE"] = route
-                row[route] = _time_graph(_apply_loop(H, L3, xq, yq, wsq3), max(1, steps // 10), 10) * 1e3
-            os.environ.pop("HSS_CSR_BATCH_ROUTE")
-            routes3[f"b{bq}_us"] = row
-        extra["nm24_11008x4096_batch_routes"] = routes3
-        del L3, W3
-        torch.cuda.empty_cache()
-
-        # decoder layer: 7 projections per token, b = 1
-        wl_dl = syn.WORKLOADS["decoder_layer"]
-        projs = []
-        for which in range(7):
-            Wp = _bf16(syn.weight(wl_dl, which))
-            projs.append(Layer(H, Wp, "csr", wl_dl.frac, wl_dl.rank[which], wl_dl.seed, which,
-                               rotation_bytes=GIB / 7))
-            del Wp
-        tok_bytes = sum(p.w_bytes for p in projs)
-        _log(f"decoder layer ready: {tok_bytes} compressed bytes per token")
-        # q, k, v read the same input, as do gate and up: 4 launches per token
-        # (grouped); the 7-launch order is timed as well.
-        groups = [[0, 1, 2], [3], [4, 5], [6]]
-        ws4 = torch.zeros(max(H.hss_apply_group_workspace_size([projs[w].mats[0] for w in grp], 1)
-                              for grp in groups), dtype=torch.uint8, device="cuda")
-        xin = [[_bf16(syn.activations(wl_dl, 1, grp[0], s)) for s in range(4)] for grp in groups]
-        ys4 = [torch.empty((1, p.m), dtype=torch.bfloat16, device="cuda") for p in projs]
-
-        def layer_step(i):
-            for gi, grp in enumerate(groups):
-                mats = [projs[w].mats[i % len(projs[w].mats)] for w in grp]
-                if len(grp) == 1:
-                    H.hss_apply(mats[0], xin[gi][i % 4], ys4[grp[0]], ws4)
-                else:
-                    H.hss_apply_group(mats, xin[gi][i % 4], [ys4[w] for w in grp], ws4)
-
-        def layer_step_7(i):
-            for gi, grp in enumerate(groups):
-                for w in grp:
-                    H.hss_apply(projs[w].mats[i % len(projs[w].mats)], xin[gi][i % 4], ys4[w], ws4)
-        ms4 = _time_graph(layer_step, wl_dl.tokens, 5)
-        ms4_7 = _time_graph(layer_step_7, wl_dl.tokens, 5)
-        extra["decoder_layer_7proj"] = {"ms_per_token": ms4, "tokens_per_s": 1 / (ms4 * 1e-3),
-                                        "gbs": tok_bytes / (ms4 * 1e-3) / 1e9, "bytes_per_token": tok_bytes,
-                                        "tokens": wl_dl.tokens, "launches_per_token": 4,
-                                        "ms_per_token_7_launches": ms4_7}
-        del projs
-        torch.cuda.empty_cache()
-
-        # prefill: 8192^2 CSR 3 %, rank 512, b = 2048
-        wl_pf = syn.WORKLOADS["csr8192_prefill"]
-        W5 = _bf16(syn.weight(wl_pf))
-        L5 = Layer(H, W5, "csr", wl_pf.frac, wl_pf.rank[0], wl_pf.seed, rotation_bytes=GIB / 4)
-        _log(f"8192^2 layer ready: {L5.copies} rotation copies")
-        b = wl_pf.batches[0]
-        ws5 = L5.mats[0].workspace(b)
-        xs5, ys5 = _acts(wl_pf, b, 0, 2, L5.m)
-        ms5 = _time(_apply_loop(H, L5, xs5, ys5, ws5), 10, 3)
-        # the low-rank products alone (same matrix with an empty S): their MFMA rate
-        lr = [H.HSSMatrix("csr", L5.m, L5.n, torch.bfloat16, U=mat.U, Vt=mat.Vt,
-                          row_ptr=torch.zeros(L5.m + 1, dtype=torch.int32, device="cuda"), nnz=0)
-              for mat in L5.mats]
-        lr_layer = type("LR", (), {"mats": lr})
-        ms5_lr = _time(_apply_loop(H, lr_layer, xs5, ys5, ws5), 10, 3)
-        lr_flops = 2.0 * b * L5.r * (L5.m + L5.n)
-        dense_equiv = 2.0 * b * L5.m * L5.n
-        extra["prefill_8192sq_b2048"] = {
-            "ms": ms5, "tokens_per_s": b / (ms5 * 1e-3),
-            "useful_tflops": L5.flops(b) / (ms5 * 1e-3) / 1e12,
-            "lowrank_only_ms": ms5_lr,
-            "lowrank_tflops": lr_flops / (ms5_lr * 1e-3) / 1e12,
-            "lowrank_mfma_frac": lr_flops / (ms5_lr * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-            "dense_equiv_tflops": dense_equiv / (ms5 * 1e-3) / 1e12}
-
-        # training step on the same layer, b = 2048: forward, parameter
-        # gradients (hss_grad) and the input gradient (forward apply of the
-        # transposed layer); S^T's pattern is built once on the host, its
-        # values are gathered on the device every step
-        A5 = L5.mats[0]
-        t0 = time.perf_counter()
-        At5 = H.hss_transposed_layer(A5)
-        torch.cuda.synchronize()
-        at_ms = (time.perf_counter() - t0) * 1e3
-        gs5 = [_bf16(syn.random_matrix(b, L5.m, "bf16", seed=70 + i, kind="normal", scale=1.0)) for i in range(2)]
-        gsz = ctypes.c_size_t(0)
-        H._lib.check(H._lib.lib.hss_grad_workspace_size(ctypes.byref(A5.struct), b, ctypes.byref(gsz)), "ws")
-        gws = torch.empty(gsz.value, dtype=torch.uint8, device="cuda")
-        wst = At5.workspace(b)
-        dxs = torch.empty((b, L5.n), dtype=torch.bfloat16, device="cuda")
-        ms_fwd = _time(lambda i: H.hss_apply(A5, xs5[i % 2], ys5[i % 2], ws5), 10, 3)
-        ms_grad = _time(lambda i: H.hss_grad(A5, xs5[i % 2], gs5[i % 2], ws=gws), 10, 3)
-        ms_dx = _time(lambda i: H.hss_apply(At5, gs5[i % 2], dxs, wst), 10, 3)
-        ms_gather = _time(lambda i: H.hss_gather_values(A5.values, At5.perm_from_s), 10, 3)
-        grad_flops = 2.0 * b * (2 * L5.r * (L5.m + L5.n) + L5.split.k)
-        step_ms = ms_fwd + ms_grad + ms_dx + ms_gather
-        step_flops = 2 * L5.flops(b) + grad_flops
-        extra["train_8192sq_b2048"] = {
-            "step_ms": step_ms, "tokens_per_s": b / (step_ms * 1e-3),
-            "useful_tflops": step_flops / (step_ms * 1e-3) / 1e12,
-            "forward_ms": ms_fwd, "grad_ms": ms_grad, "grad_useful_tflops": grad_flops / (ms_grad * 1e-3) / 1e12,
-            "dX_ms": ms_dx, "gather_values_ms": ms_gather, "transposed_layer_setup_ms": at_ms,
-            "note": "one copy of the weights (compute-bound shape; no rotation)"}
-        del At5, gs5, gws, wst, dxs, A5
-        del L5, lr, W5
-        torch.cuda.empty_cache()
-
+        _others(H, timer, args, extra)
+    ms = head["ms_per_token"]
     out = {
         "metric": METRIC,
-        "value": 1.0 / (ms_graph * 1e-3),
+        "value": 1.0 / (ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": steps,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_graph,
+        "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "4096x4096 bf16, Student-t(3) x0.02 + 0.5% outliers x20, top-5% CSR "
-                               "(838,860 nnz) + rank-256 factors, decode b=1, cold HBM rotation, HIP-graph replay",
-                   "m": m, "n": n, "nnz": nnz_head, "rank": cfg.rank[0], "batch": 1},
-        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": _measured_traffic(),
-                     "traffic_unit": "HBM bytes per launch (FETCH_SIZE x read scale + WRITE_SIZE x write scale)",
-                     "kernel": "k_decode (one launch per decode token)",
-                     "algorithmic_bytes_per_launch": bytes_head},
-        "compressed_gbs": gbs,
-        "headline_detail": headline,
-        "split_ms": split_ms,
-        "split_w_read_gbs": m * n * 2 / (split_ms * 1e-3) / 1e9,
+        "config": {"workload": "decoder layer, 7 projections (q,k,v,o 4096x4096; gate,up 11008x4096; down "
+                               "4096x11008), bf16 Student-t(3) x0.02, each top-3% CSR + rank-409 factors; batch-1 "
+                               "decode, q/k/v and gate/up as grouped calls (4 launches per token); cold HBM "
+                               f"({head['layer_copies']} layer copies, 1 GiB flush before each timed region), "
+                               "HIP-graph replay",
+                   "tokens_per_step": 1, "batch": 1, "rank": 409, "kept_fraction": "3%"},
+        "roofline": roof,
+        "compressed_gbs_per_token": head["gbs"],
+        "hbm_frac_per_token": head["hbm_frac"],
+        "decoder_layer_7proj": head,
     }
     out.update(extra)
-    if not args.no_cpu_baseline:
-        U, V = syn.factors(m, n, cfg.rank[0], "bf16", cfg.seed)
-        out["cpu_baseline"] = _cpu_baseline(cfg, W_np, U, V, args.cpu_seconds)
-    else:
-        out["cpu_baseline"] = None
+    out["cpu_baseline"] = None if args.no_cpu_baseline else _cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

@@ -47,7 +47,11 @@ extern "C" {
 #endif
 
 #define HSS_VERSION_MAJOR 1
-#define HSS_VERSION_MINOR 4
+#define HSS_VERSION_MINOR 5
+
+/* Largest batch (columns of X) one hss_apply / hss_apply_group / hss_grad
+ * call takes: decode (1) up to a prefill of 2048 tokens. */
+#define HSS_MAX_BATCH 2048
 
 typedef enum {
   HSS_OK = 0,
@@ -67,6 +71,41 @@ typedef enum {
 
 /* Library version: 100 * major + minor. */
 int hss_version(void);
+
+/* Process-wide diagnostic switches, for comparing execution routes and for
+ * testing the decode kernel's fallback.  Each starts at the value of the
+ * environment variable named below (read once, at the first lookup), else
+ * at its default; hss_set_option changes it for every later call.  Changing
+ * a switch while another thread is inside a call of this library gives that
+ * call either value.
+ *   HSS_OPT_BATCH_ROUTE   (HSS_CSR_BATCH_ROUTE = decode | spmm | densify |
+ *       smfmac): 0 = by batch size (default), 1 = the fused decode kernel,
+ *       2 = the gather SpMM, 3 = densify + matrix cores, 4 = the sparse
+ *       matrix cores; forces a bf16 call with b >= 2 onto that route where
+ *       the route supports the matrix.  Workspace sizes cover every route.
+ *   HSS_OPT_GRAD_DS_ROUTE (HSS_GRAD_DS_ROUTE = sparse | dense): 0 = by batch
+ *       size (default), 1 = sampled product, 2 = dense G^T X then gather.
+ *       Query hss_grad_workspace_size with the same setting.
+ *   HSS_OPT_DECODE_SPIN   (HSS_DECODE_SPIN = count): polls of a stale T word
+ *       before a block computes that T row itself (default 4096).
+ *   HSS_OPT_DECODE_MERGED (HSS_DECODE_MERGED = 0): 1 (default) = T rows
+ *       produced inside the row blocks where they fit, 0 = separate
+ *       producer blocks.
+ *   HSS_OPT_DECODE_FORCE_LOCAL: 1 = every decode block ignores the T words
+ *       and computes every T row itself (same arithmetic, same bits), to
+ *       test that fallback; default 0.
+ * hss_set_option returns HSS_ERR_INVALID_ARG for an unknown option or a
+ * value out of range (routes 0..4 / 0..2, spin >= 0, flags 0..1);
+ * hss_get_option returns -1 for an unknown option. */
+typedef enum {
+  HSS_OPT_BATCH_ROUTE = 0,
+  HSS_OPT_GRAD_DS_ROUTE = 1,
+  HSS_OPT_DECODE_SPIN = 2,
+  HSS_OPT_DECODE_MERGED = 3,
+  HSS_OPT_DECODE_FORCE_LOCAL = 4
+} hss_option;
+hss_status hss_set_option(hss_option opt, int32_t value);
+int32_t hss_get_option(hss_option opt);
 
 /* Static text for a status code (never NULL). */
 const char* hss_status_string(hss_status s);
@@ -144,9 +183,16 @@ hss_status hss_get_error(const void* ws, hipStream_t stream);
  *     int32 (n <= 65536), 2 bytes per entry less to read ([HSS] implementation
  *     section: narrower indices for the stored sparse part).  Convert the
  *     int32 columns hss_split writes with hss_csr_cols_to_u16.
- *   U  dtype[m*r]  row-major m x r.
- *   Vt dtype[r*n]  row-major r x n, i.e. the n x r factor V stored
- *                  column-major, so that V^T x reads contiguous rows.
+ *   U  dtype[m*r]  row-major m x r.  bf16 U 16-byte aligned takes the
+ *                  vector path for any r: U is read as the aligned 16-byte
+ *                  pieces that cover each row, so the last piece may reach
+ *                  up to 14 bytes past U's end (inside the same aligned 16
+ *                  bytes, never into another page).
+ *   Vt dtype[r*n]  the n x r factor V of the pages stored column-major
+ *                  (equivalently V^T row-major, r x n), so that each of the r
+ *                  dot products of T = V^T x reads one contiguous stream.
+ *                  hss_transpose turns a row-major V into this form once per
+ *                  weight.
  *   flags & HSS_DQ4: a quantised dense part D is added to the layer
  *     ([SQZ] dense-and-sparse: W ~= D + S with S the outliers, e.g. the top
  *     0.5 % by |w| from hss_split, and D the residual quantised offline):
@@ -193,11 +239,19 @@ hss_status hss_apply_workspace_size(const hss_matrix* A, int32_t b, size_t* byte
  *   HSS_F32 : X, Y fp32; accumulation fp32.
  *   HSS_BF16: X bf16; products accumulated in fp32; Y bf16 = round-to-nearest-
  *             even of the fp32 result.
- * ws: at least hss_apply_workspace_size() bytes, ZERO-FILLED once before its
- *     first use.  The library keeps state in it between calls (a call
- *     counter), so the caller must not write to it afterwards; any number of
- *     calls, with any matrices and batch sizes, may then share it as long as
- *     they are ordered (same stream or events).
+ * ws: at least hss_apply_workspace_size() bytes, initialised ONCE by
+ *     hss_apply_workspace_init before its first apply.  The fused decode
+ *     kernel keeps state in it from call to call: a 32-bit call epoch, 64
+ *     arrival counters (all in the first 16 KiB) and the tagged words through
+ *     which its blocks hand T = V^T x to each other (a word is used only when
+ *     its tag is the current epoch + 1, so a word left by an earlier call is
+ *     never taken for this one's).  The caller must not write to the
+ *     workspace after the init.  Any number of calls, with any matrices and
+ *     batch sizes, may share one workspace if they are ORDERED (one stream,
+ *     or events between streams); two calls that overlap in time must use
+ *     different workspaces -- overlapping calls on one workspace can make
+ *     both return wrong values with no error.  The epoch wraps after 2^32 - 1
+ *     calls and skips the tag that a zero-filled word carries.
  * Execution: bf16 2:4 with 2 <= b <= 64 (n % 128 == 0; nm_values, nm_meta
  * and X 16-byte aligned) runs on the sparse matrix cores: S's stored values
  * and 2-bit indices are the operands of v_smfmac as they are, with fp32
@@ -211,24 +265,31 @@ hss_status hss_apply_workspace_size(const hss_matrix* A, int32_t b, size_t* byte
  * row; fp32 accumulation).  Otherwise one fused kernel per 8 columns.  On
  * the matrix-core routes (the sparse one included) zeros in an operand
  * multiply X too, so a NaN or infinity in X can reach any output of its
- * batch row.  The
- * environment variable HSS_CSR_BATCH_ROUTE = decode | spmm | densify |
- * smfmac forces a bf16 call with b >= 2 onto that route where the route
- * supports the matrix (for comparing them); the workspace size covers every
- * route.
+ * batch row.  HSS_OPT_BATCH_ROUTE (hss_set_option) forces a bf16 call with
+ * b >= 2 onto one route, for comparing them.
  * HSS_DQ4 matrices always run the fused dense-and-sparse kernel (up to 8
  * columns per pass; no workspace: hss_apply_workspace_size returns 0 and ws
  * may be NULL).
  * Returns HSS_ERR_INVALID_ARG for: A or X or Y null, unknown fmt/dtype,
  *   unknown flags (or HSS_COL16 with a 2:4 matrix or n > 65536; HSS_DQ4 with
  *   a 2:4 matrix, odd n or null dq arrays),
- *   m, n <= 0, r < 0, b < 1, b*m, b*n, m*n, r*(m+n) >= 2^31,
+ *   m, n <= 0, r < 0, b < 1 or b > HSS_MAX_BATCH, b*m, b*n, m*n,
+ *   r*(m+n) >= 2^31,
  *   nnz < 0, required arrays null, n % 4 != 0 for 2:4, X overlapping Y.
  *   HSS_ERR_WORKSPACE for a null or short workspace.  HSS_ERR_HIP if a launch
  *   fails.
  */
 hss_status hss_apply(const hss_matrix* A, int32_t b, const void* X, void* Y, void* ws,
                      size_t ws_bytes, hipStream_t stream);
+
+/* Puts an apply workspace (ws_bytes bytes, device) in its initial state, on
+ * `stream`: every byte zero, written by a kernel (no memset node, so the call
+ * may also be captured into a HIP graph).  Call it once per workspace before
+ * its first hss_apply / hss_apply_group, and again only when no call using
+ * the workspace can still be running.  ws_bytes == 0 does nothing.
+ * HSS_ERR_INVALID_ARG for a null ws with ws_bytes > 0; HSS_ERR_HIP if the
+ * launch fails. */
+hss_status hss_apply_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Grouped apply: G matrices that read the same X, e.g. the q, k and v
@@ -244,8 +305,9 @@ hss_status hss_apply(const hss_matrix* A, int32_t b, const void* X, void* Y, voi
  *   1 <= G <= HSS_MAX_GROUP; every A[g] valid for hss_apply with batch b, all
  *   with the same n, dtype and fmt (m, r and the arrays may differ).
  *   Y[g] device outputs, pairwise disjoint and disjoint from X.
- *   ws: at least hss_apply_group_workspace_size() bytes, zero-filled once,
- *   the same state rules as hss_apply (it may also serve hss_apply calls).
+ *   ws: at least hss_apply_group_workspace_size() bytes, initialised once
+ *   by hss_apply_workspace_init; the same state rules as hss_apply (it may
+ *   also serve hss_apply calls).
  * Returns HSS_ERR_INVALID_ARG for: A, X or Y null, G out of range, any matrix
  *   invalid, mismatched n/dtype/fmt, overlapping outputs; HSS_ERR_WORKSPACE for
  *   a null or short workspace; HSS_ERR_HIP if a launch fails.
@@ -338,8 +400,8 @@ hss_status hss_hier_pack(hss_dtype dt, int32_t m, int32_t n, const int32_t* r, c
  *   inputs give the same bits on every call.  dS is a sampled product on
  *   the vector units below 512 columns; from 512 on, the dense G^T X on the
  *   matrix cores (its m*n fp32 values in the workspace) then a gather
- *   (HSS_GRAD_DS_ROUTE = sparse | dense forces one; query the workspace
- *   size with the same setting).
+ *   (HSS_OPT_GRAD_DS_ROUTE forces one; query the workspace size with the
+ *   same setting).
  *   ws: at least hss_grad_workspace_size() bytes (no state kept).
  *   HSS_ERR_UNSUPPORTED: an fp32 or dense-and-sparse layer, or
  *   n * round8(b) * 2 or m * round8(b) * 2 >= 2^31.  HSS_ERR_INVALID_ARG: as

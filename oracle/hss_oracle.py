@@ -23,14 +23,14 @@ Sources (web pages; section names as printed on each page)
           - section "実装と運用パターン" (implementation patterns): S stored as
             indices + values (COO/CSR), U and V dense; the forward pass splits
             into one sparse product plus two small dense products.
+          - section "順列と階層的整列" (permutation and hierarchical alignment; its
+            vision rewrite "置換と階層的整列"): the concentration ratio rho =
+            (sum of |W| over the diagonal blocks) / (sum of |W|); a Reverse
+            Cuthill-McKee order of rows and columns pulls large |w| towards the
+            diagonal; the factorisation works on a 2 x 2 block partition, the
+            off-diagonal blocks at a low rank (8), the diagonal ones higher (32).
 [HASSLE]  aibr.jp/archives/82335 (explainer of HASSLE-free), section
           "3.中核となる技術的要素": N:M sparsity as the GPU-friendly structure.
-          section "順列と階層的整列" (permutation and hierarchical alignment; its
-          vision rewrite "置換と階層的整列"): the concentration ratio rho =
-          (sum of |W| over the diagonal blocks) / (sum of |W|); a Reverse
-          Cuthill-McKee order of rows and columns pulls large |w| towards the
-          diagonal; the factorisation works on a 2 x 2 block partition, the
-          off-diagonal blocks at a low rank (8), the diagonal ones higher (32).
 [SQZ]     aibr.jp/archives/208940 (explainer of SqueezeLLM), section
           "3.中核となる技術的要素": the dense-and-sparse decomposition W = D + S
           (the rare outliers kept exactly in a CSR matrix S, the dense rest D
@@ -113,7 +113,10 @@ def narrow(a64, dtype):
 
 
 def bits_equal(a, b):
-    """Bitwise equality of two stored arrays of the same storage type."""
+    """Bitwise equality of two stored arrays of the same storage type: the same
+    shape, the same element width and every bit pattern equal.  It compares
+    patterns, not values: +0 and -0 differ, and a NaN equals only the same NaN
+    pattern."""
     a = np.ascontiguousarray(a)
     b = np.ascontiguousarray(b)
     if a.shape != b.shape or a.dtype.itemsize != b.dtype.itemsize:
@@ -300,6 +303,18 @@ def apply_factored(S64, U64, V64, X64):
     if U64.shape[1] > 0:
         Y = Y + (X64 @ V64) @ U64.T
     return Y
+
+
+def apply_csr(m, n, row_ptr, col_idx, values, dtype, U64, V64, X64):
+    """Factored forward with S kept in CSR, as the pages store it (indices +
+    values): the sparse product through scipy.sparse, plus (X V) U^T, fp64."""
+    import scipy.sparse
+    S = scipy.sparse.csr_matrix((widen(values, dtype), np.asarray(col_idx, dtype=np.int64),
+                                 np.asarray(row_ptr, dtype=np.int64)), shape=(m, n))
+    Y = (S @ X64.T).T
+    if U64.shape[1] > 0:
+        Y = Y + (X64 @ V64) @ U64.T
+    return np.asarray(Y)
 
 
 def apply_dense(S64, U64, V64, X64):
@@ -533,7 +548,10 @@ def hier_factors(R64p, r_diag, r_off):
 
 
 def hier_param_count(k, m, n, r_diag, r_off):
-    """Stored parameters: k sparse values plus, per block, (rows + cols) * rank."""
+    """Stored parameters of the one-level 2 x 2 form: k sparse values plus, for
+    each block, (its rows + its columns) * its rank -- r_diag on the blocks
+    (0, 0) and (1, 1), r_off on (0, 1) and (1, 0); rows split at m // 2,
+    columns at n // 2.  Ranks are taken as given (no clamp to a block's side)."""
     m1, n1 = m // 2, n // 2
     m2, n2 = m - m1, n - n1
     return int(k) + (m1 + n1 + m2 + n2) * r_diag + (m1 + n2 + m2 + n1) * r_off

@@ -12,18 +12,23 @@ HIP stream into the C calls -- every step runs in the library's HIP kernels.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 from dataclasses import dataclass, field
 from typing import Optional
 
 import torch
 
-from ._lib import (HSS_BF16, HSS_COL16, HSS_DQ4, HSS_ERR_NONFINITE, HSS_F32, HSS_FMT_2OF4, HSS_FMT_CSR, HSS_OK,
-                   HSSError, HssMatrixStruct, LIB_PATH, check, lib, status_string)
+from ._lib import (HSS_BF16, HSS_COL16, HSS_DQ4, HSS_ERR_NONFINITE, HSS_F32, HSS_FMT_2OF4, HSS_FMT_CSR,
+                   HSS_MAX_BATCH, HSS_OK, HSS_OPT_BATCH_ROUTE, HSS_OPT_DECODE_FORCE_LOCAL, HSS_OPT_DECODE_MERGED,
+                   HSS_OPT_DECODE_SPIN, HSS_OPT_GRAD_DS_ROUTE, HSSError, HssMatrixStruct, LIB_PATH, check, lib,
+                   status_string)
 
 __all__ = [
     "hss_version", "hss_topk_count", "hss_split_workspace_size", "hss_split", "hss_get_error",
-    "hss_apply_workspace_size", "hss_apply", "hss_apply_group_workspace_size", "hss_apply_group",
+    "hss_set_option", "hss_get_option", "option", "HSS_MAX_BATCH",
+    "hss_apply_workspace_size", "hss_apply_workspace_init", "apply_workspace", "hss_apply",
+    "hss_apply_group_workspace_size", "hss_apply_group",
     "hss_csr_cols_to_u16", "HSS_COL16", "HSS_DQ4",
     "hss_rcm_order", "hss_concentration", "hss_hier_pack",
     "hss_grad", "hss_csr_transpose", "hss_gather_values", "hss_transpose", "hss_transposed_layer", "hss_backward",
@@ -58,6 +63,38 @@ def _dev(t: torch.Tensor):
 
 def hss_version() -> int:
     return lib.hss_version()
+
+
+# Diagnostic switches (hss_set_option); route names as the environment
+# variables spell them.
+_OPTS = {"batch_route": HSS_OPT_BATCH_ROUTE, "grad_ds_route": HSS_OPT_GRAD_DS_ROUTE,
+         "decode_spin": HSS_OPT_DECODE_SPIN, "decode_merged": HSS_OPT_DECODE_MERGED,
+         "decode_force_local": HSS_OPT_DECODE_FORCE_LOCAL}
+_OPT_WORDS = {"batch_route": {"auto": 0, "decode": 1, "spmm": 2, "densify": 3, "smfmac": 4},
+              "grad_ds_route": {"auto": 0, "sparse": 1, "dense": 2}}
+
+
+def hss_set_option(name: str, value) -> None:
+    """Set a process-wide diagnostic switch: batch_route (auto | decode | spmm |
+    densify | smfmac), grad_ds_route (auto | sparse | dense), decode_spin
+    (int), decode_merged (0 | 1), decode_force_local (0 | 1)."""
+    v = _OPT_WORDS.get(name, {}).get(value, value)
+    check(lib.hss_set_option(_OPTS[name], int(v)), f"hss_set_option({name})")
+
+
+def hss_get_option(name: str) -> int:
+    return int(lib.hss_get_option(_OPTS[name]))
+
+
+@contextlib.contextmanager
+def option(name: str, value):
+    """Scope a diagnostic switch: set on entry, the previous value restored on exit."""
+    old = hss_get_option(name)
+    hss_set_option(name, value)
+    try:
+        yield
+    finally:
+        check(lib.hss_set_option(_OPTS[name], old), f"hss_set_option({name})")
 
 
 def hss_topk_count(m: int, n: int, num: int, den: int) -> int:
@@ -197,16 +234,40 @@ class HSSMatrix:
                          values=self.values, nnz=self.nnz, dq_codes=self.dq_codes, dq_levels=self.dq_levels)
 
     def workspace(self, b: int, device=None) -> torch.Tensor:
-        """Zero-filled workspace for batch b (cached per device and size)."""
+        """Initialised apply workspace for batch b on the current stream.
+
+        Cached per (device, stream, size): the decode kernel keeps state in
+        its workspace from call to call, so calls that may overlap in time --
+        those on different streams -- must not share one.  Calls on one
+        stream are ordered and share it safely."""
         size = hss_apply_workspace_size(self, b)
         if device is None:
             held = [t for t in (self.U, self.row_ptr, self.values, self.nm_values, self.dq_codes) if t is not None]
             device = held[0].device
-        dev = device
-        key = (str(dev), size)
+        dev = torch.device(device)
+        key = (str(dev), _stream(dev), size)
         if key not in self._ws:
-            self._ws[key] = torch.zeros(max(size, 1), dtype=torch.uint8, device=dev)
+            if torch.cuda.is_current_stream_capturing():
+                # its init kernel would be captured too and reset the state on
+                # every replay, so that replays could take each other's T words
+                raise RuntimeError("create the workspace before graph capture and pass it as ws=")
+            self._ws[key] = apply_workspace(size, dev)
         return self._ws[key]
+
+
+def hss_apply_workspace_init(ws: torch.Tensor) -> torch.Tensor:
+    """Put an apply workspace in its initial state (a kernel on the current
+    stream); call once before its first apply."""
+    check(lib.hss_apply_workspace_init(_ptr(ws), ws.numel(), _stream(ws.device)), "hss_apply_workspace_init")
+    return ws
+
+
+def apply_workspace(size: int, device) -> torch.Tensor:
+    """A new apply workspace of `size` bytes on `device`, initialised on the
+    current stream.  Calls that share it must be ordered (one stream, or
+    events between streams)."""
+    ws = torch.empty(max(int(size), 1), dtype=torch.uint8, device=device)
+    return hss_apply_workspace_init(ws)
 
 
 def hss_apply_workspace_size(A: HSSMatrix, b: int) -> int:
@@ -256,7 +317,9 @@ def hss_apply_group(As, X: torch.Tensor, Ys=None, ws: Optional[torch.Tensor] = N
     if Ys is None:
         Ys = [torch.empty((b, A.m), dtype=A.dtype, device=dev) for A in As]
     if ws is None:
-        ws = torch.zeros(hss_apply_group_workspace_size(As, b), dtype=torch.uint8, device=dev)
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError("create the workspace before graph capture and pass it as ws=")
+        ws = apply_workspace(hss_apply_group_workspace_size(As, b), dev)
     yp = (ctypes.c_void_p * len(As))(*[_ptr(Y) for Y in Ys])
     check(lib.hss_apply_group(_group_structs(As), len(As), b, _ptr(X), yp, _ptr(ws), ws.numel(),
                               _stream(dev)), "hss_apply_group")

@@ -19,6 +19,12 @@ HSS_F32 = 0
 HSS_BF16 = 1
 HSS_FMT_CSR = 0
 HSS_FMT_2OF4 = 1
+HSS_MAX_BATCH = 2048
+HSS_OPT_BATCH_ROUTE = 0
+HSS_OPT_GRAD_DS_ROUTE = 1
+HSS_OPT_DECODE_SPIN = 2
+HSS_OPT_DECODE_MERGED = 3
+HSS_OPT_DECODE_FORCE_LOCAL = 4
 HSS_COL16 = 1  # hss_matrix.flags: CSR col_idx holds uint16 columns
 HSS_DQ4 = 2    # hss_matrix.flags: a 4-bit quantised dense part (dq_codes, dq_levels)
 
@@ -60,6 +66,9 @@ def _load():
                                      c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_size_t, c_void_p]),
         "hss_get_error": (ctypes.c_int, [c_void_p, c_void_p]),
+        "hss_set_option": (ctypes.c_int, [ctypes.c_int, c_int32]),
+        "hss_get_option": (c_int32, [ctypes.c_int]),
+        "hss_apply_workspace_init": (ctypes.c_int, [c_void_p, c_size_t, c_void_p]),
         "hss_apply_workspace_size": (ctypes.c_int, [P(HssMatrixStruct), c_int32, P(c_size_t)]),
         "hss_apply": (ctypes.c_int, [P(HssMatrixStruct), c_int32, c_void_p, c_void_p, c_void_p,
                                      c_size_t, c_void_p]),

@@ -22,7 +22,11 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhss.so")
 ARCH = os.environ.get("HSS_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["hss_api.cpp", "split.hip", "apply.hip", "decode.hip", "mfma.hip", "hier.hip", "spmm.hip", "grad.hip", "nm_mma.hip"]
+# decode.hip's kernel instances are spread over the decode_inst_*.hip files so
+# that they compile in parallel (the longest first).
+SOURCES = ["decode_inst_bf16_csr_b1.hip", "decode_inst_bf16_csr_bn.hip", "decode_inst_bf16_csr16_b1.hip",
+           "decode_inst_bf16_csr16_bn.hip", "decode_inst_bf16_nm.hip", "decode_inst_f32.hip", "decode.hip",
+           "mfma.hip", "spmm.hip", "nm_mma.hip", "grad.hip", "split.hip", "apply.hip", "hier.hip", "hss_api.cpp"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -52,7 +56,7 @@ def _compile(src):
 
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(os.cpu_count() or 8, 16, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]

@@ -21,12 +21,9 @@
 //   (nm_mma.hip)         values and metadata fed to v_smfmac as stored, T
 //                        from a small prologue.
 //
-// The environment variable HSS_CSR_BATCH_ROUTE = decode | spmm | densify |
-// smfmac forces the route of a bf16 batch (where that route supports it),
-// for measuring one against another.
-#include <cstdlib>
-#include <cstring>
-
+// HSS_OPT_BATCH_ROUTE (hss_set_option; first value from the environment
+// variable HSS_CSR_BATCH_ROUTE) forces the route of a bf16 batch (where that
+// route supports it), for measuring one against another.
 #include "hss_internal.h"
 
 namespace hss {
@@ -79,14 +76,15 @@ static constexpr int kSpmmMinCols = 3, kSpmmMaxCols = 128;
 // X: the call's input (the sparse matrix cores need it 16-byte aligned), or
 // null when sizing a workspace.
 static Route batch_route(const hss_matrix* A, int b, const void* X) {
-  if (b < 2) return R_DECODE;  // one column: always the fused decode kernel (no environment lookup)
+  if (b < 2) return R_DECODE;  // one column: always the fused decode kernel
   const bool sp = spmm_supported(A, b), mf = mfma_supported(A, b);
   const bool nm = nm_mma_supported(A, b) && (uintptr_t)X % 16 == 0;
-  if (const char* e = std::getenv("HSS_CSR_BATCH_ROUTE")) {
-    if (!std::strcmp(e, "decode")) return R_DECODE;
-    if (!std::strcmp(e, "spmm") && sp) return R_SPMM;
-    if (!std::strcmp(e, "densify") && mf) return R_MFMA;
-    if (!std::strcmp(e, "smfmac") && nm) return R_NM;
+  switch (option(HSS_OPT_BATCH_ROUTE)) {
+    case 1: return R_DECODE;
+    case 2: if (sp) return R_SPMM; break;
+    case 3: if (mf) return R_MFMA; break;
+    case 4: if (nm) return R_NM; break;
+    default: break;
   }
   if (nm && b >= kNmMinColsDefault) return R_NM;
   if (sp && b >= kSpmmMinCols && (b <= kSpmmMaxCols || !mf)) return R_SPMM;
@@ -135,6 +133,26 @@ hss_status launch_apply(const hss_matrix* A, int b, const void* X, void* Y, void
     launch_decode(A, bc, static_cast<const char*>(X) + (size_t)c0 * A->n * es,
                   static_cast<char*>(Y) + (size_t)c0 * A->m * es, ws, stream);
   }
+  return hipGetLastError() == hipSuccess ? HSS_OK : HSS_ERR_HIP;
+}
+
+// Every byte of p[0 .. bytes) set to zero by plain vector stores (a kernel,
+// not a memset, so it may be captured into a graph): the aligned middle as
+// 16-byte stores, the unaligned head and tail bytewise.
+__global__ __launch_bounds__(256) void k_zero_fill(unsigned char* p, size_t bytes) {
+  const size_t head = min(bytes, (size_t)((16u - ((uintptr_t)p & 15u)) & 15u));
+  const size_t nvec = (bytes - head) / 16, tail0 = head + nvec * 16;
+  const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x, nth = (size_t)gridDim.x * blockDim.x;
+  u32x4* v = reinterpret_cast<u32x4*>(p + head);
+  for (size_t i = tid; i < nvec; i += nth) v[i] = u32x4{0u, 0u, 0u, 0u};
+  if (tid < head) p[tid] = 0;
+  if (tid < bytes - tail0) p[tail0 + tid] = 0;
+}
+
+hss_status launch_zero_fill(void* p, size_t bytes, hipStream_t s) {
+  const size_t vec = bytes / 16 + 1;
+  const unsigned blocks = (unsigned)(vec / 256 + 1 < 2048 ? vec / 256 + 1 : 2048);
+  hipLaunchKernelGGL(k_zero_fill, dim3(blocks), dim3(256), 0, s, static_cast<unsigned char*>(p), bytes);
   return hipGetLastError() == hipSuccess ? HSS_OK : HSS_ERR_HIP;
 }
 

@@ -1,0 +1,11 @@
+// Instances of the fused decode kernel (bf16 2:4); the kernel is in decode_kernel.h.
+#include "decode_kernel.h"
+
+namespace hss {
+
+void decode_launch_bf16_nm(const GroupArgs& ga, unsigned grid, int bc, int uq, bool fast, int rpw, size_t lds,
+                           hipStream_t s) {
+  launch_fmt<HSS_BF16, HSS_FMT_2OF4>(ga, grid, bc, uq, fast, 0, rpw, lds, s);
+}
+
+}  // namespace hss

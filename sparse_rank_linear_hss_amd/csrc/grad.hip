@@ -196,17 +196,16 @@ static void launch_sddmm_pat(int lp, const SPattern& P, const uint16_t* Gt, cons
 // ---------------------------------------------------------------------------
 // Workspace: X^T, G^T, U^T, T^T, P^T and the GEMMs' split-K partials.
 // ---------------------------------------------------------------------------
-// dS route: the dense form from this batch on (or HSS_GRAD_DS_ROUTE =
-// sparse | dense).  Measured on the 8192 x 8192 3 % layer (sampled vs
+// dS route: the dense form from this batch on (or HSS_OPT_GRAD_DS_ROUTE:
+// 1 sampled, 2 dense).  Measured on the 8192 x 8192 3 % layer (sampled vs
 // dense, ms): b = 256 0.101 vs 0.127, b = 512 0.203 vs 0.170, b = 2048 1.15
 // vs 0.41.
 static constexpr int kDenseDsMinB = 512;
 
 static bool ds_dense(int b) {
-  if (const char* e = getenv("HSS_GRAD_DS_ROUTE")) {
-    if (!strcmp(e, "sparse")) return false;
-    if (!strcmp(e, "dense")) return true;
-  }
+  const int forced = option(HSS_OPT_GRAD_DS_ROUTE);
+  if (forced == 1) return false;
+  if (forced == 2) return true;
   return b >= kDenseDsMinB;
 }
 

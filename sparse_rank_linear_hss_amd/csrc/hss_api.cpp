@@ -2,6 +2,11 @@
 // Every check runs before any HIP call, so an error return has enqueued nothing.
 #include <limits.h>
 
+#include <algorithm>
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
+
 #include "hss_internal.h"
 
 namespace hss {  // grad.hip
@@ -14,6 +19,49 @@ hss_status launch_gather_values(int dt, int64_t nnz, const void* values, const i
                                 hipStream_t s);
 hss_status launch_transpose(int dt, int rows, int cols, const void* src, void* dst, hipStream_t s);
 hss_status launch_nm_to_csr(int m, int n, const uint32_t* meta, int32_t* row_ptr, int32_t* col, hipStream_t s);
+}  // namespace hss
+
+// ---------------------------------------------------------------------------
+// Diagnostic switches.  The first value of each comes from the environment
+// (read once, when the first switch is looked up); hss_set_option changes it
+// for the rest of the process.
+// ---------------------------------------------------------------------------
+namespace hss {
+
+namespace {
+constexpr int kNumOptions = 5;
+
+int env_route(const char* name, const char* const* words, int nwords) {
+  const char* e = std::getenv(name);
+  if (!e) return 0;
+  for (int i = 0; i < nwords; ++i)
+    if (!std::strcmp(e, words[i])) return i + 1;
+  return 0;
+}
+
+struct Options {
+  std::atomic<int> v[kNumOptions];
+  Options() {
+    static const char* const batch[] = {"decode", "spmm", "densify", "smfmac"};
+    static const char* const ds[] = {"sparse", "dense"};
+    v[HSS_OPT_BATCH_ROUTE] = env_route("HSS_CSR_BATCH_ROUTE", batch, 4);
+    v[HSS_OPT_GRAD_DS_ROUTE] = env_route("HSS_GRAD_DS_ROUTE", ds, 2);
+    const char* spin = std::getenv("HSS_DECODE_SPIN");
+    v[HSS_OPT_DECODE_SPIN] = spin ? std::max(0, atoi(spin)) : 4096;
+    const char* merged = std::getenv("HSS_DECODE_MERGED");
+    v[HSS_OPT_DECODE_MERGED] = (merged && merged[0] == '0') ? 0 : 1;
+    v[HSS_OPT_DECODE_FORCE_LOCAL] = 0;
+  }
+};
+
+Options& options() {
+  static Options o;  // initialised once, thread-safe
+  return o;
+}
+}  // namespace
+
+int option(int opt) { return options().v[opt].load(std::memory_order_relaxed); }
+
 }  // namespace hss
 
 namespace {
@@ -34,6 +82,24 @@ bool overlap(const void* a, size_t abytes, const void* b, size_t bbytes) {
 extern "C" {
 
 int hss_version(void) { return 100 * HSS_VERSION_MAJOR + HSS_VERSION_MINOR; }
+
+hss_status hss_set_option(hss_option opt, int32_t value) {
+  static const int32_t hi[] = {4, 2, INT32_MAX, 1, 1};
+  if ((int)opt < 0 || (int)opt >= hss::kNumOptions || value < 0 || value > hi[opt]) return HSS_ERR_INVALID_ARG;
+  hss::options().v[opt].store(value, std::memory_order_relaxed);
+  return HSS_OK;
+}
+
+int32_t hss_get_option(hss_option opt) {
+  if ((int)opt < 0 || (int)opt >= hss::kNumOptions) return -1;
+  return hss::option(opt);
+}
+
+hss_status hss_apply_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (ws_bytes == 0) return HSS_OK;
+  if (!ws) return HSS_ERR_INVALID_ARG;
+  return hss::launch_zero_fill(ws, ws_bytes, stream);
+}
 
 const char* hss_status_string(hss_status s) {
   switch (s) {
@@ -103,7 +169,7 @@ static hss_status check_matrix(const hss_matrix* A, int32_t b) {
     return HSS_ERR_INVALID_ARG;
   if ((A->flags & HSS_COL16) && (A->fmt != HSS_FMT_CSR || A->n > 65536)) return HSS_ERR_INVALID_ARG;
   const int64_t m = A->m, n = A->n, r = A->r;
-  if (m <= 0 || n <= 0 || r < 0 || b < 1) return HSS_ERR_INVALID_ARG;
+  if (m <= 0 || n <= 0 || r < 0 || b < 1 || b > HSS_MAX_BATCH) return HSS_ERR_INVALID_ARG;
   if (A->flags & HSS_DQ4) {
     if (A->fmt != HSS_FMT_CSR || n % 2 != 0 || !A->dq_codes || !A->dq_levels) return HSS_ERR_INVALID_ARG;
     if (r > 0) return HSS_ERR_UNSUPPORTED;

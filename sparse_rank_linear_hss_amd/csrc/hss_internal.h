@@ -104,6 +104,11 @@ __device__ __forceinline__ T uniform(T v) {
 
 // Host-side launchers (defined in the .hip files).
 namespace hss {
+// Process-wide diagnostic switches (hss_set_option); the environment gives
+// their first values, read once.  Cheap to call on every apply.
+int option(int opt);
+hss_status launch_zero_fill(void* p, size_t bytes, hipStream_t s);
+
 hss_status launch_split_csr(int dt, int m, int n, const void* W, int64_t k, int32_t* row_ptr,
                             int32_t* col_idx, void* values, void* residual, void* ws,
                             hipStream_t stream);

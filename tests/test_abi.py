@@ -30,7 +30,7 @@ def test_header_declares_the_boundary():
                  "hss_get_error", "hss_topk_count", "hss_status_string", "hss_version",
                  "hss_rcm_order", "hss_concentration", "hss_concentration_workspace_size", "hss_hier_pack",
                  "hss_grad", "hss_grad_workspace_size", "hss_csr_transpose", "hss_gather_values", "hss_transpose",
-                 "hss_nm24_to_csr"):
+                 "hss_nm24_to_csr", "hss_set_option", "hss_get_option", "hss_apply_workspace_init"):
         assert must in names
 
 
@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(hl):
 
 
 def test_version_and_strings(hl):
-    assert hl.hss_version() == 104
+    assert hl.hss_version() == 105
     for code in range(6):
         assert hl.status_string(code).startswith("HSS_")
 
@@ -132,7 +132,8 @@ def test_apply_rejects_bad_arguments(hl):
     assert _apply(hl, _matrix(hl, m=0)) == INV
     assert _apply(hl, _matrix(hl, r=-1)) == INV
     assert _apply(hl, _matrix(hl), b=0) == INV
-    assert _apply(hl, _matrix(hl, m=1 << 20), b=4096) == INV      # b*m >= 2^31
+    assert _apply(hl, _matrix(hl), b=hl.HSS_MAX_BATCH + 1) == INV   # batch beyond the contract
+    assert _apply(hl, _matrix(hl, m=1 << 20), b=2048) == INV      # b*m >= 2^31
     assert _apply(hl, _matrix(hl, U=None)) == INV
     assert _apply(hl, _matrix(hl, Vt=None)) == INV
     assert _apply(hl, _matrix(hl, nnz=-2)) == INV
@@ -149,6 +150,68 @@ def test_apply_rejects_bad_arguments(hl):
     assert lib.hss_apply_workspace_size(ctypes.byref(_matrix(hl, r=0, U=None, Vt=None)), 1,
                                         ctypes.byref(sz)) == 0
     assert sz.value >= 256
+
+
+def test_batch_range_is_1_to_2048(hl):
+    """b in [1, HSS_MAX_BATCH]: the sizing calls agree with the apply."""
+    INV = hl._lib.HSS_ERR_INVALID_ARG
+    lib = hl._lib.lib
+    sz = ctypes.c_size_t(0)
+    assert hl.HSS_MAX_BATCH == 2048
+    assert lib.hss_apply_workspace_size(ctypes.byref(_matrix(hl)), 2048, ctypes.byref(sz)) == 0
+    assert lib.hss_apply_workspace_size(ctypes.byref(_matrix(hl)), 2049, ctypes.byref(sz)) == INV
+    assert lib.hss_apply_workspace_size(ctypes.byref(_matrix(hl)), 0, ctypes.byref(sz)) == INV
+    arr = (ctypes.POINTER(hl._lib.HssMatrixStruct) * 1)(ctypes.pointer(_matrix(hl)))
+    assert lib.hss_apply_group_workspace_size(arr, 1, 2049, ctypes.byref(sz)) == INV
+    assert lib.hss_grad_workspace_size(ctypes.byref(_matrix(hl)), 2049, ctypes.byref(sz)) == INV
+
+
+def test_options_set_get_and_reject(hl):
+    """The diagnostic switches: each round-trips, bad ones are refused, and
+    the env-derived defaults are what the header states (no env set here)."""
+    INV = hl._lib.HSS_ERR_INVALID_ARG
+    lib = hl._lib.lib
+    L = hl._lib
+    defaults = {L.HSS_OPT_BATCH_ROUTE: 0, L.HSS_OPT_GRAD_DS_ROUTE: 0, L.HSS_OPT_DECODE_SPIN: 4096,
+                L.HSS_OPT_DECODE_MERGED: 1, L.HSS_OPT_DECODE_FORCE_LOCAL: 0}
+    for k in ("HSS_CSR_BATCH_ROUTE", "HSS_GRAD_DS_ROUTE", "HSS_DECODE_SPIN", "HSS_DECODE_MERGED"):
+        assert k not in os.environ
+    for opt, v in defaults.items():
+        assert lib.hss_get_option(opt) == v
+    assert lib.hss_get_option(5) == -1 and lib.hss_get_option(-1) == -1
+    for opt, bad in ((L.HSS_OPT_BATCH_ROUTE, 5), (L.HSS_OPT_GRAD_DS_ROUTE, 3), (L.HSS_OPT_DECODE_SPIN, -1),
+                     (L.HSS_OPT_DECODE_MERGED, 2), (L.HSS_OPT_DECODE_FORCE_LOCAL, -1), (7, 0)):
+        assert lib.hss_set_option(opt, bad) == INV
+    with hl.option("batch_route", "densify"):
+        assert hl.hss_get_option("batch_route") == 3
+        with hl.option("batch_route", "smfmac"):
+            assert hl.hss_get_option("batch_route") == 4
+        assert hl.hss_get_option("batch_route") == 3
+    assert hl.hss_get_option("batch_route") == 0
+    with hl.option("decode_spin", 7), hl.option("grad_ds_route", "dense"):
+        assert lib.hss_get_option(L.HSS_OPT_DECODE_SPIN) == 7 and hl.hss_get_option("grad_ds_route") == 2
+    for opt, v in defaults.items():
+        assert lib.hss_get_option(opt) == v
+
+
+def test_options_read_from_the_environment_once(hl):
+    """A fresh process takes the switches' first values from the environment."""
+    import subprocess
+    import sys
+    code = ("import sparse_rank_linear_hss_amd as h, os;"
+            "print(h.hss_get_option('batch_route'), h.hss_get_option('grad_ds_route'),"
+            " h.hss_get_option('decode_spin'), h.hss_get_option('decode_merged'));"
+            "os.environ['HSS_DECODE_SPIN'] = '5'; print(h.hss_get_option('decode_spin'))")
+    env = dict(os.environ, HSS_CSR_BATCH_ROUTE="spmm", HSS_GRAD_DS_ROUTE="dense", HSS_DECODE_SPIN="12",
+               HSS_DECODE_MERGED="0")
+    out = subprocess.run([sys.executable, "-c", code], env=env, cwd=ROOT, capture_output=True, text=True, check=True)
+    assert out.stdout.split() == ["2", "2", "12", "0", "12"]
+
+
+def test_workspace_init_rejects_bad_arguments(hl):
+    lib = hl._lib.lib
+    assert lib.hss_apply_workspace_init(None, 16, None) == hl._lib.HSS_ERR_INVALID_ARG
+    assert lib.hss_apply_workspace_init(None, 0, None) == 0           # nothing to do
 
 
 def _group(hl, mats, b=1, X=FAKE + 8192, Ys=None, ws=FAKE * 16, wsb=1 << 20):

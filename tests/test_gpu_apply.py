@@ -139,80 +139,41 @@ def test_apply_csr1024_f32_true_svd(H):
     _check(Y, O.F32, Yref, N)
 
 
-def _sampled_check(H, cfg, which, b, rows, step=0):
-    c = syn.WORKLOADS[cfg]
-    dtype = dt_of(c.dtype)
-    m, n = c.shapes[which]
-    r = c.rank[which]
-    ref = oracle_split(cfg, which)
-    U, V = syn.factors(m, n, r, dtype, c.seed, which)
-    X = syn.activations(c, b, which, step)
-    A = _matrix(H, "csr" if c.fmt == "csr" else "2:4", dtype, m, n, ref, U, V)
-    Y = to_host(H.hss_apply(A, to_dev(X, dtype)))
-    if rows is None:
-        rows = np.arange(m)
-    if c.fmt == "csr":
-        S_rows = O.csr_rows_dense(rows, n, ref["row_ptr"], ref["col_idx"], ref["values"], dtype)
-    else:
-        S_rows = O.dense_from_24(len(rows), n, ref["nm_values"][rows], ref["nm_meta"][rows], dtype)
-    Yref, N = O.apply_rows(S_rows, O.widen(U, dtype)[rows], O.widen(V, dtype), O.widen(X, dtype))
-    err = O.max_normalised_error(O.widen(Y[:, rows], dtype), Yref, N)
-    assert err <= O.TOL[dtype], f"max normalised error {err:.3e}"
-
-
-@pytest.mark.parametrize("b", [1, 16])
-def test_apply_csr4096_full(H, b):
-    _sampled_check(H, "csr4096", 0, b, None)
-
-
-@pytest.mark.parametrize("b", [1, 8, 64])
-def test_apply_nm24_11008x4096_sampled(H, b):
-    rows = np.random.default_rng(b).choice(11008, size=512, replace=False)
-    rows.sort()
-    _sampled_check(H, "nm24_11008x4096", 0, b, rows)
-
-
-@pytest.mark.parametrize("which", [0, 4, 6])
-def test_apply_decoder_layer_sampled(H, which):
-    m = syn.WORKLOADS["decoder_layer"].shapes[which][0]
-    rows = np.random.default_rng(which).choice(m, size=384, replace=False)
-    rows.sort()
-    for step in range(2):
-        _sampled_check(H, "decoder_layer", which, 1, rows, step)
-
-
-def test_apply_csr8192_prefill_sampled(H):
-    rows = np.random.default_rng(5).choice(8192, size=96, replace=False)
-    rows.sort()
-    _sampled_check(H, "csr8192_prefill", 0, 2048, rows)
-
-
 @pytest.mark.parametrize("fmt,dtype,b,m", [("csr", O.BF16, 1, 300), ("csr", O.F32, 3, 300), ("2:4", O.BF16, 8, 300),
                                            ("2:4", O.F32, 2, 300), ("csr", O.BF16, 1, 1030),
                                            ("2:4", O.BF16, 1, 1030), ("csr", O.BF16, 1, 100)])
-def test_apply_local_fallback_is_bitwise_identical(H, monkeypatch, fmt, dtype, b, m):
-    """With a zero poll budget every block computes the T rows it finds stale
-    itself; the result must be bit-identical to the normal hand-off (one bf16
-    CSR column: the T rows come from the row blocks themselves, 4, 2 and 1 per
-    block at m = 100, 300 and 1030)."""
-    n, r = 512, 40
-    monkeypatch.setenv("HSS_CSR_BATCH_ROUTE", "decode")   # the fused kernel's hand-off is what is tested
+def test_apply_local_fallback_is_bitwise_identical(H, hss_opt, fmt, dtype, b, m):
+    """Every block computing every T row itself (decode_force_local: no T word
+    is taken from the hand-off) must give the bits of the normal hand-off, and
+    so must a zero poll budget (a mix, depending on timing).  One bf16 CSR
+    column: the T rows come from the row blocks themselves, 4, 2 and 1 per
+    block at m = 100, 300 and 1030.  r = 40 and 41: U rows on and off the
+    16-byte grid."""
+    n = 512
+    hss_opt("batch_route", "decode")   # the fused kernel's hand-off is what is tested
     W = syn.random_matrix(m, n, dtype, seed=21, kind="t3")
     ref = O.split_csr(W, dtype, O.topk_count(m, n, 5, 100)) if fmt == "csr" else O.split_24(W, dtype)
-    U, V = _factors(m, n, r, dtype, 22)
-    X = syn.random_matrix(b, n, dtype, seed=23, kind="normal", scale=1.0)
-    A = _matrix(H, fmt, dtype, m, n, ref, U, V)
-    Xd = to_dev(X, dtype)
-    Y_normal = to_host(H.hss_apply(A, Xd))
-    monkeypatch.setenv("HSS_DECODE_SPIN", "0")
-    Y_local = to_host(H.hss_apply(A, Xd))
-    monkeypatch.delenv("HSS_DECODE_SPIN")
-    assert O.bits_equal(Y_normal, Y_local)
-    S64 = _dense_S(fmt, dtype, m, n, ref)
-    U64, V64, X64 = O.widen(U, dtype), O.widen(V, dtype), O.widen(X, dtype)
-    err = O.max_normalised_error(O.widen(Y_local, dtype), O.apply_factored(S64, U64, V64, X64),
-                                 O.normaliser(S64, U64, V64, X64))
-    assert err <= O.TOL[dtype]
+    Xd = None
+    for r in (40, 41):
+        U, V = _factors(m, n, r, dtype, 22)
+        X = syn.random_matrix(b, n, dtype, seed=23, kind="normal", scale=1.0)
+        A = _matrix(H, fmt, dtype, m, n, ref, U, V)
+        Xd = to_dev(X, dtype)
+        Y_normal = to_host(H.hss_apply(A, Xd))
+        hss_opt("decode_force_local", 1)
+        Y_forced = to_host(H.hss_apply(A, Xd))
+        hss_opt("decode_force_local", 0)
+        hss_opt("decode_spin", 0)
+        Y_spin0 = to_host(H.hss_apply(A, Xd))
+        hss_opt("decode_spin", 4096)
+        assert O.bits_equal(Y_normal, Y_forced), r
+        assert O.bits_equal(Y_normal, Y_spin0), r
+        assert O.bits_equal(Y_normal, to_host(H.hss_apply(A, Xd))), r   # the state after forced calls
+        S64 = _dense_S(fmt, dtype, m, n, ref)
+        U64, V64, X64 = O.widen(U, dtype), O.widen(V, dtype), O.widen(X, dtype)
+        err = O.max_normalised_error(O.widen(Y_forced, dtype), O.apply_factored(S64, U64, V64, X64),
+                                     O.normaliser(S64, U64, V64, X64))
+        assert err <= O.TOL[dtype]
 
 
 def test_apply_shared_workspace_many_calls(H):
@@ -233,7 +194,7 @@ def test_apply_shared_workspace_many_calls(H):
         xs.append(X)
         expect.append([to_host(H.hss_apply(A, x)) for x in X])     # each with its own workspace
     size = max(H.hss_apply_workspace_size(A, x[0].shape[0]) for A, x in zip(mats, xs))
-    ws = torch.zeros(size, dtype=torch.uint8, device="cuda")
+    ws = H.apply_workspace(size, "cuda")
     for it in range(40):
         k = it % 2
         i = (it // 2) % 3

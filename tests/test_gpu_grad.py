@@ -176,7 +176,7 @@ def test_backward_8192_layer_sampled(H):
 
 
 @pytest.mark.parametrize("route,b", [("dense", 16), ("sparse", 600), ("dense", 5)])
-def test_ds_routes_forced(H, monkeypatch, route, b):
+def test_ds_routes_forced(H, hss_opt, route, b):
     """Both forms of dS (the sampled product and the dense G^T X plus gather)
     on the other side of their default batch threshold."""
     m, n, r = 130, 264, 8
@@ -186,7 +186,7 @@ def test_ds_routes_forced(H, monkeypatch, route, b):
     X64, G64 = O.widen(X, DT), O.widen(G, DT)
     g = O.backward(m, n, ref["row_ptr"], ref["col_idx"], S64, U64, V64, X64, G64)
     N = O.backward_normalisers(m, n, ref["row_ptr"], ref["col_idx"], S64, U64, V64, X64, G64)
-    monkeypatch.setenv("HSS_GRAD_DS_ROUTE", route)
+    hss_opt("grad_ds_route", route)
     out = H.hss_grad(A, to_dev(X, DT), to_dev(G, DT))
     _within(out["dS"].cpu().numpy(), g["dS"], N["dS"], "dS")
     _within(out["dU"].cpu().numpy(), g["dU"], N["dU"], "dU")
@@ -207,11 +207,11 @@ def _layer24(H, m, n, r, seed):
 @pytest.mark.parametrize("m,n,r,b,route", [(40, 64, 8, 5, None), (130, 96, 16, 33, None), (70, 128, 4, 16, "dense"),
                                            (36, 32, 4, 1, None),
                                            (64, 256, 16, 600, None), (64, 256, 16, 600, "sparse")])
-def test_backward_2of4_matches_oracle(H, monkeypatch, m, n, r, b, route):
+def test_backward_2of4_matches_oracle(H, hss_opt, m, n, r, b, route):
     """A 2:4 layer: dS laid out as nm_values, dU, dV, and dX through the
     transposed layer built from the 2:4 positions."""
     if route:
-        monkeypatch.setenv("HSS_GRAD_DS_ROUTE", route)
+        hss_opt("grad_ds_route", route)
     A, s, rp, ci, S64, U64, V64 = _layer24(H, m, n, r, 100 + m + b)
     X = syn.random_matrix(b, n, DT, seed=101, kind="normal", scale=1.0)
     G = syn.random_matrix(b, m, DT, seed=102, kind="normal", scale=1.0)

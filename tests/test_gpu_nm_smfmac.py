@@ -60,22 +60,22 @@ CASES = [
 
 
 @pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}x{c[1]}-r{c[2]}-b{c[3]}" for c in CASES])
-def test_smfmac_matches_oracle(H, monkeypatch, case):
+def test_smfmac_matches_oracle(H, hss_opt, case):
     m, n, r, b = case
     seed = 5 * m + n + 3 * r + b
     A, S64, U64, V64 = _layer(H, m, n, r, seed)
     X = syn.random_matrix(b, n, DT, seed=seed + 1, kind="normal", scale=1.0)
     Xd = to_dev(X, DT)
-    monkeypatch.setenv("HSS_CSR_BATCH_ROUTE", "smfmac")
+    hss_opt("batch_route", "smfmac")
     Y1 = H.hss_apply(A, Xd)
     _check(Y1, S64, U64, V64, O.widen(X, DT))
     assert O.bits_equal(to_host(Y1), to_host(H.hss_apply(A, Xd)))      # deterministic
-    monkeypatch.delenv("HSS_CSR_BATCH_ROUTE")
+    hss_opt("batch_route", "auto")
     assert O.bits_equal(to_host(Y1), to_host(H.hss_apply(A, Xd)))      # the default route for 2..64 columns
 
 
 @pytest.mark.parametrize("b", [2, 16, 64])
-def test_smfmac_agrees_with_decode_and_densify(H, monkeypatch, b):
+def test_smfmac_agrees_with_decode_and_densify(H, hss_opt, b):
     """The other routes of the same call stay within the bar (they differ in
     rounding: T is bf16 on the matrix-core routes, fp32 in the decode)."""
     m, n, r = 200, 512, 48
@@ -83,7 +83,7 @@ def test_smfmac_agrees_with_decode_and_densify(H, monkeypatch, b):
     X = syn.random_matrix(b, n, DT, seed=91 + b, kind="normal", scale=1.0)
     Xd = to_dev(X, DT)
     for route in ("smfmac", "decode", "densify"):
-        monkeypatch.setenv("HSS_CSR_BATCH_ROUTE", route)
+        hss_opt("batch_route", route)
         _check(H.hss_apply(A, Xd), S64, U64, V64, O.widen(X, DT))
 
 
@@ -156,7 +156,7 @@ def test_smfmac_11008x4096_sampled(H, b):
     assert err <= O.TOL[DT], f"max normalised error {err:.3e}"
 
 
-def test_smfmac_shared_workspace_across_routes(H, monkeypatch):
+def test_smfmac_shared_workspace_across_routes(H, hss_opt):
     """One workspace, calls alternating between this route, the fused decode
     and the densified GEMM (whose scratch overlaps the T partials): every
     result equals the one from a fresh workspace (the T tile counters live in
@@ -168,11 +168,11 @@ def test_smfmac_shared_workspace_across_routes(H, monkeypatch):
     xs = {b: to_dev(syn.random_matrix(b, n, DT, seed=102 + b, kind="normal", scale=1.0), DT) for b in (8, 16, 40)}
     expect = {}
     for b, route in calls:
-        monkeypatch.setenv("HSS_CSR_BATCH_ROUTE", route)
+        hss_opt("batch_route", route)
         expect[(b, route)] = to_host(H.hss_apply(A, xs[b]))
     size = max(H.hss_apply_workspace_size(A, b) for b in xs)
-    ws = torch.zeros(size, dtype=torch.uint8, device="cuda")
+    ws = H.apply_workspace(size, "cuda")
     for it in range(3):
         for b, route in calls:
-            monkeypatch.setenv("HSS_CSR_BATCH_ROUTE", route)
+            hss_opt("batch_route", route)
             assert O.bits_equal(to_host(H.hss_apply(A, xs[b], ws=ws)), expect[(b, route)]), (it, b, route)

@@ -61,12 +61,12 @@ CASES = [
 
 @pytest.mark.parametrize("route", ["spmm", "decode", "densify"])
 @pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}x{c[1]}-r{c[2]}-b{c[3]}" for c in CASES])
-def test_route_matches_oracle(H, monkeypatch, route, case):
+def test_route_matches_oracle(H, hss_opt, route, case):
     m, n, r, b = case
     seed = m + 3 * n + r + b
     A, S64, U64, V64 = _layer(H, m, n, r, seed)
     X = syn.random_matrix(b, n, DT, seed=seed + 1, kind="normal", scale=1.0)
-    monkeypatch.setenv("HSS_CSR_BATCH_ROUTE", route)
+    hss_opt("batch_route", route)
     Xd = to_dev(X, DT)
     Y1 = H.hss_apply(A, Xd)
     _check(Y1, S64, U64, V64, O.widen(X, DT))
@@ -74,10 +74,10 @@ def test_route_matches_oracle(H, monkeypatch, route, case):
 
 
 @pytest.mark.parametrize("b,r", [(7, 6), (16, 0), (64, 32)])
-def test_spmm_empty_sparse_part_and_empty_rows(H, monkeypatch, b, r):
+def test_spmm_empty_sparse_part_and_empty_rows(H, hss_opt, b, r):
     """k = 0 (a pure low-rank product, or exact zeros with r = 0), and a
     split so sparse that most rows are empty."""
-    monkeypatch.setenv("HSS_CSR_BATCH_ROUTE", "spmm")
+    hss_opt("batch_route", "spmm")
     for frac in ((0, 100), (1, 1000)):
         A, S64, U64, V64 = _layer(H, 150, 96, r, 7 + b, frac=frac)
         X = syn.random_matrix(b, 96, DT, seed=8, kind="normal", scale=1.0)
@@ -85,8 +85,8 @@ def test_spmm_empty_sparse_part_and_empty_rows(H, monkeypatch, b, r):
 
 
 @pytest.mark.parametrize("b", [3, 16, 40])
-def test_spmm_col16_bit_equal_to_int32(H, monkeypatch, b):
-    monkeypatch.setenv("HSS_CSR_BATCH_ROUTE", "spmm")
+def test_spmm_col16_bit_equal_to_int32(H, hss_opt, b):
+    hss_opt("batch_route", "spmm")
     A32, S64, U64, V64 = _layer(H, 140, 300, 24, 30 + b)
     A16, _, _, _ = _layer(H, 140, 300, 24, 30 + b, col16=True)
     Xd = to_dev(syn.random_matrix(b, 300, DT, seed=31, kind="normal", scale=1.0), DT)
@@ -95,9 +95,9 @@ def test_spmm_col16_bit_equal_to_int32(H, monkeypatch, b):
 
 
 @pytest.mark.parametrize("b", [16, 64])
-def test_spmm_graph_replay_matches_eager(H, monkeypatch, b):
+def test_spmm_graph_replay_matches_eager(H, hss_opt, b):
     import torch
-    monkeypatch.setenv("HSS_CSR_BATCH_ROUTE", "spmm")
+    hss_opt("batch_route", "spmm")
     m, n = 300, 256
     A, _, _, _ = _layer(H, m, n, 48, 61)
     xs = [to_dev(syn.random_matrix(b, n, DT, seed=62 + i, kind="normal", scale=1.0), DT) for i in range(3)]
@@ -120,8 +120,8 @@ def test_spmm_graph_replay_matches_eager(H, monkeypatch, b):
 
 
 @pytest.mark.parametrize("b", [12, 48])
-def test_spmm_group_equals_single_applies(H, monkeypatch, b):
-    monkeypatch.setenv("HSS_CSR_BATCH_ROUTE", "spmm")
+def test_spmm_group_equals_single_applies(H, hss_opt, b):
+    hss_opt("batch_route", "spmm")
     n = 256
     layers = [_layer(H, m, n, r, 70 + m) for m, r in ((200, 16), (64, 0), (301, 40))]
     X = syn.random_matrix(b, n, DT, seed=71, kind="normal", scale=1.0)
@@ -132,7 +132,7 @@ def test_spmm_group_equals_single_applies(H, monkeypatch, b):
         _check(Y, S64, U64, V64, O.widen(X, DT))
 
 
-def _full(H, wl, b, rows, route, monkeypatch):
+def _full(H, wl, b, rows, route, hss_opt):
     c = syn.WORKLOADS[wl]
     m, n = c.shapes[0]
     r = c.rank[0]
@@ -143,7 +143,7 @@ def _full(H, wl, b, rows, route, monkeypatch):
                     row_ptr=_raw(ref["row_ptr"]), col_idx=_raw(ref["col_idx"]),
                     values=to_dev(ref["values"], DT), nnz=len(ref["col_idx"]))
     X = syn.activations(c, b, 0, 0)
-    monkeypatch.setenv("HSS_CSR_BATCH_ROUTE", route)
+    hss_opt("batch_route", route)
     Y = to_host(H.hss_apply(A, to_dev(X, DT)))
     S_rows = O.csr_rows_dense(rows, n, ref["row_ptr"], ref["col_idx"], ref["values"], DT)
     Yref, N = O.apply_rows(S_rows, O.widen(U, DT)[rows], O.widen(V, DT), O.widen(X, DT))
@@ -152,14 +152,14 @@ def _full(H, wl, b, rows, route, monkeypatch):
 
 
 @pytest.mark.parametrize("b", [4, 64, 256])
-def test_spmm_4096_layer_sampled(H, monkeypatch, b):
+def test_spmm_4096_layer_sampled(H, hss_opt, b):
     """The 4096 x 4096 top-5 % rank-256 layer on the gather route."""
     rows = np.sort(np.random.default_rng(b).choice(4096, size=256, replace=False))
-    _full(H, "csr4096", b, rows, "spmm", monkeypatch)
+    _full(H, "csr4096", b, rows, "spmm", hss_opt)
 
 
-def test_spmm_8192_prefill_sampled(H, monkeypatch):
+def test_spmm_8192_prefill_sampled(H, hss_opt):
     """The 8192 x 8192 top-3 % rank-512 layer at b = 2048 on the gather route
     (32 batch tiles of 64 columns)."""
     rows = np.sort(np.random.default_rng(9).choice(8192, size=64, replace=False))
-    _full(H, "csr8192_prefill", 2048, rows, "spmm", monkeypatch)
+    _full(H, "csr8192_prefill", 2048, rows, "spmm", hss_opt)

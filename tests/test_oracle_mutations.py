@@ -28,6 +28,49 @@ def _fails(*tests):
     return False
 
 
+def _bits_equal_by_value(a, b):
+    a, b = np.asarray(a), np.asarray(b)
+    return a.shape == b.shape and bool(np.array_equal(a, b))      # values: +0 == -0, NaN != NaN
+
+
+def _bits_equal_flat(a, b):
+    a, b = np.ascontiguousarray(a).reshape(-1), np.ascontiguousarray(b).reshape(-1)
+    if a.size != b.size or a.dtype.itemsize != b.dtype.itemsize:   # shape ignored
+        return False
+    v = {2: np.uint16, 4: np.uint32, 8: np.uint64}[a.dtype.itemsize]
+    return bool(np.array_equal(a.view(v), b.view(v)))
+
+
+def _bits_equal_low_half(a, b):
+    a, b = np.ascontiguousarray(a), np.ascontiguousarray(b)
+    if a.shape != b.shape:
+        return False
+    return bool(np.array_equal(a.view(np.uint8)[..., ::2], b.view(np.uint8)[..., ::2]))   # half the bytes
+
+
+def _hier_count_halves_equal(k, m, n, r_diag, r_off):
+    return int(k) + 2 * (m // 2 + n // 2) * (r_diag + r_off)       # odd sides lose a row/column
+
+
+def _hier_count_dense_blocks(k, m, n, r_diag, r_off):
+    return int(k) + 2 * (m // 2) * (n // 2) // 64 * (r_diag + r_off)
+
+
+def _hier_count_one_diag(k, m, n, r_diag, r_off):
+    return int(k) + (m // 2 + n // 2) * r_diag + (m + n) * r_off
+
+
+_orig_apply_csr = H.apply_csr
+
+
+def _apply_csr_no_lowrank(m, n, rp, ci, vals, dt, U, V, X):
+    return _orig_apply_csr(m, n, rp, ci, vals, dt, U[:, :0], V[:, :0], X)     # the factor term dropped
+
+
+def _apply_csr_rows_shifted(m, n, rp, ci, vals, dt, U, V, X):
+    return np.roll(_orig_apply_csr(m, n, rp, ci, vals, dt, U, V, X), 1, axis=1)
+
+
 _orig_nm24_pattern = H.nm24_pattern
 
 
@@ -312,6 +355,15 @@ CASES = [
     ("backward", _backward_dS_transposed_index, [P.test_backward_one_hot_upstream_and_full_support_brute_force]),
     ("csr_transpose", _csr_transpose_row_major_order, [P.test_csr_transpose_is_the_transposed_matrix]),
     ("nm24_pattern", _nm24_pattern_slots_swapped, [P.test_nm24_pattern_is_the_mask_in_storage_order]),
+    ("apply_csr", _apply_csr_no_lowrank, [lambda: P.test_apply_csr_equals_the_hand_loop(11, 3)]),
+    ("apply_csr", _apply_csr_rows_shifted, [lambda: P.test_apply_csr_equals_the_hand_loop(12, 0)]),
+    ("bits_equal", _bits_equal_by_value, [P.test_bits_equal_compares_bit_patterns]),
+    ("bits_equal", _bits_equal_flat, [P.test_bits_equal_compares_bit_patterns]),
+    ("bits_equal", _bits_equal_low_half, [P.test_bits_equal_compares_bit_patterns]),
+    ("hier_param_count", _hier_count_halves_equal, [P.test_hier_param_count_hand_counts]),
+    ("hier_param_count", _hier_count_dense_blocks, [P.test_hier_param_count_hand_counts]),
+    ("hier_param_count", _hier_count_one_diag,
+     [lambda: P.test_hier_param_count_counts_the_stored_factors(9, 9, 3, 1)]),
 ]
 
 

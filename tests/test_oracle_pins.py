@@ -328,6 +328,22 @@ def test_normaliser_loop_definition():
             assert abs(N[c, i] - sum(abs(A[i, j] * X[c, j]) for j in range(S.shape[1]))) <= 1e-13
 
 
+@pytest.mark.parametrize("seed,r", [(11, 3), (12, 0)])
+def test_apply_csr_equals_the_hand_loop(seed, r):
+    """The CSR-form apply against the definition written out as loops: for
+    each output, the stored entries of row i times X, plus sum_l U[i, l] (V^T x)_l."""
+    s, S, U, V, X = _tiny_problem(seed, m=7, n=9, r=max(r, 1), b=2, k=15)
+    U, V = U[:, :r], V[:, :r]
+    m, n = S.shape
+    Y = O.apply_csr(m, n, s["row_ptr"], s["col_idx"], s["values"], O.F32, U, V, X)
+    vals = O.widen(s["values"], O.F32)
+    for c in range(X.shape[0]):
+        for i in range(m):
+            acc = sum(vals[p] * X[c, s["col_idx"][p]] for p in range(s["row_ptr"][i], s["row_ptr"][i + 1]))
+            acc += sum(U[i, l] * sum(V[j, l] * X[c, j] for j in range(n)) for l in range(r))
+            assert abs(Y[c, i] - acc) <= 1e-12 * (1 + abs(acc))
+
+
 def test_apply_rows_matches_full():
     s, S, U, V, X = _tiny_problem(4, m=9, n=12, r=2, b=3, k=20)
     rows = np.array([0, 4, 8])
@@ -559,10 +575,45 @@ def test_hier_full_rank_reproduces_residual_and_eckart_young():
         assert abs(np.linalg.norm(blk - U @ V.T) - np.sqrt(np.sum(s[r:] ** 2))) < 1e-10
 
 
-def test_hier_param_count_512_example():
-    # the pages' 512 x 512 example: diagonal blocks rank 32, off-diagonal rank 8 (no S)
-    assert O.hier_param_count(0, 512, 512, 32, 8) == (256 + 256) * 32 * 2 + (256 + 256) * 8 * 2 == 40960
-    assert O.hier_param_count(10, 5, 3, 2, 1) == 10 + (2 + 1 + 3 + 2) * 2 + (2 + 2 + 3 + 1) * 1
+def test_hier_param_count_hand_counts():
+    """Hand-counted fixtures (the page's 512 x 512 block ranks, and odd sides)."""
+    with open(os.path.join(GOLDEN, "hier_param_count_hand.json")) as f:
+        g = json.load(f)
+    for c in g["cases"]:
+        assert O.hier_param_count(c["k"], c["m"], c["n"], c["r_diag"], c["r_off"]) == c["params"], c["note"]
+
+
+@pytest.mark.parametrize("m,n,r_diag,r_off", [(9, 9, 3, 1), (7, 12, 2, 2), (12, 7, 3, 0), (2, 3, 1, 1)])
+def test_hier_param_count_counts_the_stored_factors(m, n, r_diag, r_off):
+    """Brute force: the entries of the factors hier_factors actually returns
+    (every block's U and V), plus k, equal the count."""
+    R = np.random.default_rng(m * 31 + n).standard_normal((m, n))
+    blocks = O.hier_factors(R, r_diag, r_off)
+    stored = sum(U.size + V.size for U, V in blocks.values())
+    assert O.hier_param_count(5, m, n, r_diag, r_off) == 5 + stored
+
+
+def test_bits_equal_compares_bit_patterns():
+    """bits_equal is the checker behind every bitwise parity assertion, so its
+    negative cases are pinned: patterns, not values, decide."""
+    f = np.array([1.0, -2.5, 3.0], dtype=np.float32)
+    assert O.bits_equal(f, f.copy())
+    assert O.bits_equal(f, f.view(np.uint32))                     # same bits, another view
+    assert not O.bits_equal(np.array([0.0], np.float32), np.array([-0.0], np.float32))   # +0 vs -0
+    qnan = np.array([0x7FC00000], np.uint32).view(np.float32)
+    pnan = np.array([0x7FC00001], np.uint32).view(np.float32)
+    assert O.bits_equal(qnan, qnan.copy())                         # the same NaN pattern
+    assert not O.bits_equal(qnan, pnan)                            # NaN payloads differ
+    g = f.copy()
+    g.view(np.uint32)[1] ^= 1                                      # one bit of one element
+    assert not O.bits_equal(f, g)
+    assert not O.bits_equal(f, f[:2])                              # shape
+    assert not O.bits_equal(f.reshape(3, 1), f.reshape(1, 3))      # shape, same size
+    assert not O.bits_equal(f, f.astype(np.float64))               # element width
+    h = np.array([0x3F80, 0x8000], np.uint16)                      # bf16 patterns 1.0, -0
+    assert O.bits_equal(h, h.copy())
+    assert not O.bits_equal(h, np.array([0x3F80, 0x0000], np.uint16))
+    assert not O.bits_equal(h, np.array([0x3F80, 0x8001], np.uint16))
 
 
 @pytest.mark.parametrize("permuted", [False, True])
@@ -718,3 +769,27 @@ def test_nm24_pattern_is_the_mask_in_storage_order():
     assert np.array_equal(ci, cols) and np.array_equal(O.csr_row_of_entry(6, rp), rows)
     assert np.array_equal(O.dense_from_csr(6, 40, rp, ci, s["nm_values"].reshape(-1), O.BF16),
                           O.dense_from_24(6, 40, s["nm_values"], s["nm_meta"], O.BF16))
+
+
+def test_svd_factor_cache_matches_its_manifest():
+    """The full-size factors the GPU parity tests use (written by
+    tests/golden/make_svd_factors.py from oracle calls only): each entry's
+    Eckart-Young check held when it was written, the singular values it
+    recorded are ordered, and the cached files hash to the manifest."""
+    import hashlib
+    man = _golden("svd_factors_manifest.json")
+    cache = os.path.join(os.path.dirname(GOLDEN), "_svd_cache")
+    assert len(man["entries"]) == 10
+    for name, e in man["entries"].items():
+        assert abs(e["eckart_young_lhs"] - e["eckart_young_rhs"]) <= 1e-9 * e["eckart_young_rhs"], name
+        assert e["sigma_r_minus_1"] >= e["sigma_r"] > 0, name
+        key, which = name.rsplit(".", 1)
+        cfg = syn.WORKLOADS[key]
+        assert (e["m"], e["n"]) == cfg.shapes[int(which)] and e["r"] == cfg.rank[int(which)]
+        if not os.path.isdir(cache):
+            continue
+        for part, shape in (("U", (e["m"], e["r"])), ("V", (e["n"], e["r"]))):
+            a = np.load(os.path.join(cache, f"{name}.{part}.npy"), allow_pickle=False)
+            assert a.shape == shape and a.dtype == np.uint16
+            if not os.path.exists(os.path.join(cache, f"{name}.rebuilt")):
+                assert hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest() == e[f"sha256_{part}"]
