@@ -297,8 +297,11 @@ hss_status hss_apply_workspace_init(void* ws, size_t ws_bytes, hipStream_t strea
  * ([HSS] implementation-patterns section: the compressed layers run layer by
  * layer; these share their input).
  * ------------------------------------------------------------------------
- * Y[g] (b x A[g]->m) = X (b x n) times (S_g + U_g V_g^T)^T for g < G, with
- * exactly the arithmetic of hss_apply on each matrix.  In the decode regime
+ * Y[g] (b x A[g]->m) = X (b x n) times (S_g + U_g V_g^T)^T for g < G, to
+ * hss_apply's bound.  The bits can differ from a single hss_apply of the
+ * same matrix where the two calls take different launch plans (a lone
+ * matrix may produce its T rows inside its row blocks, which sums them in a
+ * different order); every call is deterministic.  In the decode regime
  * (everything hss_apply runs in its fused kernel) all G matrices go through
  * ONE launch per pass of up to 8 columns instead of G; on the matrix cores
  * the matrices are applied one after another.

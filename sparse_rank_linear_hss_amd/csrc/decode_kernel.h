@@ -706,7 +706,10 @@ __device__ __forceinline__ void finish_epoch(const DecodeArgs& a, int nsub, bool
 }
 
 // Grid: blocks [0, r) are T producers (row l of T each; the lowest block ids
-// are dispatched first), the rest own 4*RPW output rows each.
+// are dispatched first), the rest own 4*RPW output rows each.  (Producers of
+// 2, 4 or 8 T rows each, so that fewer producer blocks hold residency slots,
+// measured slower on the decoder layer -- 61-67 vs 59 us per token: the T
+// rows, which every row block waits for, are then published later.)
 //
 // FAST instances are launched only when r > 0, X is staged through registers
 // into LDS in one pass, and the sparse operand takes its vector path; with
@@ -782,27 +785,31 @@ __global__ __launch_bounds__(MTR > 0 ? kMergedThreads : 256) void k_decode(Group
 
   // ---- T producer: Vt row l and X loaded together, published tagged into
   //      every replica ----
-  if (producer) {
-    const int l = local;
-    const uint32_t e = load_epoch(a);
-    t_row<DT, BC, NT>(Vt + (int64_t)l * n, X, n, bc, a.vec, red);
-    if (t == 0) {
-      const uint32_t arrived = arrive_issue(a, sub, e);
+  if constexpr (!MERGED) {
+    if (producer) {
+      const int l = local;
+      const uint32_t e = load_epoch(a);
+      t_row<DT, BC, NT>(Vt + (int64_t)l * n, X, n, bc, a.vec, red);
+      uint32_t arrived = 0;
+      if (t == 0) arrived = arrive_issue(a, sub, e);
+      // lane rep of wave 0 publishes the row into replica rep
+      if (t < kTReplicas) {
 #pragma unroll
-      for (int c = 0; c < BC; ++c) {
-        if (c < bc) {
-          const uint64_t word =
-              (uint64_t)__float_as_uint(red_sum<BC, NW>(red, c)) | ((uint64_t)tag_of(e) << 32);
-          for (int rep = 0; rep < kTReplicas; ++rep)
-            __hip_atomic_store(a.Tt + (int64_t)rep * a.t_stride + (int64_t)c * r + l, word,
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int c = 0; c < BC; ++c) {
+          if (c < bc) {
+            const uint64_t word = (uint64_t)__float_as_uint(red_sum<BC, NW>(red, c)) | ((uint64_t)tag_of(e) << 32);
+            __hip_atomic_store(a.Tt + (int64_t)t * a.t_stride + (int64_t)c * r + l, word, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+          }
         }
       }
-      uint32_t top = 0;
-      const bool sub_last = arrive_check(a, G, nsub, sub, arrived, top);
-      finish_epoch(a, nsub, sub_last, top, tag_of(e));
+      if (t == 0) {
+        uint32_t top = 0;
+        const bool sub_last = arrive_check(a, G, nsub, sub, arrived, top);
+        finish_epoch(a, nsub, sub_last, top, tag_of(e));
+      }
+      return;
     }
-    return;
   }
 
   // ---- row blocks ----

@@ -111,9 +111,12 @@ LAYER_CALLS = [(0, 1, 2), (3,), (4, 5), (6,)]   # q k v | o | gate up | down
 def test_decoder_layer_every_row_grouped_and_graph(H):
     """Seven projections (r = 409: U rows off the 16-byte grid), 3 tokens of
     batch-1 decode through the grouped calls; every output of every
-    projection against the oracle; the grouped calls bit-equal to single
-    applies; a HIP graph of the whole token sequence replayed twice (with
-    eager calls on the same workspace in between) bit-equal to the eager run."""
+    projection against the oracle, for the grouped calls and for single
+    applies of each projection (a lone 4096 x 4096 matrix takes another
+    launch plan, so the two may differ in the last bits); the token sequence
+    repeated gives the same bits; a HIP graph of the whole sequence replayed
+    twice (with eager calls on the same workspace in between) bit-equal to
+    the eager run."""
     import torch
     cfg = "decoder_layer"
     c = syn.WORKLOADS[cfg]
@@ -137,17 +140,17 @@ def test_decoder_layer_every_row_grouped_and_graph(H):
 
     run_layer()
     eager = {k: to_host(v) for k, v in ys.items()}
-    # grouped == single, bit for bit
-    for t in range(tokens):
-        for call in LAYER_CALLS:
-            for w in call:
-                single = to_host(H.hss_apply(mats[w][0], xd[(t, call[0])]))
-                assert O.bits_equal(single, eager[(t, w)]), (t, w)
+    run_layer()
+    for k, y in ys.items():
+        assert O.bits_equal(to_host(y), eager[k]), k                  # deterministic
+    single = {(t, w): to_host(H.hss_apply(mats[w][0], xd[(t, call[0])]))
+              for t in range(tokens) for call in LAYER_CALLS for w in call}
     # oracle, every row of every projection (the input of a group is its first projection's x)
     for call in LAYER_CALLS:
         for w in call:
             A, ref, U, V = mats[w]
-            _check_all_rows(cfg, w, ref, U, V, [(xs[(t, call[0])], eager[(t, w)]) for t in range(tokens)])
+            _check_all_rows(cfg, w, ref, U, V, [(xs[(t, call[0])], eager[(t, w)]) for t in range(tokens)] +
+                            [(xs[(t, call[0])], single[(t, w)]) for t in range(tokens)])
     # graph replay of the whole sequence
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
