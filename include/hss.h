@@ -282,6 +282,25 @@ hss_status hss_apply_workspace_size(const hss_matrix* A, int32_t b, size_t* byte
 hss_status hss_apply(const hss_matrix* A, int32_t b, const void* X, void* Y, void* ws,
                      size_t ws_bytes, hipStream_t stream);
 
+/* hss_apply without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments, arithmetic, routes and errors as
+ * hss_apply, with the workspace replaced by a scratch array that the library
+ * holds in each GPU's memory: hss_noalloc_scratch_bytes() bytes (16 MiB),
+ * kept until the process ends, and cleared by the first call on each device
+ * (on that call's stream).  The call allocates and frees nothing.
+ * HSS_ERR_WORKSPACE when the route this call takes needs more workspace
+ * than the scratch holds (e.g. a large CSR layer densified for the matrix
+ * cores at prefill batches): use hss_apply with a workspace of
+ * hss_apply_workspace_size() bytes for those.  Every call on one GPU shares
+ * that GPU's scratch, which keeps the last call's state: calls that overlap
+ * in time on one GPU (other streams or threads) race and can return wrong
+ * values with no error, so order them (one stream, or events).
+ * HSS_ERR_HIP if the scratch's device address cannot be looked up or a
+ * launch fails. */
+hss_status hss_apply_noalloc(const hss_matrix* A, int32_t b, const void* X, void* Y, hipStream_t stream);
+size_t hss_noalloc_scratch_bytes(void);
+
 /* Puts an apply workspace (ws_bytes bytes, device) in its initial state, on
  * `stream`: every byte zero, written by a kernel (no memset node, so the call
  * may also be captured into a HIP graph).  Call it once per workspace before

@@ -27,7 +27,7 @@ from ._lib import (HSS_BF16, HSS_COL16, HSS_DQ4, HSS_ERR_NONFINITE, HSS_F32, HSS
 __all__ = [
     "hss_version", "hss_topk_count", "hss_split_workspace_size", "hss_split", "hss_get_error",
     "hss_set_option", "hss_get_option", "option", "HSS_MAX_BATCH",
-    "hss_apply_workspace_size", "hss_apply_workspace_init", "apply_workspace", "hss_apply",
+    "hss_apply_workspace_size", "hss_apply_workspace_init", "apply_workspace", "hss_apply", "hss_apply_noalloc",
     "hss_apply_group_workspace_size", "hss_apply_group",
     "hss_csr_cols_to_u16", "HSS_COL16", "HSS_DQ4",
     "hss_rcm_order", "hss_concentration", "hss_hier_pack",
@@ -290,6 +290,20 @@ def hss_apply(A: HSSMatrix, X: torch.Tensor, Y: Optional[torch.Tensor] = None,
         ws = A.workspace(b, dev)
     check(lib.hss_apply(ctypes.byref(A.struct), b, _ptr(X), _ptr(Y), _ptr(ws), ws.numel(),
                         _stream(dev)), "hss_apply")
+    return Y
+
+
+def hss_apply_noalloc(A: HSSMatrix, X: torch.Tensor, Y: torch.Tensor) -> torch.Tensor:
+    """Y (b x m, preallocated) = X (b x n) (S + U V^T)^T on the current stream,
+    with the library's own per-GPU scratch instead of a workspace: the call
+    allocates nothing.  Calls that overlap in time on one GPU race."""
+    dev = _dev(X)
+    if X.dim() != 2 or X.shape[1] != A.n or not X.is_contiguous() or X.dtype != A.dtype:
+        raise ValueError("X must be a contiguous b x n tensor of the matrix dtype")
+    if Y.shape != (X.shape[0], A.m) or not Y.is_contiguous() or Y.dtype != A.dtype:
+        raise ValueError("Y must be a contiguous b x m tensor of the matrix dtype")
+    check(lib.hss_apply_noalloc(ctypes.byref(A.struct), X.shape[0], _ptr(X), _ptr(Y), _stream(dev)),
+          "hss_apply_noalloc")
     return Y
 
 

@@ -69,6 +69,8 @@ def _load():
         "hss_set_option": (ctypes.c_int, [ctypes.c_int, c_int32]),
         "hss_get_option": (c_int32, [ctypes.c_int]),
         "hss_apply_workspace_init": (ctypes.c_int, [c_void_p, c_size_t, c_void_p]),
+        "hss_apply_noalloc": (ctypes.c_int, [P(HssMatrixStruct), c_int32, c_void_p, c_void_p, c_void_p]),
+        "hss_noalloc_scratch_bytes": (c_size_t, []),
         "hss_apply_workspace_size": (ctypes.c_int, [P(HssMatrixStruct), c_int32, P(c_size_t)]),
         "hss_apply": (ctypes.c_int, [P(HssMatrixStruct), c_int32, c_void_p, c_void_p, c_void_p,
                                      c_size_t, c_void_p]),

@@ -26,7 +26,7 @@ ARCH = os.environ.get("HSS_OFFLOAD_ARCH", "gfx950")
 # that they compile in parallel (the longest first).
 SOURCES = ["decode_inst_bf16_csr_b1.hip", "decode_inst_bf16_csr_bn.hip", "decode_inst_bf16_csr16_b1.hip",
            "decode_inst_bf16_csr16_bn.hip", "decode_inst_bf16_nm.hip", "decode_inst_f32.hip", "decode.hip",
-           "mfma.hip", "spmm.hip", "nm_mma.hip", "grad.hip", "split.hip", "apply.hip", "hier.hip", "hss_api.cpp"]
+           "mfma.hip", "spmm.hip", "nm_mma.hip", "grad.hip", "split.hip", "apply.hip", "hier.hip", "noalloc.hip", "hss_api.cpp"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

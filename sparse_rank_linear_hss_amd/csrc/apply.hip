@@ -108,6 +108,18 @@ size_t apply_ws_bytes(const hss_matrix* A, int b) {
   return decode_ctl_bytes() + mx;
 }
 
+// Workspace bytes of the route this call takes (hss_apply_workspace_size
+// covers every route a call could be forced onto).
+size_t apply_route_ws_bytes(const hss_matrix* A, int b, const void* X) {
+  if (is_dq(A)) return 0;
+  switch (batch_route(A, b, X)) {
+    case R_NM: return decode_ctl_bytes() + nm_mma_ws_bytes(A, b);
+    case R_MFMA: return decode_ctl_bytes() + mfma_ws_bytes(A, b);
+    case R_SPMM: return decode_ctl_bytes() + spmm_ws_bytes(A, b);
+    default: return decode_ctl_bytes() + decode_t_bytes(A);
+  }
+}
+
 hss_status launch_apply(const hss_matrix* A, int b, const void* X, void* Y, void* ws,
                         hipStream_t stream) {
   if (is_dq(A)) {

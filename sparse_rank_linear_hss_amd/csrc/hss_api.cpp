@@ -203,13 +203,24 @@ hss_status hss_apply_workspace_size(const hss_matrix* A, int32_t b, size_t* byte
   return HSS_OK;
 }
 
-hss_status hss_apply(const hss_matrix* A, int32_t b, const void* X, void* Y, void* ws,
-                     size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+// The argument checks of hss_apply (also those of hss_apply_noalloc).
+hss_status hss::check_apply_args(const hss_matrix* A, int32_t b, const void* X, void* Y) {
   hss_status st = check_matrix(A, b);
   if (st != HSS_OK) return st;
   if (!X || !Y) return HSS_ERR_INVALID_ARG;
   const size_t es = dsize(A->dtype);
   if (overlap(X, (size_t)b * A->n * es, Y, (size_t)b * A->m * es)) return HSS_ERR_INVALID_ARG;
+  return HSS_OK;
+}
+
+extern "C" {
+
+hss_status hss_apply(const hss_matrix* A, int32_t b, const void* X, void* Y, void* ws,
+                     size_t ws_bytes, hipStream_t stream) {
+  const hss_status st = hss::check_apply_args(A, b, X, Y);
+  if (st != HSS_OK) return st;
   const size_t need = hss::apply_ws_bytes(A, b);
   if ((need > 0 && !ws) || ws_bytes < need) return HSS_ERR_WORKSPACE;
   return hss::launch_apply(A, b, X, Y, ws, stream);

@@ -117,6 +117,8 @@ hss_status launch_split_24(int dt, int m, int n, const void* W, void* nm_values,
 size_t split_ws_bytes(int fmt, int m);
 
 size_t apply_ws_bytes(const hss_matrix* A, int b);
+size_t apply_route_ws_bytes(const hss_matrix* A, int b, const void* X);
+hss_status check_apply_args(const hss_matrix* A, int32_t b, const void* X, void* Y);
 hss_status launch_apply(const hss_matrix* A, int b, const void* X, void* Y, void* ws,
                         hipStream_t stream);
 size_t apply_group_ws_bytes(const hss_matrix* const* A, int G, int b);

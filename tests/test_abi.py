@@ -208,6 +208,21 @@ def test_options_read_from_the_environment_once(hl):
     assert out.stdout.split() == ["2", "2", "12", "0", "12"]
 
 
+def test_apply_noalloc_checks_on_the_host(hl):
+    """The no-allocation apply refuses bad arguments, and routes whose
+    workspace exceeds its scratch, before any device work."""
+    INV, WS = hl._lib.HSS_ERR_INVALID_ARG, hl._lib.HSS_ERR_WORKSPACE
+    lib = hl._lib.lib
+    assert lib.hss_noalloc_scratch_bytes() == 16 << 20
+    assert lib.hss_apply_noalloc(None, 1, FAKE, FAKE * 2, None) == INV
+    s = _matrix(hl)
+    assert lib.hss_apply_noalloc(ctypes.byref(s), 0, FAKE, FAKE * 2, None) == INV
+    assert lib.hss_apply_noalloc(ctypes.byref(s), 1, None, FAKE * 2, None) == INV
+    assert lib.hss_apply_noalloc(ctypes.byref(s), 1, FAKE, FAKE + 2, None) == INV      # X overlaps Y
+    big = _matrix(hl, m=8192, n=8192, r=8)                                               # densified at b = 2048
+    assert lib.hss_apply_noalloc(ctypes.byref(big), 2048, FAKE * 1024, FAKE * 1024 + (1 << 26), None) == WS
+
+
 def test_workspace_init_rejects_bad_arguments(hl):
     lib = hl._lib.lib
     assert lib.hss_apply_workspace_init(None, 16, None) == hl._lib.HSS_ERR_INVALID_ARG
