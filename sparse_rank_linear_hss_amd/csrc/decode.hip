@@ -68,6 +68,7 @@ struct MatrixLaunch {
   DecodeArgs a;
   size_t lds;
   int uq;  // U pieces per lane and row (0: element-wise U reads)
+  int cp;  // CSR chunks per row loaded up front
   bool fast;
   int rpw;
 };
@@ -112,8 +113,10 @@ static MatrixLaunch matrix_launch(const hss_matrix* A, int bc, const void* X, vo
   L.uq = (A->dtype == HSS_BF16 && A->r > 0 && (uintptr_t)A->U % 16 == 0) ? (A->r <= 506 ? 1 : 2) : 0;
   L.lds = tbytes + mbytes + (a.x_lds ? xbytes : 0);
   L.fast = A->dtype == HSS_BF16 && A->r > 0 && a.x_lds && a.vec &&
-           (size_t)bc * A->n / 8 <= 256 * (size_t)kXRFast &&
            (A->fmt == HSS_FMT_CSR ? a.vec_csr : a.nm_fast);
+  // Rows averaging more than 192 entries (the 4096 x 11008 down projection
+  // at 3 %: 330) load their second 256-entry chunk up front as well.
+  L.cp = A->fmt == HSS_FMT_CSR && A->nnz > 192 * (int64_t)A->m ? 2 : 1;
   // Rows per wave: more rows per block means fewer copies of X staged through
   // L2 into LDS and fewer blocks queueing loads on each CU (measured best:
   // 2 for 4096 rows, 4 for 11008 rows); small matrices keep one row per wave
@@ -131,6 +134,8 @@ static MatrixLaunch matrix_launch(const hss_matrix* A, int bc, const void* X, vo
 // block (1, 2 or 4; 0: not merged) and sets rpw.
 static int merged_plan(const hss_matrix* const* A, int G, int bc, bool fast_bf16, int fmt, int& rpw) {
   if (bc != 1 || !fast_bf16 || fmt == HSS_FMT_2OF4 || !merged_enabled()) return 0;
+  for (int g = 0; g < G; ++g)
+    if (A[g]->n / 8 > kMergedThreads) return 0;  // a block's threads hold X one 16-byte vector each
   const int cus = cu_count();
   constexpr int mw = kMergedThreads / 64;
   for (int rp = 1; rp <= 4; rp *= 2) {
@@ -160,6 +165,7 @@ void launch_decode_group(const hss_matrix* const* A, int G, int bc, const void* 
   char* tw = static_cast<char*>(ws) + kCtlBytes;
   size_t lds = 0;
   int uq = -1;  // the group's: 0 if any matrix needs element-wise U reads, else the largest
+  int cp = 1;
   bool fast = true;
   int rpw = 4;
   MatrixLaunch L[kMaxGroup];
@@ -168,6 +174,7 @@ void launch_decode_group(const hss_matrix* const* A, int G, int bc, const void* 
     tw += decode_t_bytes(A[g]);
     lds = lds > L[g].lds ? lds : L[g].lds;
     uq = (L[g].uq == 0 || uq == 0) ? 0 : (uq > L[g].uq ? uq : L[g].uq);
+    cp = cp > L[g].cp ? cp : L[g].cp;
     fast = fast && L[g].fast;
     rpw = rpw < L[g].rpw ? rpw : L[g].rpw;
   }
@@ -190,10 +197,10 @@ void launch_decode_group(const hss_matrix* const* A, int G, int bc, const void* 
     decode_launch_f32(ga, grid, fmt, bc, rpw, lds, s);
   } else {
     if (fmt == HSS_FMT_CSR) {
-      if (bc == 1) decode_launch_bf16_csr_b1(ga, grid, uq, fast, mtr, rpw, lds, s);
+      if (bc == 1) decode_launch_bf16_csr_b1(ga, grid, uq, fast, mtr, rpw, cp, lds, s);
       else decode_launch_bf16_csr_bn(ga, grid, bc, uq, fast, rpw, lds, s);
     } else if (fmt == kFmtCsr16) {
-      if (bc == 1) decode_launch_bf16_csr16_b1(ga, grid, uq, fast, mtr, rpw, lds, s);
+      if (bc == 1) decode_launch_bf16_csr16_b1(ga, grid, uq, fast, mtr, rpw, cp, lds, s);
       else decode_launch_bf16_csr16_bn(ga, grid, bc, uq, fast, rpw, lds, s);
     } else {
       decode_launch_bf16_nm(ga, grid, bc, uq, fast, rpw, lds, s);

@@ -3,9 +3,9 @@
 
 namespace hss {
 
-void decode_launch_bf16_csr_b1(const GroupArgs& ga, unsigned grid, int uq, bool fast, int mtr, int rpw,
+void decode_launch_bf16_csr_b1(const GroupArgs& ga, unsigned grid, int uq, bool fast, int mtr, int rpw, int cp,
                                size_t lds, hipStream_t s) {
-  launch_bc<HSS_BF16, HSS_FMT_CSR, 1>(ga, grid, uq, fast, mtr, rpw, lds, s);
+  launch_bc<HSS_BF16, HSS_FMT_CSR, 1>(ga, grid, uq, fast, mtr, rpw, cp, lds, s);
 }
 
 }  // namespace hss

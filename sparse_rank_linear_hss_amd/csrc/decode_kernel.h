@@ -40,14 +40,17 @@
 
 namespace hss {
 
-// Control region (uint32 words) at the start of the apply workspace.  Each
-// counter sits on its own 128-byte line.
+// Control region (uint32 words) at the start of the apply workspace: the
+// call epoch, then two sets of arrival counters (a top counter and 64 spread
+// counters each); a call counts on set (epoch & 1).  Each word sits on its
+// own 128-byte line.
 static constexpr int kCtlEpoch = 0;
-static constexpr int kCtlTop = 32;
-static constexpr int kCtlSub0 = 64;
-static constexpr int kCtlSubStride = 32;
+static constexpr int kCtlLine = 32;                  // words per line
 static constexpr int kNumSub = 64;
-static constexpr size_t kCtlBytes = 16384;
+static constexpr int kCtlSetWords = (1 + kNumSub) * kCtlLine;
+static constexpr size_t kCtlBytes = 32768;          // >= (1 + 2 * 65) lines
+__device__ __forceinline__ int ctl_top(uint32_t epoch) { return kCtlLine + (int)(epoch & 1u) * kCtlSetWords; }
+__device__ __forceinline__ int ctl_sub(uint32_t epoch, int k) { return ctl_top(epoch) + kCtlLine * (1 + k); }
 // Copies of the tagged T words; block b reads copy b % kTReplicas, so each
 // line is polled by 1/kTReplicas of the blocks.
 static constexpr int kTReplicas = 8;
@@ -143,9 +146,10 @@ __device__ __forceinline__ float dot16(const u32x4& a, const u32x4& b, float acc
 }
 
 // A call's T words carry tag epoch + 1.  The epoch runs 0 .. 2^32 - 2 and
-// then wraps to 0, so no tag is ever 0, the tag of a zero-filled word.
+// then wraps to 1 (keeping the parity alternating, which picks the counter
+// set), so no tag is ever 0, the tag of a zero-filled word.
 __device__ __forceinline__ uint32_t tag_of(uint32_t epoch) { return epoch + 1u; }
-__device__ __forceinline__ uint32_t next_epoch(uint32_t tag) { return tag == 0xffffffffu ? 0u : tag; }
+__device__ __forceinline__ uint32_t next_epoch(uint32_t tag) { return tag == 0xffffffffu ? 1u : tag; }
 
 // Sum of the NW per-wave partials red[w][c] in a fixed order (NW = 4, 8 or 16).
 template <int BC, int NW>
@@ -229,19 +233,23 @@ __device__ __forceinline__ void t_row(const typename Elem<DT>::bits_t* __restric
 // partial chunk (nnz % 4 entries) cannot be read as a vector; lanes 0..3
 // load its entries one by one at kernel start (clamped, so always valid) and
 // the chunk reads them back with readlane -- no load sits in the consume path.
+// CP = 2 also loads the pass-1 chunks up front (rows of up to 509 entries
+// then need no dependent load); passes beyond are loaded in the consume loop.
 // ---------------------------------------------------------------------------
-template <int DT, int RPW>
+template <int DT, int RPW, int CP = 1>
 struct CsrChunks {
   static constexpr int VB = 4 * sizeof(typename Elem<DT>::bits_t);  // value bytes per chunk
   typedef uint32_t vchunk_t __attribute__((ext_vector_type(VB / 4)));
   int st[RPW], en[RPW], e0[RPW];
   u32x4 cq[RPW];
   vchunk_t vq[RPW];
+  u32x4 cq1[CP > 1 ? RPW : 1];   // pass 1 (CP == 2)
+  vchunk_t vq1[CP > 1 ? RPW : 1];
   uint32_t tcol, tval;  // lane k < 4: entry (nnz & ~3) + k of the array tail
 };
 
-template <int DT, int FMT, int RPW>
-__device__ __forceinline__ void csr_tail_issue(const DecodeArgs& a, CsrChunks<DT, RPW>& ch) {
+template <int DT, int FMT, int RPW, int CP = 1>
+__device__ __forceinline__ void csr_tail_issue(const DecodeArgs& a, CsrChunks<DT, RPW, CP>& ch) {
   using bits_t = typename Elem<DT>::bits_t;
   const int64_t e = (a.nnz & ~(int64_t)3) + (lane_id() & 3);
   const int64_t ec = e < a.nnz - 1 ? e : a.nnz - 1;
@@ -252,11 +260,11 @@ __device__ __forceinline__ void csr_tail_issue(const DecodeArgs& a, CsrChunks<DT
   ch.tval = (uint32_t)__builtin_nontemporal_load(static_cast<const bits_t*>(a.vals) + ec);
 }
 
-template <int DT, int FMT, int RPW>
+template <int DT, int FMT, int RPW, int CP = 1>
 __device__ __forceinline__ void csr_issue(const DecodeArgs& a, const int (&rb)[RPW + 1],
-                                          CsrChunks<DT, RPW>& ch) {
+                                          CsrChunks<DT, RPW, CP>& ch) {
   using bits_t = typename Elem<DT>::bits_t;
-  using vchunk_t = typename CsrChunks<DT, RPW>::vchunk_t;
+  using vchunk_t = typename CsrChunks<DT, RPW, CP>::vchunk_t;
   const int lane = lane_id();
   const bits_t* __restrict__ vals = static_cast<const bits_t*>(a.vals);
   const int64_t last = ((a.nnz - 4) & ~(int64_t)3);  // highest aligned full chunk
@@ -269,6 +277,17 @@ __device__ __forceinline__ void csr_issue(const DecodeArgs& a, const int (&rb)[R
       const int64_t ec = ch.e0[i] < last ? ch.e0[i] : last;
       ch.cq[i] = col_chunk<FMT>(a, ec);
       ch.vq[i] = __builtin_nontemporal_load(reinterpret_cast<const vchunk_t*>(vals + ec));
+    }
+  }
+  if constexpr (CP > 1) {
+    if (a.vec_csr) {
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) {
+        const int64_t e1 = ch.e0[i] + 256;
+        const int64_t ec = e1 < last ? e1 : last;
+        ch.cq1[i] = col_chunk<FMT>(a, ec);
+        ch.vq1[i] = __builtin_nontemporal_load(reinterpret_cast<const vchunk_t*>(vals + ec));
+      }
     }
   }
 }
@@ -323,12 +342,12 @@ __device__ __forceinline__ void csr_chunk_fma(const ChunkX<DT, BC>& g, float (&a
   }
 }
 
-template <int DT, int FMT, int BC, int RPW>
-__device__ __forceinline__ void csr_consume(const DecodeArgs& a, CsrChunks<DT, RPW>& ch,
+template <int DT, int FMT, int BC, int RPW, int CP = 1>
+__device__ __forceinline__ void csr_consume(const DecodeArgs& a, CsrChunks<DT, RPW, CP>& ch,
                                             const typename Elem<DT>::bits_t* __restrict__ xsrc,
                                             float (&ssum)[RPW][BC]) {
   using bits_t = typename Elem<DT>::bits_t;
-  using vchunk_t = typename CsrChunks<DT, RPW>::vchunk_t;
+  using vchunk_t = typename CsrChunks<DT, RPW, CP>::vchunk_t;
   const int lane = lane_id();
   const bits_t* __restrict__ vals = static_cast<const bits_t*>(a.vals);
   const int64_t last = ((a.nnz - 4) & ~(int64_t)3);
@@ -345,6 +364,14 @@ __device__ __forceinline__ void csr_consume(const DecodeArgs& a, CsrChunks<DT, R
       for (int c = 0; c < BC; ++c) accs[i][c] = 0.f;
       csr_chunk_fma<DT, BC>(g[i], accs[i]);
     }
+    if constexpr (CP > 1) {  // the prefetched pass-1 chunks, in the same order as the loop below
+#pragma unroll
+      for (int i = 0; i < RPW; ++i)
+        csr_chunk_gather<DT, BC>(a, ch.e0[i] + 256, ch.st[i], ch.en[i], ch.cq1[i], ch.vq1[i], ch.tcol, ch.tval,
+                                 xsrc, g[i]);
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) csr_chunk_fma<DT, BC>(g[i], accs[i]);
+    }
   }
 #pragma unroll
   for (int i = 0; i < RPW; ++i) {
@@ -355,7 +382,7 @@ __device__ __forceinline__ void csr_consume(const DecodeArgs& a, CsrChunks<DT, R
     if (a.vec_csr) {
 #pragma unroll
       for (int c = 0; c < BC; ++c) acc[c] = accs[i][c];
-      for (int base = (st & ~3) + 256; base < en; base += 256) {  // rows longer than 256 - 3
+      for (int base = (st & ~3) + 256 * CP; base < en; base += 256) {  // rows longer than 256 CP - 3
         const int e = base + 4 * lane;
         const int64_t ec = e < last ? e : last;
         const u32x4 cc = col_chunk<FMT>(a, ec);
@@ -660,15 +687,21 @@ __device__ __forceinline__ void u_epilogue(const DecodeArgs& a, int row0, const 
 // Arrival count, in three stages so that no atomic round trip sits on a
 // block's critical path.  Thread 0 of every block:
 //   arrive_issue  once its epoch load has returned, bumps one of the 64
-//                 spread counters.  An empty asm that reads the epoch register
-//                 and yields an opaque zero offset orders the add after that
-//                 load and keeps the compiler from rewriting the single-lane
-//                 add as a wave scan that waits for the result at once;
+//                 spread counters of set (epoch & 1).  An empty asm that reads
+//                 the epoch register and yields an opaque zero offset orders
+//                 the add after that load and keeps the compiler from
+//                 rewriting the single-lane add as a wave scan that waits for
+//                 the result at once;
 //   arrive_check  later, reads that result; the last arrival on a spread
-//                 counter bumps the top counter;
+//                 counter bumps the set's top counter;
 //   finish_epoch  at the block's end, the last arrival overall (every block
-//                 has read the epoch) clears the counters and advances the
-//                 epoch for the next call, which starts after this kernel.
+//                 has read the epoch) advances the epoch for the next call,
+//                 which starts after this kernel -- one store.
+// The other set was used by the previous call, which has completed: block 0
+// clears it (clear_next_set) early in this call, away from any critical
+// path, for the next call to count on.  (Clearing this call's own counters
+// at its end put 66 device-scope stores between its last block and the end
+// of the kernel.)
 // ---------------------------------------------------------------------------
 // The call epoch, read coherently at device scope (from L2): caches above L2
 // are not guaranteed to be clean between launches.
@@ -679,30 +712,32 @@ __device__ __forceinline__ uint32_t load_epoch(const DecodeArgs& a) {
 __device__ __forceinline__ uint32_t arrive_issue(const DecodeArgs& a, int sub, uint32_t epoch) {
   uint32_t off = 0;
   asm volatile("" : "+v"(off) : "v"(epoch));
-  return __hip_atomic_fetch_add(a.ctl + kCtlSub0 + kCtlSubStride * sub + off, 1u, __ATOMIC_RELAXED,
-                                __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_fetch_add(a.ctl + ctl_sub(epoch, sub) + off, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ bool arrive_check(const DecodeArgs& a, int G, int nsub, int sub, uint32_t arrived,
-                                             uint32_t& top) {
+__device__ __forceinline__ bool arrive_check(const DecodeArgs& a, int G, int nsub, int sub, uint32_t epoch,
+                                             uint32_t arrived, uint32_t& top) {
   const bool sub_last = arrived == (uint32_t)((G - sub + nsub - 1) / nsub) - 1;
   if (sub_last) {
     uint32_t off = 0;
     asm volatile("" : "+v"(off));  // opaque: keeps the add a plain single-lane atomic
-    top = __hip_atomic_fetch_add(a.ctl + kCtlTop + off, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    top = __hip_atomic_fetch_add(a.ctl + ctl_top(epoch) + off, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   return sub_last;
 }
 
 __device__ __forceinline__ void finish_epoch(const DecodeArgs& a, int nsub, bool sub_last, uint32_t top,
                                              uint32_t tag) {
-  if (sub_last && top == (uint32_t)nsub - 1) {
-    for (int k = 0; k < nsub; ++k)
-      __hip_atomic_store(a.ctl + kCtlSub0 + kCtlSubStride * k, 0u, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(a.ctl + kCtlTop, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (sub_last && top == (uint32_t)nsub - 1)
     __hip_atomic_store(a.ctl + kCtlEpoch, next_epoch(tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+}
+
+// Block 0, threads 0 .. 64: clear the counter set of the next call (the one
+// the previous call counted on).
+__device__ __forceinline__ void clear_next_set(const DecodeArgs& a, uint32_t epoch) {
+  const int t = threadIdx.x;
+  if (blockIdx.x == 0 && t <= kNumSub)
+    __hip_atomic_store(a.ctl + ctl_top(epoch + 1u) + kCtlLine * t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Grid: blocks [0, r) are T producers (row l of T each; the lowest block ids
@@ -729,10 +764,10 @@ __device__ __forceinline__ void finish_epoch(const DecodeArgs& a, int nsub, bool
 // beat 1024, whose 4096 waves take ~1 us to launch, delaying the last T rows.)
 static constexpr int kXR = 4;      // staged X vectors per thread held in registers
 static constexpr size_t kMaxLdsAll = 112 * 1024;  // dynamic LDS a decode block may request
-static constexpr int kXRFast = 2;  // FAST: exactly this many, no branches (bc * n <= 4096 bf16)
+static constexpr int kXRFast = 2;  // FAST: this many in the prologue, unconditionally; any more after it
 static constexpr int kMergedThreads = 512;  // MERGED block size
 
-template <int DT, int FMT, int BC, int RPW, int UQ, bool FAST, int MTR>
+template <int DT, int FMT, int BC, int RPW, int UQ, bool FAST, int MTR, int CP>
 __global__ __launch_bounds__(MTR > 0 ? kMergedThreads : 256) void k_decode(GroupArgs ga) {
   using bits_t = typename Elem<DT>::bits_t;
   constexpr bool MERGED = MTR > 0;  // producers merged into the row blocks, MTR T rows each at most
@@ -757,7 +792,7 @@ __global__ __launch_bounds__(MTR > 0 ? kMergedThreads : 256) void k_decode(Group
     a.nm_fast = FMT == HSS_FMT_2OF4;
     a.x_pad = FMT == HSS_FMT_2OF4;
     __builtin_assume(a.r > 0);
-    __builtin_assume(a.bc * a.n > 0 && a.bc * a.n <= 256 * kXRFast * (16 / (int)sizeof(bits_t)));
+    __builtin_assume(a.bc * a.n > 0);
   }
   const int nb = ga.row_start[gi + 1] - ga.row_start[gi];  // row blocks of this matrix
   if constexpr (MERGED) {
@@ -803,9 +838,10 @@ __global__ __launch_bounds__(MTR > 0 ? kMergedThreads : 256) void k_decode(Group
           }
         }
       }
+      clear_next_set(a, e);
       if (t == 0) {
         uint32_t top = 0;
-        const bool sub_last = arrive_check(a, G, nsub, sub, arrived, top);
+        const bool sub_last = arrive_check(a, G, nsub, sub, e, arrived, top);
         finish_epoch(a, nsub, sub_last, top, tag_of(e));
       }
       return;
@@ -828,7 +864,8 @@ __global__ __launch_bounds__(MTR > 0 ? kMergedThreads : 256) void k_decode(Group
   const bool xreg = a.x_lds && a.vec;
   const int xvecs = xreg ? bc * n / NV : 0;
   constexpr int XR = MERGED ? 1 : (FAST ? kXRFast : kXR);
-  if constexpr (FAST) __builtin_assume(xvecs > 0 && xvecs <= NT * XR);
+  if constexpr (FAST) __builtin_assume(xvecs > 0);
+  if constexpr (MERGED) __builtin_assume(xvecs <= NT * XR);
   u32x4 xr[XR];
   // Lanes past the end read vector 0: one address for the whole wave (a
   // single request, served from L1), where clamping to the last vector would
@@ -865,18 +902,20 @@ __global__ __launch_bounds__(MTR > 0 ? kMergedThreads : 256) void k_decode(Group
   }
 
   // vector loads that depend on nothing: epoch, U rows, 2:4 words
-  if (!MERGED && r > 0) epoch = load_epoch(a);
+  // every block reads the epoch and arrives, also those of a matrix with no
+  // low-rank term in a grouped launch: the arrival quotas count every block
+  if constexpr (!MERGED) epoch = load_epoch(a);
   UBuf<UQ> ub[RPW];
   if (r > 0) u_issue<DT, RPW, UQ>(a, row0, ub);
   NmWords<RPW> nw;
   if constexpr (FMT == HSS_FMT_2OF4) nm_issue<DT, RPW>(a, row0, nw);
-  CsrChunks<DT, RPW> ch;
+  CsrChunks<DT, RPW, CP> ch;
   if constexpr (is_csr<FMT>) {
-    if (a.vec_csr) csr_tail_issue<DT, FMT, RPW>(a, ch);
+    if (a.vec_csr) csr_tail_issue<DT, FMT, RPW, CP>(a, ch);
   }
 
   // CSR chunks: the one dependent load (MERGED: after the T row is out)
-  if constexpr (is_csr<FMT> && !MERGED) csr_issue<DT, FMT, RPW>(a, rb, ch);
+  if constexpr (is_csr<FMT> && !MERGED) csr_issue<DT, FMT, RPW, CP>(a, rb, ch);
 
   // X for LDS, issued last otherwise: writing it to LDS waits for every load
   // above, all of which the sparse part needs right after the barrier anyway.
@@ -910,10 +949,10 @@ __global__ __launch_bounds__(MTR > 0 ? kMergedThreads : 256) void k_decode(Group
         __hip_atomic_store(a.Tt + (int64_t)rep * a.t_stride + l, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
-    csr_issue<DT, FMT, RPW>(a, rb, ch);
+    csr_issue<DT, FMT, RPW, CP>(a, rb, ch);
   }
 
-  if (r > 0 && t == 0) epoch_sh = epoch;
+  if (t == 0) epoch_sh = epoch;
   {
     u32x4* dst = reinterpret_cast<u32x4*>(xs);
 #pragma unroll
@@ -947,9 +986,10 @@ __global__ __launch_bounds__(MTR > 0 ? kMergedThreads : 256) void k_decode(Group
   // Arrival right before the barrier: every load above has returned (X went
   // last), so nothing later waits for this atomic by accident.
   uint32_t arrived = 0;
-  if (r > 0 && t == 0) arrived = arrive_issue(a, sub, epoch);
+  if (t == 0) arrived = arrive_issue(a, sub, epoch);
   __syncthreads();
   const uint32_t tag = tag_of(epoch_sh);
+  clear_next_set(a, epoch_sh);
 
   // T words, first pass.  FAST: issued now and read after the sparse part,
   // which then has no memory wait that could catch them (its operands all
@@ -972,13 +1012,13 @@ __global__ __launch_bounds__(MTR > 0 ? kMergedThreads : 256) void k_decode(Group
   // sparse part
   float ssum[RPW][BC];
   if constexpr (is_csr<FMT>)
-    csr_consume<DT, FMT, BC, RPW>(a, ch, xsrc, ssum);
+    csr_consume<DT, FMT, BC, RPW, CP>(a, ch, xsrc, ssum);
   else
     nm_consume<DT, BC, RPW>(a, row0, nw, xsrc, ssum);
 
   bool sub_last = false;
   uint32_t top = 0;
-  if (r > 0 && t == 0) sub_last = arrive_check(a, G, nsub, sub, arrived, top);
+  if (t == 0) sub_last = arrive_check(a, G, nsub, sub, epoch_sh, arrived, top);
 
   // T -> LDS: this block's replica (other passes read after the sparse part,
   // when the producers, dispatched first, have normally published), tag
@@ -1050,16 +1090,16 @@ __global__ __launch_bounds__(MTR > 0 ? kMergedThreads : 256) void k_decode(Group
 // ---------------------------------------------------------------------------
 // Launch one instance; more than 64 KiB of dynamic LDS (wide batches: X for
 // 8 columns) must be allowed per kernel first, once.
-template <int DT, int FMT, int BC, int RPW, int UQ, bool FAST, int MTR = 0>
+template <int DT, int FMT, int BC, int RPW, int UQ, bool FAST, int MTR = 0, int CP = 1>
 static void launch_k(const GroupArgs& ga, unsigned grid, size_t lds, hipStream_t s) {
   static bool big_lds = false;
   if (lds > 64 * 1024 && !big_lds) {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(&k_decode<DT, FMT, BC, RPW, UQ, FAST, MTR>),
+    hipFuncSetAttribute(reinterpret_cast<const void*>(&k_decode<DT, FMT, BC, RPW, UQ, FAST, MTR, CP>),
                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLdsAll);
     big_lds = true;
   }
-  hipLaunchKernelGGL((k_decode<DT, FMT, BC, RPW, UQ, FAST, MTR>), dim3(grid), dim3(MTR > 0 ? kMergedThreads : 256),
-                     lds, s, ga);
+  hipLaunchKernelGGL((k_decode<DT, FMT, BC, RPW, UQ, FAST, MTR, CP>), dim3(grid),
+                     dim3(MTR > 0 ? kMergedThreads : 256), lds, s, ga);
 }
 
 template <int DT, int FMT, int RPW, int UQ>
@@ -1069,8 +1109,10 @@ static void launch_merged_tr(const GroupArgs& ga, unsigned grid, int mtr, size_t
   else launch_k<DT, FMT, 1, RPW, UQ, true, 4>(ga, grid, lds, s);
 }
 
+// cp: CSR chunks per row loaded up front (2 only for one bf16 CSR column on
+// the FAST path).
 template <int DT, int FMT, int BC, int UQ>
-static void launch_v(const GroupArgs& ga, unsigned grid, bool fast, int mtr, int rpw, size_t lds,
+static void launch_v(const GroupArgs& ga, unsigned grid, bool fast, int mtr, int rpw, int cp, size_t lds,
                      hipStream_t s) {
   if constexpr (DT == HSS_BF16) {
     if constexpr (BC == 1 && is_csr<FMT> && UQ > 0) {
@@ -1085,6 +1127,17 @@ static void launch_v(const GroupArgs& ga, unsigned grid, bool fast, int mtr, int
       }
     }
     if (fast) {
+      if constexpr (BC == 1 && is_csr<FMT>) {
+        if (cp == 2) {
+          if (rpw == 1)
+            launch_k<DT, FMT, BC, 1, UQ, true, 0, 2>(ga, grid, lds, s);
+          else if (rpw == 4)
+            launch_k<DT, FMT, BC, 4, UQ, true, 0, 2>(ga, grid, lds, s);
+          else
+            launch_k<DT, FMT, BC, 2, UQ, true, 0, 2>(ga, grid, lds, s);
+          return;
+        }
+      }
       if (rpw == 1)
         launch_k<DT, FMT, BC, 1, UQ, true>(ga, grid, lds, s);
       else if (rpw == 4)
@@ -1101,31 +1154,31 @@ static void launch_v(const GroupArgs& ga, unsigned grid, bool fast, int mtr, int
 }
 
 template <int DT, int FMT, int BC>
-static void launch_bc(const GroupArgs& ga, unsigned grid, int uq, bool fast, int mtr, int rpw, size_t lds,
+static void launch_bc(const GroupArgs& ga, unsigned grid, int uq, bool fast, int mtr, int rpw, int cp, size_t lds,
                       hipStream_t s) {
   if constexpr (DT == HSS_BF16) {
-    if (uq == 1) return launch_v<DT, FMT, BC, 1>(ga, grid, fast, mtr, rpw, lds, s);
-    if (uq == 2) return launch_v<DT, FMT, BC, 2>(ga, grid, fast, mtr, rpw, lds, s);
+    if (uq == 1) return launch_v<DT, FMT, BC, 1>(ga, grid, fast, mtr, rpw, cp, lds, s);
+    if (uq == 2) return launch_v<DT, FMT, BC, 2>(ga, grid, fast, mtr, rpw, cp, lds, s);
   }
-  launch_v<DT, FMT, BC, 0>(ga, grid, fast, 0, rpw, lds, s);
+  launch_v<DT, FMT, BC, 0>(ga, grid, fast, 0, rpw, cp, lds, s);
 }
 
 template <int DT, int FMT>
 static void launch_fmt(const GroupArgs& ga, unsigned grid, int bc, int uq, bool fast, int mtr, int rpw,
                        size_t lds, hipStream_t s) {
-  if (bc == 1) launch_bc<DT, FMT, 1>(ga, grid, uq, fast, mtr, rpw, lds, s);
-  else if (bc == 2) launch_bc<DT, FMT, 2>(ga, grid, uq, fast, 0, rpw, lds, s);
-  else if (bc <= 4) launch_bc<DT, FMT, 4>(ga, grid, uq, fast, 0, rpw, lds, s);
-  else launch_bc<DT, FMT, 8>(ga, grid, uq, fast, 0, rpw, lds, s);
+  if (bc == 1) launch_bc<DT, FMT, 1>(ga, grid, uq, fast, mtr, rpw, 1, lds, s);
+  else if (bc == 2) launch_bc<DT, FMT, 2>(ga, grid, uq, fast, 0, rpw, 1, lds, s);
+  else if (bc <= 4) launch_bc<DT, FMT, 4>(ga, grid, uq, fast, 0, rpw, 1, lds, s);
+  else launch_bc<DT, FMT, 8>(ga, grid, uq, fast, 0, rpw, 1, lds, s);
 }
 
 // Instances of launch_fmt, compiled in separate files (decode_inst_*.hip)
 // so that the build runs them in parallel.
-void decode_launch_bf16_csr_b1(const GroupArgs& ga, unsigned grid, int uq, bool fast, int mtr, int rpw,
+void decode_launch_bf16_csr_b1(const GroupArgs& ga, unsigned grid, int uq, bool fast, int mtr, int rpw, int cp,
                                size_t lds, hipStream_t s);
 void decode_launch_bf16_csr_bn(const GroupArgs& ga, unsigned grid, int bc, int uq, bool fast, int rpw,
                                size_t lds, hipStream_t s);
-void decode_launch_bf16_csr16_b1(const GroupArgs& ga, unsigned grid, int uq, bool fast, int mtr, int rpw,
+void decode_launch_bf16_csr16_b1(const GroupArgs& ga, unsigned grid, int uq, bool fast, int mtr, int rpw, int cp,
                                  size_t lds, hipStream_t s);
 void decode_launch_bf16_csr16_bn(const GroupArgs& ga, unsigned grid, int bc, int uq, bool fast, int rpw,
                                  size_t lds, hipStream_t s);

@@ -83,8 +83,14 @@ SMALL = [
     ("csr", 7990, 256, 60, 1), ("csr", 2047, 64, 252, 1), ("2:4", 2100, 256, 16, 1),
     # ... and 2 or 4 T rows per block (r up to 4x the blocks)
     ("csr", 2048, 256, 400, 1), ("csr", 1024, 128, 500, 1),
-    # ... with r % 4 != 0 (U rows read element by element)
+    # ... with r % 4 != 0 (U rows read as 16-byte pieces straddling row ends)
     ("csr", 1030, 512, 41, 1), ("csr", 2050, 256, 409, 1),
+    # inputs wider than 4096 on the one-column fast path: X staged beyond the
+    # prologue's two vectors per thread; rows of ~410 entries take both CSR
+    # chunks up front, rows of ~820 continue in the consume loop; r > 506
+    # (two U pieces per lane)
+    ("csr", 300, 8192, 24, 1), ("csr", 70, 16384, 16, 1), ("csr", 2051, 11008, 409, 1),
+    ("csr", 200, 4096, 700, 1), ("2:4", 100, 8192, 8, 1),
 ]
 
 
@@ -248,6 +254,8 @@ GROUPS = [
     ("csr", [(512, 200), (256, 100), (300, 4)], 256, 1),
     ("csr", [(4096, 64), (4096, 64), (4090, 64)], 128, 1),
     ("csr", [(1000, 201), (600, 99)], 512, 1),
+    # wide inputs: both CSR chunks up front for the long-row matrix only
+    ("csr", [(300, 40), (200, 41)], 8192, 1),
 ]
 
 
@@ -272,6 +280,35 @@ def test_apply_group(H, dtype, case):
     for A, Y, (Yref, N) in zip(mats, Ys, refs):
         _check(Y, dtype, Yref, N)
         assert O.bits_equal(to_host(Y), to_host(H.hss_apply(A, Xd)))
+
+
+@pytest.mark.parametrize("dtype,b", [(O.BF16, 1), (O.F32, 1), (O.BF16, 3)])
+def test_apply_group_with_rank0_member_shares_a_workspace(H, dtype, b):
+    """A grouped call that includes a matrix with no low-rank term, called
+    again and again on one workspace with changing inputs (single calls in
+    between): every result equals the one from a fresh workspace.  Every
+    block of a launch counts towards the call epoch, so no later call takes
+    an earlier call's T words as its own."""
+    n = 96
+    shapes = [(130, 7), (130, 0), (65, 33)]
+    mats = []
+    for i, (m, r) in enumerate(shapes):
+        W = syn.random_matrix(m, n, dtype, seed=300 + 7 * i + m, kind="t3")
+        ref = O.split_csr(W, dtype, O.topk_count(m, n, 5, 100))
+        U, V = _factors(m, n, r, dtype, 310 + i)
+        mats.append(_matrix(H, "csr", dtype, m, n, ref, U, V))
+    xs = [to_dev(syn.random_matrix(b, n, dtype, seed=320 + j, kind="normal", scale=1.0), dtype) for j in range(3)]
+    expect = [[to_host(y) for y in H.hss_apply_group(mats, x)] for x in xs]      # fresh workspace each
+    expect0 = [to_host(H.hss_apply(mats[2], x, ws=H.apply_workspace(H.hss_apply_workspace_size(mats[2], b), "cuda")))
+               for x in xs]
+    ws = H.apply_workspace(H.hss_apply_group_workspace_size(mats, b), "cuda")
+    for it in range(12):
+        j = it % 3
+        Ys = H.hss_apply_group(mats, xs[j], ws=ws)
+        for g in range(3):
+            assert O.bits_equal(to_host(Ys[g]), expect[j][g]), (it, g)
+        if it % 4 == 3:
+            assert O.bits_equal(to_host(H.hss_apply(mats[2], xs[(j + 1) % 3], ws=ws)), expect0[(j + 1) % 3]), it
 
 
 def test_apply_group_graph_replay(H):
