@@ -49,7 +49,7 @@ size_t decode_t_bytes(const hss_matrix* A) {
 // 0 if even one column does not fit.
 int decode_max_cols(const hss_matrix* A) {
   for (int bc = 8; bc >= 1; bc /= 2) {
-    const size_t tb = align16(sizeof(float) * (size_t)bc * A->r) +
+    const size_t tb = align16(sizeof(float) * (size_t)bc * t_ld(A->r)) +
                       align16(4 * (size_t)((A->r + 31) / 32));
     if (tb <= max_lds(A)) return bc;
   }
@@ -89,7 +89,7 @@ static MatrixLaunch matrix_launch(const hss_matrix* A, int bc, const void* X, vo
   a.spin = spin_limit();
 
   const size_t es = A->dtype == HSS_F32 ? 4 : 2;
-  const size_t tbytes = align16(sizeof(float) * (size_t)bc * A->r);
+  const size_t tbytes = align16(sizeof(float) * (size_t)bc * t_ld(A->r));
   const size_t mbytes = align16(4 * (size_t)((A->r + 31) / 32));
   const bool nm_fast = A->fmt == HSS_FMT_2OF4 && A->dtype == HSS_BF16 && ((uintptr_t)X % 16 == 0) &&
                        A->n % 32 == 0 && (uintptr_t)A->nm_values % 16 == 0 && (uintptr_t)A->nm_meta % 4 == 0 &&

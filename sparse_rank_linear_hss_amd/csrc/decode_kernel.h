@@ -245,7 +245,7 @@ struct CsrChunks {
   vchunk_t vq[RPW];
   u32x4 cq1[CP > 1 ? RPW : 1];   // pass 1 (CP == 2)
   vchunk_t vq1[CP > 1 ? RPW : 1];
-  uint32_t tcol, tval;  // lane k < 4: entry (nnz & ~3) + k of the array tail
+  uint32_t tcol = 0, tval = 0;  // lane k < 4: entry (nnz & ~3) + k of the array tail
 };
 
 template <int DT, int FMT, int RPW, int CP = 1>
@@ -302,13 +302,31 @@ struct ChunkX {
   float x[4][BC];   // gathered X
 };
 
+// The array's last partial chunk as wave-uniform values (read from lanes
+// 0..3 once per wave, outside any lane-dependent branch: a readlane under a
+// divergent select compiles into an exec-masked branch per entry).
+struct CsrTail {
+  int col[4];
+  uint32_t val[4];
+};
+
+__device__ __forceinline__ CsrTail csr_tail_values(uint32_t tcol, uint32_t tval) {
+  CsrTail t;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    t.col[k] = __builtin_amdgcn_readlane((int)tcol, k);
+    t.val[k] = (uint32_t)__builtin_amdgcn_readlane((int)tval, k);
+  }
+  return t;
+}
+
 template <int DT, int BC, typename VC>
 __device__ __forceinline__ void csr_chunk_gather(const DecodeArgs& a, int e, int st, int en, const u32x4& cc,
-                                                 const VC& vv, uint32_t tcol, uint32_t tval,
+                                                 const VC& vv, const CsrTail& tl,
                                                  const typename Elem<DT>::bits_t* __restrict__ xsrc,
                                                  ChunkX<DT, BC>& g) {
   using bits_t = typename Elem<DT>::bits_t;
-  const bool whole = e + 4 <= a.nnz;  // else: the array's tail, from lanes 0..3
+  const bool whole = e + 4 <= a.nnz;  // else: the array's tail
   const int cols[4] = {(int)cc.x, (int)cc.y, (int)cc.z, (int)cc.w};
   uint32_t vb4[4];
   if constexpr (sizeof(bits_t) == 2) {
@@ -320,12 +338,12 @@ __device__ __forceinline__ void csr_chunk_gather(const DecodeArgs& a, int e, int
   for (int k = 0; k < 4; ++k) {
     const int ek = e + k;
     g.in[k] = ek >= st && ek < en;
-    const int ck = whole ? cols[k] : __builtin_amdgcn_readlane((int)tcol, k);
-    g.vb[k] = whole ? vb4[k] : (uint32_t)__builtin_amdgcn_readlane((int)tval, k);
+    const int ck = whole ? cols[k] : tl.col[k];
+    g.vb[k] = whole ? vb4[k] : tl.val[k];
     const int cx = g.in[k] ? ck : 0;
 #pragma unroll
     for (int c = 0; c < BC; ++c)
-      g.x[k][c] = fval<DT>(xsrc[(int64_t)min(c, a.bc - 1) * a.n + cx]);
+      g.x[k][c] = fval<DT>(xsrc[(c == 0 ? 0 : (int64_t)min(c, a.bc - 1) * a.n) + cx]);
   }
 }
 
@@ -352,12 +370,13 @@ __device__ __forceinline__ void csr_consume(const DecodeArgs& a, CsrChunks<DT, R
   const bits_t* __restrict__ vals = static_cast<const bits_t*>(a.vals);
   const int64_t last = ((a.nnz - 4) & ~(int64_t)3);
   float accs[RPW][BC];
+  const CsrTail tl = csr_tail_values(ch.tcol, ch.tval);
   if (a.vec_csr) {
     // first chunks of all rows: every gather first, then the products
     ChunkX<DT, BC> g[RPW];
 #pragma unroll
     for (int i = 0; i < RPW; ++i)
-      csr_chunk_gather<DT, BC>(a, ch.e0[i], ch.st[i], ch.en[i], ch.cq[i], ch.vq[i], ch.tcol, ch.tval, xsrc, g[i]);
+      csr_chunk_gather<DT, BC>(a, ch.e0[i], ch.st[i], ch.en[i], ch.cq[i], ch.vq[i], tl, xsrc, g[i]);
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
 #pragma unroll
@@ -367,8 +386,7 @@ __device__ __forceinline__ void csr_consume(const DecodeArgs& a, CsrChunks<DT, R
     if constexpr (CP > 1) {  // the prefetched pass-1 chunks, in the same order as the loop below
 #pragma unroll
       for (int i = 0; i < RPW; ++i)
-        csr_chunk_gather<DT, BC>(a, ch.e0[i] + 256, ch.st[i], ch.en[i], ch.cq1[i], ch.vq1[i], ch.tcol, ch.tval,
-                                 xsrc, g[i]);
+        csr_chunk_gather<DT, BC>(a, ch.e0[i] + 256, ch.st[i], ch.en[i], ch.cq1[i], ch.vq1[i], tl, xsrc, g[i]);
 #pragma unroll
       for (int i = 0; i < RPW; ++i) csr_chunk_fma<DT, BC>(g[i], accs[i]);
     }
@@ -388,7 +406,7 @@ __device__ __forceinline__ void csr_consume(const DecodeArgs& a, CsrChunks<DT, R
         const u32x4 cc = col_chunk<FMT>(a, ec);
         const vchunk_t vv = __builtin_nontemporal_load(reinterpret_cast<const vchunk_t*>(vals + ec));
         ChunkX<DT, BC> gl;
-        csr_chunk_gather<DT, BC>(a, e, st, en, cc, vv, ch.tcol, ch.tval, xsrc, gl);
+        csr_chunk_gather<DT, BC>(a, e, st, en, cc, vv, tl, xsrc, gl);
         csr_chunk_fma<DT, BC>(gl, acc);
       }
     } else {
@@ -610,13 +628,20 @@ __device__ __forceinline__ void u_issue(const DecodeArgs& a, int row0, UBuf<UQ> 
   }
 }
 
+// T in LDS: column c's value l at Tp[c * t_ld(r) + l], with kTPad zeros on
+// each side of every column, so a piece reads its 8 T values from one base
+// (its first l, clamped to r) without clamping each index.
+static constexpr int kTPad = 8;
+__device__ __host__ __forceinline__ int t_ld(int r) { return r + 2 * kTPad; }
+
 template <int DT, int BC, int RPW, int UQ>
 __device__ __forceinline__ void u_epilogue(const DecodeArgs& a, int row0, const UBuf<UQ> (&ub)[RPW],
-                                           const float* __restrict__ Ts, float (&acc)[RPW][BC]) {
+                                           const float* __restrict__ Tp, float (&acc)[RPW][BC]) {
   using bits_t = typename Elem<DT>::bits_t;
   const bits_t* __restrict__ U = static_cast<const bits_t*>(a.U);
   const int lane = lane_id();
   const int m = a.m, r = a.r, bc = a.bc;
+  const int tld = t_ld(r);
 #pragma unroll
   for (int i = 0; i < RPW; ++i) {
     const int row = row0 + i;
@@ -628,14 +653,14 @@ __device__ __forceinline__ void u_epilogue(const DecodeArgs& a, int row0, const 
       const int sh = (int)(e0 & 7);  // the row starts at element sh of its first piece
 #pragma unroll
       for (int q = 0; q < UQ; ++q) {
-        const int lb = 8 * (lane + 64 * q) - sh;  // l of the piece's first element
-        // T reads first (clamped index, no branch), then the masked products
+        const int lb = 8 * (lane + 64 * q) - sh;  // l of the piece's first element (>= -7)
+        const int base = min(lb, r);               // reads stay inside the column and its pads
+        // T reads first (no branch), then the masked products
         float tq[8][BC];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          const int lc = min(max(lb + k, 0), r - 1);
 #pragma unroll
-          for (int c = 0; c < BC; ++c) tq[k][c] = Ts[min(c, bc - 1) * r + lc];
+          for (int c = 0; c < BC; ++c) tq[k][c] = Tp[(c == 0 ? 0 : min(c, bc - 1) * tld) + base + k];
         }
         const uint32_t w[4] = {ub[i].p[q].x, ub[i].p[q].y, ub[i].p[q].z, ub[i].p[q].w};
 #pragma unroll
@@ -653,7 +678,7 @@ __device__ __forceinline__ void u_epilogue(const DecodeArgs& a, int row0, const 
         const float u = fval<DT>(U[e0 + l]);
 #pragma unroll
         for (int c = 0; c < BC; ++c)
-          if (c < bc) acc[i][c] = fmaf(u, Ts[c * r + l], acc[i][c]);
+          if (c < bc) acc[i][c] = fmaf(u, Tp[c * tld + l], acc[i][c]);
       }
     } else {
       float tq[kUPL][BC];
@@ -661,7 +686,7 @@ __device__ __forceinline__ void u_epilogue(const DecodeArgs& a, int row0, const 
       for (int q = 0; q < kUPL; ++q) {
         const int lc = min(lane + 64 * q, r - 1);
 #pragma unroll
-        for (int c = 0; c < BC; ++c) tq[q][c] = Ts[min(c, bc - 1) * r + lc];
+        for (int c = 0; c < BC; ++c) tq[q][c] = Tp[min(c, bc - 1) * tld + lc];
       }
 #pragma unroll
       for (int q = 0; q < kUPL; ++q) {
@@ -677,7 +702,7 @@ __device__ __forceinline__ void u_epilogue(const DecodeArgs& a, int row0, const 
         const float u = fval<DT>(U[(int64_t)row * r + l]);
 #pragma unroll
         for (int c = 0; c < BC; ++c)
-          if (c < bc) acc[i][c] = fmaf(u, Ts[c * r + l], acc[i][c]);
+          if (c < bc) acc[i][c] = fmaf(u, Tp[c * tld + l], acc[i][c]);
       }
     }
   }
@@ -811,7 +836,7 @@ __global__ __launch_bounds__(MTR > 0 ? kMergedThreads : 256) void k_decode(Group
   const int G = (int)gridDim.x;
   const bits_t* __restrict__ X = static_cast<const bits_t*>(a.X);
   const bits_t* __restrict__ Vt = static_cast<const bits_t*>(a.Vt);
-  float* Ts = reinterpret_cast<float*>(smem + a.t_off);
+  float* Tp = reinterpret_cast<float*>(smem + a.t_off) + kTPad;  // T column 0, element 0
   uint32_t* miss = reinterpret_cast<uint32_t*>(smem + a.miss_off);
   bits_t* xs = reinterpret_cast<bits_t*>(smem + a.x_off);
   const bits_t* xsrc = a.x_lds ? xs : X;
@@ -962,6 +987,10 @@ __global__ __launch_bounds__(MTR > 0 ? kMergedThreads : 256) void k_decode(Group
     }
   }
   for (int q = t; q < (r + 31) / 32; q += NT) miss[q] = 0;
+  for (int q = t; q < 2 * kTPad * bc; q += NT) {  // the zero pads around every T column
+    const int c = q / (2 * kTPad), j = q % (2 * kTPad);
+    Tp[c * t_ld(r) + (j < kTPad ? j - kTPad : r + j - kTPad)] = 0.f;
+  }
   if (xvecs > 0) {
     // the rest of X, four vectors per thread in flight per step (unconditional
     // loads, past the end of X: vector 0)
@@ -1044,7 +1073,8 @@ __global__ __launch_bounds__(MTR > 0 ? kMergedThreads : 256) void k_decode(Group
             v = __hip_atomic_load(Tr + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
           if ((uint32_t)(v >> 32) == tag && a.spin >= 0) {
-            Ts[e] = __uint_as_float((uint32_t)v);
+            const int ce = BC == 1 ? 0 : e / r;
+            Tp[ce * t_ld(r) + e - ce * r] = __uint_as_float((uint32_t)v);
           } else {
             const int l = e % r;
             atomicOr(&miss[l >> 5], 1u << (l & 31));
@@ -1059,7 +1089,7 @@ __global__ __launch_bounds__(MTR > 0 ? kMergedThreads : 256) void k_decode(Group
         const int l = wi * 32 + __ffs(bits) - 1;
         bits &= bits - 1;
         t_row<DT, BC, NT>(Vt + (int64_t)l * n, a.x_pad ? X : xsrc, n, bc, a.vec, red);
-        if (t < bc) Ts[(int64_t)t * r + l] = red_sum<BC, NW>(red, t);
+        if (t < bc) Tp[t * t_ld(r) + l] = red_sum<BC, NW>(red, t);
         __syncthreads();
       }
     }
@@ -1067,7 +1097,7 @@ __global__ __launch_bounds__(MTR > 0 ? kMergedThreads : 256) void k_decode(Group
 
   // low-rank epilogue, store
   float lacc[RPW][BC];
-  if (r > 0) u_epilogue<DT, BC, RPW, UQ>(a, row0, ub, Ts, lacc);
+  if (r > 0) u_epilogue<DT, BC, RPW, UQ>(a, row0, ub, Tp, lacc);
   bits_t* __restrict__ Y = static_cast<bits_t*>(a.Y);
   const int lane = lane_id();
 #pragma unroll
