@@ -104,11 +104,16 @@ typedef enum {
   HSS_OPT_DECODE_MERGED = 3,
   HSS_OPT_DECODE_FORCE_LOCAL = 4
 } hss_option;
-hss_status hss_set_option(hss_option opt, int32_t value);
-int32_t hss_get_option(hss_option opt);
+hss_status hss_set_option(int32_t opt, int32_t value);
+int32_t hss_get_option(int32_t opt);
 
-/* Static text for a status code (never NULL). */
-const char* hss_status_string(hss_status s);
+/* Entry points take enumerations (hss_format, hss_dtype, hss_option,
+ * hss_status) as int32_t, so that a value outside the enumeration is a
+ * rejected argument rather than undefined behaviour. */
+
+/* Static text for a status code (never NULL; "HSS: unknown status" for a
+ * value that is none). */
+const char* hss_status_string(int32_t s);
 
 /* Number of weights stage 1 keeps for a kept fraction num/den:
  *   floor(m * n * num / den), exact integer arithmetic ([HSS] worked example:
@@ -157,9 +162,9 @@ int64_t hss_topk_count(int64_t m, int64_t n, int64_t num, int64_t den);
  *   n % 4 != 0 for 2:4, residual aliasing W.  HSS_ERR_WORKSPACE for a null or
  *   short workspace.  HSS_ERR_HIP if a launch fails.
  */
-hss_status hss_split_workspace_size(hss_format fmt, hss_dtype dt, int32_t m, int32_t n,
+hss_status hss_split_workspace_size(int32_t fmt, int32_t dt, int32_t m, int32_t n,
                                     size_t* bytes);
-hss_status hss_split(hss_format fmt, hss_dtype dt, int32_t m, int32_t n, const void* W, int64_t k,
+hss_status hss_split(int32_t fmt, int32_t dt, int32_t m, int32_t n, const void* W, int64_t k,
                      int32_t* row_ptr, int32_t* col_idx, void* values, void* nm_values,
                      uint32_t* nm_meta, void* residual, void* ws, size_t ws_bytes,
                      hipStream_t stream);
@@ -374,7 +379,7 @@ hss_status hss_rcm_order(int32_t n, const int32_t* row_ptr, const int32_t* col_i
  *   HSS_ERR_INVALID_ARG: bad dtype or size, null W or out, perm with m != n;
  *   HSS_ERR_WORKSPACE; HSS_ERR_HIP. */
 hss_status hss_concentration_workspace_size(int32_t m, int32_t n, size_t* bytes);
-hss_status hss_concentration(hss_dtype dt, int32_t m, int32_t n, const void* W, const int32_t* perm, double* out,
+hss_status hss_concentration(int32_t dt, int32_t m, int32_t n, const void* W, const int32_t* perm, double* out,
                              void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* hss_hier_pack: flat factors of the 2 x 2 block low-rank term, for the
@@ -395,7 +400,7 @@ hss_status hss_concentration(hss_dtype dt, int32_t m, int32_t n, const void* W, 
  *   HSS_ERR_INVALID_ARG: bad dtype, m or n < 2, r[b] < 0 or larger than its
  *   block's smaller side, null arrays, perm with m != n, m*R or R*n >= 2^31;
  *   HSS_ERR_HIP. */
-hss_status hss_hier_pack(hss_dtype dt, int32_t m, int32_t n, const int32_t* r, const void* const* U,
+hss_status hss_hier_pack(int32_t dt, int32_t m, int32_t n, const int32_t* r, const void* const* U,
                          const void* const* Vt, const int32_t* perm, void* U_cat, void* Vt_cat, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
@@ -458,7 +463,7 @@ hss_status hss_csr_transpose(int32_t m, int32_t n, const int32_t* row_ptr, const
  *   perm must hold indices in [0, nnz).
  *   HSS_ERR_INVALID_ARG: bad dtype, nnz < 0 or >= 2^31, null arrays with
  *   nnz > 0, values overlapping values_t.  HSS_ERR_HIP. */
-hss_status hss_gather_values(hss_dtype dt, int64_t nnz, const void* values, const int32_t* perm, void* values_t,
+hss_status hss_gather_values(int32_t dt, int64_t nnz, const void* values, const int32_t* perm, void* values_t,
                              hipStream_t stream);
 
 /* hss_transpose: dst (cols x rows, row-major) = src (rows x cols,
@@ -466,7 +471,7 @@ hss_status hss_gather_values(hss_dtype dt, int64_t nnz, const void* values, cons
  *   layer: its U is V = (stored V^T)^T, its V^T is U^T).
  *   HSS_ERR_INVALID_ARG: bad dtype, rows or cols < 1, rows * cols >= 2^31,
  *   rows > 2,097,120, null or overlapping arrays.  HSS_ERR_HIP. */
-hss_status hss_transpose(hss_dtype dt, int32_t rows, int32_t cols, const void* src, void* dst, hipStream_t stream);
+hss_status hss_transpose(int32_t dt, int32_t rows, int32_t cols, const void* src, void* dst, hipStream_t stream);
 
 #ifdef __cplusplus
 }

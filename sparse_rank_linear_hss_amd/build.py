@@ -44,29 +44,43 @@ def _hipcc():
     raise RuntimeError("hipcc not found (need ROCm)")
 
 
-def _compile(src):
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(src, bdir, extra):
+    obj = os.path.join(bdir, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [_hipcc(), *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *COMMON, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+# Host-sanitizer build (tests/test_host_sanitizers.py): the host code of every
+# source instrumented with AddressSanitizer and UndefinedBehaviorSanitizer, the
+# device code left as it is (each -fsanitize= applies to the host pass only).
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined"]
+
+
+def build(verbose: bool = True, sanitize: bool = False, lib: str = None, build_dir: str = None) -> str:
+    """Compile every source and link the library (in-tree by default).
+    sanitize: the host-sanitizer variant, written to `lib` (required)."""
+    bdir = build_dir or (os.path.join(ROOT, "_build", "sanitize") if sanitize else BUILD)
+    out = lib or LIB
+    if sanitize and lib is None:
+        raise ValueError("the sanitizer build needs its own output path")
+    os.makedirs(bdir, exist_ok=True)
+    extra = SANITIZE if sanitize else []
     with cf.ThreadPoolExecutor(max_workers=min(os.cpu_count() or 8, 16, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+        objs = list(ex.map(lambda src: _compile(src, bdir, extra), SOURCES))
+    tmp = out + ".tmp"
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra, "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

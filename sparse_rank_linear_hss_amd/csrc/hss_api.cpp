@@ -83,14 +83,14 @@ extern "C" {
 
 int hss_version(void) { return 100 * HSS_VERSION_MAJOR + HSS_VERSION_MINOR; }
 
-hss_status hss_set_option(hss_option opt, int32_t value) {
+hss_status hss_set_option(int32_t opt, int32_t value) {
   static const int32_t hi[] = {4, 2, INT32_MAX, 1, 1};
   if ((int)opt < 0 || (int)opt >= hss::kNumOptions || value < 0 || value > hi[opt]) return HSS_ERR_INVALID_ARG;
   hss::options().v[opt].store(value, std::memory_order_relaxed);
   return HSS_OK;
 }
 
-int32_t hss_get_option(hss_option opt) {
+int32_t hss_get_option(int32_t opt) {
   if ((int)opt < 0 || (int)opt >= hss::kNumOptions) return -1;
   return hss::option(opt);
 }
@@ -101,7 +101,7 @@ hss_status hss_apply_workspace_init(void* ws, size_t ws_bytes, hipStream_t strea
   return hss::launch_zero_fill(ws, ws_bytes, stream);
 }
 
-const char* hss_status_string(hss_status s) {
+const char* hss_status_string(int32_t s) {
   switch (s) {
     case HSS_OK: return "HSS_OK";
     case HSS_ERR_INVALID_ARG: return "HSS_ERR_INVALID_ARG: invalid argument";
@@ -121,7 +121,7 @@ int64_t hss_topk_count(int64_t m, int64_t n, int64_t num, int64_t den) {
   return (int64_t)q;
 }
 
-hss_status hss_split_workspace_size(hss_format fmt, hss_dtype dt, int32_t m, int32_t n,
+hss_status hss_split_workspace_size(int32_t fmt, int32_t dt, int32_t m, int32_t n,
                                     size_t* bytes) {
   if (!bytes || !valid_fmt(fmt) || !valid_dtype(dt) || m <= 0 || n <= 0 ||
       (int64_t)m * n >= kLimit)
@@ -130,7 +130,7 @@ hss_status hss_split_workspace_size(hss_format fmt, hss_dtype dt, int32_t m, int
   return HSS_OK;
 }
 
-hss_status hss_split(hss_format fmt, hss_dtype dt, int32_t m, int32_t n, const void* W, int64_t k,
+hss_status hss_split(int32_t fmt, int32_t dt, int32_t m, int32_t n, const void* W, int64_t k,
                      int32_t* row_ptr, int32_t* col_idx, void* values, void* nm_values,
                      uint32_t* nm_meta, void* residual, void* ws, size_t ws_bytes,
                      hipStream_t stream) {
@@ -286,7 +286,7 @@ hss_status hss_concentration_workspace_size(int32_t m, int32_t n, size_t* bytes)
   return HSS_OK;
 }
 
-hss_status hss_concentration(hss_dtype dt, int32_t m, int32_t n, const void* W, const int32_t* perm, double* out,
+hss_status hss_concentration(int32_t dt, int32_t m, int32_t n, const void* W, const int32_t* perm, double* out,
                              void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!valid_dtype(dt) || m < 1 || n < 1 || (int64_t)m * n >= kLimit || !W || !out) return HSS_ERR_INVALID_ARG;
   if (perm && m != n) return HSS_ERR_INVALID_ARG;
@@ -294,7 +294,7 @@ hss_status hss_concentration(hss_dtype dt, int32_t m, int32_t n, const void* W, 
   return hss::launch_concentration(dt, m, n, W, perm, out, ws, stream);
 }
 
-hss_status hss_hier_pack(hss_dtype dt, int32_t m, int32_t n, const int32_t* r, const void* const* U,
+hss_status hss_hier_pack(int32_t dt, int32_t m, int32_t n, const int32_t* r, const void* const* U,
                          const void* const* Vt, const int32_t* perm, void* U_cat, void* Vt_cat, hipStream_t stream) {
   if (!valid_dtype(dt) || m < 2 || n < 2 || !r || !U || !Vt) return HSS_ERR_INVALID_ARG;
   if (perm && m != n) return HSS_ERR_INVALID_ARG;
@@ -365,7 +365,7 @@ hss_status hss_csr_transpose(int32_t m, int32_t n, const int32_t* row_ptr, const
   return hss::csr_transpose_host(m, n, row_ptr, col_idx, row_ptr_t, col_idx_t, perm);
 }
 
-hss_status hss_gather_values(hss_dtype dt, int64_t nnz, const void* values, const int32_t* perm, void* values_t,
+hss_status hss_gather_values(int32_t dt, int64_t nnz, const void* values, const int32_t* perm, void* values_t,
                              hipStream_t stream) {
   if (!valid_dtype(dt) || nnz < 0 || nnz >= kLimit) return HSS_ERR_INVALID_ARG;
   if (nnz == 0) return HSS_OK;
@@ -375,7 +375,7 @@ hss_status hss_gather_values(hss_dtype dt, int64_t nnz, const void* values, cons
   return hss::launch_gather_values(dt, nnz, values, perm, values_t, stream);
 }
 
-hss_status hss_transpose(hss_dtype dt, int32_t rows, int32_t cols, const void* src, void* dst, hipStream_t stream) {
+hss_status hss_transpose(int32_t dt, int32_t rows, int32_t cols, const void* src, void* dst, hipStream_t stream) {
   if (!valid_dtype(dt) || rows < 1 || cols < 1 || (int64_t)rows * cols >= kLimit || !src || !dst)
     return HSS_ERR_INVALID_ARG;
   if ((rows + 31) / 32 > 65535) return HSS_ERR_INVALID_ARG;

@@ -87,7 +87,10 @@ __global__ __launch_bounds__(256) void k_split_hist(const typename Elem<DT>::bit
                                                     int shift, int first) {
   using E = Elem<DT>;
   __shared__ uint32_t h[kHistCopies * kHistStride];
-  if (ws[W_REM] == 0) return;  // k == 0: uniform across the grid
+  // k == 0 (uniform across the grid): nothing to count, but the first pass
+  // still reads every key for the non-finite check
+  const bool counting = ws[W_REM] != 0;
+  if (!counting && !first) return;
   const uint32_t prefix = ws[W_PREFIX];
   const int hs = shift + 8;
   for (int i = threadIdx.x; i < kHistCopies * kHistStride; i += 256) h[i] = 0;
@@ -98,7 +101,7 @@ __global__ __launch_bounds__(256) void k_split_hist(const typename Elem<DT>::bit
     const uint32_t key = bits & E::key_mask;
     bad |= first && key >= E::key_inf;
     const uint32_t hi = hs >= 32 ? 0u : (key >> hs);
-    if (hi == prefix) atomicAdd(&hc[(key >> shift) & 255u], 1u);
+    if (counting && hi == prefix) atomicAdd(&hc[(key >> shift) & 255u], 1u);
   };
   const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;

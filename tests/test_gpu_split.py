@@ -96,13 +96,16 @@ def test_split_24_nm24_11008x4096_vs_oracle(H):
     _assert_24_equal(sp, oracle_split("nm24_11008x4096"))
 
 
-@pytest.mark.parametrize("fmt", ["csr", "2:4"])
+@pytest.mark.parametrize("fmt,k", [("csr", 10), ("csr", 0), ("csr", 144), ("2:4", None)])
 @pytest.mark.parametrize("bad", [float("nan"), float("inf"), -float("inf")])
-def test_split_flags_nonfinite(H, fmt, bad):
+def test_split_flags_nonfinite(H, fmt, k, bad):
+    """A NaN or infinity in W is reported for every k, also k = 0 (nothing
+    kept: no threshold search, but the first pass still reads every key) and
+    k = m n (everything kept)."""
     W = syn.random_matrix(9, 16, O.F32, seed=1, kind="t3").copy()
     W[4, 5] = bad
     with pytest.raises(H.HSSError) as ei:
-        H.hss_split(to_dev(W, O.F32), fmt, k=10 if fmt == "csr" else None)
+        H.hss_split(to_dev(W, O.F32), fmt, k=k)
     assert ei.value.code == 4
     # a finite matrix afterwards (fresh workspace state) is fine
     H.hss_split(to_dev(np.zeros((9, 16), np.float32), O.F32), fmt, k=3 if fmt == "csr" else None)
