@@ -57,6 +57,9 @@ def _args():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-headline", action="store_true", help="skip the other workloads")
+    ap.add_argument("--only", default=None,
+                    help="comma-separated sections to run (headline, csr1024, csr4096, nm24, prefill, train); "
+                         "for profiling runs: the JSON line then lacks the sections left out")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run three plain 256 MiB device-to-device copies (a known-size "
                          "reference for hardware byte counters)")
@@ -274,32 +277,29 @@ def _decoder_layer(H, timer, args):
     seq = timer.graph(step, wl.tokens, 5) if K != wl.tokens else trials
     ms7 = sorted(timer.graph(step_7, wl.tokens, 5))[len(trials) // 2]
 
-    # per-launch durations: HIP events around every launch on the library's
-    # stream (torch's current stream), the GPU queue pre-filled with flushes
-    # so that the events bracket the kernels and not the host's enqueue
-    ev_tokens = min(K, 32)
-    per = [[] for _ in LAYER_GROUPS]
-    for rep in range(max(1, math.ceil(K / ev_tokens))):
-        for _ in range(24):
-            timer.flush()
-        evs = []
-        for i in range(ev_tokens):
+    # per-launch durations: each launch's share of the token, measured as
+    # the token graph's time less that of the same graph without the launch
+    # (HIP events around the replays on the library's stream, torch's current
+    # stream), so a launch's time includes its start after the one before it,
+    # as a kernel trace of the sequence records it
+    def step_without(skip):
+        def f(i):
             for gi in range(len(LAYER_GROUPS)):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                call(gi, rep * ev_tokens + i)
-                e1.record()
-                evs.append((gi, e0, e1))
-        torch.cuda.synchronize()
-        for gi, e0, e1 in evs:
-            per[gi].append(e0.elapsed_time(e1))
-    per_ms = [sorted(v)[len(v) // 2] for v in per]
+                if gi != skip:
+                    call(gi, i)
+        return f
+
+    per_ms = []
+    for gi in range(len(LAYER_GROUPS)):
+        t = timer.graph(step_without(gi), K, 5)
+        per_ms.append(ms - sorted(t)[len(t) // 2])
     launches = []
     for gi, grp in enumerate(LAYER_GROUPS):
         launches.append({"group": GROUP_NAMES[gi], "projections": [wl.proj_names[w] for w in grp],
-                         "algorithmic_bytes": group_bytes[gi], "us_median": per_ms[gi] * 1e3,
+                         "algorithmic_bytes": group_bytes[gi], "us_in_sequence": per_ms[gi] * 1e3,
                          "gbs": group_bytes[gi] / (per_ms[gi] * 1e-3) / 1e9,
-                         "hbm_frac": group_bytes[gi] / (per_ms[gi] * 1e-3) / 1e9 / HBM_PEAK_GBS})
+                         "hbm_frac": group_bytes[gi] / (per_ms[gi] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "traffic_bytes": _measured_traffic(f"decoder_layer.{GROUP_NAMES[gi]}")})
     dom = max(range(len(LAYER_GROUPS)), key=lambda g: per_ms[g])
     roof = _hbm_roofline(group_bytes[dom], per_ms[dom], f"k_decode ({GROUP_NAMES[dom]} launch of the decoder layer)",
                          _measured_traffic(f"decoder_layer.{GROUP_NAMES[dom]}"))
@@ -416,15 +416,28 @@ def _routes(H, timer, L, wl, batches, routes, skip):
     return res
 
 
-def _others(H, timer, args, extra):
-    import numpy as np
-    import torch
-    import hss_synth as syn
+def _others(H, timer, args, extra, want):
+    if want("csr1024"):
+        _csr1024(H, timer, args, extra)
+    if want("csr4096"):
+        _csr4096(H, timer, args, extra)
+    if want("nm24"):
+        _nm24(H, timer, args, extra)
+    if want("prefill") or want("train"):
+        _prefill_train(H, timer, args, extra, want)
 
+
+def _csr1024(H, timer, args, extra):
     # 1024^2 fp32, top 5 %, rank 64, b = 1 (launch-bound correctness scale)
     L1, W1, _, r1 = _single_layer(H, timer, args, "csr1024_f32", [1], 1)
     extra["csr1024_f32"] = r1
     del L1, W1
+
+
+def _csr4096(H, timer, args, extra):
+    import numpy as np
+    import torch
+    import hss_synth as syn
 
     # 4096^2 5 % + rank 256: b = 1, 16; 16-bit columns; routes; hierarchical; dense-and-sparse
     wl = syn.WORKLOADS["csr4096"]
@@ -518,6 +531,10 @@ def _others(H, timer, args, extra):
     del L, W
     torch.cuda.empty_cache()
 
+
+def _nm24(H, timer, args, extra):
+    import torch
+    import hss_synth as syn
     # 11008 x 4096 2:4, rank 64, b = 1, 8, 64, and its routes
     wl3 = syn.WORKLOADS["nm24_11008x4096"]
     L3, W3, _, r3 = _single_layer(H, timer, args, "nm24_11008x4096", list(wl3.batches), 64)
@@ -527,6 +544,11 @@ def _others(H, timer, args, extra):
     del L3, W3
     torch.cuda.empty_cache()
 
+
+def _prefill_train(H, timer, args, extra, want):
+    import ctypes
+    import torch
+    import hss_synth as syn
     # prefill: 8192^2 CSR 3 %, rank 512, b = 2048 (matrix cores; rotation keeps
     # the densify's read of S honest), and the low-rank products alone
     wl5 = syn.WORKLOADS["csr8192_prefill"]
@@ -536,52 +558,54 @@ def _others(H, timer, args, extra):
     b = wl5.batches[0]
     ws5 = L5.mats[0].workspace(b)
     xs5, ys5 = _acts(wl5, b, 0, 2, L5.m)
-    t5 = timer.graph(_apply_loop(H, L5, xs5, ys5, ws5), 8, 2)
-    ms5 = sorted(t5)[len(t5) // 2]
-    lr = type("LR", (), {"mats": [H.HSSMatrix("csr", L5.m, L5.n, torch.bfloat16, U=mat.U, Vt=mat.Vt,
-                                              row_ptr=torch.zeros(L5.m + 1, dtype=torch.int32, device="cuda"),
-                                              nnz=0) for mat in L5.mats]})
-    t5l = timer.graph(_apply_loop(H, lr, xs5, ys5, ws5), 8, 2)
-    ms5_lr = sorted(t5l)[len(t5l) // 2]
-    lr_flops = 2.0 * b * L5.r * (L5.m + L5.n)
-    lr_tf = lr_flops / (ms5_lr * 1e-3) / 1e12
-    extra["prefill_8192sq_b2048"] = {
-        "ms": ms5, "ms_pct": _pct(t5), "tokens_per_s": b / (ms5 * 1e-3),
-        "useful_tflops": L5.flops(b) / (ms5 * 1e-3) / 1e12,
-        "dense_equiv_tflops": 2.0 * b * L5.m * L5.n / (ms5 * 1e-3) / 1e12,
-        "lowrank_only_ms": ms5_lr, "lowrank_tflops": lr_tf, "lowrank_mfma_frac": lr_tf / BF16_PEAK_TFLOPS,
-        "roofline": {"bound": "mfma", "achieved": lr_tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": lr_tf / BF16_PEAK_TFLOPS, "traffic": None,
-                     "kernel": "low-rank products (T^T = X V, Y = T U^T) of one call with an empty S",
-                     "algorithmic_flops_per_call": lr_flops}}
-    del lr
+    if want("prefill"):
+        t5 = timer.graph(_apply_loop(H, L5, xs5, ys5, ws5), 8, 2)
+        ms5 = sorted(t5)[len(t5) // 2]
+        lr = type("LR", (), {"mats": [H.HSSMatrix("csr", L5.m, L5.n, torch.bfloat16, U=mat.U, Vt=mat.Vt,
+                                                  row_ptr=torch.zeros(L5.m + 1, dtype=torch.int32, device="cuda"),
+                                                  nnz=0) for mat in L5.mats]})
+        t5l = timer.graph(_apply_loop(H, lr, xs5, ys5, ws5), 8, 2)
+        ms5_lr = sorted(t5l)[len(t5l) // 2]
+        lr_flops = 2.0 * b * L5.r * (L5.m + L5.n)
+        lr_tf = lr_flops / (ms5_lr * 1e-3) / 1e12
+        extra["prefill_8192sq_b2048"] = {
+            "ms": ms5, "ms_pct": _pct(t5), "tokens_per_s": b / (ms5 * 1e-3),
+            "useful_tflops": L5.flops(b) / (ms5 * 1e-3) / 1e12,
+            "dense_equiv_tflops": 2.0 * b * L5.m * L5.n / (ms5 * 1e-3) / 1e12,
+            "lowrank_only_ms": ms5_lr, "lowrank_tflops": lr_tf, "lowrank_mfma_frac": lr_tf / BF16_PEAK_TFLOPS,
+            "roofline": {"bound": "mfma", "achieved": lr_tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": lr_tf / BF16_PEAK_TFLOPS, "traffic": None,
+                         "kernel": "low-rank products (T^T = X V, Y = T U^T) of one call with an empty S",
+                         "algorithmic_flops_per_call": lr_flops}}
+        del lr
 
-    # training step on the same layer, b = 2048: forward, parameter gradients
-    # (hss_grad) and the input gradient (apply of the transposed layer)
-    A5 = L5.mats[0]
-    t0 = time.perf_counter()
-    At5 = H.hss_transposed_layer(A5)
-    torch.cuda.synchronize()
-    at_ms = (time.perf_counter() - t0) * 1e3
-    gs5 = [_bf16(syn.random_matrix(b, L5.m, "bf16", seed=70 + i, kind="normal", scale=1.0)) for i in range(2)]
-    gsz = ctypes.c_size_t(0)
-    H._lib.check(H._lib.lib.hss_grad_workspace_size(ctypes.byref(A5.struct), b, ctypes.byref(gsz)), "ws")
-    gws = torch.empty(gsz.value, dtype=torch.uint8, device="cuda")
-    wst = At5.workspace(b)
-    dxs = torch.empty((b, L5.n), dtype=torch.bfloat16, device="cuda")
-    ms_fwd = timer.eager(lambda i: H.hss_apply(A5, xs5[i % 2], ys5[i % 2], ws5), 10, 3)
-    ms_grad = timer.eager(lambda i: H.hss_grad(A5, xs5[i % 2], gs5[i % 2], ws=gws), 10, 3)
-    ms_dx = timer.eager(lambda i: H.hss_apply(At5, gs5[i % 2], dxs, wst), 10, 3)
-    ms_gather = timer.eager(lambda i: H.hss_gather_values(A5.values, At5.perm_from_s), 10, 3)
-    grad_flops = 2.0 * b * (2 * L5.r * (L5.m + L5.n) + L5.split.k)
-    step_ms = ms_fwd + ms_grad + ms_dx + ms_gather
-    extra["train_8192sq_b2048"] = {
-        "step_ms": step_ms, "tokens_per_s": b / (step_ms * 1e-3),
-        "useful_tflops": (2 * L5.flops(b) + grad_flops) / (step_ms * 1e-3) / 1e12,
-        "forward_ms": ms_fwd, "grad_ms": ms_grad, "grad_useful_tflops": grad_flops / (ms_grad * 1e-3) / 1e12,
-        "dX_ms": ms_dx, "gather_values_ms": ms_gather, "transposed_layer_setup_ms": at_ms,
-        "note": "one copy of the weights (compute-bound shape), stream launches"}
-    del At5, gs5, gws, wst, dxs, A5, L5, W5
+    if want("train"):
+        # training step on the same layer, b = 2048: forward, parameter gradients
+        # (hss_grad) and the input gradient (apply of the transposed layer)
+        A5 = L5.mats[0]
+        t0 = time.perf_counter()
+        At5 = H.hss_transposed_layer(A5)
+        torch.cuda.synchronize()
+        at_ms = (time.perf_counter() - t0) * 1e3
+        gs5 = [_bf16(syn.random_matrix(b, L5.m, "bf16", seed=70 + i, kind="normal", scale=1.0)) for i in range(2)]
+        gsz = ctypes.c_size_t(0)
+        H._lib.check(H._lib.lib.hss_grad_workspace_size(ctypes.byref(A5.struct), b, ctypes.byref(gsz)), "ws")
+        gws = torch.empty(gsz.value, dtype=torch.uint8, device="cuda")
+        wst = At5.workspace(b)
+        dxs = torch.empty((b, L5.n), dtype=torch.bfloat16, device="cuda")
+        ms_fwd = timer.eager(lambda i: H.hss_apply(A5, xs5[i % 2], ys5[i % 2], ws5), 10, 3)
+        ms_grad = timer.eager(lambda i: H.hss_grad(A5, xs5[i % 2], gs5[i % 2], ws=gws), 10, 3)
+        ms_dx = timer.eager(lambda i: H.hss_apply(At5, gs5[i % 2], dxs, wst), 10, 3)
+        ms_gather = timer.eager(lambda i: H.hss_gather_values(A5.values, At5.perm_from_s), 10, 3)
+        grad_flops = 2.0 * b * (2 * L5.r * (L5.m + L5.n) + L5.split.k)
+        step_ms = ms_fwd + ms_grad + ms_dx + ms_gather
+        extra["train_8192sq_b2048"] = {
+            "step_ms": step_ms, "tokens_per_s": b / (step_ms * 1e-3),
+            "useful_tflops": (2 * L5.flops(b) + grad_flops) / (step_ms * 1e-3) / 1e12,
+            "forward_ms": ms_fwd, "grad_ms": ms_grad, "grad_useful_tflops": grad_flops / (ms_grad * 1e-3) / 1e12,
+            "dX_ms": ms_dx, "gather_values_ms": ms_gather, "transposed_layer_setup_ms": at_ms,
+            "note": "one copy of the weights (compute-bound shape), stream launches"}
+        del At5, gs5, gws, wst, dxs, A5, L5, W5
     torch.cuda.empty_cache()
 
 
@@ -607,10 +631,15 @@ def main():
         del src, dst
     timer = Timer(args.trials)
 
-    head, roof = _decoder_layer(H, timer, args)
+    sections = {"headline"} if args.only_headline else (set(args.only.split(",")) if args.only else None)
+    want = (lambda name: True) if sections is None else (lambda name: name in sections)
     extra = {}
-    if not args.only_headline:
-        _others(H, timer, args, extra)
+    if not want("headline"):
+        _others(H, timer, args, extra, want)
+        print(json.dumps({"metric": METRIC, "value": None, "sections": sorted(sections), **extra}), flush=True)
+        return
+    head, roof = _decoder_layer(H, timer, args)
+    _others(H, timer, args, extra, want)
     ms = head["ms_per_token"]
     out = {
         "metric": METRIC,

@@ -81,6 +81,7 @@ struct NmArgs {
   uint16_t* Y;             // b x m
   int m, n, r, b, tld;
   int uvec;                // U rows 16-byte aligned (r % 8 == 0, U aligned)
+  int nbx, nby;            // row blocks, 32-column batch tiles
 };
 
 // T's row stride: 16-byte rows.
@@ -115,6 +116,12 @@ static_assert(kNmRowBytes * 32 == 32 * kNmStride * 4, "staging area = the wave's
 // Block (bx, by): rows 32 RT bx .. (RT tiles of 32), batch columns 32 by ..
 // 32 by + 31.  WV waves take its 128-column stages in turn (wave w: stages
 // w, w + WV, ...); D stages in flight per lane.
+//
+// The 1-D grid is dealt round robin to the 8 XCDs, so block id runs on XCD
+// id % 8.  Blocks 8 q + j of one run of 8 nby ids (j < 8) are the nby batch
+// tiles of row block 8 (q / nby) + j: all tiles of a row block run on one
+// XCD at about the same time, and S, streamed by the first, is an L2 hit
+// for the others instead of a second read from HBM.
 template <int RT, int D, int WV>
 __global__ __launch_bounds__(64 * WV) void k_nm_smfmac(NmArgs a) {
   constexpr int kNmWaves = WV, kNmThreads = 64 * WV;
@@ -123,7 +130,10 @@ __global__ __launch_bounds__(64 * WV) void k_nm_smfmac(NmArgs a) {
   __shared__ __align__(16) float red[kNmWaves][32 * RT][kNmStride];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int i = lane & 31, h = lane >> 5;
-  const int row0 = blockIdx.x * 32 * RT, c0 = blockIdx.y * 32;
+  const int xj = (int)blockIdx.x & 7, xq = (int)blockIdx.x >> 3;
+  const int bx = 8 * (xq / a.nby) + xj, by = xq % a.nby;
+  if (bx >= a.nbx) return;  // the grid is a whole number of runs
+  const int row0 = bx * 32 * RT, c0 = by * 32;
   const int n = a.n, nst = n >> 7;         // 128-column stages (n % 128 == 0)
   const int per = (nst + kNmWaves - 1) / kNmWaves;  // stages per wave
   char* const stg = reinterpret_cast<char*>(&red[w][0][0]);
@@ -371,9 +381,11 @@ size_t nm_mma_ws_bytes(const hss_matrix* A, int b) {
 }
 
 template <int RT>
-static void launch_nm_rt(const NmArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)((a.m + 32 * RT - 1) / (32 * RT)), (unsigned)((a.b + 31) / 32));
-  hipLaunchKernelGGL((k_nm_smfmac<RT, 2, kNmBlockWaves>), grid, dim3(64 * kNmBlockWaves), 0, s, a);
+static void launch_nm_rt(NmArgs a, hipStream_t s) {
+  a.nbx = (a.m + 32 * RT - 1) / (32 * RT);
+  a.nby = (a.b + 31) / 32;
+  const unsigned grid = (unsigned)((a.nbx + 7) / 8 * 8 * a.nby);
+  hipLaunchKernelGGL((k_nm_smfmac<RT, 2, kNmBlockWaves>), dim3(grid), dim3(64 * kNmBlockWaves), 0, s, a);
 }
 
 // X must be 16-byte aligned (the caller routes other X elsewhere).

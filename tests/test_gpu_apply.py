@@ -208,6 +208,39 @@ def test_apply_shared_workspace_many_calls(H):
         assert O.bits_equal(to_host(Y), expect[k][i]), (it, k, i)
 
 
+@pytest.mark.parametrize("fmt,b", [("csr", 1), ("2:4", 1), ("csr", 2), ("csr", 5)])
+def test_apply_on_two_streams_at_once(H, fmt, b):
+    """One matrix applied from two streams (default priority) with nothing
+    ordering the calls of one stream against the other's: the binding gives
+    each stream its own workspace, so every result equals the one-stream
+    result bit for bit."""
+    import torch
+    dtype = O.BF16
+    m, n, r, calls = 2100, 512, 40, 24
+    W = syn.random_matrix(m, n, dtype, seed=51, kind="t3")
+    ref = O.split_csr(W, dtype, O.topk_count(m, n, 5, 100)) if fmt == "csr" else O.split_24(W, dtype)
+    U, V = _factors(m, n, r, dtype, 52)
+    A = _matrix(H, fmt, dtype, m, n, ref, U, V)
+    xs = [to_dev(syn.random_matrix(b, n, dtype, seed=53 + i, kind="normal", scale=1.0), dtype) for i in range(4)]
+    expect = [to_host(H.hss_apply(A, x)) for x in xs]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    ys = [[torch.empty((b, m), dtype=torch.bfloat16, device="cuda") for _ in range(calls)] for _ in streams]
+    wss = []
+    for s in streams:
+        with torch.cuda.stream(s):
+            wss.append(A.workspace(b))
+    torch.cuda.synchronize()
+    assert wss[0].data_ptr() != wss[1].data_ptr()
+    for it in range(calls):
+        for si, s in enumerate(streams):
+            with torch.cuda.stream(s):
+                H.hss_apply(A, xs[(it + si) % 4], ys[si][it])
+    torch.cuda.synchronize()
+    for si in range(2):
+        for it in range(calls):
+            assert O.bits_equal(to_host(ys[si][it]), expect[(it + si) % 4]), (si, it)
+
+
 @pytest.mark.parametrize("fmt,b,m", [("csr", 1, 200), ("csr", 5, 200), ("2:4", 1, 200), ("csr", 32, 200),
                                      ("2:4", 64, 200), ("csr", 1, 1030), ("2:4", 1, 1030)])
 def test_apply_graph_replay_matches_eager(H, fmt, b, m):
