@@ -47,7 +47,7 @@ extern "C" {
 #endif
 
 #define HSS_VERSION_MAJOR 1
-#define HSS_VERSION_MINOR 5
+#define HSS_VERSION_MINOR 6
 
 /* Largest batch (columns of X) one hss_apply / hss_apply_group / hss_grad
  * call takes: decode (1) up to a prefill of 2048 tokens. */
@@ -207,9 +207,34 @@ hss_status hss_get_error(const void* ws, hipStream_t stream);
  *       D[i][j] = dq_levels[16 i + code(i, j)].
  *     Requires fmt == HSS_FMT_CSR, n even and r == 0 (a dense part together
  *     with a low-rank term returns HSS_ERR_UNSUPPORTED).
+ *   flags & HSS_HIER2: the low-rank term is the one-level 2 x 2 block form
+ *     ([HSS] section "順列と階層的整列": a higher rank on the diagonal blocks
+ *     than off them) held compactly, with no zeros: rows split at m0 = m/2,
+ *     columns at n0 = n/2, block b = (bi, bj) in the order 00, 01, 10, 11 of
+ *     rank hier_r[b] is U_b (rows of half bi) times V_b^T (columns of half
+ *     bj), and the term is their sum, each on its own block.  The matrix is
+ *     in the basis the blocks are defined in: for a layer reordered by a
+ *     permutation P (hss_rcm_order), S, X and Y are all in the permuted
+ *     order (S' = P S P^T from hss_csr_permute, x' = x[perm], y[perm[i]] =
+ *     y'[i]), as when P is folded into the neighbouring layers.
+ *       r  = hier_r[0] + hier_r[1] + hier_r[2] + hier_r[3];
+ *       ru = hier_r[0] + hier_r[1] = hier_r[2] + hier_r[3] (required);
+ *       U  dtype[m*ru]: row i < m0 holds [U_00 row i | U_01 row i], row
+ *          i >= m0 holds [U_10 row i - m0 | U_11 row i - m0];
+ *       Vt dtype[r * (n - n0)]: row o_b + l (o_b = hier_r[0] + ... +
+ *          hier_r[b-1]) holds row l of V_b^T, the n0 (bj = 0) or n - n0
+ *          (bj = 1) values of its column half, first; rows are n - n0 long
+ *          (with odd n the last value of a first-half row is not read).
+ *     hss_hier_pack_compact writes U and Vt from the four blocks.  Requires
+ *     fmt == HSS_FMT_CSR, no HSS_DQ4, m >= 2, n >= 2, every hier_r[b] >= 0.
+ *     Up to 8 columns per pass the fused decode kernel reads the compact
+ *     factors directly; wider batches first expand them into flat m x r /
+ *     r x n factors inside the workspace (hss_apply_workspace_size counts
+ *     them).  hss_grad does not take HSS_HIER2 (HSS_ERR_UNSUPPORTED).
  */
 #define HSS_COL16 1
 #define HSS_DQ4 2
+#define HSS_HIER2 4
 
 typedef struct hss_matrix {
   int32_t fmt;   /* hss_format */
@@ -226,6 +251,7 @@ typedef struct hss_matrix {
   const void* Vt;
   const uint8_t* dq_codes; /* HSS_DQ4 only (else ignored) */
   const void* dq_levels;   /* HSS_DQ4 only (else ignored) */
+  int32_t hier_r[4];       /* HSS_HIER2 only (else ignored): block ranks, order 00, 01, 10, 11 */
 } hss_matrix;
 
 /* out[i] = (uint16) col_idx[i] for i < nnz, on `stream`: the 16-bit column
@@ -402,6 +428,34 @@ hss_status hss_concentration(int32_t dt, int32_t m, int32_t n, const void* W, co
  *   HSS_ERR_HIP. */
 hss_status hss_hier_pack(int32_t dt, int32_t m, int32_t n, const int32_t* r, const void* const* U,
                          const void* const* Vt, const int32_t* perm, void* U_cat, void* Vt_cat, hipStream_t stream);
+
+/* hss_hier_pack_compact: the compact factors of an HSS_HIER2 matrix from its
+ *   four blocks (layouts as documented at HSS_HIER2; bits copied, device
+ *   arrays).  Block b = (bi, bj), in the order 00, 01, 10, 11: U[b] (rows
+ *   of half bi) x r[b] and Vt[b] r[b] x (columns of half bj), row-major, in
+ *   the blocks' own (permuted) order.  Writes U_c (m x ru, ru = r[0] + r[1]
+ *   = r[2] + r[3]) and Vt_c (R x (n - n/2), R = sum r[b]); the unread last
+ *   value of a first-half Vt_c row (odd n) is set to zero.
+ *   r, U, Vt: HOST arrays of 4 (the U and Vt entries are device pointers;
+ *   NULL for a rank-0 block).
+ *   HSS_ERR_INVALID_ARG: bad dtype, m or n < 2, r[b] < 0 or larger than its
+ *   block's smaller side, r[0] + r[1] != r[2] + r[3], null arrays,
+ *   m*ru or R*n >= 2^31; HSS_ERR_HIP. */
+hss_status hss_hier_pack_compact(int32_t dt, int32_t m, int32_t n, const int32_t* r, const void* const* U,
+                                 const void* const* Vt, void* U_c, void* Vt_c, hipStream_t stream);
+
+/* hss_csr_permute: the CSR pattern of S' = P S P^T, S'[i][j] =
+ *   S[perm[i]][perm[j]], for a square n x n S (the sparse part of a layer
+ *   reordered by perm, e.g. hss_rcm_order's), in HOST memory, computed on
+ *   the host, synchronously (once per pattern): row_ptr_p (int32[n+1]) and
+ *   col_idx_p (int32[nnz]) with each row's columns ascending; from
+ *   (int32[nnz]): entry q of S' is entry from[q] of S (hss_gather_values
+ *   moves the values).
+ *   HSS_ERR_INVALID_ARG: n < 1, null arrays, row_ptr[0] != 0, decreasing
+ *   row_ptr, a column outside [0, n), perm not a permutation of [0, n),
+ *   repeated columns within a row. */
+hss_status hss_csr_permute(int32_t n, const int32_t* row_ptr, const int32_t* col_idx, const int32_t* perm,
+                           int32_t* row_ptr_p, int32_t* col_idx_p, int32_t* from);
 
 /* ------------------------------------------------------------------------
  * Backward pass ([HSS] section "実装と運用パターン", the backward formulas):

@@ -65,7 +65,10 @@ Readings where the pages are silent or ambiguous:
   the original index at position i; the permuted matrix is W'[i, j] =
   W[perm[i], perm[j]].  S stays in the original order (stage 1 before the
   permutation); each block of the permuted residual gets its own truncated
-  SVD.
+  SVD.  A layer reordered by perm can also be held entirely in the permuted
+  order (as when the permutation is folded into the neighbouring layers):
+  S' = P S P^T (csr_permute), x' = x[perm], y[perm] = y'; its block term is
+  then the plain block matrix, with no permutation inside.
 
 * Backward: the pages give dS, dU and dV; the input gradient dX = G A is
   added, since a layer's backward pass needs it.  dS is restricted to S's
@@ -573,6 +576,28 @@ def hier_lowrank_dense(blocks, perm, m, n):
     L = np.zeros((m, n))
     L[np.ix_(p, p)] = Lp
     return L
+
+
+def csr_permute(n, row_ptr, col_idx, perm):
+    """S' = P S P^T of a square n x n CSR pattern, S'[i, j] = S[perm[i],
+    perm[j]]: (row_ptr', col_idx', src) with each row's columns ascending;
+    entry q of S' is entry src[q] of S (values' = values[src]).  Row i of S'
+    is row perm[i] of S with every column c renamed to its position pos[c]
+    (pos = the inverse of perm)."""
+    perm = np.asarray(perm, dtype=np.int64)
+    pos = np.empty(n, dtype=np.int64)
+    pos[perm] = np.arange(n)
+    rp = np.asarray(row_ptr, dtype=np.int64)
+    ci = np.asarray(col_idx, dtype=np.int64)
+    out_rp = [0]
+    out_ci, src = [], []
+    for i in range(n):
+        row = sorted((int(pos[ci[p]]), p) for p in range(rp[perm[i]], rp[perm[i] + 1]))
+        out_ci.extend(c for c, _ in row)
+        src.extend(p for _, p in row)
+        out_rp.append(len(out_ci))
+    return (np.array(out_rp, dtype=np.int32), np.array(out_ci, dtype=np.int32),
+            np.array(src, dtype=np.int64))
 
 
 def hier_apply(S64, blocks, perm, X64):

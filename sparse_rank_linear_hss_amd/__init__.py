@@ -19,7 +19,7 @@ from typing import Optional
 
 import torch
 
-from ._lib import (HSS_BF16, HSS_COL16, HSS_DQ4, HSS_ERR_NONFINITE, HSS_F32, HSS_FMT_2OF4, HSS_FMT_CSR,
+from ._lib import (HSS_BF16, HSS_COL16, HSS_DQ4, HSS_ERR_NONFINITE, HSS_HIER2, HSS_F32, HSS_FMT_2OF4, HSS_FMT_CSR,
                    HSS_MAX_BATCH, HSS_OK, HSS_OPT_BATCH_ROUTE, HSS_OPT_DECODE_FORCE_LOCAL, HSS_OPT_DECODE_MERGED,
                    HSS_OPT_DECODE_SPIN, HSS_OPT_GRAD_DS_ROUTE, HSSError, HssMatrixStruct, LIB_PATH, check, lib,
                    status_string)
@@ -29,8 +29,8 @@ __all__ = [
     "hss_set_option", "hss_get_option", "option", "HSS_MAX_BATCH",
     "hss_apply_workspace_size", "hss_apply_workspace_init", "apply_workspace", "hss_apply", "hss_apply_noalloc",
     "hss_apply_group_workspace_size", "hss_apply_group",
-    "hss_csr_cols_to_u16", "HSS_COL16", "HSS_DQ4",
-    "hss_rcm_order", "hss_concentration", "hss_hier_pack",
+    "hss_csr_cols_to_u16", "HSS_COL16", "HSS_DQ4", "HSS_HIER2",
+    "hss_rcm_order", "hss_concentration", "hss_hier_pack", "hss_hier_pack_compact", "hss_csr_permute",
     "hss_grad", "hss_csr_transpose", "hss_gather_values", "hss_transpose", "hss_transposed_layer", "hss_backward",
     "hss_nm24_to_csr",
     "HSSMatrix", "SplitResult", "HSSError",
@@ -179,12 +179,17 @@ class HSSMatrix:
     65536, see hss_csr_cols_to_u16) -- the matrix then carries HSS_COL16.
     dq_codes (uint8, m x n/2: the 4-bit codes of columns 2j and 2j+1 in the
     low and high nibble of byte j) with dq_levels (m x 16, the matrix dtype)
-    add the quantised dense part D of the dense-and-sparse form (HSS_DQ4)."""
+    add the quantised dense part D of the dense-and-sparse form (HSS_DQ4).
+    hier_r (ranks of the 2 x 2 blocks 00, 01, 10, 11) makes the low-rank term
+    the compact block form (HSS_HIER2): U m x (hier_r[0] + hier_r[1]) and
+    Vt sum(hier_r) x (n - n // 2) as hss_hier_pack_compact writes them, the
+    matrix in the blocks' (permuted) order."""
 
     def __init__(self, fmt, m, n, dtype, U=None, Vt=None, row_ptr=None, col_idx=None, values=None,
-                 nnz=None, nm_values=None, nm_meta=None, dq_codes=None, dq_levels=None):
+                 nnz=None, nm_values=None, nm_meta=None, dq_codes=None, dq_levels=None, hier_r=None):
         self.fmt = _FMT[fmt]
         self.flags = HSS_COL16 if (col_idx is not None and col_idx.dtype == torch.int16) else 0
+        self.hier_r = None if hier_r is None else [int(v) for v in hier_r]
         if dq_codes is not None:
             assert dq_codes.dtype == torch.uint8 and dq_codes.is_contiguous() and dq_codes.numel() == m * n // 2
             assert dq_levels is not None and dq_levels.dtype == dtype and dq_levels.is_contiguous()
@@ -194,9 +199,17 @@ class HSSMatrix:
         self.m, self.n = int(m), int(n)
         self.dtype = dtype
         self.U, self.Vt = U, Vt
-        self.r = 0 if U is None else int(U.shape[1])
+        if self.hier_r is not None:
+            self.flags |= HSS_HIER2
+            self.r = sum(self.hier_r)
+            ru = self.hier_r[0] + self.hier_r[1]
+            if self.r > 0:
+                assert U.shape == (self.m, ru) and Vt.shape == (self.r, self.n - self.n // 2)
+        else:
+            self.r = 0 if U is None else int(U.shape[1])
+            if self.r > 0:
+                assert U.shape == (self.m, self.r) and Vt.shape == (self.r, self.n)
         if self.r > 0:
-            assert U.shape == (self.m, self.r) and Vt.shape == (self.r, self.n)
             assert U.dtype == dtype and Vt.dtype == dtype and U.is_contiguous() and Vt.is_contiguous()
         self.row_ptr, self.col_idx, self.values = row_ptr, col_idx, values
         self.nm_values, self.nm_meta = nm_values, nm_meta
@@ -210,6 +223,8 @@ class HSSMatrix:
         s.nm_values, s.nm_meta = _ptr(nm_values), _ptr(nm_meta)
         s.U, s.Vt = (_ptr(U), _ptr(Vt)) if self.r > 0 else (None, None)
         s.dq_codes, s.dq_levels = _ptr(dq_codes), _ptr(dq_levels)
+        if self.hier_r is not None:
+            s.hier_r = (ctypes.c_int32 * 4)(*self.hier_r)
         self.struct = s
 
     @classmethod
@@ -231,7 +246,8 @@ class HSSMatrix:
         return HSSMatrix("csr", self.m, self.n, self.dtype, U=self.U, Vt=self.Vt, row_ptr=self.row_ptr,
                          col_idx=c16 if c16 is not None else torch.zeros(0, dtype=torch.int16,
                                                                            device=self.row_ptr.device),
-                         values=self.values, nnz=self.nnz, dq_codes=self.dq_codes, dq_levels=self.dq_levels)
+                         values=self.values, nnz=self.nnz, dq_codes=self.dq_codes, dq_levels=self.dq_levels,
+                         hier_r=self.hier_r)
 
     def workspace(self, b: int, device=None) -> torch.Tensor:
         """Initialised apply workspace for batch b on the current stream.
@@ -413,6 +429,50 @@ def hss_hier_pack(U, Vt, m: int, n: int, perm: Optional[torch.Tensor] = None):
     return Ucat, Vtcat
 
 
+def hss_hier_pack_compact(U, Vt, m: int, n: int):
+    """Compact factors (U_c m x ru, Vt_c R x (n - n // 2)) of an HSS_HIER2
+    matrix from its blocks U[b] Vt[b], b in the order 00, 01, 10, 11 (None
+    for a rank-0 block), in the blocks' own order; with hier_r = the block
+    ranks they make HSSMatrix(..., hier_r=...)."""
+    dtype = next(u.dtype for u in U if u is not None)
+    dev = next(u.device for u in U if u is not None)
+    r = [0 if u is None else int(u.shape[1]) for u in U]
+    R, ru = sum(r), r[0] + r[1]
+    rows, cols = (m // 2, m - m // 2), (n // 2, n - n // 2)
+    for b, (u, v) in enumerate(zip(U, Vt)):
+        if u is None:
+            continue
+        if not u.is_contiguous() or not v.is_contiguous() or u.dtype != dtype or v.dtype != dtype:
+            raise ValueError("blocks must be contiguous tensors of one dtype")
+        if tuple(u.shape) != (rows[b >> 1], r[b]) or tuple(v.shape) != (r[b], cols[b & 1]):
+            raise ValueError(f"block {b}: U {tuple(u.shape)} / Vt {tuple(v.shape)} do not fit a {m} x {n} matrix")
+    Uc = torch.empty((m, ru), dtype=dtype, device=dev)
+    Vtc = torch.empty((R, n - n // 2), dtype=dtype, device=dev)
+    r_arr = (ctypes.c_int32 * 4)(*r)
+    u_arr = (ctypes.c_void_p * 4)(*[_ptr(u) for u in U])
+    v_arr = (ctypes.c_void_p * 4)(*[_ptr(v) for v in Vt])
+    check(lib.hss_hier_pack_compact(_DT[dtype], int(m), int(n), r_arr, u_arr, v_arr, _ptr(Uc), _ptr(Vtc),
+                                    _stream(dev)), "hss_hier_pack_compact")
+    return Uc, Vtc
+
+
+def hss_csr_permute(row_ptr, col_idx, perm, n: int):
+    """S' = P S P^T (S'[i][j] = S[perm[i]][perm[j]]) of a square CSR pattern,
+    on the host: (row_ptr_p, col_idx_p, from), entry q of S' being entry
+    from[q] of S (hss_gather_values moves the values)."""
+    import numpy as np
+    rp = np.ascontiguousarray(row_ptr.cpu().numpy() if isinstance(row_ptr, torch.Tensor) else row_ptr, dtype=np.int32)
+    ci = np.ascontiguousarray(col_idx.cpu().numpy() if isinstance(col_idx, torch.Tensor) else col_idx, dtype=np.int32)
+    pm = np.ascontiguousarray(perm.cpu().numpy() if isinstance(perm, torch.Tensor) else perm, dtype=np.int32)
+    nnz = int(rp[n])
+    rpp = np.zeros(int(n) + 1, dtype=np.int32)
+    cip = np.zeros(max(nnz, 1), dtype=np.int32)
+    frm = np.zeros(max(nnz, 1), dtype=np.int32)
+    check(lib.hss_csr_permute(int(n), rp.ctypes.data, ci.ctypes.data if nnz else None, pm.ctypes.data,
+                              rpp.ctypes.data, cip.ctypes.data, frm.ctypes.data), "hss_csr_permute")
+    return rpp, cip[:nnz], frm[:nnz]
+
+
 
 # ---------------------------------------------------------------------------
 # Backward pass
@@ -493,8 +553,8 @@ def hss_transposed_layer(A: HSSMatrix) -> HSSMatrix:
     host transpose (of the 2:4 positions for a 2:4 layer), its values
     gathered on the device, U' = V and V'^T = U^T from the stored factors.
     hss_apply(A^T, G) is the input gradient G A."""
-    if A.flags & HSS_DQ4:
-        raise ValueError("the transposed layer is built for CSR and 2:4 layers")
+    if A.flags & (HSS_DQ4 | HSS_HIER2):
+        raise ValueError("the transposed layer is built for CSR and 2:4 layers with flat factors")
     if A.fmt == HSS_FMT_2OF4:
         dev = A.nm_meta.device
         row_ptr, cols = hss_nm24_to_csr(A)

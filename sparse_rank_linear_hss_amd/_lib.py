@@ -27,6 +27,7 @@ HSS_OPT_DECODE_MERGED = 3
 HSS_OPT_DECODE_FORCE_LOCAL = 4
 HSS_COL16 = 1  # hss_matrix.flags: CSR col_idx holds uint16 columns
 HSS_DQ4 = 2    # hss_matrix.flags: a 4-bit quantised dense part (dq_codes, dq_levels)
+HSS_HIER2 = 4  # hss_matrix.flags: compact 2 x 2 block low-rank term (hier_r)
 
 c_int32, c_int64, c_size_t, c_void_p = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
 
@@ -41,6 +42,7 @@ class HssMatrixStruct(ctypes.Structure):
         ("nm_values", c_void_p), ("nm_meta", c_void_p),
         ("U", c_void_p), ("Vt", c_void_p),
         ("dq_codes", c_void_p), ("dq_levels", c_void_p),
+        ("hier_r", c_int32 * 4),
     ]
 
 
@@ -89,6 +91,9 @@ def _load():
         "hss_grad": (ctypes.c_int, [P(HssMatrixStruct), c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                     c_void_p, c_size_t, c_void_p]),
         "hss_csr_transpose": (ctypes.c_int, [c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+        "hss_hier_pack_compact": (ctypes.c_int, [ctypes.c_int, c_int32, c_int32, P(c_int32), P(c_void_p),
+                                                 P(c_void_p), c_void_p, c_void_p, c_void_p]),
+        "hss_csr_permute": (ctypes.c_int, [c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
         "hss_gather_values": (ctypes.c_int, [ctypes.c_int, c_int64, c_void_p, c_void_p, c_void_p, c_void_p]),
         "hss_transpose": (ctypes.c_int, [ctypes.c_int, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
         "hss_nm24_to_csr": (ctypes.c_int, [c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),

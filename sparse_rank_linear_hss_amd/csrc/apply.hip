@@ -37,6 +37,23 @@ int decode_max_cols(const hss_matrix* A);
 int decode_dq_max_cols(const hss_matrix* A);
 void launch_decode_dq(const hss_matrix* A, int bc, const void* X, void* Y, hipStream_t s);
 static bool is_dq(const hss_matrix* A) { return (A->flags & HSS_DQ4) != 0; }
+static bool is_hier(const hss_matrix* A) { return (A->flags & HSS_HIER2) != 0; }
+static size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// A block-structured (HSS_HIER2) matrix takes the fused decode kernel with
+// its compact factors; the batched routes read flat factors, expanded per
+// call into the workspace (m x r and r x n, zeros outside the blocks).
+static size_t hier_flat_bytes(const hss_matrix* A) {
+  const size_t es = A->dtype == HSS_F32 ? 4 : 2;
+  return a256((size_t)A->m * A->r * es) + a256((size_t)A->r * A->n * es);
+}
+static hss_matrix flat_view(const hss_matrix* A, void* Uf, void* Vtf) {
+  hss_matrix F = *A;
+  F.flags &= ~HSS_HIER2;
+  F.U = Uf;
+  F.Vt = Vtf;
+  return F;
+}
 
 static constexpr int kDecodeCols = 8;
 
@@ -75,8 +92,10 @@ static constexpr int kSpmmMinCols = 3, kSpmmMaxCols = 128;
 
 // X: the call's input (the sparse matrix cores need it 16-byte aligned), or
 // null when sizing a workspace.
-static Route batch_route(const hss_matrix* A, int b, const void* X) {
+static Route batch_route(const hss_matrix* A0, int b, const void* X) {
   if (b < 2) return R_DECODE;  // one column: always the fused decode kernel
+  const hss_matrix F = is_hier(A0) ? flat_view(A0, nullptr, nullptr) : *A0;  // routes decide on shapes only
+  const hss_matrix* A = &F;
   const bool sp = spmm_supported(A, b), mf = mfma_supported(A, b);
   const bool nm = nm_mma_supported(A, b) && (uintptr_t)X % 16 == 0;
   switch (option(HSS_OPT_BATCH_ROUTE)) {
@@ -95,28 +114,33 @@ static Route batch_route(const hss_matrix* A, int b, const void* X) {
 // Layout: [decode control region | decode T words or MFMA buffers].  The
 // control region persists between calls; everything after it is per-call
 // scratch, so both paths can share one workspace.
-size_t apply_ws_bytes(const hss_matrix* A, int b) {
-  if (is_dq(A)) return 0;
+size_t apply_ws_bytes(const hss_matrix* A0, int b) {
+  if (is_dq(A0)) return 0;
   // every route the call may take (the route can be forced at call time)
-  const size_t dec = decode_t_bytes(A);
+  const size_t dec = decode_t_bytes(A0);
+  const hss_matrix F = is_hier(A0) ? flat_view(A0, nullptr, nullptr) : *A0;
+  const hss_matrix* A = &F;
   const size_t mf = mfma_supported(A, b) ? mfma_ws_bytes(A, b) : 0;
   const size_t sp = spmm_supported(A, b) ? spmm_ws_bytes(A, b) : 0;
   const size_t nm = nm_mma_supported(A, b) ? nm_mma_ws_bytes(A, b) : 0;
-  size_t mx = dec > mf ? dec : mf;
-  mx = mx > sp ? mx : sp;
+  size_t mx = mf > sp ? mf : sp;
   mx = mx > nm ? mx : nm;
-  return decode_ctl_bytes() + mx;
+  if (is_hier(A0) && b >= 2) mx += hier_flat_bytes(A0);
+  return decode_ctl_bytes() + (dec > mx ? dec : mx);
 }
 
 // Workspace bytes of the route this call takes (hss_apply_workspace_size
 // covers every route a call could be forced onto).
-size_t apply_route_ws_bytes(const hss_matrix* A, int b, const void* X) {
-  if (is_dq(A)) return 0;
-  switch (batch_route(A, b, X)) {
-    case R_NM: return decode_ctl_bytes() + nm_mma_ws_bytes(A, b);
-    case R_MFMA: return decode_ctl_bytes() + mfma_ws_bytes(A, b);
-    case R_SPMM: return decode_ctl_bytes() + spmm_ws_bytes(A, b);
-    default: return decode_ctl_bytes() + decode_t_bytes(A);
+size_t apply_route_ws_bytes(const hss_matrix* A0, int b, const void* X) {
+  if (is_dq(A0)) return 0;
+  const hss_matrix F = is_hier(A0) ? flat_view(A0, nullptr, nullptr) : *A0;
+  const hss_matrix* A = &F;
+  const size_t flat = is_hier(A0) ? hier_flat_bytes(A0) : 0;
+  switch (batch_route(A0, b, X)) {
+    case R_NM: return decode_ctl_bytes() + flat + nm_mma_ws_bytes(A, b);
+    case R_MFMA: return decode_ctl_bytes() + flat + mfma_ws_bytes(A, b);
+    case R_SPMM: return decode_ctl_bytes() + flat + spmm_ws_bytes(A, b);
+    default: return decode_ctl_bytes() + decode_t_bytes(A0);
   }
 }
 
@@ -134,9 +158,21 @@ hss_status launch_apply(const hss_matrix* A, int b, const void* X, void* Y, void
     return hipGetLastError() == hipSuccess ? HSS_OK : HSS_ERR_HIP;
   }
   const Route route = batch_route(A, b, X);
-  if (route == R_NM) return launch_nm_mma(A, b, X, Y, static_cast<char*>(ws) + decode_ctl_bytes(), stream);
-  if (route == R_MFMA) return launch_mfma(A, b, X, Y, static_cast<char*>(ws) + decode_ctl_bytes(), stream);
-  if (route == R_SPMM) return launch_spmm(A, b, X, Y, static_cast<char*>(ws) + decode_ctl_bytes(), stream);
+  char* scratch = static_cast<char*>(ws) + decode_ctl_bytes();
+  hss_matrix F;
+  if (route != R_DECODE && is_hier(A)) {
+    const size_t es = A->dtype == HSS_F32 ? 4 : 2;
+    void* Uf = A->r > 0 ? scratch : nullptr;
+    void* Vtf = A->r > 0 ? scratch + a256((size_t)A->m * A->r * es) : nullptr;
+    const hss_status st = launch_hier_expand(A, Uf, Vtf, stream);
+    if (st != HSS_OK) return st;
+    scratch += hier_flat_bytes(A);
+    F = flat_view(A, Uf, Vtf);
+    A = &F;
+  }
+  if (route == R_NM) return launch_nm_mma(A, b, X, Y, scratch, stream);
+  if (route == R_MFMA) return launch_mfma(A, b, X, Y, scratch, stream);
+  if (route == R_SPMM) return launch_spmm(A, b, X, Y, scratch, stream);
   const size_t es = A->dtype == HSS_F32 ? 4 : 2;
   const int cols = decode_max_cols(A);
   if (cols == 0) return HSS_ERR_UNSUPPORTED;

@@ -87,6 +87,24 @@ static MatrixLaunch matrix_launch(const hss_matrix* A, int bc, const void* X, vo
   a.t_stride = t_stride_words(A->r);
   a.nnz = A->nnz;
   a.spin = spin_limit();
+  const bool hier = (A->flags & HSS_HIER2) != 0;
+  if (hier) {  // the 2 x 2 block-structured low-rank term in compact form
+    a.ru = A->hier_r[0] + A->hier_r[1];
+    a.v_ld = hier_vt_ld(A->n);
+    a.h_m0 = A->m / 2;
+    a.h_toff = a.ru;
+    a.h_n0 = A->n / 2;
+    a.h_l1 = A->hier_r[0];
+    a.h_l2 = A->hier_r[0] + A->hier_r[1];
+    a.h_l3 = a.h_l2 + A->hier_r[2];
+  } else {
+    a.ru = A->r;
+    a.v_ld = A->n;
+    a.h_m0 = A->m;
+    a.h_toff = 0;
+    a.h_n0 = A->n;
+    a.h_l1 = a.h_l2 = a.h_l3 = A->r;
+  }
 
   const size_t es = A->dtype == HSS_F32 ? 4 : 2;
   const size_t tbytes = align16(sizeof(float) * (size_t)bc * t_ld(A->r));
@@ -103,14 +121,15 @@ static MatrixLaunch matrix_launch(const hss_matrix* A, int bc, const void* X, vo
   a.x_pad = nm_fast && a.x_lds;
   // Vector dot products: X rows and Vt rows start 16-byte aligned.
   a.vec = ((uintptr_t)X % 16 == 0) && ((size_t)A->n * es) % 16 == 0 &&
-          (A->r == 0 || (uintptr_t)A->Vt % 16 == 0);
+          (A->r == 0 || (uintptr_t)A->Vt % 16 == 0) && ((size_t)a.v_ld * es) % 16 == 0 &&
+          ((size_t)a.h_n0 * es) % 16 == 0;
   a.vec_csr = A->fmt == HSS_FMT_CSR && A->nnz >= 4 && (uintptr_t)A->col_idx % (col16_of(A) ? 8 : 16) == 0 &&
               (uintptr_t)A->values % (4 * es) == 0;
   a.nm_fast = A->fmt == HSS_FMT_2OF4 && A->dtype == HSS_BF16 && a.vec && A->n % 32 == 0 &&
               (uintptr_t)A->nm_values % 16 == 0 && (uintptr_t)A->nm_meta % 4 == 0;
   // bf16 U rows as aligned 16-byte pieces (any r): one piece per lane covers
   // r <= 506, two r <= 1018 (and give the same bits there as one would).
-  L.uq = (A->dtype == HSS_BF16 && A->r > 0 && (uintptr_t)A->U % 16 == 0) ? (A->r <= 506 ? 1 : 2) : 0;
+  L.uq = (A->dtype == HSS_BF16 && a.ru > 0 && (uintptr_t)A->U % 16 == 0) ? (a.ru <= 506 ? 1 : 2) : 0;
   L.lds = tbytes + mbytes + (a.x_lds ? xbytes : 0);
   L.fast = A->dtype == HSS_BF16 && A->r > 0 && a.x_lds && a.vec &&
            (A->fmt == HSS_FMT_CSR ? a.vec_csr : a.nm_fast);

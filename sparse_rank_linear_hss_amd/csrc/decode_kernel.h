@@ -78,7 +78,20 @@ struct DecodeArgs {
   int nm_fast;    // bf16 2:4 with n % 32 == 0 and aligned rows: vector words
   int spin;       // polls of a stale T word before computing it locally
   int t_off, miss_off, x_off;  // dynamic LDS layout (bytes)
+  // Block structure of the low-rank term (a flat matrix: ru = r, v_ld = n,
+  // h_m0 = m, h_toff = 0, h_n0 = n, h_l1 = h_l2 = h_l3 = r).  U rows hold ru
+  // values (row stride ru); rows i >= h_m0 take them against T[h_toff ..
+  // h_toff + ru).  T row l dots V^T row l (row stride v_ld) with X columns
+  // [0, h_n0), or [h_n0, n) when h_l1 <= l < h_l2 or l >= h_l3.
+  int ru, v_ld, h_m0, h_toff, h_n0, h_l1, h_l2, h_l3;
 };
+
+// First X column and column count of T row l.
+__device__ __forceinline__ void t_cols(const DecodeArgs& a, int l, int& c0, int& len) {
+  const bool hi = (l >= a.h_l1 && l < a.h_l2) || l >= a.h_l3;
+  c0 = hi ? a.h_n0 : 0;
+  len = hi ? a.n - a.h_n0 : a.h_n0;
+}
 
 // Several matrices that share X in one launch (at most kMaxGroup): the grid is
 // the producer blocks of every matrix, then the row blocks of every matrix.
@@ -163,7 +176,9 @@ __device__ __forceinline__ float red_sum(float (*red)[BC], int c) {
   return s;
 }
 
-// Block-wide T[c][l] = Vt[l,:] . X[c,:] for c < bc (all NT threads).  Thread
+// Block-wide T[c][l] = v[0 .. n) . xsrc[c * xld + (0 .. n)] for c < bc (all
+// NT threads; v is V^T row l over the row's X columns, xsrc the first of
+// them in column 0 of X, xld the X row stride).  Thread
 // t covers 16-byte vectors q = t + NT*k; TV of them (per operand) are loaded
 // before any is used.  Slots past the end load vector 0 (one address for the
 // whole wave, a single request) and are skipped at use; clamping them to the
@@ -172,7 +187,7 @@ __device__ __forceinline__ float red_sum(float (*red)[BC], int c) {
 // barrier.
 template <int DT, int BC, int NT>
 __device__ __forceinline__ void t_row(const typename Elem<DT>::bits_t* __restrict__ v,
-                                      const typename Elem<DT>::bits_t* __restrict__ xsrc, int n,
+                                      const typename Elem<DT>::bits_t* __restrict__ xsrc, int n, int xld,
                                       int bc, int vec, float (*red)[BC]) {
   using bits_t = typename Elem<DT>::bits_t;
   constexpr int TV = BC <= 2 ? 4 : (BC <= 4 ? 2 : 1);
@@ -197,7 +212,7 @@ __device__ __forceinline__ void t_row(const typename Elem<DT>::bits_t* __restric
         vv[k] = __builtin_nontemporal_load(v4 + qc);
 #pragma unroll
         for (int c = 0; c < BC; ++c)
-          xv[k][c] = reinterpret_cast<const u32x4*>(xsrc + (int64_t)min(c, bc - 1) * n)[qc];
+          xv[k][c] = reinterpret_cast<const u32x4*>(xsrc + (int64_t)min(c, bc - 1) * xld)[qc];
       }
 #pragma unroll
       for (int k = 0; k < TV; ++k) {
@@ -214,7 +229,7 @@ __device__ __forceinline__ void t_row(const typename Elem<DT>::bits_t* __restric
     const float vj = fval<DT>(v[j]);
 #pragma unroll
     for (int c = 0; c < BC; ++c)
-      if (c < bc) acc[c] = fmaf(vj, fval<DT>(xsrc[(int64_t)c * n + j]), acc[c]);
+      if (c < bc) acc[c] = fmaf(vj, fval<DT>(xsrc[(int64_t)c * xld + j]), acc[c]);
   }
   const int w = t >> 6;
 #pragma unroll
@@ -606,7 +621,7 @@ __device__ __forceinline__ void u_issue(const DecodeArgs& a, int row0, UBuf<UQ> 
   using bits_t = typename Elem<DT>::bits_t;
   const bits_t* __restrict__ U = static_cast<const bits_t*>(a.U);
   const int lane = lane_id();
-  const int m = a.m, r = a.r;
+  const int m = a.m, r = a.ru;
 #pragma unroll
   for (int i = 0; i < RPW; ++i) {
     const int64_t rowc = min(row0 + i, m - 1);
@@ -636,18 +651,22 @@ __device__ __host__ __forceinline__ int t_ld(int r) { return r + 2 * kTPad; }
 
 template <int DT, int BC, int RPW, int UQ>
 __device__ __forceinline__ void u_epilogue(const DecodeArgs& a, int row0, const UBuf<UQ> (&ub)[RPW],
-                                           const float* __restrict__ Tp, float (&acc)[RPW][BC]) {
+                                           const float* __restrict__ Tp0, float (&acc)[RPW][BC]) {
   using bits_t = typename Elem<DT>::bits_t;
   const bits_t* __restrict__ U = static_cast<const bits_t*>(a.U);
   const int lane = lane_id();
-  const int m = a.m, r = a.r, bc = a.bc;
-  const int tld = t_ld(r);
+  const int m = a.m, r = a.ru, bc = a.bc;
+  const int tld = t_ld(a.r);
 #pragma unroll
   for (int i = 0; i < RPW; ++i) {
     const int row = row0 + i;
 #pragma unroll
     for (int c = 0; c < BC; ++c) acc[i][c] = 0.f;
     if (row >= m) continue;
+    // this row's T values: T[h_toff ..] in the second row half of a block-
+    // structured term (pieces still read at most 8 past r or 7 before 0:
+    // other T values or the column's zero pads)
+    const float* __restrict__ Tp = Tp0 + (row >= a.h_m0 ? a.h_toff : 0);
     if constexpr (UQ > 0) {
       const int64_t e0 = (int64_t)row * r;
       const int sh = (int)(e0 & 7);  // the row starts at element sh of its first piece
@@ -849,7 +868,9 @@ __global__ __launch_bounds__(MTR > 0 ? kMergedThreads : 256) void k_decode(Group
     if (producer) {
       const int l = local;
       const uint32_t e = load_epoch(a);
-      t_row<DT, BC, NT>(Vt + (int64_t)l * n, X, n, bc, a.vec, red);
+      int tc0, tlen;
+      t_cols(a, l, tc0, tlen);
+      t_row<DT, BC, NT>(Vt + (int64_t)l * a.v_ld, X + tc0, tlen, n, bc, a.vec, red);
       uint32_t arrived = 0;
       if (t == 0) arrived = arrive_issue(a, sub, e);
       // lane rep of wave 0 publishes the row into replica rep
@@ -912,9 +933,12 @@ __global__ __launch_bounds__(MTR > 0 ? kMergedThreads : 256) void k_decode(Group
   // MERGED: the epoch, X and this block's Vt rows go out first, so its T rows
   // can be published as soon as they return (loads return in issue order).
   // Slots past r load row l % r (a valid row, not the same one for every
-  // block) and publish nothing.
+  // block) and publish nothing.  Thread t takes vector t of each row and the
+  // X vector it meets (t itself, or t + n/2 / NV for a row of the second
+  // column half of a block-structured term), as t_row does.
   uint32_t epoch = 0;
-  u32x4 vt[MERGED ? MTR : 1];
+  u32x4 vt[MERGED ? MTR : 1], xt[MERGED ? MTR : 1];
+  int tvecs[MERGED ? MTR : 1];
   if constexpr (MERGED) {
     epoch = load_epoch(a);
     x_issue();
@@ -922,7 +946,12 @@ __global__ __launch_bounds__(MTR > 0 ? kMergedThreads : 256) void k_decode(Group
     for (int i = 0; i < MTR; ++i) {
       const int l = local + nb * i;
       const int lc = l < r ? l : l % r;
-      vt[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Vt + (int64_t)lc * n) + (t < xvecs ? t : 0));
+      int tc0, tlen;
+      t_cols(a, lc, tc0, tlen);
+      tvecs[i] = tlen / NV;
+      const int q = t < tvecs[i] ? t : 0;
+      vt[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Vt + (int64_t)lc * a.v_ld) + q);
+      xt[i] = reinterpret_cast<const u32x4*>(X + tc0)[q];
     }
   }
 
@@ -955,7 +984,7 @@ __global__ __launch_bounds__(MTR > 0 ? kMergedThreads : 256) void k_decode(Group
     __syncthreads();
     float p[MTR];
 #pragma unroll
-    for (int i = 0; i < MTR; ++i) p[i] = wave_sum(t < xvecs ? dot16<DT>(vt[i], xr[0], 0.f) : 0.f);
+    for (int i = 0; i < MTR; ++i) p[i] = wave_sum(t < tvecs[i] ? dot16<DT>(vt[i], xt[i], 0.f) : 0.f);
     uint32_t done = 0;
     if (lane_id() == 0) {
 #pragma unroll
@@ -1028,13 +1057,27 @@ __global__ __launch_bounds__(MTR > 0 ? kMergedThreads : 256) void k_decode(Group
   // still stale here is re-read below.
   constexpr int kTW = MERGED ? 1 : (FAST ? 2 : 4);
   const uint64_t* __restrict__ Tr = a.Tt + (int64_t)(blockIdx.x % kTReplicas) * a.t_stride;
-  const int ttotal = bc * r;
+  // The T rows this block reads: all r of them, or, for a block-structured
+  // term whose rows all lie in one row half, that half's ru rows (the
+  // epilogue reads no others).  Slot e is column e / tn, row tlo + e % tn.
+  int tlo = 0, tn = r;
+  if (a.h_m0 < m) {
+    const int first = local * NW * RPW, last = first + NW * RPW - 1;
+    if (first >= a.h_m0) {
+      tlo = a.h_toff;
+      tn = a.ru;
+    } else if (last < a.h_m0) {
+      tn = a.ru;
+    }
+  }
+  const int ttotal = bc * tn;
+  auto t_word = [&](int e) { return BC == 1 ? tlo + e : (e / tn) * r + tlo + e % tn; };
   uint64_t tv[kTW];
   if constexpr (FAST) {
 #pragma unroll
     for (int k = 0; k < kTW; ++k) {
       const int e = t + NT * k;
-      tv[k] = __hip_atomic_load(Tr + (e < ttotal ? e : e % ttotal), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      tv[k] = __hip_atomic_load(Tr + t_word(e < ttotal ? e : e % ttotal), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 
@@ -1059,7 +1102,7 @@ __global__ __launch_bounds__(MTR > 0 ? kMergedThreads : 256) void k_decode(Group
 #pragma unroll
         for (int k = 0; k < kTW; ++k) {
           const int e = base + t + NT * k;
-          tv[k] = __hip_atomic_load(Tr + (e < ttotal ? e : e % ttotal), __ATOMIC_RELAXED,
+          tv[k] = __hip_atomic_load(Tr + t_word(e < ttotal ? e : e % ttotal), __ATOMIC_RELAXED,
                                     __HIP_MEMORY_SCOPE_AGENT);
         }
       }
@@ -1070,13 +1113,13 @@ __global__ __launch_bounds__(MTR > 0 ? kMergedThreads : 256) void k_decode(Group
           uint64_t v = tv[k];
           for (int s = 0; (uint32_t)(v >> 32) != tag && s < a.spin; ++s) {
             __builtin_amdgcn_s_sleep(1);
-            v = __hip_atomic_load(Tr + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            v = __hip_atomic_load(Tr + t_word(e), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
+          const int ce = BC == 1 ? 0 : e / tn;
+          const int l = tlo + (BC == 1 ? e : e - ce * tn);
           if ((uint32_t)(v >> 32) == tag && a.spin >= 0) {
-            const int ce = BC == 1 ? 0 : e / r;
-            Tp[ce * t_ld(r) + e - ce * r] = __uint_as_float((uint32_t)v);
+            Tp[ce * t_ld(r) + l] = __uint_as_float((uint32_t)v);
           } else {
-            const int l = e % r;
             atomicOr(&miss[l >> 5], 1u << (l & 31));
           }
         }
@@ -1088,7 +1131,9 @@ __global__ __launch_bounds__(MTR > 0 ? kMergedThreads : 256) void k_decode(Group
       while (bits) {
         const int l = wi * 32 + __ffs(bits) - 1;
         bits &= bits - 1;
-        t_row<DT, BC, NT>(Vt + (int64_t)l * n, a.x_pad ? X : xsrc, n, bc, a.vec, red);
+        int tc0, tlen;
+        t_cols(a, l, tc0, tlen);
+        t_row<DT, BC, NT>(Vt + (int64_t)l * a.v_ld, (a.x_pad ? X : xsrc) + tc0, tlen, n, bc, a.vec, red);
         if (t < bc) Tp[t * t_ld(r) + l] = red_sum<BC, NW>(red, t);
         __syncthreads();
       }

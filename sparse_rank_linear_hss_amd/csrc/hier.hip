@@ -244,4 +244,133 @@ hss_status launch_hier_pack(int dt, int m, int n, const int32_t* r, const void* 
   return hipGetLastError() == hipSuccess ? HSS_OK : HSS_ERR_HIP;
 }
 
+// ---------------------------------------------------------------------------
+// Compact form of the block term (HSS_HIER2), in the blocks' own order: U_c
+// row i holds the factors of the two blocks of i's row half side by side
+// (ru = r00 + r01 = r10 + r11 values), V^T_c row o_b + l holds row l of
+// block b's V^T over its column half only, rows n - n/2 long.  Nothing is
+// zero but the unread last value of a first-half row when n is odd.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void k_pack_compact_u(HierBlocks hb, int m, T* Uc) {
+  const int ru = hb.r[0] + hb.r[1], m1 = m / 2;
+  const int64_t total = (int64_t)m * ru;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+    const int i = (int)(e / ru), k = (int)(e - (int64_t)i * ru);
+    const int half = i < m1 ? 0 : 1, ii = i - (half ? m1 : 0);
+    const int b0 = 2 * half, b = k < hb.r[b0] ? b0 : b0 + 1, kk = b == b0 ? k : k - hb.r[b0];
+    Uc[e] = static_cast<const T*>(hb.U[b])[(int64_t)ii * hb.r[b] + kk];
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_pack_compact_vt(HierBlocks hb, int n, T* Vtc) {
+  const int R = hb.off[4], n1 = n / 2, ld = hier_vt_ld(n);
+  const int64_t total = (int64_t)R * ld;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+    const int c = (int)(e / ld), j = (int)(e - (int64_t)c * ld);
+    int b = 0;
+    while (c >= hb.off[b + 1]) ++b;
+    const int w = (b & 1) ? n - n1 : n1;  // columns of block b's half
+    Vtc[e] = j < w ? static_cast<const T*>(hb.Vt[b])[(int64_t)(c - hb.off[b]) * w + j] : T(0);
+  }
+}
+
+hss_status launch_hier_pack_compact(int dt, int m, int n, const int32_t* r, const void* const* U,
+                                    const void* const* Vt, void* Uc, void* Vtc, hipStream_t s) {
+  HierBlocks hb = {};
+  hb.off[0] = 0;
+  for (int b = 0; b < 4; ++b) {
+    hb.U[b] = U[b];
+    hb.Vt[b] = Vt[b];
+    hb.r[b] = r[b];
+    hb.off[b + 1] = hb.off[b] + r[b];
+  }
+  const int R = hb.off[4], ru = r[0] + r[1];
+  if (R == 0) return HSS_OK;
+  const unsigned gu = (unsigned)std::min<int64_t>(((int64_t)m * ru + 255) / 256, 8192);
+  const unsigned gv = (unsigned)std::min<int64_t>(((int64_t)R * hier_vt_ld(n) + 255) / 256, 8192);
+  if (dt == HSS_F32) {
+    if (ru > 0) hipLaunchKernelGGL(k_pack_compact_u<uint32_t>, dim3(gu), dim3(256), 0, s, hb, m, static_cast<uint32_t*>(Uc));
+    hipLaunchKernelGGL(k_pack_compact_vt<uint32_t>, dim3(gv), dim3(256), 0, s, hb, n, static_cast<uint32_t*>(Vtc));
+  } else {
+    if (ru > 0) hipLaunchKernelGGL(k_pack_compact_u<uint16_t>, dim3(gu), dim3(256), 0, s, hb, m, static_cast<uint16_t*>(Uc));
+    hipLaunchKernelGGL(k_pack_compact_vt<uint16_t>, dim3(gv), dim3(256), 0, s, hb, n, static_cast<uint16_t*>(Vtc));
+  }
+  return hipGetLastError() == hipSuccess ? HSS_OK : HSS_ERR_HIP;
+}
+
+// The compact factors of an HSS_HIER2 matrix expanded into flat factors of
+// the same basis (U_f m x R, V^T_f R x n, zeros outside each block), for the
+// batched routes: U_f[i][c] = U_c[i][c - h ru] when column c belongs to the
+// blocks of i's row half h (c in [h ru, (h + 1) ru)), V^T_f[l][j] =
+// V^T_c[l][j - bj n/2] when column j lies in the column half bj of row l's
+// block.
+template <typename T>
+__global__ __launch_bounds__(256) void k_expand_u(const T* __restrict__ Uc, int m, int ru, T* Uf) {
+  const int R = 2 * ru, m1 = m / 2;
+  const int64_t total = (int64_t)m * R;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+    const int i = (int)(e / R), c = (int)(e - (int64_t)i * R);
+    const int h = i < m1 ? 0 : 1;
+    Uf[e] = (c >= h * ru && c < (h + 1) * ru) ? Uc[(int64_t)i * ru + (c - h * ru)] : T(0);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_expand_vt(const T* __restrict__ Vtc, int n, int R, int l1, int l2, int l3,
+                                                   T* Vtf) {
+  const int n1 = n / 2, ld = hier_vt_ld(n);
+  const int64_t total = (int64_t)R * n;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+    const int l = (int)(e / n), j = (int)(e - (int64_t)l * n);
+    const int bj = ((l >= l1 && l < l2) || l >= l3) ? 1 : 0;  // column half of row l's block
+    const int jj = j - (bj ? n1 : 0);
+    Vtf[e] = ((j >= n1) == (bj == 1)) ? Vtc[(int64_t)l * ld + jj] : T(0);
+  }
+}
+
+hss_status launch_hier_expand(const hss_matrix* A, void* Uf, void* Vtf, hipStream_t s) {
+  const int m = A->m, n = A->n, R = A->r, ru = A->hier_r[0] + A->hier_r[1];
+  if (R == 0) return HSS_OK;
+  const int l1 = A->hier_r[0], l2 = l1 + A->hier_r[1], l3 = l2 + A->hier_r[2];
+  const unsigned gu = (unsigned)std::min<int64_t>(((int64_t)m * R + 255) / 256, 8192);
+  const unsigned gv = (unsigned)std::min<int64_t>(((int64_t)R * n + 255) / 256, 8192);
+  if (A->dtype == HSS_F32) {
+    hipLaunchKernelGGL(k_expand_u<uint32_t>, dim3(gu), dim3(256), 0, s, static_cast<const uint32_t*>(A->U), m, ru,
+                       static_cast<uint32_t*>(Uf));
+    hipLaunchKernelGGL(k_expand_vt<uint32_t>, dim3(gv), dim3(256), 0, s, static_cast<const uint32_t*>(A->Vt), n, R,
+                       l1, l2, l3, static_cast<uint32_t*>(Vtf));
+  } else {
+    hipLaunchKernelGGL(k_expand_u<uint16_t>, dim3(gu), dim3(256), 0, s, static_cast<const uint16_t*>(A->U), m, ru,
+                       static_cast<uint16_t*>(Uf));
+    hipLaunchKernelGGL(k_expand_vt<uint16_t>, dim3(gv), dim3(256), 0, s, static_cast<const uint16_t*>(A->Vt), n, R,
+                       l1, l2, l3, static_cast<uint16_t*>(Vtf));
+  }
+  return hipGetLastError() == hipSuccess ? HSS_OK : HSS_ERR_HIP;
+}
+
+// S' = P S P^T on the host: row i of S' is row perm[i] of S with every
+// column j renamed pos[j] (pos = perm's inverse) and the row sorted by the
+// new columns; from[q] = S's storage index of S''s entry q.
+hss_status csr_permute_host(int n, const int32_t* row_ptr, const int32_t* col_idx, const int32_t* perm,
+                            const int32_t* pos, int32_t* row_ptr_p, int32_t* col_idx_p, int32_t* from) {
+  std::vector<std::pair<int32_t, int32_t>> row;
+  int64_t q = 0;
+  row_ptr_p[0] = 0;
+  for (int i = 0; i < n; ++i) {
+    const int src = perm[i];
+    row.clear();
+    for (int64_t p = row_ptr[src]; p < row_ptr[src + 1]; ++p) row.emplace_back(pos[col_idx[p]], (int32_t)p);
+    std::sort(row.begin(), row.end());
+    for (const auto& e : row) {
+      col_idx_p[q] = e.first;
+      from[q] = e.second;
+      ++q;
+    }
+    row_ptr_p[i + 1] = (int32_t)q;
+  }
+  return HSS_OK;
+}
+
 }  // namespace hss

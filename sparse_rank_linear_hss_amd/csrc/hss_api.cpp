@@ -6,6 +6,7 @@
 #include <atomic>
 #include <cstdlib>
 #include <cstring>
+#include <vector>
 
 #include "hss_internal.h"
 
@@ -165,7 +166,7 @@ hss_status hss_get_error(const void* ws, hipStream_t stream) {
 }
 
 static hss_status check_matrix(const hss_matrix* A, int32_t b) {
-  if (!A || !valid_fmt(A->fmt) || !valid_dtype(A->dtype) || (A->flags & ~(HSS_COL16 | HSS_DQ4)) != 0)
+  if (!A || !valid_fmt(A->fmt) || !valid_dtype(A->dtype) || (A->flags & ~(HSS_COL16 | HSS_DQ4 | HSS_HIER2)) != 0)
     return HSS_ERR_INVALID_ARG;
   if ((A->flags & HSS_COL16) && (A->fmt != HSS_FMT_CSR || A->n > 65536)) return HSS_ERR_INVALID_ARG;
   const int64_t m = A->m, n = A->n, r = A->r;
@@ -173,6 +174,16 @@ static hss_status check_matrix(const hss_matrix* A, int32_t b) {
   if (A->flags & HSS_DQ4) {
     if (A->fmt != HSS_FMT_CSR || n % 2 != 0 || !A->dq_codes || !A->dq_levels) return HSS_ERR_INVALID_ARG;
     if (r > 0) return HSS_ERR_UNSUPPORTED;
+  }
+  if (A->flags & HSS_HIER2) {
+    if (A->fmt != HSS_FMT_CSR || (A->flags & HSS_DQ4) || m < 2 || n < 2) return HSS_ERR_INVALID_ARG;
+    int64_t sum = 0;
+    for (int k = 0; k < 4; ++k) {
+      if (A->hier_r[k] < 0) return HSS_ERR_INVALID_ARG;
+      sum += A->hier_r[k];
+    }
+    if (sum != r || (int64_t)A->hier_r[0] + A->hier_r[1] != (int64_t)A->hier_r[2] + A->hier_r[3])
+      return HSS_ERR_INVALID_ARG;
   }
   if (m * n >= kLimit || (int64_t)b * m >= kLimit || (int64_t)b * n >= kLimit ||
       r * (m + n) >= kLimit)
@@ -311,13 +322,53 @@ hss_status hss_hier_pack(int32_t dt, int32_t m, int32_t n, const int32_t* r, con
   return hss::launch_hier_pack(dt, m, n, r, U, Vt, perm, U_cat, Vt_cat, stream);
 }
 
+hss_status hss_hier_pack_compact(int32_t dt, int32_t m, int32_t n, const int32_t* r, const void* const* U,
+                                 const void* const* Vt, void* U_c, void* Vt_c, hipStream_t stream) {
+  if (!valid_dtype(dt) || m < 2 || n < 2 || !r || !U || !Vt) return HSS_ERR_INVALID_ARG;
+  const int32_t rows[2] = {m / 2, m - m / 2}, cols[2] = {n / 2, n - n / 2};
+  int64_t R = 0;
+  for (int b = 0; b < 4; ++b) {
+    const int32_t lim = std::min(rows[b >> 1], cols[b & 1]);
+    if (r[b] < 0 || r[b] > lim) return HSS_ERR_INVALID_ARG;
+    if (r[b] > 0 && (!U[b] || !Vt[b])) return HSS_ERR_INVALID_ARG;
+    R += r[b];
+  }
+  const int64_t ru = (int64_t)r[0] + r[1];
+  if (ru != (int64_t)r[2] + r[3]) return HSS_ERR_INVALID_ARG;
+  if (R > 0 && (!U_c || !Vt_c)) return HSS_ERR_INVALID_ARG;
+  if ((int64_t)m * ru >= kLimit || R * (int64_t)n >= kLimit) return HSS_ERR_INVALID_ARG;
+  if (R == 0) return HSS_OK;
+  const size_t es = dsize(dt);
+  if (overlap(U_c, (size_t)m * ru * es, Vt_c, (size_t)R * cols[1] * es)) return HSS_ERR_INVALID_ARG;
+  return hss::launch_hier_pack_compact(dt, m, n, r, U, Vt, U_c, Vt_c, stream);
+}
+
+hss_status hss_csr_permute(int32_t n, const int32_t* row_ptr, const int32_t* col_idx, const int32_t* perm,
+                           int32_t* row_ptr_p, int32_t* col_idx_p, int32_t* from) {
+  if (n < 1 || !row_ptr || !perm || !row_ptr_p || row_ptr[0] != 0) return HSS_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < n; ++i)
+    if (row_ptr[i + 1] < row_ptr[i]) return HSS_ERR_INVALID_ARG;
+  const int64_t nnz = row_ptr[n];
+  if (nnz > 0 && (!col_idx || !col_idx_p || !from)) return HSS_ERR_INVALID_ARG;
+  std::vector<int32_t> pos(n, -1);  // pos[perm[i]] = i
+  for (int32_t i = 0; i < n; ++i) {
+    if (perm[i] < 0 || perm[i] >= n || pos[perm[i]] >= 0) return HSS_ERR_INVALID_ARG;
+    pos[perm[i]] = i;
+  }
+  for (int32_t i = 0; i < n; ++i)
+    for (int64_t p = row_ptr[i]; p < row_ptr[i + 1]; ++p)
+      if (col_idx[p] < 0 || col_idx[p] >= n || (p > row_ptr[i] && col_idx[p] == col_idx[p - 1]))
+        return HSS_ERR_INVALID_ARG;
+  return hss::csr_permute_host(n, row_ptr, col_idx, perm, pos.data(), row_ptr_p, col_idx_p, from);
+}
+
 // ---------------------------------------------------------------------------
 // Backward pass
 // ---------------------------------------------------------------------------
 static hss_status check_grad(const hss_matrix* A, int32_t b) {
   hss_status st = check_matrix(A, b);
   if (st != HSS_OK) return st;
-  if (A->dtype != HSS_BF16 || (A->flags & HSS_DQ4)) return HSS_ERR_UNSUPPORTED;
+  if (A->dtype != HSS_BF16 || (A->flags & (HSS_DQ4 | HSS_HIER2))) return HSS_ERR_UNSUPPORTED;
   const int64_t ldt = ((int64_t)b + 7) / 8 * 8;
   if ((int64_t)A->n * ldt * 2 >= kLimit || (int64_t)A->m * ldt * 2 >= kLimit) return HSS_ERR_UNSUPPORTED;
   return HSS_OK;

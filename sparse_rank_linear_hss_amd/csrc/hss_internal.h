@@ -10,6 +10,9 @@
 
 namespace hss {
 
+// Row length of the compact V^T of an HSS_HIER2 matrix: the wider column half.
+__host__ __device__ inline int hier_vt_ld(int n) { return n - n / 2; }
+
 // Native 16-byte vector (usable with the nontemporal load/store builtins).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -131,4 +134,9 @@ hss_status launch_concentration(int dt, int m, int n, const void* W, const int32
                                 hipStream_t s);
 hss_status launch_hier_pack(int dt, int m, int n, const int32_t* r, const void* const* U, const void* const* Vt,
                             const int32_t* perm, void* Ucat, void* Vtcat, hipStream_t s);
+hss_status launch_hier_pack_compact(int dt, int m, int n, const int32_t* r, const void* const* U,
+                                    const void* const* Vt, void* Uc, void* Vtc, hipStream_t s);
+hss_status launch_hier_expand(const hss_matrix* A, void* Uf, void* Vtf, hipStream_t s);
+hss_status csr_permute_host(int n, const int32_t* row_ptr, const int32_t* col_idx, const int32_t* perm,
+                            const int32_t* pos, int32_t* row_ptr_p, int32_t* col_idx_p, int32_t* from);
 }  // namespace hss

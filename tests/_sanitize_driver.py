@@ -21,13 +21,15 @@ c_i32, c_i64, c_sz, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctyp
 class M(ctypes.Structure):  # struct hss_matrix
     _fields_ = [("fmt", c_i32), ("dtype", c_i32), ("m", c_i32), ("n", c_i32), ("r", c_i32), ("flags", c_i32),
                 ("nnz", c_i64), ("row_ptr", c_vp), ("col_idx", c_vp), ("values", c_vp), ("nm_values", c_vp),
-                ("nm_meta", c_vp), ("U", c_vp), ("Vt", c_vp), ("dq_codes", c_vp), ("dq_levels", c_vp)]
+                ("nm_meta", c_vp), ("U", c_vp), ("Vt", c_vp), ("dq_codes", c_vp), ("dq_levels", c_vp),
+                ("hier_r", c_i32 * 4)]
 
 
 P = ctypes.POINTER
 for name, res, args in [
         ("hss_rcm_order", ctypes.c_int, [c_i32, c_vp, c_vp, c_vp]),
         ("hss_csr_transpose", ctypes.c_int, [c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp]),
+        ("hss_csr_permute", ctypes.c_int, [c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
         ("hss_apply", ctypes.c_int, [P(M), c_i32, c_vp, c_vp, c_vp, c_sz, c_vp]),
         ("hss_apply_noalloc", ctypes.c_int, [P(M), c_i32, c_vp, c_vp, c_vp]),
         ("hss_apply_workspace_size", ctypes.c_int, [P(M), c_i32, P(c_sz)]),
@@ -64,7 +66,7 @@ def expect(code, want, what):
 
 
 # counts, strings, switches
-assert lib.hss_version() == 105
+assert lib.hss_version() == 106
 for code in range(-1, 8):
     assert lib.hss_status_string(code).startswith(b"HSS")
 assert lib.hss_topk_count(1024, 1024, 5, 100) == 52428
@@ -86,6 +88,12 @@ for fmt in (0, 1):
             expect(lib.hss_apply_group_workspace_size(arr, 2, b, ctypes.byref(sz)), 0, "group_workspace_size")
             expect(lib.hss_grad_workspace_size(ctypes.byref(s), b, ctypes.byref(sz)), 0, "grad_workspace_size")
         expect(lib.hss_apply_workspace_size(ctypes.byref(mat(m=m, n=n)), 2049, ctypes.byref(sz)), INV, "b > max")
+# the compact 2 x 2 block form: flat factors for the batched routes counted in
+for m, n, hr in [(2, 2, (1, 0, 0, 1)), (130, 131, (8, 3, 3, 8)), (4096, 4096, (96, 32, 32, 96))]:
+    for b in (1, 2, 3, 64, 129, 2048):
+        s = mat(m=m, n=n, r=sum(hr), nnz=min(10, m * n), flags=4, hier_r=(c_i32 * 4)(*hr))
+        expect(lib.hss_apply_workspace_size(ctypes.byref(s), b, ctypes.byref(sz)), 0, "hier workspace_size")
+        assert b == 1 or sz.value >= sum(hr) * (m + n) * 2, (m, n, b, sz.value)
 
 # argument checks that fail before any device work
 expect(lib.hss_apply(None, 1, c_vp(FAKE), c_vp(2 * FAKE), c_vp(3 * FAKE), c_sz(1 << 20), None), INV, "apply null")
@@ -134,6 +142,22 @@ for n, density in [(1, 0.0), (6, 0.0), (40, 0.1), (257, 0.02), (1000, 0.004), (6
                                  cit.ctypes.data, pt.ctypes.data), 0, "csr_transpose")
     ert, ect, ept = O.csr_transpose(m2, n, rp, ci)
     assert np.array_equal(rpt, ert) and np.array_equal(cit[:nnz], ect) and np.array_equal(pt[:nnz], ept)
+    # P S P^T of the duplicate-free pattern, for the RCM order and a random one
+    keep = np.ones(len(ci), dtype=bool)
+    rr = np.repeat(np.arange(n), np.diff(rp))
+    if len(ci) > 1:
+        keep[1:] = ~((rr[1:] == rr[:-1]) & (ci[1:] == ci[:-1]))
+    ci_u = ci[keep].astype(np.int32)
+    rp_u = np.concatenate([[0], np.cumsum(np.bincount(rr[keep], minlength=n))]).astype(np.int32) if n else rp
+    nnz_u = int(rp_u[-1])
+    for pm in (perm, rng.permutation(n).astype(np.int32)):
+        prp = np.zeros(n + 1, dtype=np.int32)
+        pci = np.zeros(max(nnz_u, 1), dtype=np.int32)
+        src = np.zeros(max(nnz_u, 1), dtype=np.int32)
+        expect(lib.hss_csr_permute(n, rp_u.ctypes.data, ci_u.ctypes.data if nnz_u else None, pm.ctypes.data,
+                                   prp.ctypes.data, pci.ctypes.data, src.ctypes.data), 0, "csr_permute")
+        orp, oci, osrc = O.csr_permute(n, rp_u, ci_u, pm)
+        assert np.array_equal(prp, orp) and np.array_equal(pci[:nnz_u], oci) and np.array_equal(src[:nnz_u], osrc)
 bad_rp = np.array([0, 2, 1], dtype=np.int32)
 bad_ci = np.array([0, 5], dtype=np.int32)
 perm = np.zeros(2, dtype=np.int32)

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(hl):
 
 
 def test_version_and_strings(hl):
-    assert hl.hss_version() == 105
+    assert hl.hss_version() == 106
     for code in range(6):
         assert hl.status_string(code).startswith("HSS_")
 
@@ -115,7 +115,24 @@ def test_apply_rejects_bad_arguments(hl):
     assert lib.hss_apply(None, 1, FAKE, FAKE * 2, FAKE * 3, 1 << 20, None) == INV
     assert _apply(hl, _matrix(hl, fmt=5)) == INV
     assert _apply(hl, _matrix(hl, dtype=3)) == INV
-    assert _apply(hl, _matrix(hl, flags=4)) == INV                  # unknown flag
+    assert _apply(hl, _matrix(hl, flags=8)) == INV                  # unknown flag
+    # compact 2 x 2 block term (HSS_HIER2): CSR only, ranks >= 0 summing to r, equal per row half
+    H4 = (ctypes.c_int32 * 4)
+    assert _apply(hl, _matrix(hl, flags=4, hier_r=H4(1, 1, 1, 1)), wsb=0) == WS  # valid: only the workspace short
+    assert _apply(hl, _matrix(hl, flags=4, hier_r=H4(1, 1, 1, 0))) == INV          # sum != r
+    assert _apply(hl, _matrix(hl, flags=4, hier_r=H4(2, 1, 0, 1))) == INV          # 3 != 1 per row half
+    assert _apply(hl, _matrix(hl, flags=4, hier_r=H4(3, -1, 1, 1))) == INV         # negative rank
+    assert _apply(hl, _matrix(hl, flags=4, hier_r=H4(1, 1, 1, 1), fmt=1, nm_values=FAKE, nm_meta=FAKE)) == INV
+    assert _apply(hl, _matrix(hl, flags=6, hier_r=H4(0, 0, 0, 0), r=0, U=None, Vt=None, dq_codes=FAKE,
+                              dq_levels=FAKE)) == INV                   # not with the dense part
+    assert _apply(hl, _matrix(hl, flags=4, hier_r=H4(1, 1, 1, 1), m=1)) == INV     # both halves need rows
+    hsz = ctypes.c_size_t(0)
+    for b in (1, 2, 8, 64, 300):
+        assert lib.hss_apply_workspace_size(ctypes.byref(_matrix(hl, flags=4, hier_r=H4(1, 1, 1, 1))), b,
+                                            ctypes.byref(hsz)) == 0 and hsz.value > 0
+    g_ok = ctypes.c_size_t(0)
+    assert lib.hss_grad_workspace_size(ctypes.byref(_matrix(hl, flags=4, hier_r=H4(1, 1, 1, 1))), 4,
+                                       ctypes.byref(g_ok)) == hl._lib.HSS_ERR_UNSUPPORTED
     # dense-and-sparse (HSS_DQ4): arrays required, CSR only, n even, no low-rank term
     assert _apply(hl, _matrix(hl, flags=2, r=0, U=None, Vt=None)) == INV
     assert _apply(hl, _matrix(hl, flags=2, r=0, U=None, Vt=None, dq_codes=FAKE)) == INV

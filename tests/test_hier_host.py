@@ -101,3 +101,35 @@ def test_csr_transpose_rejects_bad_arguments(H):
     assert call([1, 1, 2], [0, 1], 2, 2) == INV
     assert call([0, 2, 1], [0, 1], 2, 2) == INV
     assert call([0, 1, 2], [0, 2], 2, 2) == INV                  # column outside [0, n)
+
+
+@pytest.mark.parametrize("n,density,seed", [(1, 1.0, 0), (7, 0.4, 1), (90, 0.05, 2), (300, 0.03, 3), (33, 0.0, 4)])
+def test_csr_permute_matches_oracle(H, n, density, seed):
+    """The library's host P S P^T of a CSR pattern is the oracle's: same
+    pattern, same source indices (bit-exact), for a random and the RCM
+    permutation."""
+    rng = np.random.default_rng(seed)
+    rp, ci = _csr(rng.random((n, n)) < density)
+    for perm in (rng.permutation(n).astype(np.int32), H.hss_rcm_order(rp, ci, n)):
+        prp, pci, src = H.hss_csr_permute(rp, ci, perm, n)
+        orp, oci, osrc = O.csr_permute(n, rp, ci, perm)
+        assert np.array_equal(prp, orp) and np.array_equal(pci, oci) and np.array_equal(src, osrc)
+
+
+def test_csr_permute_rejects_bad_arguments(H):
+    lib, INV = H._lib.lib, H._lib.HSS_ERR_INVALID_ARG
+    out = np.zeros(8, dtype=np.int32)
+
+    def call(rp, ci, perm, n):
+        rp, ci, perm = (np.asarray(a, dtype=np.int32) for a in (rp, ci, perm))
+        return lib.hss_csr_permute(n, rp.ctypes.data, ci.ctypes.data, perm.ctypes.data, out.ctypes.data,
+                                   out.ctypes.data, out.ctypes.data)
+    assert call([0, 1, 2], [1, 0], [1, 0], 2) == 0
+    assert call([0, 1, 2], [1, 0], [1, 0], 0) == INV             # n < 1
+    assert call([1, 1, 2], [1, 0], [1, 0], 2) == INV             # row_ptr[0] != 0
+    assert call([0, 2, 1], [1, 0], [1, 0], 2) == INV             # decreasing row_ptr
+    assert call([0, 1, 2], [2, 0], [1, 0], 2) == INV             # column outside [0, n)
+    assert call([0, 1, 2], [1, 0], [1, 1], 2) == INV             # not a permutation
+    assert call([0, 1, 2], [1, 0], [0, 2], 2) == INV
+    assert call([0, 2, 2], [1, 1], [0, 1], 2) == INV             # a repeated column
+    assert lib.hss_csr_permute(2, None, None, None, None, None, None) == INV

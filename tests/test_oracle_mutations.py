@@ -114,6 +114,42 @@ def _csr_transpose_row_major_order(m, n, rp, ci):
     return rpt, cit, np.arange(len(perm))                          # storage order kept
 
 
+def _csr_permute_cols_by_perm(n, row_ptr, col_idx, perm):
+    perm = np.asarray(perm, dtype=np.int64)
+    rp, ci = np.asarray(row_ptr, dtype=np.int64), np.asarray(col_idx, dtype=np.int64)
+    out_rp, out_ci, src = [0], [], []
+    for i in range(n):
+        row = sorted((int(perm[ci[p]]), p) for p in range(rp[perm[i]], rp[perm[i] + 1]))  # perm, not its inverse
+        out_ci.extend(c for c, _ in row)
+        src.extend(p for _, p in row)
+        out_rp.append(len(out_ci))
+    return np.array(out_rp, dtype=np.int32), np.array(out_ci, dtype=np.int32), np.array(src, dtype=np.int64)
+
+
+def _csr_permute_rows_by_inverse(n, row_ptr, col_idx, perm):
+    inv = np.argsort(np.asarray(perm))
+    rp, ci = np.asarray(row_ptr, dtype=np.int64), np.asarray(col_idx, dtype=np.int64)
+    out_rp, out_ci, src = [0], [], []
+    for i in range(n):
+        row = sorted((int(inv[ci[p]]), p) for p in range(rp[inv[i]], rp[inv[i] + 1]))  # row inv[i], not perm[i]
+        out_ci.extend(c for c, _ in row)
+        src.extend(p for _, p in row)
+        out_rp.append(len(out_ci))
+    return np.array(out_rp, dtype=np.int32), np.array(out_ci, dtype=np.int32), np.array(src, dtype=np.int64)
+
+
+_orig_csr_permute = H.csr_permute
+
+
+def _csr_permute_unsorted(n, row_ptr, col_idx, perm):
+    rp, ci, src = _orig_csr_permute(n, row_ptr, col_idx, perm)
+    for i in range(n):                                     # each row in S's storage order instead
+        seg = slice(rp[i], rp[i + 1])
+        o = np.argsort(src[seg], kind="stable")
+        ci[seg], src[seg] = ci[seg][o], src[seg][o]
+    return rp, ci, src
+
+
 def _apply_no_lowrank(S, U, V, X):
     return X @ S.T
 
@@ -355,6 +391,12 @@ CASES = [
     ("backward", _backward_dS_transposed_index, [P.test_backward_one_hot_upstream_and_full_support_brute_force]),
     ("csr_transpose", _csr_transpose_row_major_order, [P.test_csr_transpose_is_the_transposed_matrix]),
     ("nm24_pattern", _nm24_pattern_slots_swapped, [P.test_nm24_pattern_is_the_mask_in_storage_order]),
+    ("csr_permute", _csr_permute_cols_by_perm,
+     [P.test_csr_permute_hand_example, lambda: P.test_csr_permute_is_the_permuted_matrix(17, 0.2, 2)]),
+    ("csr_permute", _csr_permute_rows_by_inverse,
+     [P.test_csr_permute_hand_example, lambda: P.test_csr_permute_is_the_permuted_matrix(17, 0.2, 2)]),
+    ("csr_permute", _csr_permute_unsorted,
+     [P.test_csr_permute_hand_example, lambda: P.test_csr_permute_is_the_permuted_matrix(17, 0.2, 2)]),
     ("apply_csr", _apply_csr_no_lowrank, [lambda: P.test_apply_csr_equals_the_hand_loop(11, 3)]),
     ("apply_csr", _apply_csr_rows_shifted, [lambda: P.test_apply_csr_equals_the_hand_loop(12, 0)]),
     ("bits_equal", _bits_equal_by_value, [P.test_bits_equal_compares_bit_patterns]),

@@ -742,6 +742,42 @@ def test_csr_transpose_is_the_transposed_matrix():
     assert sorted(perm.tolist()) == list(range(len(ci)))
 
 
+def test_csr_permute_hand_example():
+    """3 x 3 pattern, perm = [2, 0, 1] (so pos = [1, 2, 0]), worked by hand
+    from S'[i][j] = S[perm[i]][perm[j]]: entries p0 (0,0), p1 (0,2), p2 (1,1),
+    p3 (2,0), p4 (2,1) of S become row 0 = S's row 2 at columns pos[0] = 1,
+    pos[1] = 2; row 1 = S's row 0 at pos[2] = 0, pos[0] = 1; row 2 = S's row
+    1 at pos[1] = 2."""
+    rp, ci, src = O.csr_permute(3, [0, 2, 3, 5], [0, 2, 1, 0, 1], [2, 0, 1])
+    assert rp.tolist() == [0, 2, 4, 5]
+    assert ci.tolist() == [1, 2, 0, 1, 2]
+    assert src.tolist() == [3, 4, 1, 0, 2]
+
+
+@pytest.mark.parametrize("n,density,seed", [(1, 1.0, 0), (6, 0.5, 1), (17, 0.2, 2), (40, 0.05, 3), (9, 0.0, 4)])
+def test_csr_permute_is_the_permuted_matrix(n, density, seed):
+    """Brute force: the permuted pattern with the values moved by src is
+    W[perm][:, perm] of the dense matrix; columns ascend in every row; src is
+    a permutation; permuting back by the inverse returns S exactly."""
+    rng = np.random.default_rng(seed)
+    D = np.where(rng.random((n, n)) < density, rng.standard_normal((n, n)), 0.0)
+    rp = np.concatenate([[0], np.cumsum((D != 0).sum(axis=1))]).astype(np.int32)
+    ci = np.nonzero(D)[1].astype(np.int32)
+    vals = D[np.nonzero(D)]
+    perm = rng.permutation(n)
+    prp, pci, src = O.csr_permute(n, rp, ci, perm)
+    Dp = np.zeros((n, n))
+    for i in range(n):
+        seg = slice(prp[i], prp[i + 1])
+        assert np.all(np.diff(pci[seg]) > 0)
+        Dp[i, pci[seg]] = vals[src[seg]]
+    assert np.array_equal(Dp, D[perm][:, perm])
+    assert sorted(src.tolist()) == list(range(len(ci)))
+    inv = np.argsort(perm)
+    brp, bci, bsrc = O.csr_permute(n, prp, pci, inv)
+    assert np.array_equal(brp, rp) and np.array_equal(bci, ci) and np.array_equal(src[bsrc], np.arange(len(ci)))
+
+
 def test_backward_sampled_equals_full():
     m, n = 10, 8
     rp, ci, S, U, V, X, G = _bw_case(m, n, r=3, b=6, seed=8)
