@@ -283,7 +283,7 @@ hss_status hss_apply_workspace_size(const hss_matrix* A, int32_t b, size_t* byte
  *     different workspaces -- overlapping calls on one workspace can make
  *     both return wrong values with no error.  The epoch wraps after 2^32 - 1
  *     calls and skips the tag that a zero-filled word carries.
- * Execution: bf16 2:4 with 2 <= b <= 64 (n % 128 == 0; nm_values, nm_meta
+ * Execution: bf16 2:4 with 3 <= b <= 64 (n % 128 == 0; nm_values, nm_meta
  * and X 16-byte aligned) runs on the sparse matrix cores: S's stored values
  * and 2-bit indices are the operands of v_smfmac as they are, with fp32
  * accumulation, and T = X V is rounded to bf16 once before U T is added.  bf16 2:4 beyond 64

@@ -73,10 +73,11 @@ enum Route { R_DECODE = 0, R_SPMM = 1, R_MFMA = 2, R_NM = 3 };
 
 // Default batch range of the 2:4 route on the sparse matrix cores.
 // Measured on the 11008 x 4096 rank-64 layer (decode / densify vs sparse
-// matrix cores, us): b = 2 decode 20.2 vs 18.3; b = 3 decode 25.3 vs 18.5;
-// b = 8 decode 46.0 vs 19.1; b = 16 densify 46.0 vs 20.7; b = 32 densify
-// 48.5 vs 25.8; b = 64 densify 60.1 vs 41.6.
-static constexpr int kNmMinColsDefault = 2;
+// matrix cores, us, 16-call graphs): b = 2 decode 20.0 vs 21.6 (three runs:
+// the decode passes won by 1.5-2.0); b = 3 decode 25.3 vs 18.5; b = 8 decode
+// 49.5 vs 22.5; b = 16 densify 47.2 vs 23.9; b = 32 densify 48.5 vs 25.8;
+// b = 64 densify 61.4 vs 44.5.
+static constexpr int kNmMinColsDefault = 3;
 
 // Default batch range of the gather SpMM for bf16 CSR: below it the fused
 // decode passes, above it S densified for the matrix cores.  Measured on the

@@ -71,7 +71,8 @@ def test_smfmac_matches_oracle(H, hss_opt, case):
     _check(Y1, S64, U64, V64, O.widen(X, DT))
     assert O.bits_equal(to_host(Y1), to_host(H.hss_apply(A, Xd)))      # deterministic
     hss_opt("batch_route", "auto")
-    assert O.bits_equal(to_host(Y1), to_host(H.hss_apply(A, Xd)))      # the default route for 2..64 columns
+    if b >= 3:
+        assert O.bits_equal(to_host(Y1), to_host(H.hss_apply(A, Xd)))  # the default route for 3..64 columns
 
 
 @pytest.mark.parametrize("b", [2, 16, 64])
@@ -136,9 +137,10 @@ def test_smfmac_group_equals_single_applies(H):
 
 
 @pytest.mark.parametrize("b", [2, 33])
-def test_smfmac_11008x4096_sampled(H, b):
-    """The 11008 x 4096 2:4 rank-64 layer (rows sampled; b = 8 and 64 run in
-    the apply tests through the same default route)."""
+def test_smfmac_11008x4096_sampled(H, hss_opt, b):
+    """The 11008 x 4096 2:4 rank-64 layer on this route (rows sampled; every
+    row at b = 8 and 64, through the default route, in the full-size tests)."""
+    hss_opt("batch_route", "smfmac")
     c = syn.WORKLOADS["nm24_11008x4096"]
     m, n = c.shapes[0]
     r = c.rank[0]
