@@ -71,9 +71,18 @@ def _log(msg):
 
 
 def _decode_source_hash():
+    """sha256 of the decode kernel's code: the csrc/decode* sources and
+    csrc/hss_internal.h in name order, with // comments and blank space
+    removed (an edit to a comment does not make measured counters stale)."""
+    import re
     csrc = os.path.join(ROOT, "sparse_rank_linear_hss_amd", "csrc")
     names = sorted(f for f in os.listdir(csrc) if f.startswith("decode")) + ["hss_internal.h"]
-    return hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read() for f in names)).hexdigest()
+    code = []
+    for f in names:
+        text = open(os.path.join(csrc, f), encoding="utf-8").read()
+        text = re.sub(r"//[^\n]*", "", text)
+        code.append(re.sub(r"\s+", " ", text).strip())
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()
 
 
 def _measured_traffic(kernel_key):

@@ -22,17 +22,20 @@
 // Cross-block hand-off of T (a launch costs ~2.5 us and a same-address device
 // atomic ~10 ns once every block hits it, so no hot counters and no
 // cache-wide acquire fences):
-//   * T row l is produced by "home" block l mod G at the start of the launch
-//     and published as 64-bit words (fp32 value, call tag) with coherent
-//     (agent-scope) stores -- there is no done counter;
+//   * T row l is produced at the start of the launch by producer block l (the
+//     lowest block ids, dispatched first) or, for one CSR column, by a row
+//     block that also produces it (merged producers), and published into 8
+//     replicas as 64-bit words (fp32 value, call tag) with coherent
+//     (agent-scope) stores -- there is no done counter for T;
 //   * every block reads the tagged words with coherent loads after its own
 //     sparse work, polls a stale word a bounded number of times, then computes
 //     any row still missing itself (same arithmetic, so the same bits).  No
 //     wait can hang and a stale value is never used;
 //   * the call tag is epoch+1, the epoch being read by every block at its
-//     start.  Each block then bumps one of 64 spread arrival counters; the
-//     last block to arrive (two-level count) advances the epoch and clears the
-//     counters.  All blocks have read the epoch before it can advance.
+//     start.  Each block then bumps one of 64 spread arrival counters of the
+//     set of the epoch's parity; the last block to arrive (two-level count)
+//     stores the next epoch, and block 0 clears the other set for the next
+//     call.  All blocks have read the epoch before it can advance.
 
 #pragma once
 

@@ -581,21 +581,32 @@ __global__ __launch_bounds__(256, (FM * FN >= 16 ? 1 : 2)) void k_gemm_h(GemmArg
     h_load<FM, FN>(r0, g, ops, nst1, min(s_begin + 1, last), m0, n0);
     h_load<FM, FN>(r1, g, ops, nst1, min(s_begin + 2, last), m0, n0);
     __syncthreads();
-    for (int s = s_begin; s < s_end; s += 2) {
+    // Pairs of stages, then an odd last one: no exit from the middle of the
+    // loop body.  With one, the compiler moved accumulators between AGPRs
+    // and VGPRs on every iteration (the 128 x 128 tile then took 88 VGPRs +
+    // 128 AGPRs, now 82 + 64; the 128 x 256 tile spilled).  The 128 x 256
+    // tile with two register sets, which now fits (128 + 128), measured no
+    // faster: 28.5 against 27.2 us for the K = 512 product of the 8192^2
+    // prefill, 305 against 299 us with the dense S.
+    int s = s_begin;
+    for (; s + 1 < s_end; s += 2) {
       // stage s in hb0, s + 1 in r0, s + 2 in r1
       h_compute<FM, FN>(hb0, wm, wn, acc);
       h_store<FM, FN>(hb1, r0);
       h_load<FM, FN>(r0, g, ops, nst1, min(s + 3, last), m0, n0);
       __syncthreads();
-      if (s + 1 >= s_end) break;  // block-uniform
       h_compute<FM, FN>(hb1, wm, wn, acc);
       h_store<FM, FN>(hb0, r1);
       h_load<FM, FN>(r1, g, ops, nst1, min(s + 4, last), m0, n0);
       __syncthreads();
     }
+    if (s < s_end) {  // stage s, in hb0; the barrier frees hb0 for the output staging
+      h_compute<FM, FN>(hb0, wm, wn, acc);
+      __syncthreads();
+    }
   } else if (!DEEP && s_begin < s_end) {
-    // one register set (the 128 x 256 tile: a second set does not fit
-    // beside its 128 accumulators at two blocks per CU)
+    // one register set (128 x 256 tiles: two measured no faster; 256 x 256:
+    // a second set does not fit beside the 256 accumulators)
     const int last = s_end - 1;
     HRegs<FM, FN> r;
     h_load<FM, FN>(r, g, ops, nst1, s_begin, m0, n0);
