@@ -426,10 +426,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_big(GemmArgs g) {
 // stage is loaded into registers (buffer loads: one 32-bit offset per row,
 // rows past the end read as zeros) while the one before it is computed,
 // written to the other of two LDS buffers, and costs one barrier.  Rows of a
-// stage are 64 bytes; chunk c (8 bf16) of row r sits at slot c ^ ((r >> 1) & 3),
-// so both the stores (4 lanes per row) and the fragment reads (8 consecutive
-// rows per 8 lanes) hit 8 distinct 16-byte bank groups.  Needs K1 and K2
-// multiples of 32 and 16-byte aligned rows.
+// stage are 64 bytes; chunk c (8 bf16) of row r sits at slot c ^ h_swz(r),
+// so that the stores and the fragment reads do not conflict on LDS banks.
+// Needs K1 and K2 multiples of 32 and 16-byte aligned rows.
 // ---------------------------------------------------------------------------
 static constexpr int kHK = 32;
 
@@ -438,6 +437,17 @@ struct HTile {
   static constexpr int TM = 64 * FM, TN = 64 * FN;  // block tile
   static constexpr int STAGE = (TM + TN) * kHK;      // bf16 per LDS buffer: A rows, then B rows
 };
+
+// Slot of 16-byte chunk c of LDS row r is c ^ h_swz(r).  A fragment read
+// (ds_read_b128, lane l: row base + l % 32, one chunk) must put the lanes the
+// LDS serves together on distinct banks: 8 consecutive rows in a 128-byte
+// bank window, or 16 in a 256-byte one.  Rows are 64 bytes, so rows r and
+// r + 2 (r + 4) share a window position and need different slots;
+// ((r >> 1) & 3) ^ ((r >> 3) & 1) gives that for both group sizes (the
+// former (r >> 1) & 3 repeated every 8 rows: 88-94 % of the LDS cycles of the
+// prefill GEMMs were bank conflicts by SQ_LDS_BANK_CONFLICT).  Stores (4 lanes
+// per row, rows in order) fill whole windows and do not conflict.
+__device__ __forceinline__ int h_swz(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
 
 template <int FM, int FN>
 struct HRegs {
@@ -481,12 +491,12 @@ __device__ __forceinline__ void h_store(uint16_t* __restrict__ buf, const HRegs<
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int row = (t >> 2) + 64 * i, c = t & 3;
-    *reinterpret_cast<u32x4*>(buf + row * kHK + 8 * (c ^ ((row >> 1) & 3))) = r.a[i];
+    *reinterpret_cast<u32x4*>(buf + row * kHK + 8 * (c ^ h_swz(row))) = r.a[i];
   }
 #pragma unroll
   for (int i = 0; i < FN; ++i) {
     const int row = (t >> 2) + 64 * i, c = t & 3;
-    *reinterpret_cast<u32x4*>(buf + HTile<FM, FN>::TM * kHK + row * kHK + 8 * (c ^ ((row >> 1) & 3))) = r.b[i];
+    *reinterpret_cast<u32x4*>(buf + HTile<FM, FN>::TM * kHK + row * kHK + 8 * (c ^ h_swz(row))) = r.b[i];
   }
 }
 
@@ -501,12 +511,12 @@ __device__ __forceinline__ void h_compute(const uint16_t* __restrict__ buf, int 
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int row = wm * 32 * FM + 32 * i + (lane & 31);
-      af[i] = *reinterpret_cast<const bf16x8*>(buf + row * kHK + 8 * (c ^ ((row >> 1) & 3)));
+      af[i] = *reinterpret_cast<const bf16x8*>(buf + row * kHK + 8 * (c ^ h_swz(row)));
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int row = wn * 32 * FN + 32 * j + (lane & 31);
-      bfr[j] = *reinterpret_cast<const bf16x8*>(buf + HTile<FM, FN>::TM * kHK + row * kHK + 8 * (c ^ ((row >> 1) & 3)));
+      bfr[j] = *reinterpret_cast<const bf16x8*>(buf + HTile<FM, FN>::TM * kHK + row * kHK + 8 * (c ^ h_swz(row)));
     }
 #pragma unroll
     for (int i = 0; i < FM; ++i)
