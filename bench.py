@@ -582,6 +582,21 @@ def _nm24(H, timer, args, extra):
     L3, W3, _, r3 = _single_layer(H, timer, args, "nm24_11008x4096", list(wl3.batches), 64)
     r3["batch_routes"] = _routes(H, timer, L3, wl3, (2, 8, 16, 64), ("smfmac", "decode", "densify"),
                                  lambda rt, b: (rt == "decode" and b > 8) or (rt == "densify" and b < 16))
+    # the 2:4 split of this weight (offline, once per weight): W read once,
+    # from cold HBM (a flush before each call)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    sms = []
+    for _ in range(5):
+        timer.flush()
+        torch.cuda.synchronize()
+        e0.record()
+        H.hss_split(W3, "2:4", check_finite=False)
+        e1.record()
+        torch.cuda.synchronize()
+        sms.append(e0.elapsed_time(e1))
+    split_ms = sorted(sms)[2]
+    r3["split_ms"] = split_ms
+    r3["split_w_read_gbs"] = W3.numel() * 2 / (split_ms * 1e-3) / 1e9
     extra["nm24_11008x4096"] = r3
     del L3, W3
     torch.cuda.empty_cache()

@@ -416,6 +416,85 @@ __global__ __launch_bounds__(256) void k_split_24(const typename Elem<DT>::bits_
   if (bad) atomicOr(&ws[W_ERR], 1u);
 }
 
+// The same selection with 16-byte loads and stores: one thread per 32
+// columns of one row, the 64 (bf16) or 128 (fp32) bytes of W read as whole
+// vectors, the 16 kept values and the residual written as whole vectors.
+// Needs n % 32 == 0 and W, nm_values and residual 16-byte aligned.
+template <int DT>
+__global__ __launch_bounds__(256) void k_split_24v(const typename Elem<DT>::bits_t* __restrict__ W,
+                                                   int m, int n,
+                                                   typename Elem<DT>::bits_t* __restrict__ nmv,
+                                                   uint32_t* __restrict__ meta,
+                                                   typename Elem<DT>::bits_t* __restrict__ residual,
+                                                   uint32_t* __restrict__ ws) {
+  using E = Elem<DT>;
+  using bits_t = typename E::bits_t;
+  constexpr int PW = 4 / (int)sizeof(bits_t);  // values per 32-bit word
+  constexpr int NW = 32 / PW;                   // words per 32 columns
+  const int words = n >> 5;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)m * words) return;
+  const int row = (int)(gid / words);
+  const int w = (int)(gid - (int64_t)row * words);
+  const int c0 = w * 32;
+  uint32_t win[NW];
+  const u32x4* src = reinterpret_cast<const u32x4*>(W + (int64_t)row * n + c0);
+#pragma unroll
+  for (int v = 0; v < NW / 4; ++v) {
+    const u32x4 q = src[v];
+    win[4 * v] = q.x; win[4 * v + 1] = q.y; win[4 * v + 2] = q.z; win[4 * v + 3] = q.w;
+  }
+  auto val = [&](int k) -> uint32_t {
+    if constexpr (PW == 2) return (win[k >> 1] >> (16 * (k & 1))) & 0xffffu;
+    else return win[k];
+  };
+  uint32_t kept[16], res[32];
+  uint32_t word = 0;
+  bool bad = false;
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    uint32_t b[4], key[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      b[q] = val(4 * g + q);
+      key[q] = b[q] & E::key_mask;
+      bad |= key[q] >= E::key_inf;
+    }
+    uint32_t keepm = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      int rank = 0;
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+        rank += (p != q) && (key[p] > key[q] || (key[p] == key[q] && p < q));
+      keepm |= (uint32_t)(rank < 2) << q;
+    }
+    const int i0 = __ffs(keepm) - 1;
+    const int i1 = 31 - __clz(keepm);
+    word |= (uint32_t)(i0 | (i1 << 2)) << (4 * g);
+    kept[2 * g] = b[i0];
+    kept[2 * g + 1] = b[i1];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) res[4 * g + q] = (keepm >> q & 1u) ? 0u : b[q];
+  }
+  auto pack = [&](const uint32_t* v, int j) -> uint32_t {  // 32-bit word j of a value list
+    if constexpr (PW == 2) return v[2 * j] | (v[2 * j + 1] << 16);
+    else return v[j];
+  };
+  u32x4* dv = reinterpret_cast<u32x4*>(nmv + (int64_t)row * (n >> 1) + (c0 >> 1));
+#pragma unroll
+  for (int v = 0; v < NW / 8; ++v)
+    dv[v] = u32x4{pack(kept, 4 * v), pack(kept, 4 * v + 1), pack(kept, 4 * v + 2), pack(kept, 4 * v + 3)};
+  if (residual) {
+    u32x4* dr = reinterpret_cast<u32x4*>(residual + (int64_t)row * n + c0);
+#pragma unroll
+    for (int v = 0; v < NW / 4; ++v)
+      dr[v] = u32x4{pack(res, 4 * v), pack(res, 4 * v + 1), pack(res, 4 * v + 2), pack(res, 4 * v + 3)};
+  }
+  meta[(int64_t)row * words + w] = word;
+  if (bad) atomicOr(&ws[W_ERR], 1u);
+}
+
 __global__ void k_zero_err(uint32_t* ws) { ws[W_ERR] = 0; }
 
 static inline unsigned grid_for(int64_t work, int per_block, unsigned cap) {
@@ -491,7 +570,18 @@ hss_status launch_split_24(int dt, int m, int n, const void* W, void* nm_values,
   const int64_t threads = (int64_t)m * ((n + 31) / 32);
   const unsigned grid = (unsigned)((threads + 255) / 256);
   hipLaunchKernelGGL(k_zero_err, dim3(1), dim3(1), 0, s, ws);
-  if (dt == HSS_F32)
+  const bool vec = n % 32 == 0 && (uintptr_t)W % 16 == 0 && (uintptr_t)nm_values % 16 == 0 &&
+                   (uintptr_t)residual % 16 == 0;
+  if (vec) {
+    if (dt == HSS_F32)
+      hipLaunchKernelGGL((k_split_24v<HSS_F32>), dim3(grid), dim3(256), 0, s,
+                         static_cast<const uint32_t*>(W), m, n, static_cast<uint32_t*>(nm_values),
+                         nm_meta, static_cast<uint32_t*>(residual), ws);
+    else
+      hipLaunchKernelGGL((k_split_24v<HSS_BF16>), dim3(grid), dim3(256), 0, s,
+                         static_cast<const uint16_t*>(W), m, n, static_cast<uint16_t*>(nm_values),
+                         nm_meta, static_cast<uint16_t*>(residual), ws);
+  } else if (dt == HSS_F32)
     hipLaunchKernelGGL((k_split_24<HSS_F32>), dim3(grid), dim3(256), 0, s,
                        static_cast<const uint32_t*>(W), m, n, static_cast<uint32_t*>(nm_values),
                        nm_meta, static_cast<uint32_t*>(residual), ws);

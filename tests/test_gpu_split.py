@@ -82,10 +82,12 @@ def _assert_24_equal(sp, ref):
 @pytest.mark.parametrize("dtype", [O.F32, O.BF16])
 @pytest.mark.parametrize("shape", [(1, 4), (3, 8), (5, 36), (17, 32), (33, 100), (64, 4096), (7, 4100)])
 def test_split_24_small(H, dtype, shape):
+    """n % 32 == 0 takes the 16-byte load / store path, other widths the
+    element-wise one; with and without the residual."""
     m, n = shape
-    for kind in KINDS:
+    for i, kind in enumerate(KINDS):
         W = syn.random_matrix(m, n, dtype, seed=7 * m + n, kind=kind)
-        sp = H.hss_split(to_dev(W, dtype), "2:4", residual=True)
+        sp = H.hss_split(to_dev(W, dtype), "2:4", residual=i % 2 == 0)
         _assert_24_equal(sp, O.split_24(W, dtype))
 
 
