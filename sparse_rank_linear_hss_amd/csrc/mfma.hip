@@ -704,24 +704,43 @@ __global__ __launch_bounds__(256, (FM * FN >= 16 ? 1 : 2)) void k_gemm_h(GemmArg
   }
 }
 
-// Dense bf16 copy D (m x n, row-major) of a CSR matrix, one wave per row:
-// the row is zeroed with 16-byte stores, a fence waits for those stores, then
-// the lanes scatter the row's entries (no other wave touches the row).
-// Segment 1 of the batched apply then reads S as a dense operand.
+// Dense bf16 copy D (m x n, row-major) of a CSR matrix, one wave per row,
+// kDensSeg columns at a time: the wave zeroes its segment in LDS, its lanes
+// scatter the row's entries that fall in the segment, and the segment goes out
+// in 16-byte stores, so D is written once.  (Zeroing the row in memory and
+// scattering the entries over it wrote every row twice, the second time in
+// 2-byte stores: 51 us for the 8192^2 layer.)  Segment 1 of the batched apply
+// then reads S as a dense operand.
+static constexpr int kDensSeg = 4096;  // columns per segment: 8 KiB of LDS per wave
 template <typename COL>
 __global__ __launch_bounds__(256) void k_csr_densify(const int32_t* __restrict__ row_ptr,
                                                      const COL* __restrict__ col_idx,
                                                      const uint16_t* __restrict__ vals, int m, int n,
                                                      uint16_t* __restrict__ D) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= m) return;
+  __shared__ __align__(16) uint16_t seg[4][kDensSeg];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int row = blockIdx.x * 4 + w;
+  if (row >= m) return;  // no block-wide barrier below
   uint16_t* Dr = D + (int64_t)row * n;  // n % 8 == 0, D 16-byte aligned
+  uint16_t* L = seg[w];
+  const int p0 = row_ptr[row], p1 = row_ptr[row + 1];
   const u32x4 z = {0u, 0u, 0u, 0u};
-  for (int j = 8 * lane; j < n; j += 512) *reinterpret_cast<u32x4*>(Dr + j) = z;
-  __threadfence_block();  // the zeros are written before any entry is
-  const int p1 = row_ptr[row + 1];
-  for (int p = row_ptr[row] + lane; p < p1; p += 64) Dr[col_idx[p]] = vals[p];
+  for (int c0 = 0; c0 < n; c0 += kDensSeg) {
+    const int len = min(kDensSeg, n - c0);  // a multiple of 8
+    for (int j = 8 * lane; j < len; j += 512) *reinterpret_cast<u32x4*>(L + j) = z;
+    // A wave's LDS accesses complete in issue order; the empty asm keeps the
+    // compiler from moving the 2-byte entry stores above the zeros, and the
+    // 16-byte reads below above the entry stores.
+    asm volatile("" ::: "memory");
+    for (int p = p0 + lane; p < p1; p += 64) {
+      const int c = (int)col_idx[p] - c0;
+      if ((unsigned)c < (unsigned)len) L[c] = vals[p];
+    }
+    asm volatile("" ::: "memory");
+    for (int j = 8 * lane; j < len; j += 512)
+      *reinterpret_cast<u32x4*>(Dr + c0 + j) = *reinterpret_cast<const u32x4*>(L + j);
+    asm volatile("" ::: "memory");  // the next segment's zeros after these reads
+  }
 }
 
 // out[n * ldc + m] = sum_z P[z][n][m] (z ascending), as bf16 or fp32.
@@ -758,12 +777,14 @@ static int choose_splits(int tiles, int nch, int target = 256) {
 // Kernel choice for one GEMM (M x N outputs, K = K1 + K2): k_gemm_h for
 // dense 16-byte-aligned operands with K segments in whole stages of 32 and
 // M, N >= 128 -- 128 x 256 tiles when there are at least 64 of them, else
-// 128 x 128, with K split until there are ~512 blocks (two per CU); else
+// 128 x 128, with K split until there are ~256 blocks (one per CU); else
 // 256 x 128 tiles (k_gemm_big) for dense aligned operands and N >= 256; else
 // k_gemm<BN>.  Measured on the 8192^2 rank-512 layer at b = 2048: the
 // 2048 x 8192 products take 23 us (K 512) and 238 us (K 8704, 49 % of the
 // bf16 MFMA peak) with 128 x 256 tiles, 26 and 249 us with 256 x 256; the
-// 2048 x 512 one (K 8192) 37 us with 128 x 128 tiles split 8 ways.
+// 2048 x 512 one (K 8192, operands in cache) 25.9 us with 128 x 128 tiles
+// split 4 ways, 26.6 split 8 ways (which also gives k_reduce twice the
+// partials to read), 31.0 split 16 ways, 40.5 with 128 x 256 tiles split 4.
 enum : int { G_SMALL = 0, G_BIG = 1, G_H = 2 };
 struct GemmCfg {
   int kind;
@@ -778,7 +799,7 @@ static GemmCfg gemm_cfg(int M, int N, int K1, int K2, bool big_ok, bool h_ok) {
     c.fm = 2;
     c.fn = N >= 256 && cdiv(M, 128) * cdiv(N, 256) >= 64 ? 4 : 2;
     c.bn = 64 * c.fn;
-    c.splits = choose_splits(cdiv(M, 64 * c.fm) * cdiv(N, 64 * c.fn), K1 / kHK + K2 / kHK, 512);
+    c.splits = choose_splits(cdiv(M, 64 * c.fm) * cdiv(N, 64 * c.fn), K1 / kHK + K2 / kHK, 256);
   } else if (big_ok && N >= 256) {
     c.fm = c.fn = 0;
     c.kind = G_BIG;
