@@ -91,13 +91,16 @@ static int nm_tld(int r) { return (r + 7) & ~7; }
 // v: the rows' values loaded row-contiguous (for row tile t, lane l: row
 // 32 t + 8 k + l / 8, bytes 16 (l % 8) .. of the stage's 128-byte row
 // segment, k = 0..3), so each load instruction covers 8 whole 128-byte row
-// segments; mw: the 4 metadata words of row 32 t + l % 32; x: per chunk c,
-// the two 16-byte pieces of X row 32 by + l % 32 its B operand takes.
+// segments; mw: the 4 metadata words of row 32 t + l % 32; x: the stage's
+// 256-byte segments of the block's 32 X rows, loaded the same way (lane l:
+// row 32 by + l / 16 + 4 j, bytes 16 (l % 16) ..).  (Loading X in the B
+// operand's layout -- 16 bytes from each of 32 rows per instruction -- made
+// every X load touch 32 cache lines: 17 us per block at b = 32 against 8.)
 template <int RT>
 struct NmStage {
   u32x4 v[RT][4];
   u32x4 mw[RT];
-  u32x4 x[4][2];
+  u32x4 x[8];
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t nm_rsrc(const uint16_t* p, int64_t bytes) {
@@ -109,8 +112,10 @@ __device__ __forceinline__ u32x4 nm_bload(__amdgpu_buffer_rsrc_t r, uint32_t off
 }
 
 // Rows of a wave's staging area in LDS: 128 bytes + 16 of padding, so the
-// operand reads (lane l: row l % 32) fall on distinct banks.
+// operand reads (lane l: row l % 32) fall on distinct banks; X rows: 256 +
+// 16 bytes for the same reason.
 static constexpr int kNmRowBytes = 144;
+static constexpr int kNmXRowBytes = 272;
 static_assert(kNmRowBytes * 32 == 32 * kNmStride * 4, "staging area = the wave's reduction tile");
 
 // Block (bx, by): rows 32 RT bx .. (RT tiles of 32), batch columns 32 by ..
@@ -128,6 +133,7 @@ __global__ __launch_bounds__(64 * WV) void k_nm_smfmac(NmArgs a) {
   // Each wave's slice is its staging area during the main loop and its
   // partial tiles afterwards (only that wave touches it in between).
   __shared__ __align__(16) float red[kNmWaves][32 * RT][kNmStride];
+  __shared__ __align__(16) char xsh[kNmWaves][32 * kNmXRowBytes];  // each wave's X segments
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int i = lane & 31, h = lane >> 5;
   const int xj = (int)blockIdx.x & 7, xq = (int)blockIdx.x >> 3;
@@ -198,7 +204,11 @@ __global__ __launch_bounds__(64 * WV) void k_nm_smfmac(NmArgs a) {
       vbase[t][k] = reinterpret_cast<const char*>(a.vals) + (int64_t)min(row0 + 32 * t + 8 * k + vr, a.m - 1) * n + vb;
     mrow[t] = a.meta + (int64_t)rows[t] * (n >> 5);
   }
-  const uint32_t xo = 2u * ((uint32_t)(c0 + i) * (uint32_t)n + 8u * (uint32_t)h);
+  // X: lane l loads row c0 + l / 16 + 4 j, bytes 16 (l % 16) .. of each
+  // stage's 256-byte row segment (rows past b read as zeros)
+  const uint32_t xo = 2u * (uint32_t)(c0 + (lane >> 4)) * (uint32_t)n + 16u * (uint32_t)(lane & 15);
+  const uint32_t xstep = 8u * (uint32_t)n;  // 4 rows
+  char* const xs = &xsh[w][0];
 
   // Stage k of this wave (clamped into the matrix: loads are unconditional).
   auto issue = [&](NmStage<RT>& st, int k) {
@@ -210,11 +220,7 @@ __global__ __launch_bounds__(64 * WV) void k_nm_smfmac(NmArgs a) {
       st.mw[t] = *reinterpret_cast<const u32x4*>(mrow[t] + 4 * sg);
     }
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint32_t o = xo + 256u * (uint32_t)sg + 64u * (uint32_t)c;
-      st.x[c][0] = nm_bload(rx, o);
-      st.x[c][1] = nm_bload(rx, o + 32u);
-    }
+    for (int j = 0; j < 8; ++j) st.x[j] = nm_bload(rx, xo + 256u * (uint32_t)sg + xstep * (uint32_t)j);
   };
   auto consume = [&](const NmStage<RT>& st, bool ok) {
     // the stage's rows into the staging area, then each chunk's A operand
@@ -225,9 +231,14 @@ __global__ __launch_bounds__(64 * WV) void k_nm_smfmac(NmArgs a) {
       for (int q = 0; q < 4; ++q)
         *reinterpret_cast<u32x4*>(stg + (32 * t + 8 * q + vr) * kNmRowBytes + vb) = st.v[t][q];
 #pragma unroll
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<u32x4*>(xs + ((lane >> 4) + 4 * j) * kNmXRowBytes + 16 * (lane & 15)) = st.x[j];
+#pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const nm_u32x8 bx = {st.x[c][0].x, st.x[c][0].y, st.x[c][0].z, st.x[c][0].w,
-                           st.x[c][1].x, st.x[c][1].y, st.x[c][1].z, st.x[c][1].w};
+      // B operand of chunk c: X row c0 + i, bytes 64 c + 16 h and 64 c + 32 + 16 h
+      const u32x4 x0 = *reinterpret_cast<const u32x4*>(xs + i * kNmXRowBytes + 64 * c + 16 * h);
+      const u32x4 x1 = *reinterpret_cast<const u32x4*>(xs + i * kNmXRowBytes + 64 * c + 32 + 16 * h);
+      const nm_u32x8 bx = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
         const u32x4 z = {0u, 0u, 0u, 0u};
