@@ -293,7 +293,10 @@ hss_status hss_apply_workspace_size(const hss_matrix* A, int32_t b, size_t* byte
  * copy inside the workspace, so the workspace then holds m*n*2 more bytes).
  * bf16 CSR with 3 <= b <= 128 runs the gather SpMM (T = X V rounded to bf16
  * once, X^T staged in the workspace, then every stored entry gathers its X^T
- * row; fp32 accumulation).  Otherwise one fused kernel per 8 columns.  On
+ * row; fp32 accumulation).  Otherwise one fused kernel per 8 columns (T =
+ * X V accumulated in fp32; for bf16 matrices whose U is 16-byte aligned it is
+ * rounded to bf16 once before U T is added, as on every other route; fp32
+ * matrices keep it in fp32).  On
  * the matrix-core routes (the sparse one included) zeros in an operand
  * multiply X too, so a NaN or infinity in X can reach any output of its
  * batch row.  HSS_OPT_BATCH_ROUTE (hss_set_option) forces a bf16 call with

@@ -30,6 +30,7 @@ static size_t max_lds(const hss_matrix* A) { return A->fmt == HSS_FMT_CSR ? kMax
 static bool col16_of(const hss_matrix* A) { return A->fmt == HSS_FMT_CSR && (A->flags & HSS_COL16); }
 
 static size_t align16(size_t x) { return (x + 15) / 16 * 16; }
+static constexpr size_t kMaskTabBytes = 256 * 16;  // u_epilogue's mask table (bf16 U pieces)
 
 size_t decode_ctl_bytes() { return kCtlBytes; }
 
@@ -49,7 +50,7 @@ size_t decode_t_bytes(const hss_matrix* A) {
 // 0 if even one column does not fit.
 int decode_max_cols(const hss_matrix* A) {
   for (int bc = 8; bc >= 1; bc /= 2) {
-    const size_t tb = align16(sizeof(float) * (size_t)bc * t_ld(A->r)) +
+    const size_t tb = align16(sizeof(float) * (size_t)bc * t_ld2(A->r)) + kMaskTabBytes +
                       align16(4 * (size_t)((A->r + 31) / 32));
     if (tb <= max_lds(A)) return bc;
   }
@@ -107,7 +108,12 @@ static MatrixLaunch matrix_launch(const hss_matrix* A, int bc, const void* X, vo
   }
 
   const size_t es = A->dtype == HSS_F32 ? 4 : 2;
-  const size_t tbytes = align16(sizeof(float) * (size_t)bc * t_ld(A->r));
+  // bf16 U rows as aligned 16-byte pieces (any r): one piece per lane covers
+  // r <= 506, two r <= 1018 (and give the same bits there as one would).
+  L.uq = (A->dtype == HSS_BF16 && a.ru > 0 && (uintptr_t)A->U % 16 == 0) ? (a.ru <= 506 ? 1 : 2) : 0;
+  // T: fp32, or bf16 in two copies (the same bytes, see t_ld2), plus the
+  // pieces' mask table
+  const size_t tbytes = align16(sizeof(float) * (size_t)bc * t_ld2(A->r)) + (L.uq > 0 ? kMaskTabBytes : 0);
   const size_t mbytes = align16(4 * (size_t)((A->r + 31) / 32));
   const bool nm_fast = A->fmt == HSS_FMT_2OF4 && A->dtype == HSS_BF16 && ((uintptr_t)X % 16 == 0) &&
                        A->n % 32 == 0 && (uintptr_t)A->nm_values % 16 == 0 && (uintptr_t)A->nm_meta % 4 == 0 &&
@@ -115,6 +121,7 @@ static MatrixLaunch matrix_launch(const hss_matrix* A, int bc, const void* X, vo
   // the 2:4 fast path reads 64-byte X chunks at a 64-byte lane stride: pad them
   const size_t xbytes = align16((size_t)bc * A->n * es * (nm_fast ? 5 : 4) / 4);
   a.t_off = 0;
+  a.mtab_off = (int)(tbytes - (L.uq > 0 ? kMaskTabBytes : 0));
   a.miss_off = (int)tbytes;
   a.x_off = (int)(tbytes + mbytes);
   a.x_lds = tbytes + mbytes + xbytes <= max_lds(A);
@@ -127,9 +134,6 @@ static MatrixLaunch matrix_launch(const hss_matrix* A, int bc, const void* X, vo
               (uintptr_t)A->values % (4 * es) == 0;
   a.nm_fast = A->fmt == HSS_FMT_2OF4 && A->dtype == HSS_BF16 && a.vec && A->n % 32 == 0 &&
               (uintptr_t)A->nm_values % 16 == 0 && (uintptr_t)A->nm_meta % 4 == 0;
-  // bf16 U rows as aligned 16-byte pieces (any r): one piece per lane covers
-  // r <= 506, two r <= 1018 (and give the same bits there as one would).
-  L.uq = (A->dtype == HSS_BF16 && a.ru > 0 && (uintptr_t)A->U % 16 == 0) ? (a.ru <= 506 ? 1 : 2) : 0;
   L.lds = tbytes + mbytes + (a.x_lds ? xbytes : 0);
   L.fast = A->dtype == HSS_BF16 && A->r > 0 && a.x_lds && a.vec &&
            (A->fmt == HSS_FMT_CSR ? a.vec_csr : a.nm_fast);
@@ -430,7 +434,7 @@ __global__ __launch_bounds__(256) void k_decode_dq(DqArgs q) {
     }
 #pragma unroll
     for (int c = 0; c < BC; ++c) {
-      const float s = wave_sum(acc[c]) + ssum[i][c];
+      const float s = wave_sum(acc[c] + ssum[i][c]);  // the dense part's and the outliers' lane shares
       if (row < m && c < bc && lane == c) {
         if constexpr (DT == HSS_F32)
           Y[(int64_t)c * m + row] = __float_as_uint(s);

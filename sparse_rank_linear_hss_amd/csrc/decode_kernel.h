@@ -81,6 +81,7 @@ struct DecodeArgs {
   int nm_fast;    // bf16 2:4 with n % 32 == 0 and aligned rows: vector words
   int spin;       // polls of a stale T word before computing it locally
   int t_off, miss_off, x_off;  // dynamic LDS layout (bytes)
+  int mtab_off;                // bf16 U pieces: the 256-entry mask table (4 KiB)
   // Block structure of the low-rank term (a flat matrix: ru = r, v_ld = n,
   // h_m0 = m, h_toff = 0, h_n0 = n, h_l1 = h_l2 = h_l3 = r).  U rows hold ru
   // values (row stride ru); rows i >= h_m0 take them against T[h_toff ..
@@ -437,7 +438,7 @@ __device__ __forceinline__ void csr_consume(const DecodeArgs& a, CsrChunks<DT, R
       }
     }
 #pragma unroll
-    for (int c = 0; c < BC; ++c) ssum[i][c] = wave_sum(acc[c]);
+    for (int c = 0; c < BC; ++c) ssum[i][c] = acc[c];  // this lane's share; the row's sum is taken with U's
   }
 }
 
@@ -598,7 +599,7 @@ __device__ __forceinline__ void nm_consume(const DecodeArgs& a, int row0, const 
 #pragma unroll
   for (int i = 0; i < RPW; ++i)
 #pragma unroll
-    for (int c = 0; c < BC; ++c) ssum[i][c] = wave_sum(acc[i][c]);
+    for (int c = 0; c < BC; ++c) ssum[i][c] = acc[i][c];  // this lane's share; the row's sum is taken with U's
 }
 
 // ---------------------------------------------------------------------------
@@ -652,14 +653,80 @@ __device__ __forceinline__ void u_issue(const DecodeArgs& a, int row0, UBuf<UQ> 
 static constexpr int kTPad = 8;
 __device__ __host__ __forceinline__ int t_ld(int r) { return r + 2 * kTPad; }
 
+// bf16 T (bf16 matrices whose U rows are read as 16-byte pieces): T is
+// rounded to bf16 once, as the matrix-core routes round it, and each column
+// holds two copies of its padded values, E (element j = T[j - kTPad]) and,
+// t_ld2(r) elements later, O (element j = E[j + 1]), so that every pair
+// T[l], T[l + 1] is one aligned 32-bit word, of E when l + kTPad is even and
+// of O when it is odd.  A piece's 8 products are then 4 v_dot2_f32_bf16 of
+// U words and T words, with the elements outside the row zeroed in both by
+// a mask from a 256-entry table (one 16-byte read), where the fp32 T took
+// 8 conversions, 8 FMAs and 8 range selects.  Both copies are zero outside
+// [0, r) (the column's region is cleared before T is written).
+__device__ __host__ __forceinline__ int t_ld2(int r) { return (t_ld(r) + 1) & ~1; }
+// Halfword mask of a 16-byte piece whose elements k with bit k of m8 set
+// are kept: entry m8 of the table, built once per block.
+__device__ __forceinline__ u32x4 piece_mask(int m8) {
+  uint32_t w[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    w[q] = ((m8 >> (2 * q)) & 1 ? 0x0000ffffu : 0u) | ((m8 >> (2 * q + 1)) & 1 ? 0xffff0000u : 0u);
+  return u32x4{w[0], w[1], w[2], w[3]};
+}
+
 template <int DT, int BC, int RPW, int UQ>
 __device__ __forceinline__ void u_epilogue(const DecodeArgs& a, int row0, const UBuf<UQ> (&ub)[RPW],
-                                           const float* __restrict__ Tp0, float (&acc)[RPW][BC]) {
+                                           const float* __restrict__ Tp0, const unsigned char* __restrict__ smem,
+                                           float (&acc)[RPW][BC]) {
   using bits_t = typename Elem<DT>::bits_t;
   const bits_t* __restrict__ U = static_cast<const bits_t*>(a.U);
   const int lane = lane_id();
   const int m = a.m, r = a.ru, bc = a.bc;
   const int tld = t_ld(a.r);
+  if constexpr (DT == HSS_BF16 && UQ > 0) {
+    const uint16_t* __restrict__ T16 = reinterpret_cast<const uint16_t*>(smem + a.t_off);
+    const u32x4* __restrict__ mtab = reinterpret_cast<const u32x4*>(smem + a.mtab_off);
+    const int ld2 = t_ld2(a.r);
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int row = row0 + i;
+#pragma unroll
+      for (int c = 0; c < BC; ++c) acc[i][c] = 0.f;
+      if (row >= m) continue;
+      const int toff = row >= a.h_m0 ? a.h_toff : 0;  // T[h_toff ..] for the second row half of a block term
+      const int64_t e0 = (int64_t)row * r;
+      const int sh = (int)(e0 & 7);  // the row starts at element sh of its first piece
+#pragma unroll
+      for (int q = 0; q < UQ; ++q) {
+        const int lb = 8 * (lane + 64 * q) - sh;  // l of the piece's first element (>= -7)
+        const int base = min(lb, r);               // reads stay inside the column and its pads
+        // elements k with 0 <= lb + k < r are kept
+        const int lo = min(max(-lb, 0), 8), hi = min(max(r - lb, 0), 8);
+        const u32x4 mk = mtab[(0xff << lo) & (0xffu >> (8 - hi)) & 0xff];
+        const u32x4 uw = {ub[i].p[q].x & mk.x, ub[i].p[q].y & mk.y, ub[i].p[q].z & mk.z, ub[i].p[q].w & mk.w};
+        const int s0 = base + toff + kTPad;  // E element of the piece's first T value
+        const int off = (s0 & 1) ? ld2 + s0 - 1 : s0;
+#pragma unroll
+        for (int c = 0; c < BC; ++c) {
+          const uint32_t* __restrict__ tw =
+              reinterpret_cast<const uint32_t*>(T16 + (c == 0 ? 0 : min(c, bc - 1) * 2 * ld2) + off);
+          float f = acc[i][c];
+          f = dot2_bf16(uw.x, tw[0] & mk.x, f);
+          f = dot2_bf16(uw.y, tw[1] & mk.y, f);
+          f = dot2_bf16(uw.z, tw[2] & mk.z, f);
+          f = dot2_bf16(uw.w, tw[3] & mk.w, f);
+          acc[i][c] = f;
+        }
+      }
+      for (int l = 512 * UQ - sh + lane; l < r; l += 64) {  // beyond the pieces in registers
+        const float u = fval<DT>(U[e0 + l]);
+#pragma unroll
+        for (int c = 0; c < BC; ++c)
+          if (c < bc) acc[i][c] = fmaf(u, bf16lo(T16[c * 2 * ld2 + l + toff + kTPad]), acc[i][c]);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < RPW; ++i) {
     const int row = row0 + i;
@@ -1019,10 +1086,29 @@ __global__ __launch_bounds__(MTR > 0 ? kMergedThreads : 256) void k_decode(Group
     }
   }
   for (int q = t; q < (r + 31) / 32; q += NT) miss[q] = 0;
-  for (int q = t; q < 2 * kTPad * bc; q += NT) {  // the zero pads around every T column
-    const int c = q / (2 * kTPad), j = q % (2 * kTPad);
-    Tp[c * t_ld(r) + (j < kTPad ? j - kTPad : r + j - kTPad)] = 0.f;
+  constexpr bool T16 = DT == HSS_BF16 && UQ > 0;  // bf16 T in two copies (u_epilogue)
+  if constexpr (T16) {
+    // both copies of every column zero (the pads stay so), and the mask table
+    uint32_t* tz = reinterpret_cast<uint32_t*>(smem + a.t_off);
+    for (int q = t; q < bc * t_ld2(r); q += NT) tz[q] = 0u;
+    if (t < 256) reinterpret_cast<u32x4*>(smem + a.mtab_off)[t] = piece_mask(t);
+  } else {
+    for (int q = t; q < 2 * kTPad * bc; q += NT) {  // the zero pads around every T column
+      const int c = q / (2 * kTPad), j = q % (2 * kTPad);
+      Tp[c * t_ld(r) + (j < kTPad ? j - kTPad : r + j - kTPad)] = 0.f;
+    }
   }
+  // T value l of column c into LDS
+  auto t_put = [&](int c, int l, float v) {
+    if constexpr (T16) {
+      uint16_t* col = reinterpret_cast<uint16_t*>(smem + a.t_off) + c * 2 * t_ld2(r);
+      const uint16_t h = f32_to_bf16(v);
+      col[l + kTPad] = h;                  // E
+      col[t_ld2(r) + l + kTPad - 1] = h;   // O (O[j] = E[j + 1])
+    } else {
+      Tp[c * t_ld(r) + l] = v;
+    }
+  };
   if (xvecs > 0) {
     // the rest of X, four vectors per thread in flight per step (unconditional
     // loads, past the end of X: vector 0)
@@ -1121,7 +1207,7 @@ __global__ __launch_bounds__(MTR > 0 ? kMergedThreads : 256) void k_decode(Group
           const int ce = BC == 1 ? 0 : e / tn;
           const int l = tlo + (BC == 1 ? e : e - ce * tn);
           if ((uint32_t)(v >> 32) == tag && a.spin >= 0) {
-            Tp[ce * t_ld(r) + l] = __uint_as_float((uint32_t)v);
+            t_put(ce, l, __uint_as_float((uint32_t)v));
           } else {
             atomicOr(&miss[l >> 5], 1u << (l & 31));
           }
@@ -1137,7 +1223,7 @@ __global__ __launch_bounds__(MTR > 0 ? kMergedThreads : 256) void k_decode(Group
         int tc0, tlen;
         t_cols(a, l, tc0, tlen);
         t_row<DT, BC, NT>(Vt + (int64_t)l * a.v_ld, (a.x_pad ? X : xsrc) + tc0, tlen, n, bc, a.vec, red);
-        if (t < bc) Tp[t * t_ld(r) + l] = red_sum<BC, NW>(red, t);
+        if (t < bc) t_put(t, l, red_sum<BC, NW>(red, t));
         __syncthreads();
       }
     }
@@ -1145,7 +1231,7 @@ __global__ __launch_bounds__(MTR > 0 ? kMergedThreads : 256) void k_decode(Group
 
   // low-rank epilogue, store
   float lacc[RPW][BC];
-  if (r > 0) u_epilogue<DT, BC, RPW, UQ>(a, row0, ub, Tp, lacc);
+  if (r > 0) u_epilogue<DT, BC, RPW, UQ>(a, row0, ub, Tp, smem, lacc);
   bits_t* __restrict__ Y = static_cast<bits_t*>(a.Y);
   const int lane = lane_id();
 #pragma unroll
@@ -1153,7 +1239,7 @@ __global__ __launch_bounds__(MTR > 0 ? kMergedThreads : 256) void k_decode(Group
     const int row = row0 + i;
 #pragma unroll
     for (int c = 0; c < BC; ++c) {
-      const float s = (r > 0 ? wave_sum(lacc[i][c]) : 0.f) + ssum[i][c];
+      const float s = wave_sum((r > 0 ? lacc[i][c] : 0.f) + ssum[i][c]);  // one reduction per row and column
       if (row < m && c < bc && lane == c) {
         if constexpr (DT == HSS_F32)
           Y[(int64_t)c * m + row] = __float_as_uint(s);
