@@ -379,6 +379,35 @@ __device__ __forceinline__ void csr_chunk_fma(const ChunkX<DT, BC>& g, float (&a
   }
 }
 
+// bf16 chunk (entries e .. e + 3) of a row whose entries all lie in whole
+// chunks of the arrays (en <= nnz rounded down to 4: every row but those in
+// the arrays' last partial chunk).  The four X values are gathered at the
+// chunk's columns as they are -- every column is a valid index, also for
+// entries outside [st, en) -- the entries outside [st, en) are zeroed in the
+// values and in the gathered X (so that no product of them reaches the sum,
+// whatever their values), and the two pairs go to v_dot2_f32_bf16: about
+// half the instructions of csr_chunk_gather + csr_chunk_fma, which a launch
+// of many rows spends a good part of its time issuing.
+template <int BC, typename VC>
+__device__ __forceinline__ void csr_chunk_dot2(const DecodeArgs& a, int e, int st, int en, const u32x4& cc,
+                                               const VC& vv, const uint16_t* __restrict__ xsrc, float (&acc)[BC]) {
+  const int lo = min(max(st - e, 0), 4), hi = min(max(en - e, 0), 4);
+  const int m4 = (0xf << lo) & (0xf >> (4 - hi));  // bit k: entry e + k is the row's
+  const uint32_t k01 = (m4 & 1 ? 0x0000ffffu : 0u) | (m4 & 2 ? 0xffff0000u : 0u);
+  const uint32_t k23 = (m4 & 4 ? 0x0000ffffu : 0u) | (m4 & 8 ? 0xffff0000u : 0u);
+  const uint32_t v01 = vv.x & k01, v23 = vv.y & k23;
+  uint32_t x01[BC], x23[BC];
+#pragma unroll
+  for (int c = 0; c < BC; ++c) {
+    const uint16_t* __restrict__ xc = xsrc + (c == 0 ? 0 : (int64_t)min(c, a.bc - 1) * a.n);
+    const uint32_t x0 = xc[cc.x], x1 = xc[cc.y], x2 = xc[cc.z], x3 = xc[cc.w];
+    x01[c] = (x0 | (x1 << 16)) & k01;
+    x23[c] = (x2 | (x3 << 16)) & k23;
+  }
+#pragma unroll
+  for (int c = 0; c < BC; ++c) acc[c] = dot2_bf16(v23, x23[c], dot2_bf16(v01, x01[c], acc[c]));
+}
+
 template <int DT, int FMT, int BC, int RPW, int CP = 1>
 __device__ __forceinline__ void csr_consume(const DecodeArgs& a, CsrChunks<DT, RPW, CP>& ch,
                                             const typename Elem<DT>::bits_t* __restrict__ xsrc,
@@ -390,7 +419,28 @@ __device__ __forceinline__ void csr_consume(const DecodeArgs& a, CsrChunks<DT, R
   const int64_t last = ((a.nnz - 4) & ~(int64_t)3);
   float accs[RPW][BC];
   const CsrTail tl = csr_tail_values(ch.tcol, ch.tval);
-  if (a.vec_csr) {
+  const int64_t nnz4 = a.nnz & ~(int64_t)3;  // rows ending at or before this take csr_chunk_dot2 (bf16)
+  if (DT == HSS_BF16 && a.vec_csr) {
+    const uint16_t* __restrict__ x16 = reinterpret_cast<const uint16_t*>(xsrc);
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+#pragma unroll
+      for (int c = 0; c < BC; ++c) accs[i][c] = 0.f;
+      if (ch.en[i] <= nnz4) {  // wave-uniform
+        csr_chunk_dot2<BC>(a, ch.e0[i], ch.st[i], ch.en[i], ch.cq[i], ch.vq[i], x16, accs[i]);
+        if constexpr (CP > 1)
+          csr_chunk_dot2<BC>(a, ch.e0[i] + 256, ch.st[i], ch.en[i], ch.cq1[i], ch.vq1[i], x16, accs[i]);
+      } else {
+        ChunkX<DT, BC> g;
+        csr_chunk_gather<DT, BC>(a, ch.e0[i], ch.st[i], ch.en[i], ch.cq[i], ch.vq[i], tl, xsrc, g);
+        csr_chunk_fma<DT, BC>(g, accs[i]);
+        if constexpr (CP > 1) {
+          csr_chunk_gather<DT, BC>(a, ch.e0[i] + 256, ch.st[i], ch.en[i], ch.cq1[i], ch.vq1[i], tl, xsrc, g);
+          csr_chunk_fma<DT, BC>(g, accs[i]);
+        }
+      }
+    }
+  } else if (a.vec_csr) {
     // first chunks of all rows: every gather first, then the products
     ChunkX<DT, BC> g[RPW];
 #pragma unroll
@@ -424,9 +474,13 @@ __device__ __forceinline__ void csr_consume(const DecodeArgs& a, CsrChunks<DT, R
         const int64_t ec = e < last ? e : last;
         const u32x4 cc = col_chunk<FMT>(a, ec);
         const vchunk_t vv = __builtin_nontemporal_load(reinterpret_cast<const vchunk_t*>(vals + ec));
-        ChunkX<DT, BC> gl;
-        csr_chunk_gather<DT, BC>(a, e, st, en, cc, vv, tl, xsrc, gl);
-        csr_chunk_fma<DT, BC>(gl, acc);
+        if (DT == HSS_BF16 && en <= nnz4) {
+          csr_chunk_dot2<BC>(a, e, st, en, cc, vv, reinterpret_cast<const uint16_t*>(xsrc), acc);
+        } else {
+          ChunkX<DT, BC> gl;
+          csr_chunk_gather<DT, BC>(a, e, st, en, cc, vv, tl, xsrc, gl);
+          csr_chunk_fma<DT, BC>(gl, acc);
+        }
       }
     } else {
       for (int p = st + lane; p < en; p += 64) {
