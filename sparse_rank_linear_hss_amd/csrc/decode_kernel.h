@@ -1215,12 +1215,19 @@ __global__ __launch_bounds__(MTR > 0 ? kMergedThreads : 256) void k_decode(Group
   }
   const int ttotal = bc * tn;
   auto t_word = [&](int e) { return BC == 1 ? tlo + e : (e / tn) * r + tlo + e % tn; };
+  // slots past the end re-read a word this block reads anyway (e - ttotal,
+  // or word 0 when that is past the end too): a conditional subtract, not an
+  // integer division
+  auto t_slot = [&](int e) {
+    const int w = e - ttotal;
+    return e < ttotal ? e : (w < ttotal ? w : 0);
+  };
   uint64_t tv[kTW];
   if constexpr (FAST) {
 #pragma unroll
     for (int k = 0; k < kTW; ++k) {
       const int e = t + NT * k;
-      tv[k] = __hip_atomic_load(Tr + t_word(e < ttotal ? e : e % ttotal), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      tv[k] = __hip_atomic_load(Tr + t_word(t_slot(e)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 
@@ -1245,8 +1252,7 @@ __global__ __launch_bounds__(MTR > 0 ? kMergedThreads : 256) void k_decode(Group
 #pragma unroll
         for (int k = 0; k < kTW; ++k) {
           const int e = base + t + NT * k;
-          tv[k] = __hip_atomic_load(Tr + t_word(e < ttotal ? e : e % ttotal), __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_AGENT);
+          tv[k] = __hip_atomic_load(Tr + t_word(t_slot(e)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
 #pragma unroll
