@@ -49,7 +49,7 @@ namespace hss {
 // own 128-byte line.
 static constexpr int kCtlEpoch = 0;
 static constexpr int kCtlLine = 32;                  // words per line
-static constexpr int kNumSub = 64;
+static constexpr int kNumSub = 64;  // a power of two (arrive_check divides by it with a shift)
 static constexpr int kCtlSetWords = (1 + kNumSub) * kCtlLine;
 static constexpr size_t kCtlBytes = 32768;          // >= (1 + 2 * 65) lines
 __device__ __forceinline__ int ctl_top(uint32_t epoch) { return kCtlLine + (int)(epoch & 1u) * kCtlSetWords; }
@@ -286,14 +286,16 @@ __device__ __forceinline__ void csr_issue(const DecodeArgs& a, const int (&rb)[R
   using vchunk_t = typename CsrChunks<DT, RPW, CP>::vchunk_t;
   const int lane = lane_id();
   const bits_t* __restrict__ vals = static_cast<const bits_t*>(a.vals);
-  const int64_t last = ((a.nnz - 4) & ~(int64_t)3);  // highest aligned full chunk
+  // highest aligned full chunk; entry indices fit 32 bits (arrays hold
+  // fewer than 2^31 elements), so the clamps are 32-bit
+  const uint32_t last = (uint32_t)((a.nnz - 4) & ~(int64_t)3);
 #pragma unroll
   for (int i = 0; i < RPW; ++i) {
     ch.st[i] = uniform(rb[i]);
     ch.en[i] = uniform(rb[i + 1]);
     ch.e0[i] = (ch.st[i] & ~3) + 4 * lane;
     if (a.vec_csr) {
-      const int64_t ec = ch.e0[i] < last ? ch.e0[i] : last;
+      const uint32_t ec = min((uint32_t)ch.e0[i], last);
       ch.cq[i] = col_chunk<FMT>(a, ec);
       ch.vq[i] = __builtin_nontemporal_load(reinterpret_cast<const vchunk_t*>(vals + ec));
     }
@@ -302,8 +304,7 @@ __device__ __forceinline__ void csr_issue(const DecodeArgs& a, const int (&rb)[R
     if (a.vec_csr) {
 #pragma unroll
       for (int i = 0; i < RPW; ++i) {
-        const int64_t e1 = ch.e0[i] + 256;
-        const int64_t ec = e1 < last ? e1 : last;
+        const uint32_t ec = min((uint32_t)ch.e0[i] + 256u, last);
         ch.cq1[i] = col_chunk<FMT>(a, ec);
         ch.vq1[i] = __builtin_nontemporal_load(reinterpret_cast<const vchunk_t*>(vals + ec));
       }
@@ -682,20 +683,20 @@ __device__ __forceinline__ void u_issue(const DecodeArgs& a, int row0, UBuf<UQ> 
   const int m = a.m, r = a.ru;
 #pragma unroll
   for (int i = 0; i < RPW; ++i) {
-    const int64_t rowc = min(row0 + i, m - 1);
+    const int rowc = min(row0 + i, m - 1);  // U has fewer than 2^31 elements: 32-bit offsets
     if constexpr (UQ > 0) {
-      const int64_t e0 = rowc * r;
-      const int64_t p0 = e0 >> 3, plast = (e0 + r - 1) >> 3;
+      const int e0 = rowc * r;
+      const int p0 = e0 >> 3, plast = (e0 + r - 1) >> 3;
 #pragma unroll
       for (int q = 0; q < UQ; ++q) {
-        const int64_t p = p0 + lane + 64 * q;
+        const int p = p0 + lane + 64 * q;
         ub[i].p[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(U) + (p <= plast ? p : p0));
       }
     } else {
 #pragma unroll
       for (int q = 0; q < kUPL; ++q) {
         const int l = lane + 64 * q;
-        ub[i].e[q] = __builtin_nontemporal_load(U + rowc * r + min(l, r - 1));  // masked at use
+        ub[i].e[q] = __builtin_nontemporal_load(U + (int64_t)rowc * r + min(l, r - 1));  // masked at use
       }
     }
   }
@@ -885,7 +886,9 @@ __device__ __forceinline__ uint32_t arrive_issue(const DecodeArgs& a, int sub, u
 
 __device__ __forceinline__ bool arrive_check(const DecodeArgs& a, int G, int nsub, int sub, uint32_t epoch,
                                              uint32_t arrived, uint32_t& top) {
-  const bool sub_last = arrived == (uint32_t)((G - sub + nsub - 1) / nsub) - 1;
+  // blocks on counter sub: ceil((G - sub) / nsub), nsub being G (< 64: one each) or 64
+  const uint32_t quota = nsub == kNumSub ? (uint32_t)(G - sub + kNumSub - 1) >> 6 : 1u;
+  const bool sub_last = arrived == quota - 1;
   if (sub_last) {
     uint32_t off = 0;
     asm volatile("" : "+v"(off));  // opaque: keeps the add a plain single-lane atomic
@@ -984,7 +987,8 @@ __global__ __launch_bounds__(MTR > 0 ? kMergedThreads : 256) void k_decode(Group
   bits_t* xs = reinterpret_cast<bits_t*>(smem + a.x_off);
   const bits_t* xsrc = a.x_lds ? xs : X;
   const int nsub = G < kNumSub ? G : kNumSub;
-  const int sub = (int)blockIdx.x % nsub;
+  // counter of this block: blockIdx mod nsub, nsub being G (< 64) or 64
+  const int sub = G < kNumSub ? (int)blockIdx.x : (int)(blockIdx.x & (kNumSub - 1));
 
   // ---- T producer: Vt row l and X loaded together, published tagged into
   //      every replica ----
