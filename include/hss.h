@@ -47,7 +47,7 @@ extern "C" {
 #endif
 
 #define HSS_VERSION_MAJOR 1
-#define HSS_VERSION_MINOR 6
+#define HSS_VERSION_MINOR 7
 
 /* Largest batch (columns of X) one hss_apply / hss_apply_group / hss_grad
  * call takes: decode (1) up to a prefill of 2048 tokens. */
@@ -94,15 +94,27 @@ int hss_version(void);
  *   HSS_OPT_DECODE_FORCE_LOCAL: 1 = every decode block ignores the T words
  *       and computes every T row itself (same arithmetic, same bits), to
  *       test that fallback; default 0.
+ *   HSS_OPT_DECODE_WAVE_PRODUCERS (HSS_DECODE_WAVE_PRODUCERS = 0): 1
+ *       (default) = in one-column bf16 decode launches with separate
+ *       producer blocks and n <= 4096, each wave of a producer block makes
+ *       one T row (same bits); 0 = one T row per producer block.
+ *   HSS_OPT_DECODE_RPW (HSS_DECODE_RPW = 1 | 2 | 4): output rows per wave of
+ *       the decode kernel's row blocks (launches that merge the T producers
+ *       into the row blocks choose their own); 0 (default) = by matrix
+ *       height: 1 below 2048 rows, else 4 for one column and, for more
+ *       columns, 2 below 8192 rows, else 4.  Bits do not depend on it.
  * hss_set_option returns HSS_ERR_INVALID_ARG for an unknown option or a
- * value out of range (routes 0..4 / 0..2, spin >= 0, flags 0..1);
+ * value out of range (routes 0..4 / 0..2, spin >= 0, flags 0..1, rows per
+ * wave 0, 1, 2 or 4);
  * hss_get_option returns -1 for an unknown option. */
 typedef enum {
   HSS_OPT_BATCH_ROUTE = 0,
   HSS_OPT_GRAD_DS_ROUTE = 1,
   HSS_OPT_DECODE_SPIN = 2,
   HSS_OPT_DECODE_MERGED = 3,
-  HSS_OPT_DECODE_FORCE_LOCAL = 4
+  HSS_OPT_DECODE_FORCE_LOCAL = 4,
+  HSS_OPT_DECODE_WAVE_PRODUCERS = 5,
+  HSS_OPT_DECODE_RPW = 6
 } hss_option;
 hss_status hss_set_option(int32_t opt, int32_t value);
 int32_t hss_get_option(int32_t opt);

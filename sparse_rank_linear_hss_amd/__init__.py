@@ -21,6 +21,7 @@ import torch
 
 from ._lib import (HSS_BF16, HSS_COL16, HSS_DQ4, HSS_ERR_NONFINITE, HSS_HIER2, HSS_F32, HSS_FMT_2OF4, HSS_FMT_CSR,
                    HSS_MAX_BATCH, HSS_OK, HSS_OPT_BATCH_ROUTE, HSS_OPT_DECODE_FORCE_LOCAL, HSS_OPT_DECODE_MERGED,
+                   HSS_OPT_DECODE_RPW, HSS_OPT_DECODE_WAVE_PRODUCERS,
                    HSS_OPT_DECODE_SPIN, HSS_OPT_GRAD_DS_ROUTE, HSSError, HssMatrixStruct, LIB_PATH, check, lib,
                    status_string)
 
@@ -69,7 +70,8 @@ def hss_version() -> int:
 # variables spell them.
 _OPTS = {"batch_route": HSS_OPT_BATCH_ROUTE, "grad_ds_route": HSS_OPT_GRAD_DS_ROUTE,
          "decode_spin": HSS_OPT_DECODE_SPIN, "decode_merged": HSS_OPT_DECODE_MERGED,
-         "decode_force_local": HSS_OPT_DECODE_FORCE_LOCAL}
+         "decode_force_local": HSS_OPT_DECODE_FORCE_LOCAL, "decode_wave_producers": HSS_OPT_DECODE_WAVE_PRODUCERS,
+         "decode_rpw": HSS_OPT_DECODE_RPW}
 _OPT_WORDS = {"batch_route": {"auto": 0, "decode": 1, "spmm": 2, "densify": 3, "smfmac": 4},
               "grad_ds_route": {"auto": 0, "sparse": 1, "dense": 2}}
 

@@ -25,6 +25,8 @@ HSS_OPT_GRAD_DS_ROUTE = 1
 HSS_OPT_DECODE_SPIN = 2
 HSS_OPT_DECODE_MERGED = 3
 HSS_OPT_DECODE_FORCE_LOCAL = 4
+HSS_OPT_DECODE_WAVE_PRODUCERS = 5
+HSS_OPT_DECODE_RPW = 6
 HSS_COL16 = 1  # hss_matrix.flags: CSR col_idx holds uint16 columns
 HSS_DQ4 = 2    # hss_matrix.flags: a 4-bit quantised dense part (dq_codes, dq_levels)
 HSS_HIER2 = 4  # hss_matrix.flags: compact 2 x 2 block low-rank term (hier_r)

@@ -142,9 +142,11 @@ static MatrixLaunch matrix_launch(const hss_matrix* A, int bc, const void* X, vo
   L.cp = A->fmt == HSS_FMT_CSR && A->nnz > 192 * (int64_t)A->m ? 2 : 1;
   // Rows per wave: more rows per block means fewer copies of X staged through
   // L2 into LDS and fewer blocks queueing loads on each CU (measured best:
-  // 2 for 4096 rows, 4 for 11008 rows); small matrices keep one row per wave
-  // for parallelism.  Four rows per wave exist only as FAST instances.
-  L.rpw = A->m >= 8192 ? 4 : (A->m >= 2048 ? 2 : 1);
+  // 4 for one column from 2048 rows -- the decoder layer's q/k/v launch 13.0
+  // against 14.0 us with 2 -- and 4 for 11008 rows, 2 for 4096 rows at more
+  // columns); small matrices keep one row per wave for parallelism.  Four
+  // rows per wave exist only as FAST instances.
+  L.rpw = A->m >= 8192 ? 4 : (A->m >= 2048 ? (bc == 1 ? 4 : 2) : 1);
   return L;
 }
 
@@ -201,15 +203,23 @@ void launch_decode_group(const hss_matrix* const* A, int G, int bc, const void* 
     fast = fast && L[g].fast;
     rpw = rpw < L[g].rpw ? rpw : L[g].rpw;
   }
+  if (option(HSS_OPT_DECODE_RPW) > 0) rpw = option(HSS_OPT_DECODE_RPW);
   if (!fast && rpw > 2) rpw = 2;
   const int dt = A[0]->dtype, fmt = col16_of(A[0]) ? kFmtCsr16 : A[0]->fmt;
   if (uq < 0) uq = 0;
   const int mtr = merged_plan(A, G, bc, fast && dt == HSS_BF16 && uq > 0, fmt, rpw);
   const bool merged = mtr > 0;
+  // Wave producers (one bf16 column on the FAST path, X of at most 4096
+  // elements): one T row per wave, four per block.  The q/k/v launch of the
+  // decoder layer then has 309 producer blocks instead of 1,227, and its
+  // producers and row blocks all fit on the CUs at once.
+  bool wave_prod = !merged && bc == 1 && fast && dt == HSS_BF16 && option(HSS_OPT_DECODE_WAVE_PRODUCERS) != 0;
+  for (int g = 0; g < G; ++g) wave_prod = wave_prod && (size_t)A[g]->n * 2 <= 2 * 256 * 16;
+  ga.prod_rows = wave_prod ? 4 : 1;
   ga.prod_start[0] = 0;
   for (int g = 0; g < G; ++g) {
     ga.a[g] = L[g].a;
-    ga.prod_start[g + 1] = ga.prod_start[g] + (merged ? 0 : A[g]->r);
+    ga.prod_start[g + 1] = ga.prod_start[g] + (merged ? 0 : (A[g]->r + ga.prod_rows - 1) / ga.prod_rows);
   }
   ga.row_start[0] = ga.prod_start[G];
   const int rows_per_block = (merged ? kMergedThreads / 64 : 4) * rpw;

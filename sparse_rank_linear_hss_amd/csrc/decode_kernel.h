@@ -106,6 +106,7 @@ struct GroupArgs {
   DecodeArgs a[kMaxGroup];
   int G;
   int prod_start[kMaxGroup + 1];  // producer blocks of matrix g: [prod_start[g], prod_start[g + 1])
+  int prod_rows;                   // T rows per producer block: 1, or one per wave (wave producers)
   int row_start[kMaxGroup + 1];   // row blocks of matrix g (after all producers)
 };
 
@@ -242,6 +243,55 @@ __device__ __forceinline__ void t_row(const typename Elem<DT>::bits_t* __restric
     if (lane_id() == 0) red[w][c] = s;
   }
   __syncthreads();
+}
+
+// T row of one producer wave (one column, vector path): the same value, bit
+// for bit, as t_row<DT, 1, NT> computes with a whole block, because lane L
+// keeps the partial sums of the NT / 64 threads L, L + 64, ... of t_row, each
+// over the same vectors in the same order, and adds their wave sums as
+// red_sum does.  vv holds Vt row's vectors q = 64 s + L + NT k (k < KV, s <
+// NT / 64; loaded by t_wave_issue), xl the row's X in LDS; n <= NT * KV *
+// (16-byte vector elements).
+static constexpr int kWaveProdKV = 2;
+template <int DT, int NT>
+__device__ __forceinline__ void t_wave_issue(const typename Elem<DT>::bits_t* __restrict__ v, int n,
+                                             u32x4 (&vv)[kWaveProdKV][NT / 64]) {
+  constexpr int NV = 16 / sizeof(typename Elem<DT>::bits_t);
+  const int nv = n / NV, lane = lane_id();
+  const u32x4* v4 = reinterpret_cast<const u32x4*>(v);
+#pragma unroll
+  for (int k = 0; k < kWaveProdKV; ++k) {
+#pragma unroll
+    for (int s = 0; s < NT / 64; ++s) {
+      const int q = 64 * s + lane + NT * k;
+      vv[k][s] = __builtin_nontemporal_load(v4 + (q < nv ? q : 0));  // past the end: vector 0, skipped
+    }
+  }
+}
+
+template <int DT, int NT>
+__device__ __forceinline__ float t_wave_sum(const u32x4 (&vv)[kWaveProdKV][NT / 64],
+                                            const typename Elem<DT>::bits_t* xl, int n) {
+  constexpr int NS = NT / 64;
+  static_assert(NS == 4, "red_sum order of four waves");
+  constexpr int NV = 16 / sizeof(typename Elem<DT>::bits_t);
+  const int nv = n / NV, lane = lane_id();
+  const u32x4* x4 = reinterpret_cast<const u32x4*>(xl);
+  float acc[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) acc[s] = 0.f;
+#pragma unroll
+  for (int k = 0; k < kWaveProdKV; ++k) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int q = 64 * s + lane + NT * k;
+      if (q < nv) acc[s] = dot16<DT>(vv[k][s], x4[q], acc[s]);
+    }
+  }
+  float ws[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) ws[s] = wave_sum(acc[s]);
+  return (ws[0] + ws[1]) + (ws[2] + ws[3]);
 }
 
 // ---------------------------------------------------------------------------
@@ -993,6 +1043,54 @@ __global__ __launch_bounds__(MTR > 0 ? kMergedThreads : 256) void k_decode(Group
   // ---- T producer: Vt row l and X loaded together, published tagged into
   //      every replica ----
   if constexpr (!MERGED) {
+    if constexpr (FAST && BC == 1 && NT == 256) {
+      // Wave producers: wave w owns T row local * NW + w.  Every wave loads
+      // its Vt row (rows past r: row r - 1, published by no one) while the
+      // block stages X in LDS once, so a producer holds a residency slot of
+      // one wave per T row instead of four, and a launch of a few thousand
+      // blocks fits on the CUs at once.
+      if (producer && ga.prod_rows > 1) {
+        const uint32_t e = load_epoch(a);
+        const int l = local * NW + w;  // wave-uniform
+        const int lc = l < r ? l : r - 1;
+        int tc0, tlen;
+        t_cols(a, lc, tc0, tlen);
+        u32x4 vv[kWaveProdKV][NT / 64];
+        t_wave_issue<DT, NT>(Vt + (int64_t)lc * a.v_ld, tlen, vv);
+        // X (n / NV <= 2 * NT vectors) into LDS, unpadded
+        const u32x4* X4 = reinterpret_cast<const u32x4*>(X);
+        u32x4* dst = reinterpret_cast<u32x4*>(smem + a.x_off);
+        const int xv = n / (16 / (int)sizeof(bits_t));
+        u32x4 xq[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int q = t + NT * k;
+          xq[k] = X4[q < xv ? q : 0];
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int q = t + NT * k;
+          if (q < xv) dst[q] = xq[k];
+        }
+        __syncthreads();
+        const float tval =
+            t_wave_sum<DT, NT>(vv, reinterpret_cast<const bits_t*>(smem + a.x_off) + tc0, tlen);
+        uint32_t arrived = 0;
+        if (t == 0) arrived = arrive_issue(a, sub, e);
+        if (l < r && lane_id() < kTReplicas) {
+          const uint64_t word = (uint64_t)__float_as_uint(tval) | ((uint64_t)tag_of(e) << 32);
+          __hip_atomic_store(a.Tt + (int64_t)lane_id() * a.t_stride + l, word, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        }
+        clear_next_set(a, e);
+        if (t == 0) {
+          uint32_t top = 0;
+          const bool sub_last = arrive_check(a, G, nsub, sub, e, arrived, top);
+          finish_epoch(a, nsub, sub_last, top, tag_of(e));
+        }
+        return;
+      }
+    }
     if (producer) {
       const int l = local;
       const uint32_t e = load_epoch(a);
@@ -1234,6 +1332,7 @@ __global__ __launch_bounds__(MTR > 0 ? kMergedThreads : 256) void k_decode(Group
       tv[k] = __hip_atomic_load(Tr + t_word(t_slot(e)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
+
 
   // sparse part
   float ssum[RPW][BC];

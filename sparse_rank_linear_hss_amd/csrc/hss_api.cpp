@@ -30,7 +30,7 @@ hss_status launch_nm_to_csr(int m, int n, const uint32_t* meta, int32_t* row_ptr
 namespace hss {
 
 namespace {
-constexpr int kNumOptions = 5;
+constexpr int kNumOptions = 7;
 
 int env_route(const char* name, const char* const* words, int nwords) {
   const char* e = std::getenv(name);
@@ -52,6 +52,11 @@ struct Options {
     const char* merged = std::getenv("HSS_DECODE_MERGED");
     v[HSS_OPT_DECODE_MERGED] = (merged && merged[0] == '0') ? 0 : 1;
     v[HSS_OPT_DECODE_FORCE_LOCAL] = 0;
+    const char* wp = std::getenv("HSS_DECODE_WAVE_PRODUCERS");
+    v[HSS_OPT_DECODE_WAVE_PRODUCERS] = (wp && wp[0] == '0') ? 0 : 1;
+    const char* rpw = std::getenv("HSS_DECODE_RPW");
+    const int rv = rpw ? atoi(rpw) : 0;
+    v[HSS_OPT_DECODE_RPW] = (rv == 1 || rv == 2 || rv == 4) ? rv : 0;
   }
 };
 
@@ -85,8 +90,9 @@ extern "C" {
 int hss_version(void) { return 100 * HSS_VERSION_MAJOR + HSS_VERSION_MINOR; }
 
 hss_status hss_set_option(int32_t opt, int32_t value) {
-  static const int32_t hi[] = {4, 2, INT32_MAX, 1, 1};
+  static const int32_t hi[] = {4, 2, INT32_MAX, 1, 1, 1, 4};
   if ((int)opt < 0 || (int)opt >= hss::kNumOptions || value < 0 || value > hi[opt]) return HSS_ERR_INVALID_ARG;
+  if (opt == HSS_OPT_DECODE_RPW && value == 3) return HSS_ERR_INVALID_ARG;
   hss::options().v[opt].store(value, std::memory_order_relaxed);
   return HSS_OK;
 }

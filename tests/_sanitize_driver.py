@@ -66,12 +66,12 @@ def expect(code, want, what):
 
 
 # counts, strings, switches
-assert lib.hss_version() == 106
+assert lib.hss_version() == 107
 for code in range(-1, 8):
     assert lib.hss_status_string(code).startswith(b"HSS")
 assert lib.hss_topk_count(1024, 1024, 5, 100) == 52428
 assert lib.hss_topk_count(2 ** 40, 2 ** 40, 2 ** 20, 1) == -1 and lib.hss_topk_count(1, 1, 1, 0) == -1
-for opt, val, want in [(0, 3, 0), (0, 5, INV), (1, 2, 0), (2, 0, 0), (3, 1, 0), (4, 1, 0), (4, 2, INV), (9, 0, INV),
+for opt, val, want in [(0, 3, 0), (0, 5, INV), (1, 2, 0), (2, 0, 0), (3, 1, 0), (4, 1, 0), (4, 2, INV), (5, 0, 0), (5, 2, INV), (5, 1, 0), (9, 0, INV),
                        (-1, 0, INV), (0, 0, 0), (1, 0, 0), (2, 4096, 0), (4, 0, 0)]:
     expect(lib.hss_set_option(opt, val), want, f"set_option({opt}, {val})")
 assert lib.hss_get_option(99) == -1

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(hl):
 
 
 def test_version_and_strings(hl):
-    assert hl.hss_version() == 106
+    assert hl.hss_version() == 107
     for code in range(6):
         assert hl.status_string(code).startswith("HSS_")
 
@@ -190,14 +190,18 @@ def test_options_set_get_and_reject(hl):
     lib = hl._lib.lib
     L = hl._lib
     defaults = {L.HSS_OPT_BATCH_ROUTE: 0, L.HSS_OPT_GRAD_DS_ROUTE: 0, L.HSS_OPT_DECODE_SPIN: 4096,
-                L.HSS_OPT_DECODE_MERGED: 1, L.HSS_OPT_DECODE_FORCE_LOCAL: 0}
-    for k in ("HSS_CSR_BATCH_ROUTE", "HSS_GRAD_DS_ROUTE", "HSS_DECODE_SPIN", "HSS_DECODE_MERGED"):
+                L.HSS_OPT_DECODE_MERGED: 1, L.HSS_OPT_DECODE_FORCE_LOCAL: 0, L.HSS_OPT_DECODE_WAVE_PRODUCERS: 1,
+                L.HSS_OPT_DECODE_RPW: 0}
+    for k in ("HSS_CSR_BATCH_ROUTE", "HSS_GRAD_DS_ROUTE", "HSS_DECODE_SPIN", "HSS_DECODE_MERGED",
+              "HSS_DECODE_WAVE_PRODUCERS", "HSS_DECODE_RPW"):
         assert k not in os.environ
     for opt, v in defaults.items():
         assert lib.hss_get_option(opt) == v
-    assert lib.hss_get_option(5) == -1 and lib.hss_get_option(-1) == -1
+    assert lib.hss_get_option(7) == -1 and lib.hss_get_option(-1) == -1
     for opt, bad in ((L.HSS_OPT_BATCH_ROUTE, 5), (L.HSS_OPT_GRAD_DS_ROUTE, 3), (L.HSS_OPT_DECODE_SPIN, -1),
-                     (L.HSS_OPT_DECODE_MERGED, 2), (L.HSS_OPT_DECODE_FORCE_LOCAL, -1), (7, 0)):
+                     (L.HSS_OPT_DECODE_MERGED, 2), (L.HSS_OPT_DECODE_FORCE_LOCAL, -1),
+                     (L.HSS_OPT_DECODE_WAVE_PRODUCERS, 2), (L.HSS_OPT_DECODE_RPW, 3),
+                     (L.HSS_OPT_DECODE_RPW, 8), (7, 0)):
         assert lib.hss_set_option(opt, bad) == INV
     with hl.option("batch_route", "densify"):
         assert hl.hss_get_option("batch_route") == 3

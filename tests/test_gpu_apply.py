@@ -182,6 +182,47 @@ def test_apply_local_fallback_is_bitwise_identical(H, hss_opt, fmt, dtype, b, m)
         assert err <= O.TOL[dtype]
 
 
+@pytest.mark.parametrize("fmt,n,shapes", [("csr", 128, [(3000, 64), (2000, 63), (700, 1)]),
+                                            ("csr", 4096, [(2100, 41), (900, 5)]),
+                                            ("csr", 4104, [(2100, 41)]),
+                                            ("2:4", 512, [(2500, 9), (1100, 3)])])
+def test_decode_producer_layouts_are_bitwise_identical(H, hss_opt, fmt, n, shapes):
+    """One bf16 column with separate T producer blocks (merging off): one T row
+    per producer wave (four per block; X of at most 4096 elements) and one T
+    row per block give the same bits for every rows-per-wave setting, and so
+    does every block computing every T row itself.  Ranks that leave the last
+    producer block with idle waves (63, 41, 9, ...), several matrices in one
+    launch, and X one vector too wide for the wave producers (n = 4104)."""
+    dtype = O.BF16
+    hss_opt("batch_route", "decode")
+    hss_opt("decode_merged", 0)
+    X = syn.random_matrix(1, n, dtype, seed=n + 5, kind="normal", scale=1.0)
+    Xd = to_dev(X, dtype)
+    mats, refs = [], []
+    for i, (m, r) in enumerate(shapes):
+        W = syn.random_matrix(m, n, dtype, seed=300 + 11 * i + m, kind="t3")
+        ref = O.split_csr(W, dtype, O.topk_count(m, n, 3, 100)) if fmt == "csr" else O.split_24(W, dtype)
+        U, V = _factors(m, n, r, dtype, 400 + i)
+        mats.append(_matrix(H, fmt, dtype, m, n, ref, U, V))
+        S64 = _dense_S(fmt, dtype, m, n, ref)
+        Uw, Vw, Xw = O.widen(U, dtype), O.widen(V, dtype), O.widen(X, dtype)
+        refs.append((O.apply_factored(S64, Uw, Vw, Xw), O.normaliser(S64, Uw, Vw, Xw)))
+    Ys = H.hss_apply_group(mats, Xd)
+    for Y, (Yref, N) in zip(Ys, refs):
+        _check(Y, dtype, Yref, N)
+    base = [to_host(Y) for Y in Ys]
+    for wave in (0, 1):
+        for rpw in (0, 1, 2, 4):
+            for local in (0, 1):
+                hss_opt("decode_wave_producers", wave)
+                hss_opt("decode_rpw", rpw)
+                hss_opt("decode_force_local", local)
+                got = [to_host(Y) for Y in H.hss_apply_group(mats, Xd)]
+                for i, (g, e) in enumerate(zip(got, base)):
+                    assert O.bits_equal(g, e), (wave, rpw, local, i)
+    hss_opt("decode_force_local", 0)
+
+
 def test_apply_shared_workspace_many_calls(H):
     """One workspace shared by two matrices of different shape, rank and batch,
     called alternately many times: every result equals the one from a fresh
