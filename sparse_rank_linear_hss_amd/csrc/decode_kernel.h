@@ -1333,7 +1333,6 @@ __global__ __launch_bounds__(MTR > 0 ? kMergedThreads : 256) void k_decode(Group
     }
   }
 
-
   // sparse part
   float ssum[RPW][BC];
   if constexpr (is_csr<FMT>)
